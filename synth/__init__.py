@@ -1,0 +1,230 @@
+"""Seeded synthetic decode batches for block top-k sparse decode attention.
+
+This module draws inputs only: random tensors, lengths and page tables.  It holds
+none of the method's arithmetic (no means, no scores, no selection, no softmax),
+so the CPU oracle and the HIP library can both be fed from it without sharing
+any computation.
+
+Every tensor is drawn on the CPU from one ``torch.Generator`` seeded with
+``1000 * config + variant`` in a fixed order (lengths, page permutation,
+per-block key offsets, heavy-block mask and directions, key noise, values,
+queries, then filler for unused slots), in float32, then cast to the cache dtype
+with round-to-nearest-even.  Both sides therefore read identical bytes.
+
+Value model (workload descriptions of the five decode shapes):
+  K_t = z_t + o_block + [heavy] * 2.0 * u_block,  z ~ N(0,1)^D, o ~ N(0, 0.5^2)^D,
+  u a unit vector (normalised Gaussian); V, Q ~ N(0,1).
+The per-block offset belongs to the physical page, so a page shared by several
+sequences (a common prompt prefix) has one offset.  Slots past a sequence's last
+token, and pages no sequence references, hold large filler values (|x| ~ 100)
+so that a kernel reading them gives visibly wrong results.
+
+Layouts: q [B,Hq,D]; k_cache [pages,Hkv,P,D]; v_cache [pages,Hkv,D,P];
+block_table [B,max_blocks] int32 (entries past a sequence's blocks point at a
+filler page, never at an invalid id); seq_lens [B] int32.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional, Sequence
+
+import torch
+
+PAGE = 16
+FILLER_SCALE = 100.0
+
+
+@dataclass
+class Batch:
+    name: str
+    seed: int
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    num_pages: int
+    max_blocks: int
+    top_k: int
+    dtype: torch.dtype
+    q: torch.Tensor
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    block_table: torch.Tensor
+    seq_lens: torch.Tensor
+    notes: dict = field(default_factory=dict)
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    def n_blocks(self) -> torch.Tensor:
+        return (self.seq_lens + self.page_size - 1) // self.page_size
+
+    def to(self, device) -> "Batch":
+        kw = dict(self.__dict__)
+        for key in ("q", "k_cache", "v_cache", "block_table", "seq_lens"):
+            kw[key] = getattr(self, key).to(device)
+        return Batch(**kw)
+
+
+def make_batch(*, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+               seq_lens: Sequence[int] | torch.Tensor | None = None,
+               len_range: Optional[tuple[int, int]] = None,
+               top_k: int, dtype: torch.dtype = torch.bfloat16, seed: int = 0,
+               table: str = "shuffled", shared_prefix: int = 0, heavy_frac: float = 0.0,
+               offset_std: float = 0.5, page_size: int = PAGE, spare_pages: int = 2,
+               max_blocks: Optional[int] = None, name: str = "custom") -> Batch:
+    """Draw one decode batch.
+
+    table: "identity" (sequence b owns pages b*max_blocks + j), "shuffled"
+    (a random permutation of all used pages) or "shared" (the first
+    shared_prefix tokens' pages are the same physical pages for every sequence,
+    private pages shuffled).  seq_lens count the newest token.
+    """
+    if num_q_heads % num_kv_heads:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    g = torch.Generator().manual_seed(int(seed))
+    P = page_size
+    # 1. lengths
+    if seq_lens is not None:
+        lens = torch.as_tensor(list(seq_lens) if not torch.is_tensor(seq_lens) else seq_lens,
+                               dtype=torch.int64).reshape(batch)
+    else:
+        lo, hi = len_range
+        lens = torch.randint(lo, hi + 1, (batch,), generator=g, dtype=torch.int64)
+    if int(lens.min()) < 1:
+        raise ValueError("every sequence holds at least its newest token")
+    nblk = (lens + P - 1) // P
+    if max_blocks is None:
+        max_blocks = int(nblk.max()) + 1
+    if int(nblk.max()) > max_blocks:
+        raise ValueError("max_blocks too small")
+
+    # 2. page assignment
+    bt = torch.empty((batch, max_blocks), dtype=torch.int64)
+    if table == "identity":
+        used = batch * max_blocks
+        for b in range(batch):
+            bt[b] = torch.arange(b * max_blocks, (b + 1) * max_blocks)
+        num_pages = used + spare_pages
+        filler_page = used  # spare page
+        for b in range(batch):
+            bt[b, int(nblk[b]):] = filler_page
+        perm_used = None
+    else:
+        n_shared = (shared_prefix // P) if table == "shared" else 0
+        if table == "shared" and shared_prefix % P:
+            raise ValueError("shared prefix must be a whole number of pages")
+        if table not in ("shuffled", "shared"):
+            raise ValueError(f"unknown table kind {table}")
+        private = int((nblk - n_shared).clamp(min=0).sum())
+        used = n_shared + private
+        num_pages = used + spare_pages
+        perm = torch.randperm(num_pages, generator=g)
+        shared_ids = perm[:n_shared]
+        priv_ids = perm[n_shared:used]
+        filler_page = int(perm[used]) if spare_pages > 0 else int(perm[0])
+        cur = 0
+        for b in range(batch):
+            nb = int(nblk[b])
+            if n_shared:
+                if nb < n_shared:
+                    raise ValueError("sequence shorter than the shared prefix")
+                bt[b, :n_shared] = shared_ids
+            cnt = nb - n_shared
+            bt[b, n_shared:nb] = priv_ids[cur:cur + cnt]
+            cur += cnt
+            bt[b, nb:] = filler_page
+        perm_used = perm[:used]
+
+    hkv, D = num_kv_heads, head_dim
+    # 3. per-block key offsets, one per (physical page, KV head)
+    offset = torch.randn((num_pages, hkv, D), generator=g) * offset_std
+    # 4. heavy blocks: +2.0 along a random unit direction
+    heavy = torch.rand((num_pages, hkv), generator=g) < heavy_frac
+    direc = torch.randn((num_pages, hkv, D), generator=g)
+    direc = direc / direc.norm(dim=-1, keepdim=True)
+    offset = offset + heavy.unsqueeze(-1).to(torch.float32) * 2.0 * direc
+    # 5. key noise, 6. values, 7. queries
+    k = torch.randn((num_pages, hkv, P, D), generator=g)
+    k += offset.unsqueeze(2)
+    v = torch.randn((num_pages, hkv, D, P), generator=g)
+    q = torch.randn((batch, num_q_heads, D), generator=g)
+
+    # 8. filler for slots no sequence uses: pages not referenced, and the tail of
+    #    each sequence's last page
+    valid = torch.zeros((num_pages, P), dtype=torch.bool)
+    for b in range(batch):
+        nb, L = int(nblk[b]), int(lens[b])
+        pages = bt[b, :nb]
+        valid[pages[:-1]] = True
+        last_valid = L - (nb - 1) * P
+        valid[pages[-1], :last_valid] = True
+    invalid = ~valid
+    if bool(invalid.any()):
+        n_inv = int(invalid.sum())
+        fk = torch.randn((n_inv, hkv, D), generator=g) * FILLER_SCALE
+        fv = torch.randn((n_inv, hkv, D), generator=g) * FILLER_SCALE
+        pi, ti = invalid.nonzero(as_tuple=True)
+        k[pi, :, ti, :] = fk
+        v[pi, :, :, ti] = fv
+
+    batch_obj = Batch(name=name, seed=int(seed), batch=batch, num_q_heads=num_q_heads,
+                      num_kv_heads=hkv, head_dim=D, page_size=P, num_pages=num_pages,
+                      max_blocks=max_blocks, top_k=int(top_k), dtype=dtype,
+                      q=q.to(dtype), k_cache=k.to(dtype), v_cache=v.to(dtype),
+                      block_table=bt.to(torch.int32), seq_lens=lens.to(torch.int32),
+                      notes={"table": table, "shared_prefix": shared_prefix,
+                             "heavy_frac": heavy_frac, "filler_page": filler_page})
+    return batch_obj
+
+
+# The five decode workloads.  seed = 1000 * config + variant.
+CONFIGS = {
+    1: dict(name="tiny-fp32", batch=1, num_q_heads=2, num_kv_heads=1, head_dim=64,
+            seq_lens=[1024], top_k=8, dtype=torch.float32, table="identity"),
+    2: dict(name="qwen3-0.6b", batch=64, num_q_heads=16, num_kv_heads=8, head_dim=128,
+            seq_lens=[8192] * 64, top_k=16, dtype=torch.bfloat16, table="identity",
+            heavy_frac=0.05),
+    3: dict(name="qwen3-8b", batch=32, num_q_heads=32, num_kv_heads=8, head_dim=128,
+            len_range=(4096, 32768), top_k=32, dtype=torch.bfloat16, table="shuffled"),
+    4: dict(name="qwen3-30b-a3b", batch=16, num_q_heads=32, num_kv_heads=4, head_dim=128,
+            seq_lens=[2048 + 30720] * 16, top_k=64, dtype=torch.bfloat16, table="shared",
+            shared_prefix=2048),
+    5: dict(name="qwen3-32b", batch=8, num_q_heads=64, num_kv_heads=8, head_dim=128,
+            seq_lens=[32768] * 8, top_k=64, dtype=torch.bfloat16, table="shuffled"),
+}
+SWEEP_LENS = (8192, 16384, 32768, 65536)
+
+
+def make_config(config: int, variant: int = 0, *, context: Optional[int] = None,
+                table: Optional[str] = None, top_k: Optional[int] = None,
+                heavy_frac: Optional[float] = None, batch: Optional[int] = None) -> Batch:
+    """One of the five workloads, with optional overrides.
+
+    config 5 takes ``context`` from its sweep (default 32768).  ``batch``
+    truncates the batch (for quick checks); lengths are drawn for the full batch
+    first so the leading sequences are the same as in the full workload.
+    """
+    spec = dict(CONFIGS[config])
+    name = spec.pop("name")
+    if context is not None:
+        spec["seq_lens"] = [context] * spec["batch"]
+        spec.pop("len_range", None)
+    if table is not None:
+        spec["table"] = table
+    if top_k is not None:
+        spec["top_k"] = top_k
+    if heavy_frac is not None:
+        spec["heavy_frac"] = heavy_frac
+    if batch is not None and batch != spec["batch"]:
+        if "len_range" in spec:
+            g = torch.Generator().manual_seed(1000 * config + variant)
+            lo, hi = spec.pop("len_range")
+            lens = torch.randint(lo, hi + 1, (spec["batch"],), generator=g, dtype=torch.int64)
+            spec["seq_lens"] = lens[:batch].tolist()
+        else:
+            spec["seq_lens"] = spec["seq_lens"][:batch]
+        spec["batch"] = batch
+    return make_batch(seed=1000 * config + variant, name=name, **spec)
