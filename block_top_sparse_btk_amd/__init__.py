@@ -1,0 +1,266 @@
+"""Python binding of libbtk: block top-k sparse decode attention on MI355X.
+
+Argument marshalling only: every step of the method runs in the HIP kernels of
+``libbtk.so`` (built from ``csrc/`` for gfx950 by ``build.py``).  PyTorch
+supplies device memory and the current HIP stream.  Importing works without a
+GPU; calling a compute function without the built library raises.
+
+The functions carry the names of the C entry points declared in
+``include/btk.h`` and take torch tensors laid out as documented there:
+  q, out       [B, Hq, D]                 bf16 or fp32
+  k_cache      [num_pages, Hkv, 16, D]    token-major pages
+  v_cache      [num_pages, Hkv, D, 16]    dim-major pages
+  block_table  [B, max_blocks] int32, seq_lens [B] int32
+  centroids    [num_pages, Hkv, D] fp32, indices [B, Hkv, top_k] int32
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbtk.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "btk.h")
+
+BTK_OK, BTK_ERR_NULL, BTK_ERR_SHAPE, BTK_ERR_UNSUPPORTED, BTK_ERR_WORKSPACE, BTK_ERR_HIP = range(6)
+BTK_BF16, BTK_F32 = 0, 1
+PAGE_SIZE = 16
+
+
+class btk_problem_t(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("max_blocks_per_seq", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("sm_scale", ctypes.c_float)]
+
+
+class BtkError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        msg = _lib().btk_status_string(status).decode()
+        if status == BTK_ERR_HIP:
+            msg += f" (hipError {_lib().btk_last_hip_error()})"
+        super().__init__(f"{what}: {msg}")
+        self.status = status
+
+
+_LIB = None
+
+
+def _lib():
+    """Load libbtk.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libbtk.so not built: run `python {os.path.join(_HERE, 'build.py')}`"
+                               " (or __graft_entry__.build())")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, vp, i32, sz = ctypes.POINTER(btk_problem_t), ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        st = ctypes.c_int
+        lib.btk_abi_version.restype = ctypes.c_int
+        lib.btk_status_string.restype = ctypes.c_char_p
+        lib.btk_status_string.argtypes = [st]
+        lib.btk_last_hip_error.restype = ctypes.c_int
+        lib.btk_workspace_bytes.restype = sz
+        lib.btk_workspace_bytes.argtypes = [P, i32]
+        lib.btk_centroid_update.restype = st
+        lib.btk_centroid_update.argtypes = [P, vp, vp, vp, vp, vp, vp]
+        lib.btk_select.restype = st
+        lib.btk_select.argtypes = [P, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
+        lib.btk_sparse_attend.restype = st
+        lib.btk_sparse_attend.argtypes = [P, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
+        lib.btk_dense_attend.restype = st
+        lib.btk_dense_attend.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        _LIB = lib
+    return _LIB
+
+
+def header_symbols() -> list[str]:
+    """Names of the functions declared in include/btk.h."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(btk_[a-z_]+)\s*\(", text)))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BTK_BF16
+    if t.dtype == torch.float32:
+        return BTK_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def make_problem(q: torch.Tensor, k_cache: torch.Tensor, block_table: torch.Tensor,
+                 sm_scale: float = 0.0) -> btk_problem_t:
+    B, hq, dim = q.shape
+    num_pages, hkv, page, kd = k_cache.shape
+    if kd != dim:
+        raise ValueError("q and k_cache head_dim differ")
+    return btk_problem_t(B, hq, hkv, dim, page, num_pages, block_table.shape[1], _dtype_code(q),
+                         float(sm_scale))
+
+
+def btk_workspace_bytes(problem: btk_problem_t, top_k: int) -> int:
+    return int(_lib().btk_workspace_bytes(ctypes.byref(problem), int(top_k)))
+
+
+def new_workspace(problem: btk_problem_t, top_k: int, device) -> torch.Tensor:
+    """A zero-filled workspace tensor of btk_workspace_bytes(problem, top_k) bytes."""
+    n = btk_workspace_bytes(problem, top_k)
+    if n == 0:
+        raise ValueError("invalid problem for this library build")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def workspace_error_bits(workspace: torch.Tensor) -> int:
+    """Sticky error bits that kernels set for out-of-range device inputs."""
+    return int(workspace[:4].view(torch.int32).item())
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, device=None) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t.data_ptr()
+
+
+def _expect(t: Optional[torch.Tensor], name: str, shape) -> None:
+    if t is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _check_shapes(p: btk_problem_t, q=None, k_cache=None, v_cache=None, block_table=None,
+                  seq_lens=None, centroids=None, indices=None, out=None, lse=None, scores=None,
+                  first_pos=None, top_k=None) -> None:
+    """The C ABI cannot see device buffer sizes: check every tensor against the problem."""
+    B, hq, hkv, D, P = p.batch, p.num_q_heads, p.num_kv_heads, p.head_dim, p.page_size
+    _expect(q, "q", (B, hq, D))
+    _expect(out, "out", (B, hq, D))
+    _expect(k_cache, "k_cache", (p.num_pages, hkv, P, D))
+    _expect(v_cache, "v_cache", (p.num_pages, hkv, D, P))
+    _expect(block_table, "block_table", (B, p.max_blocks_per_seq))
+    _expect(seq_lens, "seq_lens", (B,))
+    _expect(first_pos, "first_pos", (B,))
+    _expect(centroids, "centroids", (p.num_pages, hkv, D))
+    _expect(lse, "lse", (B, hq))
+    _expect(scores, "scores", (B, hkv, p.max_blocks_per_seq))
+    if indices is not None:
+        _expect(indices, "indices", (B, hkv, top_k if top_k is not None else indices.shape[-1]))
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check(status: int, what: str) -> None:
+    if status != BTK_OK:
+        raise BtkError(status, what)
+
+
+def btk_centroid_update(k_cache, block_table, seq_lens, centroids, first_pos=None,
+                        problem: Optional[btk_problem_t] = None, q_heads: Optional[int] = None):
+    """S1: recompute centroids of the touched pages (all pages if first_pos is None)."""
+    dev = k_cache.device
+    if problem is None:
+        num_pages, hkv, page, dim = k_cache.shape
+        problem = btk_problem_t(block_table.shape[0], q_heads or hkv, hkv, dim, page, num_pages,
+                                block_table.shape[1], _dtype_code(k_cache), 0.0)
+    _check_shapes(problem, k_cache=k_cache, block_table=block_table, seq_lens=seq_lens,
+                  centroids=centroids, first_pos=first_pos)
+    fp = _dev(first_pos, "first_pos", torch.int32, dev) if first_pos is not None else None
+    st = _lib().btk_centroid_update(ctypes.byref(problem), _dev(k_cache, "k_cache", None, dev),
+                                    _dev(block_table, "block_table", torch.int32, dev),
+                                    _dev(seq_lens, "seq_lens", torch.int32, dev), fp,
+                                    _dev(centroids, "centroids", torch.float32, dev), _stream(dev))
+    _check(st, "btk_centroid_update")
+    return centroids
+
+
+def btk_select(q, centroids, block_table, seq_lens, top_k, workspace, indices=None, scores=None,
+               sm_scale: float = 0.0, problem: Optional[btk_problem_t] = None):
+    """S2+S3: group block scores and top-k block indices [B, Hkv, top_k] int32."""
+    dev = q.device
+    if problem is None:
+        num_pages, hkv, dim = centroids.shape
+        problem = btk_problem_t(q.shape[0], q.shape[1], hkv, dim, PAGE_SIZE, num_pages,
+                                block_table.shape[1], _dtype_code(q), float(sm_scale))
+    if indices is None:
+        indices = torch.empty((problem.batch, problem.num_kv_heads, int(top_k)), dtype=torch.int32,
+                              device=dev)
+    _check_shapes(problem, q=q, block_table=block_table, seq_lens=seq_lens, centroids=centroids,
+                  indices=indices, scores=scores, top_k=top_k)
+    sp = _dev(scores, "scores", torch.float32, dev) if scores is not None else None
+    st = _lib().btk_select(ctypes.byref(problem), _dev(q, "q", None, dev),
+                           _dev(centroids, "centroids", torch.float32, dev),
+                           _dev(block_table, "block_table", torch.int32, dev),
+                           _dev(seq_lens, "seq_lens", torch.int32, dev), int(top_k),
+                           _dev(indices, "indices", torch.int32, dev), sp,
+                           _dev(workspace, "workspace", torch.uint8, dev), workspace.numel(),
+                           _stream(dev))
+    _check(st, "btk_select")
+    return indices
+
+
+def btk_sparse_attend(q, k_cache, v_cache, block_table, seq_lens, indices, workspace, out=None,
+                      lse=None, sm_scale: float = 0.0, problem: Optional[btk_problem_t] = None):
+    """S4: exact softmax attention over the listed blocks; returns out [B, Hq, D]."""
+    dev = q.device
+    problem = problem or make_problem(q, k_cache, block_table, sm_scale)
+    out = torch.empty_like(q) if out is None else out
+    _check_shapes(problem, q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
+                  seq_lens=seq_lens, indices=indices, out=out, lse=lse)
+    lp = _dev(lse, "lse", torch.float32, dev) if lse is not None else None
+    st = _lib().btk_sparse_attend(ctypes.byref(problem), _dev(q, "q", None, dev),
+                                  _dev(k_cache, "k_cache", q.dtype, dev),
+                                  _dev(v_cache, "v_cache", q.dtype, dev),
+                                  _dev(block_table, "block_table", torch.int32, dev),
+                                  _dev(seq_lens, "seq_lens", torch.int32, dev),
+                                  _dev(indices, "indices", torch.int32, dev), indices.shape[-1],
+                                  _dev(out, "out", q.dtype, dev), lp,
+                                  _dev(workspace, "workspace", torch.uint8, dev), workspace.numel(),
+                                  _stream(dev))
+    _check(st, "btk_sparse_attend")
+    return out
+
+
+def btk_dense_attend(q, k_cache, v_cache, block_table, seq_lens, workspace, out=None, lse=None,
+                     sm_scale: float = 0.0, problem: Optional[btk_problem_t] = None):
+    """S5: dense paged decode attention over every block; returns out [B, Hq, D]."""
+    dev = q.device
+    problem = problem or make_problem(q, k_cache, block_table, sm_scale)
+    out = torch.empty_like(q) if out is None else out
+    _check_shapes(problem, q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
+                  seq_lens=seq_lens, out=out, lse=lse)
+    lp = _dev(lse, "lse", torch.float32, dev) if lse is not None else None
+    st = _lib().btk_dense_attend(ctypes.byref(problem), _dev(q, "q", None, dev),
+                                 _dev(k_cache, "k_cache", q.dtype, dev),
+                                 _dev(v_cache, "v_cache", q.dtype, dev),
+                                 _dev(block_table, "block_table", torch.int32, dev),
+                                 _dev(seq_lens, "seq_lens", torch.int32, dev),
+                                 _dev(out, "out", q.dtype, dev), lp,
+                                 _dev(workspace, "workspace", torch.uint8, dev), workspace.numel(),
+                                 _stream(dev))
+    _check(st, "btk_dense_attend")
+    return out
+
+
+def sparse_decode_step(q, k_cache, v_cache, block_table, seq_lens, centroids, top_k, workspace,
+                       first_pos=None, out=None, indices=None, lse=None, scores=None,
+                       sm_scale: float = 0.0, problem: Optional[btk_problem_t] = None):
+    """One decode step of the method: S1 (touched pages), S2+S3, S4, all on the current stream."""
+    problem = problem or make_problem(q, k_cache, block_table, sm_scale)
+    btk_centroid_update(k_cache, block_table, seq_lens, centroids, first_pos, problem=problem)
+    indices = btk_select(q, centroids, block_table, seq_lens, top_k, workspace,
+                         indices=indices, scores=scores, problem=problem)
+    out = btk_sparse_attend(q, k_cache, v_cache, block_table, seq_lens, indices, workspace,
+                            out=out, lse=lse, problem=problem)
+    return out, indices

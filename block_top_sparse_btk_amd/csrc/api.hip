@@ -1,0 +1,168 @@
+// C ABI of libbtk: host-side validation, launch planning and dispatch.
+// Every argument is checked here before the first HIP call, so a rejected call
+// has no side effects and the checks run on machines without a GPU.
+#include <math.h>
+
+#include "../../include/btk.h"
+#include "btk_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+btk_status_t hip_status(hipError_t e) {
+    if (e == hipSuccess) return BTK_OK;
+    g_last_hip_error = (int)e;
+    return BTK_ERR_HIP;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Validates the problem; fills the internal dims on success.
+btk_status_t check_problem(const btk_problem_t *p, btk::Dims *d) {
+    if (!p) return BTK_ERR_NULL;
+    if (p->batch < 1 || p->num_q_heads < 1 || p->num_kv_heads < 1 || p->head_dim < 1 ||
+        p->page_size < 1 || p->num_pages < 1 || p->max_blocks_per_seq < 1)
+        return BTK_ERR_SHAPE;
+    if (p->num_q_heads % p->num_kv_heads) return BTK_ERR_SHAPE;
+    if (!(isfinite(p->sm_scale))) return BTK_ERR_SHAPE;
+    if (p->dtype != BTK_BF16 && p->dtype != BTK_F32) return BTK_ERR_UNSUPPORTED;
+    if (p->head_dim != 64 && p->head_dim != 128) return BTK_ERR_UNSUPPORTED;
+    if (p->page_size != btk::kPage) return BTK_ERR_UNSUPPORTED;
+    if (p->num_q_heads / p->num_kv_heads > btk::kMaxGroup) return BTK_ERR_UNSUPPORTED;
+    if (p->max_blocks_per_seq > btk::kMaxBlocksPerSeq) return BTK_ERR_UNSUPPORTED;
+    // grid sizes stay well inside 32 bits
+    if ((size_t)p->batch * p->num_kv_heads * p->max_blocks_per_seq > ((size_t)1 << 31))
+        return BTK_ERR_UNSUPPORTED;
+    d->B = p->batch;
+    d->Hq = p->num_q_heads;
+    d->Hkv = p->num_kv_heads;
+    d->D = p->head_dim;
+    d->num_pages = p->num_pages;
+    d->max_blocks = p->max_blocks_per_seq;
+    d->dtype = p->dtype;
+    d->sm_scale = p->sm_scale > 0.f ? p->sm_scale : 1.0f / sqrtf((float)p->head_dim);
+    return BTK_OK;
+}
+
+bool top_k_ok(int32_t top_k) { return top_k >= 1 && top_k <= btk::kMaxBlocksPerSeq; }
+
+}  // namespace
+
+namespace btk {
+
+WorkspaceLayout workspace_layout(const Dims &d, int top_k) {
+    const size_t units = (size_t)d.B * d.Hkv;
+    const AttendPlan sp = plan_attend(d, top_k, false);
+    const AttendPlan dp = plan_attend(d, d.max_blocks, true);
+    const size_t nsplit = sp.nsplit_max > dp.nsplit_max ? sp.nsplit_max : dp.nsplit_max;
+    const size_t row = (size_t)d.group() * d.D + 2 * (size_t)d.group();
+    WorkspaceLayout w;
+    w.sel_counters = 256;
+    w.att_counters = w.sel_counters + align256(units * sizeof(uint32_t));
+    w.scores = w.att_counters + align256(units * sizeof(uint32_t));
+    w.partials = w.scores + align256(units * d.max_blocks * sizeof(float));
+    w.total = w.partials + align256(units * nsplit * row * sizeof(float));
+    return w;
+}
+
+}  // namespace btk
+
+extern "C" {
+
+int btk_abi_version(void) { return BTK_ABI_VERSION; }
+
+const char *btk_status_string(btk_status_t s) {
+    switch (s) {
+    case BTK_OK: return "ok";
+    case BTK_ERR_NULL: return "a required pointer is NULL";
+    case BTK_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case BTK_ERR_UNSUPPORTED: return "unsupported dtype, head_dim, page_size or limit";
+    case BTK_ERR_WORKSPACE: return "workspace missing or too small";
+    case BTK_ERR_HIP: return "HIP runtime error at launch";
+    }
+    return "unknown status";
+}
+
+int btk_last_hip_error(void) { return g_last_hip_error; }
+
+size_t btk_workspace_bytes(const btk_problem_t *problem, int32_t top_k) {
+    btk::Dims d;
+    if (check_problem(problem, &d) != BTK_OK || !top_k_ok(top_k)) return 0;
+    return btk::workspace_layout(d, top_k).total;
+}
+
+btk_status_t btk_centroid_update(const btk_problem_t *problem, const void *k_cache,
+                                 const int32_t *block_table, const int32_t *seq_lens,
+                                 const int32_t *first_pos, float *centroids, void *stream) {
+    btk::Dims d;
+    btk_status_t st = check_problem(problem, &d);
+    if (st != BTK_OK) return st;
+    if (!k_cache || !block_table || !seq_lens || !centroids) return BTK_ERR_NULL;
+    return hip_status(btk::launch_centroid_update(d, k_cache, block_table, seq_lens, first_pos,
+                                                  centroids, (hipStream_t)stream));
+}
+
+btk_status_t btk_select(const btk_problem_t *problem, const void *q, const float *centroids,
+                        const int32_t *block_table, const int32_t *seq_lens, int32_t top_k,
+                        int32_t *indices, float *scores, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    btk::Dims d;
+    btk_status_t st = check_problem(problem, &d);
+    if (st != BTK_OK) return st;
+    if (!q || !centroids || !block_table || !seq_lens || !indices) return BTK_ERR_NULL;
+    if (!top_k_ok(top_k)) return BTK_ERR_SHAPE;
+    const btk::WorkspaceLayout w = btk::workspace_layout(d, top_k);
+    if (!workspace || workspace_bytes < w.total) return BTK_ERR_WORKSPACE;
+    char *ws = static_cast<char *>(workspace);
+    float *sc = scores ? scores : reinterpret_cast<float *>(ws + w.scores);
+    const btk::SelectPlan plan = btk::plan_select(d);
+    return hip_status(btk::launch_select(d, plan, q, centroids, block_table, seq_lens, top_k,
+                                         indices, sc,
+                                         reinterpret_cast<uint32_t *>(ws + w.sel_counters),
+                                         reinterpret_cast<uint32_t *>(ws), (hipStream_t)stream));
+}
+
+btk_status_t btk_sparse_attend(const btk_problem_t *problem, const void *q, const void *k_cache,
+                               const void *v_cache, const int32_t *block_table,
+                               const int32_t *seq_lens, const int32_t *indices, int32_t top_k,
+                               void *out, float *lse, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+    btk::Dims d;
+    btk_status_t st = check_problem(problem, &d);
+    if (st != BTK_OK) return st;
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !indices || !out)
+        return BTK_ERR_NULL;
+    if (!top_k_ok(top_k)) return BTK_ERR_SHAPE;
+    const btk::WorkspaceLayout w = btk::workspace_layout(d, top_k);
+    if (!workspace || workspace_bytes < w.total) return BTK_ERR_WORKSPACE;
+    char *ws = static_cast<char *>(workspace);
+    const btk::AttendPlan plan = btk::plan_attend(d, top_k, false);
+    return hip_status(btk::launch_attend(d, plan, false, q, k_cache, v_cache, block_table,
+                                         seq_lens, indices, top_k, out, lse,
+                                         reinterpret_cast<float *>(ws + w.partials),
+                                         reinterpret_cast<uint32_t *>(ws + w.att_counters),
+                                         reinterpret_cast<uint32_t *>(ws), (hipStream_t)stream));
+}
+
+btk_status_t btk_dense_attend(const btk_problem_t *problem, const void *q, const void *k_cache,
+                              const void *v_cache, const int32_t *block_table,
+                              const int32_t *seq_lens, void *out, float *lse, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+    btk::Dims d;
+    btk_status_t st = check_problem(problem, &d);
+    if (st != BTK_OK) return st;
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out) return BTK_ERR_NULL;
+    // the dense path needs no top_k; size the workspace as for top_k = 1
+    const btk::WorkspaceLayout w = btk::workspace_layout(d, 1);
+    if (!workspace || workspace_bytes < w.total) return BTK_ERR_WORKSPACE;
+    char *ws = static_cast<char *>(workspace);
+    const btk::AttendPlan plan = btk::plan_attend(d, d.max_blocks, true);
+    return hip_status(btk::launch_attend(d, plan, true, q, k_cache, v_cache, block_table,
+                                         seq_lens, nullptr, 0, out, lse,
+                                         reinterpret_cast<float *>(ws + w.partials),
+                                         reinterpret_cast<uint32_t *>(ws + w.att_counters),
+                                         reinterpret_cast<uint32_t *>(ws), (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,110 @@
+// Internal declarations shared by the HIP translation units of libbtk.
+// Device helpers for gfx950 (wave64, MFMA), the launch plans that the C ABI
+// computes on the host, and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace btk {
+
+constexpr int kWave = 64;
+constexpr int kPage = 16;           // tokens per page (block); all kernels assume it
+constexpr int kMaxBlocksPerSeq = 8192;  // select keeps <= 32 keys per thread x 256
+constexpr int kMaxGroup = 16;       // query heads per KV head: MFMA tile rows
+
+// error bits in workspace word 0
+constexpr uint32_t kErrSeqLen = 1u;
+constexpr uint32_t kErrPage = 2u;
+constexpr uint32_t kErrIndex = 4u;
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) short short4_t;
+typedef __attribute__((ext_vector_type(4))) float floatx4_t;
+
+// ---- device helpers ------------------------------------------------------
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+    return __uint_as_float(h << 16);
+}
+
+// float -> bf16 bits, round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Order-preserving map of a float score to uint32 (larger score -> larger key);
+// -0.0 maps like +0.0 so that the two tie.
+__device__ __forceinline__ uint32_t score_key(float s) {
+    uint32_t u = __float_as_uint(s);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ void store_relaxed(float *p, float v) {
+    __hip_atomic_store(reinterpret_cast<uint32_t *>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float load_relaxed(const float *p) {
+    return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t *>(p),
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+__device__ __forceinline__ void flag_error(uint32_t *err, uint32_t bit) {
+    if (err) atomicOr(err, bit);
+}
+
+// ---- launch plans ----------------------------------------------------------
+
+struct Dims {
+    int B, Hq, Hkv, D, num_pages, max_blocks, dtype;
+    float sm_scale;  // resolved (> 0)
+    int group() const { return Hq / Hkv; }
+};
+
+struct SelectPlan {
+    int chunk;       // blocks scored per workgroup
+    int nchunk_max;  // chunks per unit at max_blocks
+};
+
+struct AttendPlan {
+    int bps;         // list entries (blocks) per workgroup split
+    int nsplit_max;  // splits per unit at the longest list
+};
+
+SelectPlan plan_select(const Dims &d);
+AttendPlan plan_attend(const Dims &d, int list_len_max, bool dense);
+
+// Workspace layout (bytes, each region 256-aligned):
+//   [0, 256)                   error word + spare
+//   select counters            B*Hkv uint32
+//   attend counters            B*Hkv uint32
+//   scores scratch             B*Hkv*max_blocks float
+//   attend partials            B*Hkv*nsplit_max*(r*D + 2r) float (max of sparse, dense)
+struct WorkspaceLayout {
+    size_t sel_counters, att_counters, scores, partials, total;
+};
+WorkspaceLayout workspace_layout(const Dims &d, int top_k);
+
+// ---- launchers (return hipError_t of the launch) --------------------------
+
+hipError_t launch_centroid_update(const Dims &d, const void *k_cache, const int32_t *block_table,
+                                  const int32_t *seq_lens, const int32_t *first_pos,
+                                  float *centroids, hipStream_t stream);
+
+hipError_t launch_select(const Dims &d, const SelectPlan &plan, const void *q,
+                         const float *centroids, const int32_t *block_table,
+                         const int32_t *seq_lens, int top_k, int32_t *indices, float *scores,
+                         uint32_t *counters, uint32_t *err, hipStream_t stream);
+
+hipError_t launch_attend(const Dims &d, const AttendPlan &plan, bool dense, const void *q,
+                         const void *k_cache, const void *v_cache, const int32_t *block_table,
+                         const int32_t *seq_lens, const int32_t *indices, int top_k, void *out,
+                         float *lse, float *partials, uint32_t *counters, uint32_t *err,
+                         hipStream_t stream);
+
+}  // namespace btk

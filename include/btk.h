@@ -1,0 +1,172 @@
+/*
+ * btk.h -- block top-k sparse decode attention on AMD MI355X (gfx950).
+ *
+ * The method: keys of each KV head are grouped into fixed-size blocks (one KV
+ * cache page each), every block is summarised by its mean key (its centroid),
+ * the query heads that share a KV head (one grouped-query "query group") score
+ * every centroid together, keep the top-k blocks, and run exact softmax
+ * attention over only those blocks.  Sources: Pith review of "Kinetics:
+ * Rethinking Test-Time Scaling Laws" (pith.science), section "What carries the
+ * argument"; paging, block = page and top-k counted in pages: Kinetics README
+ * (GitLite mirror), section "Benchmark Block TopK Attention throughput".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every buffer argument is a DEVICE pointer owned by the caller, unless it is
+ *    marked "host".  The library never allocates, frees or synchronises device
+ *    memory; every call is enqueued asynchronously on `stream` (a hipStream_t,
+ *    NULL = the default stream) and returns once its kernels are launched.
+ *  - Arguments are validated on the host before any HIP call.  A rejected call
+ *    returns an error status and touches nothing.  No C++ exception crosses the
+ *    ABI.  A launch failure returns BTK_ERR_HIP (see btk_last_hip_error()).
+ *  - Device-resident contents (page ids, lengths, indices) are not inspected on
+ *    the host.  Kernels never read outside the caller's buffers for any input:
+ *    an out-of-range page id, length or index is skipped, and, where the call
+ *    has a workspace, sets a sticky bit in workspace word 0 (bit 0: a length
+ *    outside [1, max_blocks_per_seq * page_size]; bit 1: a page id outside
+ *    [0, num_pages); bit 2: a block index outside [0, n_b) or repeated).
+ *    Results for such inputs are unspecified.
+ *
+ * Notation: B = batch, Hq / Hkv = query / KV heads, r = Hq / Hkv (the query
+ * group size; query head h uses KV head h / r), D = head_dim, P = page_size,
+ * L_b = seq_lens[b] (counts the newest token), n_b = ceil(L_b / P) blocks,
+ * block j of sequence b holds logical tokens [j*P, min(L_b, j*P+P)).
+ *
+ * Layouts (row-major):
+ *   q, out       [B][Hq][D]                dtype
+ *   k_cache      [num_pages][Hkv][P][D]    dtype   token-major pages
+ *   v_cache      [num_pages][Hkv][D][P]    dtype   dim-major pages
+ *   block_table  [B][max_blocks_per_seq]   int32   logical block -> page id
+ *   seq_lens     [B]                       int32
+ *   centroids    [num_pages][Hkv][D]       float32
+ *   indices      [B][Hkv][top_k]           int32
+ *   scores       [B][Hkv][max_blocks_per_seq] float32
+ *   lse          [B][Hq]                   float32 (natural log)
+ */
+#ifndef BTK_H
+#define BTK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BTK_ABI_VERSION 1
+
+typedef enum {
+    BTK_OK = 0,
+    BTK_ERR_NULL = 1,        /* a required pointer is NULL */
+    BTK_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+    BTK_ERR_UNSUPPORTED = 3, /* valid, but not built: dtype, head_dim, page_size, limits */
+    BTK_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than btk_workspace_bytes() */
+    BTK_ERR_HIP = 5          /* the HIP runtime reported an error at launch */
+} btk_status_t;
+
+typedef enum { BTK_BF16 = 0, BTK_F32 = 1 } btk_dtype_t;
+
+/* Problem description (host struct, read during the call only).
+ * Supported: dtype BTK_BF16 or BTK_F32; head_dim 64 or 128; page_size 16;
+ * 1 <= r <= 16; max_blocks_per_seq <= 8192 (contexts up to 131072 tokens).
+ * sm_scale <= 0 selects 1/sqrt(head_dim); it scales both the block scores and
+ * the attention logits. */
+typedef struct {
+    int32_t batch;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t page_size;
+    int32_t num_pages;
+    int32_t max_blocks_per_seq;
+    int32_t dtype; /* btk_dtype_t */
+    float sm_scale;
+} btk_problem_t;
+
+/* Version of this ABI (BTK_ABI_VERSION of the built library). */
+int btk_abi_version(void);
+
+/* Human-readable name of a status code (static storage). */
+const char *btk_status_string(btk_status_t status);
+
+/* hipError_t code of the last BTK_ERR_HIP returned on this host thread. */
+int btk_last_hip_error(void);
+
+/* Bytes of device workspace that btk_select, btk_sparse_attend and
+ * btk_dense_attend need for this problem and top_k (host; no HIP call).
+ * Returns 0 if the problem is invalid.  The caller allocates it, ZERO-FILLS it
+ * once before its first use, and may then reuse it for any number of calls of
+ * the same or a smaller problem: each completed call leaves its internal
+ * counters at zero again.  Calls that may overlap in time (different streams)
+ * need separate workspaces. */
+size_t btk_workspace_bytes(const btk_problem_t *problem, int32_t top_k);
+
+/* S1 -- centroid update.  (Pith review, "What carries the argument": blocks are
+ * summarised by their averaged key vector.)
+ * For every block j of sequence b with j >= first_pos[b] / P (every block of
+ * every sequence when first_pos is NULL) and every KV head g:
+ *     centroids[page][g][:] = (sum of the block's valid keys, in fp32) / v_j,
+ * page = block_table[b][j], v_j = min(P, L_b - j*P).  Other pages are left
+ * untouched.  In decode, pass first_pos[b] = position of the token just
+ * appended (L_b - 1), so only the page holding it is recomputed.  A page shared
+ * by several sequences must hold the same number of valid tokens in each;
+ * rebuilding it from several sequences writes identical values.
+ *   k_cache    in   [num_pages][Hkv][P][D] dtype
+ *   first_pos  in   [B] int32 device pointer, or NULL
+ *   centroids  in/out [num_pages][Hkv][D] float32 */
+btk_status_t btk_centroid_update(const btk_problem_t *problem, const void *k_cache,
+                                 const int32_t *block_table, const int32_t *seq_lens,
+                                 const int32_t *first_pos, float *centroids, void *stream);
+
+/* S2 + S3 -- block scoring and top-k selection.  (Pith review, "What carries
+ * the argument": blocks are scored by their averaged keys per query group and
+ * the top k blocks are kept; top-k counted in pages: Kinetics README, "Benchmark
+ * Block TopK Attention throughput".)
+ * For unit (b, g) and block j < n_b, the group score is
+ *     s_j = sm_scale * qbar . centroids[block_table[b][j]][g],
+ *     qbar = mean of q[b][h] over the r query heads h of group g,
+ * computed in fp32 (equal to the mean of the heads' scaled logits up to
+ * rounding).  The k_b = min(top_k, n_b) blocks with the largest s_j are kept;
+ * equal scores go to the lower j (-0.0 equals +0.0).  indices[b][g][0..k_b) holds
+ * them in ascending j, and indices[b][g][k_b..top_k) = -1.  NaN scores give
+ * unspecified selections.
+ *   q        in   [B][Hq][D] dtype
+ *   top_k    1 .. 8192
+ *   indices  out  [B][Hkv][top_k] int32
+ *   scores   out  [B][Hkv][max_blocks_per_seq] float32, or NULL; entries
+ *                 j >= n_b are not written
+ *   workspace     btk_workspace_bytes(problem, top_k) bytes (see above) */
+btk_status_t btk_select(const btk_problem_t *problem, const void *q, const float *centroids,
+                        const int32_t *block_table, const int32_t *seq_lens, int32_t top_k,
+                        int32_t *indices, float *scores, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/* S4 -- exact softmax attention over the selected blocks.  (Pith review, "What
+ * carries the argument": attention runs over only the retrieved blocks.)
+ * For query head h of sequence b, g = h / r, the token set is every valid token
+ * of the blocks listed in indices[b][g][0..top_k) (entries < 0 are skipped; the
+ * list must name at least one block and no block twice).  With
+ * l_t = sm_scale * q[b][h] . K_t:
+ *     out[b][h] = sum_t softmax(l)_t V_t,   lse[b][h] = ln sum_t exp(l_t).
+ * Accumulation is fp32; out is rounded to dtype (bf16: nearest-even).
+ *   out  out [B][Hq][D] dtype;  lse out [B][Hq] float32, or NULL */
+btk_status_t btk_sparse_attend(const btk_problem_t *problem, const void *q, const void *k_cache,
+                               const void *v_cache, const int32_t *block_table,
+                               const int32_t *seq_lens, const int32_t *indices, int32_t top_k,
+                               void *out, float *lse, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/* S5 -- dense paged decode attention: the same computation as btk_sparse_attend
+ * over all n_b blocks of every sequence (the comparison path; Kinetics README,
+ * "Benchmark Block TopK Attention throughput", dense paged attention of one
+ * decoder layer). */
+btk_status_t btk_dense_attend(const btk_problem_t *problem, const void *q, const void *k_cache,
+                              const void *v_cache, const int32_t *block_table,
+                              const int32_t *seq_lens, void *out, float *lse, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BTK_H */

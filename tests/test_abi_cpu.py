@@ -1,0 +1,118 @@
+"""C-ABI checks that need no GPU: the library loads, exports what include/btk.h
+declares, and rejects bad arguments on the host before any HIP call.  Every
+call here is invalid on purpose, so none of them reaches the HIP runtime."""
+import ctypes
+
+import pytest
+
+import block_top_sparse_btk_amd as btk
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: each call below fails validation first
+
+
+def _problem(**kw):
+    base = dict(batch=4, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
+                num_pages=100, max_blocks_per_seq=20, dtype=btk.BTK_BF16, sm_scale=0.0)
+    base.update(kw)
+    return btk.btk_problem_t(*[base[f] for f, _ in btk.btk_problem_t._fields_])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = btk._lib()
+    names = btk.header_symbols()
+    assert {"btk_centroid_update", "btk_select", "btk_sparse_attend", "btk_dense_attend",
+            "btk_workspace_bytes"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+    assert lib.btk_abi_version() == 1
+
+
+def test_status_strings():
+    lib = btk._lib()
+    for s in range(6):
+        assert lib.btk_status_string(s)
+    assert lib.btk_status_string(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("kw,ok", [
+    ({}, True),
+    (dict(dtype=btk.BTK_F32, head_dim=64), True),
+    (dict(head_dim=96), False),
+    (dict(page_size=32), False),
+    (dict(num_q_heads=7), False),
+    (dict(num_q_heads=34, num_kv_heads=2), False),  # group of 17
+    (dict(max_blocks_per_seq=8193), False),
+    (dict(dtype=7), False),
+    (dict(batch=0), False),
+    (dict(num_pages=0), False),
+    (dict(sm_scale=float("nan")), False),
+])
+def test_workspace_bytes_validates_problem(kw, ok):
+    n = btk.btk_workspace_bytes(_problem(**kw), 16)
+    assert (n > 0) == ok
+
+
+def test_workspace_bytes_grows_with_problem_and_rejects_bad_top_k():
+    small = btk.btk_workspace_bytes(_problem(), 16)
+    big = btk.btk_workspace_bytes(_problem(batch=64, max_blocks_per_seq=2048), 16)
+    assert big > small > 0
+    assert btk.btk_workspace_bytes(_problem(), 0) == 0
+    assert btk.btk_workspace_bytes(_problem(), 8193) == 0
+    # the region for the scores scratch alone: B*Hkv*max_blocks floats
+    assert big >= 64 * 2 * 2048 * 4
+
+
+def test_null_problem_and_null_pointers():
+    lib = btk._lib()
+    assert lib.btk_centroid_update(None, FAKE, FAKE, FAKE, None, FAKE, None) == btk.BTK_ERR_NULL
+    p = ctypes.byref(_problem())
+    assert lib.btk_centroid_update(p, None, FAKE, FAKE, None, FAKE, None) == btk.BTK_ERR_NULL
+    assert lib.btk_centroid_update(p, FAKE, FAKE, FAKE, None, None, None) == btk.BTK_ERR_NULL
+    assert lib.btk_select(p, None, FAKE, FAKE, FAKE, 4, FAKE, None, FAKE, 1 << 30,
+                          None) == btk.BTK_ERR_NULL
+    assert lib.btk_select(p, FAKE, FAKE, FAKE, FAKE, 4, None, None, FAKE, 1 << 30,
+                          None) == btk.BTK_ERR_NULL
+    assert lib.btk_sparse_attend(p, FAKE, FAKE, FAKE, FAKE, FAKE, None, 4, FAKE, None, FAKE,
+                                 1 << 30, None) == btk.BTK_ERR_NULL
+    assert lib.btk_dense_attend(p, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, 1 << 30,
+                                None) == btk.BTK_ERR_NULL
+
+
+def test_unsupported_and_shape_errors_come_first():
+    lib = btk._lib()
+    bad = ctypes.byref(_problem(head_dim=96))
+    assert lib.btk_select(bad, FAKE, FAKE, FAKE, FAKE, 4, FAKE, None, FAKE, 1 << 30,
+                          None) == btk.BTK_ERR_UNSUPPORTED
+    bad = ctypes.byref(_problem(num_q_heads=9))
+    assert lib.btk_dense_attend(bad, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30,
+                                None) == btk.BTK_ERR_SHAPE
+    p = ctypes.byref(_problem())
+    assert lib.btk_select(p, FAKE, FAKE, FAKE, FAKE, 0, FAKE, None, FAKE, 1 << 30,
+                          None) == btk.BTK_ERR_SHAPE
+    assert lib.btk_sparse_attend(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -3, FAKE, None, FAKE,
+                                 1 << 30, None) == btk.BTK_ERR_SHAPE
+
+
+def test_workspace_too_small_is_rejected_before_launch():
+    lib = btk._lib()
+    prob = _problem()
+    need = btk.btk_workspace_bytes(prob, 8)
+    p = ctypes.byref(prob)
+    assert lib.btk_select(p, FAKE, FAKE, FAKE, FAKE, 8, FAKE, None, FAKE, need - 1,
+                          None) == btk.BTK_ERR_WORKSPACE
+    assert lib.btk_select(p, FAKE, FAKE, FAKE, FAKE, 8, FAKE, None, None, need,
+                          None) == btk.BTK_ERR_WORKSPACE
+    assert lib.btk_sparse_attend(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, None, FAKE,
+                                 need - 1, None) == btk.BTK_ERR_WORKSPACE
+    dense_need = btk.btk_workspace_bytes(prob, 1)
+    assert lib.btk_dense_attend(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                dense_need - 1, None) == btk.BTK_ERR_WORKSPACE
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    q = torch.zeros(1, 2, 64)
+    with pytest.raises(ValueError):
+        btk.btk_dense_attend(q, torch.zeros(4, 1, 16, 64), torch.zeros(4, 1, 64, 16),
+                             torch.zeros(1, 4, dtype=torch.int32), torch.ones(1, dtype=torch.int32),
+                             torch.zeros(10, dtype=torch.uint8))

@@ -1,0 +1,296 @@
+"""Parity of the HIP library (through the C ABI) with the CPU oracle, on the GPU.
+
+Every input comes from ``synth`` (seeded, CPU) and is copied to the device, so
+both sides read identical bytes.  Expected values come only from ``oracle``.
+Covered: edge shapes (single token, partial last blocks, k >= n_b, k = 1,
+group sizes 1..16, head_dim 64/128, bf16/fp32, identity/shuffled/shared page
+tables, block lists with -1 padding), the five decode workloads at full size in
+the launch configuration the benchmark times, the decode-mode centroid update,
+determinism, page relabelling, and the kernels' device-side input guards.
+"""
+import math
+
+import pytest
+import torch
+
+import block_top_sparse_btk_amd as btk
+import oracle
+import synth
+from parity import (CENTROID_TOL, SCORE_TOL, check_indices, check_lse, check_outputs, max_abs,
+                    n_blocks)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _gpu_step(bt, dev=DEV, top_k=None, dense=True):
+    """All library calls on one batch; returns CPU copies of everything."""
+    top_k = top_k or bt.top_k
+    d = bt.to(dev)
+    prob = btk.make_problem(d.q, d.k_cache, d.block_table)
+    ws = btk.new_workspace(prob, top_k, dev)
+    cent = torch.zeros((bt.num_pages, bt.num_kv_heads, bt.head_dim), dtype=torch.float32, device=dev)
+    btk.btk_centroid_update(d.k_cache, d.block_table, d.seq_lens, cent, problem=prob)
+    scores = torch.full((bt.batch, bt.num_kv_heads, bt.max_blocks), float("nan"), device=dev)
+    idx = btk.btk_select(d.q, cent, d.block_table, d.seq_lens, top_k, ws, scores=scores,
+                         problem=prob)
+    out = torch.empty_like(d.q)
+    lse = torch.empty((bt.batch, bt.num_q_heads), dtype=torch.float32, device=dev)
+    btk.btk_sparse_attend(d.q, d.k_cache, d.v_cache, d.block_table, d.seq_lens, idx, ws, out=out,
+                          lse=lse, problem=prob)
+    res = dict(centroids=cent, scores=scores, indices=idx, out=out, lse=lse)
+    if dense:
+        dout = torch.empty_like(d.q)
+        dlse = torch.empty_like(lse)
+        btk.btk_dense_attend(d.q, d.k_cache, d.v_cache, d.block_table, d.seq_lens, ws, out=dout,
+                             lse=dlse, problem=prob)
+        res.update(dense_out=dout, dense_lse=dlse)
+    torch.cuda.synchronize()
+    res = {k: v.cpu() for k, v in res.items()}
+    res["err_bits"] = btk.workspace_error_bits(ws)
+    res["_dev"] = (d, prob, ws)
+    return res
+
+
+def _attend_on(bt_dev, prob, ws, indices_cpu, dev=DEV):
+    out = torch.empty_like(bt_dev.q)
+    lse = torch.empty((bt_dev.batch, bt_dev.num_q_heads), dtype=torch.float32, device=dev)
+    btk.btk_sparse_attend(bt_dev.q, bt_dev.k_cache, bt_dev.v_cache, bt_dev.block_table,
+                          bt_dev.seq_lens, indices_cpu.to(dev), ws, out=out, lse=lse, problem=prob)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+def full_parity(bt, top_k=None, dense=True, label=""):
+    top_k = top_k or bt.top_k
+    _say(f"[parity] {label} {bt.name} B={bt.batch} Hq={bt.num_q_heads} Hkv={bt.num_kv_heads} "
+         f"D={bt.head_dim} {bt.dtype} k={top_k} lens[:4]={bt.seq_lens[:4].tolist()} "
+         f"table={bt.notes.get('table')}")
+    g = _gpu_step(bt, top_k=top_k, dense=dense)
+    ora = oracle.sparse_step(bt.q, bt.k_cache, bt.v_cache, bt.block_table, bt.seq_lens, top_k)
+    assert g["err_bits"] == 0
+    # S1 centroids (both start from zeros; untouched pages stay zero on both sides)
+    c_err = max_abs(g["centroids"], ora["centroids"])
+    assert c_err <= CENTROID_TOL, c_err
+    # S2 scores on valid blocks
+    nbs = n_blocks(bt.seq_lens)
+    s_err = 0.0
+    for b, nb in enumerate(nbs):
+        s_err = max(s_err, max_abs(g["scores"][b, :, :nb], ora["scores"][b, :, :nb]))
+    assert s_err <= SCORE_TOL, s_err
+    # S3 selection under the margin rule
+    st = check_indices(g["indices"], ora["indices"], ora["scores"], bt.seq_lens, top_k)
+    # S4 end to end on units whose selections agree
+    o_err = check_outputs(g["out"], ora["out"], bt.dtype, st["equal_mask"], bt.group)
+    l_err = check_lse(g["lse"], ora["lse"], bt.dtype, st["equal_mask"], bt.group)
+    # S4 alone, fed the oracle's selection, on every unit
+    d, prob, ws = g["_dev"]
+    a_out, a_lse = _attend_on(d, prob, ws, ora["indices"])
+    a_err = check_outputs(a_out, ora["out"], bt.dtype, what="attend(oracle idx)")
+    check_lse(a_lse, ora["lse"], bt.dtype)
+    res = dict(centroid=c_err, score=s_err, out=o_err, lse=l_err, attend=a_err,
+               units=st["units"], near_tie=st["near_tie"], differ=st["differ"],
+               min_strict_margin=st["min_strict_margin"])
+    if dense:
+        dout, dlse, _ = oracle.attend(bt.q, bt.k_cache, bt.v_cache, bt.block_table, bt.seq_lens)
+        res["dense_out"] = check_outputs(g["dense_out"], dout, bt.dtype, what="dense out")
+        res["dense_lse"] = check_lse(g["dense_lse"], dlse, bt.dtype)
+    assert btk.workspace_error_bits(ws) == 0
+    _say(f"[parity]   ok {res}")
+    return res
+
+
+# ------------------------------------------------------------------ edge shapes
+
+EDGE = [
+    # (label, kwargs for synth.make_batch)
+    ("single-token", dict(batch=3, num_q_heads=4, num_kv_heads=2, head_dim=128, seq_lens=[1, 1, 1],
+                          top_k=4)),
+    ("page-edges", dict(batch=6, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                        seq_lens=[15, 16, 17, 31, 32, 33], top_k=1)),
+    ("k-exceeds-blocks", dict(batch=3, num_q_heads=8, num_kv_heads=4, head_dim=128,
+                              seq_lens=[40, 200, 16], top_k=20)),
+    ("ragged-tail-many-chunks", dict(batch=5, num_q_heads=8, num_kv_heads=1, head_dim=128,
+                                     seq_lens=[4097, 9000, 12345, 70, 2049], top_k=33)),
+    ("group-1", dict(batch=4, num_q_heads=4, num_kv_heads=4, head_dim=128,
+                     seq_lens=[500, 777, 1024, 3], top_k=7)),
+    ("group-16", dict(batch=2, num_q_heads=32, num_kv_heads=2, head_dim=128, seq_lens=[1500, 999],
+                      top_k=12)),
+    ("d64-bf16", dict(batch=4, num_q_heads=8, num_kv_heads=2, head_dim=64, seq_lens=[300, 1, 1025, 64],
+                      top_k=5)),
+    ("d128-fp32", dict(batch=3, num_q_heads=6, num_kv_heads=2, head_dim=128, seq_lens=[333, 48, 1000],
+                       top_k=6, dtype=torch.float32)),
+    ("d64-fp32-heavy", dict(batch=3, num_q_heads=4, num_kv_heads=1, head_dim=64,
+                            seq_lens=[2000, 100, 513], top_k=9, dtype=torch.float32, heavy_frac=0.1)),
+    ("shared-prefix", dict(batch=4, num_q_heads=8, num_kv_heads=1, head_dim=128,
+                           seq_lens=[300, 290, 512, 257], top_k=10, table="shared", shared_prefix=256)),
+    ("identity-table", dict(batch=3, num_q_heads=4, num_kv_heads=2, head_dim=128,
+                            seq_lens=[1000, 1001, 1002], top_k=16, table="identity")),
+    ("long-8k-blocks", dict(batch=1, num_q_heads=2, num_kv_heads=1, head_dim=128, seq_lens=[131072],
+                            top_k=64, spare_pages=3, max_blocks=8192)),
+]
+
+
+@pytest.mark.parametrize("label,kw", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_shapes(label, kw):
+    kw = dict(kw)
+    kw.setdefault("dtype", torch.bfloat16)
+    kw.setdefault("seed", 100 + len(label))
+    bt = synth.make_batch(name=label, **kw)
+    full_parity(bt, label=label)
+
+
+# ------------------------------------------------------------------ the five workloads
+
+_CACHE = {}
+
+
+def _workload(cfg, context=None):
+    key = (cfg, context)
+    if key not in _CACHE:
+        _CACHE.clear()  # keep host memory bounded: one workload at a time
+        _CACHE[key] = synth.make_config(cfg, context=context)
+    return _CACHE[key]
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_workload_parity(cfg):
+    bt = _workload(cfg)
+    full_parity(bt, label=f"config {cfg}")
+
+
+@pytest.mark.parametrize("context", synth.SWEEP_LENS)
+def test_long_generation_sweep_parity(context):
+    bt = _workload(5, context)
+    full_parity(bt, label=f"config 5 @ {context}")
+
+
+def test_tiny_workload_variants():
+    # shuffled table, and k = all 64 blocks (sparse must then equal dense)
+    bt = synth.make_config(1, variant=1, table="shuffled")
+    full_parity(bt, label="config 1 shuffled")
+    bt = synth.make_config(1, variant=2, top_k=64)
+    g = _gpu_step(bt, top_k=64)
+    assert (g["indices"][0, 0] == torch.arange(64, dtype=torch.int32)).all()
+    assert max_abs(g["out"], g["dense_out"]) <= 1e-5
+    assert max_abs(g["lse"], g["dense_lse"]) <= 1e-5
+
+
+# ------------------------------------------------------------------ decode-mode S1
+
+def test_centroid_update_touched_pages_only():
+    bt = synth.make_config(3, batch=8)
+    d = bt.to(DEV)
+    prob = btk.make_problem(d.q, d.k_cache, d.block_table)
+    full = oracle.centroids(bt.k_cache, bt.block_table, bt.seq_lens)
+    first = (bt.seq_lens - 1).to(torch.int32)
+    cent = full.clone()
+    P = bt.page_size
+    touched = set()
+    for b in range(bt.batch):
+        page = int(bt.block_table[b, (int(bt.seq_lens[b]) - 1) // P])
+        cent[page] = float("nan")  # stale: must be recomputed
+        touched.add(page)
+    cent_d = cent.to(DEV)
+    btk.btk_centroid_update(d.k_cache, d.block_table, d.seq_lens, cent_d, first_pos=first.to(DEV),
+                            problem=prob)
+    torch.cuda.synchronize()
+    got = cent_d.cpu()
+    assert torch.isfinite(got).all()
+    assert max_abs(got, full) <= CENTROID_TOL
+    untouched = [p for p in range(bt.num_pages) if p not in touched]
+    assert torch.equal(got[untouched], full[untouched])
+
+
+# ------------------------------------------------------------------ determinism, paging
+
+def test_bitwise_determinism_and_page_relabelling():
+    bt = synth.make_config(3, batch=6)
+    a = _gpu_step(bt)
+    b = _gpu_step(bt)
+    for k in ("centroids", "indices", "out", "lse", "dense_out", "dense_lse"):
+        assert torch.equal(a[k], b[k]), k
+    # renumber the physical pages: logical results must not change at all
+    gen = torch.Generator().manual_seed(9)
+    perm = torch.randperm(bt.num_pages, generator=gen)
+    bt2 = synth.Batch(**{**bt.__dict__})
+    bt2.k_cache = torch.empty_like(bt.k_cache)
+    bt2.v_cache = torch.empty_like(bt.v_cache)
+    bt2.k_cache[perm] = bt.k_cache
+    bt2.v_cache[perm] = bt.v_cache
+    bt2.block_table = perm[bt.block_table.long()].to(torch.int32)
+    c = _gpu_step(bt2)
+    for k in ("indices", "out", "lse", "dense_out", "dense_lse"):
+        assert torch.equal(a[k], c[k]), k
+    assert torch.equal(c["centroids"][perm], a["centroids"])
+
+
+def test_workspace_reuse_across_calls_and_smaller_problem():
+    big = synth.make_config(2, batch=16)
+    small = synth.make_batch(batch=3, num_q_heads=16, num_kv_heads=8, head_dim=128,
+                             seq_lens=[700, 20, 4000], top_k=16, seed=77)
+    d = big.to(DEV)
+    prob = btk.make_problem(d.q, d.k_cache, d.block_table)
+    ws = btk.new_workspace(prob, 16, DEV)
+    cent = torch.zeros((big.num_pages, 8, 128), device=DEV)
+    btk.btk_centroid_update(d.k_cache, d.block_table, d.seq_lens, cent, problem=prob)
+    for _ in range(3):
+        idx = btk.btk_select(d.q, cent, d.block_table, d.seq_lens, 16, ws, problem=prob)
+        out = btk.btk_sparse_attend(d.q, d.k_cache, d.v_cache, d.block_table, d.seq_lens, idx, ws,
+                                    problem=prob)
+    torch.cuda.synchronize()
+    ora = oracle.sparse_step(big.q, big.k_cache, big.v_cache, big.block_table, big.seq_lens, 16)
+    st = check_indices(idx.cpu(), ora["indices"], ora["scores"], big.seq_lens, 16)
+    check_outputs(out, ora["out"], torch.bfloat16, st["equal_mask"], big.group)
+    # the same workspace serves a smaller problem
+    s = small.to(DEV)
+    sp = btk.make_problem(s.q, s.k_cache, s.block_table)
+    assert btk.btk_workspace_bytes(sp, 16) <= ws.numel()
+    scent = torch.zeros((small.num_pages, 8, 128), device=DEV)
+    btk.btk_centroid_update(s.k_cache, s.block_table, s.seq_lens, scent, problem=sp)
+    idx = btk.btk_select(s.q, scent, s.block_table, s.seq_lens, 16, ws, problem=sp)
+    out = btk.btk_sparse_attend(s.q, s.k_cache, s.v_cache, s.block_table, s.seq_lens, idx, ws,
+                                problem=sp)
+    torch.cuda.synchronize()
+    ora = oracle.sparse_step(small.q, small.k_cache, small.v_cache, small.block_table,
+                             small.seq_lens, 16)
+    st = check_indices(idx.cpu(), ora["indices"], ora["scores"], small.seq_lens, 16)
+    check_outputs(out, ora["out"], torch.bfloat16, st["equal_mask"], small.group)
+    assert btk.workspace_error_bits(ws) == 0
+
+
+# ------------------------------------------------------------------ device-side guards
+
+def test_out_of_range_device_inputs_are_flagged_not_read():
+    bt = synth.make_batch(batch=3, num_q_heads=4, num_kv_heads=2, head_dim=128,
+                          seq_lens=[100, 50, 30], top_k=3, seed=5)
+    d = bt.to(DEV)
+    prob = btk.make_problem(d.q, d.k_cache, d.block_table)
+    cent = torch.zeros((bt.num_pages, 2, 128), device=DEV)
+    btk.btk_centroid_update(d.k_cache, d.block_table, d.seq_lens, cent, problem=prob)
+    # a page id past the pool: skipped by every kernel, flagged by select/attend
+    bad_bt = d.block_table.clone()
+    bad_bt[0, 1] = bt.num_pages + 1000
+    ws = btk.new_workspace(prob, 3, DEV)
+    btk.btk_select(d.q, cent, bad_bt, d.seq_lens, 3, ws, problem=prob)
+    torch.cuda.synchronize()
+    assert btk.workspace_error_bits(ws) & 2
+    # an index past the sequence's blocks
+    ws = btk.new_workspace(prob, 3, DEV)
+    idx = torch.tensor([[[0, 1, 99]] * 2, [[0, 1, 2]] * 2, [[0, 1, -1]] * 2], dtype=torch.int32,
+                       device=DEV)
+    btk.btk_sparse_attend(d.q, d.k_cache, d.v_cache, d.block_table, d.seq_lens, idx, ws,
+                          problem=prob)
+    torch.cuda.synchronize()
+    assert btk.workspace_error_bits(ws) & 4
+    # a length beyond the table
+    ws = btk.new_workspace(prob, 3, DEV)
+    bad_len = d.seq_lens.clone()
+    bad_len[2] = bt.max_blocks * 16 + 1
+    btk.btk_dense_attend(d.q, d.k_cache, d.v_cache, d.block_table, bad_len, ws, problem=prob)
+    torch.cuda.synchronize()
+    assert btk.workspace_error_bits(ws) & 1
