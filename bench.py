@@ -1,0 +1,351 @@
+"""Benchmark: block top-k sparse decode attention on one MI355X.
+
+A step is one decode step of the method over the whole batch, all on one HIP
+stream: S1 centroid update of the page holding each sequence's newest token,
+S2+S3 group scoring and top-k selection, S4 attention over the selected blocks.
+The KV append itself is the caller's op and is not timed; lengths stay fixed
+so every step is the same work.  The workload is the Qwen3-8B-shaped decode
+layer (B=32, Hq=32, Hkv=8, D=128, bf16, ragged contexts U[4096, 32768], shuffled
+16-token pages, top-k = 32 blocks), drawn by ``synth`` with seed 3000.
+
+Inputs are resident in HBM before timing starts.  The step rotates over
+``--replicas`` independent copies of the KV cache, centroids and tables so that
+consecutive steps touch different memory: a sparse step's working set (about
+220 MB) would otherwise stay in the 256 MB last-level cache between steps,
+which a real model, with its other layers in between, never sees.
+
+Prints one JSON line.  ``value`` is query-tokens/s = B / step time.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
+METRIC = "sparse decode attention query-tokens/s + achieved HBM GB/s (% of peak), vs dense"
+WORKLOAD = ("qwen3-8b-shaped decode layer: B=32, Hq=32, Hkv=8 (group 4), D=128, bf16, "
+            "contexts U[4096,32768], 16-token pages, shuffled block table, top_k=32 blocks")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "select_kernel_qwen3-8b_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "block_top_sparse_btk_amd", "csrc", f)
+                  for f in ("select.hip", "btk_internal.h")]
+
+
+# ---------------------------------------------------------------- byte model
+
+def dense_kv_bytes_per_token(num_kv_heads: int, head_dim: int, elem_bytes: int) -> int:
+    """K and V bytes one cached token costs one layer's dense decode attention."""
+    return 2 * num_kv_heads * head_dim * elem_bytes
+
+
+def selected_tokens(indices, seq_lens, page=16):
+    """Valid tokens of the selected blocks, per (sequence, KV head) unit."""
+    out = []
+    for b, L in enumerate([int(x) for x in seq_lens]):
+        row = []
+        for g in range(indices.shape[1]):
+            js = [j for j in indices[b, g].tolist() if j >= 0]
+            row.append(sum(min(page, L - j * page) for j in js))
+        out.append(row)
+    return out
+
+
+def algorithmic_bytes(seq_lens, num_q_heads, num_kv_heads, head_dim, top_k, elem_bytes,
+                      page=16, sel_tokens=None):
+    """Bytes each kernel of a step must move (reads + writes), by the method's definition.
+
+    Per unit (sequence b, KV head g), r = Hq/Hkv, e = element bytes, n_b blocks:
+      S1 centroid:  the newest token's page keys (v_last*D*e) + one centroid (4*D)
+      S2+S3 select: group queries (r*D*e) + n_b centroids (4*D*n_b) + k indices (4*k),
+                    and the sequence's block table (4*n_b) once per sequence
+      S4 attend:    k indices + their block-table entries (8*k), queries (r*D*e),
+                    K and V of the selected blocks' valid tokens (2*v_j*D*e), out (r*D*e)
+      dense:        table (4*n_b per sequence) + q and out (2*r*D*e) + all K,V (2*L*D*e)
+    """
+    r, D, e, P = num_q_heads // num_kv_heads, head_dim, elem_bytes, page
+    cen = sel = att = dense = 0
+    for b, L in enumerate([int(x) for x in seq_lens]):
+        nb = (L + P - 1) // P
+        kb = min(top_k, nb)
+        v_last = L - (nb - 1) * P
+        sel += 4 * nb
+        dense += 4 * nb
+        for g in range(num_kv_heads):
+            # valid tokens of the selected blocks: exact when the selection is
+            # given, else every selected block full (or all of L when k >= n_b)
+            toks = sel_tokens[b][g] if sel_tokens is not None else (L if kb == nb else kb * P)
+            cen += v_last * D * e + 4 * D
+            sel += r * D * e + 4 * D * nb + 4 * top_k
+            att += 8 * top_k + 2 * r * D * e + 2 * toks * D * e
+            dense += 2 * r * D * e + 2 * L * D * e
+    return {"centroid": cen, "select": sel, "attend": att, "step": cen + sel + att,
+            "dense": dense}
+
+
+# ---------------------------------------------------------------- helpers
+
+def _sources_digest() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _measured_traffic():
+    """HBM bytes per select launch from the committed rocprofv3 counter runs,
+    or None if the kernel source changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != _sources_digest():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def _cpu_baseline(bt, seconds: float):
+    """The oracle's sparse step on the host cores, time-bounded."""
+    import torch
+    import oracle
+
+    first = (bt.seq_lens - 1).to(torch.int32)
+    cents = oracle.centroids(bt.k_cache, bt.block_table, bt.seq_lens)
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.sparse_step(bt.q, bt.k_cache, bt.v_cache, bt.block_table, bt.seq_lens, bt.top_k,
+                           cents=cents, first_pos=first)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds and steps >= 2:
+            break
+    per_step = el / steps
+    return {"value": bt.batch / per_step, "unit": "query-tokens/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"{steps} full sparse decode steps of the same batch (S1 newest-token pages, "
+                      f"scores, top-k, attention), {el:.1f} s of CPU time on "
+                      f"{oracle.max_threads()} threads"}
+
+
+# ---------------------------------------------------------------- main
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--replicas", type=int, default=6)
+    ap.add_argument("--dense-steps", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="skip the HIP-graph replay measurement")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after timing, run plain 1 GiB device copies (counter calibration)")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+
+    import block_top_sparse_btk_amd as btk
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bt = synth.make_config(3)
+    B, hq, hkv, D, k = bt.batch, bt.num_q_heads, bt.num_kv_heads, bt.head_dim, bt.top_k
+    e = 2
+    nbytes = algorithmic_bytes(bt.seq_lens.tolist(), hq, hkv, D, k, e)
+
+    # replicas: independent device copies of everything a step reads or writes
+    reps = []
+    base = bt.to(dev)
+    prob = btk.make_problem(base.q, base.k_cache, base.block_table)
+    first = (base.seq_lens - 1).to(torch.int32)
+    for i in range(args.replicas):
+        d = base if i == 0 else bt.to(dev)
+        cent = torch.zeros((bt.num_pages, hkv, D), dtype=torch.float32, device=dev)
+        btk.btk_centroid_update(d.k_cache, d.block_table, d.seq_lens, cent, problem=prob)
+        reps.append(dict(d=d, cent=cent, ws=btk.new_workspace(prob, k, dev),
+                         idx=torch.empty((B, hkv, k), dtype=torch.int32, device=dev),
+                         out=torch.empty_like(d.q), first=first.clone()))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    lib = btk._lib()
+    hs = stream.cuda_stream
+
+    # Lean dispatch: the C entry points with prebuilt argument tuples, so host
+    # overhead stays far below the GPU time of a step (the binding's per-call
+    # shape checks were done when the replicas were built).
+    def calls(rep):
+        d = rep["d"]
+        P = ctypes.byref(prob)
+        p = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        ws, wsn = p(rep["ws"]), rep["ws"].numel()
+        return ((P, p(d.k_cache), p(d.block_table), p(d.seq_lens), p(rep["first"]),
+                 p(rep["cent"]), hs),
+                (P, p(d.q), p(rep["cent"]), p(d.block_table), p(d.seq_lens), k, p(rep["idx"]),
+                 None, ws, wsn, hs),
+                (P, p(d.q), p(d.k_cache), p(d.v_cache), p(d.block_table), p(d.seq_lens),
+                 p(rep["idx"]), k, p(rep["out"]), None, ws, wsn, hs),
+                (P, p(d.q), p(d.k_cache), p(d.v_cache), p(d.block_table), p(d.seq_lens),
+                 p(rep["dout"]), None, ws, wsn, hs))
+
+    for rep in reps:
+        rep["dout"] = torch.empty_like(rep["d"].q)
+        rep["calls"] = calls(rep)
+    f_cen, f_sel, f_att, f_den = (lib.btk_centroid_update, lib.btk_select, lib.btk_sparse_attend,
+                                  lib.btk_dense_attend)
+
+    def step(rep, ev=None):
+        c = rep["calls"]
+        st = f_cen(*c[0])
+        if ev is not None:
+            ev[0].record(stream)
+        st |= f_sel(*c[1])
+        if ev is not None:
+            ev[1].record(stream)
+        st |= f_att(*c[2])
+        if st:
+            raise RuntimeError("library call failed")
+
+    for i in range(args.warmup):
+        step(reps[i % len(reps)])
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, bracketed by synchronize; HIP events on the
+    # library's stream bracket every select launch (the dominant kernel)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(reps[i % len(reps)], evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1e3 * wall / args.steps
+    sel_us = 1e3 * sum(a.elapsed_time(b) for a, b in evs) / args.steps
+
+    # per-kernel breakdown (separate pass, events between every launch)
+    kev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        c, ev = reps[i % len(reps)]["calls"], kev[i]
+        ev[0].record(stream)
+        f_cen(*c[0])
+        ev[1].record(stream)
+        f_sel(*c[1])
+        ev[2].record(stream)
+        f_att(*c[2])
+        ev[3].record(stream)
+    torch.cuda.synchronize()
+    kern = {name: 1e3 * sum(ev[j].elapsed_time(ev[j + 1]) for ev in kev) / args.steps
+            for j, name in enumerate(("centroid", "select", "attend"))}
+
+    # the same step replayed from HIP graphs (one captured step per replica)
+    graph_ms = None
+    if args.graph:
+        graphs = []
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for rep in reps:  # capture on a side stream; the calls name it explicitly
+                c = rep["calls"]
+                gc = [tuple(x if x is not hs else side.cuda_stream for x in cc) for cc in c]
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    f_cen(*gc[0])
+                    f_sel(*gc[1])
+                    f_att(*gc[2])
+                graphs.append(g)
+        stream.wait_stream(side)
+        for i in range(args.warmup):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        graph_ms = 1e3 * (time.perf_counter() - t0) / args.steps
+
+    # dense comparison on the same inputs
+    for i in range(3):
+        f_den(*reps[i % len(reps)]["calls"][3])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.dense_steps):
+        f_den(*reps[i % len(reps)]["calls"][3])
+    torch.cuda.synchronize()
+    dense_ms = 1e3 * (time.perf_counter() - t0) / args.dense_steps
+    for r in reps:
+        if btk.workspace_error_bits(r["ws"]):
+            raise RuntimeError("device-side input guard fired during the benchmark")
+
+    if args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    # exact S4 bytes from the blocks actually selected (every replica selects the same)
+    nbytes = algorithmic_bytes(bt.seq_lens.tolist(), hq, hkv, D, k, e,
+                               sel_tokens=selected_tokens(reps[0]["idx"].cpu(), bt.seq_lens))
+    step_gbps = nbytes["step"] / (ms_per_step * 1e-3) / 1e9
+    sel_gbps = nbytes["select"] / (sel_us * 1e-6) / 1e9
+    dense_gbps = nbytes["dense"] / (dense_ms * 1e-3) / 1e9
+    value = B / (ms_per_step * 1e-3)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded Qwen3-8B-shaped decode batch (no dataset or weights)",
+        "config": {"workload": WORKLOAD, "batch": B, "num_q_heads": hq, "num_kv_heads": hkv,
+                   "head_dim": D, "page_size": 16, "top_k": k, "seed": bt.seed,
+                   "mean_context": round(float(bt.seq_lens.float().mean()), 1),
+                   "replicas": args.replicas},
+        "step_gbps": round(step_gbps, 1),
+        "step_frac_of_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
+        "bytes_per_step": nbytes["step"],
+        "bytes_per_token": round(nbytes["step"] / B, 1),
+        "kernels_us": {kk: round(v, 2) for kk, v in kern.items()},
+        "roofline": {"bound": "hbm", "kernel": "select (S2+S3 centroid scan + top-k)",
+                     "achieved": round(sel_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(sel_gbps / HBM_PEAK_GBPS, 4), "traffic": _measured_traffic(),
+                     "algorithmic_bytes_per_launch": nbytes["select"],
+                     "avg_launch_us": round(sel_us, 3)},
+        "dense": {"value": round(B / (dense_ms * 1e-3), 1), "unit": "query-tokens/s",
+                  "ms_per_step": round(dense_ms, 4), "gbps": round(dense_gbps, 1),
+                  "frac_of_peak": round(dense_gbps / HBM_PEAK_GBPS, 4),
+                  "bytes_per_step": nbytes["dense"],
+                  "bytes_per_token": round(nbytes["dense"] / B, 1)},
+        "speedup_vs_dense": round(dense_ms / ms_per_step, 2),
+        "graph_replay": None if graph_ms is None else {
+            "ms_per_step": round(graph_ms, 5), "value": round(B / (graph_ms * 1e-3), 1),
+            "step_gbps": round(nbytes["step"] / (graph_ms * 1e-3) / 1e9, 1)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = _cpu_baseline(bt, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

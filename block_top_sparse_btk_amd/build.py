@@ -9,9 +9,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 SOURCES = ["api.hip", "centroid.hip", "select.hip", "attend.hip"]
 LIB = os.path.join(HERE, "libbtk.so")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE,
     "-Wno-unused-parameter",
     # hipcc -O3 forms packed fp32 instructions from scalar float code by itself;
     # keep them out of every kernel.

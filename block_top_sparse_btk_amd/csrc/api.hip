@@ -3,7 +3,7 @@
 // has no side effects and the checks run on machines without a GPU.
 #include <math.h>
 
-#include "../../include/btk.h"
+#include "btk.h"
 #include "btk_internal.h"
 
 namespace {

@@ -23,7 +23,7 @@
 // normaliser and the log-sum-exp sum the unrounded weights.  Blocks are double-buffered:
 // the loads of the next group are in flight while the current one is computed.
 // Waves merge through LDS; splits merge through the workspace in the
-// workgroup that finishes last (release/acquire counter per unit).
+// workgroup that finishes last (a counter per unit, see arrive_last).
 #include "btk_internal.h"
 
 namespace btk {
@@ -222,6 +222,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
     const int cnt = max(0, min(i1, w0 + per_wave) - w0);
 
     // lane m < cnt holds page id and valid tokens of this wave's m-th entry
+    // (page -1 and 0 tokens for a skipped or invalid entry)
     int my_page = -1, my_v = 0;
     if (lane < cnt) {
         int j = DENSE ? (w0 + lane) : a.indices[(size_t)unit * a.top_k + w0 + lane];
@@ -256,49 +257,42 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
         typename F::KFrag k[kG];
         typename F::VFrag v[kG];
     };
+    // Loads and their consumers are unconditional, so the compiler can keep
+    // the next stage in flight (precise vmcnt) while the current one computes:
+    // a slot past the wave's list re-reads its last entry (a cache hit) and an
+    // invalid entry reads page 0; both are masked to zero weight below.
+    const int safe_page = my_page >= 0 ? my_page : 0;
     auto issue = [&](Stage &s, int m0) {
 #pragma unroll
         for (int u = 0; u < kG; ++u) {
-            const int m = m0 + u;
-            if (m < cnt) {
-                const int page = __builtin_amdgcn_readlane(my_page, m);
-                if (page >= 0) {
-                    F::load_k(s.k[u], kbase + page * page_stride, lane);
-                    F::load_v(s.v[u], vbase + page * page_stride, lane);
-                }
-            }
+            const int m = min(m0 + u, cnt - 1);
+            const int page = __builtin_amdgcn_readlane(safe_page, m);
+            F::load_k(s.k[u], kbase + page * page_stride, lane);
+            F::load_v(s.v[u], vbase + page * page_stride, lane);
         }
     };
     auto compute = [&](Stage &s, int m0) {
-        bool any = false;  // wave-uniform: page ids and counts come from readlane
-#pragma unroll
-        for (int u = 0; u < kG; ++u)
-            any |= (m0 + u < cnt) && __builtin_amdgcn_readlane(my_page, m0 + u) >= 0;
-        if (!any) return;
         float sv[kG][4];
+        int vv[kG];
         float gmax = -INFINITY;
 #pragma unroll
         for (int u = 0; u < kG; ++u) {
-            const int m = m0 + u;
-            const int page = m < cnt ? __builtin_amdgcn_readlane(my_page, m) : -1;
-            const int v = m < cnt ? __builtin_amdgcn_readlane(my_v, m) : 0;
-            if (page >= 0) {
-                const floatx4_t acc = F::qk(s.k[u], qf);
+            const int m = min(m0 + u, cnt - 1);
+            // valid tokens of this slot, 0 for a repeated or invalid entry (wave-uniform)
+            vv[u] = m0 + u < cnt ? __builtin_amdgcn_readlane(my_v, m) : 0;
+            const floatx4_t acc = F::qk(s.k[u], qf);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = 4 * (lane >> 4) + e;
-                    sv[u][e] = t < v ? acc[e] * a.scale_log2 : -INFINITY;
-                    gmax = fmaxf(gmax, sv[u][e]);
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sv[u][e] = -INFINITY;
+            for (int e = 0; e < 4; ++e) {
+                const int t = 4 * (lane >> 4) + e;
+                sv[u][e] = t < vv[u] ? acc[e] * a.scale_log2 : -INFINITY;
+                gmax = fmaxf(gmax, sv[u][e]);
             }
         }
         gmax = fmaxf(gmax, __shfl_xor(gmax, 16));
         gmax = fmaxf(gmax, __shfl_xor(gmax, 32));
-        const float m_new = fmaxf(m_run, gmax);  // finite: the group has a valid token
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
+        const float m_new = fmaxf(m_run, gmax);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;  // nothing valid yet: keep zeros
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // 0 when m_run = -inf
         z_run *= alpha;
         // O rows are heads 4*(l/16)+e; alpha of head h lives in lane h
 #pragma unroll
@@ -310,33 +304,30 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
         m_run = m_new;
 #pragma unroll
         for (int u = 0; u < kG; ++u) {
-            const int m = m0 + u;
-            const int page = m < cnt ? __builtin_amdgcn_readlane(my_page, m) : -1;
-            const int v = m < cnt ? __builtin_amdgcn_readlane(my_v, m) : 0;
-            if (page >= 0) {
-                float p[4];
+            float p[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float pe = __builtin_amdgcn_exp2f(sv[u][e] - m_new);
-                    z_run += pe;  // the normaliser (and lse) use the unrounded weights
-                    p[e] = F::round_p(pe);
-                }
-                if (v < kPage) F::mask_v(s.v[u], v, lane);
-                F::pv(o, p, s.v[u]);
+            for (int e = 0; e < 4; ++e) {
+                const float pe = __builtin_amdgcn_exp2f(sv[u][e] - m_use);  // 0 for masked tokens
+                z_run += pe;  // the normaliser (and lse) use the unrounded weights
+                p[e] = F::round_p(pe);
             }
+            if (vv[u] < kPage) F::mask_v(s.v[u], vv[u], lane);  // no 0 * garbage in P.V
+            F::pv(o, p, s.v[u]);
         }
     };
 
-    Stage sa, sb;
     if (cnt > 0) {
+        Stage sa, sb;
         issue(sa, 0);
-        for (int m0 = 0;; m0 += 2 * kG) {
-            if (m0 + kG < cnt) issue(sb, m0 + kG);
+        for (int m0 = 0;;) {
+            issue(sb, m0 + kG);
             compute(sa, m0);
-            if (m0 + kG >= cnt) break;
-            if (m0 + 2 * kG < cnt) issue(sa, m0 + 2 * kG);
-            compute(sb, m0 + kG);
-            if (m0 + 2 * kG >= cnt) break;
+            m0 += kG;
+            if (m0 >= cnt) break;
+            issue(sa, m0 + kG);
+            compute(sb, m0);
+            m0 += kG;
+            if (m0 >= cnt) break;
         }
     }
 
@@ -395,42 +386,57 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
     if (nsplit == 1) return;
 
     // ---- the last split of this unit merges all splits
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t prev = atomicAdd(&a.counters[unit], 1u);
-        is_last = (prev == (uint32_t)(nsplit - 1));
+    if (!arrive_last(&a.counters[unit], (uint32_t)nsplit, &is_last)) return;
+    // split weights: every (split, head) max and normaliser fetched at once into
+    // LDS (reusing the wave-merge area), then w[s][h] = exp2(m_s - M_h)
+    float *wm = smem;                  // [nsplit][r] split maxima, then weights
+    float *wz = smem + nsplit * r;     // [nsplit][r] split normalisers
+    float *hz = wz + nsplit * r;       // [r] merged normaliser
+    __syncthreads();                   // the wave-merge area is free again
+    const float *parts = a.partials + (size_t)unit * a.nsplit_max * row;
+    for (int i = tid; i < nsplit * r; i += kThreads) {
+        const int sp = i / r, h = i % r;
+        wm[i] = load_relaxed(parts + (size_t)sp * row + r * D + h);
+        wz[i] = load_relaxed(parts + (size_t)sp * row + r * D + r + h);
     }
     __syncthreads();
-    if (!is_last) return;
-    __threadfence();
-    if (tid == 0) a.counters[unit] = 0u;
-    const float *parts = a.partials + (size_t)unit * a.nsplit_max * row;
-    for (int idx = tid; idx < r * D; idx += kThreads) {
-        const int h = idx / D, d = idx % D;
+    if (tid < r) {
         float M = -INFINITY;
-        for (int s = 0; s < nsplit; ++s) M = fmaxf(M, load_relaxed(parts + (size_t)s * row + r * D + h));
-        float acc = 0.f, Z = 0.f;
-        if (M > -INFINITY) {
-            for (int s = 0; s < nsplit; ++s) {
-                const float *ps = parts + (size_t)s * row;
-                const float ms = load_relaxed(ps + r * D + h);
-                if (ms > -INFINITY) {
-                    const float w = __builtin_amdgcn_exp2f(ms - M);
-                    acc += w * load_relaxed(ps + idx);
-                    Z += w * load_relaxed(ps + r * D + r + h);
-                }
-            }
+        for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, wm[sp * r + tid]);
+        float Z = 0.f;
+        for (int sp = 0; sp < nsplit; ++sp) {
+            const float ms = wm[sp * r + tid];
+            const float w = ms > -INFINITY ? __builtin_amdgcn_exp2f(ms - M) : 0.f;
+            wm[sp * r + tid] = w;
+            Z += w * wz[sp * r + tid];
         }
-        store_out<T>(outp + (size_t)h * D + d, acc / Z);
-        if (d == 0 && a.lse) a.lse[(size_t)b * a.Hq + (size_t)g * r + h] = M * kLn2 + logf(Z);
+        hz[tid] = Z;
+        if (a.lse) a.lse[(size_t)b * a.Hq + (size_t)g * r + tid] = M * kLn2 + logf(Z);
+    }
+    __syncthreads();
+    // weighted sum of the split outputs: loads of eight splits in flight per thread
+    for (int idx = tid; idx < r * D; idx += kThreads) {
+        const int h = idx / D;
+        float acc = 0.f;
+        int sp = 0;
+        for (; sp + 8 <= nsplit; sp += 8) {
+            float o8[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) o8[u] = load_relaxed(parts + (size_t)(sp + u) * row + idx);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc += wm[(sp + u) * r + h] * o8[u];
+        }
+        for (; sp < nsplit; ++sp) acc += wm[sp * r + h] * load_relaxed(parts + (size_t)sp * row + idx);
+        store_out<T>(outp + idx, acc / hz[h]);
     }
 }
 
 template <typename T, int D, bool DENSE>
 hipError_t launch(const Dims &d, const AttendPlan &plan, AttendArgs a, hipStream_t stream) {
     const size_t grid = (size_t)d.B * d.Hkv * plan.nsplit_max;
-    const size_t lds = sizeof(float) * ((size_t)kWaves * d.group() * D + 2 * kWaves * 16);
+    const size_t wave_merge = (size_t)kWaves * d.group() * D + 2 * kWaves * 16;
+    const size_t split_merge = 2 * (size_t)plan.nsplit_max * d.group() + d.group();
+    const size_t lds = sizeof(float) * (wave_merge > split_merge ? wave_merge : split_merge);
     hipLaunchKernelGGL((attend_kernel<T, D, DENSE>), dim3((unsigned)grid), dim3(kThreads), lds,
                        stream, a);
     return hipGetLastError();
@@ -445,16 +451,24 @@ hipError_t launch_dtype(const Dims &d, const AttendPlan &plan, bool dense, Atten
 }  // namespace
 
 AttendPlan plan_attend(const Dims &d, int list_len_max, bool dense) {
-    AttendPlan p;
+    // The split merge keeps nsplit * r maxima and normalisers in LDS: at most
+    // kMaxSplitHeads of each.  A wave holds at most 64 list entries (one per lane).
+    constexpr int kMaxSplitHeads = 2048;
     const size_t units = (size_t)d.B * d.Hkv;
+    const int r = d.group();
+    auto nsplit = [&](int bps) { return (list_len_max + bps - 1) / bps; };
+    AttendPlan p;
     if (dense) {
-        p.bps = 64;  // 16 blocks (128 KiB of bf16 K+V at D=128) per wave
+        p.bps = 128;  // 32 blocks (256 KiB of bf16 K+V at D=128) per wave
     } else {
-        // about 512 workgroups in flight, at least two blocks per wave
+        // about 512 workgroups, at least two blocks per wave
         p.bps = 64;
-        while (p.bps > 8 && units * (size_t)((list_len_max + p.bps - 1) / p.bps) < 512) p.bps /= 2;
+        while (p.bps > 8 && units * (size_t)nsplit(p.bps) < 512 &&
+               nsplit(p.bps / 2) * r <= kMaxSplitHeads)
+            p.bps /= 2;
     }
-    p.nsplit_max = (list_len_max + p.bps - 1) / p.bps;
+    while (nsplit(p.bps) * r > kMaxSplitHeads && p.bps < 4 * kWave) p.bps *= 2;
+    p.nsplit_max = nsplit(p.bps);
     return p;
 }
 

@@ -11,7 +11,7 @@ namespace btk {
 
 constexpr int kWave = 64;
 constexpr int kPage = 16;           // tokens per page (block); all kernels assume it
-constexpr int kMaxBlocksPerSeq = 8192;  // select keeps <= 32 keys per thread x 256
+constexpr int kMaxBlocksPerSeq = 8192;  // select holds one key per block in LDS
 constexpr int kMaxGroup = 16;       // query heads per KV head: MFMA tile rows
 
 // error bits in workspace word 0
@@ -52,6 +52,30 @@ __device__ __forceinline__ void store_relaxed(float *p, float v) {
 __device__ __forceinline__ float load_relaxed(const float *p) {
     return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t *>(p),
                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Cross-workgroup hand-off without L2 maintenance.  Every value another
+// workgroup reads is written with store_relaxed and read with load_relaxed:
+// agent-scope atomic accesses, which gfx950 performs coherently across the
+// XCDs' L2 caches.  A workgroup publishes by waiting until its own such stores
+// have completed, then counting itself in with an agent-scope atomic; the one
+// that brings the count to `total` sees every other workgroup's stores with its
+// own load_relaxed reads.  A device-scope __threadfence() would instead write
+// back and invalidate the whole L2 of the XCD in every workgroup.
+// Returns true in all threads of the last workgroup, which also re-arms the
+// counter to zero for the next launch.
+__device__ __forceinline__ bool arrive_last(uint32_t *counter, uint32_t total, int *flag) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t prev =
+            __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag = prev == total - 1;
+        if (prev == total - 1)
+            __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    return *flag != 0;
 }
 
 __device__ __forceinline__ void flag_error(uint32_t *err, uint32_t bit) {

@@ -1,0 +1,38 @@
+"""The benchmark's byte accounting, pinned to the pages' Table 2 figure
+(Pith review of "Kinetics: Rethinking Test-Time Scaling Laws", referee report,
+major comment 1: Qwen3-32B holds 8 GB of KV cache per 32K-token sequence)."""
+import json
+import os
+
+import bench
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "table2_kv_bytes.json")
+
+
+def test_dense_bytes_per_token_match_table2():
+    fx = json.load(open(GOLDEN))
+    per_layer = bench.dense_kv_bytes_per_token(fx["num_kv_heads"], fx["head_dim"],
+                                               fx["bytes_per_element"])
+    assert per_layer * fx["layers"] * fx["tokens"] == fx["kv_bytes"]
+    # the dense model's KV term over one 32K sequence of one layer is the same figure
+    b = bench.algorithmic_bytes([fx["tokens"]], 64, fx["num_kv_heads"], fx["head_dim"], 64,
+                                fx["bytes_per_element"])
+    kv_only = b["dense"] - 4 * (fx["tokens"] // 16) - 2 * 64 * fx["head_dim"] * 2
+    assert kv_only * fx["layers"] == fx["kv_bytes"]
+
+
+def test_sparse_bytes_shrink_and_k_at_least_blocks_reads_everything():
+    b = bench.algorithmic_bytes([32768] * 8, 64, 8, 128, 64, 2)
+    assert b["step"] < b["dense"] / 10
+    # centroid scan is 1/16 of the dense KV bytes for fp32 centroids and bf16 K+V
+    scan = 8 * 8 * 4 * 128 * 2048
+    assert 16 * scan == 8 * 8 * 2 * 32768 * 128 * 2
+    full = bench.algorithmic_bytes([100], 4, 2, 64, 64, 2)  # 7 blocks < k
+    kv_att = full["attend"] - 2 * (8 * 64 + 2 * 2 * 64 * 2)
+    assert kv_att == 2 * 2 * 100 * 64 * 2
+
+
+def test_exact_selected_tokens():
+    import torch
+    idx = torch.tensor([[[0, 6, -1]]], dtype=torch.int32)
+    assert bench.selected_tokens(idx, [100]) == [[16 + 4]]

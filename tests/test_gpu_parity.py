@@ -294,3 +294,41 @@ def test_out_of_range_device_inputs_are_flagged_not_read():
     btk.btk_dense_attend(d.q, d.k_cache, d.v_cache, d.block_table, bad_len, ws, problem=prob)
     torch.cuda.synchronize()
     assert btk.workspace_error_bits(ws) & 1
+
+
+# ------------------------------------------------------------------ graph capture
+
+def test_decode_step_replayed_from_a_graph_matches_eager():
+    bt = synth.make_config(3, batch=8)
+    d = bt.to(DEV)
+    prob = btk.make_problem(d.q, d.k_cache, d.block_table)
+    ws = btk.new_workspace(prob, bt.top_k, DEV)
+    cent = torch.zeros((bt.num_pages, bt.num_kv_heads, bt.head_dim), device=DEV)
+    btk.btk_centroid_update(d.k_cache, d.block_table, d.seq_lens, cent, problem=prob)
+    first = (d.seq_lens - 1).to(torch.int32)
+    out = torch.empty_like(d.q)
+    idx = torch.empty((bt.batch, bt.num_kv_heads, bt.top_k), dtype=torch.int32, device=DEV)
+    btk.sparse_decode_step(d.q, d.k_cache, d.v_cache, d.block_table, d.seq_lens, cent, bt.top_k,
+                           ws, first_pos=first, out=out, indices=idx, problem=prob)
+    torch.cuda.synchronize()
+    eager_out, eager_idx = out.clone(), idx.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            btk.sparse_decode_step(d.q, d.k_cache, d.v_cache, d.block_table, d.seq_lens, cent,
+                                   bt.top_k, ws, first_pos=first, out=out, indices=idx,
+                                   problem=prob)
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(4):
+        out.zero_()
+        idx.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_out), rep
+        assert torch.equal(idx, eager_idx), rep
+        # eager work between replays
+        btk.btk_select(d.q, cent, d.block_table, d.seq_lens, bt.top_k, ws, problem=prob)
+        torch.cuda.synchronize()
+    assert btk.workspace_error_bits(ws) == 0
