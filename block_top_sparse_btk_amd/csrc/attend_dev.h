@@ -1,0 +1,468 @@
+// Device code of S4 / S5 (attention of a query group over a list of KV
+// blocks), shared by the stand-alone attention kernels and the single-launch
+// decode step.
+// S4 / S5: exact softmax attention of a query group over a list of KV blocks
+// (the selected blocks, or every block for the dense comparison).
+// (Pith review of "Kinetics: Rethinking Test-Time Scaling Laws", "What carries
+// the argument": attention runs over only the retrieved top-k blocks; the dense
+// path is the paged decode attention it is compared with, Kinetics README
+// (GitLite mirror), "Benchmark Block TopK Attention throughput".)
+//
+// Work unit: one (sequence, KV head) pair and a split of its block list; one
+// 256-thread workgroup per split, its four waves take contiguous runs of the
+// split.  A wave handles the r query heads of the group at once with MFMA
+// tiles whose 16 rows cover the group (rows >= r are zero queries):
+//   S^T[t][h] = K_tile (16 tokens x D) . Q^T        (16x16x32 bf16 / 16x16x4 f32)
+// The 16x16 fp32 result leaves lane l holding tokens 4*(l/16)+e of head l%16,
+// which is exactly the A-operand layout of the next product, so probabilities
+// never leave registers:
+//   O[h][d] += P (heads x 16 tokens) . V_tile (16 tokens x D)   (16x16x16 bf16)
+// V pages are stored dim-major ([D][16] per page and head), so each lane's
+// B operand (4 consecutive tokens of one dimension) is one 8-byte load and a
+// wave instruction reads 512 contiguous bytes.  K pages are token-major and each
+// lane reads 16 contiguous bytes per K instruction.
+// Online softmax runs per group of G blocks in the base-2 domain with the
+// scale folded in; the P fed to the bf16 product is rounded to bf16, while the
+// normaliser and the log-sum-exp sum the unrounded weights.  Blocks are double-buffered:
+// the loads of the next group are in flight while the current one is computed.
+// Waves merge through LDS; splits merge through the workspace in the
+// workgroup that finishes last (a counter per unit, see arrive_last).
+#pragma once
+#include "btk_internal.h"
+
+namespace btk {
+namespace att {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+template <typename T, int D>
+struct Mfma;
+
+// bf16: QK with v_mfma_f32_16x16x32_bf16, PV with v_mfma_f32_16x16x16_bf16.
+template <int D>
+struct Mfma<uint16_t, D> {
+    static constexpr int NK = D / 32;
+    static constexpr int NV = D / 16;
+    struct KFrag {
+        bf16x8_t x[NK];
+    };
+    struct VFrag {
+        short4_t x[NV];
+    };
+    using QFrag = KFrag;
+
+    // lane l: token l%16, dims 32*i + 8*(l/16) .. +8
+    __device__ static void load_k(KFrag &f, const uint16_t *tile, int lane) {
+        const uint16_t *p = tile + (lane & 15) * D + 8 * (lane >> 4);
+#pragma unroll
+        for (int i = 0; i < NK; ++i)
+            f.x[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(p + 32 * i));
+    }
+    // lane l: head l%16 (zero when >= r), same dims as load_k
+    __device__ static void load_q(QFrag &f, const uint16_t *qg, int r, int lane) {
+        const int h = lane & 15;
+        const uint16_t *p = qg + h * D + 8 * (lane >> 4);
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+            uint4 w = h < r ? *reinterpret_cast<const uint4 *>(p + 32 * i) : make_uint4(0, 0, 0, 0);
+            f.x[i] = __builtin_bit_cast(bf16x8_t, w);
+        }
+    }
+    __device__ static floatx4_t qk(const KFrag &k, const QFrag &q) {
+        floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NK; ++i)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k.x[i], q.x[i], acc, 0, 0, 0);
+        return acc;
+    }
+    // lane l: dim 16*n + l%16, tokens 4*(l/16) .. +4 of the dim-major tile
+    __device__ static void load_v(VFrag &f, const uint16_t *tile, int lane) {
+        const uint16_t *p = tile + (lane & 15) * kPage + 4 * (lane >> 4);
+#pragma unroll
+        for (int n = 0; n < NV; ++n)
+            f.x[n] = __builtin_bit_cast(short4_t,
+                                        *reinterpret_cast<const uint2 *>(p + 16 * kPage * n));
+    }
+    __device__ static void mask_v(VFrag &f, int v, int lane) {
+        const int t0 = 4 * (lane >> 4);
+#pragma unroll
+        for (int n = 0; n < NV; ++n)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (t0 + e >= v) f.x[n][e] = 0;
+    }
+    __device__ static float round_p(float p) { return bf16_bits_to_f32(f32_to_bf16_bits(p)); }
+    __device__ static void pv(floatx4_t (&o)[NV], const float (&p)[4], const VFrag &v) {
+        short4_t a;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] = (short)(__float_as_uint(p[e]) >> 16);  // p is bf16-exact
+#pragma unroll
+        for (int n = 0; n < NV; ++n)
+            o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, v.x[n], o[n], 0, 0, 0);
+    }
+};
+
+// fp32: both products with v_mfma_f32_16x16x4f32 (one k-slot per lane group).
+template <int D>
+struct Mfma<float, D> {
+    static constexpr int NK = D / 4;
+    static constexpr int NV = D / 16;
+    struct KFrag {
+        float x[NK];
+    };
+    struct VFrag {
+        float4 x[NV];
+    };
+    using QFrag = KFrag;
+
+    // lane l: token l%16, dims (l/16)*(D/4) + i
+    __device__ static void load_k(KFrag &f, const float *tile, int lane) {
+        const float *p = tile + (lane & 15) * D + (lane >> 4) * (D / 4);
+#pragma unroll
+        for (int i = 0; i < NK; i += 4) {
+            float4 w = *reinterpret_cast<const float4 *>(p + i);
+            f.x[i] = w.x;
+            f.x[i + 1] = w.y;
+            f.x[i + 2] = w.z;
+            f.x[i + 3] = w.w;
+        }
+    }
+    __device__ static void load_q(QFrag &f, const float *qg, int r, int lane) {
+        const int h = lane & 15;
+        const float *p = qg + h * D + (lane >> 4) * (D / 4);
+#pragma unroll
+        for (int i = 0; i < NK; i += 4) {
+            float4 w = h < r ? *reinterpret_cast<const float4 *>(p + i)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+            f.x[i] = w.x;
+            f.x[i + 1] = w.y;
+            f.x[i + 2] = w.z;
+            f.x[i + 3] = w.w;
+        }
+    }
+    __device__ static floatx4_t qk(const KFrag &k, const QFrag &q) {
+        floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NK; ++i)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k.x[i], q.x[i], acc, 0, 0, 0);
+        return acc;
+    }
+    // lane l: dim 16*n + l%16, tokens 4*(l/16) .. +4
+    __device__ static void load_v(VFrag &f, const float *tile, int lane) {
+        const float *p = tile + (lane & 15) * kPage + 4 * (lane >> 4);
+#pragma unroll
+        for (int n = 0; n < NV; ++n) f.x[n] = *reinterpret_cast<const float4 *>(p + 16 * kPage * n);
+    }
+    __device__ static void mask_v(VFrag &f, int v, int lane) {
+        const int t0 = 4 * (lane >> 4);
+#pragma unroll
+        for (int n = 0; n < NV; ++n) {
+            if (t0 + 0 >= v) f.x[n].x = 0.f;
+            if (t0 + 1 >= v) f.x[n].y = 0.f;
+            if (t0 + 2 >= v) f.x[n].z = 0.f;
+            if (t0 + 3 >= v) f.x[n].w = 0.f;
+        }
+    }
+    __device__ static float round_p(float p) { return p; }
+    // MFMA e contracts token 4*(l/16)+e of every lane group
+    __device__ static void pv(floatx4_t (&o)[NV], const float (&p)[4], const VFrag &v) {
+#pragma unroll
+        for (int n = 0; n < NV; ++n) {
+            o[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[0], v.x[n].x, o[n], 0, 0, 0);
+            o[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[1], v.x[n].y, o[n], 0, 0, 0);
+            o[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[2], v.x[n].z, o[n], 0, 0, 0);
+            o[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[3], v.x[n].w, o[n], 0, 0, 0);
+        }
+    }
+};
+
+struct AttendArgs {
+    const void *q, *k, *v;
+    const int32_t *bt, *seq_lens, *indices;
+    void *out;
+    float *lse, *partials;
+    uint32_t *counters, *err;
+    int Hq, Hkv, num_pages, max_blocks, top_k, bps, nsplit_max;
+    float scale_log2;
+    uint32_t *ready;  // decode step only: per-unit "selection published" flags
+};
+
+// Spin bound of the decode step's wait for a unit's selection (~0.1 s).
+constexpr uint32_t kReadySpinLimit = 1u << 22;
+
+template <typename T>
+__device__ __forceinline__ void store_out(T *p, float x);
+template <>
+__device__ __forceinline__ void store_out<uint16_t>(uint16_t *p, float x) {
+    *p = (uint16_t)f32_to_bf16_bits(x);
+}
+template <>
+__device__ __forceinline__ void store_out<float>(float *p, float x) {
+    *p = x;
+}
+
+// One (unit, split) item: attention of the unit's query group over its share of
+// the block list, kG blocks per pipeline stage.  (Continued:)
+//
+// the block list.  smem: the wave-merge / split-merge area (see launch sizing);
+// is_last: one LDS word.  Inside a decode step (a.ready set) the item first
+// waits until the unit's selection is published and reads the indices with
+// agent-coherent loads; the unit's last item re-arms the flag.
+template <typename T, int D, bool DENSE, int kG>
+__device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int split, float *smem,
+                                            int *is_last_p) {
+    using F = Mfma<T, D>;
+    constexpr int NV = F::NV;
+    int &is_last = *is_last_p;
+
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int b = unit / a.Hkv, g = unit % a.Hkv;
+    const int r = a.Hq / a.Hkv;
+    const int L = a.seq_lens[b];
+    if (L < 1 || L > a.max_blocks * kPage) {
+        if (split == 0 && tid == 0) flag_error(a.err, kErrSeqLen);
+        return;
+    }
+    const int nb = (L + kPage - 1) / kPage;
+    const int len = DENSE ? nb : a.top_k;
+    const int nsplit = (len + a.bps - 1) / a.bps;
+    if (split >= nsplit) return;
+    if (!DENSE && a.ready) {  // decode step: wait for the unit's selection
+        if (tid == 0) {
+            uint32_t spins = 0;
+            while (__hip_atomic_load(&a.ready[unit], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   0u) {
+                __builtin_amdgcn_s_sleep(2);
+                if (++spins > kReadySpinLimit) {  // never expected: report, do not hang
+                    flag_error(a.err, kErrTimeout);
+                    break;
+                }
+            }
+        }
+        __syncthreads();
+    }
+    const int i0 = split * a.bps, i1 = min(len, i0 + a.bps);
+    const int per_wave = a.bps / kWaves;
+    const int w0 = i0 + wave * per_wave;
+    const int cnt = max(0, min(i1, w0 + per_wave) - w0);
+
+    // lane m < cnt holds page id and valid tokens of this wave's m-th entry
+    // (page -1 and 0 tokens for a skipped or invalid entry)
+    int my_page = -1, my_v = 0;
+    if (lane < cnt) {
+        int j = DENSE ? (w0 + lane) : load_relaxed_i32(a.indices + (size_t)unit * a.top_k + w0 + lane);
+        if (!DENSE && j >= nb) {
+            flag_error(a.err, kErrIndex);
+            j = -1;
+        }
+        if (j >= 0) {
+            const int p = a.bt[(size_t)b * a.max_blocks + j];
+            if (p >= 0 && p < a.num_pages) {
+                my_page = p;
+                my_v = min(kPage, L - j * kPage);
+            } else {
+                flag_error(a.err, kErrPage);
+            }
+        }
+    }
+
+    const T *qg = static_cast<const T *>(a.q) + ((size_t)b * a.Hq + (size_t)g * r) * D;
+    typename F::QFrag qf;
+    F::load_q(qf, qg, r, lane);
+    const size_t page_stride = (size_t)a.Hkv * kPage * D;
+    const T *kbase = static_cast<const T *>(a.k) + (size_t)g * kPage * D;
+    const T *vbase = static_cast<const T *>(a.v) + (size_t)g * kPage * D;
+
+    float m_run = -INFINITY, z_run = 0.f;
+    floatx4_t o[NV];
+#pragma unroll
+    for (int n = 0; n < NV; ++n) o[n] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+    struct Stage {
+        typename F::KFrag k[kG];
+        typename F::VFrag v[kG];
+    };
+    // Loads and their consumers are unconditional, so the compiler can keep
+    // the next stage in flight (precise vmcnt) while the current one computes:
+    // a slot past the wave's list re-reads its last entry (a cache hit) and an
+    // invalid entry reads page 0; both are masked to zero weight below.
+    const int safe_page = my_page >= 0 ? my_page : 0;
+    auto issue = [&](Stage &s, int m0) {
+#pragma unroll
+        for (int u = 0; u < kG; ++u) {
+            const int m = min(m0 + u, cnt - 1);
+            const int page = __builtin_amdgcn_readlane(safe_page, m);
+            F::load_k(s.k[u], kbase + page * page_stride, lane);
+            F::load_v(s.v[u], vbase + page * page_stride, lane);
+        }
+    };
+    auto compute = [&](Stage &s, int m0) {
+        float sv[kG][4];
+        int vv[kG];
+        float gmax = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < kG; ++u) {
+            const int m = min(m0 + u, cnt - 1);
+            // valid tokens of this slot, 0 for a repeated or invalid entry (wave-uniform)
+            vv[u] = m0 + u < cnt ? __builtin_amdgcn_readlane(my_v, m) : 0;
+            const floatx4_t acc = F::qk(s.k[u], qf);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 4 * (lane >> 4) + e;
+                sv[u][e] = t < vv[u] ? acc[e] * a.scale_log2 : -INFINITY;
+                gmax = fmaxf(gmax, sv[u][e]);
+            }
+        }
+        gmax = fmaxf(gmax, __shfl_xor(gmax, 16));
+        gmax = fmaxf(gmax, __shfl_xor(gmax, 32));
+        const float m_new = fmaxf(m_run, gmax);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;  // nothing valid yet: keep zeros
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // 0 when m_run = -inf
+        z_run *= alpha;
+        // O rows are heads 4*(l/16)+e; alpha of head h lives in lane h
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float ar = __shfl(alpha, 4 * (lane >> 4) + e);
+#pragma unroll
+            for (int n = 0; n < NV; ++n) o[n][e] *= ar;
+        }
+        m_run = m_new;
+#pragma unroll
+        for (int u = 0; u < kG; ++u) {
+            float p[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float pe = __builtin_amdgcn_exp2f(sv[u][e] - m_use);  // 0 for masked tokens
+                z_run += pe;  // the normaliser (and lse) use the unrounded weights
+                p[e] = F::round_p(pe);
+            }
+            if (vv[u] < kPage) F::mask_v(s.v[u], vv[u], lane);  // no 0 * garbage in P.V
+            F::pv(o, p, s.v[u]);
+        }
+    };
+
+    if (cnt > 0) {
+        Stage sa, sb;
+        issue(sa, 0);
+        for (int m0 = 0;;) {
+            issue(sb, m0 + kG);
+            compute(sa, m0);
+            m0 += kG;
+            if (m0 >= cnt) break;
+            issue(sa, m0 + kG);
+            compute(sb, m0);
+            m0 += kG;
+            if (m0 >= cnt) break;
+        }
+    }
+
+    // ---- merge the four waves through LDS
+    float *so = smem;                          // [kWaves][r][D]
+    float *sm = smem + kWaves * r * D;         // [kWaves][16]
+    float *sz = sm + kWaves * 16;              // [kWaves][16]
+    float z = z_run;
+    z += __shfl_xor(z, 16);
+    z += __shfl_xor(z, 32);
+    if (lane < 16) {
+        sm[wave * 16 + lane] = m_run;
+        sz[wave * 16 + lane] = z;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int h = 4 * (lane >> 4) + e;
+        if (h < r) {
+#pragma unroll
+            for (int n = 0; n < NV; ++n) so[(wave * r + h) * D + 16 * n + (lane & 15)] = o[n][e];
+        }
+    }
+    __syncthreads();
+
+    const int row = 2 * r + r * D;  // floats per partial: o[r][D], m[r], z[r]
+    float *part = a.partials + ((size_t)unit * a.nsplit_max + split) * row;
+    T *outp = static_cast<T *>(a.out) + ((size_t)b * a.Hq + (size_t)g * r) * D;
+    for (int idx = tid; idx < r * D; idx += kThreads) {
+        const int h = idx / D, d = idx % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm[w * 16 + h]);
+        float acc = 0.f, Z = 0.f;
+        if (M > -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float mw = sm[w * 16 + h];
+                if (mw > -INFINITY) {
+                    const float s = __builtin_amdgcn_exp2f(mw - M);
+                    acc += s * so[(w * r + h) * D + d];
+                    Z += s * sz[w * 16 + h];
+                }
+            }
+        }
+        if (nsplit == 1) {
+            store_out<T>(outp + (size_t)h * D + d, acc / Z);
+            if (d == 0 && a.lse) a.lse[(size_t)b * a.Hq + (size_t)g * r + h] = M * kLn2 + logf(Z);
+        } else {
+            store_relaxed(part + idx, acc);
+            if (d == 0) {
+                store_relaxed(part + r * D + h, M);
+                store_relaxed(part + r * D + r + h, Z);
+            }
+        }
+    }
+    if (nsplit == 1) {
+        if (!DENSE && a.ready && tid == 0)
+            __hip_atomic_store(&a.ready[unit], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+
+    // ---- the last split of this unit merges all splits
+    if (!arrive_last(&a.counters[unit], (uint32_t)nsplit, &is_last)) return;
+    if (!DENSE && a.ready && tid == 0)  // every split has read the selection
+        __hip_atomic_store(&a.ready[unit], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // split weights: every (split, head) max and normaliser fetched at once into
+    // LDS (reusing the wave-merge area), then w[s][h] = exp2(m_s - M_h)
+    float *wm = smem;                  // [nsplit][r] split maxima, then weights
+    float *wz = smem + nsplit * r;     // [nsplit][r] split normalisers
+    float *hz = wz + nsplit * r;       // [r] merged normaliser
+    __syncthreads();                   // the wave-merge area is free again
+    const float *parts = a.partials + (size_t)unit * a.nsplit_max * row;
+    for (int i = tid; i < nsplit * r; i += kThreads) {
+        const int sp = i / r, h = i % r;
+        wm[i] = load_relaxed(parts + (size_t)sp * row + r * D + h);
+        wz[i] = load_relaxed(parts + (size_t)sp * row + r * D + r + h);
+    }
+    __syncthreads();
+    if (tid < r) {
+        float M = -INFINITY;
+        for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, wm[sp * r + tid]);
+        float Z = 0.f;
+        for (int sp = 0; sp < nsplit; ++sp) {
+            const float ms = wm[sp * r + tid];
+            const float w = ms > -INFINITY ? __builtin_amdgcn_exp2f(ms - M) : 0.f;
+            wm[sp * r + tid] = w;
+            Z += w * wz[sp * r + tid];
+        }
+        hz[tid] = Z;
+        if (a.lse) a.lse[(size_t)b * a.Hq + (size_t)g * r + tid] = M * kLn2 + logf(Z);
+    }
+    __syncthreads();
+    // weighted sum of the split outputs: loads of eight splits in flight per thread
+    for (int idx = tid; idx < r * D; idx += kThreads) {
+        const int h = idx / D;
+        float acc = 0.f;
+        int sp = 0;
+        for (; sp + 8 <= nsplit; sp += 8) {
+            float o8[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) o8[u] = load_relaxed(parts + (size_t)(sp + u) * row + idx);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc += wm[(sp + u) * r + h] * o8[u];
+        }
+        for (; sp < nsplit; ++sp) acc += wm[sp * r + h] * load_relaxed(parts + (size_t)sp * row + idx);
+        store_out<T>(outp + idx, acc / hz[h]);
+    }
+}
+
+}  // namespace att
+}  // namespace btk

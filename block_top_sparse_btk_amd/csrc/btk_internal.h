@@ -18,6 +18,7 @@ constexpr int kMaxGroup = 16;       // query heads per KV head: MFMA tile rows
 constexpr uint32_t kErrSeqLen = 1u;
 constexpr uint32_t kErrPage = 2u;
 constexpr uint32_t kErrIndex = 4u;
+constexpr uint32_t kErrTimeout = 8u;  // decode step: a unit's selection never arrived
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) short short4_t;
@@ -52,6 +53,14 @@ __device__ __forceinline__ void store_relaxed(float *p, float v) {
 __device__ __forceinline__ float load_relaxed(const float *p) {
     return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t *>(p),
                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+__device__ __forceinline__ void store_relaxed_i32(int32_t *p, int32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ int32_t load_relaxed_i32(const int32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Cross-workgroup hand-off without L2 maintenance.  Every value another

@@ -2,43 +2,13 @@
 // (Pith review of "Kinetics: Rethinking Test-Time Scaling Laws", "What carries
 // the argument": blocks are summarised by their averaged key vectors.)
 //
-// One wave per (page, KV head) block.  A key row of D elements is read as 16-byte
-// vectors: LPR lanes cover one token row, TPI rows are read per instruction,
-// so one wave instruction moves a contiguous 1 KiB of the token-major page.
-// Partial sums over token rows are folded with cross-lane xor shuffles.
-#include "btk_internal.h"
+// One wave per (page, KV head) block (block_centroid in centroid_dev.h).
+#include "centroid_dev.h"
 
 namespace btk {
 namespace {
 
 constexpr int kWavesPerWg = 4;
-
-template <typename T>
-struct Vec16;
-template <>
-struct Vec16<uint16_t> {
-    static constexpr int n = 8;
-    __device__ static void add(const void *p, float (&acc)[8]) {
-        uint4 w = *reinterpret_cast<const uint4 *>(p);
-        uint32_t x[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc[2 * i] += bf16_bits_to_f32(x[i] & 0xffffu);
-            acc[2 * i + 1] += bf16_bits_to_f32(x[i] >> 16);
-        }
-    }
-};
-template <>
-struct Vec16<float> {
-    static constexpr int n = 4;
-    __device__ static void add(const void *p, float (&acc)[4]) {
-        float4 w = *reinterpret_cast<const float4 *>(p);
-        acc[0] += w.x;
-        acc[1] += w.y;
-        acc[2] += w.z;
-        acc[3] += w.w;
-    }
-};
 
 // grid: x = block chunk (rebuild) or 1 (touched mode), y = KV head, z = sequence
 template <typename T, int D>
@@ -46,11 +16,6 @@ __global__ __launch_bounds__(kWave * kWavesPerWg) void centroid_kernel(
     const T *__restrict__ k_cache, const int32_t *__restrict__ block_table,
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ first_pos,
     float *__restrict__ centroids, int Hkv, int num_pages, int max_blocks, int blocks_per_wg) {
-    constexpr int VEC = Vec16<T>::n;
-    constexpr int LPR = D / VEC;       // lanes per token row
-    constexpr int TPI = kWave / LPR;   // token rows per wave instruction
-    static_assert(kWave % LPR == 0 && kPage % TPI == 0, "layout");
-
     const int b = blockIdx.z, g = blockIdx.y;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int L = seq_lens[b];
@@ -66,35 +31,12 @@ __global__ __launch_bounds__(kWave * kWavesPerWg) void centroid_kernel(
         j0 = blockIdx.x * blocks_per_wg;
         j1 = min(nb, j0 + blocks_per_wg);
     }
-    const int col = lane % LPR, row = lane / LPR;
     for (int j = j0 + wave; j < j1; j += kWavesPerWg) {
         const int page = block_table[(size_t)b * max_blocks + j];
         if (page < 0 || page >= num_pages) continue;
         const int v = min(kPage, L - j * kPage);
-        const T *base = k_cache + ((size_t)page * Hkv + g) * kPage * D;
-        float acc[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
-#pragma unroll
-        for (int t0 = 0; t0 < kPage; t0 += TPI) {
-            const int t = t0 + row;
-            if (t < v) Vec16<T>::add(base + (size_t)t * D + col * VEC, acc);
-        }
-#pragma unroll
-        for (int off = LPR; off < kWave; off <<= 1) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], off);
-        }
-        if (row == 0) {
-            float *dst = centroids + ((size_t)page * Hkv + g) * D + col * VEC;
-            const float vf = (float)v;
-#pragma unroll
-            for (int e = 0; e < VEC; e += 4) {
-                float4 o = make_float4(acc[e] / vf, acc[e + 1] / vf, acc[e + 2] / vf,
-                                       acc[e + 3] / vf);
-                *reinterpret_cast<float4 *>(dst + e) = o;
-            }
-        }
+        block_centroid<T, D>(k_cache + ((size_t)page * Hkv + g) * kPage * D, v,
+                             centroids + ((size_t)page * Hkv + g) * D, nullptr, lane);
     }
 }
 

@@ -1,0 +1,76 @@
+// Device code of S1 (block centroid = mean of a page's valid keys, fp32
+// accumulation), shared by the stand-alone centroid kernel and the
+// single-launch decode step.  (Pith review of "Kinetics: Rethinking Test-Time
+// Scaling Laws", "What carries the argument": blocks are summarised by their
+// averaged key vectors.)
+#pragma once
+#include "btk_internal.h"
+
+namespace btk {
+
+template <typename T>
+struct Vec16;
+template <>
+struct Vec16<uint16_t> {
+    static constexpr int n = 8;
+    __device__ static void add(const void *p, float (&acc)[8]) {
+        uint4 w = *reinterpret_cast<const uint4 *>(p);
+        uint32_t x[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] += bf16_bits_to_f32(x[i] & 0xffffu);
+            acc[2 * i + 1] += bf16_bits_to_f32(x[i] >> 16);
+        }
+    }
+};
+template <>
+struct Vec16<float> {
+    static constexpr int n = 4;
+    __device__ static void add(const void *p, float (&acc)[4]) {
+        float4 w = *reinterpret_cast<const float4 *>(p);
+        acc[0] += w.x;
+        acc[1] += w.y;
+        acc[2] += w.z;
+        acc[3] += w.w;
+    }
+};
+
+// Mean of the v valid keys of one token-major (page, head) tile, by one wave.
+// A key row of D elements is read as 16-byte vectors: LPR lanes cover a token
+// row and TPI rows are read per instruction (1 KiB contiguous per wave
+// instruction); partial sums over rows are folded with xor shuffles.  The
+// centroid row is written to gdst (global) and, if given, to ldst (LDS).
+template <typename T, int D>
+__device__ __forceinline__ void block_centroid(const T *tile, int v, float *gdst, float *ldst,
+                                               int lane) {
+    constexpr int VEC = Vec16<T>::n;
+    constexpr int LPR = D / VEC;      // lanes per token row
+    constexpr int TPI = kWave / LPR;  // token rows per wave instruction
+    static_assert(kWave % LPR == 0 && kPage % TPI == 0, "layout");
+    const int col = lane % LPR, row = lane / LPR;
+    float acc[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int t0 = 0; t0 < kPage; t0 += TPI) {
+        const int t = t0 + row;
+        if (t < v) Vec16<T>::add(tile + (size_t)t * D + col * VEC, acc);
+    }
+#pragma unroll
+    for (int off = LPR; off < kWave; off <<= 1) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], off);
+    }
+    if (row == 0) {
+        const float vf = (float)v;
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4) {
+            const float4 o = make_float4(acc[e] / vf, acc[e + 1] / vf, acc[e + 2] / vf,
+                                         acc[e + 3] / vf);
+            *reinterpret_cast<float4 *>(gdst + col * VEC + e) = o;
+            if (ldst) *reinterpret_cast<float4 *>(ldst + col * VEC + e) = o;
+        }
+    }
+}
+
+}  // namespace btk

@@ -1,0 +1,524 @@
+// Device code of S2 + S3 (group scoring and top-k selection), shared by the
+// stand-alone select kernel and the single-launch decode step.
+// (Pith review of "Kinetics: Rethinking Test-Time Scaling Laws", "What carries
+// the argument": key blocks are scored by their averaged key vectors per query
+// group and the top k blocks are retrieved.)
+//
+// Scoring is a bandwidth-bound GEMV: a unit (sequence b, KV head g) streams the
+// n_b centroid rows (D fp32 = 512 B at D=128) named by its block table.  The
+// unit's blocks are cut into chunks; one 256-thread workgroup scores one chunk.
+// The r query heads of the group are folded into their mean on entry
+// (linearity: the mean of the heads' logits equals the logit of the mean query),
+// so each block costs one D-long dot product.  16 lanes (one DPP row) hold a
+// centroid row; loads run in two stages of four rows per lane so one stage is in
+// flight while the other is reduced; scores are staged in LDS and leave the
+// workgroup as contiguous stores.
+//
+// Selection runs in the workgroup that finishes a unit's last chunk (a counter
+// per unit, see arrive_last), so it overlaps the scoring of later units.
+#pragma once
+#include "centroid_dev.h"
+
+namespace btk {
+namespace sel {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kMaxChunk = 512;
+constexpr int kUnroll = 4;          // rows per lane per pipeline stage
+
+struct SelectArgs {
+    const void *q;
+    const float *cent;
+    const int32_t *bt;
+    const int32_t *seq_lens;
+    int32_t *indices;
+    float *scores;
+    uint32_t *counters;
+    uint32_t *err;
+    int Hq, Hkv, num_pages, max_blocks, top_k, chunk, nchunk_max;
+    float scale;
+    // single-launch decode step only (NULL in the stand-alone select): the
+    // chunk that holds a touched page recomputes its centroid (S1) first
+    const void *k_cache;
+    const int32_t *first_pos;
+    float *cent_out;
+};
+
+// LDS used by one chunk's scan.
+struct ScoreSmem {
+    float *qraw;  // [r * D] the group's queries
+    float *qs;    // [D] scaled mean query
+    int *pages;   // [kMaxChunk] page ids of the chunk
+    float *sc;    // [kMaxChunk] scores of the chunk
+    int *flag;    // one word
+};
+
+// LDS used by the top-k selection.
+struct TopkSmem {
+    uint32_t *hist;      // [256 + 64] radix bins + per-lane spare bins
+    uint32_t *cand;      // [64] compacted candidates
+    uint32_t *above;     // [64] bitmap words
+    uint32_t *equal;     // [64]
+    uint32_t *red;       // [2 * kWaves]
+    int *scan_red;       // [kWaves]
+    uint32_t *keys;      // [max_blocks] keys, workgroup-wide path only
+};
+
+template <typename T>
+__device__ __forceinline__ float load_q(const T *p);
+template <>
+__device__ __forceinline__ float load_q<uint16_t>(const uint16_t *p) {
+    return bf16_bits_to_f32(*p);
+}
+template <>
+__device__ __forceinline__ float load_q<float>(const float *p) {
+    return *p;
+}
+
+// Sum of one wave-uniform count per wave over the workgroup (one barrier).
+__device__ __forceinline__ int wg_sum(int wave_count, int *red, int &parity) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    if (lane == 0) red[parity * kWaves + wave] = wave_count;
+    __syncthreads();
+    int s = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) s += red[parity * kWaves + w];
+    parity ^= 1;
+    return s;
+}
+
+// Exclusive prefix sum over the workgroup in thread order.
+__device__ __forceinline__ int wg_exclusive_scan(int x, int *red) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    int inc = x;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        int y = __shfl_up(inc, off);
+        if (lane >= off) inc += y;
+    }
+    __syncthreads();  // red may still be read by a previous step
+    if (lane == kWave - 1) red[wave] = inc;
+    __syncthreads();
+    int before = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+        if (w < wave) before += red[w];
+    return before + inc - x;
+}
+
+// Wave-wide sum and max of a per-lane value, uniform result: DPP within each
+// 16-lane row, then the four row results are read out.
+template <int CTRL>
+__device__ __forceinline__ int dpp(int x) {
+    return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
+    x += (uint32_t)dpp<0xB1>((int)x);   // quad xor 1
+    x += (uint32_t)dpp<0x4E>((int)x);   // quad xor 2
+    x += (uint32_t)dpp<0x141>((int)x);  // half-row mirror
+    x += (uint32_t)dpp<0x140>((int)x);  // row mirror
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 0) + (uint32_t)__builtin_amdgcn_readlane((int)x, 16) +
+           (uint32_t)__builtin_amdgcn_readlane((int)x, 32) + (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+    x = max(x, (uint32_t)dpp<0xB1>((int)x));
+    x = max(x, (uint32_t)dpp<0x4E>((int)x));
+    x = max(x, (uint32_t)dpp<0x141>((int)x));
+    x = max(x, (uint32_t)dpp<0x140>((int)x));
+    return max(max((uint32_t)__builtin_amdgcn_readlane((int)x, 0), (uint32_t)__builtin_amdgcn_readlane((int)x, 16)),
+               max((uint32_t)__builtin_amdgcn_readlane((int)x, 32), (uint32_t)__builtin_amdgcn_readlane((int)x, 48)));
+}
+
+// Wave-wide inclusive prefix sum (lane order) of a per-lane count, in DPP:
+// shifts by 1, 2, 4, 8 within each 16-lane row, then the row totals are carried
+// across rows with the row broadcasts of lanes 15 and 31.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+    x += (uint32_t)dpp<0x111>((int)x);  // row_shr:1
+    x += (uint32_t)dpp<0x112>((int)x);  // row_shr:2
+    x += (uint32_t)dpp<0x114>((int)x);  // row_shr:4
+    x += (uint32_t)dpp<0x118>((int)x);  // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return x;
+}
+
+// One radix-selection pass over the keys inside [lo, hi] (see select_topk_wave):
+// histogram into 256 LDS bins of width 2^shift, locate the bin that holds the
+// key of rank `need` counted from the top, and shrink [lo, hi] to it.  Keys out
+// of range are counted in a per-lane spare bin, so the loop has no branches.
+template <int N>
+__device__ __forceinline__ void radix_pass(const uint32_t (&key)[N], uint32_t &lo, uint32_t &hi,
+                                           int &need, uint32_t *hist, int lane) {
+    const uint32_t span = hi - lo;
+    const int shift = max(0, 24 - __builtin_clz(span));  // (span >> shift) < 256
+    reinterpret_cast<uint4 *>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const uint32_t off = key[i] - lo;
+        atomicAdd(&hist[off <= span ? (off >> shift) : 256u + lane], 1u);
+    }
+    __builtin_amdgcn_wave_barrier();
+    const uint4 h = reinterpret_cast<const uint4 *>(hist)[lane];  // bins 4l .. 4l+3
+    const uint32_t lane_sum = h.x + h.y + h.z + h.w;
+    const uint32_t above_lane = wave_sum_u32(lane_sum) - wave_inclusive_scan(lane_sum);
+    int bin = -1;
+    uint32_t above_bin = 0u, acc = above_lane;
+    const uint32_t hv[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+    for (int e = 3; e >= 0; --e) {  // from this lane's top bin down
+        if (bin < 0 && acc < (uint32_t)need && acc + hv[e] >= (uint32_t)need) {
+            bin = 4 * lane + e;
+            above_bin = acc;
+        }
+        acc += hv[e];
+    }
+    const int src = (int)__builtin_ctzll(__ballot(bin >= 0));  // exactly one lane has it
+    const uint32_t b_sel = (uint32_t)__builtin_amdgcn_readlane(bin, src);
+    need -= __builtin_amdgcn_readlane((int)above_bin, src);
+    const uint32_t top = (b_sel << shift) + ((1u << shift) - 1u);  // bin's top offset
+    if (top < span) hi = lo + top;
+    lo += b_sel << shift;
+}
+
+// Top-k of a unit's nb scores in one wave (nb <= 64 * KMAX <= 2048).
+// Lane l holds the keys of blocks i*64 + l in registers.  The kb-th largest key
+// T is found by radix selection over value ranges: a pass histograms the keys
+// inside [lo, hi] into 256 bins and shrinks [lo, hi] to the bin holding the rank
+// still needed, resolving eight bits.  After the first pass the keys left in
+// range are usually few: up to 64 of them are compacted one per lane, so the
+// remaining passes cost a few instructions.  The winners (every key above T,
+// then keys equal to T in block order until kb) are recorded as LDS bitmaps
+// built from ballots (slot i's ballot is bitmap words 2i and 2i+1), and a
+// popcount prefix sum writes them in ascending block order.
+template <int KMAX>
+__device__ __forceinline__ void select_topk_wave(const float *sc, int nb, int top_k, int32_t *out,
+                                                 TopkSmem &sm) {
+    static_assert(KMAX <= 32, "one bitmap word per lane covers 2048 blocks");
+    uint32_t *hist = sm.hist, *cand = sm.cand, *above_bits = sm.above, *equal_bits = sm.equal;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int kb = min(top_k, nb);
+    uint32_t key[KMAX];
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {  // all loads in flight together
+        const int j = i * kWave + lane;
+        key[i] = j < nb ? __float_as_uint(load_relaxed(sc + j)) : 0u;
+    }
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {
+        const int j = i * kWave + lane;
+        key[i] = j < nb ? score_key(__uint_as_float(key[i])) : 0u;  // 0 = no key
+        kmin = j < nb ? min(kmin, key[i]) : kmin;
+        kmax = max(kmax, key[i]);
+    }
+    uint32_t lo = ~wave_max_u32(~kmin), hi = wave_max_u32(kmax);
+    int need = kb;  // rank of T among the keys inside [lo, hi], counted from the top
+    if (lo < hi) radix_pass(key, lo, hi, need, hist, lane);
+    if (lo < hi) {
+        // keys still in range, compacted one per lane when they fit
+        int m = 0;
+#pragma unroll
+        for (int i = 0; i < KMAX; ++i) m += __popcll(__ballot(key[i] - lo <= hi - lo));
+        if (m <= kWave) {
+            int base = 0;
+#pragma unroll
+            for (int i = 0; i < KMAX; ++i) {
+                const bool in = key[i] - lo <= hi - lo;
+                const uint64_t mask = __ballot(in);
+                const int pos = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                           (uint32_t)(mask >> 32),
+                                           __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+                if (in) cand[pos] = key[i];
+                base += __popcll(mask);
+            }
+            __builtin_amdgcn_wave_barrier();
+            const uint32_t one[1] = {lane < m ? cand[lane] : 0u};  // 0 is below any range
+            while (lo < hi) radix_pass(one, lo, hi, need, hist, lane);
+        } else {
+            while (lo < hi) radix_pass(key, lo, hi, need, hist, lane);
+        }
+    }
+    const uint32_t T = lo;
+    const int take_eq = need;  // keys equal to T to keep, lowest block index first
+    // bitmaps: word w covers blocks [32w, 32w + 32); slot i's ballot is words 2i, 2i+1
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {
+        const uint64_t a = __ballot(key[i] > T);
+        const uint64_t e = __ballot(key[i] == T);  // absent keys are 0 < T
+        if (lane == 0) {
+            above_bits[2 * i] = (uint32_t)a;
+            above_bits[2 * i + 1] = (uint32_t)(a >> 32);
+            equal_bits[2 * i] = (uint32_t)e;
+            equal_bits[2 * i + 1] = (uint32_t)(e >> 32);
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    uint32_t a = lane < 2 * KMAX ? above_bits[lane] : 0u;
+    uint32_t e = lane < 2 * KMAX ? equal_bits[lane] : 0u;
+    int e_before = (int)(wave_inclusive_scan((uint32_t)__popc(e)) - (uint32_t)__popc(e));
+    while (e && e_before < take_eq) {  // lowest-index equal keys first
+        const uint32_t bit = e & (0u - e);
+        a |= bit;
+        e ^= bit;
+        ++e_before;
+    }
+    int pos = (int)(wave_inclusive_scan((uint32_t)__popc(a)) - (uint32_t)__popc(a));
+    while (a) {
+        if (pos < kb) store_relaxed_i32(out + pos, lane * 32 + __builtin_ctz(a));
+        ++pos;
+        a &= a - 1u;
+    }
+    for (int i = kb + lane; i < top_k; i += kWave) store_relaxed_i32(out + i, -1);
+}
+
+// Top-k of a unit's nb scores by the whole workgroup.  Thread t holds the keys
+// of blocks i*256 + t in registers (at most KMAX each) for counting, and a
+// copy goes to LDS for the ordered passes.  The kb-th largest key T is found by
+// bisection over the 32-bit key space: every thread counts its keys at or above
+// the probe with plain compares, a DPP wave sum and one barrier give the total.
+// Then every key above T is kept plus the lowest-index keys equal to T; thread t
+// walks blocks [t*R, t*R + R) so that thread order is block order, and two
+// workgroup prefix sums place the winners in ascending order.
+template <int KMAX>
+__device__ __forceinline__ void select_topk_wg(const float *sc, int nb, int top_k, int32_t *out,
+                                               TopkSmem &sm) {
+    uint32_t *red = sm.red, *keys_lds = sm.keys;
+    int *scan_red = sm.scan_red;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int kb = min(top_k, nb);
+    uint32_t key[KMAX];
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {  // all loads in flight together
+        const int j = i * kThreads + tid;
+        key[i] = j < nb ? __float_as_uint(load_relaxed(sc + j)) : 0u;
+    }
+    uint32_t tmax = 0u;
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {
+        const int j = i * kThreads + tid;
+        if (j < nb) {
+            key[i] = score_key(__uint_as_float(key[i]));
+            keys_lds[j] = key[i];
+        } else {
+            key[i] = 0u;  // no key
+        }
+        tmax = max(tmax, key[i]);
+    }
+    int parity = 0;
+    auto wg_total = [&](uint32_t wave_value, bool take_max) {
+        if (lane == 0) red[parity * kWaves + wave] = wave_value;
+        __syncthreads();
+        uint32_t v = red[parity * kWaves];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) {
+            const uint32_t x = red[parity * kWaves + w];
+            v = take_max ? max(v, x) : v + x;
+        }
+        parity ^= 1;
+        return v;
+    };
+    auto count_ge = [&](uint32_t t) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int i = 0; i < KMAX; ++i) c += key[i] >= t ? 1u : 0u;  // absent keys are 0 < t
+        return (int)wg_total(wave_sum_u32(c), false);
+    };
+    // largest T in [1, max key] with #{key >= T} >= kb (valid keys are >= 1)
+    uint32_t lo = 1u, hi = wg_total(wave_max_u32(tmax), true);
+    while (lo < hi) {
+        const uint32_t mid = lo + (uint32_t)(((uint64_t)hi - lo + 1) >> 1);
+        if (count_ge(mid) >= kb) lo = mid;
+        else hi = mid - 1;
+    }
+    const uint32_t T = lo;
+    const int gt = T == 0xffffffffu ? 0 : count_ge(T + 1);
+    const int take_eq = kb - gt;  // keys equal to T to keep, lowest index first
+    const int R = (nb + kThreads - 1) / kThreads;
+    const int j0 = tid * R, j1 = min(nb, j0 + R);
+    int my_eq = 0;
+    for (int j = j0; j < j1; ++j) my_eq += keys_lds[j] == T ? 1 : 0;
+    const int eq_before = wg_exclusive_scan(my_eq, scan_red);
+    int my_sel = 0;
+    for (int j = j0, e = eq_before; j < j1; ++j) {
+        const uint32_t k = keys_lds[j];
+        if (k > T || (k == T && e++ < take_eq)) ++my_sel;
+    }
+    int pos = wg_exclusive_scan(my_sel, scan_red);
+    for (int j = j0, e = eq_before; j < j1; ++j) {
+        const uint32_t k = keys_lds[j];
+        if ((k > T || (k == T && e++ < take_eq)) && pos < kb) store_relaxed_i32(out + pos++, j);
+    }
+    for (int i = kb + tid; i < top_k; i += kThreads) store_relaxed_i32(out + i, -1);
+}
+
+// Selection of the unit's top-k blocks, by the workgroup that scored its last
+// chunk.  One wave handles up to 2048 blocks with no barrier; longer contexts
+// use the whole workgroup.
+__device__ __forceinline__ void select_topk(const float *sc, int nb, int top_k, int32_t *out,
+                                            TopkSmem &sm) {
+    const int tid = threadIdx.x;
+    if (min(top_k, nb) == nb) {  // every block is kept
+        for (int i = tid; i < top_k; i += kThreads) store_relaxed_i32(out + i, i < nb ? i : -1);
+        return;
+    }
+    if (nb > 32 * kWave) {
+        if (nb <= 16 * kThreads) select_topk_wg<16>(sc, nb, top_k, out, sm);
+        else select_topk_wg<32>(sc, nb, top_k, out, sm);
+        return;
+    }
+    if (tid >= kWave) return;
+    if (nb <= 8 * kWave) select_topk_wave<8>(sc, nb, top_k, out, sm);
+    else if (nb <= 16 * kWave) select_topk_wave<16>(sc, nb, top_k, out, sm);
+    else select_topk_wave<32>(sc, nb, top_k, out, sm);
+}
+
+// Sum over the 16 lanes of a DPP row (result in every lane of the row).
+__device__ __forceinline__ float row16_sum(float x) {
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               0xB1, 0xF, 0xF, false));  // quad xor 1
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               0x4E, 0xF, 0xF, false));  // quad xor 2
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               0x141, 0xF, 0xF, false));  // half mirror
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               0x140, 0xF, 0xF, false));  // mirror
+    return x;
+}
+
+// The per-lane part of a centroid row's dot product with the scaled mean
+// query (VPL floats per lane); the scan and the decode step's re-score of a
+// freshly updated centroid share it so that both give identical scores.
+template <int VPL>
+__device__ __forceinline__ float row_partial(const float (&qf)[VPL], const float4 (&cv)[VPL / 4]) {
+    float s = 0.f;
+#pragma unroll
+    for (int v = 0; v < VPL / 4; ++v)
+        s += qf[4 * v] * cv[v].x + qf[4 * v + 1] * cv[v].y + qf[4 * v + 2] * cv[v].z +
+             qf[4 * v + 3] * cv[v].w;
+    return s;
+}
+
+// Scores one chunk of a unit's blocks into a.scores (and, inside a decode step,
+// first refreshes the centroids of the chunk's touched pages).  Returns true in
+// the workgroup that completed the unit's last chunk, which must then select;
+// nb receives the unit's block count.
+template <typename T, int D>
+__device__ __forceinline__ bool score_chunk(const SelectArgs &a, int unit, int c, ScoreSmem &sm,
+                                            float *crow, int &nb_out) {
+    constexpr int LPR = 16;                       // lanes per centroid row: one DPP row
+    constexpr int VPL = D / LPR;                  // floats per lane per row (8 or 4)
+    constexpr int RPI = kWave / LPR;              // rows per wave per load step
+    constexpr int ROWS = kWaves * RPI * kUnroll;  // rows per workgroup stage
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int b = unit / a.Hkv, g = unit % a.Hkv;
+    const int r = a.Hq / a.Hkv;
+    int32_t *out = a.indices + (size_t)unit * a.top_k;
+
+    const int L = a.seq_lens[b];
+    if (L < 1 || L > a.max_blocks * kPage) {
+        if (c == 0) {
+            for (int i = tid; i < a.top_k; i += kThreads) store_relaxed_i32(out + i, -1);
+            if (tid == 0) flag_error(a.err, kErrSeqLen);
+        }
+        return false;
+    }
+    const int nb = (L + kPage - 1) / kPage;
+    const int nchunks = (nb + a.chunk - 1) / a.chunk;
+    if (c >= nchunks) return false;
+    const int j0 = c * a.chunk, n = min(nb, j0 + a.chunk) - j0;
+
+    // setup in one round trip: the group's queries and the chunk's page ids
+    const T *qp = static_cast<const T *>(a.q) + ((size_t)b * a.Hq + (size_t)g * r) * D;
+    for (int i = tid; i < r * D; i += kThreads) sm.qraw[i] = load_q<T>(qp + i);
+    for (int i = tid; i < n; i += kThreads) {
+        int p = a.bt[(size_t)b * a.max_blocks + j0 + i];
+        if (p < 0 || p >= a.num_pages) {
+            flag_error(a.err, kErrPage);
+            p = -1;
+        }
+        sm.pages[i] = p;
+    }
+    __syncthreads();
+    if (tid < D) {  // group mean query, pre-scaled
+        float s = 0.f;
+        for (int h = 0; h < r; ++h) s += sm.qraw[h * D + tid];
+        sm.qs[tid] = s * (a.scale / (float)r);
+    }
+    __syncthreads();
+
+    const int col = lane % LPR, rsub = lane / LPR;
+    float qf[VPL];
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) qf[e] = sm.qs[col * VPL + e];
+    // Loads are unconditional so that the next stage stays in flight while the
+    // current one is reduced: rows past the chunk re-read its last row and an
+    // invalid page reads page 0; neither result is kept.
+    typedef float4 Row[VPL / 4];
+    auto issue = [&](Row (&cv)[kUnroll], int base) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int row = min(base + u * kWaves * RPI + wave * RPI + rsub, n - 1);
+            const int p = max(sm.pages[row], 0);
+            const float4 *src = reinterpret_cast<const float4 *>(
+                a.cent + ((size_t)p * a.Hkv + g) * D + col * VPL);
+#pragma unroll
+            for (int v = 0; v < VPL / 4; ++v) cv[u][v] = src[v];
+        }
+    };
+    auto reduce = [&](const Row (&cv)[kUnroll], int base) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int row = base + u * kWaves * RPI + wave * RPI + rsub;
+            const float s = row16_sum(row_partial<VPL>(qf, cv[u]));
+            if (col == 0 && row < n) sm.sc[row] = sm.pages[row] >= 0 ? s : -INFINITY;
+        }
+    };
+    Row ca[kUnroll], cb[kUnroll];
+    issue(ca, 0);
+    for (int base = 0;;) {
+        issue(cb, base + ROWS);
+        reduce(ca, base);
+        base += ROWS;
+        if (base >= n) break;
+        issue(ca, base + ROWS);
+        reduce(cb, base);
+        base += ROWS;
+        if (base >= n) break;
+    }
+
+    // decode step: pages touched since the last step get their centroid
+    // recomputed from the keys, stored for later steps, and re-scored here (one
+    // wave per touched page; crow is the wave's LDS row)
+    if (a.first_pos) {
+        const int fp = a.first_pos[b];
+        if (fp >= 0 && fp < L) {
+            for (int j = max(j0, fp / kPage) + wave; j < j0 + n; j += kWaves) {
+                const int page = sm.pages[j - j0];
+                if (page < 0) continue;
+                const int v = min(kPage, L - j * kPage);
+                float *row_lds = crow + wave * D;
+                block_centroid<T, D>(static_cast<const T *>(a.k_cache) +
+                                         ((size_t)page * a.Hkv + g) * kPage * D,
+                                     v, a.cent_out + ((size_t)page * a.Hkv + g) * D, row_lds, lane);
+                __builtin_amdgcn_wave_barrier();
+                Row cv;
+#pragma unroll
+                for (int vv = 0; vv < VPL / 4; ++vv)
+                    cv[vv] = reinterpret_cast<const float4 *>(row_lds + col * VPL)[vv];
+                const float s = row16_sum(row_partial<VPL>(qf, cv));
+                if (lane == 0) sm.sc[j - j0] = s;
+                __builtin_amdgcn_wave_barrier();
+            }
+        }
+    }
+    __syncthreads();
+    float *sc = a.scores + (size_t)unit * a.max_blocks;
+    for (int i = tid; i < n; i += kThreads) store_relaxed(sc + j0 + i, sm.sc[i]);
+    nb_out = nb;
+    return arrive_last(&a.counters[unit], (uint32_t)nchunks, sm.flag);
+}
+
+}  // namespace sel
+}  // namespace btk
