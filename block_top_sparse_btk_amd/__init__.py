@@ -75,6 +75,8 @@ def _lib():
         lib.btk_sparse_attend.argtypes = [P, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
         lib.btk_dense_attend.restype = st
         lib.btk_dense_attend.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.btk_decode_step.restype = st
+        lib.btk_decode_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
         _LIB = lib
     return _LIB
 
@@ -251,6 +253,35 @@ def btk_dense_attend(q, k_cache, v_cache, block_table, seq_lens, workspace, out=
                                  _stream(dev))
     _check(st, "btk_dense_attend")
     return out
+
+
+def btk_decode_step(q, k_cache, v_cache, block_table, seq_lens, centroids, top_k, workspace,
+                    first_pos=None, indices=None, out=None, lse=None, sm_scale: float = 0.0,
+                    problem: Optional[btk_problem_t] = None):
+    """S1 (touched pages) + S2 + S3 + S4 in one launch; returns (out, indices)."""
+    dev = q.device
+    problem = problem or make_problem(q, k_cache, block_table, sm_scale)
+    out = torch.empty_like(q) if out is None else out
+    if indices is None:
+        indices = torch.empty((problem.batch, problem.num_kv_heads, int(top_k)), dtype=torch.int32,
+                              device=dev)
+    _check_shapes(problem, q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
+                  seq_lens=seq_lens, centroids=centroids, indices=indices, out=out, lse=lse,
+                  first_pos=first_pos, top_k=top_k)
+    fp = _dev(first_pos, "first_pos", torch.int32, dev) if first_pos is not None else None
+    lp = _dev(lse, "lse", torch.float32, dev) if lse is not None else None
+    st = _lib().btk_decode_step(ctypes.byref(problem), _dev(q, "q", None, dev),
+                                _dev(k_cache, "k_cache", q.dtype, dev),
+                                _dev(v_cache, "v_cache", q.dtype, dev),
+                                _dev(block_table, "block_table", torch.int32, dev),
+                                _dev(seq_lens, "seq_lens", torch.int32, dev), fp,
+                                _dev(centroids, "centroids", torch.float32, dev), int(top_k),
+                                _dev(indices, "indices", torch.int32, dev),
+                                _dev(out, "out", q.dtype, dev), lp,
+                                _dev(workspace, "workspace", torch.uint8, dev), workspace.numel(),
+                                _stream(dev))
+    _check(st, "btk_decode_step")
+    return out, indices
 
 
 def sparse_decode_step(q, k_cache, v_cache, block_table, seq_lens, centroids, top_k, workspace,

@@ -62,7 +62,9 @@ WorkspaceLayout workspace_layout(const Dims &d, int top_k) {
     w.att_counters = w.sel_counters + align256(units * sizeof(uint32_t));
     w.scores = w.att_counters + align256(units * sizeof(uint32_t));
     w.partials = w.scores + align256(units * d.max_blocks * sizeof(float));
-    w.total = w.partials + align256(units * nsplit * row * sizeof(float));
+    w.ready = w.partials + align256(units * nsplit * row * sizeof(float));
+    w.queue = w.ready + align256(units * sizeof(uint32_t));
+    w.total = w.queue + 256;
     return w;
 }
 
@@ -163,6 +165,33 @@ btk_status_t btk_dense_attend(const btk_problem_t *problem, const void *q, const
                                          reinterpret_cast<float *>(ws + w.partials),
                                          reinterpret_cast<uint32_t *>(ws + w.att_counters),
                                          reinterpret_cast<uint32_t *>(ws), (hipStream_t)stream));
+}
+
+btk_status_t btk_decode_step(const btk_problem_t *problem, const void *q, const void *k_cache,
+                             const void *v_cache, const int32_t *block_table,
+                             const int32_t *seq_lens, const int32_t *first_pos, float *centroids,
+                             int32_t top_k, int32_t *indices, void *out, float *lse,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+    btk::Dims d;
+    btk_status_t st = check_problem(problem, &d);
+    if (st != BTK_OK) return st;
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !centroids || !indices || !out)
+        return BTK_ERR_NULL;
+    if (!top_k_ok(top_k)) return BTK_ERR_SHAPE;
+    if (d.B > btk::kMaxStepBatch) return BTK_ERR_UNSUPPORTED;
+    const btk::WorkspaceLayout w = btk::workspace_layout(d, top_k);
+    if (!workspace || workspace_bytes < w.total) return BTK_ERR_WORKSPACE;
+    char *ws = static_cast<char *>(workspace);
+    const btk::SelectPlan sp = btk::plan_select(d);
+    const btk::AttendPlan ap = btk::plan_attend(d, top_k, false);
+    return hip_status(btk::launch_decode_step(
+        d, sp, ap, q, k_cache, v_cache, block_table, seq_lens, first_pos, centroids, top_k,
+        indices, reinterpret_cast<float *>(ws + w.scores), out, lse,
+        reinterpret_cast<float *>(ws + w.partials),
+        reinterpret_cast<uint32_t *>(ws + w.sel_counters),
+        reinterpret_cast<uint32_t *>(ws + w.att_counters),
+        reinterpret_cast<uint32_t *>(ws + w.ready), reinterpret_cast<uint32_t *>(ws + w.queue),
+        reinterpret_cast<uint32_t *>(ws), (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -13,6 +13,7 @@ constexpr int kWave = 64;
 constexpr int kPage = 16;           // tokens per page (block); all kernels assume it
 constexpr int kMaxBlocksPerSeq = 8192;  // select holds one key per block in LDS
 constexpr int kMaxGroup = 16;       // query heads per KV head: MFMA tile rows
+constexpr int kMaxStepBatch = 1024; // decode step: per-sequence item prefix kept in LDS
 
 // error bits in workspace word 0
 constexpr uint32_t kErrSeqLen = 1u;
@@ -118,8 +119,10 @@ AttendPlan plan_attend(const Dims &d, int list_len_max, bool dense);
 //   attend counters            B*Hkv uint32
 //   scores scratch             B*Hkv*max_blocks float
 //   attend partials            B*Hkv*nsplit_max*(r*D + 2r) float (max of sparse, dense)
+//   ready flags                B*Hkv uint32 (decode step)
+//   queue                      2 uint32 (decode step)
 struct WorkspaceLayout {
-    size_t sel_counters, att_counters, scores, partials, total;
+    size_t sel_counters, att_counters, scores, partials, ready, queue, total;
 };
 WorkspaceLayout workspace_layout(const Dims &d, int top_k);
 
@@ -139,5 +142,14 @@ hipError_t launch_attend(const Dims &d, const AttendPlan &plan, bool dense, cons
                          const int32_t *seq_lens, const int32_t *indices, int top_k, void *out,
                          float *lse, float *partials, uint32_t *counters, uint32_t *err,
                          hipStream_t stream);
+
+hipError_t launch_decode_step(const Dims &d, const SelectPlan &sp, const AttendPlan &ap,
+                              const void *q, const void *k_cache, const void *v_cache,
+                              const int32_t *block_table, const int32_t *seq_lens,
+                              const int32_t *first_pos, float *centroids, int top_k,
+                              int32_t *indices, float *scores, void *out, float *lse,
+                              float *partials, uint32_t *sel_counters, uint32_t *att_counters,
+                              uint32_t *ready, uint32_t *queue, uint32_t *err,
+                              hipStream_t stream);
 
 }  // namespace btk

@@ -24,7 +24,8 @@
  *    an out-of-range page id, length or index is skipped, and, where the call
  *    has a workspace, sets a sticky bit in workspace word 0 (bit 0: a length
  *    outside [1, max_blocks_per_seq * page_size]; bit 1: a page id outside
- *    [0, num_pages); bit 2: a block index outside [0, n_b) or repeated).
+ *    [0, num_pages); bit 2: a block index outside [0, n_b); bit 3: a decode step's wait for a
+ *    unit's selection gave up, which no valid call is expected to reach).
  *    Results for such inputs are unspecified.
  *
  * Notation: B = batch, Hq / Hkv = query / KV heads, r = Hq / Hkv (the query
@@ -164,6 +165,23 @@ btk_status_t btk_dense_attend(const btk_problem_t *problem, const void *q, const
                               const void *v_cache, const int32_t *block_table,
                               const int32_t *seq_lens, void *out, float *lse, void *workspace,
                               size_t workspace_bytes, void *stream);
+
+/* One whole decode step in a single launch: S1 for the touched pages (as
+ * btk_centroid_update with first_pos; none when first_pos is NULL), then S2+S3
+ * (as btk_select) and S4 (as btk_sparse_attend), with results identical to
+ * those three calls.  A persistent kernel takes scoring and attention work from
+ * a queue in the workspace; the attention of a unit starts once its selection
+ * is published, so the selection's latency hides behind other units' work.
+ * (Pith review, "What carries the argument"; the single-launch form is this
+ * library's own design.)
+ *   centroids  in/out   indices out [B][Hkv][top_k]   out/lse out as btk_sparse_attend
+ *   batch      <= 1024 (BTK_ERR_UNSUPPORTED beyond; the separate calls have no such limit)
+ *   workspace  btk_workspace_bytes(problem, top_k), zero-filled once, as above. */
+btk_status_t btk_decode_step(const btk_problem_t *problem, const void *q, const void *k_cache,
+                             const void *v_cache, const int32_t *block_table,
+                             const int32_t *seq_lens, const int32_t *first_pos, float *centroids,
+                             int32_t top_k, int32_t *indices, void *out, float *lse,
+                             void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

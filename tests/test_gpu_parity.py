@@ -332,3 +332,63 @@ def test_decode_step_replayed_from_a_graph_matches_eager():
         btk.btk_select(d.q, cent, d.block_table, d.seq_lens, bt.top_k, ws, problem=prob)
         torch.cuda.synchronize()
     assert btk.workspace_error_bits(ws) == 0
+
+
+# ------------------------------------------------------------------ single-launch decode step
+
+STEP_CASES = [("config1", dict(cfg=1)), ("config2", dict(cfg=2)), ("config3", dict(cfg=3)),
+              ("config4", dict(cfg=4)), ("config5-8k", dict(cfg=5, context=8192)),
+              ("config5-64k", dict(cfg=5, context=65536)),
+              ("ragged-small", dict(kw=dict(batch=5, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                                            seq_lens=[1, 17, 300, 5000, 33], top_k=12, seed=31))),
+              ("d64-group1", dict(kw=dict(batch=3, num_q_heads=4, num_kv_heads=4, head_dim=64,
+                                          seq_lens=[100, 999, 64], top_k=5, seed=32))),
+              ("fp32-d128", dict(kw=dict(batch=2, num_q_heads=6, num_kv_heads=2, head_dim=128,
+                                         seq_lens=[333, 1000], top_k=6, seed=33,
+                                         dtype=torch.float32)))]
+
+
+@pytest.mark.parametrize("label,spec", STEP_CASES, ids=[c[0] for c in STEP_CASES])
+def test_decode_step_equals_separate_calls_and_oracle(label, spec):
+    if "cfg" in spec:
+        bt = _workload(spec["cfg"], spec.get("context"))
+    else:
+        bt = synth.make_batch(name=label, **spec["kw"])
+    _say(f"[step] {label}")
+    d = bt.to(DEV)
+    prob = btk.make_problem(d.q, d.k_cache, d.block_table)
+    k = bt.top_k
+    first = (d.seq_lens - 1).to(torch.int32)
+    full = oracle.centroids(bt.k_cache, bt.block_table, bt.seq_lens)
+    stale = full.clone()
+    for b in range(bt.batch):  # the newest token's page is stale before the step
+        stale[int(bt.block_table[b, (int(bt.seq_lens[b]) - 1) // 16])] = float("nan")
+    # separate calls
+    ws1 = btk.new_workspace(prob, k, DEV)
+    c1 = stale.to(DEV)
+    lse1 = torch.empty((bt.batch, bt.num_q_heads), device=DEV)
+    out1, idx1 = btk.sparse_decode_step(d.q, d.k_cache, d.v_cache, d.block_table, d.seq_lens, c1,
+                                        k, ws1, first_pos=first, lse=lse1, problem=prob)
+    # one launch, three times in a row on one workspace
+    ws2 = btk.new_workspace(prob, k, DEV)
+    results = []
+    for rep in range(3):
+        c2 = stale.to(DEV)
+        lse2 = torch.empty_like(lse1)
+        out2, idx2 = btk.btk_decode_step(d.q, d.k_cache, d.v_cache, d.block_table, d.seq_lens, c2,
+                                         k, ws2, first_pos=first, lse=lse2, problem=prob)
+        torch.cuda.synchronize()
+        results.append((out2.cpu(), idx2.cpu(), lse2.cpu(), c2.cpu()))
+    torch.cuda.synchronize()
+    assert btk.workspace_error_bits(ws1) == 0 and btk.workspace_error_bits(ws2) == 0
+    for out2, idx2, lse2, c2 in results:
+        assert torch.equal(idx2, idx1.cpu())
+        assert torch.equal(out2, out1.cpu())
+        assert torch.equal(lse2, lse1.cpu())
+        assert torch.equal(c2, c1.cpu())
+    # and against the oracle
+    assert max_abs(results[0][3], full) <= CENTROID_TOL
+    ora = oracle.sparse_step(bt.q, bt.k_cache, bt.v_cache, bt.block_table, bt.seq_lens, k)
+    st = check_indices(results[0][1], ora["indices"], ora["scores"], bt.seq_lens, k)
+    check_outputs(results[0][0], ora["out"], bt.dtype, st["equal_mask"], bt.group)
+    check_lse(results[0][2], ora["lse"], bt.dtype, st["equal_mask"], bt.group)
