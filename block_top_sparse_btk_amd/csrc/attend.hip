@@ -50,13 +50,20 @@ AttendPlan plan_attend(const Dims &d, int list_len_max, bool dense) {
     if (dense) {
         p.bps = 128;  // 32 blocks (256 KiB of bf16 K+V at D=128) per wave
     } else {
-        // about 512 workgroups, at least two blocks per wave
-        p.bps = 64;
-        while (p.bps > 8 && units * (size_t)nsplit(p.bps) < 512 &&
-               nsplit(p.bps / 2) * r <= kMaxSplitHeads)
-            p.bps /= 2;
+        // about 256 workgroups (whole lists where that gives enough of them:
+        // a split costs a round of partial stores and loads), each wave with
+        // at least two blocks when the list allows it and at most 64, and the
+        // list spread evenly over the four waves of a split
+        const int want = (int)((256 + units - 1) / units);
+        int ns = want < list_len_max / 8 ? want : list_len_max / 8;
+        if (ns < 1) ns = 1;
+        if (ns < (list_len_max + 4 * kWave - 1) / (4 * kWave))
+            ns = (list_len_max + 4 * kWave - 1) / (4 * kWave);
+        p.bps = (list_len_max + ns - 1) / ns;
+        p.bps = (p.bps + kWaves - 1) / kWaves * kWaves;
     }
-    while (nsplit(p.bps) * r > kMaxSplitHeads && p.bps < 4 * kWave) p.bps *= 2;
+    while (nsplit(p.bps) * r > kMaxSplitHeads && p.bps < 4 * kWave)
+        p.bps = 2 * p.bps < 4 * kWave ? 2 * p.bps : 4 * kWave;
     p.nsplit_max = nsplit(p.bps);
     return p;
 }
@@ -68,7 +75,7 @@ hipError_t launch_attend(const Dims &d, const AttendPlan &plan, bool dense, cons
                          hipStream_t stream) {
     AttendArgs a{q, k_cache, v_cache, block_table, seq_lens, indices, out, lse, partials,
                  counters, err, d.Hq, d.Hkv, d.num_pages, d.max_blocks, top_k, plan.bps,
-                 plan.nsplit_max, d.sm_scale * 1.44269504088896340736f};
+                 plan.nsplit_max, d.sm_scale * 1.44269504088896340736f, nullptr};
     if (d.dtype == 0)
         return d.D == 128 ? launch_dtype<uint16_t, 128>(d, plan, dense, a, stream)
                           : launch_dtype<uint16_t, 64>(d, plan, dense, a, stream);

@@ -23,11 +23,14 @@
 // lane reads 16 contiguous bytes per K instruction.
 // Online softmax runs per group of G blocks in the base-2 domain with the
 // scale folded in; the P fed to the bf16 product is rounded to bf16, while the
-// normaliser and the log-sum-exp sum the unrounded weights.  Blocks are double-buffered:
-// the loads of the next group are in flight while the current one is computed.
+// normaliser and the log-sum-exp sum the unrounded weights.  Blocks are
+// double-buffered: the loads of the next group are in flight while the current
+// one is computed.
 // Waves merge through LDS; splits merge through the workspace in the
 // workgroup that finishes last (a counter per unit, see arrive_last).
 #pragma once
+#include <type_traits>
+
 #include "btk_internal.h"
 
 namespace btk {
@@ -186,11 +189,22 @@ struct AttendArgs {
     uint32_t *counters, *err;
     int Hq, Hkv, num_pages, max_blocks, top_k, bps, nsplit_max;
     float scale_log2;
-    uint32_t *ready;  // decode step only: per-unit "selection published" flags
+    // decode step only (NULL otherwise): the selection as published inside the
+    // launch, [units][top_k] words (tag << 32 | block index); an entry is valid
+    // once its tag equals the launch's own
+    const uint64_t *tagged;
 };
 
 // Spin bound of the decode step's wait for a unit's selection (~0.1 s).
 constexpr uint32_t kReadySpinLimit = 1u << 22;
+
+// K and V fragments of N blocks (one pipeline stage).
+template <typename F, int N>
+struct Stage {
+    static constexpr int kN = N;
+    typename F::KFrag k[N];
+    typename F::VFrag v[N];
+};
 
 template <typename T>
 __device__ __forceinline__ void store_out(T *p, float x);
@@ -204,15 +218,13 @@ __device__ __forceinline__ void store_out<float>(float *p, float x) {
 }
 
 // One (unit, split) item: attention of the unit's query group over its share of
-// the block list, kG blocks per pipeline stage.  (Continued:)
-//
-// the block list.  smem: the wave-merge / split-merge area (see launch sizing);
-// is_last: one LDS word.  Inside a decode step (a.ready set) the item first
-// waits until the unit's selection is published and reads the indices with
-// agent-coherent loads; the unit's last item re-arms the flag.
+// the block list, kG blocks per pipeline stage.  smem: the wave-merge / split-merge area (see launch
+// sizing); is_last: one LDS word.  Inside a decode step (a.tagged set) each wave
+// reads its entries of the unit's published selection, waiting (bounded) until
+// all of them carry the launch's tag.
 template <typename T, int D, bool DENSE, int kG>
 __device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int split, float *smem,
-                                            int *is_last_p) {
+                                            int *is_last_p, uint32_t tag = 0u) {
     using F = Mfma<T, D>;
     constexpr int NV = F::NV;
     int &is_last = *is_last_p;
@@ -220,6 +232,23 @@ __device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int s
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int b = unit / a.Hkv, g = unit % a.Hkv;
     const int r = a.Hq / a.Hkv;
+    // a sparse list has top_k entries whatever the length, so its entries are
+    // requested together with the length
+    const int per_wave = a.bps / kWaves;
+    int cnt = 0, w0 = 0;
+    uint64_t entry = 0;
+    if (!DENSE) {
+        const int i0 = split * a.bps, i1 = min(a.top_k, i0 + a.bps);
+        w0 = i0 + wave * per_wave;
+        cnt = max(0, min(i1, w0 + per_wave) - w0);
+        if (lane < cnt) {
+            if (a.tagged)
+                entry = __hip_atomic_load(a.tagged + (size_t)unit * a.top_k + w0 + lane,
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else
+                entry = (uint32_t)a.indices[(size_t)unit * a.top_k + w0 + lane];
+        }
+    }
     const int L = a.seq_lens[b];
     if (L < 1 || L > a.max_blocks * kPage) {
         if (split == 0 && tid == 0) flag_error(a.err, kErrSeqLen);
@@ -229,30 +258,31 @@ __device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int s
     const int len = DENSE ? nb : a.top_k;
     const int nsplit = (len + a.bps - 1) / a.bps;
     if (split >= nsplit) return;
-    if (!DENSE && a.ready) {  // decode step: wait for the unit's selection
-        if (tid == 0) {
-            uint32_t spins = 0;
-            while (__hip_atomic_load(&a.ready[unit], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                   0u) {
-                __builtin_amdgcn_s_sleep(2);
-                if (++spins > kReadySpinLimit) {  // never expected: report, do not hang
-                    flag_error(a.err, kErrTimeout);
-                    break;
-                }
+    if (DENSE) {
+        const int i0 = split * a.bps, i1 = min(len, i0 + a.bps);
+        w0 = i0 + wave * per_wave;
+        cnt = max(0, min(i1, w0 + per_wave) - w0);
+    } else if (a.tagged) {
+        // decode step: wait until this wave's entries are published
+        uint32_t spins = 0;
+        while (__ballot(lane < cnt && (uint32_t)(entry >> 32) != tag)) {
+            if (++spins > kReadySpinLimit) {  // never expected: report, do not hang
+                if (lane == 0) flag_error(a.err, kErrTimeout);
+                if ((uint32_t)(entry >> 32) != tag) entry = 0xffffffffu;  // skipped
+                break;
             }
+            __builtin_amdgcn_s_sleep(2);
+            if (lane < cnt && (uint32_t)(entry >> 32) != tag)
+                entry = __hip_atomic_load(a.tagged + (size_t)unit * a.top_k + w0 + lane,
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        __syncthreads();
     }
-    const int i0 = split * a.bps, i1 = min(len, i0 + a.bps);
-    const int per_wave = a.bps / kWaves;
-    const int w0 = i0 + wave * per_wave;
-    const int cnt = max(0, min(i1, w0 + per_wave) - w0);
 
     // lane m < cnt holds page id and valid tokens of this wave's m-th entry
     // (page -1 and 0 tokens for a skipped or invalid entry)
     int my_page = -1, my_v = 0;
     if (lane < cnt) {
-        int j = DENSE ? (w0 + lane) : load_relaxed_i32(a.indices + (size_t)unit * a.top_k + w0 + lane);
+        int j = DENSE ? (w0 + lane) : (int32_t)(uint32_t)entry;
         if (!DENSE && j >= nb) {
             flag_error(a.err, kErrIndex);
             j = -1;
@@ -280,30 +310,28 @@ __device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int s
 #pragma unroll
     for (int n = 0; n < NV; ++n) o[n] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-    struct Stage {
-        typename F::KFrag k[kG];
-        typename F::VFrag v[kG];
-    };
     // Loads and their consumers are unconditional, so the compiler can keep
     // the next stage in flight (precise vmcnt) while the current one computes:
     // a slot past the wave's list re-reads its last entry (a cache hit) and an
     // invalid entry reads page 0; both are masked to zero weight below.
     const int safe_page = my_page >= 0 ? my_page : 0;
-    auto issue = [&](Stage &s, int m0) {
+    auto issue = [&](auto &s, int m0) {
+        constexpr int kN = std::remove_reference_t<decltype(s)>::kN;
 #pragma unroll
-        for (int u = 0; u < kG; ++u) {
+        for (int u = 0; u < kN; ++u) {
             const int m = min(m0 + u, cnt - 1);
             const int page = __builtin_amdgcn_readlane(safe_page, m);
             F::load_k(s.k[u], kbase + page * page_stride, lane);
             F::load_v(s.v[u], vbase + page * page_stride, lane);
         }
     };
-    auto compute = [&](Stage &s, int m0) {
-        float sv[kG][4];
-        int vv[kG];
+    auto compute = [&](auto &s, int m0) {
+        constexpr int kN = std::remove_reference_t<decltype(s)>::kN;
+        float sv[kN][4];
+        int vv[kN];
         float gmax = -INFINITY;
 #pragma unroll
-        for (int u = 0; u < kG; ++u) {
+        for (int u = 0; u < kN; ++u) {
             const int m = min(m0 + u, cnt - 1);
             // valid tokens of this slot, 0 for a repeated or invalid entry (wave-uniform)
             vv[u] = m0 + u < cnt ? __builtin_amdgcn_readlane(my_v, m) : 0;
@@ -330,7 +358,7 @@ __device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int s
         }
         m_run = m_new;
 #pragma unroll
-        for (int u = 0; u < kG; ++u) {
+        for (int u = 0; u < kN; ++u) {
             float p[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -344,7 +372,7 @@ __device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int s
     };
 
     if (cnt > 0) {
-        Stage sa, sb;
+        Stage<F, kG> sa, sb;
         issue(sa, 0);
         for (int m0 = 0;;) {
             issue(sb, m0 + kG);
@@ -410,16 +438,10 @@ __device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int s
             }
         }
     }
-    if (nsplit == 1) {
-        if (!DENSE && a.ready && tid == 0)
-            __hip_atomic_store(&a.ready[unit], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return;
-    }
+    if (nsplit == 1) return;
 
     // ---- the last split of this unit merges all splits
     if (!arrive_last(&a.counters[unit], (uint32_t)nsplit, &is_last)) return;
-    if (!DENSE && a.ready && tid == 0)  // every split has read the selection
-        __hip_atomic_store(&a.ready[unit], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // split weights: every (split, head) max and normaliser fetched at once into
     // LDS (reusing the wave-merge area), then w[s][h] = exp2(m_s - M_h)
     float *wm = smem;                  // [nsplit][r] split maxima, then weights

@@ -19,7 +19,7 @@ constexpr int kMaxStepBatch = 1024; // decode step: per-sequence item prefix kep
 constexpr uint32_t kErrSeqLen = 1u;
 constexpr uint32_t kErrPage = 2u;
 constexpr uint32_t kErrIndex = 4u;
-constexpr uint32_t kErrTimeout = 8u;  // decode step: a unit's selection never arrived
+constexpr uint32_t kErrTimeout = 8u;  // decode step: a wait for published data gave up
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) short short4_t;
@@ -119,10 +119,10 @@ AttendPlan plan_attend(const Dims &d, int list_len_max, bool dense);
 //   attend counters            B*Hkv uint32
 //   scores scratch             B*Hkv*max_blocks float
 //   attend partials            B*Hkv*nsplit_max*(r*D + 2r) float (max of sparse, dense)
-//   ready flags                B*Hkv uint32 (decode step)
-//   queue                      2 uint32 (decode step)
+//   published selections       B*Hkv*top_k uint64 (decode step)
+//   queue                      3 uint32 (decode step)
 struct WorkspaceLayout {
-    size_t sel_counters, att_counters, scores, partials, ready, queue, total;
+    size_t sel_counters, att_counters, scores, partials, tagged, queue, total;
 };
 WorkspaceLayout workspace_layout(const Dims &d, int top_k);
 
@@ -149,7 +149,7 @@ hipError_t launch_decode_step(const Dims &d, const SelectPlan &sp, const AttendP
                               const int32_t *first_pos, float *centroids, int top_k,
                               int32_t *indices, float *scores, void *out, float *lse,
                               float *partials, uint32_t *sel_counters, uint32_t *att_counters,
-                              uint32_t *ready, uint32_t *queue, uint32_t *err,
+                              uint64_t *tagged, uint32_t *queue, uint32_t *err,
                               hipStream_t stream);
 
 }  // namespace btk

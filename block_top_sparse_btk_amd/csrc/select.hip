@@ -14,7 +14,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
     __shared__ int pages[kMaxChunk];
     __shared__ float sc_lds[kMaxChunk];
     __shared__ int is_last;
-    __shared__ uint32_t hist[256 + kWave], cand[kWave], above[kWave], equal[kWave];
+    __shared__ uint32_t hist[256 + kWave], cand[4 * kWave], above[kWave], equal[kWave];
     __shared__ uint32_t red[2 * kWaves];
     __shared__ int scan_red[kWaves];
     extern __shared__ uint32_t keys[];  // max_blocks words, long contexts only
@@ -22,11 +22,11 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
     TopkSmem tk{hist, cand, above, equal, red, scan_red, keys};
     const int unit = blockIdx.x / a.nchunk_max, c = blockIdx.x % a.nchunk_max;
     int nb = 0;
-    if (!score_chunk<T, D>(a, unit, c, sm, nullptr, nb)) return;
+    if (!score_chunk<T, D, 4>(a, unit, c, sm, nullptr, nb)) return;
     // the selecting wave(s) take issue priority over scanning waves on the SIMD
     __builtin_amdgcn_s_setprio(3);
-    select_topk(a.scores + (size_t)unit * a.max_blocks, nb, a.top_k,
-                a.indices + (size_t)unit * a.top_k, tk);
+    select_topk(PlainScores{a.scores + (size_t)unit * a.max_blocks}, nb, a.top_k,
+                TopkOut{a.indices + (size_t)unit * a.top_k, nullptr, 0u}, tk);
 }
 
 template <typename T, int D>
@@ -59,7 +59,7 @@ hipError_t launch_select(const Dims &d, const SelectPlan &plan, const void *q,
                          uint32_t *counters, uint32_t *err, hipStream_t stream) {
     SelectArgs a{q, centroids, block_table, seq_lens, indices, scores, counters, err,
                  d.Hq, d.Hkv, d.num_pages, d.max_blocks, top_k, plan.chunk, plan.nchunk_max,
-                 d.sm_scale};
+                 d.sm_scale, nullptr, nullptr, nullptr};
     if (d.dtype == 0)
         return d.D == 128 ? launch<uint16_t, 128>(d, plan, a, stream)
                           : launch<uint16_t, 64>(d, plan, a, stream);

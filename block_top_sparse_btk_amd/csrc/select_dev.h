@@ -10,9 +10,11 @@
 // The r query heads of the group are folded into their mean on entry
 // (linearity: the mean of the heads' logits equals the logit of the mean query),
 // so each block costs one D-long dot product.  16 lanes (one DPP row) hold a
-// centroid row; loads run in two stages of four rows per lane so one stage is in
-// flight while the other is reduced; scores are staged in LDS and leave the
-// workgroup as contiguous stores.
+// centroid row; loads run in two stages of KU rows per lane so one stage is in
+// flight while the other is reduced (the stand-alone kernel takes KU = 4 to stay
+// at five waves per SIMD, the decode step, whose attention already sets two
+// waves per SIMD, KU = 8); scores are staged in LDS and leave the workgroup as
+// contiguous stores.
 //
 // Selection runs in the workgroup that finishes a unit's last chunk (a counter
 // per unit, see arrive_last), so it overlaps the scoring of later units.
@@ -25,7 +27,6 @@ namespace sel {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxChunk = 512;
-constexpr int kUnroll = 4;          // rows per lane per pipeline stage
 
 struct SelectArgs {
     const void *q;
@@ -57,12 +58,42 @@ struct ScoreSmem {
 // LDS used by the top-k selection.
 struct TopkSmem {
     uint32_t *hist;      // [256 + 64] radix bins + per-lane spare bins
-    uint32_t *cand;      // [64] compacted candidates
+    uint32_t *cand;      // [256] compacted candidates
     uint32_t *above;     // [64] bitmap words
     uint32_t *equal;     // [64]
     uint32_t *red;       // [2 * kWaves]
     int *scan_red;       // [kWaves]
     uint32_t *keys;      // [max_blocks] keys, workgroup-wide path only
+};
+
+// Where a selection goes: the caller's index row and, inside a decode step, the
+// same entries tagged with the launch's tag for the launch's own readers.
+struct TopkOut {
+    int32_t *idx;      // [top_k]
+    uint64_t *tagged;  // [top_k] or NULL
+    uint32_t tag;
+    __device__ __forceinline__ void put(int pos, int32_t j) const {
+        store_relaxed_i32(idx + pos, j);
+        if (tagged)
+            __hip_atomic_store(tagged + pos, ((uint64_t)tag << 32) | (uint32_t)j,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+};
+
+// Where the selecting workgroup reads a unit's scores from: fill() loads the
+// float bits of blocks j = i * stride + first (0 for j >= nb), all loads in
+// flight together.  The scores were stored by every chunk with store_relaxed
+// before it counted itself in (see arrive_last).
+struct PlainScores {
+    const float *sc;  // [nb]
+    template <int N>
+    __device__ __forceinline__ void fill(uint32_t (&bits)[N], int first, int stride, int nb) const {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int j = i * stride + first;
+            bits[i] = j < nb ? __float_as_uint(load_relaxed(sc + j)) : 0u;
+        }
+    }
 };
 
 template <typename T>
@@ -147,19 +178,9 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
 // histogram into 256 LDS bins of width 2^shift, locate the bin that holds the
 // key of rank `need` counted from the top, and shrink [lo, hi] to it.  Keys out
 // of range are counted in a per-lane spare bin, so the loop has no branches.
-template <int N>
-__device__ __forceinline__ void radix_pass(const uint32_t (&key)[N], uint32_t &lo, uint32_t &hi,
-                                           int &need, uint32_t *hist, int lane) {
-    const uint32_t span = hi - lo;
-    const int shift = max(0, 24 - __builtin_clz(span));  // (span >> shift) < 256
-    reinterpret_cast<uint4 *>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-        const uint32_t off = key[i] - lo;
-        atomicAdd(&hist[off <= span ? (off >> shift) : 256u + lane], 1u);
-    }
-    __builtin_amdgcn_wave_barrier();
+// The bin (of the 256 in hist) that holds the key of rank `need` counted from
+// the top; `need` becomes that key's rank inside the bin.  Wave-uniform.
+__device__ __forceinline__ uint32_t locate_bin(const uint32_t *hist, int &need, int lane) {
     const uint4 h = reinterpret_cast<const uint4 *>(hist)[lane];  // bins 4l .. 4l+3
     const uint32_t lane_sum = h.x + h.y + h.z + h.w;
     const uint32_t above_lane = wave_sum_u32(lane_sum) - wave_inclusive_scan(lane_sum);
@@ -175,36 +196,76 @@ __device__ __forceinline__ void radix_pass(const uint32_t (&key)[N], uint32_t &l
         acc += hv[e];
     }
     const int src = (int)__builtin_ctzll(__ballot(bin >= 0));  // exactly one lane has it
-    const uint32_t b_sel = (uint32_t)__builtin_amdgcn_readlane(bin, src);
     need -= __builtin_amdgcn_readlane((int)above_bin, src);
+    return (uint32_t)__builtin_amdgcn_readlane(bin, src);
+}
+
+template <int N>
+__device__ __forceinline__ void radix_pass(const uint32_t (&key)[N], uint32_t &lo, uint32_t &hi,
+                                           int &need, uint32_t *hist, int lane) {
+    const uint32_t span = hi - lo;
+    const int shift = max(0, 24 - __builtin_clz(span));  // (span >> shift) < 256
+    reinterpret_cast<uint4 *>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const uint32_t off = key[i] - lo;
+        atomicAdd(&hist[off <= span ? (off >> shift) : 256u + lane], 1u);
+    }
+    __builtin_amdgcn_wave_barrier();
+    const uint32_t b_sel = locate_bin(hist, need, lane);
     const uint32_t top = (b_sel << shift) + ((1u << shift) - 1u);  // bin's top offset
     if (top < span) hi = lo + top;
     lo += b_sel << shift;
+}
+
+// Number of the wave's keys inside [lo, hi] (wave-uniform).
+template <int N>
+__device__ __forceinline__ int count_in_range(const uint32_t (&key)[N], uint32_t lo, uint32_t hi) {
+    int m = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) m += __popcll(__ballot(key[i] - lo <= hi - lo));
+    return m;
+}
+
+// Writes the wave's keys inside [lo, hi] to cand[0 .. m), slot by slot.
+template <int N>
+__device__ __forceinline__ void compact(const uint32_t (&key)[N], uint32_t lo, uint32_t hi,
+                                        uint32_t *cand, int lane) {
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const bool in = key[i] - lo <= hi - lo;
+        const uint64_t mask = __ballot(in);
+        const int pos = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                   (uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+        if (in) cand[pos] = key[i];
+        base += __popcll(mask);
+    }
 }
 
 // Top-k of a unit's nb scores in one wave (nb <= 64 * KMAX <= 2048).
 // Lane l holds the keys of blocks i*64 + l in registers.  The kb-th largest key
 // T is found by radix selection over value ranges: a pass histograms the keys
 // inside [lo, hi] into 256 bins and shrinks [lo, hi] to the bin holding the rank
-// still needed, resolving eight bits.  After the first pass the keys left in
-// range are usually few: up to 64 of them are compacted one per lane, so the
-// remaining passes cost a few instructions.  The winners (every key above T,
+// still needed, resolving eight bits.  The first pass leaves about a hundred
+// keys in range at the usual score spreads (its top bins span whole binades):
+// up to 256 are compacted four per lane for the next, cheap passes, and once
+// at most 64 are left each lane counts the candidates above and at its own
+// key, which names T directly.  The winners (every key above T,
 // then keys equal to T in block order until kb) are recorded as LDS bitmaps
 // built from ballots (slot i's ballot is bitmap words 2i and 2i+1), and a
 // popcount prefix sum writes them in ascending block order.
-template <int KMAX>
-__device__ __forceinline__ void select_topk_wave(const float *sc, int nb, int top_k, int32_t *out,
-                                                 TopkSmem &sm) {
+template <int KMAX, typename Src>
+__device__ __forceinline__ void select_topk_wave(const Src &src, int nb, int top_k,
+                                                 const TopkOut &out, TopkSmem &sm) {
     static_assert(KMAX <= 32, "one bitmap word per lane covers 2048 blocks");
     uint32_t *hist = sm.hist, *cand = sm.cand, *above_bits = sm.above, *equal_bits = sm.equal;
     const int lane = threadIdx.x & (kWave - 1);
     const int kb = min(top_k, nb);
     uint32_t key[KMAX];
-#pragma unroll
-    for (int i = 0; i < KMAX; ++i) {  // all loads in flight together
-        const int j = i * kWave + lane;
-        key[i] = j < nb ? __float_as_uint(load_relaxed(sc + j)) : 0u;
-    }
+    src.fill(key, lane, kWave, nb);
     uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) {
@@ -217,27 +278,46 @@ __device__ __forceinline__ void select_topk_wave(const float *sc, int nb, int to
     int need = kb;  // rank of T among the keys inside [lo, hi], counted from the top
     if (lo < hi) radix_pass(key, lo, hi, need, hist, lane);
     if (lo < hi) {
-        // keys still in range, compacted one per lane when they fit
-        int m = 0;
-#pragma unroll
-        for (int i = 0; i < KMAX; ++i) m += __popcll(__ballot(key[i] - lo <= hi - lo));
-        if (m <= kWave) {
-            int base = 0;
-#pragma unroll
-            for (int i = 0; i < KMAX; ++i) {
-                const bool in = key[i] - lo <= hi - lo;
-                const uint64_t mask = __ballot(in);
-                const int pos = base + (int)__builtin_amdgcn_mbcnt_hi(
-                                           (uint32_t)(mask >> 32),
-                                           __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-                if (in) cand[pos] = key[i];
-                base += __popcll(mask);
-            }
+        int m = count_in_range(key, lo, hi);
+        while (lo < hi && m > 4 * kWave) {  // rare: keys bunched in one bin
+            radix_pass(key, lo, hi, need, hist, lane);
+            m = count_in_range(key, lo, hi);
+        }
+        if (lo < hi) {
+            // up to 256 keys left: four per lane, then passes over those
+            compact(key, lo, hi, cand, lane);
             __builtin_amdgcn_wave_barrier();
-            const uint32_t one[1] = {lane < m ? cand[lane] : 0u};  // 0 is below any range
-            while (lo < hi) radix_pass(one, lo, hi, need, hist, lane);
-        } else {
-            while (lo < hi) radix_pass(key, lo, hi, need, hist, lane);
+            uint32_t k4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) k4[e] = e * kWave + lane < m ? cand[e * kWave + lane] : 0u;
+            __builtin_amdgcn_wave_barrier();
+            while (lo < hi && m > kWave) {
+                radix_pass(k4, lo, hi, need, hist, lane);
+                m = count_in_range(k4, lo, hi);
+            }
+            if (lo < hi) {
+                // at most 64 keys left: every lane ranks its own against all
+                // of them (LDS broadcast reads); T is the one of rank `need`
+                compact(k4, lo, hi, cand, lane);
+                __builtin_amdgcn_wave_barrier();
+                const uint32_t mine = lane < m ? cand[lane] : 0u;
+                int gt = 0, ge = 0;
+                for (int t = 0; t < m; t += 4) {  // m is wave-uniform
+                    const uint4 c4 = reinterpret_cast<const uint4 *>(cand)[t / 4];
+                    const uint32_t cv[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if (t + e < m) {
+                            gt += cv[e] > mine ? 1 : 0;
+                            ge += cv[e] >= mine ? 1 : 0;
+                        }
+                    }
+                }
+                const int src_lane =
+                    (int)__builtin_ctzll(__ballot(lane < m && gt < need && ge >= need));
+                lo = (uint32_t)__builtin_amdgcn_readlane((int)mine, src_lane);
+                need -= __builtin_amdgcn_readlane(gt, src_lane);  // keys equal to T to take
+            }
         }
     }
     const uint32_t T = lo;
@@ -266,11 +346,11 @@ __device__ __forceinline__ void select_topk_wave(const float *sc, int nb, int to
     }
     int pos = (int)(wave_inclusive_scan((uint32_t)__popc(a)) - (uint32_t)__popc(a));
     while (a) {
-        if (pos < kb) store_relaxed_i32(out + pos, lane * 32 + __builtin_ctz(a));
+        if (pos < kb) out.put(pos, lane * 32 + __builtin_ctz(a));
         ++pos;
         a &= a - 1u;
     }
-    for (int i = kb + lane; i < top_k; i += kWave) store_relaxed_i32(out + i, -1);
+    for (int i = kb + lane; i < top_k; i += kWave) out.put(i, -1);
 }
 
 // Top-k of a unit's nb scores by the whole workgroup.  Thread t holds the keys
@@ -281,19 +361,15 @@ __device__ __forceinline__ void select_topk_wave(const float *sc, int nb, int to
 // Then every key above T is kept plus the lowest-index keys equal to T; thread t
 // walks blocks [t*R, t*R + R) so that thread order is block order, and two
 // workgroup prefix sums place the winners in ascending order.
-template <int KMAX>
-__device__ __forceinline__ void select_topk_wg(const float *sc, int nb, int top_k, int32_t *out,
-                                               TopkSmem &sm) {
+template <int KMAX, typename Src>
+__device__ __forceinline__ void select_topk_wg(const Src &src, int nb, int top_k,
+                                               const TopkOut &out, TopkSmem &sm) {
     uint32_t *red = sm.red, *keys_lds = sm.keys;
     int *scan_red = sm.scan_red;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int kb = min(top_k, nb);
     uint32_t key[KMAX];
-#pragma unroll
-    for (int i = 0; i < KMAX; ++i) {  // all loads in flight together
-        const int j = i * kThreads + tid;
-        key[i] = j < nb ? __float_as_uint(load_relaxed(sc + j)) : 0u;
-    }
+    src.fill(key, tid, kThreads, nb);
     uint32_t tmax = 0u;
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) {
@@ -348,30 +424,31 @@ __device__ __forceinline__ void select_topk_wg(const float *sc, int nb, int top_
     int pos = wg_exclusive_scan(my_sel, scan_red);
     for (int j = j0, e = eq_before; j < j1; ++j) {
         const uint32_t k = keys_lds[j];
-        if ((k > T || (k == T && e++ < take_eq)) && pos < kb) store_relaxed_i32(out + pos++, j);
+        if ((k > T || (k == T && e++ < take_eq)) && pos < kb) out.put(pos++, j);
     }
-    for (int i = kb + tid; i < top_k; i += kThreads) store_relaxed_i32(out + i, -1);
+    for (int i = kb + tid; i < top_k; i += kThreads) out.put(i, -1);
 }
 
 // Selection of the unit's top-k blocks, by the workgroup that scored its last
 // chunk.  One wave handles up to 2048 blocks with no barrier; longer contexts
 // use the whole workgroup.
-__device__ __forceinline__ void select_topk(const float *sc, int nb, int top_k, int32_t *out,
-                                            TopkSmem &sm) {
+template <typename Src>
+__device__ __forceinline__ void select_topk(const Src &src, int nb, int top_k,
+                                            const TopkOut &out, TopkSmem &sm) {
     const int tid = threadIdx.x;
     if (min(top_k, nb) == nb) {  // every block is kept
-        for (int i = tid; i < top_k; i += kThreads) store_relaxed_i32(out + i, i < nb ? i : -1);
+        for (int i = tid; i < top_k; i += kThreads) out.put(i, i < nb ? i : -1);
         return;
     }
     if (nb > 32 * kWave) {
-        if (nb <= 16 * kThreads) select_topk_wg<16>(sc, nb, top_k, out, sm);
-        else select_topk_wg<32>(sc, nb, top_k, out, sm);
+        if (nb <= 16 * kThreads) select_topk_wg<16>(src, nb, top_k, out, sm);
+        else select_topk_wg<32>(src, nb, top_k, out, sm);
         return;
     }
     if (tid >= kWave) return;
-    if (nb <= 8 * kWave) select_topk_wave<8>(sc, nb, top_k, out, sm);
-    else if (nb <= 16 * kWave) select_topk_wave<16>(sc, nb, top_k, out, sm);
-    else select_topk_wave<32>(sc, nb, top_k, out, sm);
+    if (nb <= 8 * kWave) select_topk_wave<8>(src, nb, top_k, out, sm);
+    else if (nb <= 16 * kWave) select_topk_wave<16>(src, nb, top_k, out, sm);
+    else select_topk_wave<32>(src, nb, top_k, out, sm);
 }
 
 // Sum over the 16 lanes of a DPP row (result in every lane of the row).
@@ -403,20 +480,32 @@ __device__ __forceinline__ float row_partial(const float (&qf)[VPL], const float
 // Scores one chunk of a unit's blocks into a.scores (and, inside a decode step,
 // first refreshes the centroids of the chunk's touched pages).  Returns true in
 // the workgroup that completed the unit's last chunk, which must then select;
-// nb receives the unit's block count.
-template <typename T, int D>
+// nb receives the unit's block count.  KU: rows per lane per pipeline stage
+// (two stages of 4 * 4 * KU rows are in flight).
+template <typename T, int D, int KU>
 __device__ __forceinline__ bool score_chunk(const SelectArgs &a, int unit, int c, ScoreSmem &sm,
                                             float *crow, int &nb_out) {
     constexpr int LPR = 16;                       // lanes per centroid row: one DPP row
     constexpr int VPL = D / LPR;                  // floats per lane per row (8 or 4)
     constexpr int RPI = kWave / LPR;              // rows per wave per load step
-    constexpr int ROWS = kWaves * RPI * kUnroll;  // rows per workgroup stage
+    constexpr int ROWS = kWaves * RPI * KU;       // rows per workgroup stage
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int b = unit / a.Hkv, g = unit % a.Hkv;
     const int r = a.Hq / a.Hkv;
     int32_t *out = a.indices + (size_t)unit * a.top_k;
+    const int j0 = c * a.chunk;
 
+    // setup in one round trip: the group's queries, the chunk's slice of the
+    // block-table row (entries past the sequence are read but never used), the
+    // length and the decode position
+    const T *qp = static_cast<const T *>(a.q) + ((size_t)b * a.Hq + (size_t)g * r) * D;
+    for (int i = tid; i < r * D; i += kThreads) sm.qraw[i] = load_q<T>(qp + i);
+    const int jn = min(a.chunk, a.max_blocks - j0);
+    for (int i = tid; i < jn; i += kThreads) sm.pages[i] = a.bt[(size_t)b * a.max_blocks + j0 + i];
     const int L = a.seq_lens[b];
+    const int fp = a.first_pos ? a.first_pos[b] : -1;
+    __syncthreads();
+
     if (L < 1 || L > a.max_blocks * kPage) {
         if (c == 0) {
             for (int i = tid; i < a.top_k; i += kThreads) store_relaxed_i32(out + i, -1);
@@ -427,20 +516,14 @@ __device__ __forceinline__ bool score_chunk(const SelectArgs &a, int unit, int c
     const int nb = (L + kPage - 1) / kPage;
     const int nchunks = (nb + a.chunk - 1) / a.chunk;
     if (c >= nchunks) return false;
-    const int j0 = c * a.chunk, n = min(nb, j0 + a.chunk) - j0;
-
-    // setup in one round trip: the group's queries and the chunk's page ids
-    const T *qp = static_cast<const T *>(a.q) + ((size_t)b * a.Hq + (size_t)g * r) * D;
-    for (int i = tid; i < r * D; i += kThreads) sm.qraw[i] = load_q<T>(qp + i);
-    for (int i = tid; i < n; i += kThreads) {
-        int p = a.bt[(size_t)b * a.max_blocks + j0 + i];
+    const int n = min(nb, j0 + a.chunk) - j0;
+    for (int i = tid; i < n; i += kThreads) {  // the entries this thread loaded
+        const int p = sm.pages[i];
         if (p < 0 || p >= a.num_pages) {
             flag_error(a.err, kErrPage);
-            p = -1;
+            sm.pages[i] = -1;
         }
-        sm.pages[i] = p;
     }
-    __syncthreads();
     if (tid < D) {  // group mean query, pre-scaled
         float s = 0.f;
         for (int h = 0; h < r; ++h) s += sm.qraw[h * D + tid];
@@ -456,9 +539,9 @@ __device__ __forceinline__ bool score_chunk(const SelectArgs &a, int unit, int c
     // current one is reduced: rows past the chunk re-read its last row and an
     // invalid page reads page 0; neither result is kept.
     typedef float4 Row[VPL / 4];
-    auto issue = [&](Row (&cv)[kUnroll], int base) {
+    auto issue = [&](Row (&cv)[KU], int base) {
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < KU; ++u) {
             const int row = min(base + u * kWaves * RPI + wave * RPI + rsub, n - 1);
             const int p = max(sm.pages[row], 0);
             const float4 *src = reinterpret_cast<const float4 *>(
@@ -467,15 +550,15 @@ __device__ __forceinline__ bool score_chunk(const SelectArgs &a, int unit, int c
             for (int v = 0; v < VPL / 4; ++v) cv[u][v] = src[v];
         }
     };
-    auto reduce = [&](const Row (&cv)[kUnroll], int base) {
+    auto reduce = [&](const Row (&cv)[KU], int base) {
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < KU; ++u) {
             const int row = base + u * kWaves * RPI + wave * RPI + rsub;
             const float s = row16_sum(row_partial<VPL>(qf, cv[u]));
             if (col == 0 && row < n) sm.sc[row] = sm.pages[row] >= 0 ? s : -INFINITY;
         }
     };
-    Row ca[kUnroll], cb[kUnroll];
+    Row ca[KU], cb[KU];
     issue(ca, 0);
     for (int base = 0;;) {
         issue(cb, base + ROWS);
@@ -491,32 +574,29 @@ __device__ __forceinline__ bool score_chunk(const SelectArgs &a, int unit, int c
     // decode step: pages touched since the last step get their centroid
     // recomputed from the keys, stored for later steps, and re-scored here (one
     // wave per touched page; crow is the wave's LDS row)
-    if (a.first_pos) {
-        const int fp = a.first_pos[b];
-        if (fp >= 0 && fp < L) {
-            for (int j = max(j0, fp / kPage) + wave; j < j0 + n; j += kWaves) {
-                const int page = sm.pages[j - j0];
-                if (page < 0) continue;
-                const int v = min(kPage, L - j * kPage);
-                float *row_lds = crow + wave * D;
-                block_centroid<T, D>(static_cast<const T *>(a.k_cache) +
-                                         ((size_t)page * a.Hkv + g) * kPage * D,
-                                     v, a.cent_out + ((size_t)page * a.Hkv + g) * D, row_lds, lane);
-                __builtin_amdgcn_wave_barrier();
-                Row cv;
+    if (a.first_pos && fp >= 0 && fp < L) {
+        for (int j = max(j0, fp / kPage) + wave; j < j0 + n; j += kWaves) {
+            const int page = sm.pages[j - j0];
+            if (page < 0) continue;
+            const int v = min(kPage, L - j * kPage);
+            float *row_lds = crow + wave * D;
+            block_centroid<T, D>(static_cast<const T *>(a.k_cache) +
+                                     ((size_t)page * a.Hkv + g) * kPage * D,
+                                 v, a.cent_out + ((size_t)page * a.Hkv + g) * D, row_lds, lane);
+            __builtin_amdgcn_wave_barrier();
+            Row cv;
 #pragma unroll
-                for (int vv = 0; vv < VPL / 4; ++vv)
-                    cv[vv] = reinterpret_cast<const float4 *>(row_lds + col * VPL)[vv];
-                const float s = row16_sum(row_partial<VPL>(qf, cv));
-                if (lane == 0) sm.sc[j - j0] = s;
-                __builtin_amdgcn_wave_barrier();
-            }
+            for (int vv = 0; vv < VPL / 4; ++vv)
+                cv[vv] = reinterpret_cast<const float4 *>(row_lds + col * VPL)[vv];
+            const float s = row16_sum(row_partial<VPL>(qf, cv));
+            if (lane == 0) sm.sc[j - j0] = s;
+            __builtin_amdgcn_wave_barrier();
         }
     }
     __syncthreads();
+    nb_out = nb;
     float *sc = a.scores + (size_t)unit * a.max_blocks;
     for (int i = tid; i < n; i += kThreads) store_relaxed(sc + j0 + i, sm.sc[i]);
-    nb_out = nb;
     return arrive_last(&a.counters[unit], (uint32_t)nchunks, sm.flag);
 }
 

@@ -4,19 +4,26 @@
 // top-k blocks, attention over the kept blocks.)
 //
 // Work items come from a queue counter in the workspace, in this order:
-//   1. scoring items, one per (sequence, KV head, chunk), unit-major: the chunk
-//      that holds a touched page first recomputes its centroid, then the chunk
-//      is scored; the workgroup that completes a unit's last chunk selects the
-//      unit's top-k blocks and publishes a per-unit ready flag once its index
-//      stores are complete;
-//   2. attention items, one per (unit, split), unit-major: each waits for its
-//      unit's flag (bounded spin, never expected to be long) and attends.
-// Every scoring item precedes every attention item, and the workgroup that
-// selects a unit already holds that unit's last scoring item and never waits,
+//   1. scoring items, one per (sequence, KV head, chunk), unit-major with a
+//      unit's chunks from last to first: the chunk that holds a touched page
+//      first recomputes its centroid, then the chunk is scored; the workgroup
+//      that completes the unit (a counter per unit) selects its top-k blocks
+//      and publishes them as tagged entries (the launch's tag in the high
+//      word, so an entry is its own ready flag);
+//   2. attention items, one per (unit, split), unit-major: each wave waits
+//      (bounded spin, never expected to be long) until its entries carry the
+//      launch's tag, then attends.
+// Scoring never waits and every scoring item precedes every attention item,
 // so the waits always end.  By the time the attention items of the last units
 // are reached, their selections have run behind the attention of earlier units,
-// so selection latency is off the critical path.  The device functions are the
-// same as the stand-alone kernels', so results are identical to the three calls.
+// so selection latency is mostly off the critical path.  The device functions
+// are the same as the stand-alone kernels', so results are identical to the
+// three calls.
+//
+// The launch tag is one more than a launch counter kept in the queue words; the
+// last workgroup to leave advances the counter (skipping the value whose
+// successor would be 0, so that a tag is never 0 and two launches in a row never
+// share one) and re-arms the queue.
 #include "attend_dev.h"
 #include "select_dev.h"
 
@@ -30,9 +37,14 @@ using sel::kWaves;
 struct StepArgs {
     sel::SelectArgs s;
     att::AttendArgs t;
-    uint32_t *queue;  // [0] next item, [1] workgroups that have left
+    uint64_t *tagged;  // [units][top_k] published selections (also t.tagged)
+    uint32_t *queue;   // [0] items taken beyond the grid, [1] workgroups that have left,
+                       // [2] launch counter
     int B, units, nsplit;
 };
+
+constexpr int kStageBlocks = 1;  // bf16 attention pipeline stage (fp32: 2, see attend.hip)
+constexpr int kScanRows = 4;     // centroid rows per lane per scan stage
 
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
@@ -40,12 +52,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
     __shared__ int pages[kMaxChunk];
     __shared__ float sc_lds[kMaxChunk];
     __shared__ int flag;
-    __shared__ uint32_t hist[256 + kWave], cand[kWave], above[kWave], equal[kWave];
+    __shared__ uint32_t hist[256 + kWave], cand[4 * kWave], above[kWave], equal[kWave];
     __shared__ uint32_t red[2 * kWaves];
     __shared__ int scan_red[kWaves];
     __shared__ float crow[kWaves * D];
     __shared__ uint32_t prefix[kMaxStepBatch + 1];  // scoring items before each sequence
     __shared__ int item_s;
+    __shared__ uint32_t tag_s;
     // queries while scoring, top-k keys of long contexts, attention merges
     extern __shared__ float dyn[];
     sel::ScoreSmem sm{dyn, qs, pages, sc_lds, &flag};
@@ -53,6 +66,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
     const int tid = threadIdx.x;
     const int Hkv = a.s.Hkv;
 
+    // the launch tag is fetched while the prefix is built; the first item is
+    // the workgroup's own index, later ones come from the queue (offset by the
+    // grid), so the launch does not open with every workgroup's atomic at once
+    if (tid == 0)
+        tag_s = __hip_atomic_load(&a.queue[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
     // scoring items per sequence: Hkv * chunks (one item for an invalid length,
     // which writes -1 indices and flags the error)
     for (int b0 = 0; b0 < a.B; b0 += kThreads) {
@@ -73,44 +91,51 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
     const int n_score = (int)prefix[a.B];
     const int total = n_score + a.units * a.nsplit;
 
+    const uint32_t tag = tag_s;
+    int item = (int)blockIdx.x;
+    // the next item from the queue (LDS is reused by the next item)
+    auto next_item = [&]() {
+        __syncthreads();
+        if (tid == 0) item_s = (int)(gridDim.x + atomicAdd(&a.queue[0], 1u));
+        __syncthreads();
+        return item_s;
+    };
+    // every scoring item precedes every attention item, so a workgroup runs
+    // the two kinds in two loops (each with registers of its own)
     int b_cur = 0;
-    for (;;) {
-        if (tid == 0) item_s = (int)atomicAdd(&a.queue[0], 1u);
-        __syncthreads();
-        const int item = item_s;
-        __syncthreads();
-        if (item >= total) break;
-        if (item < n_score) {
-            while ((int)prefix[b_cur + 1] <= item) ++b_cur;  // items only grow
-            const int nc = (int)(prefix[b_cur + 1] - prefix[b_cur]) / Hkv;
-            const int rel = item - (int)prefix[b_cur];
-            const int unit = b_cur * Hkv + rel / nc, c = rel % nc;
-            int nb = 0;
-            if (sel::score_chunk<T, D>(a.s, unit, c, sm, crow, nb)) {
-                __builtin_amdgcn_s_setprio(3);
-                sel::select_topk(a.s.scores + (size_t)unit * a.s.max_blocks, nb, a.s.top_k,
-                                 a.s.indices + (size_t)unit * a.s.top_k, tk);
-                __builtin_amdgcn_s_setprio(0);
-                // publish: the index stores are complete before the flag is set
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                __syncthreads();
-                if (tid == 0)
-                    __hip_atomic_store(&a.t.ready[unit], 1u, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-            }
-        } else {
-            const int rel = item - n_score;
-            att::attend_item<T, D, false, (sizeof(T) == 4 ? 2 : 1)>(a.t, rel / a.nsplit,
-                                                                   rel % a.nsplit, dyn, &flag);
+    while (item < n_score) {
+        while ((int)prefix[b_cur + 1] <= item) ++b_cur;  // items only grow
+        const int nc = (int)(prefix[b_cur + 1] - prefix[b_cur]) / Hkv;
+        const int rel = item - (int)prefix[b_cur];
+        // a unit's chunks go last to first: the one that refreshes the newest
+        // page starts first, so that it is rarely the one left to select
+        const int unit = b_cur * Hkv + rel / nc, c = nc - 1 - rel % nc;
+        int nb = 0;
+        if (sel::score_chunk<T, D, kScanRows>(a.s, unit, c, sm, crow, nb)) {
+            __builtin_amdgcn_s_setprio(3);
+            sel::select_topk(sel::PlainScores{a.s.scores + (size_t)unit * a.s.max_blocks},
+                             nb, a.s.top_k,
+                             sel::TopkOut{a.s.indices + (size_t)unit * a.s.top_k,
+                                          a.tagged + (size_t)unit * a.s.top_k, tag},
+                             tk);
+            __builtin_amdgcn_s_setprio(0);
         }
-        __syncthreads();  // LDS is reused by the next item
+        item = next_item();
     }
-    // the last workgroup to leave re-arms the queue for the next launch
+    while (item < total) {
+        const int rel = item - n_score;
+        att::attend_item<T, D, false, (sizeof(T) == 4 ? 2 : kStageBlocks)>(
+            a.t, rel / a.nsplit, rel % a.nsplit, dyn, &flag, tag);
+        item = next_item();
+    }
+    // the last workgroup to leave re-arms the queue and advances the counter
     if (tid == 0) {
         const uint32_t prev = atomicAdd(&a.queue[1], 1u);
         if (prev == gridDim.x - 1) {
             __hip_atomic_store(&a.queue[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(&a.queue[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.queue[2], tag == 0xffffffffu ? 0u : tag, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
@@ -169,7 +194,7 @@ hipError_t launch_decode_step(const Dims &d, const SelectPlan &sp, const AttendP
                               const int32_t *first_pos, float *centroids, int top_k,
                               int32_t *indices, float *scores, void *out, float *lse,
                               float *partials, uint32_t *sel_counters, uint32_t *att_counters,
-                              uint32_t *ready, uint32_t *queue, uint32_t *err,
+                              uint64_t *tagged, uint32_t *queue, uint32_t *err,
                               hipStream_t stream) {
     StepArgs a;
     a.s = sel::SelectArgs{q, centroids, block_table, seq_lens, indices, scores, sel_counters, err,
@@ -177,7 +202,8 @@ hipError_t launch_decode_step(const Dims &d, const SelectPlan &sp, const AttendP
                           d.sm_scale, k_cache, first_pos, centroids};
     a.t = att::AttendArgs{q, k_cache, v_cache, block_table, seq_lens, indices, out, lse, partials,
                           att_counters, err, d.Hq, d.Hkv, d.num_pages, d.max_blocks, top_k, ap.bps,
-                          ap.nsplit_max, d.sm_scale * 1.44269504088896340736f, ready};
+                          ap.nsplit_max, d.sm_scale * 1.44269504088896340736f, tagged};
+    a.tagged = tagged;
     a.queue = queue;
     a.B = d.B;
     a.units = d.B * d.Hkv;
