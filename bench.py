@@ -3,10 +3,13 @@
 A step is one decode step of the method over the whole batch, all on one HIP
 stream: S1 centroid update of the page holding each sequence's newest token,
 S2+S3 group scoring and top-k selection, S4 attention over the selected blocks.
-The KV append itself is the caller's op and is not timed; lengths stay fixed
-so every step is the same work.  The workload is the Qwen3-8B-shaped decode
-layer (B=32, Hq=32, Hkv=8, D=128, bf16, ragged contexts U[4096, 32768], shuffled
-16-token pages, top-k = 32 blocks), drawn by ``synth`` with seed 3000.
+The timed step is the library's single-launch form (btk_decode_step); the same
+step as three calls (btk_centroid_update, btk_select, btk_sparse_attend) is
+timed beside it with a per-kernel breakdown.  The KV append itself is the
+caller's op and is not timed; lengths stay fixed so every step is the same
+work.  The workload is the Qwen3-8B-shaped decode layer (B=32, Hq=32, Hkv=8,
+D=128, bf16, ragged contexts U[4096, 32768], shuffled 16-token pages, top-k =
+32 blocks), drawn by ``synth`` with seed 3000.
 
 Inputs are resident in HBM before timing starts.  The step rotates over
 ``--replicas`` independent copies of the KV cache, centroids and tables so that
@@ -34,9 +37,10 @@ HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 METRIC = "sparse decode attention query-tokens/s + achieved HBM GB/s (% of peak), vs dense"
 WORKLOAD = ("qwen3-8b-shaped decode layer: B=32, Hq=32, Hkv=8 (group 4), D=128, bf16, "
             "contexts U[4096,32768], 16-token pages, shuffled block table, top_k=32 blocks")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "select_kernel_qwen3-8b_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_kernel_qwen3-8b_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "block_top_sparse_btk_amd", "csrc", f)
-                  for f in ("select.hip", "btk_internal.h")]
+                  for f in ("step.hip", "select_dev.h", "attend_dev.h", "centroid_dev.h",
+                            "btk_internal.h")]
 
 
 # ---------------------------------------------------------------- byte model
@@ -101,8 +105,8 @@ def _sources_digest() -> str:
 
 
 def _measured_traffic():
-    """HBM bytes per select launch from the committed rocprofv3 counter runs,
-    or None if the kernel source changed since they were taken."""
+    """HBM bytes per decode-step launch from the committed rocprofv3 counter
+    runs, or None if the kernel source changed since they were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -193,80 +197,86 @@ def main(argv=None):
         P = ctypes.byref(prob)
         p = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
         ws, wsn = p(rep["ws"]), rep["ws"].numel()
-        return ((P, p(d.k_cache), p(d.block_table), p(d.seq_lens), p(rep["first"]),
-                 p(rep["cent"]), hs),
-                (P, p(d.q), p(rep["cent"]), p(d.block_table), p(d.seq_lens), k, p(rep["idx"]),
-                 None, ws, wsn, hs),
-                (P, p(d.q), p(d.k_cache), p(d.v_cache), p(d.block_table), p(d.seq_lens),
-                 p(rep["idx"]), k, p(rep["out"]), None, ws, wsn, hs),
-                (P, p(d.q), p(d.k_cache), p(d.v_cache), p(d.block_table), p(d.seq_lens),
-                 p(rep["dout"]), None, ws, wsn, hs))
+        return {"step": (P, p(d.q), p(d.k_cache), p(d.v_cache), p(d.block_table),
+                         p(d.seq_lens), p(rep["first"]), p(rep["cent"]), k, p(rep["idx"]),
+                         p(rep["out"]), None, ws, wsn, hs),
+                "cen": (P, p(d.k_cache), p(d.block_table), p(d.seq_lens), p(rep["first"]),
+                        p(rep["cent"]), hs),
+                "sel": (P, p(d.q), p(rep["cent"]), p(d.block_table), p(d.seq_lens), k,
+                        p(rep["idx"]), None, ws, wsn, hs),
+                "att": (P, p(d.q), p(d.k_cache), p(d.v_cache), p(d.block_table), p(d.seq_lens),
+                        p(rep["idx"]), k, p(rep["sout"]), None, ws, wsn, hs),
+                "den": (P, p(d.q), p(d.k_cache), p(d.v_cache), p(d.block_table), p(d.seq_lens),
+                        p(rep["dout"]), None, ws, wsn, hs)}
 
     for rep in reps:
         rep["dout"] = torch.empty_like(rep["d"].q)
+        rep["sout"] = torch.empty_like(rep["d"].q)
         rep["calls"] = calls(rep)
-    f_cen, f_sel, f_att, f_den = (lib.btk_centroid_update, lib.btk_select, lib.btk_sparse_attend,
-                                  lib.btk_dense_attend)
+    f_step, f_cen, f_sel, f_att, f_den = (lib.btk_decode_step, lib.btk_centroid_update,
+                                          lib.btk_select, lib.btk_sparse_attend,
+                                          lib.btk_dense_attend)
 
-    def step(rep, ev=None):
-        c = rep["calls"]
-        st = f_cen(*c[0])
-        if ev is not None:
-            ev[0].record(stream)
-        st |= f_sel(*c[1])
-        if ev is not None:
-            ev[1].record(stream)
-        st |= f_att(*c[2])
+    def check(st):
         if st:
-            raise RuntimeError("library call failed")
+            raise RuntimeError(f"library call failed: {lib.btk_status_string(st).decode()}")
+
+    def sep_step(rep):
+        c = rep["calls"]
+        check(f_cen(*c["cen"]) | f_sel(*c["sel"]) | f_att(*c["att"]))
 
     for i in range(args.warmup):
-        step(reps[i % len(reps)])
+        check(f_step(*reps[i % len(reps)]["calls"]["step"]))
+        sep_step(reps[i % len(reps)])
     torch.cuda.synchronize()
 
-    # timed region: exactly K steps, bracketed by synchronize; HIP events on the
-    # library's stream bracket every select launch (the dominant kernel)
+    # timed region: exactly K steps, bracketed by synchronize; a HIP event pair
+    # on the library's stream brackets every launch (the step is one kernel)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(reps[i % len(reps)], evs[i])
+        evs[i][0].record(stream)
+        check(f_step(*reps[i % len(reps)]["calls"]["step"]))
+        evs[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = 1e3 * wall / args.steps
-    sel_us = 1e3 * sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    step_us = 1e3 * sum(a.elapsed_time(b) for a, b in evs) / args.steps
 
-    # per-kernel breakdown (separate pass, events between every launch)
+    # the same step as three calls: whole-step time, then a per-kernel pass
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        sep_step(reps[i % len(reps)])
+    torch.cuda.synchronize()
+    sep_ms = 1e3 * (time.perf_counter() - t0) / args.steps
     kev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for i in range(args.steps):
         c, ev = reps[i % len(reps)]["calls"], kev[i]
         ev[0].record(stream)
-        f_cen(*c[0])
+        f_cen(*c["cen"])
         ev[1].record(stream)
-        f_sel(*c[1])
+        f_sel(*c["sel"])
         ev[2].record(stream)
-        f_att(*c[2])
+        f_att(*c["att"])
         ev[3].record(stream)
     torch.cuda.synchronize()
     kern = {name: 1e3 * sum(ev[j].elapsed_time(ev[j + 1]) for ev in kev) / args.steps
             for j, name in enumerate(("centroid", "select", "attend"))}
 
-    # the same step replayed from HIP graphs (one captured step per replica)
+    # the step replayed from HIP graphs (one captured launch per replica)
     graph_ms = None
     if args.graph:
         graphs = []
         side = torch.cuda.Stream(dev)
         side.wait_stream(stream)
         with torch.cuda.stream(side):
-            for rep in reps:  # capture on a side stream; the calls name it explicitly
-                c = rep["calls"]
-                gc = [tuple(x if x is not hs else side.cuda_stream for x in cc) for cc in c]
+            for rep in reps:  # capture on a side stream; the call names it explicitly
+                c = tuple(x if x is not hs else side.cuda_stream for x in rep["calls"]["step"])
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=side):
-                    f_cen(*gc[0])
-                    f_sel(*gc[1])
-                    f_att(*gc[2])
+                    check(f_step(*c))
                 graphs.append(g)
         stream.wait_stream(side)
         for i in range(args.warmup):
@@ -280,16 +290,19 @@ def main(argv=None):
 
     # dense comparison on the same inputs
     for i in range(3):
-        f_den(*reps[i % len(reps)]["calls"][3])
+        check(f_den(*reps[i % len(reps)]["calls"]["den"]))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.dense_steps):
-        f_den(*reps[i % len(reps)]["calls"][3])
+        check(f_den(*reps[i % len(reps)]["calls"]["den"]))
     torch.cuda.synchronize()
     dense_ms = 1e3 * (time.perf_counter() - t0) / args.dense_steps
     for r in reps:
         if btk.workspace_error_bits(r["ws"]):
             raise RuntimeError("device-side input guard fired during the benchmark")
+    for r in reps:  # the two forms of the step agree
+        if not torch.equal(r["out"], r["sout"]):
+            raise RuntimeError("single-launch and three-call steps disagree")
 
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -302,7 +315,7 @@ def main(argv=None):
     nbytes = algorithmic_bytes(bt.seq_lens.tolist(), hq, hkv, D, k, e,
                                sel_tokens=selected_tokens(reps[0]["idx"].cpu(), bt.seq_lens))
     step_gbps = nbytes["step"] / (ms_per_step * 1e-3) / 1e9
-    sel_gbps = nbytes["select"] / (sel_us * 1e-6) / 1e9
+    launch_gbps = nbytes["step"] / (step_us * 1e-6) / 1e9
     dense_gbps = nbytes["dense"] / (dense_ms * 1e-3) / 1e9
     value = B / (ms_per_step * 1e-3)
     result = {
@@ -326,12 +339,18 @@ def main(argv=None):
         "step_frac_of_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
         "bytes_per_step": nbytes["step"],
         "bytes_per_token": round(nbytes["step"] / B, 1),
-        "kernels_us": {kk: round(v, 2) for kk, v in kern.items()},
-        "roofline": {"bound": "hbm", "kernel": "select (S2+S3 centroid scan + top-k)",
-                     "achieved": round(sel_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(sel_gbps / HBM_PEAK_GBPS, 4), "traffic": _measured_traffic(),
-                     "algorithmic_bytes_per_launch": nbytes["select"],
-                     "avg_launch_us": round(sel_us, 3)},
+        "roofline": {"bound": "hbm",
+                     "kernel": "decode_step_kernel (S1 + S2 + S3 + S4 in one launch)",
+                     "achieved": round(launch_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(launch_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": _measured_traffic(),
+                     "algorithmic_bytes_per_launch": nbytes["step"],
+                     "avg_launch_us": round(step_us, 3)},
+        "three_calls": {"ms_per_step": round(sep_ms, 5),
+                        "value": round(B / (sep_ms * 1e-3), 1),
+                        "kernels_us": {kk: round(v, 2) for kk, v in kern.items()},
+                        "algorithmic_bytes": {kk: nbytes[kk]
+                                              for kk in ("centroid", "select", "attend")}},
         "dense": {"value": round(B / (dense_ms * 1e-3), 1), "unit": "query-tokens/s",
                   "ms_per_step": round(dense_ms, 4), "gbps": round(dense_gbps, 1),
                   "frac_of_peak": round(dense_gbps / HBM_PEAK_GBPS, 4),
