@@ -73,15 +73,19 @@ def algorithmic_bytes(seq_lens, num_q_heads, num_kv_heads, head_dim, top_k, elem
       S4 attend:    k indices + their block-table entries (8*k), queries (r*D*e),
                     K and V of the selected blocks' valid tokens (2*v_j*D*e), out (r*D*e)
       dense:        table (4*n_b per sequence) + q and out (2*r*D*e) + all K,V (2*L*D*e)
+      local:        the same over the most recent min(k, n_b) blocks: their table
+                    entries (4*k_b per sequence), q and out, K,V of their valid tokens
     """
     r, D, e, P = num_q_heads // num_kv_heads, head_dim, elem_bytes, page
-    cen = sel = att = dense = 0
+    cen = sel = att = dense = local = 0
     for b, L in enumerate([int(x) for x in seq_lens]):
         nb = (L + P - 1) // P
         kb = min(top_k, nb)
         v_last = L - (nb - 1) * P
         sel += 4 * nb
         dense += 4 * nb
+        local += 4 * kb
+        local_toks = L - P * (nb - kb)
         for g in range(num_kv_heads):
             # valid tokens of the selected blocks: exact when the selection is
             # given, else every selected block full (or all of L when k >= n_b)
@@ -90,8 +94,9 @@ def algorithmic_bytes(seq_lens, num_q_heads, num_kv_heads, head_dim, top_k, elem
             sel += r * D * e + 4 * D * nb + 4 * top_k
             att += 8 * top_k + 2 * r * D * e + 2 * toks * D * e
             dense += 2 * r * D * e + 2 * L * D * e
+            local += 2 * r * D * e + 2 * local_toks * D * e
     return {"centroid": cen, "select": sel, "attend": att, "step": cen + sel + att,
-            "dense": dense}
+            "dense": dense, "local": local}
 
 
 # ---------------------------------------------------------------- helpers
@@ -207,15 +212,17 @@ def main(argv=None):
                 "att": (P, p(d.q), p(d.k_cache), p(d.v_cache), p(d.block_table), p(d.seq_lens),
                         p(rep["idx"]), k, p(rep["sout"]), None, ws, wsn, hs),
                 "den": (P, p(d.q), p(d.k_cache), p(d.v_cache), p(d.block_table), p(d.seq_lens),
-                        p(rep["dout"]), None, ws, wsn, hs)}
+                        p(rep["dout"]), None, ws, wsn, hs),
+                "loc": (P, p(d.q), p(d.k_cache), p(d.v_cache), p(d.block_table), p(d.seq_lens),
+                        k, p(rep["dout"]), None, ws, wsn, hs)}
 
     for rep in reps:
         rep["dout"] = torch.empty_like(rep["d"].q)
         rep["sout"] = torch.empty_like(rep["d"].q)
         rep["calls"] = calls(rep)
-    f_step, f_cen, f_sel, f_att, f_den = (lib.btk_decode_step, lib.btk_centroid_update,
-                                          lib.btk_select, lib.btk_sparse_attend,
-                                          lib.btk_dense_attend)
+    f_step, f_cen, f_sel, f_att, f_den, f_loc = (lib.btk_decode_step, lib.btk_centroid_update,
+                                                 lib.btk_select, lib.btk_sparse_attend,
+                                                 lib.btk_dense_attend, lib.btk_local_attend)
 
     def check(st):
         if st:
@@ -297,6 +304,16 @@ def main(argv=None):
         check(f_den(*reps[i % len(reps)]["calls"]["den"]))
     torch.cuda.synchronize()
     dense_ms = 1e3 * (time.perf_counter() - t0) / args.dense_steps
+
+    # local-window baseline (the most recent top_k blocks), same inputs
+    for i in range(args.warmup):
+        check(f_loc(*reps[i % len(reps)]["calls"]["loc"]))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        check(f_loc(*reps[i % len(reps)]["calls"]["loc"]))
+    torch.cuda.synchronize()
+    local_ms = 1e3 * (time.perf_counter() - t0) / args.steps
     for r in reps:
         if btk.workspace_error_bits(r["ws"]):
             raise RuntimeError("device-side input guard fired during the benchmark")
@@ -357,6 +374,12 @@ def main(argv=None):
                   "bytes_per_step": nbytes["dense"],
                   "bytes_per_token": round(nbytes["dense"] / B, 1)},
         "speedup_vs_dense": round(dense_ms / ms_per_step, 2),
+        "local_window": {"window_blocks": k, "value": round(B / (local_ms * 1e-3), 1),
+                         "unit": "query-tokens/s", "ms_per_step": round(local_ms, 5),
+                         "gbps": round(nbytes["local"] / (local_ms * 1e-3) / 1e9, 1),
+                         "frac_of_peak": round(nbytes["local"] / (local_ms * 1e-3) / 1e9
+                                               / HBM_PEAK_GBPS, 4),
+                         "bytes_per_step": nbytes["local"]},
         "graph_replay": None if graph_ms is None else {
             "ms_per_step": round(graph_ms, 5), "value": round(B / (graph_ms * 1e-3), 1),
             "step_gbps": round(nbytes["step"] / (graph_ms * 1e-3) / 1e9, 1)},

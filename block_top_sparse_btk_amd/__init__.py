@@ -75,6 +75,8 @@ def _lib():
         lib.btk_sparse_attend.argtypes = [P, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
         lib.btk_dense_attend.restype = st
         lib.btk_dense_attend.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.btk_local_attend.restype = st
+        lib.btk_local_attend.argtypes = [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
         lib.btk_decode_step.restype = st
         lib.btk_decode_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
         _LIB = lib
@@ -252,6 +254,29 @@ def btk_dense_attend(q, k_cache, v_cache, block_table, seq_lens, workspace, out=
                                  _dev(workspace, "workspace", torch.uint8, dev), workspace.numel(),
                                  _stream(dev))
     _check(st, "btk_dense_attend")
+    return out
+
+
+def btk_local_attend(q, k_cache, v_cache, block_table, seq_lens, window_blocks, workspace,
+                     out=None, lse=None, sm_scale: float = 0.0,
+                     problem: Optional[btk_problem_t] = None):
+    """Local-window baseline: attention over the most recent min(window_blocks, n_b)
+    blocks of each sequence; returns out [B, Hq, D]."""
+    dev = q.device
+    problem = problem or make_problem(q, k_cache, block_table, sm_scale)
+    out = torch.empty_like(q) if out is None else out
+    _check_shapes(problem, q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
+                  seq_lens=seq_lens, out=out, lse=lse)
+    lp = _dev(lse, "lse", torch.float32, dev) if lse is not None else None
+    st = _lib().btk_local_attend(ctypes.byref(problem), _dev(q, "q", None, dev),
+                                 _dev(k_cache, "k_cache", q.dtype, dev),
+                                 _dev(v_cache, "v_cache", q.dtype, dev),
+                                 _dev(block_table, "block_table", torch.int32, dev),
+                                 _dev(seq_lens, "seq_lens", torch.int32, dev), int(window_blocks),
+                                 _dev(out, "out", q.dtype, dev), lp,
+                                 _dev(workspace, "workspace", torch.uint8, dev), workspace.numel(),
+                                 _stream(dev))
+    _check(st, "btk_local_attend")
     return out
 
 

@@ -140,7 +140,7 @@ btk_status_t btk_sparse_attend(const btk_problem_t *problem, const void *q, cons
     if (!workspace || workspace_bytes < w.total) return BTK_ERR_WORKSPACE;
     char *ws = static_cast<char *>(workspace);
     const btk::AttendPlan plan = btk::plan_attend(d, top_k, false);
-    return hip_status(btk::launch_attend(d, plan, false, q, k_cache, v_cache, block_table,
+    return hip_status(btk::launch_attend(d, plan, 0, q, k_cache, v_cache, block_table,
                                          seq_lens, indices, top_k, out, lse,
                                          reinterpret_cast<float *>(ws + w.partials),
                                          reinterpret_cast<uint32_t *>(ws + w.att_counters),
@@ -160,8 +160,29 @@ btk_status_t btk_dense_attend(const btk_problem_t *problem, const void *q, const
     if (!workspace || workspace_bytes < w.total) return BTK_ERR_WORKSPACE;
     char *ws = static_cast<char *>(workspace);
     const btk::AttendPlan plan = btk::plan_attend(d, d.max_blocks, true);
-    return hip_status(btk::launch_attend(d, plan, true, q, k_cache, v_cache, block_table,
+    return hip_status(btk::launch_attend(d, plan, 1, q, k_cache, v_cache, block_table,
                                          seq_lens, nullptr, 0, out, lse,
+                                         reinterpret_cast<float *>(ws + w.partials),
+                                         reinterpret_cast<uint32_t *>(ws + w.att_counters),
+                                         reinterpret_cast<uint32_t *>(ws), (hipStream_t)stream));
+}
+
+btk_status_t btk_local_attend(const btk_problem_t *problem, const void *q, const void *k_cache,
+                              const void *v_cache, const int32_t *block_table,
+                              const int32_t *seq_lens, int32_t window_blocks, void *out,
+                              float *lse, void *workspace, size_t workspace_bytes,
+                              void *stream) {
+    btk::Dims d;
+    btk_status_t st = check_problem(problem, &d);
+    if (st != BTK_OK) return st;
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out) return BTK_ERR_NULL;
+    if (!top_k_ok(window_blocks)) return BTK_ERR_SHAPE;
+    const btk::WorkspaceLayout w = btk::workspace_layout(d, window_blocks);
+    if (!workspace || workspace_bytes < w.total) return BTK_ERR_WORKSPACE;
+    char *ws = static_cast<char *>(workspace);
+    const btk::AttendPlan plan = btk::plan_attend(d, window_blocks, false);
+    return hip_status(btk::launch_attend(d, plan, 2, q, k_cache, v_cache, block_table,
+                                         seq_lens, nullptr, window_blocks, out, lse,
                                          reinterpret_cast<float *>(ws + w.partials),
                                          reinterpret_cast<uint32_t *>(ws + w.att_counters),
                                          reinterpret_cast<uint32_t *>(ws), (hipStream_t)stream));

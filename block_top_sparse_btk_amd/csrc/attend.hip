@@ -1,40 +1,44 @@
-// S4 / S5 stand-alone: one workgroup per (unit, split) (device code in attend_dev.h).
+// S4 / S5 and the local-window baseline, stand-alone: one workgroup per (unit,
+// split) (device code in attend_dev.h).
 #include "attend_dev.h"
 
 namespace btk {
 using namespace att;
 namespace {
 
-// blocks per pipeline stage: one for the short bf16 sparse lists (fewer
-// registers, more waves in flight), two elsewhere.  The fp32 sparse kernel keeps
-// two-block stages: its one-block build gave wrong outputs on the GPU while
-// every bf16 build with the same source was exact, so that variant is not used.
-template <typename T, bool DENSE>
-constexpr int stage_blocks() { return (DENSE || sizeof(T) == 4) ? 2 : 1; }
+// blocks per pipeline stage: one for the short bf16 lists (fewer registers,
+// more waves in flight), two for every block and for fp32.  The fp32 kernels
+// keep two-block stages: the one-block fp32 build of the selected-list kernel
+// gave wrong outputs on the GPU while every bf16 build with the same source was
+// exact, so that variant is not used.
+template <typename T, int MODE>
+constexpr int stage_blocks() { return (MODE == kAll || sizeof(T) == 4) ? 2 : 1; }
 
-template <typename T, int D, bool DENSE>
+template <typename T, int D, int MODE>
 __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
     extern __shared__ float smem[];
     __shared__ int is_last;
-    attend_item<T, D, DENSE, stage_blocks<T, DENSE>()>(a, blockIdx.x / a.nsplit_max,
-                                                    blockIdx.x % a.nsplit_max, smem, &is_last);
+    attend_item<T, D, MODE, stage_blocks<T, MODE>()>(a, blockIdx.x / a.nsplit_max,
+                                                  blockIdx.x % a.nsplit_max, smem, &is_last);
 }
 
-template <typename T, int D, bool DENSE>
+template <typename T, int D, int MODE>
 hipError_t launch(const Dims &d, const AttendPlan &plan, AttendArgs a, hipStream_t stream) {
     const size_t grid = (size_t)d.B * d.Hkv * plan.nsplit_max;
     const size_t wave_merge = (size_t)kWaves * d.group() * D + 2 * kWaves * 16;
     const size_t split_merge = 2 * (size_t)plan.nsplit_max * d.group() + d.group();
     const size_t lds = sizeof(float) * (wave_merge > split_merge ? wave_merge : split_merge);
-    hipLaunchKernelGGL((attend_kernel<T, D, DENSE>), dim3((unsigned)grid), dim3(kThreads), lds,
+    hipLaunchKernelGGL((attend_kernel<T, D, MODE>), dim3((unsigned)grid), dim3(kThreads), lds,
                        stream, a);
     return hipGetLastError();
 }
 
 template <typename T, int D>
-hipError_t launch_dtype(const Dims &d, const AttendPlan &plan, bool dense, AttendArgs a,
+hipError_t launch_dtype(const Dims &d, const AttendPlan &plan, int mode, AttendArgs a,
                         hipStream_t stream) {
-    return dense ? launch<T, D, true>(d, plan, a, stream) : launch<T, D, false>(d, plan, a, stream);
+    if (mode == kAll) return launch<T, D, kAll>(d, plan, a, stream);
+    if (mode == kRecent) return launch<T, D, kRecent>(d, plan, a, stream);
+    return launch<T, D, kSelected>(d, plan, a, stream);
 }
 
 }  // namespace
@@ -68,7 +72,7 @@ AttendPlan plan_attend(const Dims &d, int list_len_max, bool dense) {
     return p;
 }
 
-hipError_t launch_attend(const Dims &d, const AttendPlan &plan, bool dense, const void *q,
+hipError_t launch_attend(const Dims &d, const AttendPlan &plan, int mode, const void *q,
                          const void *k_cache, const void *v_cache, const int32_t *block_table,
                          const int32_t *seq_lens, const int32_t *indices, int top_k, void *out,
                          float *lse, float *partials, uint32_t *counters, uint32_t *err,
@@ -77,10 +81,10 @@ hipError_t launch_attend(const Dims &d, const AttendPlan &plan, bool dense, cons
                  counters, err, d.Hq, d.Hkv, d.num_pages, d.max_blocks, top_k, plan.bps,
                  plan.nsplit_max, d.sm_scale * 1.44269504088896340736f, nullptr};
     if (d.dtype == 0)
-        return d.D == 128 ? launch_dtype<uint16_t, 128>(d, plan, dense, a, stream)
-                          : launch_dtype<uint16_t, 64>(d, plan, dense, a, stream);
-    return d.D == 128 ? launch_dtype<float, 128>(d, plan, dense, a, stream)
-                      : launch_dtype<float, 64>(d, plan, dense, a, stream);
+        return d.D == 128 ? launch_dtype<uint16_t, 128>(d, plan, mode, a, stream)
+                          : launch_dtype<uint16_t, 64>(d, plan, mode, a, stream);
+    return d.D == 128 ? launch_dtype<float, 128>(d, plan, mode, a, stream)
+                      : launch_dtype<float, 64>(d, plan, mode, a, stream);
 }
 
 }  // namespace btk

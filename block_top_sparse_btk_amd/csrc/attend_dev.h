@@ -217,12 +217,17 @@ __device__ __forceinline__ void store_out<float>(float *p, float x) {
     *p = x;
 }
 
+// Which block list an item attends over: the unit's selection (S4), every block
+// of the sequence (S5, the dense comparison), or the most recent min(top_k, n_b)
+// blocks (the local-window baseline, where top_k is the window in blocks).
+enum ListMode : int { kSelected = 0, kAll = 1, kRecent = 2 };
+
 // One (unit, split) item: attention of the unit's query group over its share of
 // the block list, kG blocks per pipeline stage.  smem: the wave-merge / split-merge area (see launch
 // sizing); is_last: one LDS word.  Inside a decode step (a.tagged set) each wave
 // reads its entries of the unit's published selection, waiting (bounded) until
 // all of them carry the launch's tag.
-template <typename T, int D, bool DENSE, int kG>
+template <typename T, int D, int MODE, int kG>
 __device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int split, float *smem,
                                             int *is_last_p, uint32_t tag = 0u) {
     using F = Mfma<T, D>;
@@ -232,12 +237,13 @@ __device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int s
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int b = unit / a.Hkv, g = unit % a.Hkv;
     const int r = a.Hq / a.Hkv;
-    // a sparse list has top_k entries whatever the length, so its entries are
+    constexpr bool LISTED = MODE == kSelected;
+    // a selection has top_k entries whatever the length, so its entries are
     // requested together with the length
     const int per_wave = a.bps / kWaves;
     int cnt = 0, w0 = 0;
     uint64_t entry = 0;
-    if (!DENSE) {
+    if (LISTED) {
         const int i0 = split * a.bps, i1 = min(a.top_k, i0 + a.bps);
         w0 = i0 + wave * per_wave;
         cnt = max(0, min(i1, w0 + per_wave) - w0);
@@ -255,10 +261,10 @@ __device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int s
         return;
     }
     const int nb = (L + kPage - 1) / kPage;
-    const int len = DENSE ? nb : a.top_k;
+    const int len = MODE == kAll ? nb : MODE == kRecent ? min(a.top_k, nb) : a.top_k;
     const int nsplit = (len + a.bps - 1) / a.bps;
     if (split >= nsplit) return;
-    if (DENSE) {
+    if (!LISTED) {
         const int i0 = split * a.bps, i1 = min(len, i0 + a.bps);
         w0 = i0 + wave * per_wave;
         cnt = max(0, min(i1, w0 + per_wave) - w0);
@@ -282,8 +288,8 @@ __device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int s
     // (page -1 and 0 tokens for a skipped or invalid entry)
     int my_page = -1, my_v = 0;
     if (lane < cnt) {
-        int j = DENSE ? (w0 + lane) : (int32_t)(uint32_t)entry;
-        if (!DENSE && j >= nb) {
+        int j = LISTED ? (int32_t)(uint32_t)entry : nb - len + w0 + lane;  // kAll: len = nb
+        if (LISTED && j >= nb) {
             flag_error(a.err, kErrIndex);
             j = -1;
         }

@@ -137,7 +137,8 @@ hipError_t launch_select(const Dims &d, const SelectPlan &plan, const void *q,
                          const int32_t *seq_lens, int top_k, int32_t *indices, float *scores,
                          uint32_t *counters, uint32_t *err, hipStream_t stream);
 
-hipError_t launch_attend(const Dims &d, const AttendPlan &plan, bool dense, const void *q,
+// mode: 0 the selected blocks, 1 every block, 2 the most recent min(top_k, n_b)
+hipError_t launch_attend(const Dims &d, const AttendPlan &plan, int mode, const void *q,
                          const void *k_cache, const void *v_cache, const int32_t *block_table,
                          const int32_t *seq_lens, const int32_t *indices, int top_k, void *out,
                          float *lse, float *partials, uint32_t *counters, uint32_t *err,

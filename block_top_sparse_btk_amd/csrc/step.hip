@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
     }
     while (item < total) {
         const int rel = item - n_score;
-        att::attend_item<T, D, false, (sizeof(T) == 4 ? 2 : kStageBlocks)>(
+        att::attend_item<T, D, att::kSelected, (sizeof(T) == 4 ? 2 : kStageBlocks)>(
             a.t, rel / a.nsplit, rel % a.nsplit, dyn, &flag, tag);
         item = next_item();
     }

@@ -93,8 +93,9 @@ const char *btk_status_string(btk_status_t status);
 /* hipError_t code of the last BTK_ERR_HIP returned on this host thread. */
 int btk_last_hip_error(void);
 
-/* Bytes of device workspace that btk_select, btk_sparse_attend and
- * btk_dense_attend need for this problem and top_k (host; no HIP call).
+/* Bytes of device workspace that btk_select, btk_sparse_attend,
+ * btk_dense_attend, btk_local_attend (top_k = the window) and btk_decode_step
+ * need for this problem and top_k (host; no HIP call).
  * Returns 0 if the problem is invalid.  The caller allocates it, ZERO-FILLS it
  * once before its first use, and may then reuse it for any number of calls of
  * the same or a smaller problem: each completed call leaves its internal
@@ -165,6 +166,23 @@ btk_status_t btk_dense_attend(const btk_problem_t *problem, const void *q, const
                               const void *v_cache, const int32_t *block_table,
                               const int32_t *seq_lens, void *out, float *lse, void *workspace,
                               size_t workspace_bytes, void *stream);
+
+/* Local (sliding-window) attention baseline: the same computation as
+ * btk_sparse_attend over the most recent min(window_blocks, n_b) blocks of each
+ * sequence, i.e. the newest KV instead of the selected blocks, at the same
+ * per-unit block budget.  (scime summary of "Kinetics: Rethinking Test-Time
+ * Scaling Law", table "Measured effects reported in the paper": the ablation
+ * that replaces top-k KV selection by local attention, and "Experimental setup",
+ * which lists local attention among the baselines; the block granularity and
+ * the budget in pages follow the Kinetics README, "Benchmark Block TopK
+ * Attention throughput".)
+ *   window_blocks  1 .. 8192
+ *   workspace      btk_workspace_bytes(problem, window_blocks) bytes, as above
+ *   out out [B][Hq][D] dtype;  lse out [B][Hq] float32, or NULL */
+btk_status_t btk_local_attend(const btk_problem_t *problem, const void *q, const void *k_cache,
+                              const void *v_cache, const int32_t *block_table,
+                              const int32_t *seq_lens, int32_t window_blocks, void *out,
+                              float *lse, void *workspace, size_t workspace_bytes, void *stream);
 
 /* One whole decode step in a single launch: S1 for the touched pages (as
  * btk_centroid_update with first_pos; none when first_pos is NULL), then S2+S3

@@ -180,6 +180,29 @@ def attend(q, k_cache, v_cache, block_table, seq_lens, indices=None, sm_scale=0.
     return out, lse, w
 
 
+def local_indices(seq_lens, num_kv_heads, window_blocks, page_size=16):
+    """The local-window baseline's block lists [B, Hkv, window] int32: the most
+    recent min(window, n_b) blocks of each sequence, ascending, -1 padded.
+    (scime summary of "Kinetics: Rethinking Test-Time Scaling Law", "Measured
+    effects reported in the paper": local attention replaces the top-k selection
+    by the most recent KV; here at the same budget of whole blocks.)"""
+    sl = [int(x) for x in _cpu(seq_lens, torch.int32)]
+    out = torch.full((len(sl), num_kv_heads, window_blocks), -1, dtype=torch.int32)
+    for b, L in enumerate(sl):
+        nb = (L + page_size - 1) // page_size
+        w = min(window_blocks, nb)
+        out[b, :, :w] = torch.arange(nb - w, nb, dtype=torch.int32)
+    return out
+
+
+def local_attend(q, k_cache, v_cache, block_table, seq_lens, window_blocks, sm_scale=0.0,
+                 want_weights=False):
+    """Attention over the local window's blocks (see local_indices): (out, lse, weights)."""
+    idx = local_indices(seq_lens, k_cache.shape[1], window_blocks, page_size=k_cache.shape[2])
+    return attend(q, k_cache, v_cache, block_table, seq_lens, idx, sm_scale=sm_scale,
+                  want_weights=want_weights)
+
+
 def round_bf16(x: torch.Tensor) -> torch.Tensor:
     """float32 -> bfloat16 with round-to-nearest-even (the output rounding)."""
     x = _cpu(x, torch.float32)

@@ -116,3 +116,36 @@ def test_binding_refuses_host_tensors():
         btk.btk_dense_attend(q, torch.zeros(4, 1, 16, 64), torch.zeros(4, 1, 64, 16),
                              torch.zeros(1, 4, dtype=torch.int32), torch.ones(1, dtype=torch.int32),
                              torch.zeros(10, dtype=torch.uint8))
+
+
+def test_local_attend_and_decode_step_validate_before_launch():
+    lib = btk._lib()
+    prob = _problem()
+    p = ctypes.byref(prob)
+    need = btk.btk_workspace_bytes(prob, 8)
+    # local window: nulls, window range, workspace
+    assert lib.btk_local_attend(p, FAKE, None, FAKE, FAKE, FAKE, 8, FAKE, None, FAKE, need,
+                                None) == btk.BTK_ERR_NULL
+    assert lib.btk_local_attend(p, FAKE, FAKE, FAKE, FAKE, FAKE, 8, None, None, FAKE, need,
+                                None) == btk.BTK_ERR_NULL
+    for w in (0, -1, 8193):
+        assert lib.btk_local_attend(p, FAKE, FAKE, FAKE, FAKE, FAKE, w, FAKE, None, FAKE, 1 << 30,
+                                    None) == btk.BTK_ERR_SHAPE
+    assert lib.btk_local_attend(p, FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, None, FAKE, need - 1,
+                                None) == btk.BTK_ERR_WORKSPACE
+    assert lib.btk_local_attend(None, FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, None, FAKE, need,
+                                None) == btk.BTK_ERR_NULL
+    # single-launch step: nulls (first_pos and lse may be NULL), top_k, workspace, batch limit
+    args = lambda **o: [o.get(n, FAKE) for n in ("q", "k", "v", "bt", "sl")] + \
+        [o.get("fp", None), o.get("cent", FAKE), o.get("k_", 8), o.get("idx", FAKE),
+         o.get("out", FAKE), None, o.get("ws", FAKE), o.get("wsn", need), None]  # noqa: E731
+    assert lib.btk_decode_step(p, *args(cent=None)) == btk.BTK_ERR_NULL
+    assert lib.btk_decode_step(p, *args(idx=None)) == btk.BTK_ERR_NULL
+    assert lib.btk_decode_step(p, *args(v=None)) == btk.BTK_ERR_NULL
+    assert lib.btk_decode_step(p, *args(k_=0)) == btk.BTK_ERR_SHAPE
+    assert lib.btk_decode_step(p, *args(wsn=need - 1)) == btk.BTK_ERR_WORKSPACE
+    assert lib.btk_decode_step(p, *args(ws=None)) == btk.BTK_ERR_WORKSPACE
+    big = _problem(batch=1025, max_blocks_per_seq=64)
+    assert lib.btk_decode_step(ctypes.byref(big), *args(wsn=1 << 40)) == btk.BTK_ERR_UNSUPPORTED
+    bad = ctypes.byref(_problem(head_dim=96))
+    assert lib.btk_decode_step(bad, *args()) == btk.BTK_ERR_UNSUPPORTED

@@ -36,3 +36,17 @@ def test_exact_selected_tokens():
     import torch
     idx = torch.tensor([[[0, 6, -1]]], dtype=torch.int32)
     assert bench.selected_tokens(idx, [100]) == [[16 + 4]]
+
+
+def test_local_window_bytes():
+    # a window covering every block moves exactly the dense bytes
+    lens = [37, 16, 1, 200]
+    full = bench.algorithmic_bytes(lens, 8, 2, 128, 64, 2)
+    assert full["local"] == full["dense"]
+    # a window of w whole blocks moves w pages of K and V per unit, plus q/out and table
+    w, r, D, e = 4, 4, 128, 2
+    part = bench.algorithmic_bytes([1000], 8, 2, D, w, e)
+    nb = (1000 + 15) // 16
+    toks = 1000 - 16 * (nb - w)  # the last block holds 1000 - 16*62 = 8 tokens
+    assert toks == 3 * 16 + 8
+    assert part["local"] == 4 * w + 2 * (2 * r * D * e + 2 * toks * D * e)

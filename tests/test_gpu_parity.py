@@ -392,3 +392,46 @@ def test_decode_step_equals_separate_calls_and_oracle(label, spec):
     st = check_indices(results[0][1], ora["indices"], ora["scores"], bt.seq_lens, k)
     check_outputs(results[0][0], ora["out"], bt.dtype, st["equal_mask"], bt.group)
     check_lse(results[0][2], ora["lse"], bt.dtype, st["equal_mask"], bt.group)
+
+
+# ------------------------------------------------------------------ local-window baseline
+
+LOCAL_CASES = [("config2", dict(cfg=2)), ("config3", dict(cfg=3)), ("config4", dict(cfg=4)),
+               ("config5-64k", dict(cfg=5, context=65536)),
+               ("ragged-w1", dict(window=1, kw=dict(batch=5, num_q_heads=8, num_kv_heads=2,
+                                                    head_dim=128, seq_lens=[1, 17, 300, 5000, 33],
+                                                    top_k=4, seed=41))),
+               ("ragged-w-exceeds", dict(window=40, kw=dict(batch=4, num_q_heads=8, num_kv_heads=4,
+                                                            head_dim=128, seq_lens=[40, 200, 16, 641],
+                                                            top_k=4, seed=42))),
+               ("d64-w7", dict(window=7, kw=dict(batch=3, num_q_heads=4, num_kv_heads=1, head_dim=64,
+                                                 seq_lens=[100, 999, 64], top_k=5, seed=43))),
+               ("fp32-d128-w6", dict(window=6, kw=dict(batch=3, num_q_heads=6, num_kv_heads=2,
+                                                       head_dim=128, seq_lens=[333, 48, 1000],
+                                                       top_k=6, seed=44, dtype=torch.float32)))]
+
+
+@pytest.mark.parametrize("label,spec", LOCAL_CASES, ids=[c[0] for c in LOCAL_CASES])
+def test_local_window_parity(label, spec):
+    if "cfg" in spec:
+        bt = _workload(spec["cfg"], spec.get("context"))
+    else:
+        bt = synth.make_batch(name=label, **spec["kw"])
+    window = spec.get("window", bt.top_k)
+    _say(f"[local] {label} window={window}")
+    d = bt.to(DEV)
+    prob = btk.make_problem(d.q, d.k_cache, d.block_table)
+    ws = btk.new_workspace(prob, window, DEV)
+    lse = torch.empty((bt.batch, bt.num_q_heads), device=DEV)
+    out = btk.btk_local_attend(d.q, d.k_cache, d.v_cache, d.block_table, d.seq_lens, window, ws,
+                               lse=lse, problem=prob)
+    out2 = btk.btk_local_attend(d.q, d.k_cache, d.v_cache, d.block_table, d.seq_lens, window, ws,
+                                problem=prob)
+    torch.cuda.synchronize()
+    assert btk.workspace_error_bits(ws) == 0
+    assert torch.equal(out, out2)  # deterministic, workspace re-armed
+    ora_out, ora_lse, _ = oracle.local_attend(bt.q, bt.k_cache, bt.v_cache, bt.block_table,
+                                              bt.seq_lens, window)
+    err = check_outputs(out.cpu(), ora_out, bt.dtype, what="local out")
+    check_lse(lse.cpu(), ora_lse, bt.dtype)
+    _say(f"[local]   ok max_abs_out={err:.2e}")

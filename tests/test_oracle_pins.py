@@ -407,3 +407,48 @@ def test_bf16_rounding_matches_torch_cast():
     half = (base.view(torch.int32) + 0x8000).view(torch.float32)
     x = torch.cat([x, half, torch.tensor([0.0, -0.0, 1e-40, 3.0e38, -3.0e38])])
     assert torch.equal(oracle.round_bf16(x).view(torch.int16), x.to(torch.bfloat16).view(torch.int16))
+
+
+# ---------------------------------------------------------------- local-window baseline
+# (scime summary of "Kinetics: Rethinking Test-Time Scaling Law", "Measured effects
+# reported in the paper": local attention over the most recent KV replaces the top-k
+# selection; the window is counted in whole blocks, like the top-k budget.)
+
+@pytest.mark.parametrize("window", [1, 2, 3])
+def test_local_window_is_the_most_recent_tokens_of_whole_blocks(window):
+    b = _small(batch=4, seq_lens=[37, 16, 1, 50], head_dim=16)
+    out, lse, w = oracle.local_attend(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens,
+                                      window, want_weights=True)
+    for seq in range(b.batch):
+        L = int(b.seq_lens[seq])
+        nb = (L + 15) // 16
+        first = 16 * max(0, nb - window)  # the window starts on a block boundary
+        for h in range(b.num_q_heads):
+            g = h // b.group
+            keys, vals = _keys_of(b, seq, g)[first:L], _values_of(b, seq, g)[first:L]
+            qh = b.q[seq, h].double()
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                qh.reshape(1, 1, 1, -1), keys.reshape(1, 1, -1, b.head_dim),
+                vals.reshape(1, 1, -1, b.head_dim)).reshape(-1)
+            ref_lse = torch.logsumexp((keys @ qh) / math.sqrt(b.head_dim), 0)
+            assert torch.allclose(out[seq, h].double(), ref, rtol=0, atol=2e-7)
+            assert abs(float(lse[seq, h]) - float(ref_lse)) < 1e-5
+            mass = w[seq, h]
+            assert float(mass[:first].abs().sum()) == 0.0
+            assert abs(float(mass[first:L].sum()) - 1.0) < 1e-12
+
+
+def test_local_window_covering_the_sequence_equals_dense_exactly():
+    b = _small(seq_lens=[37, 16, 5])
+    lout, llse, _ = oracle.local_attend(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens, 3)
+    dout, dlse, _ = oracle.attend(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens)
+    assert torch.equal(lout, dout) and torch.equal(llse, dlse)
+
+
+def test_local_indices_layout():
+    idx = oracle.local_indices(torch.tensor([37, 16, 1, 200], dtype=torch.int32), 2, 4)
+    assert idx.shape == (4, 2, 4)
+    assert idx[0, 0].tolist() == [0, 1, 2, -1]
+    assert idx[1, 1].tolist() == [0, -1, -1, -1]
+    assert idx[2, 0].tolist() == [0, -1, -1, -1]
+    assert idx[3, 0].tolist() == [9, 10, 11, 12]
