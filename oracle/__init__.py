@@ -203,6 +203,41 @@ def local_attend(q, k_cache, v_cache, block_table, seq_lens, window_blocks, sm_s
                   want_weights=want_weights)
 
 
+def token_view(k_cache, v_cache, block_table):
+    """The same cache seen as one-token pages: (k1 [N*P][Hkv][1][D], v1 [N*P][Hkv][D][1],
+    token table [B][max_blocks*P]) with logical token i of sequence b at row
+    block_table[b][i // P] * P + i % P.  Layout only, no arithmetic."""
+    k_cache, v_cache = _cpu(k_cache), _cpu(v_cache)
+    N, hkv, P, D = k_cache.shape
+    k1 = k_cache.permute(0, 2, 1, 3).reshape(N * P, hkv, 1, D).contiguous()
+    v1 = v_cache.permute(0, 3, 1, 2).reshape(N * P, hkv, D, 1).contiguous()
+    bt = _cpu(block_table, torch.int32).to(torch.int64)
+    i = torch.arange(bt.shape[1] * P)
+    tt = (bt[:, i // P] * P + i % P).to(torch.int32)
+    return k1, v1, tt
+
+
+def token_step(q, k_cache, v_cache, block_table, seq_lens, top_tokens, sm_scale=0.0):
+    """Token-level top-k attention, the pages' upper-bound baseline (scime summary
+    of "Kinetics: Rethinking Test-Time Scaling Law", "Experimental setup": oracle
+    top-k attention; "Limitations": the sparse results use it as an upper bound).
+
+    It is the method with one-token blocks: a one-token block's mean key is the
+    key itself, so the group score of token t is (1/r) sum_h scale q_h . k_t, the
+    top_tokens best tokens are kept (ties to the lower position) and every head
+    attends over exactly those.  Computed by the block functions at page size 1
+    on token_view() of the cache.  Returns a dict with scores [B, Hkv, max_tokens],
+    indices [B, Hkv, top_tokens] (logical token positions, ascending, -1 padded),
+    out and lse.
+    """
+    k1, v1, tt = token_view(k_cache, v_cache, block_table)
+    keys = centroids(k1, tt, seq_lens)
+    sc = scores(q, keys, tt, seq_lens, page_size=1, sm_scale=sm_scale)
+    idx = select(sc, seq_lens, top_tokens, page_size=1)
+    out, lse, _ = attend(q, k1, v1, tt, seq_lens, idx, sm_scale=sm_scale)
+    return {"scores": sc, "indices": idx, "out": out, "lse": lse}
+
+
 def round_bf16(x: torch.Tensor) -> torch.Tensor:
     """float32 -> bfloat16 with round-to-nearest-even (the output rounding)."""
     x = _cpu(x, torch.float32)

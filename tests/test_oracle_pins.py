@@ -452,3 +452,73 @@ def test_local_indices_layout():
     assert idx[1, 1].tolist() == [0, -1, -1, -1]
     assert idx[2, 0].tolist() == [0, -1, -1, -1]
     assert idx[3, 0].tolist() == [9, 10, 11, 12]
+
+
+# ---------------------------------------------------------------- token-level top-k
+# (scime summary of "Kinetics: Rethinking Test-Time Scaling Law", "Experimental setup":
+# oracle top-k attention is a baseline; "Limitations": the upper bound of the sparse results.)
+
+def test_token_view_is_a_relabelling():
+    b = _small(dtype=torch.bfloat16, seq_lens=[37, 16, 5], head_dim=16)
+    k1, v1, tt = oracle.token_view(b.k_cache, b.v_cache, b.block_table)
+    for seq in range(b.batch):
+        L = int(b.seq_lens[seq])
+        for g in range(b.num_kv_heads):
+            rows = tt[seq, :L].long()
+            assert torch.equal(k1[rows, g, 0, :].double(), _keys_of(b, seq, g))
+            assert torch.equal(v1[rows, g, :, 0].double(), _values_of(b, seq, g))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_token_topk_scores_selection_and_attention(dtype):
+    b = _small(dtype=dtype, batch=3, seq_lens=[70, 33, 9], head_dim=16)
+    T = 12
+    st = oracle.token_step(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens, T)
+    scale = 1.0 / math.sqrt(b.head_dim)
+    for seq in range(b.batch):
+        L = int(b.seq_lens[seq])
+        for g in range(b.num_kv_heads):
+            keys = _keys_of(b, seq, g)
+            qs = b.q[seq, g * b.group:(g + 1) * b.group].double()
+            want = (keys @ qs.T).mean(dim=1) * scale  # mean of the group's scaled logits
+            got = st["scores"][seq, g, :L].double()
+            assert torch.allclose(got, want, rtol=0, atol=1e-6)
+            # selection: lexsort on (score desc, position asc) of the stored fp32 scores
+            s32 = st["scores"][seq, g, :L].numpy()
+            order = np.lexsort((np.arange(L), -s32.astype(np.float64)))[:min(T, L)]
+            sel = sorted(order.tolist())
+            idx = st["indices"][seq, g].tolist()
+            assert idx[:len(sel)] == sel and all(x == -1 for x in idx[len(sel):])
+            for h in range(g * b.group, (g + 1) * b.group):
+                qh = b.q[seq, h].double()
+                kk, vv = keys[sel], _values_of(b, seq, g)[sel]
+                ref = torch.nn.functional.scaled_dot_product_attention(
+                    qh.reshape(1, 1, 1, -1), kk.reshape(1, 1, -1, b.head_dim),
+                    vv.reshape(1, 1, -1, b.head_dim)).reshape(-1)
+                assert torch.allclose(st["out"][seq, h].double(), ref, rtol=0, atol=2e-7)
+                ref_lse = torch.logsumexp((kk @ qh) * scale, 0)
+                assert abs(float(st["lse"][seq, h]) - float(ref_lse)) < 1e-5
+
+
+def test_token_topk_covering_the_sequence_equals_dense():
+    b = _small(seq_lens=[37, 16, 5])
+    st = oracle.token_step(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens, 64)
+    dout, dlse, _ = oracle.attend(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens)
+    assert torch.allclose(st["out"], dout, rtol=0, atol=1e-6)
+    assert torch.allclose(st["lse"], dlse, rtol=0, atol=1e-6)
+
+
+def test_token_topk_with_keys_constant_per_block_equals_block_topk():
+    # every block's 16 keys equal: a block's tokens tie, so the top 16k tokens
+    # are the tokens of the k best blocks, and the two baselines attend alike
+    b = _small(batch=2, seq_lens=[160, 96], head_dim=16, top_k=3)
+    b.k_cache[:] = b.k_cache[:, :, :1, :]
+    k = 3
+    blk = oracle.sparse_step(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens, k)
+    tok = oracle.token_step(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens, 16 * k)
+    for seq in range(b.batch):
+        for g in range(b.num_kv_heads):
+            blocks = blk["indices"][seq, g].tolist()
+            want = [16 * j + t for j in blocks for t in range(16)]
+            assert tok["indices"][seq, g].tolist() == want
+    assert torch.allclose(tok["out"], blk["out"], rtol=0, atol=1e-6)
