@@ -75,9 +75,12 @@ def algorithmic_bytes(seq_lens, num_q_heads, num_kv_heads, head_dim, top_k, elem
       dense:        table (4*n_b per sequence) + q and out (2*r*D*e) + all K,V (2*L*D*e)
       local:        the same over the most recent min(k, n_b) blocks: their table
                     entries (4*k_b per sequence), q and out, K,V of their valid tokens
+      token:        the token-level baseline with a budget of 16*k tokens: table (4*n_b
+                    per sequence), q and out, every valid key (L*D*e) and the K,V
+                    of the kept tokens (2*min(16k, L)*D*e)
     """
     r, D, e, P = num_q_heads // num_kv_heads, head_dim, elem_bytes, page
-    cen = sel = att = dense = local = 0
+    cen = sel = att = dense = local = token = 0
     for b, L in enumerate([int(x) for x in seq_lens]):
         nb = (L + P - 1) // P
         kb = min(top_k, nb)
@@ -86,6 +89,7 @@ def algorithmic_bytes(seq_lens, num_q_heads, num_kv_heads, head_dim, top_k, elem
         dense += 4 * nb
         local += 4 * kb
         local_toks = L - P * (nb - kb)
+        token += 4 * nb
         for g in range(num_kv_heads):
             # valid tokens of the selected blocks: exact when the selection is
             # given, else every selected block full (or all of L when k >= n_b)
@@ -95,8 +99,9 @@ def algorithmic_bytes(seq_lens, num_q_heads, num_kv_heads, head_dim, top_k, elem
             att += 8 * top_k + 2 * r * D * e + 2 * toks * D * e
             dense += 2 * r * D * e + 2 * L * D * e
             local += 2 * r * D * e + 2 * local_toks * D * e
+            token += 2 * r * D * e + L * D * e + 2 * min(P * top_k, L) * D * e
     return {"centroid": cen, "select": sel, "attend": att, "step": cen + sel + att,
-            "dense": dense, "local": local}
+            "dense": dense, "local": local, "token": token}
 
 
 # ---------------------------------------------------------------- helpers
@@ -314,6 +319,26 @@ def main(argv=None):
         check(f_loc(*reps[i % len(reps)]["calls"]["loc"]))
     torch.cuda.synchronize()
     local_ms = 1e3 * (time.perf_counter() - t0) / args.steps
+
+    # token-level baseline (budget 16 * top_k tokens), same inputs, one workspace
+    tws = btk.new_token_workspace(prob, 16 * k, dev)
+    P_ = ctypes.byref(prob)
+    pp = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    tok_calls = [(P_, pp(r["d"].q), pp(r["d"].k_cache), pp(r["d"].v_cache), pp(r["d"].block_table),
+                  pp(r["d"].seq_lens), 16 * k, None, pp(r["dout"]), None, pp(tws), tws.numel(), hs)
+                 for r in reps]
+    f_tok = lib.btk_token_topk_attend
+    for i in range(3):
+        check(f_tok(*tok_calls[i % len(reps)]))
+    torch.cuda.synchronize()
+    tok_steps = max(1, args.steps // 4)
+    t0 = time.perf_counter()
+    for i in range(tok_steps):
+        check(f_tok(*tok_calls[i % len(reps)]))
+    torch.cuda.synchronize()
+    token_ms = 1e3 * (time.perf_counter() - t0) / tok_steps
+    if btk.workspace_error_bits(tws):
+        raise RuntimeError("device-side input guard fired during the token-level baseline")
     for r in reps:
         if btk.workspace_error_bits(r["ws"]):
             raise RuntimeError("device-side input guard fired during the benchmark")
@@ -380,6 +405,12 @@ def main(argv=None):
                          "frac_of_peak": round(nbytes["local"] / (local_ms * 1e-3) / 1e9
                                                / HBM_PEAK_GBPS, 4),
                          "bytes_per_step": nbytes["local"]},
+        "token_topk": {"top_tokens": 16 * k, "value": round(B / (token_ms * 1e-3), 1),
+                       "unit": "query-tokens/s", "ms_per_step": round(token_ms, 5),
+                       "gbps": round(nbytes["token"] / (token_ms * 1e-3) / 1e9, 1),
+                       "frac_of_peak": round(nbytes["token"] / (token_ms * 1e-3) / 1e9
+                                             / HBM_PEAK_GBPS, 4),
+                       "bytes_per_step": nbytes["token"]},
         "graph_replay": None if graph_ms is None else {
             "ms_per_step": round(graph_ms, 5), "value": round(B / (graph_ms * 1e-3), 1),
             "step_gbps": round(nbytes["step"] / (graph_ms * 1e-3) / 1e9, 1)},

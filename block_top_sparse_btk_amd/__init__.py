@@ -77,6 +77,10 @@ def _lib():
         lib.btk_dense_attend.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.btk_local_attend.restype = st
         lib.btk_local_attend.argtypes = [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
+        lib.btk_token_workspace_bytes.restype = sz
+        lib.btk_token_workspace_bytes.argtypes = [P, i32]
+        lib.btk_token_topk_attend.restype = st
+        lib.btk_token_topk_attend.argtypes = [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
         lib.btk_decode_step.restype = st
         lib.btk_decode_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
         _LIB = lib
@@ -278,6 +282,44 @@ def btk_local_attend(q, k_cache, v_cache, block_table, seq_lens, window_blocks, 
                                  _stream(dev))
     _check(st, "btk_local_attend")
     return out
+
+
+def btk_token_workspace_bytes(problem: btk_problem_t, top_tokens: int) -> int:
+    return int(_lib().btk_token_workspace_bytes(ctypes.byref(problem), int(top_tokens)))
+
+
+def new_token_workspace(problem: btk_problem_t, top_tokens: int, device) -> torch.Tensor:
+    """A zero-filled workspace for btk_token_topk_attend."""
+    n = btk_token_workspace_bytes(problem, top_tokens)
+    if n == 0:
+        raise ValueError("invalid problem or top_tokens for this library build")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def btk_token_topk_attend(q, k_cache, v_cache, block_table, seq_lens, top_tokens, workspace,
+                          token_indices=None, out=None, lse=None, sm_scale: float = 0.0,
+                          problem: Optional[btk_problem_t] = None):
+    """Token-level top-k baseline; returns (out [B, Hq, D], token_indices or None)."""
+    dev = q.device
+    problem = problem or make_problem(q, k_cache, block_table, sm_scale)
+    out = torch.empty_like(q) if out is None else out
+    _check_shapes(problem, q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
+                  seq_lens=seq_lens, out=out, lse=lse)
+    if token_indices is not None and tuple(token_indices.shape) != (
+            problem.batch, problem.num_kv_heads, int(top_tokens)):
+        raise ValueError("token_indices must be [B, Hkv, top_tokens]")
+    ti = _dev(token_indices, "token_indices", torch.int32, dev) if token_indices is not None else None
+    lp = _dev(lse, "lse", torch.float32, dev) if lse is not None else None
+    st = _lib().btk_token_topk_attend(ctypes.byref(problem), _dev(q, "q", None, dev),
+                                      _dev(k_cache, "k_cache", q.dtype, dev),
+                                      _dev(v_cache, "v_cache", q.dtype, dev),
+                                      _dev(block_table, "block_table", torch.int32, dev),
+                                      _dev(seq_lens, "seq_lens", torch.int32, dev),
+                                      int(top_tokens), ti, _dev(out, "out", q.dtype, dev), lp,
+                                      _dev(workspace, "workspace", torch.uint8, dev),
+                                      workspace.numel(), _stream(dev))
+    _check(st, "btk_token_topk_attend")
+    return out, token_indices
 
 
 def btk_decode_step(q, k_cache, v_cache, block_table, seq_lens, centroids, top_k, workspace,

@@ -7,7 +7,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["api.hip", "centroid.hip", "select.hip", "attend.hip", "step.hip"]
+SOURCES = ["api.hip", "centroid.hip", "select.hip", "attend.hip", "step.hip", "token.hip"]
 LIB = os.path.join(HERE, "libbtk.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -68,6 +68,23 @@ WorkspaceLayout workspace_layout(const Dims &d, int top_k) {
     return w;
 }
 
+TokenWorkspaceLayout token_workspace_layout(const Dims &d, int top_tokens) {
+    const size_t units = (size_t)d.B * d.Hkv;
+    TokenWorkspaceLayout w;
+    w.cap = top_tokens < d.max_blocks ? top_tokens : d.max_blocks;
+    const AttendPlan ap = plan_attend(d, w.cap, false);
+    const size_t row = (size_t)d.group() * d.D + 2 * (size_t)d.group();
+    w.counters = 256;
+    w.scores = w.counters + align256(units * sizeof(uint32_t));
+    w.entries = w.scores + align256(units * (size_t)d.max_blocks * kPage * sizeof(float));
+    w.counts = w.entries + align256(units * (size_t)w.cap * sizeof(uint32_t));
+    w.ranges = w.counts + align256(units * sizeof(uint32_t));
+    w.att_counters = w.ranges + align256(2 * units * sizeof(uint32_t));
+    w.partials = w.att_counters + align256(units * sizeof(uint32_t));
+    w.total = w.partials + align256(units * (size_t)ap.nsplit_max * row * sizeof(float));
+    return w;
+}
+
 }  // namespace btk
 
 extern "C" {
@@ -186,6 +203,44 @@ btk_status_t btk_local_attend(const btk_problem_t *problem, const void *q, const
                                          reinterpret_cast<float *>(ws + w.partials),
                                          reinterpret_cast<uint32_t *>(ws + w.att_counters),
                                          reinterpret_cast<uint32_t *>(ws), (hipStream_t)stream));
+}
+
+size_t btk_token_workspace_bytes(const btk_problem_t *problem, int32_t top_tokens) {
+    btk::Dims d;
+    if (check_problem(problem, &d) != BTK_OK || top_tokens < 1 || top_tokens > btk::kMaxTopTokens)
+        return 0;
+    return btk::token_workspace_layout(d, top_tokens).total;
+}
+
+btk_status_t btk_token_topk_attend(const btk_problem_t *problem, const void *q,
+                                   const void *k_cache, const void *v_cache,
+                                   const int32_t *block_table, const int32_t *seq_lens,
+                                   int32_t top_tokens, int32_t *token_indices, void *out,
+                                   float *lse, void *workspace, size_t workspace_bytes,
+                                   void *stream) {
+    btk::Dims d;
+    btk_status_t st = check_problem(problem, &d);
+    if (st != BTK_OK) return st;
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out) return BTK_ERR_NULL;
+    if (top_tokens < 1 || top_tokens > btk::kMaxTopTokens) return BTK_ERR_SHAPE;
+    const btk::TokenWorkspaceLayout w = btk::token_workspace_layout(d, top_tokens);
+    if (!workspace || workspace_bytes < w.total) return BTK_ERR_WORKSPACE;
+    char *ws = static_cast<char *>(workspace);
+    uint32_t *err = reinterpret_cast<uint32_t *>(ws);
+    uint32_t *entries = reinterpret_cast<uint32_t *>(ws + w.entries);
+    uint32_t *counts = reinterpret_cast<uint32_t *>(ws + w.counts);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = btk::launch_token_select(
+        d, q, k_cache, block_table, seq_lens, top_tokens, w.cap,
+        reinterpret_cast<float *>(ws + w.scores), reinterpret_cast<uint32_t *>(ws + w.counters),
+        entries, counts, reinterpret_cast<uint32_t *>(ws + w.ranges), token_indices, err, s);
+    if (e != hipSuccess) return hip_status(e);
+    const btk::AttendPlan plan = btk::plan_attend(d, w.cap, false);
+    return hip_status(btk::launch_attend(d, plan, 3, q, k_cache, v_cache, block_table, seq_lens,
+                                         reinterpret_cast<const int32_t *>(entries), w.cap, out,
+                                         lse, reinterpret_cast<float *>(ws + w.partials),
+                                         reinterpret_cast<uint32_t *>(ws + w.att_counters), err,
+                                         s, counts));
 }
 
 btk_status_t btk_decode_step(const btk_problem_t *problem, const void *q, const void *k_cache,

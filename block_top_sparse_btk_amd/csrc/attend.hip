@@ -38,6 +38,7 @@ hipError_t launch_dtype(const Dims &d, const AttendPlan &plan, int mode, AttendA
                         hipStream_t stream) {
     if (mode == kAll) return launch<T, D, kAll>(d, plan, a, stream);
     if (mode == kRecent) return launch<T, D, kRecent>(d, plan, a, stream);
+    if (mode == kMasked) return launch<T, D, kMasked>(d, plan, a, stream);
     return launch<T, D, kSelected>(d, plan, a, stream);
 }
 
@@ -76,10 +77,10 @@ hipError_t launch_attend(const Dims &d, const AttendPlan &plan, int mode, const 
                          const void *k_cache, const void *v_cache, const int32_t *block_table,
                          const int32_t *seq_lens, const int32_t *indices, int top_k, void *out,
                          float *lse, float *partials, uint32_t *counters, uint32_t *err,
-                         hipStream_t stream) {
+                         hipStream_t stream, const uint32_t *counts) {
     AttendArgs a{q, k_cache, v_cache, block_table, seq_lens, indices, out, lse, partials,
                  counters, err, d.Hq, d.Hkv, d.num_pages, d.max_blocks, top_k, plan.bps,
-                 plan.nsplit_max, d.sm_scale * 1.44269504088896340736f, nullptr};
+                 plan.nsplit_max, d.sm_scale * 1.44269504088896340736f, nullptr, counts};
     if (d.dtype == 0)
         return d.D == 128 ? launch_dtype<uint16_t, 128>(d, plan, mode, a, stream)
                           : launch_dtype<uint16_t, 64>(d, plan, mode, a, stream);

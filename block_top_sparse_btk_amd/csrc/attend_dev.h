@@ -88,13 +88,14 @@ struct Mfma<uint16_t, D> {
             f.x[n] = __builtin_bit_cast(short4_t,
                                         *reinterpret_cast<const uint2 *>(p + 16 * kPage * n));
     }
-    __device__ static void mask_v(VFrag &f, int v, int lane) {
+    // zero the values of tokens outside `mask` (bit t = token t of the page)
+    __device__ static void mask_v(VFrag &f, uint32_t mask, int lane) {
         const int t0 = 4 * (lane >> 4);
 #pragma unroll
         for (int n = 0; n < NV; ++n)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                if (t0 + e >= v) f.x[n][e] = 0;
+                if (!((mask >> (t0 + e)) & 1u)) f.x[n][e] = 0;
     }
     __device__ static float round_p(float p) { return bf16_bits_to_f32(f32_to_bf16_bits(p)); }
     __device__ static void pv(floatx4_t (&o)[NV], const float (&p)[4], const VFrag &v) {
@@ -158,14 +159,14 @@ struct Mfma<float, D> {
 #pragma unroll
         for (int n = 0; n < NV; ++n) f.x[n] = *reinterpret_cast<const float4 *>(p + 16 * kPage * n);
     }
-    __device__ static void mask_v(VFrag &f, int v, int lane) {
-        const int t0 = 4 * (lane >> 4);
+    __device__ static void mask_v(VFrag &f, uint32_t mask, int lane) {
+        const uint32_t m = mask >> (4 * (lane >> 4));
 #pragma unroll
         for (int n = 0; n < NV; ++n) {
-            if (t0 + 0 >= v) f.x[n].x = 0.f;
-            if (t0 + 1 >= v) f.x[n].y = 0.f;
-            if (t0 + 2 >= v) f.x[n].z = 0.f;
-            if (t0 + 3 >= v) f.x[n].w = 0.f;
+            if (!(m & 1u)) f.x[n].x = 0.f;
+            if (!(m & 2u)) f.x[n].y = 0.f;
+            if (!(m & 4u)) f.x[n].z = 0.f;
+            if (!(m & 8u)) f.x[n].w = 0.f;
         }
     }
     __device__ static float round_p(float p) { return p; }
@@ -193,7 +194,15 @@ struct AttendArgs {
     // launch, [units][top_k] words (tag << 32 | block index); an entry is valid
     // once its tag equals the launch's own
     const uint64_t *tagged;
+    // token-level baseline only (NULL otherwise): the number of packed entries
+    // (block | token mask << 16) per unit in `indices`
+    const uint32_t *counts;
 };
+
+// Tokens 0 .. v-1 of a page.
+__device__ __forceinline__ uint32_t valid_mask(int v) {
+    return v >= kPage ? 0xFFFFu : (1u << v) - 1u;
+}
 
 // Spin bound of the decode step's wait for a unit's selection (~0.1 s).
 constexpr uint32_t kReadySpinLimit = 1u << 22;
@@ -218,9 +227,11 @@ __device__ __forceinline__ void store_out<float>(float *p, float x) {
 }
 
 // Which block list an item attends over: the unit's selection (S4), every block
-// of the sequence (S5, the dense comparison), or the most recent min(top_k, n_b)
-// blocks (the local-window baseline, where top_k is the window in blocks).
-enum ListMode : int { kSelected = 0, kAll = 1, kRecent = 2 };
+// of the sequence (S5, the dense comparison), the most recent min(top_k, n_b)
+// blocks (the local-window baseline, where top_k is the window in blocks), or
+// counts[unit] packed entries (block | token mask << 16) of the token-level
+// baseline, where top_k is the list capacity and only the masked tokens count.
+enum ListMode : int { kSelected = 0, kAll = 1, kRecent = 2, kMasked = 3 };
 
 // One (unit, split) item: attention of the unit's query group over its share of
 // the block list, kG blocks per pipeline stage.  smem: the wave-merge / split-merge area (see launch
@@ -237,7 +248,7 @@ __device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int s
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int b = unit / a.Hkv, g = unit % a.Hkv;
     const int r = a.Hq / a.Hkv;
-    constexpr bool LISTED = MODE == kSelected;
+    constexpr bool LISTED = MODE == kSelected || MODE == kMasked;
     // a selection has top_k entries whatever the length, so its entries are
     // requested together with the length
     const int per_wave = a.bps / kWaves;
@@ -256,14 +267,19 @@ __device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int s
         }
     }
     const int L = a.seq_lens[b];
+    const int count = MODE == kMasked ? (int)a.counts[unit] : 0;
     if (L < 1 || L > a.max_blocks * kPage) {
         if (split == 0 && tid == 0) flag_error(a.err, kErrSeqLen);
         return;
     }
     const int nb = (L + kPage - 1) / kPage;
-    const int len = MODE == kAll ? nb : MODE == kRecent ? min(a.top_k, nb) : a.top_k;
+    const int len = MODE == kAll      ? nb
+                    : MODE == kRecent ? min(a.top_k, nb)
+                    : MODE == kMasked ? min(count, a.top_k)
+                                      : a.top_k;
     const int nsplit = (len + a.bps - 1) / a.bps;
     if (split >= nsplit) return;
+    if (MODE == kMasked) cnt = max(0, min(cnt, len - w0));
     if (!LISTED) {
         const int i0 = split * a.bps, i1 = min(len, i0 + a.bps);
         w0 = i0 + wave * per_wave;
@@ -284,11 +300,16 @@ __device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int s
         }
     }
 
-    // lane m < cnt holds page id and valid tokens of this wave's m-th entry
-    // (page -1 and 0 tokens for a skipped or invalid entry)
-    int my_page = -1, my_v = 0;
+    // lane m < cnt holds page id and token mask (bit t: token t of the page is
+    // attended) of this wave's m-th entry (page -1 and mask 0 for a skipped or
+    // invalid entry)
+    int my_page = -1;
+    uint32_t my_mask = 0u;
     if (lane < cnt) {
-        int j = LISTED ? (int32_t)(uint32_t)entry : nb - len + w0 + lane;  // kAll: len = nb
+        int j = MODE == kMasked ? (int)(entry & 0xFFFFu)
+                : LISTED        ? (int32_t)(uint32_t)entry
+                                : nb - len + w0 + lane;  // kAll: len = nb
+        const uint32_t entry_mask = MODE == kMasked ? (uint32_t)(entry >> 16) & 0xFFFFu : 0xFFFFu;
         if (LISTED && j >= nb) {
             flag_error(a.err, kErrIndex);
             j = -1;
@@ -297,7 +318,7 @@ __device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int s
             const int p = a.bt[(size_t)b * a.max_blocks + j];
             if (p >= 0 && p < a.num_pages) {
                 my_page = p;
-                my_v = min(kPage, L - j * kPage);
+                my_mask = valid_mask(min(kPage, L - j * kPage)) & entry_mask;
             } else {
                 flag_error(a.err, kErrPage);
             }
@@ -334,18 +355,18 @@ __device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int s
     auto compute = [&](auto &s, int m0) {
         constexpr int kN = std::remove_reference_t<decltype(s)>::kN;
         float sv[kN][4];
-        int vv[kN];
+        uint32_t mk[kN];
         float gmax = -INFINITY;
 #pragma unroll
         for (int u = 0; u < kN; ++u) {
             const int m = min(m0 + u, cnt - 1);
-            // valid tokens of this slot, 0 for a repeated or invalid entry (wave-uniform)
-            vv[u] = m0 + u < cnt ? __builtin_amdgcn_readlane(my_v, m) : 0;
+            // token mask of this slot, 0 for a repeated or invalid entry (wave-uniform)
+            mk[u] = m0 + u < cnt ? (uint32_t)__builtin_amdgcn_readlane((int)my_mask, m) : 0u;
             const floatx4_t acc = F::qk(s.k[u], qf);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = 4 * (lane >> 4) + e;
-                sv[u][e] = t < vv[u] ? acc[e] * a.scale_log2 : -INFINITY;
+                sv[u][e] = ((mk[u] >> t) & 1u) ? acc[e] * a.scale_log2 : -INFINITY;
                 gmax = fmaxf(gmax, sv[u][e]);
             }
         }
@@ -372,7 +393,7 @@ __device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int s
                 z_run += pe;  // the normaliser (and lse) use the unrounded weights
                 p[e] = F::round_p(pe);
             }
-            if (vv[u] < kPage) F::mask_v(s.v[u], vv[u], lane);  // no 0 * garbage in P.V
+            if (mk[u] != 0xFFFFu) F::mask_v(s.v[u], mk[u], lane);  // no 0 * garbage in P.V
             F::pv(o, p, s.v[u]);
         }
     };

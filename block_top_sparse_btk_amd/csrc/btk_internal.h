@@ -14,6 +14,7 @@ constexpr int kPage = 16;           // tokens per page (block); all kernels assu
 constexpr int kMaxBlocksPerSeq = 8192;  // select holds one key per block in LDS
 constexpr int kMaxGroup = 16;       // query heads per KV head: MFMA tile rows
 constexpr int kMaxStepBatch = 1024; // decode step: per-sequence item prefix kept in LDS
+constexpr int kMaxTopTokens = kMaxBlocksPerSeq * kPage;  // token-level baseline budget
 
 // error bits in workspace word 0
 constexpr uint32_t kErrSeqLen = 1u;
@@ -61,6 +62,10 @@ __device__ __forceinline__ void store_relaxed_i32(int32_t *p, int32_t v) {
 }
 
 __device__ __forceinline__ int32_t load_relaxed_i32(const int32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t load_relaxed_u32(const uint32_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -137,12 +142,33 @@ hipError_t launch_select(const Dims &d, const SelectPlan &plan, const void *q,
                          const int32_t *seq_lens, int top_k, int32_t *indices, float *scores,
                          uint32_t *counters, uint32_t *err, hipStream_t stream);
 
-// mode: 0 the selected blocks, 1 every block, 2 the most recent min(top_k, n_b)
+// mode: 0 the selected blocks, 1 every block, 2 the most recent min(top_k, n_b),
+// 3 counts[unit] packed entries (block | token mask << 16) in `indices`, top_k
+// being the list capacity
 hipError_t launch_attend(const Dims &d, const AttendPlan &plan, int mode, const void *q,
                          const void *k_cache, const void *v_cache, const int32_t *block_table,
                          const int32_t *seq_lens, const int32_t *indices, int top_k, void *out,
                          float *lse, float *partials, uint32_t *counters, uint32_t *err,
-                         hipStream_t stream);
+                         hipStream_t stream, const uint32_t *counts = nullptr);
+
+// Token-level baseline: scores of every valid token, then per unit the
+// top_tokens best as packed entries (cap = min(max_blocks, top_tokens) per unit)
+// with their count, and token positions when token_idx is not NULL.
+hipError_t launch_token_select(const Dims &d, const void *q, const void *k_cache,
+                               const int32_t *block_table, const int32_t *seq_lens,
+                               int top_tokens, int cap, float *scores, uint32_t *counters,
+                               uint32_t *entries, uint32_t *counts, uint32_t *ranges,
+                               int32_t *token_idx, uint32_t *err, hipStream_t stream);
+
+// Workspace of the token-level baseline (bytes, each region 256-aligned):
+//   [0, 256) error word; counters; scores B*Hkv*max_blocks*16 float;
+//   entries B*Hkv*cap uint32; counts B*Hkv uint32; score ranges B*Hkv*2 uint32;
+//   attend counters; partials
+struct TokenWorkspaceLayout {
+    size_t counters, scores, entries, counts, ranges, att_counters, partials, total;
+    int cap;
+};
+TokenWorkspaceLayout token_workspace_layout(const Dims &d, int top_tokens);
 
 hipError_t launch_decode_step(const Dims &d, const SelectPlan &sp, const AttendPlan &ap,
                               const void *q, const void *k_cache, const void *v_cache,

@@ -202,7 +202,7 @@ hipError_t launch_decode_step(const Dims &d, const SelectPlan &sp, const AttendP
                           d.sm_scale, k_cache, first_pos, centroids};
     a.t = att::AttendArgs{q, k_cache, v_cache, block_table, seq_lens, indices, out, lse, partials,
                           att_counters, err, d.Hq, d.Hkv, d.num_pages, d.max_blocks, top_k, ap.bps,
-                          ap.nsplit_max, d.sm_scale * 1.44269504088896340736f, tagged};
+                          ap.nsplit_max, d.sm_scale * 1.44269504088896340736f, tagged, nullptr};
     a.tagged = tagged;
     a.queue = queue;
     a.B = d.B;

@@ -184,6 +184,30 @@ btk_status_t btk_local_attend(const btk_problem_t *problem, const void *q, const
                               const int32_t *seq_lens, int32_t window_blocks, void *out,
                               float *lse, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Token-level top-k attention baseline ("oracle top-k"): for unit (b, g) every
+ * valid token t < L_b is scored like a one-token block,
+ *     s_t = sm_scale * qbar . K_t,   qbar = mean of q[b][h] over the group,
+ * the K_b = min(top_tokens, L_b) highest-scoring tokens are kept (equal scores
+ * go to the lower position), and every query head of the group attends over
+ * exactly those tokens as in btk_sparse_attend.  It reads every key (the
+ * retrieval cost the block method avoids) and is the upper bound the block
+ * method is compared with.  (scime summary of "Kinetics: Rethinking Test-Time
+ * Scaling Law", "Experimental setup": oracle top-k attention among the
+ * baselines; "Limitations": the sparse results use it as their upper bound.)
+ *   top_tokens     1 .. 131072 (a budget of k blocks is top_tokens = 16 k)
+ *   token_indices  out [B][Hkv][top_tokens] int32 logical positions of the kept
+ *                  tokens, ascending, -1 padded; or NULL
+ *   out out [B][Hq][D] dtype;  lse out [B][Hq] float32, or NULL
+ *   workspace      btk_token_workspace_bytes(problem, top_tokens) bytes, zero-filled
+ *                  once before the first use and reusable as for the other calls */
+size_t btk_token_workspace_bytes(const btk_problem_t *problem, int32_t top_tokens);
+btk_status_t btk_token_topk_attend(const btk_problem_t *problem, const void *q,
+                                   const void *k_cache, const void *v_cache,
+                                   const int32_t *block_table, const int32_t *seq_lens,
+                                   int32_t top_tokens, int32_t *token_indices, void *out,
+                                   float *lse, void *workspace, size_t workspace_bytes,
+                                   void *stream);
+
 /* One whole decode step in a single launch: S1 for the touched pages (as
  * btk_centroid_update with first_pos; none when first_pos is NULL), then S2+S3
  * (as btk_select) and S4 (as btk_sparse_attend), with results identical to

@@ -26,12 +26,13 @@ def n_blocks(seq_lens, page=16):
     return [(int(L) + page - 1) // page for L in seq_lens.tolist()]
 
 
-def check_indices(gpu_idx, ora_idx, ora_scores, seq_lens, top_k, margin=MARGIN):
-    """Assert the margin rule on every unit; returns statistics."""
+def check_indices(gpu_idx, ora_idx, ora_scores, seq_lens, top_k, margin=MARGIN, page=16):
+    """Assert the margin rule on every unit; returns statistics.  page=1 applies
+    the rule to token positions (the token-level baseline)."""
     gpu_idx, ora_idx = gpu_idx.cpu(), ora_idx.cpu()
     B, H, K = ora_idx.shape
     assert K == top_k and tuple(gpu_idx.shape) == (B, H, K)
-    nbs = n_blocks(seq_lens)
+    nbs = n_blocks(seq_lens, page)
     stats = dict(units=0, strict=0, near_tie=0, differ=0, min_strict_margin=math.inf)
     equal = torch.zeros((B, H), dtype=torch.bool)
     for b in range(B):

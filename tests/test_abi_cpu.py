@@ -149,3 +149,23 @@ def test_local_attend_and_decode_step_validate_before_launch():
     assert lib.btk_decode_step(ctypes.byref(big), *args(wsn=1 << 40)) == btk.BTK_ERR_UNSUPPORTED
     bad = ctypes.byref(_problem(head_dim=96))
     assert lib.btk_decode_step(bad, *args()) == btk.BTK_ERR_UNSUPPORTED
+
+
+def test_token_baseline_validates_before_launch():
+    lib = btk._lib()
+    prob = _problem()
+    p = ctypes.byref(prob)
+    need = btk.btk_token_workspace_bytes(prob, 64)
+    assert need > btk.btk_workspace_bytes(prob, 4)  # holds every token's score
+    assert btk.btk_token_workspace_bytes(prob, 0) == 0
+    assert btk.btk_token_workspace_bytes(prob, 131073) == 0
+    ok = lambda **o: [o.get(n, FAKE) for n in ("q", "k", "v", "bt", "sl")] + \
+        [o.get("t", 64), None, o.get("out", FAKE), None, o.get("ws", FAKE), o.get("wsn", need),
+         None]  # noqa: E731
+    assert lib.btk_token_topk_attend(p, *ok(k=None)) == btk.BTK_ERR_NULL
+    assert lib.btk_token_topk_attend(p, *ok(out=None)) == btk.BTK_ERR_NULL
+    assert lib.btk_token_topk_attend(p, *ok(t=0)) == btk.BTK_ERR_SHAPE
+    assert lib.btk_token_topk_attend(p, *ok(t=131073)) == btk.BTK_ERR_SHAPE
+    assert lib.btk_token_topk_attend(p, *ok(wsn=need - 1)) == btk.BTK_ERR_WORKSPACE
+    assert lib.btk_token_topk_attend(p, *ok(ws=None)) == btk.BTK_ERR_WORKSPACE
+    assert lib.btk_token_topk_attend(None, *ok()) == btk.BTK_ERR_NULL

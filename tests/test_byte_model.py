@@ -50,3 +50,13 @@ def test_local_window_bytes():
     toks = 1000 - 16 * (nb - w)  # the last block holds 1000 - 16*62 = 8 tokens
     assert toks == 3 * 16 + 8
     assert part["local"] == 4 * w + 2 * (2 * r * D * e + 2 * toks * D * e)
+
+
+def test_token_baseline_bytes():
+    # every key once, plus the kept tokens' K and V (16k of them, or all of L)
+    r, D, e, k = 4, 128, 2, 2
+    out = bench.algorithmic_bytes([1000, 20], 8, 2, D, k, e)
+    want = 4 * 63 + 4 * 2
+    for L in (1000, 20):
+        want += 2 * (2 * r * D * e + L * D * e + 2 * min(16 * k, L) * D * e)
+    assert out["token"] == want
