@@ -163,6 +163,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="skip the HIP-graph replay measurement")
+    ap.add_argument("--no-best-of-n", dest="best_of_n", action="store_false",
+                    help="skip the shared-prefix (Best-of-N) selection comparison")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run plain 1 GiB device copies (counter calibration)")
     args = ap.parse_args(argv)
@@ -242,20 +244,21 @@ def main(argv=None):
         sep_step(reps[i % len(reps)])
     torch.cuda.synchronize()
 
-    # timed region: exactly K steps, bracketed by synchronize; a HIP event pair
-    # on the library's stream brackets every launch (the step is one kernel)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # timed region: exactly K steps (one kernel each), bracketed by synchronize
+    # and by one HIP event pair on the library's stream; the launch average is
+    # the event time over K, so it counts the gaps between launches too (an
+    # event pair around every launch would add its own ~8 us to each step)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(args.steps):
-        evs[i][0].record(stream)
         check(f_step(*reps[i % len(reps)]["calls"]["step"]))
-        evs[i][1].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = 1e3 * wall / args.steps
-    step_us = 1e3 * sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    step_us = 1e3 * ev0.elapsed_time(ev1) / args.steps
 
     # the same step as three calls: whole-step time, then a per-kernel pass
     t0 = time.perf_counter()
@@ -346,6 +349,48 @@ def main(argv=None):
         if not torch.equal(r["out"], r["sout"]):
             raise RuntimeError("single-launch and three-call steps disagree")
 
+    # Best-of-N: the Qwen3-30B-A3B-shaped batch (16 samples sharing a 2048-token
+    # prompt), select vs the shared-prefix select that reads the prompt's centroid
+    # rows once per KV head (identical results)
+    bon = None
+    if args.best_of_n:
+        b4 = synth.make_config(4)
+        d4 = b4.to(dev)
+        p4 = btk.make_problem(d4.q, d4.k_cache, d4.block_table)
+        c4 = torch.zeros((b4.num_pages, b4.num_kv_heads, b4.head_dim), device=dev)
+        btk.btk_centroid_update(d4.k_cache, d4.block_table, d4.seq_lens, c4, problem=p4)
+        w4 = btk.new_workspace(p4, b4.top_k, dev)
+        i4 = torch.empty((b4.batch, b4.num_kv_heads, b4.top_k), dtype=torch.int32, device=dev)
+        j4 = torch.empty_like(i4)
+        prefix = b4.notes.get("shared_prefix", 2048) // 16
+        run_sel = lambda: btk.btk_select(d4.q, c4, d4.block_table, d4.seq_lens, b4.top_k, w4,  # noqa: E731
+                                         indices=i4, problem=p4)
+        run_shr = lambda: btk.btk_select_shared(d4.q, c4, d4.block_table, d4.seq_lens,  # noqa: E731
+                                                [0, b4.batch], [prefix], b4.top_k, w4,
+                                                indices=j4, problem=p4)
+        times = {}
+        for name, fn in (("select", run_sel), ("select_shared", run_shr)):
+            for _ in range(5):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(args.steps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times[name] = 1e3 * e0.elapsed_time(e1) / args.steps
+        if not torch.equal(i4, j4) or btk.workspace_error_bits(w4):
+            raise RuntimeError("shared-prefix selection disagrees with select")
+        sel4 = algorithmic_bytes(b4.seq_lens.tolist(), b4.num_q_heads, b4.num_kv_heads,
+                                 b4.head_dim, b4.top_k, 2)["select"]
+        saved = (b4.batch - 1) * b4.num_kv_heads * prefix * 4 * b4.head_dim
+        bon = {"workload": "qwen3-30b-a3b-shaped Best-of-N: B=16 samples sharing a 2048-token "
+                           "prompt + 30720 private tokens, Hq=32, Hkv=4, D=128, bf16, top_k=64",
+               "select_us": round(times["select"], 2),
+               "select_shared_us": round(times["select_shared"], 2),
+               "select_bytes": sel4, "select_shared_bytes": sel4 - saved,
+               "note": "same inputs, caches warm for both; identical indices"}
+
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -411,6 +456,7 @@ def main(argv=None):
                        "frac_of_peak": round(nbytes["token"] / (token_ms * 1e-3) / 1e9
                                              / HBM_PEAK_GBPS, 4),
                        "bytes_per_step": nbytes["token"]},
+        "best_of_n": bon,
         "graph_replay": None if graph_ms is None else {
             "ms_per_step": round(graph_ms, 5), "value": round(B / (graph_ms * 1e-3), 1),
             "step_gbps": round(nbytes["step"] / (graph_ms * 1e-3) / 1e9, 1)},

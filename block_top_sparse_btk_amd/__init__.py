@@ -71,6 +71,8 @@ def _lib():
         lib.btk_centroid_update.argtypes = [P, vp, vp, vp, vp, vp, vp]
         lib.btk_select.restype = st
         lib.btk_select.argtypes = [P, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
+        lib.btk_select_shared.restype = st
+        lib.btk_select_shared.argtypes = [P, vp, vp, vp, vp, i32, vp, vp, i32, vp, vp, vp, sz, vp]
         lib.btk_sparse_attend.restype = st
         lib.btk_sparse_attend.argtypes = [P, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
         lib.btk_dense_attend.restype = st
@@ -215,6 +217,37 @@ def btk_select(q, centroids, block_table, seq_lens, top_k, workspace, indices=No
                            _dev(workspace, "workspace", torch.uint8, dev), workspace.numel(),
                            _stream(dev))
     _check(st, "btk_select")
+    return indices
+
+
+def btk_select_shared(q, centroids, block_table, seq_lens, group_start, prefix_blocks, top_k,
+                      workspace, indices=None, scores=None, sm_scale: float = 0.0,
+                      problem: Optional[btk_problem_t] = None):
+    """S2+S3 reading each group's shared prefix once; group_start (num_groups + 1)
+    and prefix_blocks (num_groups) are host sequences of ints.  Returns indices."""
+    dev = q.device
+    if problem is None:
+        num_pages, hkv, dim = centroids.shape
+        problem = btk_problem_t(q.shape[0], q.shape[1], hkv, dim, PAGE_SIZE, num_pages,
+                                block_table.shape[1], _dtype_code(q), float(sm_scale))
+    if indices is None:
+        indices = torch.empty((problem.batch, problem.num_kv_heads, int(top_k)), dtype=torch.int32,
+                              device=dev)
+    _check_shapes(problem, q=q, block_table=block_table, seq_lens=seq_lens, centroids=centroids,
+                  indices=indices, scores=scores, top_k=top_k)
+    gs = (ctypes.c_int32 * len(group_start))(*[int(x) for x in group_start])
+    pb = (ctypes.c_int32 * len(prefix_blocks))(*[int(x) for x in prefix_blocks])
+    sp = _dev(scores, "scores", torch.float32, dev) if scores is not None else None
+    st = _lib().btk_select_shared(ctypes.byref(problem), _dev(q, "q", None, dev),
+                                  _dev(centroids, "centroids", torch.float32, dev),
+                                  _dev(block_table, "block_table", torch.int32, dev),
+                                  _dev(seq_lens, "seq_lens", torch.int32, dev),
+                                  len(prefix_blocks), ctypes.cast(gs, ctypes.c_void_p),
+                                  ctypes.cast(pb, ctypes.c_void_p), int(top_k),
+                                  _dev(indices, "indices", torch.int32, dev), sp,
+                                  _dev(workspace, "workspace", torch.uint8, dev), workspace.numel(),
+                                  _stream(dev))
+    _check(st, "btk_select_shared")
     return indices
 
 

@@ -142,6 +142,44 @@ btk_status_t btk_select(const btk_problem_t *problem, const void *q, const float
                                          reinterpret_cast<uint32_t *>(ws), (hipStream_t)stream));
 }
 
+btk_status_t btk_select_shared(const btk_problem_t *problem, const void *q,
+                               const float *centroids, const int32_t *block_table,
+                               const int32_t *seq_lens, int32_t num_groups,
+                               const int32_t *group_start, const int32_t *prefix_blocks,
+                               int32_t top_k, int32_t *indices, float *scores, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+    btk::Dims d;
+    btk_status_t st = check_problem(problem, &d);
+    if (st != BTK_OK) return st;
+    if (!q || !centroids || !block_table || !seq_lens || !indices || !group_start ||
+        !prefix_blocks)
+        return BTK_ERR_NULL;
+    if (!top_k_ok(top_k)) return BTK_ERR_SHAPE;
+    if (num_groups < 1 || num_groups > btk::kMaxPrefixGroups) return BTK_ERR_UNSUPPORTED;
+    const btk::SelectPlan plan = btk::plan_select(d);
+    btk::PrefixGroups pg{};
+    pg.n = num_groups;
+    if (group_start[0] < 0) return BTK_ERR_SHAPE;
+    for (int g = 0; g < num_groups; ++g) {
+        const int a0 = group_start[g], a1 = group_start[g + 1];
+        if (a1 <= a0 || a1 > d.B) return BTK_ERR_SHAPE;
+        if (a1 - a0 > btk::kMaxGroupMembers) return BTK_ERR_UNSUPPORTED;
+        if (prefix_blocks[g] < 0 || prefix_blocks[g] > d.max_blocks) return BTK_ERR_SHAPE;
+        pg.start[g] = a0;
+        pg.blocks[g] = prefix_blocks[g];
+        pg.item0[g + 1] = pg.item0[g] + d.Hkv * ((prefix_blocks[g] + plan.chunk - 1) / plan.chunk);
+    }
+    pg.start[num_groups] = group_start[num_groups];
+    const btk::WorkspaceLayout w = btk::workspace_layout(d, top_k);
+    if (!workspace || workspace_bytes < w.total) return BTK_ERR_WORKSPACE;
+    char *ws = static_cast<char *>(workspace);
+    float *sc = scores ? scores : reinterpret_cast<float *>(ws + w.scores);
+    return hip_status(btk::launch_select_shared(
+        d, plan, pg, q, centroids, block_table, seq_lens, top_k, indices, sc,
+        reinterpret_cast<uint32_t *>(ws + w.sel_counters), reinterpret_cast<uint32_t *>(ws),
+        (hipStream_t)stream));
+}
+
 btk_status_t btk_sparse_attend(const btk_problem_t *problem, const void *q, const void *k_cache,
                                const void *v_cache, const int32_t *block_table,
                                const int32_t *seq_lens, const int32_t *indices, int32_t top_k,

@@ -21,6 +21,7 @@ constexpr uint32_t kErrSeqLen = 1u;
 constexpr uint32_t kErrPage = 2u;
 constexpr uint32_t kErrIndex = 4u;
 constexpr uint32_t kErrTimeout = 8u;  // decode step: a wait for published data gave up
+constexpr uint32_t kErrPrefix = 16u;  // a declared shared prefix differs between members
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) short short4_t;
@@ -116,6 +117,19 @@ struct AttendPlan {
 };
 
 SelectPlan plan_select(const Dims &d);
+
+// Best-of-N groups for the shared-prefix selection: sequences [start[g],
+// start[g+1]) share their first blocks[g] block-table entries; item0[g] is the
+// first shared-scoring workgroup of group g (item0[n] = their number).  Small
+// enough to travel as a kernel argument.
+constexpr int kMaxPrefixGroups = 64;
+constexpr int kMaxGroupMembers = 32;
+struct PrefixGroups {
+    int n;
+    int start[kMaxPrefixGroups + 1];
+    int blocks[kMaxPrefixGroups];
+    int item0[kMaxPrefixGroups + 1];
+};
 AttendPlan plan_attend(const Dims &d, int list_len_max, bool dense);
 
 // Workspace layout (bytes, each region 256-aligned):
@@ -145,6 +159,14 @@ hipError_t launch_select(const Dims &d, const SelectPlan &plan, const void *q,
 // mode: 0 the selected blocks, 1 every block, 2 the most recent min(top_k, n_b),
 // 3 counts[unit] packed entries (block | token mask << 16) in `indices`, top_k
 // being the list capacity
+// S2+S3 with the shared prefixes of `pg` scored once per (group, KV head):
+// results identical to launch_select.
+hipError_t launch_select_shared(const Dims &d, const SelectPlan &plan, const PrefixGroups &pg,
+                                const void *q, const float *centroids,
+                                const int32_t *block_table, const int32_t *seq_lens, int top_k,
+                                int32_t *indices, float *scores, uint32_t *counters,
+                                uint32_t *err, hipStream_t stream);
+
 hipError_t launch_attend(const Dims &d, const AttendPlan &plan, int mode, const void *q,
                          const void *k_cache, const void *v_cache, const int32_t *block_table,
                          const int32_t *seq_lens, const int32_t *indices, int top_k, void *out,

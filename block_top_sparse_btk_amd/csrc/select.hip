@@ -1,28 +1,207 @@
 // S2 + S3 stand-alone: group block scoring and top-k selection in one launch
 // (device code in select_dev.h).  Grid = units x chunks; the workgroup that
-// finishes a unit's last chunk selects its top-k blocks.
+// finishes a unit's last chunk selects its top-k blocks.  The shared-prefix
+// form adds, ahead of them, items that score each group's shared prefix once
+// (shared_item); the members' own chunks then cover their private blocks.
 #include "select_dev.h"
 
 namespace btk {
 using namespace sel;
 namespace {
 
+// Shared-prefix scoring (Best-of-N): a workgroup per (group, KV head, chunk of
+// the shared prefix) reads each shared centroid row once and scores it against
+// every member's mean query, with the same arithmetic as score_chunk, so the
+// scores are bit-identical to scoring every member alone; it checks that every
+// member's table slice equals the first member's.  It then counts itself in on
+// every member unit (whose total includes the group's shared chunks) and selects
+// for the members it completed, which is rare: these items are dispatched first.
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
-    __shared__ float qraw[kMaxGroup * D];
+__device__ __forceinline__ void shared_item(const SelectArgs &a, const PrefixGroups &pg, int item,
+                                            float *qs, int *pages, int *flags, TopkSmem &tk) {
+    constexpr int LPR = 16, VPL = D / LPR, RPI = kWave / LPR, KU = 4;
+    constexpr int ROWS = kWaves * RPI * KU;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    int g = 0;
+    while (g + 1 < pg.n && pg.item0[g + 1] <= item) ++g;
+    const int P = pg.blocks[g], first = pg.start[g], M = pg.start[g + 1] - first;
+    const int ncs = (P + a.chunk - 1) / a.chunk;
+    const int rel = item - pg.item0[g], gk = rel / ncs, c = rel % ncs;
+    const int j0 = c * a.chunk, n = min(P, j0 + a.chunk) - j0;
+    const int r = a.Hq / a.Hkv;
+
+    // set-up in one round trip: the first member's page ids, every member's
+    // queries (summed in head order, as score_chunk does) and length
+    if (tid < M) flags[tid] = 0;
+    for (int i = tid; i < n; i += kThreads) {
+        int p = a.bt[(size_t)first * a.max_blocks + j0 + i];
+        if (p < 0 || p >= a.num_pages) {
+            flag_error(a.err, kErrPage);
+            p = -1;
+        }
+        pages[i] = p;
+    }
+    for (int idx = tid; idx < M * D; idx += kThreads) {
+        const int m = idx / D, dd = idx % D;
+        const T *qp = static_cast<const T *>(a.q) + ((size_t)(first + m) * a.Hq + (size_t)gk * r) * D + dd;
+        float x[kMaxGroup];
+#pragma unroll
+        for (int h = 0; h < kMaxGroup; ++h) x[h] = h < r ? load_q<T>(qp + h * D) : 0.f;
+        float s = 0.f;
+        for (int h = 0; h < r; ++h) s += x[h];
+        qs[idx] = s * (a.scale / (float)r);
+    }
+    __syncthreads();
+    {  // every member's slice against the first member's (loads in flight together)
+        constexpr int kV = 8;
+        for (int i0 = tid; i0 < (M - 1) * n; i0 += kThreads * kV) {
+            int x[kV], y[kV];
+#pragma unroll
+            for (int u = 0; u < kV; ++u) {
+                const int i = min(i0 + u * kThreads, (M - 1) * n - 1);
+                const int m = 1 + i / n, j = i % n;
+                x[u] = a.bt[(size_t)(first + m) * a.max_blocks + j0 + j];
+                y[u] = pages[j];
+            }
+#pragma unroll
+            for (int u = 0; u < kV; ++u)
+                if (x[u] != y[u] && y[u] >= 0) flags[kMaxGroupMembers] = 1;
+        }
+    }
+
+    const int col = lane % LPR, rsub = lane / LPR;
+    typedef float4 Row[VPL / 4];
+    auto issue = [&](Row (&cv)[KU], int base) {
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+            const int row = min(base + u * kWaves * RPI + wave * RPI + rsub, n - 1);
+            const int p = max(pages[row], 0);
+            const float4 *src = reinterpret_cast<const float4 *>(
+                a.cent + ((size_t)p * a.Hkv + gk) * D + col * VPL);
+#pragma unroll
+            for (int v = 0; v < VPL / 4; ++v) cv[u][v] = src[v];
+        }
+    };
+    auto reduce = [&](const Row (&cv)[KU], int base) {
+        for (int m = 0; m < M; ++m) {
+            float qf[VPL];
+#pragma unroll
+            for (int e = 0; e < VPL; ++e) qf[e] = qs[m * D + col * VPL + e];
+            float *sc = a.scores + ((size_t)(first + m) * a.Hkv + gk) * a.max_blocks + j0;
+#pragma unroll
+            for (int u = 0; u < KU; ++u) {
+                const int row = base + u * kWaves * RPI + wave * RPI + rsub;
+                const float s = row16_sum(row_partial<VPL>(qf, cv[u]));
+                if (col == 0 && row < n) store_relaxed(sc + row, pages[row] >= 0 ? s : -INFINITY);
+            }
+        }
+    };
+    if (n > 0) {
+        Row ca[KU], cb[KU];
+        issue(ca, 0);
+        for (int base = 0;;) {
+            issue(cb, base + ROWS);
+            reduce(ca, base);
+            base += ROWS;
+            if (base >= n) break;
+            issue(ca, base + ROWS);
+            reduce(cb, base);
+            base += ROWS;
+            if (base >= n) break;
+        }
+    }
+
+    // count in on every member unit (scores stored first)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0 && flags[kMaxGroupMembers]) flag_error(a.err, kErrPrefix);
+    int nb = 0;
+    if (tid < M) {
+        const int L = a.seq_lens[first + tid];
+        if (L >= 1 && L <= a.max_blocks * kPage) {
+            nb = (L + kPage - 1) / kPage;
+            const uint32_t total = (uint32_t)(ncs + max(1, (nb - P + a.chunk - 1) / a.chunk));
+            const int unit = (first + tid) * a.Hkv + gk;
+            const uint32_t prev = __hip_atomic_fetch_add(&a.counters[unit], 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            if (prev == total - 1) {
+                __hip_atomic_store(&a.counters[unit], 0u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                flags[tid] = nb;
+            }
+        }
+    }
+    __syncthreads();
+    // the members this item completed: up to 2048 blocks one wave each (four at
+    // a time, each wave with its own LDS), longer ones with the whole workgroup
+    __builtin_amdgcn_s_setprio(3);
+    for (int m = wave; m < M; m += kWaves) {
+        const int nbm = flags[m];
+        if (nbm == 0 || nbm > 32 * kWave) continue;
+        const int unit = (first + m) * a.Hkv + gk;
+        TopkSmem w{tk.hist + wave * (256 + kWave), tk.cand + wave * 4 * kWave,
+                   tk.above + wave * kWave, tk.equal + wave * kWave, tk.red, tk.scan_red, tk.keys};
+        const PlainScores src{a.scores + (size_t)unit * a.max_blocks};
+        const TopkOut out{a.indices + (size_t)unit * a.top_k, nullptr, 0u};
+        if (min(a.top_k, nbm) == nbm) {
+            for (int i = lane; i < a.top_k; i += kWave) out.put(i, i < nbm ? i : -1);
+        } else if (nbm <= 8 * kWave) {
+            select_topk_wave<8>(src, nbm, a.top_k, out, w);
+        } else if (nbm <= 16 * kWave) {
+            select_topk_wave<16>(src, nbm, a.top_k, out, w);
+        } else {
+            select_topk_wave<32>(src, nbm, a.top_k, out, w);
+        }
+    }
+    for (int m = 0; m < M; ++m) {
+        const int nbm = flags[m];
+        if (nbm <= 32 * kWave) continue;
+        const int unit = (first + m) * a.Hkv + gk;
+        __syncthreads();
+        select_topk(PlainScores{a.scores + (size_t)unit * a.max_blocks}, nbm, a.top_k,
+                    TopkOut{a.indices + (size_t)unit * a.top_k, nullptr, 0u}, tk);
+    }
+    __builtin_amdgcn_s_setprio(0);
+}
+
+template <typename T, int D, bool SHARED>
+__global__ __launch_bounds__(kThreads, 5) void select_kernel(SelectArgs a, PrefixGroups pg) {
+    __shared__ float qraw[(SHARED ? kMaxGroupMembers : kMaxGroup) * D];
     __shared__ float qs[D];
     __shared__ int pages[kMaxChunk];
     __shared__ float sc_lds[kMaxChunk];
     __shared__ int is_last;
-    __shared__ uint32_t hist[256 + kWave], cand[4 * kWave], above[kWave], equal[kWave];
+    // one set per wave in the shared-prefix form (its items may select for
+    // several members at once)
+    constexpr int kSets = SHARED ? kWaves : 1;
+    __shared__ uint32_t hist[kSets * (256 + kWave)], cand[kSets * 4 * kWave], above[kSets * kWave],
+        equal[kSets * kWave];
     __shared__ uint32_t red[2 * kWaves];
     __shared__ int scan_red[kWaves];
+    __shared__ int flags[SHARED ? kMaxGroupMembers + 1 : 1];
     extern __shared__ uint32_t keys[];  // max_blocks words, long contexts only
     ScoreSmem sm{qraw, qs, pages, sc_lds, &is_last};
     TopkSmem tk{hist, cand, above, equal, red, scan_red, keys};
-    const int unit = blockIdx.x / a.nchunk_max, c = blockIdx.x % a.nchunk_max;
+    int item = blockIdx.x;
+    int skip = 0, extra = 0;  // a shared prefix, scored by shared items
+    if (SHARED) {
+        if (item < pg.item0[pg.n]) {  // the shared items come first
+            if (threadIdx.x <= kMaxGroupMembers) flags[threadIdx.x] = 0;
+            __syncthreads();
+            shared_item<T, D>(a, pg, item, qraw, pages, flags, tk);
+            return;
+        }
+        item -= pg.item0[pg.n];
+        const int b = item / a.nchunk_max / a.Hkv;
+        for (int g = 0; g < pg.n; ++g)
+            if (pg.start[g] <= b && b < pg.start[g + 1]) {
+                skip = pg.blocks[g];
+                extra = (skip + a.chunk - 1) / a.chunk;
+            }
+    }
+    const int unit = item / a.nchunk_max, c = item % a.nchunk_max;
     int nb = 0;
-    if (!score_chunk<T, D, 4>(a, unit, c, sm, nullptr, nb)) return;
+    if (!score_chunk<T, D, 4>(a, unit, c, sm, nullptr, nb, skip, extra)) return;
     // the selecting wave(s) take issue priority over scanning waves on the SIMD
     __builtin_amdgcn_s_setprio(3);
     select_topk(PlainScores{a.scores + (size_t)unit * a.max_blocks}, nb, a.top_k,
@@ -30,12 +209,17 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
 }
 
 template <typename T, int D>
-hipError_t launch(const Dims &d, const SelectPlan &plan, SelectArgs a, hipStream_t stream) {
+hipError_t launch(const Dims &d, const SelectPlan &plan, SelectArgs a, const PrefixGroups *pg,
+                  hipStream_t stream) {
     const size_t grid = (size_t)d.B * d.Hkv * plan.nchunk_max;
     // LDS key copy only for the workgroup-wide selection of long contexts
     const size_t lds = d.max_blocks > 32 * kWave ? sizeof(uint32_t) * (size_t)d.max_blocks : 0;
-    hipLaunchKernelGGL((select_kernel<T, D>), dim3((unsigned)grid), dim3(kThreads), lds, stream,
-                       a);
+    if (pg)
+        hipLaunchKernelGGL((select_kernel<T, D, true>), dim3((unsigned)(grid + pg->item0[pg->n])),
+                           dim3(kThreads), lds, stream, a, *pg);
+    else
+        hipLaunchKernelGGL((select_kernel<T, D, false>), dim3((unsigned)grid), dim3(kThreads),
+                           lds, stream, a, PrefixGroups{});
     return hipGetLastError();
 }
 
@@ -61,10 +245,25 @@ hipError_t launch_select(const Dims &d, const SelectPlan &plan, const void *q,
                  d.Hq, d.Hkv, d.num_pages, d.max_blocks, top_k, plan.chunk, plan.nchunk_max,
                  d.sm_scale, nullptr, nullptr, nullptr};
     if (d.dtype == 0)
-        return d.D == 128 ? launch<uint16_t, 128>(d, plan, a, stream)
-                          : launch<uint16_t, 64>(d, plan, a, stream);
-    return d.D == 128 ? launch<float, 128>(d, plan, a, stream)
-                      : launch<float, 64>(d, plan, a, stream);
+        return d.D == 128 ? launch<uint16_t, 128>(d, plan, a, nullptr, stream)
+                          : launch<uint16_t, 64>(d, plan, a, nullptr, stream);
+    return d.D == 128 ? launch<float, 128>(d, plan, a, nullptr, stream)
+                      : launch<float, 64>(d, plan, a, nullptr, stream);
+}
+
+hipError_t launch_select_shared(const Dims &d, const SelectPlan &plan, const PrefixGroups &pg,
+                                const void *q, const float *centroids,
+                                const int32_t *block_table, const int32_t *seq_lens, int top_k,
+                                int32_t *indices, float *scores, uint32_t *counters,
+                                uint32_t *err, hipStream_t stream) {
+    SelectArgs a{q, centroids, block_table, seq_lens, indices, scores, counters, err,
+                 d.Hq, d.Hkv, d.num_pages, d.max_blocks, top_k, plan.chunk, plan.nchunk_max,
+                 d.sm_scale, nullptr, nullptr, nullptr};
+    if (d.dtype == 0)
+        return d.D == 128 ? launch<uint16_t, 128>(d, plan, a, &pg, stream)
+                          : launch<uint16_t, 64>(d, plan, a, &pg, stream);
+    return d.D == 128 ? launch<float, 128>(d, plan, a, &pg, stream)
+                      : launch<float, 64>(d, plan, a, &pg, stream);
 }
 
 }  // namespace btk

@@ -481,10 +481,14 @@ __device__ __forceinline__ float row_partial(const float (&qf)[VPL], const float
 // first refreshes the centroids of the chunk's touched pages).  Returns true in
 // the workgroup that completed the unit's last chunk, which must then select;
 // nb receives the unit's block count.  KU: rows per lane per pipeline stage
-// (two stages of 4 * 4 * KU rows are in flight).
+// (two stages of 4 * 4 * KU rows are in flight).  skip: leading blocks scored
+// elsewhere (a shared prompt prefix) by `extra` other workgroups that count in
+// on the unit too; the chunks cover blocks [skip, n_b), and a unit with nothing
+// left still has chunk 0, which only counts in.
 template <typename T, int D, int KU>
 __device__ __forceinline__ bool score_chunk(const SelectArgs &a, int unit, int c, ScoreSmem &sm,
-                                            float *crow, int &nb_out) {
+                                            float *crow, int &nb_out, int skip = 0,
+                                            int extra = 0) {
     constexpr int LPR = 16;                       // lanes per centroid row: one DPP row
     constexpr int VPL = D / LPR;                  // floats per lane per row (8 or 4)
     constexpr int RPI = kWave / LPR;              // rows per wave per load step
@@ -493,7 +497,7 @@ __device__ __forceinline__ bool score_chunk(const SelectArgs &a, int unit, int c
     const int b = unit / a.Hkv, g = unit % a.Hkv;
     const int r = a.Hq / a.Hkv;
     int32_t *out = a.indices + (size_t)unit * a.top_k;
-    const int j0 = c * a.chunk;
+    const int j0 = skip + c * a.chunk;
 
     // setup in one round trip: the group's queries, the chunk's slice of the
     // block-table row (entries past the sequence are read but never used), the
@@ -514,9 +518,9 @@ __device__ __forceinline__ bool score_chunk(const SelectArgs &a, int unit, int c
         return false;
     }
     const int nb = (L + kPage - 1) / kPage;
-    const int nchunks = (nb + a.chunk - 1) / a.chunk;
+    const int nchunks = max(1, (nb - skip + a.chunk - 1) / a.chunk);
     if (c >= nchunks) return false;
-    const int n = min(nb, j0 + a.chunk) - j0;
+    const int n = max(0, min(nb, j0 + a.chunk) - j0);
     for (int i = tid; i < n; i += kThreads) {  // the entries this thread loaded
         const int p = sm.pages[i];
         if (p < 0 || p >= a.num_pages) {
@@ -558,17 +562,19 @@ __device__ __forceinline__ bool score_chunk(const SelectArgs &a, int unit, int c
             if (col == 0 && row < n) sm.sc[row] = sm.pages[row] >= 0 ? s : -INFINITY;
         }
     };
-    Row ca[KU], cb[KU];
-    issue(ca, 0);
-    for (int base = 0;;) {
-        issue(cb, base + ROWS);
-        reduce(ca, base);
-        base += ROWS;
-        if (base >= n) break;
-        issue(ca, base + ROWS);
-        reduce(cb, base);
-        base += ROWS;
-        if (base >= n) break;
+    if (n > 0) {
+        Row ca[KU], cb[KU];
+        issue(ca, 0);
+        for (int base = 0;;) {
+            issue(cb, base + ROWS);
+            reduce(ca, base);
+            base += ROWS;
+            if (base >= n) break;
+            issue(ca, base + ROWS);
+            reduce(cb, base);
+            base += ROWS;
+            if (base >= n) break;
+        }
     }
 
     // decode step: pages touched since the last step get their centroid
@@ -597,7 +603,7 @@ __device__ __forceinline__ bool score_chunk(const SelectArgs &a, int unit, int c
     nb_out = nb;
     float *sc = a.scores + (size_t)unit * a.max_blocks;
     for (int i = tid; i < n; i += kThreads) store_relaxed(sc + j0 + i, sm.sc[i]);
-    return arrive_last(&a.counters[unit], (uint32_t)nchunks, sm.flag);
+    return arrive_last(&a.counters[unit], (uint32_t)(nchunks + extra), sm.flag);
 }
 
 }  // namespace sel

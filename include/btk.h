@@ -24,8 +24,9 @@
  *    an out-of-range page id, length or index is skipped, and, where the call
  *    has a workspace, sets a sticky bit in workspace word 0 (bit 0: a length
  *    outside [1, max_blocks_per_seq * page_size]; bit 1: a page id outside
- *    [0, num_pages); bit 2: a block index outside [0, n_b); bit 3: a decode step's wait for a
- *    unit's selection gave up, which no valid call is expected to reach).
+ *    [0, num_pages); bit 2: a block index outside [0, n_b); bit 3: a wait for data
+ *    published inside a launch gave up, which no valid call is expected to reach;
+ *    bit 4: a declared shared prefix differs between group members).
  *    Results for such inputs are unspecified.
  *
  * Notation: B = batch, Hq / Hkv = query / KV heads, r = Hq / Hkv (the query
@@ -142,6 +143,29 @@ btk_status_t btk_select(const btk_problem_t *problem, const void *q, const float
                         const int32_t *block_table, const int32_t *seq_lens, int32_t top_k,
                         int32_t *indices, float *scores, void *workspace,
                         size_t workspace_bytes, void *stream);
+
+/* S2 + S3 for Best-of-N batches, reading each shared prompt page once.  The
+ * pages' cost model counts a prompt's KV as read once for all N samples (Pith
+ * review, "What carries the argument", and its referee report on the
+ * Best-of-N memory term); here the centroid rows of a group's shared prefix are
+ * read once per KV head and scored against every member's mean query.  Results
+ * (indices, scores) are bit-identical to btk_select's.
+ *   num_groups     1 .. 64
+ *   group_start    host [num_groups + 1]: group g is the sequences
+ *                  group_start[g] .. group_start[g+1]-1 (1 .. 32 of them,
+ *                  increasing, within [0, batch)); sequences outside every group
+ *                  are scored alone
+ *   prefix_blocks  host [num_groups]: the members of group g share their first
+ *                  prefix_blocks[g] block-table entries (0 .. max_blocks_per_seq);
+ *                  a member whose entries differ sets workspace bit 4 (results
+ *                  are then unspecified)
+ *   the rest as btk_select (same workspace size). */
+btk_status_t btk_select_shared(const btk_problem_t *problem, const void *q,
+                               const float *centroids, const int32_t *block_table,
+                               const int32_t *seq_lens, int32_t num_groups,
+                               const int32_t *group_start, const int32_t *prefix_blocks,
+                               int32_t top_k, int32_t *indices, float *scores, void *workspace,
+                               size_t workspace_bytes, void *stream);
 
 /* S4 -- exact softmax attention over the selected blocks.  (Pith review, "What
  * carries the argument": attention runs over only the retrieved blocks.)

@@ -169,3 +169,34 @@ def test_token_baseline_validates_before_launch():
     assert lib.btk_token_topk_attend(p, *ok(wsn=need - 1)) == btk.BTK_ERR_WORKSPACE
     assert lib.btk_token_topk_attend(p, *ok(ws=None)) == btk.BTK_ERR_WORKSPACE
     assert lib.btk_token_topk_attend(None, *ok()) == btk.BTK_ERR_NULL
+
+
+def test_select_shared_validates_groups_before_launch():
+    lib = btk._lib()
+    prob = _problem()  # batch 4, max_blocks 20
+    p = ctypes.byref(prob)
+    need = btk.btk_workspace_bytes(prob, 4)
+    I32 = ctypes.c_int32
+
+    def call(starts, blocks, ws=FAKE, wsn=need, k=4):
+        gs = (I32 * len(starts))(*starts)
+        pb = (I32 * max(1, len(blocks)))(*blocks) if blocks else None
+        return lib.btk_select_shared(p, FAKE, FAKE, FAKE, FAKE, len(blocks),
+                                     ctypes.cast(gs, ctypes.c_void_p),
+                                     ctypes.cast(pb, ctypes.c_void_p) if pb is not None else None,
+                                     k, FAKE, None, ws, wsn, None)
+    assert call([0, 3], [5], ws=None) == btk.BTK_ERR_WORKSPACE
+    assert call([0, 3], [5], wsn=need - 1) == btk.BTK_ERR_WORKSPACE
+    assert call([0, 3], [5], k=0) == btk.BTK_ERR_SHAPE
+    assert call([0, 3], []) == btk.BTK_ERR_NULL            # no prefix array
+    assert call([0, 3, 2], [5, 5]) == btk.BTK_ERR_SHAPE     # not increasing
+    assert call([0, 5], [5]) == btk.BTK_ERR_SHAPE           # past the batch
+    assert call([-1, 2], [5]) == btk.BTK_ERR_SHAPE
+    assert call([0, 2], [21]) == btk.BTK_ERR_SHAPE          # longer than max_blocks
+    assert call([0, 2], [-1]) == btk.BTK_ERR_SHAPE
+    big = _problem(batch=40, max_blocks_per_seq=8)
+    gs = (I32 * 2)(0, 33)
+    pb = (I32 * 1)(4)
+    assert lib.btk_select_shared(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, 1,
+                                 ctypes.cast(gs, ctypes.c_void_p), ctypes.cast(pb, ctypes.c_void_p),
+                                 4, FAKE, None, FAKE, 1 << 40, None) == btk.BTK_ERR_UNSUPPORTED

@@ -492,3 +492,54 @@ def test_token_topk_parity(label, spec):
     check_outputs(out.cpu(), st["out"], bt.dtype, stats["equal_mask"], bt.group)
     _say(f"[token]   ok units={stats['units']} near_tie={stats['near_tie']} "
          f"differ={stats['differ']} max_abs_out={err:.2e}")
+
+
+# ------------------------------------------------------------------ shared-prefix selection
+
+def _select_both(bt, group_start, prefix_blocks, expect_err=0):
+    d = bt.to(DEV)
+    prob = btk.make_problem(d.q, d.k_cache, d.block_table)
+    cent = torch.zeros((bt.num_pages, bt.num_kv_heads, bt.head_dim), device=DEV)
+    btk.btk_centroid_update(d.k_cache, d.block_table, d.seq_lens, cent, problem=prob)
+    ws1, ws2 = btk.new_workspace(prob, bt.top_k, DEV), btk.new_workspace(prob, bt.top_k, DEV)
+    sc1 = torch.full((bt.batch, bt.num_kv_heads, bt.max_blocks), float("nan"), device=DEV)
+    sc2 = sc1.clone()
+    i1 = btk.btk_select(d.q, cent, d.block_table, d.seq_lens, bt.top_k, ws1, scores=sc1,
+                        problem=prob)
+    for _ in range(2):  # twice: counters re-armed
+        i2 = btk.btk_select_shared(d.q, cent, d.block_table, d.seq_lens, group_start,
+                                   prefix_blocks, bt.top_k, ws2, scores=sc2, problem=prob)
+    torch.cuda.synchronize()
+    assert btk.workspace_error_bits(ws1) == 0
+    assert btk.workspace_error_bits(ws2) == expect_err
+    return i1.cpu(), i2.cpu(), sc1.cpu(), sc2.cpu()
+
+
+def test_shared_prefix_selection_equals_select_on_best_of_n():
+    bt = _workload(4)  # 16 samples sharing a 2048-token prompt (128 pages)
+    _say("[shared] config 4, one group of 16, prefix 128 blocks")
+    i1, i2, s1, s2 = _select_both(bt, [0, 16], [128])
+    assert torch.equal(i1, i2)
+    for b, nb in enumerate(n_blocks(bt.seq_lens)):
+        assert torch.equal(s1[b, :, :nb], s2[b, :, :nb])
+
+
+def test_shared_prefix_selection_groups_and_edges():
+    bt = synth.make_batch(name="shared-groups", batch=7, num_q_heads=8, num_kv_heads=2,
+                          head_dim=128, seq_lens=[700, 512, 1000, 530, 2200, 600, 900], top_k=9,
+                          seed=61, table="shared", shared_prefix=512)
+    # groups: two members with the whole shared prefix, a single member, three
+    # members declaring only part of it, one with prefix 0; sequence 6 alone
+    starts, blocks = [0, 2, 3, 5, 6], [32, 32, 7, 0]
+    _say("[shared] custom groups")
+    i1, i2, s1, s2 = _select_both(bt, starts, blocks)
+    assert torch.equal(i1, i2)
+    for b, nb in enumerate(n_blocks(bt.seq_lens)):
+        assert torch.equal(s1[b, :, :nb], s2[b, :, :nb])
+
+
+def test_shared_prefix_mismatch_is_flagged():
+    bt = synth.make_batch(name="not-shared", batch=3, num_q_heads=4, num_kv_heads=1, head_dim=128,
+                          seq_lens=[300, 400, 500], top_k=4, seed=62, table="shuffled")
+    _say("[shared] declared prefix that the tables do not share")
+    _select_both(bt, [0, 3], [4], expect_err=16)
