@@ -140,7 +140,7 @@ __device__ __forceinline__ void shared_item(const SelectArgs &a, const PrefixGro
         if (nbm == 0 || nbm > 32 * kWave) continue;
         const int unit = (first + m) * a.Hkv + gk;
         TopkSmem w{tk.hist + wave * (256 + kWave), tk.cand + wave * 4 * kWave,
-                   tk.above + wave * kWave, tk.equal + wave * kWave, tk.red, tk.scan_red, tk.keys};
+                   tk.red, tk.scan_red, tk.keys};
         const PlainScores src{a.scores + (size_t)unit * a.max_blocks};
         const TopkOut out{a.indices + (size_t)unit * a.top_k, nullptr, 0u};
         if (min(a.top_k, nbm) == nbm) {
@@ -174,14 +174,13 @@ __global__ __launch_bounds__(kThreads, 5) void select_kernel(SelectArgs a, Prefi
     // one set per wave in the shared-prefix form (its items may select for
     // several members at once)
     constexpr int kSets = SHARED ? kWaves : 1;
-    __shared__ uint32_t hist[kSets * (256 + kWave)], cand[kSets * 4 * kWave], above[kSets * kWave],
-        equal[kSets * kWave];
+    __shared__ uint32_t hist[kSets * (256 + kWave)], cand[kSets * 4 * kWave];
     __shared__ uint32_t red[2 * kWaves];
     __shared__ int scan_red[kWaves];
     __shared__ int flags[SHARED ? kMaxGroupMembers + 1 : 1];
     extern __shared__ uint32_t keys[];  // max_blocks words, long contexts only
     ScoreSmem sm{qraw, qs, pages, sc_lds, &is_last};
-    TopkSmem tk{hist, cand, above, equal, red, scan_red, keys};
+    TopkSmem tk{hist, cand, red, scan_red, keys};
     int item = blockIdx.x;
     int skip = 0, extra = 0;  // a shared prefix, scored by shared items
     if (SHARED) {
@@ -226,11 +225,13 @@ hipError_t launch(const Dims &d, const SelectPlan &plan, SelectArgs a, const Pre
 }  // namespace
 
 SelectPlan plan_select(const Dims &d) {
-    // Enough workgroups to cover 256 CUs several times over, with chunks large
-    // enough that the per-workgroup setup (mean query, page list) stays small.
+    // At least about 1024 chunks (four per resident workgroup at two per CU),
+    // each as large as that allows: a chunk's setup (queries, page list, length)
+    // and its closing store-and-count are round trips in which the workgroup
+    // streams nothing, so fewer, larger chunks keep more bytes in flight.
     const size_t rows = (size_t)d.B * d.Hkv * d.max_blocks;
     int chunk = 64;
-    while (chunk < kMaxChunk && rows / (size_t)(chunk * 2) >= 2048) chunk *= 2;
+    while (chunk < kMaxChunk && rows / (size_t)(chunk * 2) >= 1024) chunk *= 2;
     SelectPlan p;
     p.chunk = chunk;
     p.nchunk_max = (d.max_blocks + chunk - 1) / chunk;

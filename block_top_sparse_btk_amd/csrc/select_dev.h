@@ -59,8 +59,6 @@ struct ScoreSmem {
 struct TopkSmem {
     uint32_t *hist;      // [256 + 64] radix bins + per-lane spare bins
     uint32_t *cand;      // [256] compacted candidates
-    uint32_t *above;     // [64] bitmap words
-    uint32_t *equal;     // [64]
     uint32_t *red;       // [2 * kWaves]
     int *scan_red;       // [kWaves]
     uint32_t *keys;      // [max_blocks] keys, workgroup-wide path only
@@ -261,7 +259,7 @@ template <int KMAX, typename Src>
 __device__ __forceinline__ void select_topk_wave(const Src &src, int nb, int top_k,
                                                  const TopkOut &out, TopkSmem &sm) {
     static_assert(KMAX <= 32, "one bitmap word per lane covers 2048 blocks");
-    uint32_t *hist = sm.hist, *cand = sm.cand, *above_bits = sm.above, *equal_bits = sm.equal;
+    uint32_t *hist = sm.hist, *cand = sm.cand;
     const int lane = threadIdx.x & (kWave - 1);
     const int kb = min(top_k, nb);
     uint32_t key[KMAX];
@@ -291,6 +289,8 @@ __device__ __forceinline__ void select_topk_wave(const Src &src, int nb, int top
 #pragma unroll
             for (int e = 0; e < 4; ++e) k4[e] = e * kWave + lane < m ? cand[e * kWave + lane] : 0u;
             __builtin_amdgcn_wave_barrier();
+            cand[lane] = 0u;  // the finisher reads all 64 slots: absent keys are 0
+            __builtin_amdgcn_wave_barrier();
             while (lo < hi && m > kWave) {
                 radix_pass(k4, lo, hi, need, hist, lane);
                 m = count_in_range(k4, lo, hi);
@@ -300,17 +300,19 @@ __device__ __forceinline__ void select_topk_wave(const Src &src, int nb, int top
                 // of them (LDS broadcast reads); T is the one of rank `need`
                 compact(k4, lo, hi, cand, lane);
                 __builtin_amdgcn_wave_barrier();
+                // all 64 slots at once (slots from m on hold 0, below every key)
                 const uint32_t mine = lane < m ? cand[lane] : 0u;
+                uint4 c4[kWave / 4];
+#pragma unroll
+                for (int t = 0; t < kWave / 4; ++t) c4[t] = reinterpret_cast<const uint4 *>(cand)[t];
                 int gt = 0, ge = 0;
-                for (int t = 0; t < m; t += 4) {  // m is wave-uniform
-                    const uint4 c4 = reinterpret_cast<const uint4 *>(cand)[t / 4];
-                    const uint32_t cv[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+                for (int t = 0; t < kWave / 4; ++t) {
+                    const uint32_t cv[4] = {c4[t].x, c4[t].y, c4[t].z, c4[t].w};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        if (t + e < m) {
-                            gt += cv[e] > mine ? 1 : 0;
-                            ge += cv[e] >= mine ? 1 : 0;
-                        }
+                        gt += cv[e] > mine ? 1 : 0;
+                        ge += cv[e] >= mine ? 1 : 0;
                     }
                 }
                 const int src_lane =
@@ -322,21 +324,18 @@ __device__ __forceinline__ void select_topk_wave(const Src &src, int nb, int top
     }
     const uint32_t T = lo;
     const int take_eq = need;  // keys equal to T to keep, lowest block index first
-    // bitmaps: word w covers blocks [32w, 32w + 32); slot i's ballot is words 2i, 2i+1
+    // bitmaps: lane l's words cover blocks [32l, 32l + 32), the low or high
+    // half of slot l/2's ballot (lanes from 2*KMAX on hold none)
+    uint32_t a = 0u, e = 0u;
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) {
-        const uint64_t a = __ballot(key[i] > T);
-        const uint64_t e = __ballot(key[i] == T);  // absent keys are 0 < T
-        if (lane == 0) {
-            above_bits[2 * i] = (uint32_t)a;
-            above_bits[2 * i + 1] = (uint32_t)(a >> 32);
-            equal_bits[2 * i] = (uint32_t)e;
-            equal_bits[2 * i + 1] = (uint32_t)(e >> 32);
+        const uint64_t ab = __ballot(key[i] > T);
+        const uint64_t eb = __ballot(key[i] == T);  // absent keys are 0 < T
+        if ((lane >> 1) == i) {
+            a = (lane & 1) ? (uint32_t)(ab >> 32) : (uint32_t)ab;
+            e = (lane & 1) ? (uint32_t)(eb >> 32) : (uint32_t)eb;
         }
     }
-    __builtin_amdgcn_wave_barrier();
-    uint32_t a = lane < 2 * KMAX ? above_bits[lane] : 0u;
-    uint32_t e = lane < 2 * KMAX ? equal_bits[lane] : 0u;
     int e_before = (int)(wave_inclusive_scan((uint32_t)__popc(e)) - (uint32_t)__popc(e));
     while (e && e_before < take_eq) {  // lowest-index equal keys first
         const uint32_t bit = e & (0u - e);

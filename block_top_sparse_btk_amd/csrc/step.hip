@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
     __shared__ int pages[kMaxChunk];
     __shared__ float sc_lds[kMaxChunk];
     __shared__ int flag;
-    __shared__ uint32_t hist[256 + kWave], cand[4 * kWave], above[kWave], equal[kWave];
+    __shared__ uint32_t hist[256 + kWave], cand[4 * kWave];
     __shared__ uint32_t red[2 * kWaves];
     __shared__ int scan_red[kWaves];
     __shared__ float crow[kWaves * D];
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
     // queries while scoring, top-k keys of long contexts, attention merges
     extern __shared__ float dyn[];
     sel::ScoreSmem sm{dyn, qs, pages, sc_lds, &flag};
-    sel::TopkSmem tk{hist, cand, above, equal, red, scan_red, reinterpret_cast<uint32_t *>(dyn)};
+    sel::TopkSmem tk{hist, cand, red, scan_red, reinterpret_cast<uint32_t *>(dyn)};
     const int tid = threadIdx.x;
     const int Hkv = a.s.Hkv;
 
