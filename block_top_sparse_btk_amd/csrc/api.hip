@@ -62,8 +62,8 @@ WorkspaceLayout workspace_layout(const Dims &d, int top_k) {
     w.att_counters = w.sel_counters + align256(units * sizeof(uint32_t));
     w.scores = w.att_counters + align256(units * sizeof(uint32_t));
     w.partials = w.scores + align256(units * d.max_blocks * sizeof(float));
-    w.tagged = w.partials + align256(units * nsplit * row * sizeof(float));
-    w.queue = w.tagged + align256(units * (size_t)top_k * sizeof(uint64_t));
+    w.ready = w.partials + align256(units * nsplit * row * sizeof(float));
+    w.queue = w.ready + align256(units * (size_t)kReadyStride * sizeof(uint32_t));
     w.total = w.queue + 256;
     return w;
 }
@@ -304,7 +304,7 @@ btk_status_t btk_decode_step(const btk_problem_t *problem, const void *q, const 
         reinterpret_cast<float *>(ws + w.partials),
         reinterpret_cast<uint32_t *>(ws + w.sel_counters),
         reinterpret_cast<uint32_t *>(ws + w.att_counters),
-        reinterpret_cast<uint64_t *>(ws + w.tagged), reinterpret_cast<uint32_t *>(ws + w.queue),
+        reinterpret_cast<uint32_t *>(ws + w.ready), reinterpret_cast<uint32_t *>(ws + w.queue),
         reinterpret_cast<uint32_t *>(ws), (hipStream_t)stream));
 }
 

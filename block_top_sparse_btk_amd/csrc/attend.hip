@@ -80,7 +80,7 @@ hipError_t launch_attend(const Dims &d, const AttendPlan &plan, int mode, const 
                          hipStream_t stream, const uint32_t *counts) {
     AttendArgs a{q, k_cache, v_cache, block_table, seq_lens, indices, out, lse, partials,
                  counters, err, d.Hq, d.Hkv, d.num_pages, d.max_blocks, top_k, plan.bps,
-                 plan.nsplit_max, d.sm_scale * 1.44269504088896340736f, nullptr, counts};
+                 plan.nsplit_max, d.sm_scale * 1.44269504088896340736f, counts};
     if (d.dtype == 0)
         return d.D == 128 ? launch_dtype<uint16_t, 128>(d, plan, mode, a, stream)
                           : launch_dtype<uint16_t, 64>(d, plan, mode, a, stream);

@@ -190,10 +190,6 @@ struct AttendArgs {
     uint32_t *counters, *err;
     int Hq, Hkv, num_pages, max_blocks, top_k, bps, nsplit_max;
     float scale_log2;
-    // decode step only (NULL otherwise): the selection as published inside the
-    // launch, [units][top_k] words (tag << 32 | block index); an entry is valid
-    // once its tag equals the launch's own
-    const uint64_t *tagged;
     // token-level baseline only (NULL otherwise): the number of packed entries
     // (block | token mask << 16) per unit in `indices`
     const uint32_t *counts;
@@ -204,7 +200,7 @@ __device__ __forceinline__ uint32_t valid_mask(int v) {
     return v >= kPage ? 0xFFFFu : (1u << v) - 1u;
 }
 
-// Spin bound of the decode step's wait for a unit's selection (~0.1 s).
+// Spin bound of the decode step's wait for a unit's scores (~0.1 s).
 constexpr uint32_t kReadySpinLimit = 1u << 22;
 
 // K and V fragments of N blocks (one pipeline stage).
@@ -234,13 +230,14 @@ __device__ __forceinline__ void store_out<float>(float *p, float x) {
 enum ListMode : int { kSelected = 0, kAll = 1, kRecent = 2, kMasked = 3 };
 
 // One (unit, split) item: attention of the unit's query group over its share of
-// the block list, kG blocks per pipeline stage.  smem: the wave-merge / split-merge area (see launch
-// sizing); is_last: one LDS word.  Inside a decode step (a.tagged set) each wave
-// reads its entries of the unit's published selection, waiting (bounded) until
-// all of them carry the launch's tag.
+// the block list, kG blocks per pipeline stage.  smem: the wave-merge /
+// split-merge area (see launch sizing); is_last: one LDS word.  lds_list (the
+// decode step, which selects in the same workgroup): the split's share of the
+// selection in LDS, entry i of the list at lds_list[i - split * bps], instead
+// of a.indices.
 template <typename T, int D, int MODE, int kG>
 __device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int split, float *smem,
-                                            int *is_last_p, uint32_t tag = 0u) {
+                                            int *is_last_p, const int32_t *lds_list = nullptr) {
     using F = Mfma<T, D>;
     constexpr int NV = F::NV;
     int &is_last = *is_last_p;
@@ -253,18 +250,14 @@ __device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int s
     // requested together with the length
     const int per_wave = a.bps / kWaves;
     int cnt = 0, w0 = 0;
-    uint64_t entry = 0;
+    uint32_t entry = 0;
     if (LISTED) {
         const int i0 = split * a.bps, i1 = min(a.top_k, i0 + a.bps);
         w0 = i0 + wave * per_wave;
         cnt = max(0, min(i1, w0 + per_wave) - w0);
-        if (lane < cnt) {
-            if (a.tagged)
-                entry = __hip_atomic_load(a.tagged + (size_t)unit * a.top_k + w0 + lane,
-                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            else
-                entry = (uint32_t)a.indices[(size_t)unit * a.top_k + w0 + lane];
-        }
+        if (lane < cnt)
+            entry = (uint32_t)(lds_list ? lds_list[w0 - i0 + lane]
+                                        : a.indices[(size_t)unit * a.top_k + w0 + lane]);
     }
     const int L = a.seq_lens[b];
     const int count = MODE == kMasked ? (int)a.counts[unit] : 0;
@@ -284,20 +277,6 @@ __device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int s
         const int i0 = split * a.bps, i1 = min(len, i0 + a.bps);
         w0 = i0 + wave * per_wave;
         cnt = max(0, min(i1, w0 + per_wave) - w0);
-    } else if (a.tagged) {
-        // decode step: wait until this wave's entries are published
-        uint32_t spins = 0;
-        while (__ballot(lane < cnt && (uint32_t)(entry >> 32) != tag)) {
-            if (++spins > kReadySpinLimit) {  // never expected: report, do not hang
-                if (lane == 0) flag_error(a.err, kErrTimeout);
-                if ((uint32_t)(entry >> 32) != tag) entry = 0xffffffffu;  // skipped
-                break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-            if (lane < cnt && (uint32_t)(entry >> 32) != tag)
-                entry = __hip_atomic_load(a.tagged + (size_t)unit * a.top_k + w0 + lane,
-                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
     }
 
     // lane m < cnt holds page id and token mask (bit t: token t of the page is

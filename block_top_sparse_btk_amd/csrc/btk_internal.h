@@ -138,10 +138,11 @@ AttendPlan plan_attend(const Dims &d, int list_len_max, bool dense);
 //   attend counters            B*Hkv uint32
 //   scores scratch             B*Hkv*max_blocks float
 //   attend partials            B*Hkv*nsplit_max*(r*D + 2r) float (max of sparse, dense)
-//   published selections       B*Hkv*top_k uint64 (decode step)
+//   ready words                B*Hkv*kReadyStride uint32 (decode step)
 //   queue                      3 uint32 (decode step)
+constexpr int kReadyStride = 32;  // one 128-byte line per unit: each is polled on its own
 struct WorkspaceLayout {
-    size_t sel_counters, att_counters, scores, partials, tagged, queue, total;
+    size_t sel_counters, att_counters, scores, partials, ready, queue, total;
 };
 WorkspaceLayout workspace_layout(const Dims &d, int top_k);
 
@@ -198,7 +199,7 @@ hipError_t launch_decode_step(const Dims &d, const SelectPlan &sp, const AttendP
                               const int32_t *first_pos, float *centroids, int top_k,
                               int32_t *indices, float *scores, void *out, float *lse,
                               float *partials, uint32_t *sel_counters, uint32_t *att_counters,
-                              uint64_t *tagged, uint32_t *queue, uint32_t *err,
+                              uint32_t *ready, uint32_t *queue, uint32_t *err,
                               hipStream_t stream);
 
 }  // namespace btk

@@ -39,38 +39,59 @@ struct Vec16<float> {
 // A key row of D elements is read as 16-byte vectors: LPR lanes cover a token
 // row and TPI rows are read per instruction (1 KiB contiguous per wave
 // instruction); partial sums over rows are folded with xor shuffles.  The
-// centroid row is written to gdst (global) and, if given, to ldst (LDS).
+// loads (KeyTile::load) and the sum (KeyTile::mean) are separate so that a
+// caller can put other work between them; the centroid row is written to gdst
+// (global) and, if given, to ldst (LDS).
+template <typename T, int D>
+struct KeyTile {
+    static constexpr int VEC = Vec16<T>::n;
+    static constexpr int LPR = D / VEC;      // lanes per token row
+    static constexpr int TPI = kWave / LPR;  // token rows per wave instruction
+    static constexpr int NI = kPage / TPI;   // instructions per tile
+    static_assert(kWave % LPR == 0 && kPage % TPI == 0, "layout");
+    uint4 w[NI];  // raw 16-byte vectors, zero for tokens >= v
+
+    __device__ __forceinline__ void load(const T *tile, int v, int lane) {
+        const int col = lane % LPR, row = lane / LPR;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int t = i * TPI + row;
+            w[i] = t < v ? *reinterpret_cast<const uint4 *>(tile + (size_t)t * D + col * VEC)
+                         : make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+    __device__ __forceinline__ void mean(int v, float *gdst, float *ldst, int lane) const {
+        const int col = lane % LPR, row = lane / LPR;
+        float acc[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            if (i * TPI + row < v) Vec16<T>::add(&w[i], acc);
+#pragma unroll
+        for (int off = LPR; off < kWave; off <<= 1) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], off);
+        }
+        if (row == 0) {
+            const float vf = (float)v;
+#pragma unroll
+            for (int e = 0; e < VEC; e += 4) {
+                const float4 o = make_float4(acc[e] / vf, acc[e + 1] / vf, acc[e + 2] / vf,
+                                             acc[e + 3] / vf);
+                *reinterpret_cast<float4 *>(gdst + col * VEC + e) = o;
+                if (ldst) *reinterpret_cast<float4 *>(ldst + col * VEC + e) = o;
+            }
+        }
+    }
+};
+
 template <typename T, int D>
 __device__ __forceinline__ void block_centroid(const T *tile, int v, float *gdst, float *ldst,
                                                int lane) {
-    constexpr int VEC = Vec16<T>::n;
-    constexpr int LPR = D / VEC;      // lanes per token row
-    constexpr int TPI = kWave / LPR;  // token rows per wave instruction
-    static_assert(kWave % LPR == 0 && kPage % TPI == 0, "layout");
-    const int col = lane % LPR, row = lane / LPR;
-    float acc[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
-#pragma unroll
-    for (int t0 = 0; t0 < kPage; t0 += TPI) {
-        const int t = t0 + row;
-        if (t < v) Vec16<T>::add(tile + (size_t)t * D + col * VEC, acc);
-    }
-#pragma unroll
-    for (int off = LPR; off < kWave; off <<= 1) {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], off);
-    }
-    if (row == 0) {
-        const float vf = (float)v;
-#pragma unroll
-        for (int e = 0; e < VEC; e += 4) {
-            const float4 o = make_float4(acc[e] / vf, acc[e + 1] / vf, acc[e + 2] / vf,
-                                         acc[e + 3] / vf);
-            *reinterpret_cast<float4 *>(gdst + col * VEC + e) = o;
-            if (ldst) *reinterpret_cast<float4 *>(ldst + col * VEC + e) = o;
-        }
-    }
+    KeyTile<T, D> kt;
+    kt.load(tile, v, lane);
+    kt.mean(v, gdst, ldst, lane);
 }
 
 }  // namespace btk

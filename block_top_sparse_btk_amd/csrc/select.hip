@@ -142,7 +142,7 @@ __device__ __forceinline__ void shared_item(const SelectArgs &a, const PrefixGro
         TopkSmem w{tk.hist + wave * (256 + kWave), tk.cand + wave * 4 * kWave,
                    tk.red, tk.scan_red, tk.keys};
         const PlainScores src{a.scores + (size_t)unit * a.max_blocks};
-        const TopkOut out{a.indices + (size_t)unit * a.top_k, nullptr, 0u};
+        const TopkOut out{a.indices + (size_t)unit * a.top_k};
         if (min(a.top_k, nbm) == nbm) {
             for (int i = lane; i < a.top_k; i += kWave) out.put(i, i < nbm ? i : -1);
         } else if (nbm <= 8 * kWave) {
@@ -159,7 +159,7 @@ __device__ __forceinline__ void shared_item(const SelectArgs &a, const PrefixGro
         const int unit = (first + m) * a.Hkv + gk;
         __syncthreads();
         select_topk(PlainScores{a.scores + (size_t)unit * a.max_blocks}, nbm, a.top_k,
-                    TopkOut{a.indices + (size_t)unit * a.top_k, nullptr, 0u}, tk);
+                    TopkOut{a.indices + (size_t)unit * a.top_k}, tk);
     }
     __builtin_amdgcn_s_setprio(0);
 }
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(kThreads, 5) void select_kernel(SelectArgs a, Prefi
     // the selecting wave(s) take issue priority over scanning waves on the SIMD
     __builtin_amdgcn_s_setprio(3);
     select_topk(PlainScores{a.scores + (size_t)unit * a.max_blocks}, nb, a.top_k,
-                TopkOut{a.indices + (size_t)unit * a.top_k, nullptr, 0u}, tk);
+                TopkOut{a.indices + (size_t)unit * a.top_k}, tk);
 }
 
 template <typename T, int D>

@@ -64,17 +64,16 @@ struct TopkSmem {
     uint32_t *keys;      // [max_blocks] keys, workgroup-wide path only
 };
 
-// Where a selection goes: the caller's index row and, inside a decode step, the
-// same entries tagged with the launch's tag for the launch's own readers.
+// Where a selection goes: the caller's index row (or NULL) and, inside a
+// decode step, the entries [lo, hi) of it into LDS for the workgroup's own
+// attention (lds[i - lo] holds entry i).
 struct TopkOut {
-    int32_t *idx;      // [top_k]
-    uint64_t *tagged;  // [top_k] or NULL
-    uint32_t tag;
+    int32_t *idx;            // [top_k] or NULL
+    int32_t *lds = nullptr;  // [hi - lo] or NULL
+    int lo = 0, hi = 0;
     __device__ __forceinline__ void put(int pos, int32_t j) const {
-        store_relaxed_i32(idx + pos, j);
-        if (tagged)
-            __hip_atomic_store(tagged + pos, ((uint64_t)tag << 32) | (uint32_t)j,
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (idx) store_relaxed_i32(idx + pos, j);
+        if (lds && pos >= lo && pos < hi) lds[pos - lo] = j;
     }
 };
 
@@ -464,82 +463,58 @@ __device__ __forceinline__ float row16_sum(float x) {
 }
 
 // The per-lane part of a centroid row's dot product with the scaled mean
-// query (VPL floats per lane); the scan and the decode step's re-score of a
-// freshly updated centroid share it so that both give identical scores.
+// query (VPL floats per lane).  Every scoring path (the scan, the shared-prefix
+// rows, the decode step's re-score of a freshly updated centroid) shares it,
+// and its operations are fixed (per four floats one product, then three fused
+// multiply-adds, then one add; no contraction) so that every kernel computes
+// bit-identical scores whatever its code generation.
 template <int VPL>
 __device__ __forceinline__ float row_partial(const float (&qf)[VPL], const float4 (&cv)[VPL / 4]) {
+#pragma clang fp contract(off)
     float s = 0.f;
 #pragma unroll
-    for (int v = 0; v < VPL / 4; ++v)
-        s += qf[4 * v] * cv[v].x + qf[4 * v + 1] * cv[v].y + qf[4 * v + 2] * cv[v].z +
-             qf[4 * v + 3] * cv[v].w;
+    for (int v = 0; v < VPL / 4; ++v) {
+        float t = qf[4 * v] * cv[v].x;
+        t = __builtin_fmaf(qf[4 * v + 1], cv[v].y, t);
+        t = __builtin_fmaf(qf[4 * v + 2], cv[v].z, t);
+        t = __builtin_fmaf(qf[4 * v + 3], cv[v].w, t);
+        s = s + t;
+    }
     return s;
 }
 
-// Scores one chunk of a unit's blocks into a.scores (and, inside a decode step,
-// first refreshes the centroids of the chunk's touched pages).  Returns true in
-// the workgroup that completed the unit's last chunk, which must then select;
-// nb receives the unit's block count.  KU: rows per lane per pipeline stage
-// (two stages of 4 * 4 * KU rows are in flight).  skip: leading blocks scored
-// elsewhere (a shared prompt prefix) by `extra` other workgroups that count in
-// on the unit too; the chunks cover blocks [skip, n_b), and a unit with nothing
-// left still has chunk 0, which only counts in.
-template <typename T, int D, int KU>
-__device__ __forceinline__ bool score_chunk(const SelectArgs &a, int unit, int c, ScoreSmem &sm,
-                                            float *crow, int &nb_out, int skip = 0,
-                                            int extra = 0) {
+// Scores n consecutive blocks j0 .. j0+n-1 of unit (b, g) whose page ids are in
+// sm.pages[0 .. n) (invalid ones as -1) against the scaled mean query in
+// sm.qs, stages the scores in sm.sc and stores them to a.scores.  REFRESH
+// (the decode step, a.first_pos set): the pages touched since the last step
+// also get their centroid recomputed from the keys, stored for later steps and
+// re-scored here.  KU: rows per lane per pipeline stage (two stages of
+// 4 * 4 * KU rows are in flight).  Called with sm.pages and sm.qs visible to
+// every thread; ends with the stores issued (not waited for).
+template <typename T, int D, int KU, bool REFRESH>
+__device__ __forceinline__ void scan_rows(const SelectArgs &a, int b, int g, int j0, int n, int L,
+                                          int fp, ScoreSmem &sm, float *crow) {
     constexpr int LPR = 16;                       // lanes per centroid row: one DPP row
     constexpr int VPL = D / LPR;                  // floats per lane per row (8 or 4)
     constexpr int RPI = kWave / LPR;              // rows per wave per load step
     constexpr int ROWS = kWaves * RPI * KU;       // rows per workgroup stage
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const int b = unit / a.Hkv, g = unit % a.Hkv;
-    const int r = a.Hq / a.Hkv;
-    int32_t *out = a.indices + (size_t)unit * a.top_k;
-    const int j0 = skip + c * a.chunk;
-
-    // setup in one round trip: the group's queries, the chunk's slice of the
-    // block-table row (entries past the sequence are read but never used), the
-    // length and the decode position
-    const T *qp = static_cast<const T *>(a.q) + ((size_t)b * a.Hq + (size_t)g * r) * D;
-    for (int i = tid; i < r * D; i += kThreads) sm.qraw[i] = load_q<T>(qp + i);
-    const int jn = min(a.chunk, a.max_blocks - j0);
-    for (int i = tid; i < jn; i += kThreads) sm.pages[i] = a.bt[(size_t)b * a.max_blocks + j0 + i];
-    const int L = a.seq_lens[b];
-    const int fp = a.first_pos ? a.first_pos[b] : -1;
-    __syncthreads();
-
-    if (L < 1 || L > a.max_blocks * kPage) {
-        if (c == 0) {
-            for (int i = tid; i < a.top_k; i += kThreads) store_relaxed_i32(out + i, -1);
-            if (tid == 0) flag_error(a.err, kErrSeqLen);
-        }
-        return false;
-    }
-    const int nb = (L + kPage - 1) / kPage;
-    const int nchunks = max(1, (nb - skip + a.chunk - 1) / a.chunk);
-    if (c >= nchunks) return false;
-    const int n = max(0, min(nb, j0 + a.chunk) - j0);
-    for (int i = tid; i < n; i += kThreads) {  // the entries this thread loaded
-        const int p = sm.pages[i];
-        if (p < 0 || p >= a.num_pages) {
-            flag_error(a.err, kErrPage);
-            sm.pages[i] = -1;
-        }
-    }
-    if (tid < D) {  // group mean query, pre-scaled
-        float s = 0.f;
-        for (int h = 0; h < r; ++h) s += sm.qraw[h * D + tid];
-        sm.qs[tid] = s * (a.scale / (float)r);
-    }
-    __syncthreads();
-
     const int col = lane % LPR, rsub = lane / LPR;
+    // decode step: wave w refreshes the touched blocks jw, jw + 4, ... of the
+    // run; the keys of its first one are requested before the scan so that
+    // they arrive while it streams
+    const bool refresh = REFRESH && a.first_pos && fp >= 0 && fp < L;
+    const int jw = refresh ? max(j0, fp / kPage) + wave : j0 + n;
+    const T *keys = static_cast<const T *>(a.k_cache) + (size_t)g * kPage * D;
+    const size_t page_stride = (size_t)a.Hkv * kPage * D;
+    KeyTile<T, D> kt;
+    if (jw < j0 + n && sm.pages[jw - j0] >= 0)
+        kt.load(keys + (size_t)sm.pages[jw - j0] * page_stride, min(kPage, L - jw * kPage), lane);
     float qf[VPL];
 #pragma unroll
     for (int e = 0; e < VPL; ++e) qf[e] = sm.qs[col * VPL + e];
     // Loads are unconditional so that the next stage stays in flight while the
-    // current one is reduced: rows past the chunk re-read its last row and an
+    // current one is reduced: rows past the run re-read its last row and an
     // invalid page reads page 0; neither result is kept.
     typedef float4 Row[VPL / 4];
     auto issue = [&](Row (&cv)[KU], int base) {
@@ -576,33 +551,156 @@ __device__ __forceinline__ bool score_chunk(const SelectArgs &a, int unit, int c
         }
     }
 
-    // decode step: pages touched since the last step get their centroid
-    // recomputed from the keys, stored for later steps, and re-scored here (one
-    // wave per touched page; crow is the wave's LDS row)
-    if (a.first_pos && fp >= 0 && fp < L) {
-        for (int j = max(j0, fp / kPage) + wave; j < j0 + n; j += kWaves) {
-            const int page = sm.pages[j - j0];
-            if (page < 0) continue;
-            const int v = min(kPage, L - j * kPage);
-            float *row_lds = crow + wave * D;
-            block_centroid<T, D>(static_cast<const T *>(a.k_cache) +
-                                     ((size_t)page * a.Hkv + g) * kPage * D,
-                                 v, a.cent_out + ((size_t)page * a.Hkv + g) * D, row_lds, lane);
-            __builtin_amdgcn_wave_barrier();
-            Row cv;
+    // decode step: the touched blocks' centroids are recomputed, stored for
+    // later steps and re-scored (crow is the wave's LDS row).  The scan's own
+    // score of a touched block comes from another wave: it must land first.
+    if (refresh && max(j0, fp / kPage) < j0 + n) __syncthreads();
+    for (int j = jw; j < j0 + n; j += kWaves) {
+        const int page = sm.pages[j - j0];
+        if (page < 0) continue;
+        const int v = min(kPage, L - j * kPage);
+        float *row_lds = crow + wave * D;
+        if (j != jw) kt.load(keys + (size_t)page * page_stride, v, lane);
+        kt.mean(v, a.cent_out + ((size_t)page * a.Hkv + g) * D, row_lds, lane);
+        __builtin_amdgcn_wave_barrier();
+        Row cv;
 #pragma unroll
-            for (int vv = 0; vv < VPL / 4; ++vv)
-                cv[vv] = reinterpret_cast<const float4 *>(row_lds + col * VPL)[vv];
-            const float s = row16_sum(row_partial<VPL>(qf, cv));
-            if (lane == 0) sm.sc[j - j0] = s;
-            __builtin_amdgcn_wave_barrier();
-        }
+        for (int vv = 0; vv < VPL / 4; ++vv)
+            cv[vv] = reinterpret_cast<const float4 *>(row_lds + col * VPL)[vv];
+        const float s = row16_sum(row_partial<VPL>(qf, cv));
+        if (lane == 0) sm.sc[j - j0] = s;
+        __builtin_amdgcn_wave_barrier();
     }
     __syncthreads();
-    nb_out = nb;
-    float *sc = a.scores + (size_t)unit * a.max_blocks;
+    float *sc = a.scores + ((size_t)b * a.Hkv + g) * a.max_blocks;
     for (int i = tid; i < n; i += kThreads) store_relaxed(sc + j0 + i, sm.sc[i]);
+}
+
+// Marks the n page ids in sm.pages that are out of range as -1 (error bit).
+__device__ __forceinline__ void check_pages(const SelectArgs &a, ScoreSmem &sm, int n) {
+    for (int i = threadIdx.x; i < n; i += kThreads) {
+        const int p = sm.pages[i];
+        if (p < 0 || p >= a.num_pages) {
+            flag_error(a.err, kErrPage);
+            sm.pages[i] = -1;
+        }
+    }
+}
+
+// The group's mean query, pre-scaled, from the r raw queries in sm.qraw.
+template <int D>
+__device__ __forceinline__ void mean_query(const SelectArgs &a, ScoreSmem &sm) {
+    const int r = a.Hq / a.Hkv;
+    if (threadIdx.x < D) {
+        float s = 0.f;
+        for (int h = 0; h < r; ++h) s += sm.qraw[h * D + threadIdx.x];
+        sm.qs[threadIdx.x] = s * (a.scale / (float)r);
+    }
+}
+
+// Scores one chunk of a unit's blocks into a.scores (and, inside a decode step,
+// first refreshes the centroids of the chunk's touched pages).  Returns true in
+// the workgroup that completed the unit's last chunk, which must then select;
+// nb receives the unit's block count (-1 for an invalid length, whose only
+// chunk writes -1 indices).  skip: leading blocks scored elsewhere (a shared
+// prompt prefix) by `extra` other workgroups that count in on the unit too; the
+// chunks cover blocks [skip, n_b), and a unit with nothing left still has
+// chunk 0, which only counts in.
+template <typename T, int D, int KU>
+__device__ __forceinline__ bool score_chunk(const SelectArgs &a, int unit, int c, ScoreSmem &sm,
+                                            float *crow, int &nb_out, int skip = 0,
+                                            int extra = 0) {
+    const int tid = threadIdx.x;
+    const int b = unit / a.Hkv, g = unit % a.Hkv;
+    const int r = a.Hq / a.Hkv;
+    int32_t *out = a.indices + (size_t)unit * a.top_k;
+    const int j0 = skip + c * a.chunk;
+
+    // setup in one round trip: the group's queries, the chunk's slice of the
+    // block-table row (entries past the sequence are read but never used), the
+    // length and the decode position
+    const T *qp = static_cast<const T *>(a.q) + ((size_t)b * a.Hq + (size_t)g * r) * D;
+    for (int i = tid; i < r * D; i += kThreads) sm.qraw[i] = load_q<T>(qp + i);
+    const int jn = min(a.chunk, a.max_blocks - j0);
+    for (int i = tid; i < jn; i += kThreads) sm.pages[i] = a.bt[(size_t)b * a.max_blocks + j0 + i];
+    const int L = a.seq_lens[b];
+    const int fp = a.first_pos ? a.first_pos[b] : -1;
+    __syncthreads();
+
+    if (L < 1 || L > a.max_blocks * kPage) {
+        if (c == 0) {
+            for (int i = tid; i < a.top_k; i += kThreads) store_relaxed_i32(out + i, -1);
+            if (tid == 0) flag_error(a.err, kErrSeqLen);
+        }
+        nb_out = -1;  // an invalid length has exactly one item, chunk 0
+        return false;
+    }
+    const int nb = (L + kPage - 1) / kPage;
+    const int nchunks = max(1, (nb - skip + a.chunk - 1) / a.chunk);
+    if (c >= nchunks) return false;
+    const int n = max(0, min(nb, j0 + a.chunk) - j0);
+    check_pages(a, sm, n);  // the entries this thread loaded
+    mean_query<D>(a, sm);
+    __syncthreads();
+    scan_rows<T, D, KU, false>(a, b, g, j0, n, L, fp, sm, crow);
+    nb_out = nb;
     return arrive_last(&a.counters[unit], (uint32_t)(nchunks + extra), sm.flag);
+}
+
+// Decode step: scores blocks [j0, j1) of unit (b, g) of a sequence with nb
+// blocks (nb < 0: invalid length, one placeholder row that writes -1 indices
+// and flags the error), in runs of up to kMaxChunk blocks, then counts the
+// blocks in on the unit's counter.  The segment that completes the unit resets
+// the counter and sets the unit's ready word to `tag`, after every segment's
+// score stores have completed (each waits for its own before counting in).
+template <typename T, int D, int KU>
+__device__ __forceinline__ void score_segment(const SelectArgs &a, int b, int g, int j0, int j1,
+                                              int nb, ScoreSmem &sm, float *crow,
+                                              uint32_t *ready, uint32_t tag) {
+    const int tid = threadIdx.x;
+    const int unit = b * a.Hkv + g;
+    const int r = a.Hq / a.Hkv;
+    if (nb < 0) {
+        int32_t *out = a.indices + (size_t)unit * a.top_k;
+        for (int i = tid; i < a.top_k; i += kThreads) store_relaxed_i32(out + i, -1);
+        if (tid == 0) flag_error(a.err, kErrSeqLen);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0) __hip_atomic_store(ready, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    // setup in one round trip: the group's queries, the first run's slice of
+    // the block-table row, the length and the decode position
+    const T *qp = static_cast<const T *>(a.q) + ((size_t)b * a.Hq + (size_t)g * r) * D;
+    for (int i = tid; i < r * D; i += kThreads) sm.qraw[i] = load_q<T>(qp + i);
+    const int32_t *row = a.bt + (size_t)b * a.max_blocks;
+    int n = min(kMaxChunk, j1 - j0);
+    for (int i = tid; i < n; i += kThreads) sm.pages[i] = row[j0 + i];
+    const int L = a.seq_lens[b];
+    const int fp = a.first_pos ? a.first_pos[b] : -1;
+    __syncthreads();
+    mean_query<D>(a, sm);
+    for (int s0 = j0;;) {
+        check_pages(a, sm, n);
+        __syncthreads();
+        scan_rows<T, D, KU, true>(a, b, g, s0, n, L, fp, sm, crow);
+        s0 += n;
+        if (s0 >= j1) break;
+        n = min(kMaxChunk, j1 - s0);
+        __syncthreads();  // sm.pages and sm.sc are free again
+        for (int i = tid; i < n; i += kThreads) sm.pages[i] = row[s0 + i];
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t cnt = (uint32_t)(j1 - j0);
+        const uint32_t prev = __hip_atomic_fetch_add(&a.counters[unit], cnt, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        if (prev + cnt == (uint32_t)nb) {
+            __hip_atomic_store(&a.counters[unit], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(ready, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 }
 
 }  // namespace sel

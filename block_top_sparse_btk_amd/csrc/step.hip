@@ -3,22 +3,26 @@
 // carries the argument": averaged-key block summaries, per-query-group scoring,
 // top-k blocks, attention over the kept blocks.)
 //
-// Work items come from a queue counter in the workspace, in this order:
-//   1. scoring items, one per (sequence, KV head, chunk), unit-major with a
-//      unit's chunks from last to first: the chunk that holds a touched page
-//      first recomputes its centroid, then the chunk is scored; the workgroup
-//      that completes the unit (a counter per unit) selects its top-k blocks
-//      and publishes them as tagged entries (the launch's tag in the high
-//      word, so an entry is its own ready flag);
-//   2. attention items, one per (unit, split), unit-major: each wave waits
-//      (bounded spin, never expected to be long) until its entries carry the
-//      launch's tag, then attends.
-// Scoring never waits and every scoring item precedes every attention item,
-// so the waits always end.  By the time the attention items of the last units
-// are reached, their selections have run behind the attention of earlier units,
-// so selection latency is mostly off the critical path.  The device functions
-// are the same as the stand-alone kernels', so results are identical to the
-// three calls.
+// Phase 1, scoring.  The launch's centroid rows, ordered by sequence, KV head
+// and block, are cut into one equal, contiguous share per workgroup, so every
+// workgroup streams the same number of bytes and all shares end together.  A
+// share is a few segments (a run of one unit's blocks, a unit usually spanning
+// two or three workgroups), each scored in runs of up to kMaxChunk blocks; the
+// run that holds a touched page first recomputes its centroid (S1).  A segment
+// then adds its block count to the unit's counter, and the segment that
+// completes the unit marks it ready with the launch's tag.
+//
+// Phase 2, selection and attention.  Items (unit, split) come from a queue
+// counter.  An item waits (bounded spin, never expected to be long) until its
+// unit is ready, selects the unit's top-k blocks from the stored scores (S3),
+// keeps its split's share of the selection in LDS and attends (S4).  Each split
+// of a unit selects for itself (identical results), split 0 also writes the
+// indices.  Scoring never waits and a workgroup scores its whole share before
+// it takes an item, so every wait ends.
+//
+// Handing out scoring work dynamically in fixed chunks was measured slower: the
+// last chunks to be handed out run at a fair share of the bandwidth next to
+// the attention of earlier units and set the end of the launch.
 //
 // The launch tag is one more than a launch counter kept in the queue words; the
 // last workgroup to leave advances the counter (skipping the value whose
@@ -37,14 +41,18 @@ using sel::kWaves;
 struct StepArgs {
     sel::SelectArgs s;
     att::AttendArgs t;
-    uint64_t *tagged;  // [units][top_k] published selections (also t.tagged)
-    uint32_t *queue;   // [0] items taken beyond the grid, [1] workgroups that have left,
-                       // [2] launch counter
+    uint32_t *ready;  // [units * kReadyStride]: word u * kReadyStride is unit u's ready tag
+    uint32_t *queue;  // [0] items taken, [1] workgroups that have left, [2] launch counter
     int B, units, nsplit;
 };
 
 constexpr int kStageBlocks = 1;  // bf16 attention pipeline stage (fp32: 2, see attend.hip)
 constexpr int kScanRows = 4;     // centroid rows per lane per scan stage
+// Rows charged for a unit beyond its blocks when the shares are cut: a segment
+// costs round trips in which nothing streams (its setup, its closing
+// store-and-count) and the unit's touched page its refresh, so a share that
+// starts a unit gets that many fewer blocks.
+constexpr int kSegmentCost = 64;
 
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
@@ -56,7 +64,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
     __shared__ uint32_t red[2 * kWaves];
     __shared__ int scan_red[kWaves];
     __shared__ float crow[kWaves * D];
-    __shared__ uint32_t prefix[kMaxStepBatch + 1];  // scoring items before each sequence
+    __shared__ uint32_t rows[kMaxStepBatch + 1];  // centroid rows before each sequence
+    __shared__ int nbs[kMaxStepBatch];            // blocks per sequence, -1: invalid length
     __shared__ int item_s;
     __shared__ uint32_t tag_s;
     // queries while scoring, top-k keys of long contexts, attention merges
@@ -66,67 +75,89 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
     const int tid = threadIdx.x;
     const int Hkv = a.s.Hkv;
 
-    // the launch tag is fetched while the prefix is built; the first item is
-    // the workgroup's own index, later ones come from the queue (offset by the
-    // grid), so the launch does not open with every workgroup's atomic at once
+    // the launch tag is fetched while the row prefix is built: per unit
+    // kSegmentCost charged rows, then one row per block (a single placeholder
+    // row for an invalid length, which writes -1 indices and flags the error)
     if (tid == 0)
         tag_s = __hip_atomic_load(&a.queue[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-    // scoring items per sequence: Hkv * chunks (one item for an invalid length,
-    // which writes -1 indices and flags the error)
     for (int b0 = 0; b0 < a.B; b0 += kThreads) {
         const int b = b0 + tid;
         uint32_t n = 0;
         if (b < a.B) {
             const int L = a.s.seq_lens[b];
             const bool ok = L >= 1 && L <= a.s.max_blocks * kPage;
-            const int nb = ok ? (L + kPage - 1) / kPage : 0;
-            n = (uint32_t)Hkv * (uint32_t)(ok ? (nb + a.s.chunk - 1) / a.s.chunk : 1);
+            const int nb = ok ? (L + kPage - 1) / kPage : -1;
+            nbs[b] = nb;
+            n = (uint32_t)Hkv * (uint32_t)(kSegmentCost + (ok ? nb : 1));
         }
-        const uint32_t carry = b0 == 0 ? 0u : prefix[b0];
+        const uint32_t carry = b0 == 0 ? 0u : rows[b0];
         const int before = sel::wg_exclusive_scan((int)n, scan_red);
-        if (b < a.B) prefix[b + 1] = carry + (uint32_t)before + n;
-        if (b0 == 0 && tid == 0) prefix[0] = 0u;
+        if (b < a.B) rows[b + 1] = carry + (uint32_t)before + n;
+        if (b0 == 0 && tid == 0) rows[0] = 0u;
         __syncthreads();
     }
-    const int n_score = (int)prefix[a.B];
-    const int total = n_score + a.units * a.nsplit;
-
     const uint32_t tag = tag_s;
-    int item = (int)blockIdx.x;
-    // the next item from the queue (LDS is reused by the next item)
-    auto next_item = [&]() {
+
+    // ---- phase 1: this workgroup's share of the rows
+    const uint64_t R = rows[a.B];
+    const uint32_t r1 = (uint32_t)(R * (blockIdx.x + 1) / gridDim.x);
+    int b = 0;
+    for (uint32_t r = (uint32_t)(R * blockIdx.x / gridDim.x); r < r1;) {
+        while (rows[b + 1] <= r) ++b;
+        const int nb = nbs[b];
+        const uint32_t per_unit = kSegmentCost + (nb < 0 ? 1u : (uint32_t)nb);
+        const uint32_t off = r - rows[b];
+        const uint32_t g = off / per_unit, o = off % per_unit;  // o < kSegmentCost: charged rows
+        const uint32_t e = min(per_unit, o + (r1 - r));         // this share's end in the unit
+        const int j0 = (int)(o > kSegmentCost ? o - kSegmentCost : 0u);
+        const int j1 = (int)(e > kSegmentCost ? e - kSegmentCost : 0u);
+        if (j1 > j0) {
+            sel::score_segment<T, D, kScanRows>(
+                a.s, b, (int)g, j0, j1, nb, sm, crow,
+                a.ready + ((size_t)b * Hkv + g) * kReadyStride, tag);
+            __syncthreads();  // LDS is reused by the next segment
+        }
+        r += e - o;
+    }
+
+    // ---- phase 2: (unit, split) items
+    const int total = a.units * a.nsplit;
+    int32_t *list = reinterpret_cast<int32_t *>(sc_lds);  // the split's share, <= 256 entries
+    for (;;) {
+        if (tid == 0) item_s = (int)atomicAdd(&a.queue[0], 1u);
         __syncthreads();
-        if (tid == 0) item_s = (int)(gridDim.x + atomicAdd(&a.queue[0], 1u));
+        const int item = item_s;
+        if (item >= total) break;
+        const int unit = item / a.nsplit, split = item % a.nsplit;
+        const int bu = unit / Hkv;
+        if (tid == 0) {
+            const uint32_t *rw = a.ready + (size_t)unit * kReadyStride;
+            uint32_t spins = 0;
+            while (__hip_atomic_load(rw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != tag) {
+                if (++spins > att::kReadySpinLimit) {  // never expected: report, do not hang
+                    flag_error(a.s.err, kErrTimeout);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
         __syncthreads();
-        return item_s;
-    };
-    // every scoring item precedes every attention item, so a workgroup runs
-    // the two kinds in two loops (each with registers of its own)
-    int b_cur = 0;
-    while (item < n_score) {
-        while ((int)prefix[b_cur + 1] <= item) ++b_cur;  // items only grow
-        const int nc = (int)(prefix[b_cur + 1] - prefix[b_cur]) / Hkv;
-        const int rel = item - (int)prefix[b_cur];
-        // a unit's chunks go last to first: the one that refreshes the newest
-        // page starts first, so that it is rarely the one left to select
-        const int unit = b_cur * Hkv + rel / nc, c = nc - 1 - rel % nc;
-        int nb = 0;
-        if (sel::score_chunk<T, D, kScanRows>(a.s, unit, c, sm, crow, nb)) {
+        const int nb = nbs[bu];
+        const int lo = split * a.t.bps, hi = min(a.s.top_k, lo + a.t.bps);
+        if (nb >= 0) {
             __builtin_amdgcn_s_setprio(3);
-            sel::select_topk(sel::PlainScores{a.s.scores + (size_t)unit * a.s.max_blocks},
-                             nb, a.s.top_k,
-                             sel::TopkOut{a.s.indices + (size_t)unit * a.s.top_k,
-                                          a.tagged + (size_t)unit * a.s.top_k, tag},
+            sel::select_topk(sel::PlainScores{a.s.scores + (size_t)unit * a.s.max_blocks}, nb,
+                             a.s.top_k,
+                             sel::TopkOut{split == 0 ? a.s.indices + (size_t)unit * a.s.top_k
+                                                     : nullptr,
+                                          list, lo, hi},
                              tk);
             __builtin_amdgcn_s_setprio(0);
         }
-        item = next_item();
-    }
-    while (item < total) {
-        const int rel = item - n_score;
+        __syncthreads();
         att::attend_item<T, D, att::kSelected, (sizeof(T) == 4 ? 2 : kStageBlocks)>(
-            a.t, rel / a.nsplit, rel % a.nsplit, dyn, &flag, tag);
-        item = next_item();
+            a.t, unit, split, dyn, &flag, list);
+        __syncthreads();  // LDS is reused by the next item
     }
     // the last workgroup to leave re-arms the queue and advances the counter
     if (tid == 0) {
@@ -194,16 +225,19 @@ hipError_t launch_decode_step(const Dims &d, const SelectPlan &sp, const AttendP
                               const int32_t *first_pos, float *centroids, int top_k,
                               int32_t *indices, float *scores, void *out, float *lse,
                               float *partials, uint32_t *sel_counters, uint32_t *att_counters,
-                              uint64_t *tagged, uint32_t *queue, uint32_t *err,
+                              uint32_t *ready, uint32_t *queue, uint32_t *err,
                               hipStream_t stream) {
+    // a split's share of the selection (at most 4 * 64 entries) is kept in the
+    // score staging area
+    if (ap.bps > kMaxChunk) return hipErrorInvalidValue;
     StepArgs a;
     a.s = sel::SelectArgs{q, centroids, block_table, seq_lens, indices, scores, sel_counters, err,
                           d.Hq, d.Hkv, d.num_pages, d.max_blocks, top_k, sp.chunk, sp.nchunk_max,
                           d.sm_scale, k_cache, first_pos, centroids};
     a.t = att::AttendArgs{q, k_cache, v_cache, block_table, seq_lens, indices, out, lse, partials,
                           att_counters, err, d.Hq, d.Hkv, d.num_pages, d.max_blocks, top_k, ap.bps,
-                          ap.nsplit_max, d.sm_scale * 1.44269504088896340736f, tagged, nullptr};
-    a.tagged = tagged;
+                          ap.nsplit_max, d.sm_scale * 1.44269504088896340736f, nullptr};
+    a.ready = ready;
     a.queue = queue;
     a.B = d.B;
     a.units = d.B * d.Hkv;
