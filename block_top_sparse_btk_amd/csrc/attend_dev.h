@@ -231,13 +231,16 @@ enum ListMode : int { kSelected = 0, kAll = 1, kRecent = 2, kMasked = 3 };
 
 // One (unit, split) item: attention of the unit's query group over its share of
 // the block list, kG blocks per pipeline stage.  smem: the wave-merge /
-// split-merge area (see launch sizing); is_last: one LDS word.  lds_list (the
-// decode step, which selects in the same workgroup): the split's share of the
-// selection in LDS, entry i of the list at lds_list[i - split * bps], instead
-// of a.indices.
+// split-merge area (see launch sizing); is_last: one LDS word.  The decode
+// step, which selects in the same workgroup, also passes what it already holds:
+// lds_list, the split's share of the selection in LDS (entry i of the list at
+// lds_list[i - split * bps]) instead of a.indices; L_known >= 0, the sequence
+// length; lds_pages (or NULL), the sequence's block-table row in LDS.
 template <typename T, int D, int MODE, int kG>
 __device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int split, float *smem,
-                                            int *is_last_p, const int32_t *lds_list = nullptr) {
+                                            int *is_last_p, const int32_t *lds_list = nullptr,
+                                            int L_known = -1,
+                                            const int32_t *lds_pages = nullptr) {
     using F = Mfma<T, D>;
     constexpr int NV = F::NV;
     int &is_last = *is_last_p;
@@ -259,7 +262,7 @@ __device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int s
             entry = (uint32_t)(lds_list ? lds_list[w0 - i0 + lane]
                                         : a.indices[(size_t)unit * a.top_k + w0 + lane]);
     }
-    const int L = a.seq_lens[b];
+    const int L = L_known >= 0 ? L_known : a.seq_lens[b];
     const int count = MODE == kMasked ? (int)a.counts[unit] : 0;
     if (L < 1 || L > a.max_blocks * kPage) {
         if (split == 0 && tid == 0) flag_error(a.err, kErrSeqLen);
@@ -294,7 +297,7 @@ __device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int s
             j = -1;
         }
         if (j >= 0) {
-            const int p = a.bt[(size_t)b * a.max_blocks + j];
+            const int p = lds_pages ? lds_pages[j] : a.bt[(size_t)b * a.max_blocks + j];
             if (p >= 0 && p < a.num_pages) {
                 my_page = p;
                 my_mask = valid_mask(min(kPage, L - j * kPage)) & entry_mask;

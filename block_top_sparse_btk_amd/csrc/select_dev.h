@@ -649,11 +649,12 @@ __device__ __forceinline__ bool score_chunk(const SelectArgs &a, int unit, int c
 
 // Decode step: scores blocks [j0, j1) of unit (b, g) of a sequence with nb
 // blocks (nb < 0: invalid length, one placeholder row that writes -1 indices
-// and flags the error), in runs of up to kMaxChunk blocks, then counts the
+// and flags the error), in runs of up to RUN blocks (sm.pages and sm.sc hold
+// RUN entries; a run costs one round trip for its page ids), then counts the
 // blocks in on the unit's counter.  The segment that completes the unit resets
 // the counter and sets the unit's ready word to `tag`, after every segment's
 // score stores have completed (each waits for its own before counting in).
-template <typename T, int D, int KU>
+template <typename T, int D, int KU, int RUN>
 __device__ __forceinline__ void score_segment(const SelectArgs &a, int b, int g, int j0, int j1,
                                               int nb, ScoreSmem &sm, float *crow,
                                               uint32_t *ready, uint32_t tag) {
@@ -674,7 +675,7 @@ __device__ __forceinline__ void score_segment(const SelectArgs &a, int b, int g,
     const T *qp = static_cast<const T *>(a.q) + ((size_t)b * a.Hq + (size_t)g * r) * D;
     for (int i = tid; i < r * D; i += kThreads) sm.qraw[i] = load_q<T>(qp + i);
     const int32_t *row = a.bt + (size_t)b * a.max_blocks;
-    int n = min(kMaxChunk, j1 - j0);
+    int n = min(RUN, j1 - j0);
     for (int i = tid; i < n; i += kThreads) sm.pages[i] = row[j0 + i];
     const int L = a.seq_lens[b];
     const int fp = a.first_pos ? a.first_pos[b] : -1;
@@ -686,7 +687,7 @@ __device__ __forceinline__ void score_segment(const SelectArgs &a, int b, int g,
         scan_rows<T, D, KU, true>(a, b, g, s0, n, L, fp, sm, crow);
         s0 += n;
         if (s0 >= j1) break;
-        n = min(kMaxChunk, j1 - s0);
+        n = min(RUN, j1 - s0);
         __syncthreads();  // sm.pages and sm.sc are free again
         for (int i = tid; i < n; i += kThreads) sm.pages[i] = row[s0 + i];
     }

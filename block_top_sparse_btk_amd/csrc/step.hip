@@ -7,7 +7,7 @@
 // and block, are cut into one equal, contiguous share per workgroup, so every
 // workgroup streams the same number of bytes and all shares end together.  A
 // share is a few segments (a run of one unit's blocks, a unit usually spanning
-// two or three workgroups), each scored in runs of up to kMaxChunk blocks; the
+// two or three workgroups), each scored in runs of up to kRun blocks; the
 // run that holds a touched page first recomputes its centroid (S1).  A segment
 // then adds its block count to the unit's counter, and the segment that
 // completes the unit marks it ready with the launch's tag.
@@ -34,7 +34,6 @@
 namespace btk {
 namespace {
 
-using sel::kMaxChunk;
 using sel::kThreads;
 using sel::kWaves;
 
@@ -48,24 +47,30 @@ struct StepArgs {
 
 constexpr int kStageBlocks = 1;  // bf16 attention pipeline stage (fp32: 2, see attend.hip)
 constexpr int kScanRows = 4;     // centroid rows per lane per scan stage
+constexpr int kRun = 2048;       // blocks per scan run: shares (~550 blocks at 32 x 8 units of
+                                 // 17K tokens) take one run, one page-id round trip; in phase 2
+                                 // the page-id area holds the block-table row of units of up to
+                                 // kRun blocks
 // Rows charged for a unit beyond its blocks when the shares are cut: a segment
 // costs round trips in which nothing streams (its setup, its closing
 // store-and-count) and the unit's touched page its refresh, so a share that
 // starts a unit gets that many fewer blocks.
 constexpr int kSegmentCost = 64;
+// Share taper beta = kShareTaper / 64 (see the share boundaries).
+constexpr int kShareTaper = 0;
 
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
     __shared__ float qs[D];
-    __shared__ int pages[kMaxChunk];
-    __shared__ float sc_lds[kMaxChunk];
+    __shared__ int pages[kRun];
+    __shared__ float sc_lds[kRun];
     __shared__ int flag;
     __shared__ uint32_t hist[256 + kWave], cand[4 * kWave];
     __shared__ uint32_t red[2 * kWaves];
     __shared__ int scan_red[kWaves];
     __shared__ float crow[kWaves * D];
     __shared__ uint32_t rows[kMaxStepBatch + 1];  // centroid rows before each sequence
-    __shared__ int nbs[kMaxStepBatch];            // blocks per sequence, -1: invalid length
+    __shared__ int lens[kMaxStepBatch];           // sequence lengths, -1: invalid
     __shared__ int item_s;
     __shared__ uint32_t tag_s;
     // queries while scoring, top-k keys of long contexts, attention merges
@@ -87,7 +92,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
             const int L = a.s.seq_lens[b];
             const bool ok = L >= 1 && L <= a.s.max_blocks * kPage;
             const int nb = ok ? (L + kPage - 1) / kPage : -1;
-            nbs[b] = nb;
+            lens[b] = ok ? L : -1;
             n = (uint32_t)Hkv * (uint32_t)(kSegmentCost + (ok ? nb : 1));
         }
         const uint32_t carry = b0 == 0 ? 0u : rows[b0];
@@ -100,11 +105,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
 
     // ---- phase 1: this workgroup's share of the rows
     const uint64_t R = rows[a.B];
-    const uint32_t r1 = (uint32_t)(R * (blockIdx.x + 1) / gridDim.x);
+    // share boundaries R * F(w / G), F(x) = x + beta * x * (1 - x): the density
+    // falls linearly from 1 + beta to 1 - beta, since workgroups launched later
+    // (higher index) start later and share their CU with one that started first
+    const uint64_t G = gridDim.x;
+    auto boundary = [&](uint64_t w) {
+        return (uint32_t)(R * w * (64 * G + (uint64_t)kShareTaper * (G - w)) / (64 * G * G));
+    };
+    const uint32_t r1 = boundary(blockIdx.x + 1);
     int b = 0;
-    for (uint32_t r = (uint32_t)(R * blockIdx.x / gridDim.x); r < r1;) {
+    for (uint32_t r = boundary(blockIdx.x); r < r1;) {
         while (rows[b + 1] <= r) ++b;
-        const int nb = nbs[b];
+        const int nb = lens[b] < 0 ? -1 : (lens[b] + kPage - 1) / kPage;
         const uint32_t per_unit = kSegmentCost + (nb < 0 ? 1u : (uint32_t)nb);
         const uint32_t off = r - rows[b];
         const uint32_t g = off / per_unit, o = off % per_unit;  // o < kSegmentCost: charged rows
@@ -112,7 +124,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
         const int j0 = (int)(o > kSegmentCost ? o - kSegmentCost : 0u);
         const int j1 = (int)(e > kSegmentCost ? e - kSegmentCost : 0u);
         if (j1 > j0) {
-            sel::score_segment<T, D, kScanRows>(
+            sel::score_segment<T, D, kScanRows, kRun>(
                 a.s, b, (int)g, j0, j1, nb, sm, crow,
                 a.ready + ((size_t)b * Hkv + g) * kReadyStride, tag);
             __syncthreads();  // LDS is reused by the next segment
@@ -130,6 +142,21 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
         if (item >= total) break;
         const int unit = item / a.nsplit, split = item % a.nsplit;
         const int bu = unit / Hkv;
+        const int L = lens[bu];
+        const int nb = L < 0 ? -1 : (L + kPage - 1) / kPage;
+        // the sequence's block-table row is requested before the wait, so that
+        // the attention finds the selected blocks' pages in LDS
+        const bool row_lds = nb >= 0 && nb <= kRun;
+        constexpr int kRowPer = kRun / kThreads;
+        int32_t prow[kRowPer];
+        if (row_lds) {
+            const int32_t *bt_row = a.s.bt + (size_t)bu * a.s.max_blocks;
+#pragma unroll
+            for (int i = 0; i < kRowPer; ++i) {
+                const int j = i * kThreads + tid;
+                prow[i] = j < nb ? bt_row[j] : -1;
+            }
+        }
         if (tid == 0) {
             const uint32_t *rw = a.ready + (size_t)unit * kReadyStride;
             uint32_t spins = 0;
@@ -142,7 +169,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
             }
         }
         __syncthreads();
-        const int nb = nbs[bu];
         const int lo = split * a.t.bps, hi = min(a.s.top_k, lo + a.t.bps);
         if (nb >= 0) {
             __builtin_amdgcn_s_setprio(3);
@@ -154,9 +180,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
                              tk);
             __builtin_amdgcn_s_setprio(0);
         }
+        if (row_lds) {
+#pragma unroll
+            for (int i = 0; i < kRowPer; ++i)
+                if (i * kThreads + tid < nb) pages[i * kThreads + tid] = prow[i];
+        }
         __syncthreads();
         att::attend_item<T, D, att::kSelected, (sizeof(T) == 4 ? 2 : kStageBlocks)>(
-            a.t, unit, split, dyn, &flag, list);
+            a.t, unit, split, dyn, &flag, list, L < 0 ? 0 : L, row_lds ? pages : nullptr);
         __syncthreads();  // LDS is reused by the next item
     }
     // the last workgroup to leave re-arms the queue and advances the counter
@@ -229,7 +260,7 @@ hipError_t launch_decode_step(const Dims &d, const SelectPlan &sp, const AttendP
                               hipStream_t stream) {
     // a split's share of the selection (at most 4 * 64 entries) is kept in the
     // score staging area
-    if (ap.bps > kMaxChunk) return hipErrorInvalidValue;
+    if (ap.bps > kRun) return hipErrorInvalidValue;
     StepArgs a;
     a.s = sel::SelectArgs{q, centroids, block_table, seq_lens, indices, scores, sel_counters, err,
                           d.Hq, d.Hkv, d.num_pages, d.max_blocks, top_k, sp.chunk, sp.nchunk_max,
