@@ -242,18 +242,80 @@ __device__ __forceinline__ void compact(const uint32_t (&key)[N], uint32_t lo, u
     }
 }
 
+// The end of a radix selection, by one wave: the m <= 256 keys still inside
+// [lo, hi] are in cand[0 .. m).  They are taken four per lane for cheap passes;
+// once at most 64 are left each lane counts the candidates above and at its own
+// key, which names T directly.  On return lo = T and need = the number of keys
+// equal to T to keep.  Uses cand and hist.
+__device__ __forceinline__ void finish_from_cand(uint32_t *cand, int m, uint32_t &lo, uint32_t &hi,
+                                                 int &need, uint32_t *hist, int lane) {
+    uint32_t k4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) k4[e] = e * kWave + lane < m ? cand[e * kWave + lane] : 0u;
+    __builtin_amdgcn_wave_barrier();
+    cand[lane] = 0u;  // the finisher reads all 64 slots: absent keys are 0
+    __builtin_amdgcn_wave_barrier();
+    while (lo < hi && m > kWave) {
+        radix_pass(k4, lo, hi, need, hist, lane);
+        m = count_in_range(k4, lo, hi);
+    }
+    if (lo < hi) {
+        // at most 64 keys left: every lane ranks its own against all of them
+        // (LDS broadcast reads); T is the one of rank `need`
+        compact(k4, lo, hi, cand, lane);
+        __builtin_amdgcn_wave_barrier();
+        // all 64 slots at once (slots from m on hold 0, below every key)
+        const uint32_t mine = lane < m ? cand[lane] : 0u;
+        uint4 c4[kWave / 4];
+#pragma unroll
+        for (int t = 0; t < kWave / 4; ++t) c4[t] = reinterpret_cast<const uint4 *>(cand)[t];
+        int gt = 0, ge = 0;
+#pragma unroll
+        for (int t = 0; t < kWave / 4; ++t) {
+            const uint32_t cv[4] = {c4[t].x, c4[t].y, c4[t].z, c4[t].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                gt += cv[e] > mine ? 1 : 0;
+                ge += cv[e] >= mine ? 1 : 0;
+            }
+        }
+        const int src_lane = (int)__builtin_ctzll(__ballot(lane < m && gt < need && ge >= need));
+        lo = (uint32_t)__builtin_amdgcn_readlane((int)mine, src_lane);
+        need -= __builtin_amdgcn_readlane(gt, src_lane);  // keys equal to T to take
+    }
+}
+
+// Writes the winners in ascending block order, by one wave: lane l holds the
+// bitmap words a (keys above T) and e (keys equal to T) of blocks [32l, 32l+32);
+// every key above T is kept, then keys equal to T in block order until take_eq.
+__device__ __forceinline__ void write_winners(uint32_t a, uint32_t e, int take_eq, int kb,
+                                              int top_k, const TopkOut &out, int lane) {
+    int e_before = (int)(wave_inclusive_scan((uint32_t)__popc(e)) - (uint32_t)__popc(e));
+    while (e && e_before < take_eq) {  // lowest-index equal keys first
+        const uint32_t bit = e & (0u - e);
+        a |= bit;
+        e ^= bit;
+        ++e_before;
+    }
+    int pos = (int)(wave_inclusive_scan((uint32_t)__popc(a)) - (uint32_t)__popc(a));
+    while (a) {
+        if (pos < kb) out.put(pos, lane * 32 + __builtin_ctz(a));
+        ++pos;
+        a &= a - 1u;
+    }
+    for (int i = kb + lane; i < top_k; i += kWave) out.put(i, -1);
+}
+
 // Top-k of a unit's nb scores in one wave (nb <= 64 * KMAX <= 2048).
 // Lane l holds the keys of blocks i*64 + l in registers.  The kb-th largest key
 // T is found by radix selection over value ranges: a pass histograms the keys
 // inside [lo, hi] into 256 bins and shrinks [lo, hi] to the bin holding the rank
 // still needed, resolving eight bits.  The first pass leaves about a hundred
 // keys in range at the usual score spreads (its top bins span whole binades):
-// up to 256 are compacted four per lane for the next, cheap passes, and once
-// at most 64 are left each lane counts the candidates above and at its own
-// key, which names T directly.  The winners (every key above T,
-// then keys equal to T in block order until kb) are recorded as LDS bitmaps
-// built from ballots (slot i's ballot is bitmap words 2i and 2i+1), and a
-// popcount prefix sum writes them in ascending block order.
+// up to 256 are compacted and finished by finish_from_cand.  The winners
+// (every key above T, then keys equal to T in block order until kb) are
+// recorded as bitmaps built from ballots (slot i's ballot covers words 2i and
+// 2i+1) and a popcount prefix sum writes them in ascending block order.
 template <int KMAX, typename Src>
 __device__ __forceinline__ void select_topk_wave(const Src &src, int nb, int top_k,
                                                  const TopkOut &out, TopkSmem &sm) {
@@ -281,48 +343,12 @@ __device__ __forceinline__ void select_topk_wave(const Src &src, int nb, int top
             m = count_in_range(key, lo, hi);
         }
         if (lo < hi) {
-            // up to 256 keys left: four per lane, then passes over those
             compact(key, lo, hi, cand, lane);
             __builtin_amdgcn_wave_barrier();
-            uint32_t k4[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) k4[e] = e * kWave + lane < m ? cand[e * kWave + lane] : 0u;
-            __builtin_amdgcn_wave_barrier();
-            cand[lane] = 0u;  // the finisher reads all 64 slots: absent keys are 0
-            __builtin_amdgcn_wave_barrier();
-            while (lo < hi && m > kWave) {
-                radix_pass(k4, lo, hi, need, hist, lane);
-                m = count_in_range(k4, lo, hi);
-            }
-            if (lo < hi) {
-                // at most 64 keys left: every lane ranks its own against all
-                // of them (LDS broadcast reads); T is the one of rank `need`
-                compact(k4, lo, hi, cand, lane);
-                __builtin_amdgcn_wave_barrier();
-                // all 64 slots at once (slots from m on hold 0, below every key)
-                const uint32_t mine = lane < m ? cand[lane] : 0u;
-                uint4 c4[kWave / 4];
-#pragma unroll
-                for (int t = 0; t < kWave / 4; ++t) c4[t] = reinterpret_cast<const uint4 *>(cand)[t];
-                int gt = 0, ge = 0;
-#pragma unroll
-                for (int t = 0; t < kWave / 4; ++t) {
-                    const uint32_t cv[4] = {c4[t].x, c4[t].y, c4[t].z, c4[t].w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        gt += cv[e] > mine ? 1 : 0;
-                        ge += cv[e] >= mine ? 1 : 0;
-                    }
-                }
-                const int src_lane =
-                    (int)__builtin_ctzll(__ballot(lane < m && gt < need && ge >= need));
-                lo = (uint32_t)__builtin_amdgcn_readlane((int)mine, src_lane);
-                need -= __builtin_amdgcn_readlane(gt, src_lane);  // keys equal to T to take
-            }
+            finish_from_cand(cand, m, lo, hi, need, hist, lane);
         }
     }
     const uint32_t T = lo;
-    const int take_eq = need;  // keys equal to T to keep, lowest block index first
     // bitmaps: lane l's words cover blocks [32l, 32l + 32), the low or high
     // half of slot l/2's ballot (lanes from 2*KMAX on hold none)
     uint32_t a = 0u, e = 0u;
@@ -335,20 +361,136 @@ __device__ __forceinline__ void select_topk_wave(const Src &src, int nb, int top
             e = (lane & 1) ? (uint32_t)(eb >> 32) : (uint32_t)eb;
         }
     }
-    int e_before = (int)(wave_inclusive_scan((uint32_t)__popc(e)) - (uint32_t)__popc(e));
-    while (e && e_before < take_eq) {  // lowest-index equal keys first
-        const uint32_t bit = e & (0u - e);
-        a |= bit;
-        e ^= bit;
-        ++e_before;
+    write_winners(a, e, need, kb, top_k, out, lane);
+}
+
+// Top-k of a unit's nb <= 256 * KMAX <= 2048 scores by the four waves of the
+// workgroup.  Thread t holds the keys of blocks i*256 + t.  The radix passes of
+// select_topk_wave run over the workgroup: one LDS histogram fed by every wave,
+// each wave locating the bin itself (identical results).  Once at most 256 keys
+// are in range they are compacted wave by wave and wave 0 finishes alone
+// (finish_from_cand).  Bitmaps come from per-wave ballots: slot i of wave v
+// covers blocks 256i + 64v .. +63, words 8i + 2v and 8i + 2v + 1.
+template <int KMAX, typename Src>
+__device__ __forceinline__ void select_topk_wg4(const Src &src, int nb, int top_k,
+                                                const TopkOut &out, TopkSmem &sm) {
+    static_assert(KMAX <= 8, "64 bitmap words cover 2048 blocks");
+    uint32_t *hist = sm.hist, *cand = sm.cand, *red = sm.red;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int kb = min(top_k, nb);
+    uint32_t key[KMAX];
+    src.fill(key, tid, kThreads, nb);
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {
+        const int j = i * kThreads + tid;
+        key[i] = j < nb ? score_key(__uint_as_float(key[i])) : 0u;  // 0 = no key
+        kmin = j < nb ? min(kmin, key[i]) : kmin;
+        kmax = max(kmax, key[i]);
     }
-    int pos = (int)(wave_inclusive_scan((uint32_t)__popc(a)) - (uint32_t)__popc(a));
-    while (a) {
-        if (pos < kb) out.put(pos, lane * 32 + __builtin_ctz(a));
-        ++pos;
-        a &= a - 1u;
+    kmin = ~wave_max_u32(~kmin);
+    kmax = wave_max_u32(kmax);
+    if (lane == 0) {
+        red[wave] = ~kmin;
+        red[kWaves + wave] = kmax;
     }
-    for (int i = kb + lane; i < top_k; i += kWave) out.put(i, -1);
+    __syncthreads();
+    uint32_t lo = ~max(max(red[0], red[1]), max(red[2], red[3]));
+    uint32_t hi = max(max(red[kWaves], red[kWaves + 1]), max(red[kWaves + 2], red[kWaves + 3]));
+    int need = kb;
+    // keys of the workgroup inside [lo, hi] (one barrier; red's halves alternate)
+    int parity = 0;
+    auto count_wg = [&]() {
+        int c = 0;
+#pragma unroll
+        for (int i = 0; i < KMAX; ++i) c += __popcll(__ballot(key[i] - lo <= hi - lo));
+        __syncthreads();  // red / hist readers of the previous step are done
+        if (lane == 0) red[parity * kWaves + wave] = (uint32_t)c;
+        __syncthreads();
+        int m = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) m += (int)red[parity * kWaves + w];
+        parity ^= 1;
+        return m;
+    };
+    auto pass_wg = [&]() {
+        const uint32_t span = hi - lo;
+        const int shift = max(0, 24 - __builtin_clz(span));  // (span >> shift) < 256
+        __syncthreads();  // the previous pass's readers of hist are done
+        if (wave == 0) reinterpret_cast<uint4 *>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < KMAX; ++i) {
+            const uint32_t off = key[i] - lo;
+            atomicAdd(&hist[off <= span ? (off >> shift) : 256u + lane], 1u);
+        }
+        __syncthreads();
+        const uint32_t b_sel = locate_bin(hist, need, lane);  // every wave, same result
+        const uint32_t top = (b_sel << shift) + ((1u << shift) - 1u);
+        if (top < span) hi = lo + top;
+        lo += b_sel << shift;
+    };
+    int m = nb;
+    if (lo < hi) pass_wg();
+    if (lo < hi) {
+        m = count_wg();
+        while (lo < hi && m > 4 * kWave) {  // rare: keys bunched in one bin
+            pass_wg();
+            m = count_wg();
+        }
+    }
+    if (lo < hi) {
+        // compaction wave by wave: wave v's keys after those of waves < v
+        int c = 0;
+#pragma unroll
+        for (int i = 0; i < KMAX; ++i) c += __popcll(__ballot(key[i] - lo <= hi - lo));
+        __syncthreads();
+        if (lane == 0) red[wave] = (uint32_t)c;
+        __syncthreads();
+        int base = 0;
+        for (int w = 0; w < wave; ++w) base += (int)red[w];
+#pragma unroll
+        for (int i = 0; i < KMAX; ++i) {
+            const bool in = key[i] - lo <= hi - lo;
+            const uint64_t mask = __ballot(in);
+            const int pos = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                       (uint32_t)(mask >> 32),
+                                       __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+            if (in) cand[pos] = key[i];
+            base += __popcll(mask);
+        }
+        __syncthreads();
+        if (wave == 0) {
+            finish_from_cand(cand, m, lo, hi, need, hist, lane);
+            if (lane == 0) {
+                red[0] = lo;
+                red[1] = (uint32_t)need;
+            }
+        }
+        __syncthreads();
+        lo = red[0];
+        need = (int)red[1];
+        __syncthreads();  // red is reused below
+    }
+    const uint32_t T = lo;
+    // bitmaps through LDS (cand is free again): above in cand[0..64), equal in cand[64..128)
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {
+        const uint64_t ab = __ballot(key[i] > T);
+        const uint64_t eb = __ballot(key[i] == T);  // absent keys are 0 < T
+        if (lane == 0) {
+            cand[8 * i + 2 * wave] = (uint32_t)ab;
+            cand[8 * i + 2 * wave + 1] = (uint32_t)(ab >> 32);
+            cand[64 + 8 * i + 2 * wave] = (uint32_t)eb;
+            cand[64 + 8 * i + 2 * wave + 1] = (uint32_t)(eb >> 32);
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const uint32_t a = lane < 8 * KMAX ? cand[lane] : 0u;
+        const uint32_t e = lane < 8 * KMAX ? cand[64 + lane] : 0u;
+        write_winners(a, e, need, kb, top_k, out, lane);
+    }
 }
 
 // Top-k of a unit's nb scores by the whole workgroup.  Thread t holds the keys
@@ -427,9 +569,9 @@ __device__ __forceinline__ void select_topk_wg(const Src &src, int nb, int top_k
     for (int i = kb + tid; i < top_k; i += kThreads) out.put(i, -1);
 }
 
-// Selection of the unit's top-k blocks, by the workgroup that scored its last
-// chunk.  One wave handles up to 2048 blocks with no barrier; longer contexts
-// use the whole workgroup.
+// Selection of a unit's top-k blocks by a whole workgroup: one wave up to 256
+// blocks (no barrier), the four waves up to 2048 (radix passes over one shared
+// histogram), a bisection over the key space beyond.
 template <typename Src>
 __device__ __forceinline__ void select_topk(const Src &src, int nb, int top_k,
                                             const TopkOut &out, TopkSmem &sm) {
@@ -443,10 +585,13 @@ __device__ __forceinline__ void select_topk(const Src &src, int nb, int top_k,
         else select_topk_wg<32>(src, nb, top_k, out, sm);
         return;
     }
+    if (nb > 4 * kWave) {  // the whole workgroup, up to eight keys per thread
+        if (nb <= 4 * kThreads) select_topk_wg4<4>(src, nb, top_k, out, sm);
+        else select_topk_wg4<8>(src, nb, top_k, out, sm);
+        return;
+    }
     if (tid >= kWave) return;
-    if (nb <= 8 * kWave) select_topk_wave<8>(src, nb, top_k, out, sm);
-    else if (nb <= 16 * kWave) select_topk_wave<16>(src, nb, top_k, out, sm);
-    else select_topk_wave<32>(src, nb, top_k, out, sm);
+    select_topk_wave<4>(src, nb, top_k, out, sm);
 }
 
 // Sum over the 16 lanes of a DPP row (result in every lane of the row).
