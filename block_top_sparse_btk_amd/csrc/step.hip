@@ -54,10 +54,9 @@ constexpr int kRun = 2048;       // blocks per scan run: shares (~550 blocks at 
 // Rows charged for a unit beyond its blocks when the shares are cut: a segment
 // costs round trips in which nothing streams (its setup, its closing
 // store-and-count) and the unit's touched page its refresh, so a share that
-// starts a unit gets that many fewer blocks.
-constexpr int kSegmentCost = 64;
-// Share taper beta = kShareTaper / 64 (see the share boundaries).
-constexpr int kShareTaper = 0;
+// starts a unit gets that many fewer blocks (a second segment measured about
+// 6 us, some 140 rows of streaming, on the Qwen3-8B-shaped step).
+constexpr int kSegmentCost = 160;
 
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
@@ -105,16 +104,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
 
     // ---- phase 1: this workgroup's share of the rows
     const uint64_t R = rows[a.B];
-    // share boundaries R * F(w / G), F(x) = x + beta * x * (1 - x): the density
-    // falls linearly from 1 + beta to 1 - beta, since workgroups launched later
-    // (higher index) start later and share their CU with one that started first
-    const uint64_t G = gridDim.x;
-    auto boundary = [&](uint64_t w) {
-        return (uint32_t)(R * w * (64 * G + (uint64_t)kShareTaper * (G - w)) / (64 * G * G));
-    };
-    const uint32_t r1 = boundary(blockIdx.x + 1);
+    const uint32_t r1 = (uint32_t)(R * (blockIdx.x + 1) / gridDim.x);
     int b = 0;
-    for (uint32_t r = boundary(blockIdx.x); r < r1;) {
+    for (uint32_t r = (uint32_t)(R * blockIdx.x / gridDim.x); r < r1;) {
         while (rows[b + 1] <= r) ++b;
         const int nb = lens[b] < 0 ? -1 : (lens[b] + kPage - 1) / kPage;
         const uint32_t per_unit = kSegmentCost + (nb < 0 ? 1u : (uint32_t)nb);
