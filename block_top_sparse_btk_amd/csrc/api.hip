@@ -58,13 +58,13 @@ WorkspaceLayout workspace_layout(const Dims &d, int top_k) {
     const size_t nsplit = sp.nsplit_max > dp.nsplit_max ? sp.nsplit_max : dp.nsplit_max;
     const size_t row = (size_t)d.group() * d.D + 2 * (size_t)d.group();
     WorkspaceLayout w;
+    w.queue = kQueueOffset;
     w.sel_counters = 256;
     w.att_counters = w.sel_counters + align256(units * sizeof(uint32_t));
-    w.scores = w.att_counters + align256(units * sizeof(uint32_t));
+    w.ready = w.att_counters + align256(units * sizeof(uint32_t));
+    w.scores = w.ready + align256(units * (size_t)kReadyStride * sizeof(uint32_t));
     w.partials = w.scores + align256(units * d.max_blocks * sizeof(float));
-    w.ready = w.partials + align256(units * nsplit * row * sizeof(float));
-    w.queue = w.ready + align256(units * (size_t)kReadyStride * sizeof(uint32_t));
-    w.total = w.queue + 256;
+    w.total = w.partials + align256(units * nsplit * row * sizeof(float));
     return w;
 }
 
@@ -74,13 +74,15 @@ TokenWorkspaceLayout token_workspace_layout(const Dims &d, int top_tokens) {
     w.cap = top_tokens < d.max_blocks ? top_tokens : d.max_blocks;
     const AttendPlan ap = plan_attend(d, w.cap, false);
     const size_t row = (size_t)d.group() * d.D + 2 * (size_t)d.group();
+    // state kept from call to call (all zero after a call) first, then scratch,
+    // so that a smaller problem on the same workspace finds zeros there
     w.counters = 256;
-    w.scores = w.counters + align256(units * sizeof(uint32_t));
-    w.entries = w.scores + align256(units * (size_t)d.max_blocks * kPage * sizeof(float));
-    w.counts = w.entries + align256(units * (size_t)w.cap * sizeof(uint32_t));
-    w.ranges = w.counts + align256(units * sizeof(uint32_t));
+    w.ranges = w.counters + align256(units * sizeof(uint32_t));
     w.att_counters = w.ranges + align256(2 * units * sizeof(uint32_t));
-    w.partials = w.att_counters + align256(units * sizeof(uint32_t));
+    w.counts = w.att_counters + align256(units * sizeof(uint32_t));
+    w.scores = w.counts + align256(units * sizeof(uint32_t));
+    w.entries = w.scores + align256(units * (size_t)d.max_blocks * kPage * sizeof(float));
+    w.partials = w.entries + align256(units * (size_t)w.cap * sizeof(uint32_t));
     w.total = w.partials + align256(units * (size_t)ap.nsplit_max * row * sizeof(float));
     return w;
 }

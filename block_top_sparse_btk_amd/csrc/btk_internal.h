@@ -133,14 +133,18 @@ struct PrefixGroups {
 AttendPlan plan_attend(const Dims &d, int list_len_max, bool dense);
 
 // Workspace layout (bytes, each region 256-aligned):
-//   [0, 256)                   error word + spare
-//   select counters            B*Hkv uint32
-//   attend counters            B*Hkv uint32
+//   [0, 256)                   error word; decode-step queue words at byte kQueueOffset
+//   select counters            B*Hkv uint32      zero after every call
+//   attend counters            B*Hkv uint32      zero after every call
+//   ready words                B*Hkv*kReadyStride uint32 (decode step: launch tags)
 //   scores scratch             B*Hkv*max_blocks float
 //   attend partials            B*Hkv*nsplit_max*(r*D + 2r) float (max of sparse, dense)
-//   ready words                B*Hkv*kReadyStride uint32 (decode step)
-//   queue                      3 uint32 (decode step)
-constexpr int kReadyStride = 32;  // one 128-byte line per unit: each is polled on its own
+// Every region that carries state from call to call comes before the scratch,
+// the ones left at zero first and the tags next, and each grows with B*Hkv: a
+// smaller problem on the same workspace then finds zeros where it needs zeros
+// and, where it reads tags, only zeros or tags of earlier launches.
+constexpr int kReadyStride = 32;     // one 128-byte line per unit: each is polled on its own
+constexpr size_t kQueueOffset = 128;  // 4 uint32: items, exits, launch counter, spare
 struct WorkspaceLayout {
     size_t sel_counters, att_counters, scores, partials, ready, queue, total;
 };
@@ -184,9 +188,9 @@ hipError_t launch_token_select(const Dims &d, const void *q, const void *k_cache
                                int32_t *token_idx, uint32_t *err, hipStream_t stream);
 
 // Workspace of the token-level baseline (bytes, each region 256-aligned):
-//   [0, 256) error word; counters; scores B*Hkv*max_blocks*16 float;
-//   entries B*Hkv*cap uint32; counts B*Hkv uint32; score ranges B*Hkv*2 uint32;
-//   attend counters; partials
+//   [0, 256) error word; counters; score ranges B*Hkv*2 uint32; attend counters
+//   (these three zero after every call); counts B*Hkv uint32; scores
+//   B*Hkv*max_blocks*16 float; entries B*Hkv*cap uint32; partials
 struct TokenWorkspaceLayout {
     size_t counters, scores, entries, counts, ranges, att_counters, partials, total;
     int cap;

@@ -394,6 +394,111 @@ def test_decode_step_equals_separate_calls_and_oracle(label, spec):
     check_lse(results[0][2], ora["lse"], bt.dtype, st["equal_mask"], bt.group)
 
 
+def _step_both(q, k_cache, v_cache, bt, sl, cent, k, prob, ws_step, first=None):
+    """The step as one launch (on ws_step) and as three calls (fresh workspace)."""
+    c1, c2 = cent.clone(), cent.clone()
+    ws1 = btk.new_workspace(prob, k, DEV)
+    lse1 = torch.full((q.shape[0], q.shape[1]), float("nan"), device=DEV)
+    lse2 = lse1.clone()
+    out1 = torch.zeros_like(q)
+    out2 = torch.zeros_like(q)
+    _, idx1 = btk.sparse_decode_step(q, k_cache, v_cache, bt, sl, c1, k, ws1, first_pos=first,
+                                     out=out1, lse=lse1, problem=prob)
+    _, idx2 = btk.btk_decode_step(q, k_cache, v_cache, bt, sl, c2, k, ws_step, first_pos=first,
+                                  out=out2, lse=lse2, problem=prob)
+    torch.cuda.synchronize()
+    return (dict(idx=idx1.cpu(), out=out1.cpu(), lse=lse1.cpu(), cent=c1.cpu(),
+                 err=btk.workspace_error_bits(ws1)),
+            dict(idx=idx2.cpu(), out=out2.cpu(), lse=lse2.cpu(), cent=c2.cpu(),
+                 err=btk.workspace_error_bits(ws_step)))
+
+
+def test_decode_step_flags_invalid_lengths_and_pages_like_separate_calls():
+    # an empty sequence, one longer than its table row and a page id past the pool,
+    # next to valid sequences: the same error bits, -1 rows and valid results as
+    # the three calls
+    bt = synth.make_batch(name="step-guards", batch=5, num_q_heads=8, num_kv_heads=2,
+                          head_dim=128, seq_lens=[700, 40, 2500, 300, 900], top_k=8, seed=41)
+    _say("[step] invalid lengths and pages")
+    d = bt.to(DEV)
+    prob = btk.make_problem(d.q, d.k_cache, d.block_table)
+    cent = torch.zeros((bt.num_pages, 2, 128), device=DEV)
+    btk.btk_centroid_update(d.k_cache, d.block_table, d.seq_lens, cent, problem=prob)
+    sl = d.seq_lens.clone()
+    sl[1] = 0
+    sl[3] = bt.max_blocks * 16 + 1
+    table = d.block_table.clone()
+    table[4, 5] = bt.num_pages + 7
+    first = (sl - 1).clamp(min=0).to(torch.int32)
+    ws = btk.new_workspace(prob, bt.top_k, DEV)
+    a, b = _step_both(d.q, d.k_cache, d.v_cache, table, sl, cent, bt.top_k, prob, ws, first)
+    assert a["err"] == b["err"] == 1 | 2
+    assert torch.equal(a["idx"], b["idx"])
+    assert (b["idx"][1] == -1).all() and (b["idx"][3] == -1).all()
+    assert not (b["idx"][4] == 5).any()  # the bad page's block is never selected
+    ok = [0, 2, 4]
+    assert torch.equal(a["out"][ok], b["out"][ok])
+    assert torch.equal(a["lse"][ok], b["lse"][ok])
+    assert torch.equal(a["cent"], b["cent"])
+
+
+def test_decode_step_one_workspace_for_problems_of_different_batch():
+    # a smaller problem in between leaves no state behind for the larger one
+    big = synth.make_batch(name="step-ws-big", batch=6, num_q_heads=8, num_kv_heads=2,
+                           head_dim=128, seq_lens=[3000, 200, 1800, 4096, 64, 999], top_k=16,
+                           seed=42)
+    _say("[step] one workspace, batch 6 / 3 / 6")
+    d = big.to(DEV)
+    prob = btk.make_problem(d.q, d.k_cache, d.block_table)
+    cent = torch.zeros((big.num_pages, 2, 128), device=DEV)
+    btk.btk_centroid_update(d.k_cache, d.block_table, d.seq_lens, cent, problem=prob)
+    first = (d.seq_lens - 1).to(torch.int32)
+    ws = btk.new_workspace(prob, 16, DEV)
+    sub = slice(1, 4)
+    prob_s = btk.make_problem(d.q[sub], d.k_cache, d.block_table[sub])
+    for q_, t_, s_, f_, p_ in ((d.q, d.block_table, d.seq_lens, first, prob),
+                               (d.q[sub].contiguous(), d.block_table[sub].contiguous(),
+                                d.seq_lens[sub].contiguous(), first[sub].contiguous(), prob_s),
+                               (d.q, d.block_table, d.seq_lens, first, prob)):
+        a, b = _step_both(q_, d.k_cache, d.v_cache, t_, s_, cent, 16, p_, ws, f_)
+        assert a["err"] == 0 and b["err"] == 0
+        for key in ("idx", "out", "lse", "cent"):
+            assert torch.equal(a[key], b[key]), key
+
+
+def test_decode_step_shares_longer_than_one_run():
+    # about 1.4M centroid rows: every workgroup's share spans more than one
+    # 2048-block run (inputs drawn on the device; the three calls, pinned to the
+    # oracle by the other tests, are the reference)
+    B, hq, hkv, dim, nb_max = 40, 8, 8, 64, 4096
+    g = torch.Generator(device=DEV)
+    g.manual_seed(43)
+    lens = torch.randint(60000, nb_max * 16 + 1, (B,), generator=g, device=DEV,
+                         dtype=torch.int64).to(torch.int32)
+    nbs = ((lens + 15) // 16).tolist()
+    num_pages = sum(nbs) + 64
+    _say(f"[step] long shares: B={B} pages={num_pages}")
+    q = torch.randn(B, hq, dim, generator=g, device=DEV).to(torch.bfloat16)
+    k_cache = torch.randn(num_pages, hkv, 16, dim, generator=g, device=DEV).to(torch.bfloat16)
+    v_cache = torch.randn(num_pages, hkv, dim, 16, generator=g, device=DEV).to(torch.bfloat16)
+    perm = torch.randperm(num_pages, generator=g, device=DEV).to(torch.int32)
+    table = torch.full((B, nb_max), -1, dtype=torch.int32, device=DEV)
+    at = 0
+    for b, nb in enumerate(nbs):
+        table[b, :nb] = perm[at:at + nb]
+        at += nb
+    prob = btk.make_problem(q, k_cache, table)
+    cent = torch.zeros((num_pages, hkv, dim), device=DEV)
+    btk.btk_centroid_update(k_cache, table, lens, cent, problem=prob)
+    first = (lens - 1).to(torch.int32)
+    ws = btk.new_workspace(prob, 32, DEV)
+    a, b = _step_both(q, k_cache, v_cache, table, lens, cent, 32, prob, ws, first)
+    assert a["err"] == 0 and b["err"] == 0
+    for key in ("idx", "out", "lse", "cent"):
+        assert torch.equal(a[key], b[key]), key
+    assert (b["idx"] >= 0).all()
+
+
 # ------------------------------------------------------------------ local-window baseline
 
 LOCAL_CASES = [("config2", dict(cfg=2)), ("config3", dict(cfg=3)), ("config4", dict(cfg=4)),
