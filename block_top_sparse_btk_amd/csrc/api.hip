@@ -307,6 +307,7 @@ btk_status_t btk_decode_step(const btk_problem_t *problem, const void *q, const 
         reinterpret_cast<uint32_t *>(ws + w.sel_counters),
         reinterpret_cast<uint32_t *>(ws + w.att_counters),
         reinterpret_cast<uint32_t *>(ws + w.ready), reinterpret_cast<uint32_t *>(ws + w.queue),
+        reinterpret_cast<uint32_t *>(ws + btk::kStealOffset),
         reinterpret_cast<uint32_t *>(ws), (hipStream_t)stream));
 }
 

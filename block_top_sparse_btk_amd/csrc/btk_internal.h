@@ -133,7 +133,8 @@ struct PrefixGroups {
 AttendPlan plan_attend(const Dims &d, int list_len_max, bool dense);
 
 // Workspace layout (bytes, each region 256-aligned):
-//   [0, 256)                   error word; decode-step queue words at byte kQueueOffset
+//   [0, 256)                   error word; decode-step chunk counter at byte kStealOffset
+//                              and queue words at byte kQueueOffset
 //   select counters            B*Hkv uint32      zero after every call
 //   attend counters            B*Hkv uint32      zero after every call
 //   ready words                B*Hkv*kReadyStride uint32 (decode step: launch tags)
@@ -145,6 +146,7 @@ AttendPlan plan_attend(const Dims &d, int list_len_max, bool dense);
 // and, where it reads tags, only zeros or tags of earlier launches.
 constexpr int kReadyStride = 32;     // one 128-byte line per unit: each is polled on its own
 constexpr size_t kQueueOffset = 128;  // 4 uint32: items, exits, launch counter, spare
+constexpr size_t kStealOffset = 64;   // 1 uint32, off the queue words' line
 struct WorkspaceLayout {
     size_t sel_counters, att_counters, scores, partials, ready, queue, total;
 };
@@ -203,7 +205,8 @@ hipError_t launch_decode_step(const Dims &d, const SelectPlan &sp, const AttendP
                               const int32_t *first_pos, float *centroids, int top_k,
                               int32_t *indices, float *scores, void *out, float *lse,
                               float *partials, uint32_t *sel_counters, uint32_t *att_counters,
-                              uint32_t *ready, uint32_t *queue, uint32_t *err,
+                              uint32_t *ready, uint32_t *queue, uint32_t *steal,
+                              uint32_t *err,
                               hipStream_t stream);
 
 }  // namespace btk

@@ -42,6 +42,7 @@ struct StepArgs {
     att::AttendArgs t;
     uint32_t *ready;  // [units * kReadyStride]: word u * kReadyStride is unit u's ready tag
     uint32_t *queue;  // [0] items taken, [1] workgroups that have left, [2] launch counter
+    uint32_t *steal;  // scan chunks taken (a line of its own)
     int B, units, nsplit;
 };
 
@@ -57,6 +58,10 @@ constexpr int kRun = 2048;       // blocks per scan run: shares (~550 blocks at 
 // starts a unit gets that many fewer blocks (a second segment measured about
 // 6 us, some 140 rows of streaming, on the Qwen3-8B-shaped step).
 constexpr int kSegmentCost = 160;
+// The last 1/kStealFrac of the rows is handed out in chunks of kStealRows to the
+// workgroups that finish their static share first.
+constexpr int kStealFrac = 8;
+constexpr uint32_t kStealRows = 256;
 
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
@@ -102,11 +107,24 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
     }
     const uint32_t tag = tag_s;
 
-    // ---- phase 1: this workgroup's share of the rows
+    // ---- phase 1: this workgroup's static share of the first rows, then chunks
+    // of the rest while any are left (shares end at different times: the
+    // workgroups that finish first take more of the rest)
     const uint64_t R = rows[a.B];
-    const uint32_t r1 = (uint32_t)(R * (blockIdx.x + 1) / gridDim.x);
+    const uint64_t RS = R - R / kStealFrac;
+    uint32_t r = (uint32_t)(RS * blockIdx.x / gridDim.x);
+    uint32_t r1 = (uint32_t)(RS * (blockIdx.x + 1) / gridDim.x);
     int b = 0;
-    for (uint32_t r = (uint32_t)(R * blockIdx.x / gridDim.x); r < r1;) {
+    for (;;) {
+        if (r >= r1) {
+            if (tid == 0) item_s = (int)atomicAdd(a.steal, 1u);
+            __syncthreads();
+            const uint64_t c0 = RS + (uint64_t)item_s * kStealRows;
+            __syncthreads();  // item_s is written again
+            if (c0 >= R) break;
+            r = (uint32_t)c0;
+            r1 = (uint32_t)min(R, c0 + kStealRows);
+        }
         while (rows[b + 1] <= r) ++b;
         const int nb = lens[b] < 0 ? -1 : (lens[b] + kPage - 1) / kPage;
         const uint32_t per_unit = kSegmentCost + (nb < 0 ? 1u : (uint32_t)nb);
@@ -188,6 +206,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
         if (prev == gridDim.x - 1) {
             __hip_atomic_store(&a.queue[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(&a.queue[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.steal, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(&a.queue[2], tag == 0xffffffffu ? 0u : tag, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -248,8 +267,8 @@ hipError_t launch_decode_step(const Dims &d, const SelectPlan &sp, const AttendP
                               const int32_t *first_pos, float *centroids, int top_k,
                               int32_t *indices, float *scores, void *out, float *lse,
                               float *partials, uint32_t *sel_counters, uint32_t *att_counters,
-                              uint32_t *ready, uint32_t *queue, uint32_t *err,
-                              hipStream_t stream) {
+                              uint32_t *ready, uint32_t *queue, uint32_t *steal,
+                              uint32_t *err, hipStream_t stream) {
     // a split's share of the selection (at most 4 * 64 entries) is kept in the
     // score staging area
     if (ap.bps > kRun) return hipErrorInvalidValue;
@@ -262,6 +281,7 @@ hipError_t launch_decode_step(const Dims &d, const SelectPlan &sp, const AttendP
                           ap.nsplit_max, d.sm_scale * 1.44269504088896340736f, nullptr};
     a.ready = ready;
     a.queue = queue;
+    a.steal = steal;
     a.B = d.B;
     a.units = d.B * d.Hkv;
     a.nsplit = ap.nsplit_max;
