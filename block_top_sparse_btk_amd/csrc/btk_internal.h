@@ -145,7 +145,7 @@ AttendPlan plan_attend(const Dims &d, int list_len_max, bool dense);
 // smaller problem on the same workspace then finds zeros where it needs zeros
 // and, where it reads tags, only zeros or tags of earlier launches.
 constexpr int kReadyStride = 32;     // one 128-byte line per unit: each is polled on its own
-constexpr size_t kQueueOffset = 128;  // 4 uint32: items, exits, launch counter, spare
+constexpr size_t kQueueOffset = 128;  // 4 uint32: spare, exits, launch counter, spare
 constexpr size_t kStealOffset = 64;   // 1 uint32, off the queue words' line
 struct WorkspaceLayout {
     size_t sel_counters, att_counters, scores, partials, ready, queue, total;

@@ -4,30 +4,32 @@
 // top-k blocks, attention over the kept blocks.)
 //
 // Phase 1, scoring.  The launch's centroid rows, ordered by sequence, KV head
-// and block, are cut into one equal, contiguous share per workgroup, so every
-// workgroup streams the same number of bytes and all shares end together.  A
-// share is a few segments (a run of one unit's blocks, a unit usually spanning
-// two or three workgroups), each scored in runs of up to kRun blocks; the
-// run that holds a touched page first recomputes its centroid (S1).  A segment
-// then adds its block count to the unit's counter, and the segment that
+// and block (each unit charged kSegmentCost extra rows for its fixed costs), are
+// cut as follows: the first 7/8 into one equal, contiguous share per
+// workgroup, the rest into chunks that the workgroups finishing first take
+// from a counter, so that the scan ends at about the same time everywhere.  A
+// share or chunk is a few segments (a run of one unit's blocks, a unit usually
+// spanning two or three workgroups), each scored in runs of up to kRun blocks;
+// the run that holds a touched page first recomputes its centroid (S1).  A
+// segment then adds its block count to the unit's counter, and the segment that
 // completes the unit marks it ready with the launch's tag.
 //
-// Phase 2, selection and attention.  Items (unit, split) come from a queue
-// counter.  An item waits (bounded spin, never expected to be long) until its
-// unit is ready, selects the unit's top-k blocks from the stored scores (S3),
-// keeps its split's share of the selection in LDS and attends (S4).  Each split
-// of a unit selects for itself (identical results), split 0 also writes the
-// indices.  Scoring never waits and a workgroup scores its whole share before
-// it takes an item, so every wait ends.
+// Phase 2, selection and attention.  Item (unit, split) i is taken by
+// workgroup i mod G.  It waits (bounded spin, never expected to be long) until
+// its unit is ready, selects the unit's top-k blocks from the stored scores
+// (S3), keeps its split's share of the selection in LDS and attends (S4).  Each
+// split of a unit selects for itself (identical results), split 0 also writes
+// the indices.  Scoring never waits and a workgroup ends its scoring (share and
+// chunks, until none is left) before it takes an item, so every wait ends.
 //
-// Handing out scoring work dynamically in fixed chunks was measured slower: the
-// last chunks to be handed out run at a fair share of the bandwidth next to
-// the attention of earlier units and set the end of the launch.
+// Handing out all scoring work in dynamic chunks was measured slower: the last
+// chunks to be handed out run at a fair share of the bandwidth next to the
+// attention of earlier units and set the end of the launch.
 //
 // The launch tag is one more than a launch counter kept in the queue words; the
 // last workgroup to leave advances the counter (skipping the value whose
 // successor would be 0, so that a tag is never 0 and two launches in a row never
-// share one) and re-arms the queue.
+// share one) and re-arms the chunk counter and the queue words.
 #include "attend_dev.h"
 #include "select_dev.h"
 
@@ -41,7 +43,7 @@ struct StepArgs {
     sel::SelectArgs s;
     att::AttendArgs t;
     uint32_t *ready;  // [units * kReadyStride]: word u * kReadyStride is unit u's ready tag
-    uint32_t *queue;  // [0] items taken, [1] workgroups that have left, [2] launch counter
+    uint32_t *queue;  // [0] spare, [1] workgroups that have left, [2] launch counter
     uint32_t *steal;  // scan chunks taken (a line of its own)
     int B, units, nsplit;
 };
@@ -145,10 +147,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
     // ---- phase 2: (unit, split) items
     const int total = a.units * a.nsplit;
     int32_t *list = reinterpret_cast<int32_t *>(sc_lds);  // the split's share, <= 256 entries
-    for (;;) {
-        if (tid == 0) item_s = (int)atomicAdd(&a.queue[0], 1u);
-        __syncthreads();
-        const int item = item_s;
+    // item i goes to workgroup i mod G: with fewer items than resident
+    // workgroups the first G/2 take one each, one per CU (workgroups are
+    // placed on CUs in index order), so no CU runs two attentions at once
+    for (int item = (int)blockIdx.x;; item += (int)gridDim.x) {
+        __syncthreads();  // LDS is reused
         if (item >= total) break;
         const int unit = item / a.nsplit, split = item % a.nsplit;
         const int bu = unit / Hkv;
@@ -204,7 +207,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
     if (tid == 0) {
         const uint32_t prev = atomicAdd(&a.queue[1], 1u);
         if (prev == gridDim.x - 1) {
-            __hip_atomic_store(&a.queue[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(&a.queue[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(a.steal, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(&a.queue[2], tag == 0xffffffffu ? 0u : tag, __ATOMIC_RELAXED,
