@@ -59,7 +59,8 @@ WorkspaceLayout workspace_layout(const Dims &d, int top_k) {
     const size_t row = (size_t)d.group() * d.D + 2 * (size_t)d.group();
     WorkspaceLayout w;
     w.queue = kQueueOffset;
-    w.sel_counters = 256;
+    w.pflags = 256;
+    w.sel_counters = w.pflags + align256((size_t)kMaxPrefixGroups * d.Hkv * 2 * sizeof(uint32_t));
     w.att_counters = w.sel_counters + align256(units * sizeof(uint32_t));
     w.ready = w.att_counters + align256(units * sizeof(uint32_t));
     w.scores = w.ready + align256(units * (size_t)kReadyStride * sizeof(uint32_t));
@@ -169,7 +170,8 @@ btk_status_t btk_select_shared(const btk_problem_t *problem, const void *q,
         if (prefix_blocks[g] < 0 || prefix_blocks[g] > d.max_blocks) return BTK_ERR_SHAPE;
         pg.start[g] = a0;
         pg.blocks[g] = prefix_blocks[g];
-        pg.item0[g + 1] = pg.item0[g] + d.Hkv * ((prefix_blocks[g] + plan.chunk - 1) / plan.chunk);
+        pg.item0[g + 1] = pg.item0[g] + d.Hkv * ((prefix_blocks[g] + btk::kSharedChunk - 1) /
+                                                 btk::kSharedChunk);
     }
     pg.start[num_groups] = group_start[num_groups];
     const btk::WorkspaceLayout w = btk::workspace_layout(d, top_k);
@@ -178,7 +180,8 @@ btk_status_t btk_select_shared(const btk_problem_t *problem, const void *q,
     float *sc = scores ? scores : reinterpret_cast<float *>(ws + w.scores);
     return hip_status(btk::launch_select_shared(
         d, plan, pg, q, centroids, block_table, seq_lens, top_k, indices, sc,
-        reinterpret_cast<uint32_t *>(ws + w.sel_counters), reinterpret_cast<uint32_t *>(ws),
+        reinterpret_cast<uint32_t *>(ws + w.sel_counters),
+        reinterpret_cast<uint32_t *>(ws + w.pflags), reinterpret_cast<uint32_t *>(ws),
         (hipStream_t)stream));
 }
 

@@ -15,6 +15,10 @@ constexpr int kMaxBlocksPerSeq = 8192;  // select holds one key per block in LDS
 constexpr int kMaxGroup = 16;       // query heads per KV head: MFMA tile rows
 constexpr int kMaxStepBatch = 1024; // decode step: per-sequence item prefix kept in LDS
 constexpr int kMaxTopTokens = kMaxBlocksPerSeq * kPage;  // token-level baseline budget
+// Shared-prefix selection: prefix blocks per shared item.  Each of its rows is
+// scored against every member's mean query, so items are kept short to spread
+// that arithmetic over many workgroups (each row is still read once).
+constexpr int kSharedChunk = 32;
 
 // error bits in workspace word 0
 constexpr uint32_t kErrSeqLen = 1u;
@@ -135,6 +139,7 @@ AttendPlan plan_attend(const Dims &d, int list_len_max, bool dense);
 // Workspace layout (bytes, each region 256-aligned):
 //   [0, 256)                   error word; decode-step chunk counter at byte kStealOffset
 //                              and queue words at byte kQueueOffset
+//   shared-prefix flags        kMaxPrefixGroups*Hkv*2 uint32   zero after every call
 //   select counters            B*Hkv uint32      zero after every call
 //   attend counters            B*Hkv uint32      zero after every call
 //   ready words                B*Hkv*kReadyStride uint32 (decode step: launch tags)
@@ -148,7 +153,7 @@ constexpr int kReadyStride = 32;     // one 128-byte line per unit: each is poll
 constexpr size_t kQueueOffset = 128;  // 4 uint32: spare, exits, launch counter, spare
 constexpr size_t kStealOffset = 64;   // 1 uint32, off the queue words' line
 struct WorkspaceLayout {
-    size_t sel_counters, att_counters, scores, partials, ready, queue, total;
+    size_t pflags, sel_counters, att_counters, scores, partials, ready, queue, total;
 };
 WorkspaceLayout workspace_layout(const Dims &d, int top_k);
 
@@ -172,7 +177,7 @@ hipError_t launch_select_shared(const Dims &d, const SelectPlan &plan, const Pre
                                 const void *q, const float *centroids,
                                 const int32_t *block_table, const int32_t *seq_lens, int top_k,
                                 int32_t *indices, float *scores, uint32_t *counters,
-                                uint32_t *err, hipStream_t stream);
+                                uint32_t *pflags, uint32_t *err, hipStream_t stream);
 
 hipError_t launch_attend(const Dims &d, const AttendPlan &plan, int mode, const void *q,
                          const void *k_cache, const void *v_cache, const int32_t *block_table,

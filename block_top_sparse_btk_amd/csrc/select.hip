@@ -13,21 +13,23 @@ namespace {
 // the shared prefix) reads each shared centroid row once and scores it against
 // every member's mean query, with the same arithmetic as score_chunk, so the
 // scores are bit-identical to scoring every member alone; it checks that every
-// member's table slice equals the first member's.  It then counts itself in on
-// every member unit (whose total includes the group's shared chunks) and selects
-// for the members it completed, which is rare: these items are dispatched first.
+// member's table slice equals the first member's.  Once its stores are done it
+// counts itself in on the (group, KV head) flag; the members' own chunks
+// complete and select for them (see select_kernel), so the selections of a
+// group run in parallel.
 template <typename T, int D>
 __device__ __forceinline__ void shared_item(const SelectArgs &a, const PrefixGroups &pg, int item,
-                                            float *qs, int *pages, int *flags, TopkSmem &tk) {
-    constexpr int LPR = 16, VPL = D / LPR, RPI = kWave / LPR, KU = 4;
+                                            float *qs, int *pages, int *flags) {
+    constexpr int LPR = 16, VPL = D / LPR, RPI = kWave / LPR;
+    constexpr int KU = kSharedChunk / (kWaves * RPI);  // one stage covers an item
     constexpr int ROWS = kWaves * RPI * KU;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     int g = 0;
     while (g + 1 < pg.n && pg.item0[g + 1] <= item) ++g;
     const int P = pg.blocks[g], first = pg.start[g], M = pg.start[g + 1] - first;
-    const int ncs = (P + a.chunk - 1) / a.chunk;
+    const int ncs = (P + kSharedChunk - 1) / kSharedChunk;
     const int rel = item - pg.item0[g], gk = rel / ncs, c = rel % ncs;
-    const int j0 = c * a.chunk, n = min(P, j0 + a.chunk) - j0;
+    const int j0 = c * kSharedChunk, n = min(P, j0 + kSharedChunk) - j0;
     const int r = a.Hq / a.Hkv;
 
     // set-up in one round trip: the first member's page ids, every member's
@@ -41,15 +43,31 @@ __device__ __forceinline__ void shared_item(const SelectArgs &a, const PrefixGro
         }
         pages[i] = p;
     }
-    for (int idx = tid; idx < M * D; idx += kThreads) {
-        const int m = idx / D, dd = idx % D;
-        const T *qp = static_cast<const T *>(a.q) + ((size_t)(first + m) * a.Hq + (size_t)gk * r) * D + dd;
-        float x[kMaxGroup];
+    // the (member, dim) pairs of this thread, QB at a time; the loads are
+    // unconditional (clamped to valid addresses, values masked after) so that
+    // they are all in flight together rather than one branch at a time; heads
+    // are summed in order, as score_chunk does
+    constexpr int QB = 4, HB = 8;
+    for (int i0 = tid; i0 < M * D; i0 += QB * kThreads) {
+        float s[QB] = {};
+        for (int h0 = 0; h0 < r; h0 += HB) {
+            float x[QB][HB];
 #pragma unroll
-        for (int h = 0; h < kMaxGroup; ++h) x[h] = h < r ? load_q<T>(qp + h * D) : 0.f;
-        float s = 0.f;
-        for (int h = 0; h < r; ++h) s += x[h];
-        qs[idx] = s * (a.scale / (float)r);
+            for (int u = 0; u < QB; ++u) {
+                const int idx = min(i0 + u * kThreads, M * D - 1);
+                const int m = idx / D, dd = idx % D;
+                const T *qp = static_cast<const T *>(a.q) +
+                              ((size_t)(first + m) * a.Hq + (size_t)gk * r) * D + dd;
+#pragma unroll
+                for (int h = 0; h < HB; ++h) x[u][h] = load_q<T>(qp + min(h0 + h, r - 1) * D);
+            }
+#pragma unroll
+            for (int u = 0; u < QB; ++u)
+                for (int h = 0; h < HB && h0 + h < r; ++h) s[u] += x[u][h];
+        }
+#pragma unroll
+        for (int u = 0; u < QB; ++u)
+            if (i0 + u * kThreads < M * D) qs[i0 + u * kThreads] = s[u] * (a.scale / (float)r);
     }
     __syncthreads();
     {  // every member's slice against the first member's (loads in flight together)
@@ -111,70 +129,24 @@ __device__ __forceinline__ void shared_item(const SelectArgs &a, const PrefixGro
         }
     }
 
-    // count in on every member unit (scores stored first)
+    // count in on the (group, KV head) flag once the scores are stored
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (tid == 0 && flags[kMaxGroupMembers]) flag_error(a.err, kErrPrefix);
-    int nb = 0;
-    if (tid < M) {
-        const int L = a.seq_lens[first + tid];
-        if (L >= 1 && L <= a.max_blocks * kPage) {
-            nb = (L + kPage - 1) / kPage;
-            const uint32_t total = (uint32_t)(ncs + max(1, (nb - P + a.chunk - 1) / a.chunk));
-            const int unit = (first + tid) * a.Hkv + gk;
-            const uint32_t prev = __hip_atomic_fetch_add(&a.counters[unit], 1u, __ATOMIC_RELAXED,
-                                                         __HIP_MEMORY_SCOPE_AGENT);
-            if (prev == total - 1) {
-                __hip_atomic_store(&a.counters[unit], 0u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-                flags[tid] = nb;
-            }
-        }
+    if (tid == 0) {
+        if (flags[kMaxGroupMembers]) flag_error(a.err, kErrPrefix);
+        __hip_atomic_fetch_add(&a.pflags[((size_t)g * a.Hkv + gk) * 2], 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     }
-    __syncthreads();
-    // the members this item completed: up to 2048 blocks one wave each (four at
-    // a time, each wave with its own LDS), longer ones with the whole workgroup
-    __builtin_amdgcn_s_setprio(3);
-    for (int m = wave; m < M; m += kWaves) {
-        const int nbm = flags[m];
-        if (nbm == 0 || nbm > 32 * kWave) continue;
-        const int unit = (first + m) * a.Hkv + gk;
-        TopkSmem w{tk.hist + wave * (256 + kWave), tk.cand + wave * 4 * kWave,
-                   tk.red, tk.scan_red, tk.keys};
-        const PlainScores src{a.scores + (size_t)unit * a.max_blocks};
-        const TopkOut out{a.indices + (size_t)unit * a.top_k};
-        if (min(a.top_k, nbm) == nbm) {
-            for (int i = lane; i < a.top_k; i += kWave) out.put(i, i < nbm ? i : -1);
-        } else if (nbm <= 8 * kWave) {
-            select_topk_wave<8>(src, nbm, a.top_k, out, w);
-        } else if (nbm <= 16 * kWave) {
-            select_topk_wave<16>(src, nbm, a.top_k, out, w);
-        } else {
-            select_topk_wave<32>(src, nbm, a.top_k, out, w);
-        }
-    }
-    for (int m = 0; m < M; ++m) {
-        const int nbm = flags[m];
-        if (nbm <= 32 * kWave) continue;
-        const int unit = (first + m) * a.Hkv + gk;
-        __syncthreads();
-        select_topk(PlainScores{a.scores + (size_t)unit * a.max_blocks}, nbm, a.top_k,
-                    TopkOut{a.indices + (size_t)unit * a.top_k}, tk);
-    }
-    __builtin_amdgcn_s_setprio(0);
 }
 
 template <typename T, int D, bool SHARED>
-__global__ __launch_bounds__(kThreads, 5) void select_kernel(SelectArgs a, PrefixGroups pg) {
+__global__ __launch_bounds__(kThreads, SHARED ? 4 : 5) void select_kernel(SelectArgs a, PrefixGroups pg) {
     __shared__ float qraw[(SHARED ? kMaxGroupMembers : kMaxGroup) * D];
     __shared__ float qs[D];
     __shared__ int pages[kMaxChunk];
     __shared__ float sc_lds[kMaxChunk];
     __shared__ int is_last;
-    // one set per wave in the shared-prefix form (its items may select for
-    // several members at once)
-    constexpr int kSets = SHARED ? kWaves : 1;
-    __shared__ uint32_t hist[kSets * (256 + kWave)], cand[kSets * 4 * kWave];
+    __shared__ uint32_t hist[256 + kWave], cand[4 * kWave];
     __shared__ uint32_t red[2 * kWaves];
     __shared__ int scan_red[kWaves];
     __shared__ int flags[SHARED ? kMaxGroupMembers + 1 : 1];
@@ -182,12 +154,13 @@ __global__ __launch_bounds__(kThreads, 5) void select_kernel(SelectArgs a, Prefi
     ScoreSmem sm{qraw, qs, pages, sc_lds, &is_last};
     TopkSmem tk{hist, cand, red, scan_red, keys};
     int item = blockIdx.x;
-    int skip = 0, extra = 0;  // a shared prefix, scored by shared items
+    int skip = 0;  // a shared prefix, scored by shared items
+    int grp = -1;  // the group of this item's sequence
     if (SHARED) {
-        if (item < pg.item0[pg.n]) {  // the shared items come first
+        if (item < pg.item0[pg.n]) {  // the shared items come first and never wait
             if (threadIdx.x <= kMaxGroupMembers) flags[threadIdx.x] = 0;
             __syncthreads();
-            shared_item<T, D>(a, pg, item, qraw, pages, flags, tk);
+            shared_item<T, D>(a, pg, item, qraw, pages, flags);
             return;
         }
         item -= pg.item0[pg.n];
@@ -195,16 +168,49 @@ __global__ __launch_bounds__(kThreads, 5) void select_kernel(SelectArgs a, Prefi
         for (int g = 0; g < pg.n; ++g)
             if (pg.start[g] <= b && b < pg.start[g + 1]) {
                 skip = pg.blocks[g];
-                extra = (skip + a.chunk - 1) / a.chunk;
+                grp = g;
             }
     }
     const int unit = item / a.nchunk_max, c = item % a.nchunk_max;
     int nb = 0;
-    if (!score_chunk<T, D, 4>(a, unit, c, sm, nullptr, nb, skip, extra)) return;
-    // the selecting wave(s) take issue priority over scanning waves on the SIMD
-    __builtin_amdgcn_s_setprio(3);
-    select_topk(PlainScores{a.scores + (size_t)unit * a.max_blocks}, nb, a.top_k,
-                TopkOut{a.indices + (size_t)unit * a.top_k}, tk);
+    const bool completes = score_chunk<T, D, 4>(a, unit, c, sm, nullptr, nb, skip, 0);
+    // a group member that completed (or, with an invalid length, its only item)
+    // waits until the group's shared items of its KV head are done, and counts
+    // out afterwards; the last member to count out clears the flag
+    const bool member = SHARED && grp >= 0 && (completes || (nb < 0 && c == 0));
+    uint32_t *pf = member ? a.pflags + ((size_t)grp * a.Hkv + unit % a.Hkv) * 2 : nullptr;
+    if (member) {
+        const uint32_t shared_items =
+            (uint32_t)((pg.item0[grp + 1] - pg.item0[grp]) / a.Hkv);
+        if (threadIdx.x == 0) {
+            for (uint32_t spins = 0;
+                 __hip_atomic_load(pf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < shared_items;
+                 ++spins) {
+                if (spins > (1u << 22)) {  // never expected: report, do not hang
+                    flag_error(a.err, kErrTimeout);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
+        __syncthreads();
+    }
+    if (completes) {
+        // the selecting wave(s) take issue priority over scanning waves on the SIMD
+        __builtin_amdgcn_s_setprio(3);
+        select_topk(PlainScores{a.scores + (size_t)unit * a.max_blocks}, nb, a.top_k,
+                    TopkOut{a.indices + (size_t)unit * a.top_k}, tk);
+        __builtin_amdgcn_s_setprio(0);
+    }
+    if (member && threadIdx.x == 0) {
+        const uint32_t members = (uint32_t)(pg.start[grp + 1] - pg.start[grp]);
+        const uint32_t prev =
+            __hip_atomic_fetch_add(pf + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (prev + 1 == members) {
+            __hip_atomic_store(pf, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(pf + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 }
 
 template <typename T, int D>
@@ -256,10 +262,10 @@ hipError_t launch_select_shared(const Dims &d, const SelectPlan &plan, const Pre
                                 const void *q, const float *centroids,
                                 const int32_t *block_table, const int32_t *seq_lens, int top_k,
                                 int32_t *indices, float *scores, uint32_t *counters,
-                                uint32_t *err, hipStream_t stream) {
+                                uint32_t *pflags, uint32_t *err, hipStream_t stream) {
     SelectArgs a{q, centroids, block_table, seq_lens, indices, scores, counters, err,
                  d.Hq, d.Hkv, d.num_pages, d.max_blocks, top_k, plan.chunk, plan.nchunk_max,
-                 d.sm_scale, nullptr, nullptr, nullptr};
+                 d.sm_scale, nullptr, nullptr, nullptr, pflags};
     if (d.dtype == 0)
         return d.D == 128 ? launch<uint16_t, 128>(d, plan, a, &pg, stream)
                           : launch<uint16_t, 64>(d, plan, a, &pg, stream);

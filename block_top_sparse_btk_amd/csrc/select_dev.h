@@ -44,6 +44,9 @@ struct SelectArgs {
     const void *k_cache;
     const int32_t *first_pos;
     float *cent_out;
+    // shared-prefix form only (NULL otherwise): per (group, KV head) the shared
+    // items done and the members that have finished with them
+    uint32_t *pflags = nullptr;
 };
 
 // LDS used by one chunk's scan.
@@ -86,10 +89,10 @@ struct PlainScores {
     template <int N>
     __device__ __forceinline__ void fill(uint32_t (&bits)[N], int first, int stride, int nb) const {
 #pragma unroll
-        for (int i = 0; i < N; ++i) {
-            const int j = i * stride + first;
-            bits[i] = j < nb ? __float_as_uint(load_relaxed(sc + j)) : 0u;
-        }
+        for (int i = 0; i < N; ++i)  // unconditional (clamped): all in flight together
+            bits[i] = __float_as_uint(load_relaxed(sc + min(i * stride + first, nb - 1)));
+#pragma unroll
+        for (int i = 0; i < N; ++i) bits[i] = i * stride + first < nb ? bits[i] : 0u;
     }
 };
 
@@ -628,6 +631,37 @@ __device__ __forceinline__ float row_partial(const float (&qf)[VPL], const float
     return s;
 }
 
+// The setup loads of a chunk or segment in one round trip: the group's r
+// queries into sm.qraw and n (<= PMAX) page ids of sequence b's block-table row
+// from block j0 into sm.pages.  Every load is unconditional (addresses clamped
+// into range, surplus results dropped), because a conditional load compiles to
+// a branch that waits for it before the next one is issued.
+template <typename T, int D, int PMAX>
+__device__ __forceinline__ void load_setup(const SelectArgs &a, int b, int g, int j0, int n,
+                                           ScoreSmem &sm) {
+    constexpr int QN = (kMaxGroup * D + kThreads - 1) / kThreads;
+    constexpr int PN = (PMAX + kThreads - 1) / kThreads;
+    const int tid = threadIdx.x, r = a.Hq / a.Hkv;
+    const T *qp = static_cast<const T *>(a.q) + ((size_t)b * a.Hq + (size_t)g * r) * D;
+    const int32_t *row = a.bt + (size_t)b * a.max_blocks + j0;
+    float qv[QN];
+    int32_t pv[PN];
+#pragma unroll
+    for (int k = 0; k < QN; ++k) qv[k] = load_q<T>(qp + min(k * kThreads + tid, r * D - 1));
+    if (n > 0) {
+#pragma unroll
+        for (int k = 0; k < PN; ++k) pv[k] = row[min(k * kThreads + tid, n - 1)];
+    }
+#pragma unroll
+    for (int k = 0; k < QN; ++k)
+        if (k * kThreads + tid < r * D) sm.qraw[k * kThreads + tid] = qv[k];
+    if (n > 0) {
+#pragma unroll
+        for (int k = 0; k < PN; ++k)
+            if (k * kThreads + tid < n) sm.pages[k * kThreads + tid] = pv[k];
+    }
+}
+
 // Scores n consecutive blocks j0 .. j0+n-1 of unit (b, g) whose page ids are in
 // sm.pages[0 .. n) (invalid ones as -1) against the scaled mean query in
 // sm.qs, stages the scores in sm.sc and stores them to a.scores.  REFRESH
@@ -764,10 +798,9 @@ __device__ __forceinline__ bool score_chunk(const SelectArgs &a, int unit, int c
     // setup in one round trip: the group's queries, the chunk's slice of the
     // block-table row (entries past the sequence are read but never used), the
     // length and the decode position
-    const T *qp = static_cast<const T *>(a.q) + ((size_t)b * a.Hq + (size_t)g * r) * D;
-    for (int i = tid; i < r * D; i += kThreads) sm.qraw[i] = load_q<T>(qp + i);
-    const int jn = min(a.chunk, a.max_blocks - j0);
-    for (int i = tid; i < jn; i += kThreads) sm.pages[i] = a.bt[(size_t)b * a.max_blocks + j0 + i];
+    // (length and decode position requested after the rest, so that waiting
+    // for them, as scalar values, waits for everything at once)
+    load_setup<T, D, kMaxChunk>(a, b, g, j0, min(a.chunk, a.max_blocks - j0), sm);
     const int L = a.seq_lens[b];
     const int fp = a.first_pos ? a.first_pos[b] : -1;
     __syncthreads();
@@ -792,16 +825,17 @@ __device__ __forceinline__ bool score_chunk(const SelectArgs &a, int unit, int c
     return arrive_last(&a.counters[unit], (uint32_t)(nchunks + extra), sm.flag);
 }
 
-// Decode step: scores blocks [j0, j1) of unit (b, g) of a sequence with nb
-// blocks (nb < 0: invalid length, one placeholder row that writes -1 indices
-// and flags the error), in runs of up to RUN blocks (sm.pages and sm.sc hold
+// Decode step: scores blocks [j0, j1) of unit (b, g) of a sequence of length
+// L with nb blocks (nb < 0: invalid length, one placeholder row that writes -1
+// indices and flags the error) and decode position fp, in runs of up to RUN
+// blocks (sm.pages and sm.sc hold
 // RUN entries; a run costs one round trip for its page ids), then counts the
 // blocks in on the unit's counter.  The segment that completes the unit resets
 // the counter and sets the unit's ready word to `tag`, after every segment's
 // score stores have completed (each waits for its own before counting in).
 template <typename T, int D, int KU, int RUN>
 __device__ __forceinline__ void score_segment(const SelectArgs &a, int b, int g, int j0, int j1,
-                                              int nb, ScoreSmem &sm, float *crow,
+                                              int nb, int L, int fp, ScoreSmem &sm, float *crow,
                                               uint32_t *ready, uint32_t tag) {
     const int tid = threadIdx.x;
     const int unit = b * a.Hkv + g;
@@ -817,13 +851,9 @@ __device__ __forceinline__ void score_segment(const SelectArgs &a, int b, int g,
     }
     // setup in one round trip: the group's queries, the first run's slice of
     // the block-table row, the length and the decode position
-    const T *qp = static_cast<const T *>(a.q) + ((size_t)b * a.Hq + (size_t)g * r) * D;
-    for (int i = tid; i < r * D; i += kThreads) sm.qraw[i] = load_q<T>(qp + i);
-    const int32_t *row = a.bt + (size_t)b * a.max_blocks;
     int n = min(RUN, j1 - j0);
-    for (int i = tid; i < n; i += kThreads) sm.pages[i] = row[j0 + i];
-    const int L = a.seq_lens[b];
-    const int fp = a.first_pos ? a.first_pos[b] : -1;
+    load_setup<T, D, RUN>(a, b, g, j0, n, sm);
+    const int32_t *row = a.bt + (size_t)b * a.max_blocks;
     __syncthreads();
     mean_query<D>(a, sm);
     for (int s0 = j0;;) {
@@ -834,7 +864,15 @@ __device__ __forceinline__ void score_segment(const SelectArgs &a, int b, int g,
         if (s0 >= j1) break;
         n = min(RUN, j1 - s0);
         __syncthreads();  // sm.pages and sm.sc are free again
-        for (int i = tid; i < n; i += kThreads) sm.pages[i] = row[s0 + i];
+        {  // the run's page ids, all loads in flight together
+            constexpr int PN = RUN / kThreads;
+            int32_t pv[PN];
+#pragma unroll
+            for (int k = 0; k < PN; ++k) pv[k] = row[s0 + min(k * kThreads + tid, n - 1)];
+#pragma unroll
+            for (int k = 0; k < PN; ++k)
+                if (k * kThreads + tid < n) sm.pages[k * kThreads + tid] = pv[k];
+        }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();

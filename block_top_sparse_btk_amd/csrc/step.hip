@@ -77,6 +77,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
     __shared__ float crow[kWaves * D];
     __shared__ uint32_t rows[kMaxStepBatch + 1];  // centroid rows before each sequence
     __shared__ int lens[kMaxStepBatch];           // sequence lengths, -1: invalid
+    __shared__ int fps[kMaxStepBatch];            // decode positions (first touched token)
     __shared__ int item_s;
     __shared__ uint32_t tag_s;
     // queries while scoring, top-k keys of long contexts, attention merges
@@ -99,6 +100,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
             const bool ok = L >= 1 && L <= a.s.max_blocks * kPage;
             const int nb = ok ? (L + kPage - 1) / kPage : -1;
             lens[b] = ok ? L : -1;
+            fps[b] = a.s.first_pos ? a.s.first_pos[b] : -1;
             n = (uint32_t)Hkv * (uint32_t)(kSegmentCost + (ok ? nb : 1));
         }
         const uint32_t carry = b0 == 0 ? 0u : rows[b0];
@@ -137,7 +139,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
         const int j1 = (int)(e > kSegmentCost ? e - kSegmentCost : 0u);
         if (j1 > j0) {
             sel::score_segment<T, D, kScanRows, kRun>(
-                a.s, b, (int)g, j0, j1, nb, sm, crow,
+                a.s, b, (int)g, j0, j1, nb, lens[b], fps[b], sm, crow,
                 a.ready + ((size_t)b * Hkv + g) * kReadyStride, tag);
             __syncthreads();  // LDS is reused by the next segment
         }
@@ -165,10 +167,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
         if (row_lds) {
             const int32_t *bt_row = a.s.bt + (size_t)bu * a.s.max_blocks;
 #pragma unroll
-            for (int i = 0; i < kRowPer; ++i) {
-                const int j = i * kThreads + tid;
-                prow[i] = j < nb ? bt_row[j] : -1;
-            }
+            for (int i = 0; i < kRowPer; ++i)  // unconditional: all in flight together
+                prow[i] = bt_row[min(i * kThreads + tid, nb - 1)];
         }
         if (tid == 0) {
             const uint32_t *rw = a.ready + (size_t)unit * kReadyStride;
