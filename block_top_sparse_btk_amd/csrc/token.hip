@@ -91,11 +91,21 @@ __device__ __forceinline__ void score_tokens(const TokArgs &a, int unit, int c, 
     const size_t max_tok = (size_t)a.max_blocks * kPage;
 
     // set-up in one round trip: queries, the chunk's slice of the block table,
-    // the length
+    // the length.  The loads are unconditional (clamped addresses, surplus
+    // results dropped): a conditional load compiles to a branch that waits for
+    // it before the next is issued
     const T *qp = static_cast<const T *>(a.q) + ((size_t)b * a.Hq + (size_t)g * r) * D;
-    for (int i = tid; i < r * D; i += kThreads) qraw[i] = to_f32<T>(qp[i]);
+    constexpr int QN = (kMaxGroup * D + kThreads - 1) / kThreads;
+    float qv[QN];
+#pragma unroll
+    for (int k = 0; k < QN; ++k) qv[k] = to_f32<T>(qp[min(k * kThreads + tid, r * D - 1)]);
     const int jn = min(kChunkPages, a.max_blocks - j0);
-    for (int i = tid; i < jn; i += kThreads) pages[i] = a.bt[(size_t)b * a.max_blocks + j0 + i];
+    static_assert(kChunkPages <= kThreads, "one page id per thread");
+    const int pv = jn > 0 ? a.bt[(size_t)b * a.max_blocks + j0 + min(tid, jn - 1)] : -1;
+#pragma unroll
+    for (int k = 0; k < QN; ++k)
+        if (k * kThreads + tid < r * D) qraw[k * kThreads + tid] = qv[k];
+    if (tid < jn) pages[tid] = pv;
     const int L = a.seq_lens[b];
     __syncthreads();
     if (L < 1 || L > a.max_blocks * kPage) {
