@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kThreads, SHARED ? 4 : 5) void select_kernel(Select
     __shared__ int pages[kMaxChunk];
     __shared__ float sc_lds[kMaxChunk];
     __shared__ int is_last;
-    __shared__ uint32_t hist[256 + kWave], cand[4 * kWave];
+    __shared__ uint32_t hist[sel::kTopkPasses * sel::kHistWords], cand[4 * kWave];
     __shared__ uint32_t red[2 * kWaves];
     __shared__ int scan_red[kWaves];
     __shared__ int flags[SHARED ? kMaxGroupMembers + 1 : 1];

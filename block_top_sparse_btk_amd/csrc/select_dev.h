@@ -59,8 +59,13 @@ struct ScoreSmem {
 };
 
 // LDS used by the top-k selection.
+// Radix histogram: 256 bins, then one spare bin per lane for keys out of range.
+constexpr int kHistWords = 256 + kWave;
+// The workgroup selection gives each of its (at most four) passes a histogram.
+constexpr int kTopkPasses = 4;
+
 struct TopkSmem {
-    uint32_t *hist;      // [256 + 64] radix bins + per-lane spare bins
+    uint32_t *hist;      // [kTopkPasses * kHistWords] radix histograms
     uint32_t *cand;      // [256] compacted candidates
     uint32_t *red;       // [2 * kWaves]
     int *scan_red;       // [kWaves]
@@ -179,24 +184,28 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
 // key of rank `need` counted from the top, and shrink [lo, hi] to it.  Keys out
 // of range are counted in a per-lane spare bin, so the loop has no branches.
 // The bin (of the 256 in hist) that holds the key of rank `need` counted from
-// the top; `need` becomes that key's rank inside the bin.  Wave-uniform.
-__device__ __forceinline__ uint32_t locate_bin(const uint32_t *hist, int &need, int lane) {
+// the top; `need` becomes that key's rank inside the bin and, if asked for,
+// *count the number of keys in the bin.  Wave-uniform.
+__device__ __forceinline__ uint32_t locate_bin(const uint32_t *hist, int &need, int lane,
+                                               uint32_t *count = nullptr) {
     const uint4 h = reinterpret_cast<const uint4 *>(hist)[lane];  // bins 4l .. 4l+3
     const uint32_t lane_sum = h.x + h.y + h.z + h.w;
     const uint32_t above_lane = wave_sum_u32(lane_sum) - wave_inclusive_scan(lane_sum);
     int bin = -1;
-    uint32_t above_bin = 0u, acc = above_lane;
+    uint32_t above_bin = 0u, in_bin = 0u, acc = above_lane;
     const uint32_t hv[4] = {h.x, h.y, h.z, h.w};
 #pragma unroll
     for (int e = 3; e >= 0; --e) {  // from this lane's top bin down
         if (bin < 0 && acc < (uint32_t)need && acc + hv[e] >= (uint32_t)need) {
             bin = 4 * lane + e;
             above_bin = acc;
+            in_bin = hv[e];
         }
         acc += hv[e];
     }
     const int src = (int)__builtin_ctzll(__ballot(bin >= 0));  // exactly one lane has it
     need -= __builtin_amdgcn_readlane((int)above_bin, src);
+    if (count) *count = (uint32_t)__builtin_amdgcn_readlane((int)in_bin, src);
     return (uint32_t)__builtin_amdgcn_readlane(bin, src);
 }
 
@@ -369,18 +378,26 @@ __device__ __forceinline__ void select_topk_wave(const Src &src, int nb, int top
 
 // Top-k of a unit's nb <= 256 * KMAX <= 2048 scores by the four waves of the
 // workgroup.  Thread t holds the keys of blocks i*256 + t.  The radix passes of
-// select_topk_wave run over the workgroup: one LDS histogram fed by every wave,
-// each wave locating the bin itself (identical results).  Once at most 256 keys
-// are in range they are compacted wave by wave and wave 0 finishes alone
-// (finish_from_cand).  Bitmaps come from per-wave ballots: slot i of wave v
-// covers blocks 256i + 64v .. +63, words 8i + 2v and 8i + 2v + 1.
+// select_topk_wave run over the workgroup, each into its own LDS histogram (all
+// of them cleared while the keys are in flight), so that a pass costs a single
+// barrier: every wave then locates the bin itself (identical results).  Each
+// pass resolves eight bits of the range, so at most four reach lo = hi = T; a
+// pass whose bin is taken whole ends the search early (T just below the bin,
+// no equal keys to take), which usually happens by the second.
+// The first range starts at a lower bound of T rather than at the smallest key:
+// for kb <= 64, the smallest of the largest keys of a wave's first kb lanes
+// (kb keys lie at or above it), the largest of these over the waves.  Bitmaps
+// come from per-wave ballots: slot i of wave v covers blocks 256i + 64v .. +63,
+// words 8i + 2v and 8i + 2v + 1.
 template <int KMAX, typename Src>
 __device__ __forceinline__ void select_topk_wg4(const Src &src, int nb, int top_k,
                                                 const TopkOut &out, TopkSmem &sm) {
     static_assert(KMAX <= 8, "64 bitmap words cover 2048 blocks");
-    uint32_t *hist = sm.hist, *cand = sm.cand, *red = sm.red;
+    uint32_t *cand = sm.cand, *red = sm.red;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int kb = min(top_k, nb);
+    for (int i = tid; i < kTopkPasses * kHistWords / 4; i += kThreads)
+        reinterpret_cast<uint4 *>(sm.hist)[i] = make_uint4(0u, 0u, 0u, 0u);
     uint32_t key[KMAX];
     src.fill(key, tid, kThreads, nb);
     uint32_t kmin = 0xffffffffu, kmax = 0u;
@@ -391,92 +408,42 @@ __device__ __forceinline__ void select_topk_wg4(const Src &src, int nb, int top_
         kmin = j < nb ? min(kmin, key[i]) : kmin;
         kmax = max(kmax, key[i]);
     }
-    kmin = ~wave_max_u32(~kmin);
+    // nb > 256: every thread holds at least one key, so kmax is a key
+    const uint32_t bound = kb <= kWave ? (lane < kb ? kmax : 0xffffffffu) : kmin;
+    const uint32_t wave_lo = ~wave_max_u32(~bound);
     kmax = wave_max_u32(kmax);
     if (lane == 0) {
-        red[wave] = ~kmin;
+        red[wave] = wave_lo;
         red[kWaves + wave] = kmax;
     }
-    __syncthreads();
-    uint32_t lo = ~max(max(red[0], red[1]), max(red[2], red[3]));
+    __syncthreads();  // also orders the histogram clears before the passes
+    uint32_t lo = kb <= kWave ? max(max(red[0], red[1]), max(red[2], red[3]))
+                              : min(min(red[0], red[1]), min(red[2], red[3]));
     uint32_t hi = max(max(red[kWaves], red[kWaves + 1]), max(red[kWaves + 2], red[kWaves + 3]));
-    int need = kb;
-    // keys of the workgroup inside [lo, hi] (one barrier; red's halves alternate)
-    int parity = 0;
-    auto count_wg = [&]() {
-        int c = 0;
-#pragma unroll
-        for (int i = 0; i < KMAX; ++i) c += __popcll(__ballot(key[i] - lo <= hi - lo));
-        __syncthreads();  // red / hist readers of the previous step are done
-        if (lane == 0) red[parity * kWaves + wave] = (uint32_t)c;
-        __syncthreads();
-        int m = 0;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) m += (int)red[parity * kWaves + w];
-        parity ^= 1;
-        return m;
-    };
-    auto pass_wg = [&]() {
+    int need = kb;  // rank of T among the keys inside [lo, hi], counted from the top
+#pragma unroll 1
+    for (int p = 0; p < kTopkPasses && lo < hi; ++p) {
+        uint32_t *hist = sm.hist + p * kHistWords;
         const uint32_t span = hi - lo;
         const int shift = max(0, 24 - __builtin_clz(span));  // (span >> shift) < 256
-        __syncthreads();  // the previous pass's readers of hist are done
-        if (wave == 0) reinterpret_cast<uint4 *>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
-        __syncthreads();
 #pragma unroll
         for (int i = 0; i < KMAX; ++i) {
             const uint32_t off = key[i] - lo;
             atomicAdd(&hist[off <= span ? (off >> shift) : 256u + lane], 1u);
         }
         __syncthreads();
-        const uint32_t b_sel = locate_bin(hist, need, lane);  // every wave, same result
+        uint32_t in_bin;
+        const uint32_t b_sel = locate_bin(hist, need, lane, &in_bin);  // every wave, same result
         const uint32_t top = (b_sel << shift) + ((1u << shift) - 1u);
         if (top < span) hi = lo + top;
         lo += b_sel << shift;
-    };
-    int m = nb;
-    if (lo < hi) pass_wg();
-    if (lo < hi) {
-        m = count_wg();
-        while (lo < hi && m > 4 * kWave) {  // rare: keys bunched in one bin
-            pass_wg();
-            m = count_wg();
+        if (in_bin == (uint32_t)need && lo < hi) {  // every key of the bin is kept
+            hi = --lo;  // lo >= 1: valid keys are nonzero
+            need = 0;
         }
     }
-    if (lo < hi) {
-        // compaction wave by wave: wave v's keys after those of waves < v
-        int c = 0;
-#pragma unroll
-        for (int i = 0; i < KMAX; ++i) c += __popcll(__ballot(key[i] - lo <= hi - lo));
-        __syncthreads();
-        if (lane == 0) red[wave] = (uint32_t)c;
-        __syncthreads();
-        int base = 0;
-        for (int w = 0; w < wave; ++w) base += (int)red[w];
-#pragma unroll
-        for (int i = 0; i < KMAX; ++i) {
-            const bool in = key[i] - lo <= hi - lo;
-            const uint64_t mask = __ballot(in);
-            const int pos = base + (int)__builtin_amdgcn_mbcnt_hi(
-                                       (uint32_t)(mask >> 32),
-                                       __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-            if (in) cand[pos] = key[i];
-            base += __popcll(mask);
-        }
-        __syncthreads();
-        if (wave == 0) {
-            finish_from_cand(cand, m, lo, hi, need, hist, lane);
-            if (lane == 0) {
-                red[0] = lo;
-                red[1] = (uint32_t)need;
-            }
-        }
-        __syncthreads();
-        lo = red[0];
-        need = (int)red[1];
-        __syncthreads();  // red is reused below
-    }
-    const uint32_t T = lo;
-    // bitmaps through LDS (cand is free again): above in cand[0..64), equal in cand[64..128)
+    const uint32_t T = lo;  // need: the keys equal to T to keep
+    // bitmaps through LDS: above in cand[0..64), equal in cand[64..128)
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) {
         const uint64_t ab = __ballot(key[i] > T);

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
     __shared__ int pages[kRun];
     __shared__ float sc_lds[kRun];
     __shared__ int flag;
-    __shared__ uint32_t hist[256 + kWave], cand[4 * kWave];
+    __shared__ uint32_t hist[sel::kTopkPasses * sel::kHistWords], cand[4 * kWave];
     __shared__ uint32_t red[2 * kWaves];
     __shared__ int scan_red[kWaves];
     __shared__ float crow[kWaves * D];
