@@ -180,6 +180,48 @@ def make_batch(*, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int
     return batch_obj
 
 
+def make_tie_batch(*, seq_lens: Sequence[int], num_q_heads: int = 8, num_kv_heads: int = 2,
+                   head_dim: int = 128, top_k: int = 32, seed: int = 0,
+                   name: str = "ties") -> Batch:
+    """A batch whose block scores tie exactly, in runs.
+
+    Every token of a (page, KV head) tile holds one of four class vectors
+    alpha_c * u_h (alpha = 2, 1, 1/2, -1, exact in bf16; u_h a bf16 direction per
+    KV head) and every query head of group h is u_h, so a block's centroid is
+    its class vector exactly and blocks of one class score exactly alike, with
+    the classes far apart.  Per (sequence, KV head) a random number in
+    [0, 2 * top_k] of blocks takes the top class and about half of the rest the
+    second, so the k-th largest score is usually shared by many blocks, and
+    sometimes the top class is kept whole.  Tables, lengths and values as in
+    make_batch (shuffled pages).
+    """
+    bt = make_batch(batch=len(seq_lens), num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                    head_dim=head_dim, seq_lens=seq_lens, top_k=top_k, seed=seed, name=name)
+    g = torch.Generator().manual_seed(int(seed) + 7919)
+    hkv, D, P = num_kv_heads, head_dim, bt.page_size
+    u = torch.randn((hkv, D), generator=g).to(torch.bfloat16).to(torch.float32)
+    alphas = torch.tensor([2.0, 1.0, 0.5, -1.0])
+    cls = torch.randint(2, 4, (bt.num_pages, hkv), generator=g)  # the lower classes
+    second = torch.rand((bt.num_pages, hkv), generator=g) < 0.5
+    cls[second] = 1
+    nblk = (bt.seq_lens.to(torch.int64) + P - 1) // P
+    for b in range(bt.batch):
+        nb = int(nblk[b])
+        pages = bt.block_table[b, :nb].to(torch.int64)
+        for h in range(hkv):
+            n_top = int(torch.randint(0, 2 * top_k + 1, (1,), generator=g))
+            pick = torch.randperm(nb, generator=g)[:min(n_top, nb)]
+            cls[pages[pick], h] = 0
+    vec = alphas[cls].unsqueeze(-1) * u.unsqueeze(0)  # [pages, hkv, D], exact in bf16
+    k = vec.unsqueeze(2).expand(bt.num_pages, hkv, P, D).contiguous()
+    r = num_q_heads // num_kv_heads
+    q = u.repeat_interleave(r, dim=0).unsqueeze(0).expand(bt.batch, num_q_heads, D).contiguous()
+    bt.k_cache = k.to(bt.dtype)
+    bt.q = q.to(bt.dtype)
+    bt.notes["ties"] = "four key classes"
+    return bt
+
+
 # The five decode workloads.  seed = 1000 * config + variant.
 CONFIGS = {
     1: dict(name="tiny-fp32", batch=1, num_q_heads=2, num_kv_heads=1, head_dim=64,

@@ -394,6 +394,31 @@ def test_decode_step_equals_separate_calls_and_oracle(label, spec):
     check_lse(results[0][2], ora["lse"], bt.dtype, st["equal_mask"], bt.group)
 
 
+@pytest.mark.parametrize("top_k", [32, 64, 100])
+def test_exact_score_ties_keep_the_lowest_indices(top_k):
+    """Runs of blocks score exactly alike (synth.make_tie_batch), so the k-th
+    largest score is shared by many blocks: every selection path (one wave up
+    to 256 blocks, four waves up to 2048, bisection beyond; the separate calls
+    and the single launch) must keep the lowest indices among them, exactly as
+    the oracle does."""
+    lens = [16 * 100, 16 * 257 - 3, 16 * 700, 16 * 1024, 16 * 1025 - 15, 16 * 2048, 16 * 2100 + 5]
+    bt = synth.make_tie_batch(seq_lens=lens, top_k=top_k, seed=41)
+    _say(f"[ties] k={top_k} lens={lens}")
+    ora = oracle.sparse_step(bt.q, bt.k_cache, bt.v_cache, bt.block_table, bt.seq_lens, top_k)
+    g = _gpu_step(bt, top_k=top_k, dense=False)
+    assert g["err_bits"] == 0
+    assert torch.equal(g["indices"], ora["indices"])
+    d, prob, _ = g["_dev"]
+    ws = btk.new_workspace(prob, top_k, DEV)
+    cent = g["centroids"].to(DEV)
+    out, idx = btk.btk_decode_step(d.q, d.k_cache, d.v_cache, d.block_table, d.seq_lens, cent,
+                                   top_k, ws, problem=prob)
+    torch.cuda.synchronize()
+    assert btk.workspace_error_bits(ws) == 0
+    assert torch.equal(idx.cpu(), ora["indices"])
+    assert torch.equal(out.cpu(), g["out"])
+
+
 def _step_both(q, k_cache, v_cache, bt, sl, cent, k, prob, ws_step, first=None):
     """The step as one launch (on ws_step) and as three calls (fresh workspace)."""
     c1, c2 = cent.clone(), cent.clone()
