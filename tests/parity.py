@@ -6,6 +6,12 @@ If n_b <= k or margin > MARGIN, the library's index row must equal the
 oracle's bit for bit.  Otherwise several sets are correct: every selected block
 must score at least s_(k_b) - MARGIN, and the row must still be k_b distinct
 in-range blocks in ascending order followed by -1.
+The margin's unit depends on the reading of the group score: the mean of the
+heads' scaled logits (the reading the library implements) or the plain sum of
+the heads' unscaled dot products, which is larger by r * sqrt(D).  Given
+``sum_factor`` = r * sqrt(D), exactness is also demanded wherever the margin
+exceeds MARGIN in the sum's units, i.e. on almost every unit; both counts are
+reported.
 Outputs are compared with the oracle on units whose index rows are equal; the
 attention step on its own is compared on the oracle's index rows.
 """
@@ -26,14 +32,23 @@ def n_blocks(seq_lens, page=16):
     return [(int(L) + page - 1) // page for L in seq_lens.tolist()]
 
 
-def check_indices(gpu_idx, ora_idx, ora_scores, seq_lens, top_k, margin=MARGIN, page=16):
+def sum_factor(group, head_dim):
+    """Factor from the mean of the heads' scaled logits to the sum of their
+    unscaled dot products (scale 1/sqrt(D))."""
+    return group * math.sqrt(head_dim)
+
+
+def check_indices(gpu_idx, ora_idx, ora_scores, seq_lens, top_k, margin=MARGIN, page=16,
+                  sum_units=None):
     """Assert the margin rule on every unit; returns statistics.  page=1 applies
-    the rule to token positions (the token-level baseline)."""
+    the rule to token positions (the token-level baseline).  sum_units (see
+    sum_factor) also applies the rule with the margin in the sum's units."""
     gpu_idx, ora_idx = gpu_idx.cpu(), ora_idx.cpu()
     B, H, K = ora_idx.shape
     assert K == top_k and tuple(gpu_idx.shape) == (B, H, K)
     nbs = n_blocks(seq_lens, page)
-    stats = dict(units=0, strict=0, near_tie=0, differ=0, min_strict_margin=math.inf)
+    stats = dict(units=0, strict=0, near_tie=0, differ=0, min_strict_margin=math.inf,
+                 strict_sum=0)
     equal = torch.zeros((B, H), dtype=torch.bool)
     for b in range(B):
         nb = nbs[b]
@@ -50,10 +65,14 @@ def check_indices(gpu_idx, ora_idx, ora_scores, seq_lens, top_k, margin=MARGIN, 
             if nb <= top_k:
                 assert same, (b, g)
                 stats["strict"] += 1
+                stats["strict_sum"] += 1
                 continue
             s = ora_scores[b, g, :nb].double()
             srt = torch.sort(s, descending=True).values
             m = float(srt[kb - 1] - srt[kb])
+            if sum_units is not None and m * sum_units > margin:
+                stats["strict_sum"] += 1
+                assert same, (b, g, m, "sum units", row, want)
             if m > margin:
                 stats["strict"] += 1
                 stats["min_strict_margin"] = min(stats["min_strict_margin"], m)

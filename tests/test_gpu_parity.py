@@ -17,7 +17,7 @@ import block_top_sparse_btk_amd as btk
 import oracle
 import synth
 from parity import (CENTROID_TOL, SCORE_TOL, check_indices, check_lse, check_outputs, max_abs,
-                    n_blocks)
+                    n_blocks, sum_factor)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -83,7 +83,8 @@ def full_parity(bt, top_k=None, dense=True, label=""):
         s_err = max(s_err, max_abs(g["scores"][b, :, :nb], ora["scores"][b, :, :nb]))
     assert s_err <= SCORE_TOL, s_err
     # S3 selection under the margin rule
-    st = check_indices(g["indices"], ora["indices"], ora["scores"], bt.seq_lens, top_k)
+    st = check_indices(g["indices"], ora["indices"], ora["scores"], bt.seq_lens, top_k,
+                       sum_units=sum_factor(bt.group, bt.head_dim))
     # S4 end to end on units whose selections agree
     o_err = check_outputs(g["out"], ora["out"], bt.dtype, st["equal_mask"], bt.group)
     l_err = check_lse(g["lse"], ora["lse"], bt.dtype, st["equal_mask"], bt.group)
@@ -93,7 +94,8 @@ def full_parity(bt, top_k=None, dense=True, label=""):
     a_err = check_outputs(a_out, ora["out"], bt.dtype, what="attend(oracle idx)")
     check_lse(a_lse, ora["lse"], bt.dtype)
     res = dict(centroid=c_err, score=s_err, out=o_err, lse=l_err, attend=a_err,
-               units=st["units"], near_tie=st["near_tie"], differ=st["differ"],
+               units=st["units"], strict=st["strict"], strict_sum=st["strict_sum"],
+               near_tie=st["near_tie"], differ=st["differ"],
                min_strict_margin=st["min_strict_margin"])
     if dense:
         dout, dlse, _ = oracle.attend(bt.q, bt.k_cache, bt.v_cache, bt.block_table, bt.seq_lens)
@@ -244,7 +246,8 @@ def test_workspace_reuse_across_calls_and_smaller_problem():
                                     problem=prob)
     torch.cuda.synchronize()
     ora = oracle.sparse_step(big.q, big.k_cache, big.v_cache, big.block_table, big.seq_lens, 16)
-    st = check_indices(idx.cpu(), ora["indices"], ora["scores"], big.seq_lens, 16)
+    st = check_indices(idx.cpu(), ora["indices"], ora["scores"], big.seq_lens, 16,
+                       sum_units=sum_factor(big.group, big.head_dim))
     check_outputs(out, ora["out"], torch.bfloat16, st["equal_mask"], big.group)
     # the same workspace serves a smaller problem
     s = small.to(DEV)
@@ -258,7 +261,8 @@ def test_workspace_reuse_across_calls_and_smaller_problem():
     torch.cuda.synchronize()
     ora = oracle.sparse_step(small.q, small.k_cache, small.v_cache, small.block_table,
                              small.seq_lens, 16)
-    st = check_indices(idx.cpu(), ora["indices"], ora["scores"], small.seq_lens, 16)
+    st = check_indices(idx.cpu(), ora["indices"], ora["scores"], small.seq_lens, 16,
+                       sum_units=sum_factor(small.group, small.head_dim))
     check_outputs(out, ora["out"], torch.bfloat16, st["equal_mask"], small.group)
     assert btk.workspace_error_bits(ws) == 0
 
@@ -389,7 +393,8 @@ def test_decode_step_equals_separate_calls_and_oracle(label, spec):
     # and against the oracle
     assert max_abs(results[0][3], full) <= CENTROID_TOL
     ora = oracle.sparse_step(bt.q, bt.k_cache, bt.v_cache, bt.block_table, bt.seq_lens, k)
-    st = check_indices(results[0][1], ora["indices"], ora["scores"], bt.seq_lens, k)
+    st = check_indices(results[0][1], ora["indices"], ora["scores"], bt.seq_lens, k,
+                       sum_units=sum_factor(bt.group, bt.head_dim))
     check_outputs(results[0][0], ora["out"], bt.dtype, st["equal_mask"], bt.group)
     check_lse(results[0][2], ora["lse"], bt.dtype, st["equal_mask"], bt.group)
 
