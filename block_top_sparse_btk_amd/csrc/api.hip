@@ -297,7 +297,7 @@ btk_status_t btk_decode_step(const btk_problem_t *problem, const void *q, const 
     if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !centroids || !indices || !out)
         return BTK_ERR_NULL;
     if (!top_k_ok(top_k)) return BTK_ERR_SHAPE;
-    if (d.B > btk::kMaxStepBatch) return BTK_ERR_UNSUPPORTED;
+    if (d.B > btk::kMaxStepBatch || !btk::step_rows_fit(d)) return BTK_ERR_UNSUPPORTED;
     const btk::WorkspaceLayout w = btk::workspace_layout(d, top_k);
     if (!workspace || workspace_bytes < w.total) return BTK_ERR_WORKSPACE;
     char *ws = static_cast<char *>(workspace);

@@ -204,6 +204,9 @@ struct TokenWorkspaceLayout {
 };
 TokenWorkspaceLayout token_workspace_layout(const Dims &d, int top_tokens);
 
+// Whether the decode step's row count (every unit charged a fixed number of
+// rows beyond its blocks) fits its 32-bit counters.
+bool step_rows_fit(const Dims &d);
 hipError_t launch_decode_step(const Dims &d, const SelectPlan &sp, const AttendPlan &ap,
                               const void *q, const void *k_cache, const void *v_cache,
                               const int32_t *block_table, const int32_t *seq_lens,

@@ -758,7 +758,6 @@ __device__ __forceinline__ bool score_chunk(const SelectArgs &a, int unit, int c
                                             int extra = 0) {
     const int tid = threadIdx.x;
     const int b = unit / a.Hkv, g = unit % a.Hkv;
-    const int r = a.Hq / a.Hkv;
     int32_t *out = a.indices + (size_t)unit * a.top_k;
     const int j0 = skip + c * a.chunk;
 
@@ -806,7 +805,6 @@ __device__ __forceinline__ void score_segment(const SelectArgs &a, int b, int g,
                                               uint32_t *ready, uint32_t tag) {
     const int tid = threadIdx.x;
     const int unit = b * a.Hkv + g;
-    const int r = a.Hq / a.Hkv;
     if (nb < 0) {
         int32_t *out = a.indices + (size_t)unit * a.top_k;
         for (int i = tid; i < a.top_k; i += kThreads) store_relaxed_i32(out + i, -1);

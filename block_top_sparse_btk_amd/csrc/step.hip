@@ -57,9 +57,13 @@ constexpr int kRun = 2048;       // blocks per scan run: shares (~550 blocks at 
 // Rows charged for a unit beyond its blocks when the shares are cut: a segment
 // costs round trips in which nothing streams (its setup, its closing
 // store-and-count) and the unit's touched page its refresh, so a share that
-// starts a unit gets that many fewer blocks (a second segment measured about
-// 6 us, some 140 rows of streaming, on the Qwen3-8B-shaped step).
-constexpr int kSegmentCost = 160;
+// starts a unit gets that many fewer blocks.  The charge also moves share ends
+// earlier for the workgroups that start units, which then take more of the
+// stolen chunks.  Measured on the Qwen3-8B-shaped step (three length draws) and
+// on uniform-length batches of 64 to 512 units: 160 -> 520 rows shortened the
+// ragged steps by 1.4-2.8 us and left the others equal or faster; from about
+// 700 rows on the ragged steps got slower again.
+constexpr int kSegmentCost = 520;
 // The last 1/kStealFrac of the rows is handed out in chunks of kStealRows to the
 // workgroups that finish their static share first.
 constexpr int kStealFrac = 8;
@@ -262,6 +266,11 @@ hipError_t launch(const Dims &d, const SelectPlan &sp, const AttendPlan &ap, Ste
 }
 
 }  // namespace
+
+bool step_rows_fit(const Dims &d) {
+    return (uint64_t)d.B * (uint64_t)d.Hkv * ((uint64_t)d.max_blocks + kSegmentCost) <
+           ((uint64_t)1 << 32);
+}
 
 hipError_t launch_decode_step(const Dims &d, const SelectPlan &sp, const AttendPlan &ap,
                               const void *q, const void *k_cache, const void *v_cache,

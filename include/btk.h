@@ -241,7 +241,8 @@ btk_status_t btk_token_topk_attend(const btk_problem_t *problem, const void *q,
  * (Pith review, "What carries the argument"; the single-launch form is this
  * library's own design.)
  *   centroids  in/out   indices out [B][Hkv][top_k]   out/lse out as btk_sparse_attend
- *   batch      <= 1024 (BTK_ERR_UNSUPPORTED beyond; the separate calls have no such limit)
+ *   batch      <= 1024, and batch * num_kv_heads * (max_blocks_per_seq + 520) < 2^32
+ *              (BTK_ERR_UNSUPPORTED beyond; the separate calls have no such limits)
  *   workspace  btk_workspace_bytes(problem, top_k), zero-filled once, as above. */
 btk_status_t btk_decode_step(const btk_problem_t *problem, const void *q, const void *k_cache,
                              const void *v_cache, const int32_t *block_table,

@@ -149,6 +149,14 @@ def test_local_attend_and_decode_step_validate_before_launch():
     assert lib.btk_decode_step(ctypes.byref(big), *args(wsn=1 << 40)) == btk.BTK_ERR_UNSUPPORTED
     bad = ctypes.byref(_problem(head_dim=96))
     assert lib.btk_decode_step(bad, *args()) == btk.BTK_ERR_UNSUPPORTED
+    # the step's 32-bit row counters: batch * Hkv * (max_blocks + 520) must stay below 2^32
+    rows_over = _problem(batch=1024, num_q_heads=4096, num_kv_heads=4096, max_blocks_per_seq=512)
+    assert lib.btk_decode_step(ctypes.byref(rows_over), *args(wsn=1 << 40)) == \
+        btk.BTK_ERR_UNSUPPORTED
+    rows_fit = _problem(batch=1024, num_q_heads=2048, num_kv_heads=2048, max_blocks_per_seq=512)
+    need_fit = btk.btk_workspace_bytes(rows_fit, 8)
+    assert lib.btk_decode_step(ctypes.byref(rows_fit), *args(wsn=need_fit - 1)) == \
+        btk.BTK_ERR_WORKSPACE
 
 
 def test_token_baseline_validates_before_launch():
