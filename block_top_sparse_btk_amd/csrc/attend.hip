@@ -6,13 +6,15 @@ namespace btk {
 using namespace att;
 namespace {
 
-// blocks per pipeline stage: one for the short bf16 lists (fewer registers,
-// more waves in flight), two for every block and for fp32.  The fp32 kernels
-// keep two-block stages: the one-block fp32 build of the selected-list kernel
-// gave wrong outputs on the GPU while every bf16 build with the same source was
-// exact, so that variant is not used.
+// blocks per pipeline stage: one for bf16 (fewer registers; the dense
+// comparison on the Qwen3-8B-shaped layer took 488.7 instead of 501.6 us with
+// one-block stages, while a third or fourth workgroup per CU gained nothing or
+// spilled), two for fp32.  The fp32 kernels keep two-block stages: the
+// one-block fp32 build of the selected-list kernel gave wrong outputs on the
+// GPU while every bf16 build with the same source was exact, so that variant is
+// not used.
 template <typename T, int MODE>
-constexpr int stage_blocks() { return (MODE == kAll || sizeof(T) == 4) ? 2 : 1; }
+constexpr int stage_blocks() { return sizeof(T) == 4 ? 2 : 1; }
 
 template <typename T, int D, int MODE>
 __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
