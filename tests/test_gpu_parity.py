@@ -349,7 +349,13 @@ STEP_CASES = [("config1", dict(cfg=1)), ("config2", dict(cfg=2)), ("config3", di
                                           seq_lens=[100, 999, 64], top_k=5, seed=32))),
               ("fp32-d128", dict(kw=dict(batch=2, num_q_heads=6, num_kv_heads=2, head_dim=128,
                                          seq_lens=[333, 1000], top_k=6, seed=33,
-                                         dtype=torch.float32)))]
+                                         dtype=torch.float32))),
+              # the largest batch the single launch takes: the row prefix is built
+              # over four 256-sequence chunks and 2048 units share 512 workgroups
+              ("max-batch-1024", dict(kw=dict(batch=1024, num_q_heads=8, num_kv_heads=2,
+                                              head_dim=128,
+                                              seq_lens=[1 + (i * 7919) % 700 for i in range(1024)],
+                                              top_k=8, seed=34)))]
 
 
 @pytest.mark.parametrize("label,spec", STEP_CASES, ids=[c[0] for c in STEP_CASES])
