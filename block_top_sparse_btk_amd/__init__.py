@@ -85,6 +85,9 @@ def _lib():
         lib.btk_token_topk_attend.argtypes = [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
         lib.btk_decode_step.restype = st
         lib.btk_decode_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
+        lib.btk_decode_step_append.restype = st
+        lib.btk_decode_step_append.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
+                                               vp, sz, vp]
         _LIB = lib
     return _LIB
 
@@ -381,6 +384,40 @@ def btk_decode_step(q, k_cache, v_cache, block_table, seq_lens, centroids, top_k
                                 _dev(workspace, "workspace", torch.uint8, dev), workspace.numel(),
                                 _stream(dev))
     _check(st, "btk_decode_step")
+    return out, indices
+
+
+def btk_decode_step_append(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, centroids,
+                           top_k, workspace, indices=None, out=None, lse=None, sm_scale: float = 0.0,
+                           problem: Optional[btk_problem_t] = None):
+    """The decode step with the KV append fused in: k_new / v_new [B, Hkv, D] are written
+    into the caches at position seq_lens - 1, then S1 + S2 + S3 + S4; returns (out, indices)."""
+    dev = q.device
+    problem = problem or make_problem(q, k_cache, block_table, sm_scale)
+    out = torch.empty_like(q) if out is None else out
+    if indices is None:
+        indices = torch.empty((problem.batch, problem.num_kv_heads, int(top_k)), dtype=torch.int32,
+                              device=dev)
+    _check_shapes(problem, q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
+                  seq_lens=seq_lens, centroids=centroids, indices=indices, out=out, lse=lse,
+                  top_k=top_k)
+    tok = (problem.batch, problem.num_kv_heads, problem.head_dim)
+    _expect(k_new, "k_new", tok)
+    _expect(v_new, "v_new", tok)
+    lp = _dev(lse, "lse", torch.float32, dev) if lse is not None else None
+    st = _lib().btk_decode_step_append(ctypes.byref(problem), _dev(q, "q", None, dev),
+                                       _dev(k_new, "k_new", q.dtype, dev),
+                                       _dev(v_new, "v_new", q.dtype, dev),
+                                       _dev(k_cache, "k_cache", q.dtype, dev),
+                                       _dev(v_cache, "v_cache", q.dtype, dev),
+                                       _dev(block_table, "block_table", torch.int32, dev),
+                                       _dev(seq_lens, "seq_lens", torch.int32, dev),
+                                       _dev(centroids, "centroids", torch.float32, dev),
+                                       int(top_k), _dev(indices, "indices", torch.int32, dev),
+                                       _dev(out, "out", q.dtype, dev), lp,
+                                       _dev(workspace, "workspace", torch.uint8, dev),
+                                       workspace.numel(), _stream(dev))
+    _check(st, "btk_decode_step_append")
     return out, indices
 
 

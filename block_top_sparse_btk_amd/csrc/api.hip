@@ -286,16 +286,19 @@ btk_status_t btk_token_topk_attend(const btk_problem_t *problem, const void *q,
                                          s, counts));
 }
 
-btk_status_t btk_decode_step(const btk_problem_t *problem, const void *q, const void *k_cache,
-                             const void *v_cache, const int32_t *block_table,
-                             const int32_t *seq_lens, const int32_t *first_pos, float *centroids,
-                             int32_t top_k, int32_t *indices, void *out, float *lse,
-                             void *workspace, size_t workspace_bytes, void *stream) {
+// The single-launch step, with (k_new, v_new non-NULL) or without the KV append.
+static btk_status_t decode_step(const btk_problem_t *problem, const void *q, const void *k_new,
+                                const void *v_new, const void *k_cache, const void *v_cache,
+                                const int32_t *block_table, const int32_t *seq_lens,
+                                const int32_t *first_pos, float *centroids, int32_t top_k,
+                                int32_t *indices, void *out, float *lse, void *workspace,
+                                size_t workspace_bytes, void *stream, bool append) {
     btk::Dims d;
     btk_status_t st = check_problem(problem, &d);
     if (st != BTK_OK) return st;
     if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !centroids || !indices || !out)
         return BTK_ERR_NULL;
+    if (append && (!k_new || !v_new)) return BTK_ERR_NULL;
     if (!top_k_ok(top_k)) return BTK_ERR_SHAPE;
     if (d.B > btk::kMaxStepBatch || !btk::step_rows_fit(d)) return BTK_ERR_UNSUPPORTED;
     const btk::WorkspaceLayout w = btk::workspace_layout(d, top_k);
@@ -311,7 +314,29 @@ btk_status_t btk_decode_step(const btk_problem_t *problem, const void *q, const 
         reinterpret_cast<uint32_t *>(ws + w.att_counters),
         reinterpret_cast<uint32_t *>(ws + w.ready), reinterpret_cast<uint32_t *>(ws + w.queue),
         reinterpret_cast<uint32_t *>(ws + btk::kStealOffset),
-        reinterpret_cast<uint32_t *>(ws), (hipStream_t)stream));
+        reinterpret_cast<uint32_t *>(ws), (hipStream_t)stream, append ? k_new : nullptr,
+        append ? v_new : nullptr));
+}
+
+btk_status_t btk_decode_step(const btk_problem_t *problem, const void *q, const void *k_cache,
+                             const void *v_cache, const int32_t *block_table,
+                             const int32_t *seq_lens, const int32_t *first_pos, float *centroids,
+                             int32_t top_k, int32_t *indices, void *out, float *lse,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+    return decode_step(problem, q, nullptr, nullptr, k_cache, v_cache, block_table, seq_lens,
+                       first_pos, centroids, top_k, indices, out, lse, workspace,
+                       workspace_bytes, stream, false);
+}
+
+btk_status_t btk_decode_step_append(const btk_problem_t *problem, const void *q,
+                                    const void *k_new, const void *v_new, void *k_cache,
+                                    void *v_cache, const int32_t *block_table,
+                                    const int32_t *seq_lens, float *centroids, int32_t top_k,
+                                    int32_t *indices, void *out, float *lse, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+    return decode_step(problem, q, k_new, v_new, k_cache, v_cache, block_table, seq_lens,
+                       nullptr, centroids, top_k, indices, out, lse, workspace, workspace_bytes,
+                       stream, true);
 }
 
 }  // extern "C"

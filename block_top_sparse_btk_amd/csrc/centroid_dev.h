@@ -60,6 +60,13 @@ struct KeyTile {
                          : make_uint4(0u, 0u, 0u, 0u);
         }
     }
+    // token t's row, given as this lane's 16-byte slice (dims col*VEC ..)
+    __device__ __forceinline__ void set_row(int t, uint4 slice, int lane) {
+        const int row = lane / LPR;
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            if (i * TPI + row == t) w[i] = slice;
+    }
     __device__ __forceinline__ void mean(int v, float *gdst, float *ldst, int lane) const {
         const int col = lane % LPR, row = lane / LPR;
         float acc[VEC];

@@ -47,6 +47,11 @@ struct SelectArgs {
     // shared-prefix form only (NULL otherwise): per (group, KV head) the shared
     // items done and the members that have finished with them
     uint32_t *pflags = nullptr;
+    // decode step with the KV append (NULL otherwise): the newest token's key
+    // and value [B][Hkv][D], written into its cache slot (position L - 1) by the
+    // segment that refreshes that block, and the caches they are written to
+    const void *k_new = nullptr, *v_new = nullptr;
+    void *k_out = nullptr, *v_out = nullptr;
 };
 
 // LDS used by one chunk's scan.
@@ -629,6 +634,44 @@ __device__ __forceinline__ void load_setup(const SelectArgs &a, int b, int g, in
     }
 }
 
+// KV append of the decode step: the newest token of unit (b, g), slot t of
+// `page`, goes into the key tile in registers (for the centroid) and into both
+// caches.  The stores are agent-scope atomics, so they are visible to the
+// attention on any XCD once the segment has waited for them and counted in;
+// the value cache is dim-major, so its slot is one element per dimension.
+template <typename T, int D>
+__device__ __forceinline__ void append_token(const SelectArgs &a, int b, int g, int page, int t,
+                                             KeyTile<T, D> &kt, int lane) {
+    using KT = KeyTile<T, D>;
+    constexpr int VEC = KT::VEC;
+    const size_t row = ((size_t)b * a.Hkv + g) * D;
+    const size_t tile = ((size_t)page * a.Hkv + g) * kPage * D;
+    const int col = lane % KT::LPR;
+    const uint4 kn = *reinterpret_cast<const uint4 *>(static_cast<const T *>(a.k_new) + row +
+                                                      col * VEC);
+    kt.set_row(t, kn, lane);
+    if (lane < KT::LPR) {
+        uint32_t *dst = reinterpret_cast<uint32_t *>(static_cast<T *>(a.k_out) + tile +
+                                                     (size_t)t * D + col * VEC);
+        __hip_atomic_store(dst + 0, kn.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(dst + 1, kn.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(dst + 2, kn.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(dst + 3, kn.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const T *vn = static_cast<const T *>(a.v_new) + row;
+    T *vt = static_cast<T *>(a.v_out) + tile + t;
+    for (int d = lane; d < D; d += kWave) {
+        if constexpr (sizeof(T) == 2)
+            __hip_atomic_store(reinterpret_cast<uint16_t *>(vt + (size_t)d * kPage),
+                               *reinterpret_cast<const uint16_t *>(vn + d), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        else
+            __hip_atomic_store(reinterpret_cast<uint32_t *>(vt + (size_t)d * kPage),
+                               *reinterpret_cast<const uint32_t *>(vn + d), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 // Scores n consecutive blocks j0 .. j0+n-1 of unit (b, g) whose page ids are in
 // sm.pages[0 .. n) (invalid ones as -1) against the scaled mean query in
 // sm.qs, stages the scores in sm.sc and stores them to a.scores.  REFRESH
@@ -649,13 +692,17 @@ __device__ __forceinline__ void scan_rows(const SelectArgs &a, int b, int g, int
     // decode step: wave w refreshes the touched blocks jw, jw + 4, ... of the
     // run; the keys of its first one are requested before the scan so that
     // they arrive while it streams
-    const bool refresh = REFRESH && a.first_pos && fp >= 0 && fp < L;
+    const bool refresh = REFRESH && (a.first_pos || a.k_new) && fp >= 0 && fp < L;
     const int jw = refresh ? max(j0, fp / kPage) + wave : j0 + n;
     const T *keys = static_cast<const T *>(a.k_cache) + (size_t)g * kPage * D;
     const size_t page_stride = (size_t)a.Hkv * kPage * D;
     KeyTile<T, D> kt;
+    // with the KV append the newest token (position L - 1) is the last of its
+    // block and is never read from the cache: it comes from k_new
+    const int jnew = REFRESH && a.k_new ? (L - 1) / kPage : -1;
+    auto cached = [&](int j) { return min(kPage, L - j * kPage) - (j == jnew ? 1 : 0); };
     if (jw < j0 + n && sm.pages[jw - j0] >= 0)
-        kt.load(keys + (size_t)sm.pages[jw - j0] * page_stride, min(kPage, L - jw * kPage), lane);
+        kt.load(keys + (size_t)sm.pages[jw - j0] * page_stride, cached(jw), lane);
     float qf[VPL];
 #pragma unroll
     for (int e = 0; e < VPL; ++e) qf[e] = sm.qs[col * VPL + e];
@@ -706,7 +753,8 @@ __device__ __forceinline__ void scan_rows(const SelectArgs &a, int b, int g, int
         if (page < 0) continue;
         const int v = min(kPage, L - j * kPage);
         float *row_lds = crow + wave * D;
-        if (j != jw) kt.load(keys + (size_t)page * page_stride, v, lane);
+        if (j != jw) kt.load(keys + (size_t)page * page_stride, cached(j), lane);
+        if (j == jnew) append_token<T, D>(a, b, g, page, v - 1, kt, lane);
         kt.mean(v, a.cent_out + ((size_t)page * a.Hkv + g) * D, row_lds, lane);
         __builtin_amdgcn_wave_barrier();
         Row cv;

@@ -104,7 +104,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
             const bool ok = L >= 1 && L <= a.s.max_blocks * kPage;
             const int nb = ok ? (L + kPage - 1) / kPage : -1;
             lens[b] = ok ? L : -1;
-            fps[b] = a.s.first_pos ? a.s.first_pos[b] : -1;
+            // with the KV append the newest token (L - 1) is the one touched
+            fps[b] = a.s.k_new ? (ok ? L - 1 : -1) : a.s.first_pos ? a.s.first_pos[b] : -1;
             n = (uint32_t)Hkv * (uint32_t)(kSegmentCost + (ok ? nb : 1));
         }
         const uint32_t carry = b0 == 0 ? 0u : rows[b0];
@@ -279,7 +280,8 @@ hipError_t launch_decode_step(const Dims &d, const SelectPlan &sp, const AttendP
                               int32_t *indices, float *scores, void *out, float *lse,
                               float *partials, uint32_t *sel_counters, uint32_t *att_counters,
                               uint32_t *ready, uint32_t *queue, uint32_t *steal,
-                              uint32_t *err, hipStream_t stream) {
+                              uint32_t *err, hipStream_t stream, const void *k_new,
+                              const void *v_new) {
     // a split's share of the selection (at most 4 * 64 entries) is kept in the
     // score staging area
     if (ap.bps > kRun) return hipErrorInvalidValue;
@@ -287,6 +289,13 @@ hipError_t launch_decode_step(const Dims &d, const SelectPlan &sp, const AttendP
     a.s = sel::SelectArgs{q, centroids, block_table, seq_lens, indices, scores, sel_counters, err,
                           d.Hq, d.Hkv, d.num_pages, d.max_blocks, top_k, sp.chunk, sp.nchunk_max,
                           d.sm_scale, k_cache, first_pos, centroids};
+    if (k_new) {  // the caches are the caller's, written in place by the append
+        a.s.k_new = k_new;
+        a.s.v_new = v_new;
+        a.s.k_out = const_cast<void *>(k_cache);
+        a.s.v_out = const_cast<void *>(v_cache);
+        a.s.first_pos = nullptr;
+    }
     a.t = att::AttendArgs{q, k_cache, v_cache, block_table, seq_lens, indices, out, lse, partials,
                           att_counters, err, d.Hq, d.Hkv, d.num_pages, d.max_blocks, top_k, ap.bps,
                           ap.nsplit_max, d.sm_scale * 1.44269504088896340736f, nullptr};

@@ -235,9 +235,10 @@ btk_status_t btk_token_topk_attend(const btk_problem_t *problem, const void *q,
 /* One whole decode step in a single launch: S1 for the touched pages (as
  * btk_centroid_update with first_pos; none when first_pos is NULL), then S2+S3
  * (as btk_select) and S4 (as btk_sparse_attend), with results identical to
- * those three calls.  A persistent kernel takes scoring and attention work from
- * a queue in the workspace; the attention of a unit starts once its selection
- * is published, so the selection's latency hides behind other units' work.
+ * those three calls.  A persistent kernel first scores every centroid row (each
+ * workgroup a share of the rows, the last rows handed out in chunks to the
+ * workgroups that finish first), then each (sequence, KV head) selects and
+ * attends once its scores are complete.
  * (Pith review, "What carries the argument"; the single-launch form is this
  * library's own design.)
  *   centroids  in/out   indices out [B][Hkv][top_k]   out/lse out as btk_sparse_attend
@@ -249,6 +250,28 @@ btk_status_t btk_decode_step(const btk_problem_t *problem, const void *q, const 
                              const int32_t *seq_lens, const int32_t *first_pos, float *centroids,
                              int32_t top_k, int32_t *indices, void *out, float *lse,
                              void *workspace, size_t workspace_bytes, void *stream);
+
+/* btk_decode_step with the KV append of the step fused in: the newest token of
+ * each sequence, at position seq_lens[b] - 1 (seq_lens count it), is written
+ * into its cache slot from k_new / v_new before it is averaged into its
+ * block's centroid and attended, so no separate append precedes the call.  The
+ * results, centroids and caches are identical to writing k_new / v_new into the
+ * caches and then calling btk_decode_step with first_pos = seq_lens - 1.
+ * (Pith review, "What carries the argument": each decode step adds one key and
+ * value per sequence to the blocks that are summarised and selected.)
+ *   k_new, v_new  [B][Hkv][D], same dtype as q, device, read only
+ *   k_cache, v_cache  in/out: slot (seq_lens[b] - 1) % 16 of page
+ *                 block_table[b][(seq_lens[b] - 1) / 16] is written for every KV
+ *                 head; a sequence whose page id there is out of range is
+ *                 skipped and flagged like any invalid page
+ *   other arguments, limits and errors as btk_decode_step (first_pos is implied);
+ *   BTK_ERR_NULL if k_new or v_new is NULL. */
+btk_status_t btk_decode_step_append(const btk_problem_t *problem, const void *q,
+                                    const void *k_new, const void *v_new, void *k_cache,
+                                    void *v_cache, const int32_t *block_table,
+                                    const int32_t *seq_lens, float *centroids, int32_t top_k,
+                                    int32_t *indices, void *out, float *lse, void *workspace,
+                                    size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

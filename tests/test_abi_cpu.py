@@ -149,6 +149,17 @@ def test_local_attend_and_decode_step_validate_before_launch():
     assert lib.btk_decode_step(ctypes.byref(big), *args(wsn=1 << 40)) == btk.BTK_ERR_UNSUPPORTED
     bad = ctypes.byref(_problem(head_dim=96))
     assert lib.btk_decode_step(bad, *args()) == btk.BTK_ERR_UNSUPPORTED
+    # the step with the fused KV append: the new key and value are required
+    app = lambda **o: [o.get(n, FAKE) for n in ("q", "kn", "vn", "k", "v", "bt", "sl", "cent")] + \
+        [o.get("k_", 8), o.get("idx", FAKE), o.get("out", FAKE), None, o.get("ws", FAKE),
+         o.get("wsn", need), None]  # noqa: E731
+    assert lib.btk_decode_step_append(p, *app(kn=None)) == btk.BTK_ERR_NULL
+    assert lib.btk_decode_step_append(p, *app(vn=None)) == btk.BTK_ERR_NULL
+    assert lib.btk_decode_step_append(p, *app(k=None)) == btk.BTK_ERR_NULL
+    assert lib.btk_decode_step_append(p, *app(k_=0)) == btk.BTK_ERR_SHAPE
+    assert lib.btk_decode_step_append(p, *app(wsn=need - 1)) == btk.BTK_ERR_WORKSPACE
+    assert lib.btk_decode_step_append(ctypes.byref(big), *app(wsn=1 << 40)) == \
+        btk.BTK_ERR_UNSUPPORTED
     # the step's 32-bit row counters: batch * Hkv * (max_blocks + 520) must stay below 2^32
     rows_over = _problem(batch=1024, num_q_heads=4096, num_kv_heads=4096, max_blocks_per_seq=512)
     assert lib.btk_decode_step(ctypes.byref(rows_over), *args(wsn=1 << 40)) == \

@@ -449,6 +449,59 @@ def _step_both(q, k_cache, v_cache, bt, sl, cent, k, prob, ws_step, first=None):
                  err=btk.workspace_error_bits(ws_step)))
 
 
+APPEND_CASES = [("config3", dict(cfg=3)),
+                ("page-edges", dict(kw=dict(batch=6, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                                            seq_lens=[1, 16, 17, 33, 300, 5000], top_k=8,
+                                            seed=41))),
+                ("d64-fp32", dict(kw=dict(batch=3, num_q_heads=4, num_kv_heads=2, head_dim=64,
+                                          seq_lens=[100, 32, 999], top_k=5, seed=42,
+                                          dtype=torch.float32)))]
+
+
+@pytest.mark.parametrize("label,spec", APPEND_CASES, ids=[c[0] for c in APPEND_CASES])
+def test_decode_step_append_equals_append_then_step(label, spec):
+    """The fused KV append leaves caches, centroids and every output bit-identical
+    to writing the token into the caches first and then taking the step."""
+    bt = _workload(spec["cfg"]) if "cfg" in spec else synth.make_batch(name=label, **spec["kw"])
+    _say(f"[append] {label}")
+    d = bt.to(DEV)
+    prob = btk.make_problem(d.q, d.k_cache, d.block_table)
+    k, B, H = bt.top_k, bt.batch, bt.num_kv_heads
+    L = bt.seq_lens.long()
+    page = bt.block_table[torch.arange(B), (L - 1) // 16].long()[:, None]
+    slot = ((L - 1) % 16)[:, None]
+    heads = torch.arange(H)[None, :]
+    # the newest token as drawn is the one appended
+    k_new = bt.k_cache[page, heads, slot, :].contiguous()
+    v_new = bt.v_cache[page, heads, :, slot].contiguous()
+    stale = oracle.centroids(bt.k_cache, bt.block_table, bt.seq_lens)
+    stale[page[:, 0]] = float("nan")  # the newest token's page is stale before the step
+    # append, then the step
+    ws1 = btk.new_workspace(prob, k, DEV)
+    c1 = stale.to(DEV)
+    lse1 = torch.empty((B, bt.num_q_heads), device=DEV)
+    out1, idx1 = btk.btk_decode_step(d.q, d.k_cache, d.v_cache, d.block_table, d.seq_lens, c1, k,
+                                     ws1, first_pos=(d.seq_lens - 1).to(torch.int32), lse=lse1,
+                                     problem=prob)
+    # fused: the new slots hold other values before the call
+    kc, vc = d.k_cache.clone(), d.v_cache.clone()
+    pd, sd, hd = page.to(DEV), slot.to(DEV), heads.to(DEV)
+    kc[pd, hd, sd, :] = 7.0
+    vc[pd, hd, :, sd] = -7.0
+    ws2 = btk.new_workspace(prob, k, DEV)
+    c2 = stale.to(DEV)
+    lse2 = torch.empty_like(lse1)
+    out2, idx2 = btk.btk_decode_step_append(d.q, k_new.to(DEV), v_new.to(DEV), kc, vc,
+                                            d.block_table, d.seq_lens, c2, k, ws2, lse=lse2,
+                                            problem=prob)
+    torch.cuda.synchronize()
+    assert btk.workspace_error_bits(ws1) == 0 and btk.workspace_error_bits(ws2) == 0
+    assert torch.equal(kc, d.k_cache) and torch.equal(vc, d.v_cache)
+    assert torch.equal(c2, c1)
+    assert torch.equal(idx2, idx1) and torch.equal(out2, out1) and torch.equal(lse2, lse1)
+    _say(f"[append]   ok {label}")
+
+
 def test_decode_step_flags_invalid_lengths_and_pages_like_separate_calls():
     # an empty sequence, one longer than its table row and a page id past the pool,
     # next to valid sequences: the same error bits, -1 rows and valid results as
