@@ -163,6 +163,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="skip the HIP-graph replay measurement")
+    ap.add_argument("--no-append", dest="append", action="store_false",
+                    help="skip the step with the fused KV append")
     ap.add_argument("--no-best-of-n", dest="best_of_n", action="store_false",
                     help="skip the shared-prefix (Best-of-N) selection comparison")
     ap.add_argument("--copy-probe", action="store_true",
@@ -404,6 +406,40 @@ def main(argv=None):
                "select_bytes": sel4, "select_shared_bytes": sel4 - saved,
                "note": "same inputs, caches warm for both; identical indices; median of 10 replays of a HIP graph of 20 calls"}
 
+    # the step with the KV append fused in (btk_decode_step_append): the appended
+    # key and value are each sequence's newest token as drawn, so every replica's
+    # caches stay as they are and the results must equal the step's bit for bit
+    app = None
+    if args.append:
+        Ll = bt.seq_lens.long()
+        pg = bt.block_table[torch.arange(B), (Ll - 1) // 16].long()[:, None]
+        sl = ((Ll - 1) % 16)[:, None]
+        hh = torch.arange(hkv)[None, :]
+        k_new = bt.k_cache[pg, hh, sl, :].contiguous().to(dev)
+        v_new = bt.v_cache[pg, hh, :, sl].contiguous().to(dev)
+        f_app = lib.btk_decode_step_append
+        p_ = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        for rep in reps:
+            rep["aidx"] = torch.empty_like(rep["idx"])
+            rep["aout"] = torch.empty_like(rep["out"])
+            d = rep["d"]
+            rep["app"] = (ctypes.byref(prob), p_(d.q), p_(k_new), p_(v_new), p_(d.k_cache),
+                          p_(d.v_cache), p_(d.block_table), p_(d.seq_lens), p_(rep["cent"]), k,
+                          p_(rep["aidx"]), p_(rep["aout"]), None, p_(rep["ws"]),
+                          rep["ws"].numel(), hs)
+        for i in range(args.warmup):
+            check(f_app(*reps[i % len(reps)]["app"]))
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            check(f_app(*reps[i % len(reps)]["app"]))
+        torch.cuda.synchronize()
+        app_ms = 1e3 * (time.perf_counter() - t0) / args.steps
+        for rep in reps:
+            if not (torch.equal(rep["aidx"], rep["idx"]) and torch.equal(rep["aout"], rep["out"])):
+                raise RuntimeError("the step with the fused append disagrees with the step")
+        app = app_ms
+
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -418,6 +454,12 @@ def main(argv=None):
     launch_gbps = nbytes["step"] / (step_us * 1e-6) / 1e9
     dense_gbps = nbytes["dense"] / (dense_ms * 1e-3) / 1e9
     value = B / (ms_per_step * 1e-3)
+    if app is not None:
+        app_bytes = nbytes["step"] + 4 * B * hkv * D * e  # new K,V read and written
+        app = {"ms_per_step": round(app, 5), "value": round(B / (app * 1e-3), 1),
+               "bytes_per_step": app_bytes, "gbps": round(app_bytes / (app * 1e-3) / 1e9, 1),
+               "note": "btk_decode_step_append: the newest token's key and value written into "
+                       "the caches inside the same launch; results identical to the step"}
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -470,6 +512,7 @@ def main(argv=None):
                                              / HBM_PEAK_GBPS, 4),
                        "bytes_per_step": nbytes["token"]},
         "best_of_n": bon,
+        "fused_append": app,
         "graph_replay": None if graph_ms is None else {
             "ms_per_step": round(graph_ms, 5), "value": round(B / (graph_ms * 1e-3), 1),
             "step_gbps": round(nbytes["step"] / (graph_ms * 1e-3) / 1e9, 1)},

@@ -61,6 +61,9 @@ struct ScoreSmem {
     int *pages;   // [kMaxChunk] page ids of the chunk
     float *sc;    // [kMaxChunk] scores of the chunk
     int *flag;    // one word
+    // decode step with the KV append: the new token's key and value rows of the
+    // segment's unit (2 * D elements), loaded with the segment's setup
+    uint32_t *newtok = nullptr;
 };
 
 // LDS used by the top-k selection.
@@ -634,44 +637,6 @@ __device__ __forceinline__ void load_setup(const SelectArgs &a, int b, int g, in
     }
 }
 
-// KV append of the decode step: the newest token of unit (b, g), slot t of
-// `page`, goes into the key tile in registers (for the centroid) and into both
-// caches.  The stores are agent-scope atomics, so they are visible to the
-// attention on any XCD once the segment has waited for them and counted in;
-// the value cache is dim-major, so its slot is one element per dimension.
-template <typename T, int D>
-__device__ __forceinline__ void append_token(const SelectArgs &a, int b, int g, int page, int t,
-                                             KeyTile<T, D> &kt, int lane) {
-    using KT = KeyTile<T, D>;
-    constexpr int VEC = KT::VEC;
-    const size_t row = ((size_t)b * a.Hkv + g) * D;
-    const size_t tile = ((size_t)page * a.Hkv + g) * kPage * D;
-    const int col = lane % KT::LPR;
-    const uint4 kn = *reinterpret_cast<const uint4 *>(static_cast<const T *>(a.k_new) + row +
-                                                      col * VEC);
-    kt.set_row(t, kn, lane);
-    if (lane < KT::LPR) {
-        uint32_t *dst = reinterpret_cast<uint32_t *>(static_cast<T *>(a.k_out) + tile +
-                                                     (size_t)t * D + col * VEC);
-        __hip_atomic_store(dst + 0, kn.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(dst + 1, kn.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(dst + 2, kn.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(dst + 3, kn.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    const T *vn = static_cast<const T *>(a.v_new) + row;
-    T *vt = static_cast<T *>(a.v_out) + tile + t;
-    for (int d = lane; d < D; d += kWave) {
-        if constexpr (sizeof(T) == 2)
-            __hip_atomic_store(reinterpret_cast<uint16_t *>(vt + (size_t)d * kPage),
-                               *reinterpret_cast<const uint16_t *>(vn + d), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        else
-            __hip_atomic_store(reinterpret_cast<uint32_t *>(vt + (size_t)d * kPage),
-                               *reinterpret_cast<const uint32_t *>(vn + d), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-    }
-}
-
 // Scores n consecutive blocks j0 .. j0+n-1 of unit (b, g) whose page ids are in
 // sm.pages[0 .. n) (invalid ones as -1) against the scaled mean query in
 // sm.qs, stages the scores in sm.sc and stores them to a.scores.  REFRESH
@@ -680,7 +645,7 @@ __device__ __forceinline__ void append_token(const SelectArgs &a, int b, int g, 
 // re-scored here.  KU: rows per lane per pipeline stage (two stages of
 // 4 * 4 * KU rows are in flight).  Called with sm.pages and sm.qs visible to
 // every thread; ends with the stores issued (not waited for).
-template <typename T, int D, int KU, bool REFRESH>
+template <typename T, int D, int KU, bool REFRESH, bool APPEND = false>
 __device__ __forceinline__ void scan_rows(const SelectArgs &a, int b, int g, int j0, int n, int L,
                                           int fp, ScoreSmem &sm, float *crow) {
     constexpr int LPR = 16;                       // lanes per centroid row: one DPP row
@@ -692,14 +657,14 @@ __device__ __forceinline__ void scan_rows(const SelectArgs &a, int b, int g, int
     // decode step: wave w refreshes the touched blocks jw, jw + 4, ... of the
     // run; the keys of its first one are requested before the scan so that
     // they arrive while it streams
-    const bool refresh = REFRESH && (a.first_pos || a.k_new) && fp >= 0 && fp < L;
+    const bool refresh = REFRESH && (a.first_pos || APPEND) && fp >= 0 && fp < L;
     const int jw = refresh ? max(j0, fp / kPage) + wave : j0 + n;
     const T *keys = static_cast<const T *>(a.k_cache) + (size_t)g * kPage * D;
     const size_t page_stride = (size_t)a.Hkv * kPage * D;
     KeyTile<T, D> kt;
     // with the KV append the newest token (position L - 1) is the last of its
     // block and is never read from the cache: it comes from k_new
-    const int jnew = REFRESH && a.k_new ? (L - 1) / kPage : -1;
+    const int jnew = APPEND ? (L - 1) / kPage : -1;
     auto cached = [&](int j) { return min(kPage, L - j * kPage) - (j == jnew ? 1 : 0); };
     if (jw < j0 + n && sm.pages[jw - j0] >= 0)
         kt.load(keys + (size_t)sm.pages[jw - j0] * page_stride, cached(jw), lane);
@@ -754,7 +719,11 @@ __device__ __forceinline__ void scan_rows(const SelectArgs &a, int b, int g, int
         const int v = min(kPage, L - j * kPage);
         float *row_lds = crow + wave * D;
         if (j != jw) kt.load(keys + (size_t)page * page_stride, cached(j), lane);
-        if (j == jnew) append_token<T, D>(a, b, g, page, v - 1, kt, lane);
+        if (APPEND && j == jnew)  // this lane's 16-byte slice of the new key (LDS)
+            kt.set_row(v - 1,
+                       *reinterpret_cast<const uint4 *>(sm.newtok + (lane % KeyTile<T, D>::LPR) *
+                                                        (KeyTile<T, D>::VEC * sizeof(T) / 4)),
+                       lane);
         kt.mean(v, a.cent_out + ((size_t)page * a.Hkv + g) * D, row_lds, lane);
         __builtin_amdgcn_wave_barrier();
         Row cv;
@@ -847,7 +816,7 @@ __device__ __forceinline__ bool score_chunk(const SelectArgs &a, int unit, int c
 // blocks in on the unit's counter.  The segment that completes the unit resets
 // the counter and sets the unit's ready word to `tag`, after every segment's
 // score stores have completed (each waits for its own before counting in).
-template <typename T, int D, int KU, int RUN>
+template <typename T, int D, int KU, int RUN, bool APPEND = false>
 __device__ __forceinline__ void score_segment(const SelectArgs &a, int b, int g, int j0, int j1,
                                               int nb, int L, int fp, ScoreSmem &sm, float *crow,
                                               uint32_t *ready, uint32_t tag) {
@@ -866,13 +835,23 @@ __device__ __forceinline__ void score_segment(const SelectArgs &a, int b, int g,
     // the block-table row, the length and the decode position
     int n = min(RUN, j1 - j0);
     load_setup<T, D, RUN>(a, b, g, j0, n, sm);
+    if constexpr (APPEND) {  // the segment that holds the newest token takes its key and value
+        const int jn = (L - 1) / kPage;
+        if (j0 <= jn && jn < j1) {
+            constexpr int W = D * (int)sizeof(T) / 4;
+            const size_t row = ((size_t)b * a.Hkv + g) * D;
+            const uint32_t *kr = reinterpret_cast<const uint32_t *>(static_cast<const T *>(a.k_new) + row);
+            const uint32_t *vr = reinterpret_cast<const uint32_t *>(static_cast<const T *>(a.v_new) + row);
+            for (int i = tid; i < 2 * W; i += kThreads) sm.newtok[i] = i < W ? kr[i] : vr[i - W];
+        }
+    }
     const int32_t *row = a.bt + (size_t)b * a.max_blocks;
     __syncthreads();
     mean_query<D>(a, sm);
     for (int s0 = j0;;) {
         check_pages(a, sm, n);
         __syncthreads();
-        scan_rows<T, D, KU, true>(a, b, g, s0, n, L, fp, sm, crow);
+        scan_rows<T, D, KU, true, APPEND>(a, b, g, s0, n, L, fp, sm, crow);
         s0 += n;
         if (s0 >= j1) break;
         n = min(RUN, j1 - s0);

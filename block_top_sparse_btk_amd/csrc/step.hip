@@ -69,7 +69,44 @@ constexpr int kSegmentCost = 520;
 constexpr int kStealFrac = 8;
 constexpr uint32_t kStealRows = 256;
 
+// KV append (APPEND): the newest token of unit (b, g), position L - 1, goes
+// into slot (L - 1) % 16 of its page in both caches.  Phase 1 takes its key
+// from k_new for the block's centroid and never reads that slot; the unit's
+// attention item writes the slot (each split of the unit the same values) while
+// its ready poll and selection run, and waits for its own stores before it
+// attends, so no other workgroup reads the slot in this launch.  The value cache
+// is dim-major: the slot is one element per dimension.
 template <typename T, int D>
+__device__ __forceinline__ void append_to_cache(const StepArgs &a, int b, int g, int L,
+                                                int lane) {
+    constexpr int W = D * (int)sizeof(T) / 4;  // 32-bit words per row
+    const int jn = (L - 1) / kPage, t = (L - 1) % kPage;
+    const int page = a.s.bt[(size_t)b * a.s.max_blocks + jn];
+    const size_t row = ((size_t)b * a.s.Hkv + g) * D;
+    uint32_t kw[(W + kWave - 1) / kWave];
+    T vv[(D + kWave - 1) / kWave];
+#pragma unroll
+    for (int i = 0; i < (W + kWave - 1) / kWave; ++i)
+        kw[i] = reinterpret_cast<const uint32_t *>(static_cast<const T *>(a.s.k_new) + row)
+            [min(lane + i * kWave, W - 1)];
+#pragma unroll
+    for (int i = 0; i < (D + kWave - 1) / kWave; ++i)
+        vv[i] = static_cast<const T *>(a.s.v_new)[row + min(lane + i * kWave, D - 1)];
+    if (page < 0 || page >= a.s.num_pages) return;  // flagged by the scan of that block
+    const size_t tile = ((size_t)page * a.s.Hkv + g) * kPage * D;
+    uint32_t *kd = reinterpret_cast<uint32_t *>(static_cast<T *>(a.s.k_out) + tile + (size_t)t * D);
+#pragma unroll
+    for (int i = 0; i < (W + kWave - 1) / kWave; ++i)
+        if (lane + i * kWave < W) kd[lane + i * kWave] = kw[i];
+    T *vd = static_cast<T *>(a.s.v_out) + tile + t;
+#pragma unroll
+    for (int i = 0; i < (D + kWave - 1) / kWave; ++i)
+        if (lane + i * kWave < D) vd[(size_t)(lane + i * kWave) * kPage] = vv[i];
+}
+
+// APPEND: the KV append of the step is fused in (a separate instantiation, so
+// that the plain step carries none of its code).
+template <typename T, int D, bool APPEND>
 __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
     __shared__ float qs[D];
     __shared__ int pages[kRun];
@@ -79,6 +116,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
     __shared__ uint32_t red[2 * kWaves];
     __shared__ int scan_red[kWaves];
     __shared__ float crow[kWaves * D];
+    __shared__ __align__(16) uint32_t newtok[APPEND ? 2 * D * sizeof(T) / 4 : 4];
     __shared__ uint32_t rows[kMaxStepBatch + 1];  // centroid rows before each sequence
     __shared__ int lens[kMaxStepBatch];           // sequence lengths, -1: invalid
     __shared__ int fps[kMaxStepBatch];            // decode positions (first touched token)
@@ -86,7 +124,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
     __shared__ uint32_t tag_s;
     // queries while scoring, top-k keys of long contexts, attention merges
     extern __shared__ float dyn[];
-    sel::ScoreSmem sm{dyn, qs, pages, sc_lds, &flag};
+    sel::ScoreSmem sm{dyn, qs, pages, sc_lds, &flag, newtok};
     sel::TopkSmem tk{hist, cand, red, scan_red, reinterpret_cast<uint32_t *>(dyn)};
     const int tid = threadIdx.x;
     const int Hkv = a.s.Hkv;
@@ -105,7 +143,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
             const int nb = ok ? (L + kPage - 1) / kPage : -1;
             lens[b] = ok ? L : -1;
             // with the KV append the newest token (L - 1) is the one touched
-            fps[b] = a.s.k_new ? (ok ? L - 1 : -1) : a.s.first_pos ? a.s.first_pos[b] : -1;
+            fps[b] = APPEND ? (ok ? L - 1 : -1) : a.s.first_pos ? a.s.first_pos[b] : -1;
             n = (uint32_t)Hkv * (uint32_t)(kSegmentCost + (ok ? nb : 1));
         }
         const uint32_t carry = b0 == 0 ? 0u : rows[b0];
@@ -143,7 +181,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
         const int j0 = (int)(o > kSegmentCost ? o - kSegmentCost : 0u);
         const int j1 = (int)(e > kSegmentCost ? e - kSegmentCost : 0u);
         if (j1 > j0) {
-            sel::score_segment<T, D, kScanRows, kRun>(
+            sel::score_segment<T, D, kScanRows, kRun, APPEND>(
                 a.s, b, (int)g, j0, j1, nb, lens[b], fps[b], sm, crow,
                 a.ready + ((size_t)b * Hkv + g) * kReadyStride, tag);
             __syncthreads();  // LDS is reused by the next segment
@@ -175,6 +213,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
             for (int i = 0; i < kRowPer; ++i)  // unconditional: all in flight together
                 prow[i] = bt_row[min(i * kThreads + tid, nb - 1)];
         }
+        if (APPEND && nb >= 0 && tid >= kWave && tid < 2 * kWave)  // wave 1, beside the poll
+            append_to_cache<T, D>(a, bu, unit % Hkv, L, tid - kWave);
         if (tid == 0) {
             const uint32_t *rw = a.ready + (size_t)unit * kReadyStride;
             uint32_t spins = 0;
@@ -203,6 +243,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
             for (int i = 0; i < kRowPer; ++i)
                 if (i * kThreads + tid < nb) pages[i * kThreads + tid] = prow[i];
         }
+        // the appended token's cache stores are done before the block can be read
+        if (APPEND) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         att::attend_item<T, D, att::kSelected, (sizeof(T) == 4 ? 2 : kStageBlocks)>(
             a.t, unit, split, dyn, &flag, list, L < 0 ? 0 : L, row_lds ? pages : nullptr);
@@ -232,7 +274,7 @@ size_t step_lds_floats(const Dims &d, const AttendPlan &ap) {
 }
 
 // resident workgroups of the step kernel on this device (cached per device)
-template <typename T, int D>
+template <typename T, int D, bool APPEND>
 hipError_t resident_workgroups(size_t lds, int *out) {
     static int cached[64][2] = {};
     int dev = 0;
@@ -244,8 +286,8 @@ hipError_t resident_workgroups(size_t lds, int *out) {
         return hipSuccess;
     }
     int per_cu = 0, cus = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_step_kernel<T, D>, kThreads,
-                                                     lds);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_step_kernel<T, D, APPEND>,
+                                                     kThreads, lds);
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
@@ -260,9 +302,18 @@ hipError_t launch(const Dims &d, const SelectPlan &sp, const AttendPlan &ap, Ste
                   hipStream_t stream) {
     const size_t lds = sizeof(float) * step_lds_floats(d, ap);
     int grid = 0;
-    hipError_t e = resident_workgroups<T, D>(lds, &grid);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_step_kernel<T, D>), dim3(grid), dim3(kThreads), lds, stream, a);
+    hipError_t e;
+    if (a.s.k_new) {
+        e = resident_workgroups<T, D, true>(lds, &grid);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((decode_step_kernel<T, D, true>), dim3(grid), dim3(kThreads), lds,
+                           stream, a);
+    } else {
+        e = resident_workgroups<T, D, false>(lds, &grid);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((decode_step_kernel<T, D, false>), dim3(grid), dim3(kThreads), lds,
+                           stream, a);
+    }
     return hipGetLastError();
 }
 

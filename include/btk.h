@@ -262,8 +262,10 @@ btk_status_t btk_decode_step(const btk_problem_t *problem, const void *q, const 
  *   k_new, v_new  [B][Hkv][D], same dtype as q, device, read only
  *   k_cache, v_cache  in/out: slot (seq_lens[b] - 1) % 16 of page
  *                 block_table[b][(seq_lens[b] - 1) / 16] is written for every KV
- *                 head; a sequence whose page id there is out of range is
- *                 skipped and flagged like any invalid page
+ *                 head; that page must belong to sequence b alone (a shared
+ *                 prompt page is never the newest); a sequence whose page id
+ *                 there is out of range is skipped and flagged like any invalid
+ *                 page
  *   other arguments, limits and errors as btk_decode_step (first_pos is implied);
  *   BTK_ERR_NULL if k_new or v_new is NULL. */
 btk_status_t btk_decode_step_append(const btk_problem_t *problem, const void *q,
