@@ -455,7 +455,13 @@ APPEND_CASES = [("config3", dict(cfg=3)),
                                             seed=41))),
                 ("d64-fp32", dict(kw=dict(batch=3, num_q_heads=4, num_kv_heads=2, head_dim=64,
                                           seq_lens=[100, 32, 999], top_k=5, seed=42,
-                                          dtype=torch.float32)))]
+                                          dtype=torch.float32))),
+                ("d64-group8", dict(kw=dict(batch=4, num_q_heads=16, num_kv_heads=2, head_dim=64,
+                                            seq_lens=[48, 1, 2049, 700], top_k=6, seed=43))),
+                ("max-batch-1024", dict(kw=dict(batch=1024, num_q_heads=8, num_kv_heads=2,
+                                                head_dim=128,
+                                                seq_lens=[1 + (i * 7919) % 700 for i in range(1024)],
+                                                top_k=8, seed=44)))]
 
 
 @pytest.mark.parametrize("label,spec", APPEND_CASES, ids=[c[0] for c in APPEND_CASES])
