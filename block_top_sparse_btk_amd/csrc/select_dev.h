@@ -48,8 +48,9 @@ struct SelectArgs {
     // items done and the members that have finished with them
     uint32_t *pflags = nullptr;
     // decode step with the KV append (NULL otherwise): the newest token's key
-    // and value [B][Hkv][D], written into its cache slot (position L - 1) by the
-    // segment that refreshes that block, and the caches they are written to
+    // and value [B][Hkv][D] (the segment that refreshes that block averages the
+    // key from here; the unit's attention item writes both into their cache
+    // slot, position L - 1) and the caches they are written to
     const void *k_new = nullptr, *v_new = nullptr;
     void *k_out = nullptr, *v_out = nullptr;
 };
@@ -61,8 +62,8 @@ struct ScoreSmem {
     int *pages;   // [kMaxChunk] page ids of the chunk
     float *sc;    // [kMaxChunk] scores of the chunk
     int *flag;    // one word
-    // decode step with the KV append: the new token's key and value rows of the
-    // segment's unit (2 * D elements), loaded with the segment's setup
+    // decode step with the KV append: the new token's key row of the segment's
+    // unit (D elements), loaded with the segment's setup
     uint32_t *newtok = nullptr;
 };
 
@@ -835,14 +836,13 @@ __device__ __forceinline__ void score_segment(const SelectArgs &a, int b, int g,
     // the block-table row, the length and the decode position
     int n = min(RUN, j1 - j0);
     load_setup<T, D, RUN>(a, b, g, j0, n, sm);
-    if constexpr (APPEND) {  // the segment that holds the newest token takes its key and value
+    if constexpr (APPEND) {  // the segment that holds the newest token takes its key
         const int jn = (L - 1) / kPage;
         if (j0 <= jn && jn < j1) {
-            constexpr int W = D * (int)sizeof(T) / 4;
-            const size_t row = ((size_t)b * a.Hkv + g) * D;
-            const uint32_t *kr = reinterpret_cast<const uint32_t *>(static_cast<const T *>(a.k_new) + row);
-            const uint32_t *vr = reinterpret_cast<const uint32_t *>(static_cast<const T *>(a.v_new) + row);
-            for (int i = tid; i < 2 * W; i += kThreads) sm.newtok[i] = i < W ? kr[i] : vr[i - W];
+            constexpr int W = D * (int)sizeof(T) / 4;  // 32-bit words per row
+            const uint32_t *kr = reinterpret_cast<const uint32_t *>(
+                static_cast<const T *>(a.k_new) + ((size_t)b * a.Hkv + g) * D);
+            for (int i = tid; i < W; i += kThreads) sm.newtok[i] = kr[i];
         }
     }
     const int32_t *row = a.bt + (size_t)b * a.max_blocks;

@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
     __shared__ uint32_t red[2 * kWaves];
     __shared__ int scan_red[kWaves];
     __shared__ float crow[kWaves * D];
-    __shared__ __align__(16) uint32_t newtok[APPEND ? 2 * D * sizeof(T) / 4 : 4];
+    __shared__ __align__(16) uint32_t newtok[APPEND ? D * sizeof(T) / 4 : 4];  // new key
     __shared__ uint32_t rows[kMaxStepBatch + 1];  // centroid rows before each sequence
     __shared__ int lens[kMaxStepBatch];           // sequence lengths, -1: invalid
     __shared__ int fps[kMaxStepBatch];            // decode positions (first touched token)
