@@ -60,3 +60,15 @@ def test_token_baseline_bytes():
     for L in (1000, 20):
         want += 2 * (2 * r * D * e + L * D * e + 2 * min(16 * k, L) * D * e)
     assert out["token"] == want
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark runs on one GPU; asking for more exits with a message before any GPU work."""
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "one GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
