@@ -139,20 +139,6 @@ btk_status_t btk_select(const btk_problem_t *problem, const void *q, const float
     char *ws = static_cast<char *>(workspace);
     float *sc = scores ? scores : reinterpret_cast<float *>(ws + w.scores);
     const btk::SelectPlan plan = btk::plan_select(d);
-    if (d.B <= btk::kMaxStepBatch && btk::step_rows_fit(d)) {
-        // the persistent step kernel without its attention: better balanced than
-        // a chunk per workgroup, with identical scores and indices
-        const btk::AttendPlan ap = btk::plan_attend(d, top_k, false);
-        return hip_status(btk::launch_decode_step(
-            d, plan, ap, q, nullptr, nullptr, block_table, seq_lens, nullptr,
-            const_cast<float *>(centroids), top_k, indices, sc, nullptr, nullptr,
-            reinterpret_cast<float *>(ws + w.partials),
-            reinterpret_cast<uint32_t *>(ws + w.sel_counters),
-            reinterpret_cast<uint32_t *>(ws + w.att_counters),
-            reinterpret_cast<uint32_t *>(ws + w.ready), reinterpret_cast<uint32_t *>(ws + w.queue),
-            reinterpret_cast<uint32_t *>(ws + btk::kStealOffset), reinterpret_cast<uint32_t *>(ws),
-            (hipStream_t)stream, nullptr, nullptr, false));
-    }
     return hip_status(btk::launch_select(d, plan, q, centroids, block_table, seq_lens, top_k,
                                          indices, sc,
                                          reinterpret_cast<uint32_t *>(ws + w.sel_counters),

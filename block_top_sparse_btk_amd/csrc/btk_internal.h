@@ -215,7 +215,6 @@ hipError_t launch_decode_step(const Dims &d, const SelectPlan &sp, const AttendP
                               float *partials, uint32_t *sel_counters, uint32_t *att_counters,
                               uint32_t *ready, uint32_t *queue, uint32_t *steal,
                               uint32_t *err, hipStream_t stream,
-                              const void *k_new = nullptr, const void *v_new = nullptr,
-                              bool attend = true);
+                              const void *k_new = nullptr, const void *v_new = nullptr);
 
 }  // namespace btk

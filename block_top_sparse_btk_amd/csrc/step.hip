@@ -105,10 +105,8 @@ __device__ __forceinline__ void append_to_cache(const StepArgs &a, int b, int g,
 }
 
 // APPEND: the KV append of the step is fused in (a separate instantiation, so
-// that the plain step carries none of its code).  ATTEND false: phases 1 and 2
-// without the attention, i.e. S2 + S3 alone (btk_select), with results
-// identical to the chunked select kernel.
-template <typename T, int D, bool APPEND, bool ATTEND>
+// that the plain step carries none of its code).
+template <typename T, int D, bool APPEND>
 __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
     __shared__ float qs[D];
     __shared__ int pages[kRun];
@@ -206,7 +204,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
         const int nb = L < 0 ? -1 : (L + kPage - 1) / kPage;
         // the sequence's block-table row is requested before the wait, so that
         // the attention finds the selected blocks' pages in LDS
-        const bool row_lds = ATTEND && nb >= 0 && nb <= kRun;
+        const bool row_lds = nb >= 0 && nb <= kRun;
         constexpr int kRowPer = kRun / kThreads;
         int32_t prow[kRowPer];
         if (row_lds) {
@@ -240,7 +238,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
                              tk);
             __builtin_amdgcn_s_setprio(0);
         }
-        if (!ATTEND) continue;  // the indices are written
         if (row_lds) {
 #pragma unroll
             for (int i = 0; i < kRowPer; ++i)
@@ -277,7 +274,7 @@ size_t step_lds_floats(const Dims &d, const AttendPlan &ap) {
 }
 
 // resident workgroups of the step kernel on this device (cached per device)
-template <typename T, int D, bool APPEND, bool ATTEND>
+template <typename T, int D, bool APPEND>
 hipError_t resident_workgroups(size_t lds, int *out) {
     static int cached[64][2] = {};
     int dev = 0;
@@ -289,8 +286,8 @@ hipError_t resident_workgroups(size_t lds, int *out) {
         return hipSuccess;
     }
     int per_cu = 0, cus = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, decode_step_kernel<T, D, APPEND, ATTEND>, kThreads, lds);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_step_kernel<T, D, APPEND>,
+                                                     kThreads, lds);
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
@@ -302,25 +299,20 @@ hipError_t resident_workgroups(size_t lds, int *out) {
 
 template <typename T, int D>
 hipError_t launch(const Dims &d, const SelectPlan &sp, const AttendPlan &ap, StepArgs a,
-                  hipStream_t stream, bool attend) {
+                  hipStream_t stream) {
     const size_t lds = sizeof(float) * step_lds_floats(d, ap);
     int grid = 0;
     hipError_t e;
-    if (!attend) {
-        e = resident_workgroups<T, D, false, false>(lds, &grid);
+    if (a.s.k_new) {
+        e = resident_workgroups<T, D, true>(lds, &grid);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((decode_step_kernel<T, D, false, false>), dim3(grid), dim3(kThreads),
-                           lds, stream, a);
-    } else if (a.s.k_new) {
-        e = resident_workgroups<T, D, true, true>(lds, &grid);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((decode_step_kernel<T, D, true, true>), dim3(grid), dim3(kThreads), lds,
+        hipLaunchKernelGGL((decode_step_kernel<T, D, true>), dim3(grid), dim3(kThreads), lds,
                            stream, a);
     } else {
-        e = resident_workgroups<T, D, false, true>(lds, &grid);
+        e = resident_workgroups<T, D, false>(lds, &grid);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((decode_step_kernel<T, D, false, true>), dim3(grid), dim3(kThreads),
-                           lds, stream, a);
+        hipLaunchKernelGGL((decode_step_kernel<T, D, false>), dim3(grid), dim3(kThreads), lds,
+                           stream, a);
     }
     return hipGetLastError();
 }
@@ -340,7 +332,7 @@ hipError_t launch_decode_step(const Dims &d, const SelectPlan &sp, const AttendP
                               float *partials, uint32_t *sel_counters, uint32_t *att_counters,
                               uint32_t *ready, uint32_t *queue, uint32_t *steal,
                               uint32_t *err, hipStream_t stream, const void *k_new,
-                              const void *v_new, bool attend) {
+                              const void *v_new) {
     // a split's share of the selection (at most 4 * 64 entries) is kept in the
     // score staging area
     if (ap.bps > kRun) return hipErrorInvalidValue;
@@ -363,12 +355,12 @@ hipError_t launch_decode_step(const Dims &d, const SelectPlan &sp, const AttendP
     a.steal = steal;
     a.B = d.B;
     a.units = d.B * d.Hkv;
-    a.nsplit = attend ? ap.nsplit_max : 1;  // without attention an item is a whole unit
+    a.nsplit = ap.nsplit_max;
     if (d.dtype == 0)
-        return d.D == 128 ? launch<uint16_t, 128>(d, sp, ap, a, stream, attend)
-                          : launch<uint16_t, 64>(d, sp, ap, a, stream, attend);
-    return d.D == 128 ? launch<float, 128>(d, sp, ap, a, stream, attend)
-                      : launch<float, 64>(d, sp, ap, a, stream, attend);
+        return d.D == 128 ? launch<uint16_t, 128>(d, sp, ap, a, stream)
+                          : launch<uint16_t, 64>(d, sp, ap, a, stream);
+    return d.D == 128 ? launch<float, 128>(d, sp, ap, a, stream)
+                      : launch<float, 64>(d, sp, ap, a, stream);
 }
 
 }  // namespace btk
