@@ -342,6 +342,8 @@ def test_decode_step_replayed_from_a_graph_matches_eager():
 
 STEP_CASES = [("config1", dict(cfg=1)), ("config2", dict(cfg=2)), ("config3", dict(cfg=3)),
               ("config4", dict(cfg=4)), ("config5-8k", dict(cfg=5, context=8192)),
+              ("config5-16k", dict(cfg=5, context=16384)),
+              ("config5-32k", dict(cfg=5, context=32768)),
               ("config5-64k", dict(cfg=5, context=65536)),
               ("ragged-small", dict(kw=dict(batch=5, num_q_heads=8, num_kv_heads=2, head_dim=128,
                                             seq_lens=[1, 17, 300, 5000, 33], top_k=12, seed=31))),
@@ -350,6 +352,9 @@ STEP_CASES = [("config1", dict(cfg=1)), ("config2", dict(cfg=2)), ("config3", di
               ("fp32-d128", dict(kw=dict(batch=2, num_q_heads=6, num_kv_heads=2, head_dim=128,
                                          seq_lens=[333, 1000], top_k=6, seed=33,
                                          dtype=torch.float32))),
+              ("fp32-d64", dict(kw=dict(batch=3, num_q_heads=8, num_kv_heads=2, head_dim=64,
+                                        seq_lens=[2000, 17, 640], top_k=9, seed=35,
+                                        dtype=torch.float32))),
               # the largest batch the single launch takes: the row prefix is built
               # over four 256-sequence chunks and 2048 units share 512 workgroups
               ("max-batch-1024", dict(kw=dict(batch=1024, num_q_heads=8, num_kv_heads=2,
