@@ -270,3 +270,31 @@ def make_config(config: int, variant: int = 0, *, context: Optional[int] = None,
             spec["seq_lens"] = spec["seq_lens"][:batch]
         spec["batch"] = batch
     return make_batch(seed=1000 * config + variant, name=name, **spec)
+
+
+def make_new_tokens(bt: Batch, seed: int, scale: float = 1.0) -> tuple[torch.Tensor, torch.Tensor]:
+    """A fresh key and value per (sequence, KV head), [B, Hkv, D] in the batch's dtype:
+    the token a decode step appends at position seq_lens - 1.  Keys carry the same
+    per-page offset model as the cache (an offset drawn here, N(0, 0.5^2)), values
+    are N(0, 1); ``scale`` multiplies both."""
+    g = torch.Generator().manual_seed(int(seed))
+    shape = (bt.batch, bt.num_kv_heads, bt.head_dim)
+    k = torch.randn(shape, generator=g) + 0.5 * torch.randn(shape, generator=g)
+    v = torch.randn(shape, generator=g)
+    return (scale * k).to(bt.dtype), (scale * v).to(bt.dtype)
+
+
+def write_tokens(bt: Batch, k_new: torch.Tensor, v_new: torch.Tensor) -> Batch:
+    """A copy of ``bt`` (CPU) whose caches hold k_new / v_new at each sequence's
+    position seq_lens - 1 (slot (L - 1) % P of page block_table[b][(L - 1) // P]),
+    for every KV head.  Pure indexing, no arithmetic."""
+    kw = dict(bt.__dict__)
+    kc, vc = bt.k_cache.clone(), bt.v_cache.clone()
+    L = bt.seq_lens.to(torch.int64)
+    page = bt.block_table[torch.arange(bt.batch), (L - 1) // bt.page_size].to(torch.int64)
+    slot = (L - 1) % bt.page_size
+    heads = torch.arange(bt.num_kv_heads)
+    kc[page[:, None], heads[None, :], slot[:, None], :] = k_new.to(kc.dtype)
+    vc[page[:, None], heads[None, :], :, slot[:, None]] = v_new.to(vc.dtype)
+    kw["k_cache"], kw["v_cache"] = kc, vc
+    return Batch(**kw)

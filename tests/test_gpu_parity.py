@@ -408,6 +408,12 @@ def test_decode_step_equals_separate_calls_and_oracle(label, spec):
                        sum_units=sum_factor(bt.group, bt.head_dim))
     check_outputs(results[0][0], ora["out"], bt.dtype, st["equal_mask"], bt.group)
     check_lse(results[0][2], ora["lse"], bt.dtype, st["equal_mask"], bt.group)
+    # every unit, those whose selection differs near a tie included, against the
+    # oracle's attention over the step's own selection
+    o_own, l_own, _ = oracle.attend(bt.q, bt.k_cache, bt.v_cache, bt.block_table, bt.seq_lens,
+                                    results[0][1])
+    check_outputs(results[0][0], o_own, bt.dtype, what="step out on own indices")
+    check_lse(results[0][2], l_own, bt.dtype)
 
 
 @pytest.mark.parametrize("top_k", [32, 64, 100])
@@ -597,6 +603,23 @@ def test_decode_step_shares_longer_than_one_run():
     for key in ("idx", "out", "lse", "cent"):
         assert torch.equal(a[key], b[key]), key
     assert (b["idx"] >= 0).all()
+    # two of the sequences against the oracle: their pages gathered into a compact
+    # CPU cache (the oracle works per sequence, so a sub-batch is exact)
+    for sb in (0, B - 1):
+        nb = nbs[sb]
+        pages = table[sb, :nb].long()
+        kc = k_cache[pages].cpu()
+        vc = v_cache[pages].cpu()
+        tb = torch.arange(nb, dtype=torch.int32)[None, :]
+        sl = lens[sb:sb + 1].cpu()
+        ora = oracle.sparse_step(q[sb:sb + 1].cpu(), kc, vc, tb, sl, 32)
+        assert max_abs(b["cent"][pages.cpu()], ora["centroids"]) <= CENTROID_TOL
+        st = check_indices(b["idx"][sb:sb + 1], ora["indices"], ora["scores"], sl, 32,
+                           sum_units=sum_factor(hq // hkv, dim))
+        check_outputs(b["out"][sb:sb + 1], ora["out"], torch.bfloat16, st["equal_mask"], hq // hkv)
+        o_own, l_own, _ = oracle.attend(q[sb:sb + 1].cpu(), kc, vc, tb, sl, b["idx"][sb:sb + 1])
+        check_outputs(b["out"][sb:sb + 1], o_own, torch.bfloat16, what="long shares, own indices")
+        check_lse(b["lse"][sb:sb + 1], l_own, torch.bfloat16)
 
 
 # ------------------------------------------------------------------ local-window baseline
