@@ -2,6 +2,7 @@
 // Every argument is checked here before the first HIP call, so a rejected call
 // has no side effects and the checks run on machines without a GPU.
 #include <math.h>
+#include <stdlib.h>
 
 #include "btk.h"
 #include "btk_internal.h"
@@ -47,6 +48,21 @@ btk_status_t check_problem(const btk_problem_t *p, btk::Dims *d) {
 
 bool top_k_ok(int32_t top_k) { return top_k >= 1 && top_k <= btk::kMaxBlocksPerSeq; }
 
+// Test hook of the decode step, read from the environment at each call (results
+// never depend on it): BTK_STEP_TEST_FLAGS bit 0 makes every workgroup leave its
+// own share for workgroup 0 and the workgroups without phase-2 items to claim,
+// as if it had not started.
+uint32_t env_u32(const char *name, uint32_t dflt) {
+    const char *e = getenv(name);
+    if (e && *e) {
+        char *end = nullptr;
+        const unsigned long v = strtoul(e, &end, 10);
+        if (end && *end == 0 && v <= 0xffffffffUL) return (uint32_t)v;
+    }
+    return dflt;
+}
+uint32_t step_test_flags() { return env_u32("BTK_STEP_TEST_FLAGS", 0u) & 1u; }
+
 }  // namespace
 
 namespace btk {
@@ -60,7 +76,8 @@ WorkspaceLayout workspace_layout(const Dims &d, int top_k) {
     WorkspaceLayout w;
     w.queue = kQueueOffset;
     w.pflags = 256;
-    w.sel_counters = w.pflags + align256((size_t)kMaxPrefixGroups * d.Hkv * 2 * sizeof(uint32_t));
+    w.claims = w.pflags + align256((size_t)kMaxPrefixGroups * d.Hkv * 2 * sizeof(uint32_t));
+    w.sel_counters = w.claims + (size_t)2 * kMaxStepGrid * kClaimStride * sizeof(uint64_t);
     w.att_counters = w.sel_counters + align256(units * sizeof(uint32_t));
     w.ready = w.att_counters + align256(units * sizeof(uint32_t));
     w.scores = w.ready + align256(units * (size_t)kReadyStride * sizeof(uint32_t));
@@ -314,6 +331,8 @@ static btk_status_t decode_step(const btk_problem_t *problem, const void *q, con
         reinterpret_cast<uint32_t *>(ws + w.att_counters),
         reinterpret_cast<uint32_t *>(ws + w.ready), reinterpret_cast<uint32_t *>(ws + w.queue),
         reinterpret_cast<uint32_t *>(ws + btk::kStealOffset),
+        reinterpret_cast<unsigned long long *>(ws + w.claims), btk::kReadySpinLimit,
+        step_test_flags(),
         reinterpret_cast<uint32_t *>(ws), (hipStream_t)stream, append ? k_new : nullptr,
         append ? v_new : nullptr));
 }

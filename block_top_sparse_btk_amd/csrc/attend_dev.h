@@ -200,9 +200,6 @@ __device__ __forceinline__ uint32_t valid_mask(int v) {
     return v >= kPage ? 0xFFFFu : (1u << v) - 1u;
 }
 
-// Spin bound of the decode step's wait for a unit's scores (~0.1 s).
-constexpr uint32_t kReadySpinLimit = 1u << 22;
-
 // K and V fragments of N blocks (one pipeline stage).
 template <typename F, int N>
 struct Stage {

@@ -140,6 +140,8 @@ AttendPlan plan_attend(const Dims &d, int list_len_max, bool dense);
 //   [0, 256)                   error word; decode-step chunk counter at byte kStealOffset
 //                              and queue words at byte kQueueOffset
 //   shared-prefix flags        kMaxPrefixGroups*Hkv*2 uint32   zero after every call
+//   decode-step claim words    2*kMaxStepGrid*kClaimStride uint64 (the bank the next
+//                              launch uses is zero after every call)
 //   select counters            B*Hkv uint32      zero after every call
 //   attend counters            B*Hkv uint32      zero after every call
 //   ready words                B*Hkv*kReadyStride uint32 (decode step: launch tags)
@@ -150,10 +152,18 @@ AttendPlan plan_attend(const Dims &d, int list_len_max, bool dense);
 // smaller problem on the same workspace then finds zeros where it needs zeros
 // and, where it reads tags, only zeros or tags of earlier launches.
 constexpr int kReadyStride = 32;     // one 128-byte line per unit: each is polled on its own
-constexpr size_t kQueueOffset = 128;  // 4 uint32: spare, exits, launch counter, spare
-constexpr size_t kStealOffset = 64;   // 1 uint32, off the queue words' line
+constexpr size_t kQueueOffset = 128;  // 4 uint32: spare, exits, launch counter, claim bank
+constexpr size_t kStealOffset = 64;   // 1 uint32 (decode-step chunk counter), off the queue line
+// Decode step: share claims, one 64-bit word per workgroup share (a 64-byte line
+// each), in two banks that alternate from launch to launch; grids are capped at
+// kMaxStepGrid workgroups.
+constexpr int kMaxStepGrid = 2048;
+constexpr int kClaimStride = 8;       // 64-bit words
+// Bound of a decode-step wait for a unit's scores (polls, ~0.1 s; a safeguard:
+// every wait ends well before).
+constexpr uint32_t kReadySpinLimit = 1u << 22;
 struct WorkspaceLayout {
-    size_t pflags, sel_counters, att_counters, scores, partials, ready, queue, total;
+    size_t pflags, claims, sel_counters, att_counters, scores, partials, ready, queue, total;
 };
 WorkspaceLayout workspace_layout(const Dims &d, int top_k);
 
@@ -214,7 +224,8 @@ hipError_t launch_decode_step(const Dims &d, const SelectPlan &sp, const AttendP
                               int32_t *indices, float *scores, void *out, float *lse,
                               float *partials, uint32_t *sel_counters, uint32_t *att_counters,
                               uint32_t *ready, uint32_t *queue, uint32_t *steal,
-                              uint32_t *err, hipStream_t stream,
+                              unsigned long long *claims, uint32_t spin_limit,
+                              uint32_t test_flags, uint32_t *err, hipStream_t stream,
                               const void *k_new = nullptr, const void *v_new = nullptr);
 
 }  // namespace btk

@@ -809,34 +809,33 @@ __device__ __forceinline__ bool score_chunk(const SelectArgs &a, int unit, int c
     return arrive_last(&a.counters[unit], (uint32_t)(nchunks + extra), sm.flag);
 }
 
-// Decode step: scores blocks [j0, j1) of unit (b, g) of a sequence of length
-// L with nb blocks (nb < 0: invalid length, one placeholder row that writes -1
-// indices and flags the error) and decode position fp, in runs of up to RUN
-// blocks (sm.pages and sm.sc hold
-// RUN entries; a run costs one round trip for its page ids), then counts the
-// blocks in on the unit's counter.  The segment that completes the unit resets
-// the counter and sets the unit's ready word to `tag`, after every segment's
-// score stores have completed (each waits for its own before counting in).
+// Decode step: scores blocks [j0, j1) of unit (b, g) of a sequence of length L
+// with decode position fp, in runs of up to RUN blocks (sm.pages and sm.sc hold
+// RUN entries; a run costs one round trip for its page ids).  cont: the same
+// workgroup scored this unit's blocks up to j0 just before, so the group's mean
+// query is still in sm.qs and only page ids are loaded.  Ends with the score
+// stores issued (not waited for); the caller counts the blocks in later (see
+// count_in).
 template <typename T, int D, int KU, int RUN, bool APPEND = false>
-__device__ __forceinline__ void score_segment(const SelectArgs &a, int b, int g, int j0, int j1,
-                                              int nb, int L, int fp, ScoreSmem &sm, float *crow,
-                                              uint32_t *ready, uint32_t tag) {
+__device__ __forceinline__ void score_span(const SelectArgs &a, int b, int g, int j0, int j1,
+                                           int L, int fp, bool cont, ScoreSmem &sm,
+                                           float *crow) {
     const int tid = threadIdx.x;
-    const int unit = b * a.Hkv + g;
-    if (nb < 0) {
-        int32_t *out = a.indices + (size_t)unit * a.top_k;
-        for (int i = tid; i < a.top_k; i += kThreads) store_relaxed_i32(out + i, -1);
-        if (tid == 0) flag_error(a.err, kErrSeqLen);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (tid == 0) __hip_atomic_store(ready, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return;
-    }
-    // setup in one round trip: the group's queries, the first run's slice of
-    // the block-table row, the length and the decode position
+    const int32_t *row = a.bt + (size_t)b * a.max_blocks;
+    constexpr int PN = RUN / kThreads;
+    auto load_pages = [&](int s0, int n) {  // all loads in flight together
+        int32_t pv[PN];
+#pragma unroll
+        for (int k = 0; k < PN; ++k) pv[k] = row[s0 + min(k * kThreads + tid, n - 1)];
+#pragma unroll
+        for (int k = 0; k < PN; ++k)
+            if (k * kThreads + tid < n) sm.pages[k * kThreads + tid] = pv[k];
+    };
     int n = min(RUN, j1 - j0);
-    load_setup<T, D, RUN>(a, b, g, j0, n, sm);
-    if constexpr (APPEND) {  // the segment that holds the newest token takes its key
+    // setup in one round trip: (the group's queries and) the first run's page ids
+    if (cont) load_pages(j0, n);
+    else load_setup<T, D, RUN>(a, b, g, j0, n, sm);
+    if constexpr (APPEND) {  // the span that holds the newest token takes its key
         const int jn = (L - 1) / kPage;
         if (j0 <= jn && jn < j1) {
             constexpr int W = D * (int)sizeof(T) / 4;  // 32-bit words per row
@@ -845,9 +844,8 @@ __device__ __forceinline__ void score_segment(const SelectArgs &a, int b, int g,
             for (int i = tid; i < W; i += kThreads) sm.newtok[i] = kr[i];
         }
     }
-    const int32_t *row = a.bt + (size_t)b * a.max_blocks;
     __syncthreads();
-    mean_query<D>(a, sm);
+    if (!cont) mean_query<D>(a, sm);
     for (int s0 = j0;;) {
         check_pages(a, sm, n);
         __syncthreads();
@@ -856,27 +854,57 @@ __device__ __forceinline__ void score_segment(const SelectArgs &a, int b, int g,
         if (s0 >= j1) break;
         n = min(RUN, j1 - s0);
         __syncthreads();  // sm.pages and sm.sc are free again
-        {  // the run's page ids, all loads in flight together
-            constexpr int PN = RUN / kThreads;
-            int32_t pv[PN];
-#pragma unroll
-            for (int k = 0; k < PN; ++k) pv[k] = row[s0 + min(k * kThreads + tid, n - 1)];
-#pragma unroll
-            for (int k = 0; k < PN; ++k)
-                if (k * kThreads + tid < n) sm.pages[k * kThreads + tid] = pv[k];
-        }
+        load_pages(s0, n);
     }
+}
+
+// Decode step: counts cnt freshly scored blocks of unit `unit` (nb blocks) in,
+// once this workgroup's score stores have completed.  The count that completes
+// the unit resets the counter and sets the unit's ready word to `tag`; every
+// other workgroup's stores were complete before it counted in, so a reader
+// that sees the tag sees every score.
+__device__ __forceinline__ void count_in(const SelectArgs &a, int unit, int cnt, int nb,
+                                         uint32_t *ready, uint32_t tag) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (tid == 0) {
-        const uint32_t cnt = (uint32_t)(j1 - j0);
-        const uint32_t prev = __hip_atomic_fetch_add(&a.counters[unit], cnt, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        if (prev + cnt == (uint32_t)nb) {
+    if (threadIdx.x == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(&a.counters[unit], (uint32_t)cnt,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (prev + (uint32_t)cnt == (uint32_t)nb) {
             __hip_atomic_store(&a.counters[unit], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(ready, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
+}
+
+// Decode step: a unit whose length is invalid has a single placeholder row; it
+// writes -1 indices, flags the error and marks the unit ready.
+__device__ __forceinline__ void invalid_unit(const SelectArgs &a, int unit, uint32_t *ready,
+                                             uint32_t tag) {
+    const int tid = threadIdx.x;
+    int32_t *out = a.indices + (size_t)unit * a.top_k;
+    for (int i = tid; i < a.top_k; i += kThreads) store_relaxed_i32(out + i, -1);
+    if (tid == 0) flag_error(a.err, kErrSeqLen);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(ready, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Decode step: scores blocks [j0, j1) of unit (b, g) (a sequence of length L
+// with nb blocks, decode position fp; nb < 0: an invalid length, whose single
+// placeholder row writes -1 indices) and counts them in on the unit's counter;
+// the segment that completes the unit sets its ready word to `tag`.
+template <typename T, int D, int KU, int RUN, bool APPEND = false>
+__device__ __forceinline__ void score_segment(const SelectArgs &a, int b, int g, int j0, int j1,
+                                              int nb, int L, int fp, ScoreSmem &sm, float *crow,
+                                              uint32_t *ready, uint32_t tag) {
+    const int unit = b * a.Hkv + g;
+    if (nb < 0) {
+        invalid_unit(a, unit, ready, tag);
+        return;
+    }
+    score_span<T, D, KU, RUN, APPEND>(a, b, g, j0, j1, L, fp, false, sm, crow);
+    count_in(a, unit, j1 - j0, nb, ready, tag);
 }
 
 }  // namespace sel

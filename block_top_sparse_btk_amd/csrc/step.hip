@@ -14,22 +14,34 @@
 // segment then adds its block count to the unit's counter, and the segment that
 // completes the unit marks it ready with the launch's tag.
 //
+// Every share is claimed before it is scored (one atomic per share, issued with
+// the prologue's loads, so its round trip costs nothing): by its own workgroup
+// when that one starts, or else by workgroup 0 or a workgroup that holds no
+// phase-2 item, which look for unclaimed shares once their own scoring is done.
+// Workgroup 0 is dispatched before any other, so every share is claimed by a
+// running workgroup, and every slice of the scan is done without waiting: a
+// phase-2 wait therefore always ends, whether or not the whole grid is
+// resident (another kernel may hold part of the device).
+//
 // Phase 2, selection and attention.  Item (unit, split) i is taken by
-// workgroup i mod G.  It waits (bounded spin, never expected to be long) until
-// its unit is ready, selects the unit's top-k blocks from the stored scores
-// (S3), keeps its split's share of the selection in LDS and attends (S4).  Each
-// split of a unit selects for itself (identical results), split 0 also writes
-// the indices.  Scoring never waits and a workgroup ends its scoring (share and
-// chunks, until none is left) before it takes an item, so every wait ends.
+// workgroup i mod G.  It waits (bounded spin, as a safeguard only) until its
+// unit is ready, selects the unit's top-k blocks from the stored scores (S3),
+// keeps its split's share of the selection in LDS and attends (S4).  Each split
+// of a unit selects for itself (identical results), split 0 also writes the
+// indices.
 //
 // Handing out all scoring work in dynamic chunks was measured slower: the last
 // chunks to be handed out run at a fair share of the bandwidth next to the
-// attention of earlier units and set the end of the launch.
+// attention of earlier units and set the end of the launch.  So was claiming
+// the shares in small slices that idle workgroups could take from slow ones
+// (every claim and every extra segment is a round trip, several microseconds
+// while the scan saturates the memory system).
 //
 // The launch tag is one more than a launch counter kept in the queue words; the
 // last workgroup to leave advances the counter (skipping the value whose
 // successor would be 0, so that a tag is never 0 and two launches in a row never
-// share one) and re-arms the chunk counter and the queue words.
+// share one), re-arms the chunk counter and flips the bank of share claims the
+// next launch uses; each launch clears the other bank while it runs.
 #include "attend_dev.h"
 #include "select_dev.h"
 
@@ -45,6 +57,10 @@ struct StepArgs {
     uint32_t *ready;  // [units * kReadyStride]: word u * kReadyStride is unit u's ready tag
     uint32_t *queue;  // [0] spare, [1] workgroups that have left, [2] launch counter
     uint32_t *steal;  // scan chunks taken (a line of its own)
+    unsigned long long *claims;  // [2][kMaxStepGrid * kClaimStride]: a share is taken when
+                                 // its word's low 32 bits go from 0 to 1
+    uint32_t spin_limit;         // bound of a phase-2 wait (polls)
+    uint32_t test_flags;         // bit 0: owners leave their shares unclaimed (tests only)
     int B, units, nsplit;
 };
 
@@ -120,8 +136,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
     __shared__ uint32_t rows[kMaxStepBatch + 1];  // centroid rows before each sequence
     __shared__ int lens[kMaxStepBatch];           // sequence lengths, -1: invalid
     __shared__ int fps[kMaxStepBatch];            // decode positions (first touched token)
-    __shared__ int item_s;
-    __shared__ uint32_t tag_s;
+    __shared__ int item_s, owns_s;
+    __shared__ uint32_t tag_s, bank_s;
     // queries while scoring, top-k keys of long contexts, attention merges
     extern __shared__ float dyn[];
     sel::ScoreSmem sm{dyn, qs, pages, sc_lds, &flag, newtok};
@@ -129,11 +145,25 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
     const int tid = threadIdx.x;
     const int Hkv = a.s.Hkv;
 
-    // the launch tag is fetched while the row prefix is built: per unit
-    // kSegmentCost charged rows, then one row per block (a single placeholder
-    // row for an invalid length, which writes -1 indices and flags the error)
-    if (tid == 0)
-        tag_s = __hip_atomic_load(&a.queue[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    // Thread 0 fetches the launch tag and the claim bank and, in the same round
+    // trip, claims this workgroup's share in both banks (the bank is not known
+    // yet); its word in the bank this launch does not use is cleared again
+    // afterwards, so that the next launch finds it at zero.  Meanwhile the row
+    // prefix is built: per unit kSegmentCost charged rows, then one row per
+    // block (a single placeholder row for an invalid length, which writes -1
+    // indices and flags the error).
+    unsigned long long *const mine = a.claims + (size_t)blockIdx.x * kClaimStride;
+    unsigned long long own0 = 1ull, own1 = 1ull;
+    uint32_t tag0 = 0u, bank0 = 0u;
+    if (tid == 0) {
+        tag0 = __hip_atomic_load(&a.queue[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        bank0 = __hip_atomic_load(&a.queue[3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!(a.test_flags & 1u)) {
+            own0 = __hip_atomic_fetch_add(mine, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            own1 = __hip_atomic_fetch_add(mine + (size_t)kMaxStepGrid * kClaimStride, 1ull,
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
     for (int b0 = 0; b0 < a.B; b0 += kThreads) {
         const int b = b0 + tid;
         uint32_t n = 0;
@@ -152,26 +182,80 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
         if (b0 == 0 && tid == 0) rows[0] = 0u;
         __syncthreads();
     }
-    const uint32_t tag = tag_s;
+    if (tid == 0) {
+        const uint32_t bank = bank0 & 1u;
+        tag_s = tag0 + 1u;
+        bank_s = bank;
+        owns_s = (bank ? own1 : own0) == 0ull;
+        // this workgroup's word of the other bank (no other workgroup touches it)
+        __hip_atomic_store(mine + (size_t)(bank ^ 1u) * kMaxStepGrid * kClaimStride, 0ull,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    const uint32_t tag = tag_s, bank = bank_s;
+    unsigned long long *claims = a.claims + (size_t)bank * kMaxStepGrid * kClaimStride;
+    {  // the other bank's words that no workgroup of this grid owns
+        unsigned long long *other = a.claims + (size_t)(bank ^ 1u) * kMaxStepGrid * kClaimStride;
+        for (uint32_t w = gridDim.x + blockIdx.x * kThreads + tid; w < (uint32_t)kMaxStepGrid;
+             w += gridDim.x * kThreads)
+            __hip_atomic_store(other + (size_t)w * kClaimStride, 0ull, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const int total = a.units * a.nsplit;  // phase-2 items
 
-    // ---- phase 1: this workgroup's static share of the first rows, then chunks
-    // of the rest while any are left (shares end at different times: the
-    // workgroups that finish first take more of the rest)
+    // ---- phase 1: this workgroup's static share of the first rows (if it
+    // claimed it), then chunks of the rest while any are left (shares end at
+    // different times: the workgroups that finish first take more of the rest),
+    // then, in a workgroup that holds no phase-2 item, any share still unclaimed
     const uint64_t R = rows[a.B];
     const uint64_t RS = R - R / kStealFrac;
-    uint32_t r = (uint32_t)(RS * blockIdx.x / gridDim.x);
-    uint32_t r1 = (uint32_t)(RS * (blockIdx.x + 1) / gridDim.x);
+    uint32_t r = 0, r1 = 0;
+    if (owns_s) {
+        r = (uint32_t)(RS * blockIdx.x / gridDim.x);
+        r1 = (uint32_t)(RS * (blockIdx.x + 1) / gridDim.x);
+    }
+    bool chunks_left = true;
     int b = 0;
     for (;;) {
-        if (r >= r1) {
+        if (r >= r1 && chunks_left) {
             if (tid == 0) item_s = (int)atomicAdd(a.steal, 1u);
             __syncthreads();
             const uint64_t c0 = RS + (uint64_t)item_s * kStealRows;
             __syncthreads();  // item_s is written again
-            if (c0 >= R) break;
-            r = (uint32_t)c0;
-            r1 = (uint32_t)min(R, c0 + kStealRows);
+            if (c0 < R) {
+                r = (uint32_t)c0;
+                r1 = (uint32_t)min(R, c0 + kStealRows);
+            } else {
+                chunks_left = false;
+            }
         }
+        if (r >= r1) {
+            if ((int)blockIdx.x < total && blockIdx.x != 0) break;
+            // workgroup 0, or one without items: take a share whose workgroup has
+            // not started (the
+            // lowest unclaimed one; thread 0 claims it, another look if that fails)
+            if (tid == 0) item_s = 0x7fffffff;
+            __syncthreads();
+            for (uint32_t v = tid; v < gridDim.x; v += kThreads)
+                if (__hip_atomic_load(claims + (size_t)v * kClaimStride, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT) == 0ull)
+                    atomicMin(&item_s, (int)v);
+            __syncthreads();
+            if (tid == 0 && item_s != 0x7fffffff &&
+                __hip_atomic_fetch_add(claims + (size_t)item_s * kClaimStride, 1ull,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0ull)
+                item_s = -2;  // taken meanwhile: look again
+            __syncthreads();
+            const int v = item_s;
+            __syncthreads();  // item_s is written again
+            if (v == -2) continue;
+            if (v == 0x7fffffff) break;
+            r = (uint32_t)(RS * (uint32_t)v / gridDim.x);
+            r1 = (uint32_t)(RS * ((uint32_t)v + 1) / gridDim.x);
+            b = 0;
+            continue;
+        }
+        if (rows[b] > r) b = 0;
         while (rows[b + 1] <= r) ++b;
         const int nb = lens[b] < 0 ? -1 : (lens[b] + kPage - 1) / kPage;
         const uint32_t per_unit = kSegmentCost + (nb < 0 ? 1u : (uint32_t)nb);
@@ -190,7 +274,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
     }
 
     // ---- phase 2: (unit, split) items
-    const int total = a.units * a.nsplit;
     int32_t *list = reinterpret_cast<int32_t *>(sc_lds);  // the split's share, <= 256 entries
     // item i goes to workgroup i mod G: with fewer items than resident
     // workgroups the first G/2 take one each, one per CU (workgroups are
@@ -219,7 +302,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
             const uint32_t *rw = a.ready + (size_t)unit * kReadyStride;
             uint32_t spins = 0;
             while (__hip_atomic_load(rw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != tag) {
-                if (++spins > att::kReadySpinLimit) {  // never expected: report, do not hang
+                if (++spins > a.spin_limit) {  // never expected: report, do not hang
                     flag_error(a.s.err, kErrTimeout);
                     break;
                 }
@@ -250,12 +333,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
             a.t, unit, split, dyn, &flag, list, L < 0 ? 0 : L, row_lds ? pages : nullptr);
         __syncthreads();  // LDS is reused by the next item
     }
-    // the last workgroup to leave re-arms the queue and advances the counter
+    // the last workgroup to leave re-arms the queue, flips the claim bank and
+    // advances the counter
     if (tid == 0) {
         const uint32_t prev = atomicAdd(&a.queue[1], 1u);
         if (prev == gridDim.x - 1) {
             __hip_atomic_store(&a.queue[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(a.steal, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.queue[3], bank ^ 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(&a.queue[2], tag == 0xffffffffu ? 0u : tag, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -292,6 +377,7 @@ hipError_t resident_workgroups(size_t lds, int *out) {
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     cached[slot][0] = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
+    if (cached[slot][0] > kMaxStepGrid) cached[slot][0] = kMaxStepGrid;
     cached[slot][1] = (int)lds;
     *out = cached[slot][0];
     return hipSuccess;
@@ -331,8 +417,9 @@ hipError_t launch_decode_step(const Dims &d, const SelectPlan &sp, const AttendP
                               int32_t *indices, float *scores, void *out, float *lse,
                               float *partials, uint32_t *sel_counters, uint32_t *att_counters,
                               uint32_t *ready, uint32_t *queue, uint32_t *steal,
-                              uint32_t *err, hipStream_t stream, const void *k_new,
-                              const void *v_new) {
+                              unsigned long long *claims, uint32_t spin_limit,
+                              uint32_t test_flags, uint32_t *err, hipStream_t stream,
+                              const void *k_new, const void *v_new) {
     // a split's share of the selection (at most 4 * 64 entries) is kept in the
     // score staging area
     if (ap.bps > kRun) return hipErrorInvalidValue;
@@ -353,6 +440,9 @@ hipError_t launch_decode_step(const Dims &d, const SelectPlan &sp, const AttendP
     a.ready = ready;
     a.queue = queue;
     a.steal = steal;
+    a.claims = claims;
+    a.spin_limit = spin_limit;
+    a.test_flags = test_flags;
     a.B = d.B;
     a.units = d.B * d.Hkv;
     a.nsplit = ap.nsplit_max;

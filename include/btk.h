@@ -24,9 +24,11 @@
  *    an out-of-range page id, length or index is skipped, and, where the call
  *    has a workspace, sets a sticky bit in workspace word 0 (bit 0: a length
  *    outside [1, max_blocks_per_seq * page_size]; bit 1: a page id outside
- *    [0, num_pages); bit 2: a block index outside [0, n_b); bit 3: a wait for data
- *    published inside a launch gave up, which no valid call is expected to reach;
- *    bit 4: a declared shared prefix differs between group members).
+ *    [0, num_pages); bit 2: a block index outside [0, n_b); bit 3: a bounded wait
+ *    for data published inside a launch gave up, a safeguard that no call is
+ *    expected to reach (every such wait ends once the work it waits for, which is
+ *    never held by a workgroup that has not started, is done); bit 4: a declared
+ *    shared prefix differs between group members).
  *    Results for such inputs are unspecified.
  *
  * Notation: B = batch, Hq / Hkv = query / KV heads, r = Hq / Hkv (the query
@@ -238,7 +240,13 @@ btk_status_t btk_token_topk_attend(const btk_problem_t *problem, const void *q,
  * those three calls.  A persistent kernel first scores every centroid row (each
  * workgroup a share of the rows, the last rows handed out in chunks to the
  * workgroups that finish first), then each (sequence, KV head) selects and
- * attends once its scores are complete.
+ * attends once its scores are complete.  Every share is claimed before it is
+ * scored, by its own workgroup or, if that one has not started, by one that has
+ * finished its own scoring, so the call does not need its whole grid to be
+ * resident: beside other kernels (other streams or processes) it is slower, not
+ * wrong.  (Test hook: with the environment variable BTK_STEP_TEST_FLAGS=1 at the
+ * call, every workgroup leaves its own share to be taken over; results are the
+ * same.)
  * (Pith review, "What carries the argument"; the single-launch form is this
  * library's own design.)
  *   centroids  in/out   indices out [B][Hkv][top_k]   out/lse out as btk_sparse_attend
