@@ -150,7 +150,7 @@ __global__ __launch_bounds__(kThreads, SHARED ? 4 : 5) void select_kernel(Select
     __shared__ uint32_t red[2 * kWaves];
     __shared__ int scan_red[kWaves];
     __shared__ int flags[SHARED ? kMaxGroupMembers + 1 : 1];
-    extern __shared__ uint32_t keys[];  // max_blocks words, long contexts only
+    extern __shared__ uint32_t keys[];  // 512 words: top-k bitmaps beyond 2048 blocks
     ScoreSmem sm{qraw, qs, pages, sc_lds, &is_last};
     TopkSmem tk{hist, cand, red, scan_red, keys};
     int item = blockIdx.x;
@@ -217,8 +217,8 @@ template <typename T, int D>
 hipError_t launch(const Dims &d, const SelectPlan &plan, SelectArgs a, const PrefixGroups *pg,
                   hipStream_t stream) {
     const size_t grid = (size_t)d.B * d.Hkv * plan.nchunk_max;
-    // LDS key copy only for the workgroup-wide selection of long contexts
-    const size_t lds = d.max_blocks > 32 * kWave ? sizeof(uint32_t) * (size_t)d.max_blocks : 0;
+    // the top-k bitmaps of more than 2048 blocks (two words per 32 blocks)
+    const size_t lds = d.max_blocks > 32 * kWave ? sizeof(uint32_t) * 512 : 0;
     if (pg)
         hipLaunchKernelGGL((select_kernel<T, D, true>), dim3((unsigned)(grid + pg->item0[pg->n])),
                            dim3(kThreads), lds, stream, a, *pg);

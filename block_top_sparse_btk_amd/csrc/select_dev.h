@@ -78,7 +78,7 @@ struct TopkSmem {
     uint32_t *cand;      // [256] compacted candidates
     uint32_t *red;       // [2 * kWaves]
     int *scan_red;       // [kWaves]
-    uint32_t *keys;      // [max_blocks] keys, workgroup-wide path only
+    uint32_t *keys;      // bitmaps of more than 2048 blocks: [16 * KMAX] words
 };
 
 // Where a selection goes: the caller's index row (or NULL) and, inside a
@@ -307,22 +307,34 @@ __device__ __forceinline__ void finish_from_cand(uint32_t *cand, int m, uint32_t
 }
 
 // Writes the winners in ascending block order, by one wave: lane l holds the
-// bitmap words a (keys above T) and e (keys equal to T) of blocks [32l, 32l+32);
-// every key above T is kept, then keys equal to T in block order until take_eq.
-__device__ __forceinline__ void write_winners(uint32_t a, uint32_t e, int take_eq, int kb,
-                                              int top_k, const TopkOut &out, int lane) {
-    int e_before = (int)(wave_inclusive_scan((uint32_t)__popc(e)) - (uint32_t)__popc(e));
-    while (e && e_before < take_eq) {  // lowest-index equal keys first
-        const uint32_t bit = e & (0u - e);
-        a |= bit;
-        e ^= bit;
-        ++e_before;
+// NW bitmap words a[w] (keys above T) and e[w] (keys equal to T) of blocks
+// [32 (NW l + w), 32 (NW l + w) + 32); every key above T is kept, then keys
+// equal to T in block order until take_eq.
+template <int NW>
+__device__ __forceinline__ void write_winners(uint32_t (&a)[NW], uint32_t (&e)[NW], int take_eq,
+                                              int kb, int top_k, const TopkOut &out, int lane) {
+    uint32_t ecnt = 0u, acnt = 0u;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) ecnt += (uint32_t)__popc(e[w]);
+    int e_before = (int)(wave_inclusive_scan(ecnt) - ecnt);
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        while (e[w] && e_before < take_eq) {  // lowest-index equal keys first
+            const uint32_t bit = e[w] & (0u - e[w]);
+            a[w] |= bit;
+            e[w] ^= bit;
+            ++e_before;
+        }
+        acnt += (uint32_t)__popc(a[w]);
     }
-    int pos = (int)(wave_inclusive_scan((uint32_t)__popc(a)) - (uint32_t)__popc(a));
-    while (a) {
-        if (pos < kb) out.put(pos, lane * 32 + __builtin_ctz(a));
-        ++pos;
-        a &= a - 1u;
+    int pos = (int)(wave_inclusive_scan(acnt) - acnt);
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        while (a[w]) {
+            if (pos < kb) out.put(pos, (NW * lane + w) * 32 + __builtin_ctz(a[w]));
+            ++pos;
+            a[w] &= a[w] - 1u;
+        }
     }
     for (int i = kb + lane; i < top_k; i += kWave) out.put(i, -1);
 }
@@ -372,20 +384,20 @@ __device__ __forceinline__ void select_topk_wave(const Src &src, int nb, int top
     const uint32_t T = lo;
     // bitmaps: lane l's words cover blocks [32l, 32l + 32), the low or high
     // half of slot l/2's ballot (lanes from 2*KMAX on hold none)
-    uint32_t a = 0u, e = 0u;
+    uint32_t a[1] = {0u}, e[1] = {0u};
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) {
         const uint64_t ab = __ballot(key[i] > T);
         const uint64_t eb = __ballot(key[i] == T);  // absent keys are 0 < T
         if ((lane >> 1) == i) {
-            a = (lane & 1) ? (uint32_t)(ab >> 32) : (uint32_t)ab;
-            e = (lane & 1) ? (uint32_t)(eb >> 32) : (uint32_t)eb;
+            a[0] = (lane & 1) ? (uint32_t)(ab >> 32) : (uint32_t)ab;
+            e[0] = (lane & 1) ? (uint32_t)(eb >> 32) : (uint32_t)eb;
         }
     }
-    write_winners(a, e, need, kb, top_k, out, lane);
+    write_winners<1>(a, e, need, kb, top_k, out, lane);
 }
 
-// Top-k of a unit's nb <= 256 * KMAX <= 2048 scores by the four waves of the
+// Top-k of a unit's nb <= 256 * KMAX <= 8192 scores by the four waves of the
 // workgroup.  Thread t holds the keys of blocks i*256 + t.  The radix passes of
 // select_topk_wave run over the workgroup, each into its own LDS histogram (all
 // of them cleared while the keys are in flight), so that a pass costs a single
@@ -397,12 +409,17 @@ __device__ __forceinline__ void select_topk_wave(const Src &src, int nb, int top
 // for kb <= 64, the smallest of the largest keys of a wave's first kb lanes
 // (kb keys lie at or above it), the largest of these over the waves.  Bitmaps
 // come from per-wave ballots: slot i of wave v covers blocks 256i + 64v .. +63,
-// words 8i + 2v and 8i + 2v + 1.
+// words 8i + 2v and 8i + 2v + 1; they are gathered in LDS (cand up to 2048
+// blocks, the key area beyond) and wave 0 writes the winners, KMAX / 8 words
+// per lane.
 template <int KMAX, typename Src>
 __device__ __forceinline__ void select_topk_wg4(const Src &src, int nb, int top_k,
                                                 const TopkOut &out, TopkSmem &sm) {
-    static_assert(KMAX <= 8, "64 bitmap words cover 2048 blocks");
-    uint32_t *cand = sm.cand, *red = sm.red;
+    static_assert(KMAX == 4 || KMAX == 8 || KMAX == 16 || KMAX == 32, "8 KMAX bitmap words");
+    constexpr int NW = KMAX <= 8 ? 1 : KMAX / 8;  // bitmap words per lane of wave 0
+    constexpr int NWORDS = 8 * KMAX;
+    uint32_t *red = sm.red;
+    uint32_t *bm = KMAX <= 8 ? sm.cand : sm.keys;  // [0, NWORDS) above T, then equal
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int kb = min(top_k, nb);
     for (int i = tid; i < kTopkPasses * kHistWords / 4; i += kThreads)
@@ -452,105 +469,35 @@ __device__ __forceinline__ void select_topk_wg4(const Src &src, int nb, int top_
         }
     }
     const uint32_t T = lo;  // need: the keys equal to T to keep
-    // bitmaps through LDS: above in cand[0..64), equal in cand[64..128)
+    // bitmaps through LDS: above in bm[0 .. NWORDS), equal in bm[NWORDS .. 2 NWORDS)
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) {
         const uint64_t ab = __ballot(key[i] > T);
         const uint64_t eb = __ballot(key[i] == T);  // absent keys are 0 < T
         if (lane == 0) {
-            cand[8 * i + 2 * wave] = (uint32_t)ab;
-            cand[8 * i + 2 * wave + 1] = (uint32_t)(ab >> 32);
-            cand[64 + 8 * i + 2 * wave] = (uint32_t)eb;
-            cand[64 + 8 * i + 2 * wave + 1] = (uint32_t)(eb >> 32);
+            bm[8 * i + 2 * wave] = (uint32_t)ab;
+            bm[8 * i + 2 * wave + 1] = (uint32_t)(ab >> 32);
+            bm[NWORDS + 8 * i + 2 * wave] = (uint32_t)eb;
+            bm[NWORDS + 8 * i + 2 * wave + 1] = (uint32_t)(eb >> 32);
         }
     }
     __syncthreads();
     if (wave == 0) {
-        const uint32_t a = lane < 8 * KMAX ? cand[lane] : 0u;
-        const uint32_t e = lane < 8 * KMAX ? cand[64 + lane] : 0u;
-        write_winners(a, e, need, kb, top_k, out, lane);
-    }
-}
-
-// Top-k of a unit's nb scores by the whole workgroup.  Thread t holds the keys
-// of blocks i*256 + t in registers (at most KMAX each) for counting, and a
-// copy goes to LDS for the ordered passes.  The kb-th largest key T is found by
-// bisection over the 32-bit key space: every thread counts its keys at or above
-// the probe with plain compares, a DPP wave sum and one barrier give the total.
-// Then every key above T is kept plus the lowest-index keys equal to T; thread t
-// walks blocks [t*R, t*R + R) so that thread order is block order, and two
-// workgroup prefix sums place the winners in ascending order.
-template <int KMAX, typename Src>
-__device__ __forceinline__ void select_topk_wg(const Src &src, int nb, int top_k,
-                                               const TopkOut &out, TopkSmem &sm) {
-    uint32_t *red = sm.red, *keys_lds = sm.keys;
-    int *scan_red = sm.scan_red;
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const int kb = min(top_k, nb);
-    uint32_t key[KMAX];
-    src.fill(key, tid, kThreads, nb);
-    uint32_t tmax = 0u;
+        uint32_t a[NW], e[NW];
 #pragma unroll
-    for (int i = 0; i < KMAX; ++i) {
-        const int j = i * kThreads + tid;
-        if (j < nb) {
-            key[i] = score_key(__uint_as_float(key[i]));
-            keys_lds[j] = key[i];
-        } else {
-            key[i] = 0u;  // no key
+        for (int w = 0; w < NW; ++w) {
+            const int word = NW * lane + w;
+            a[w] = word < NWORDS ? bm[word] : 0u;
+            e[w] = word < NWORDS ? bm[NWORDS + word] : 0u;
         }
-        tmax = max(tmax, key[i]);
+        write_winners<NW>(a, e, need, kb, top_k, out, lane);
     }
-    int parity = 0;
-    auto wg_total = [&](uint32_t wave_value, bool take_max) {
-        if (lane == 0) red[parity * kWaves + wave] = wave_value;
-        __syncthreads();
-        uint32_t v = red[parity * kWaves];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) {
-            const uint32_t x = red[parity * kWaves + w];
-            v = take_max ? max(v, x) : v + x;
-        }
-        parity ^= 1;
-        return v;
-    };
-    auto count_ge = [&](uint32_t t) {
-        uint32_t c = 0;
-#pragma unroll
-        for (int i = 0; i < KMAX; ++i) c += key[i] >= t ? 1u : 0u;  // absent keys are 0 < t
-        return (int)wg_total(wave_sum_u32(c), false);
-    };
-    // largest T in [1, max key] with #{key >= T} >= kb (valid keys are >= 1)
-    uint32_t lo = 1u, hi = wg_total(wave_max_u32(tmax), true);
-    while (lo < hi) {
-        const uint32_t mid = lo + (uint32_t)(((uint64_t)hi - lo + 1) >> 1);
-        if (count_ge(mid) >= kb) lo = mid;
-        else hi = mid - 1;
-    }
-    const uint32_t T = lo;
-    const int gt = T == 0xffffffffu ? 0 : count_ge(T + 1);
-    const int take_eq = kb - gt;  // keys equal to T to keep, lowest index first
-    const int R = (nb + kThreads - 1) / kThreads;
-    const int j0 = tid * R, j1 = min(nb, j0 + R);
-    int my_eq = 0;
-    for (int j = j0; j < j1; ++j) my_eq += keys_lds[j] == T ? 1 : 0;
-    const int eq_before = wg_exclusive_scan(my_eq, scan_red);
-    int my_sel = 0;
-    for (int j = j0, e = eq_before; j < j1; ++j) {
-        const uint32_t k = keys_lds[j];
-        if (k > T || (k == T && e++ < take_eq)) ++my_sel;
-    }
-    int pos = wg_exclusive_scan(my_sel, scan_red);
-    for (int j = j0, e = eq_before; j < j1; ++j) {
-        const uint32_t k = keys_lds[j];
-        if ((k > T || (k == T && e++ < take_eq)) && pos < kb) out.put(pos++, j);
-    }
-    for (int i = kb + tid; i < top_k; i += kThreads) out.put(i, -1);
 }
 
 // Selection of a unit's top-k blocks by a whole workgroup: one wave up to 256
-// blocks (no barrier), the four waves up to 2048 (radix passes over one shared
-// histogram), a bisection over the key space beyond.
+// blocks (no barrier), the four waves beyond (radix passes, a histogram each;
+// the bitmaps of more than 2048 blocks go through the key area of TopkSmem,
+// which then holds at least 16 * KMAX words).
 template <typename Src>
 __device__ __forceinline__ void select_topk(const Src &src, int nb, int top_k,
                                             const TopkOut &out, TopkSmem &sm) {
@@ -559,14 +506,11 @@ __device__ __forceinline__ void select_topk(const Src &src, int nb, int top_k,
         for (int i = tid; i < top_k; i += kThreads) out.put(i, i < nb ? i : -1);
         return;
     }
-    if (nb > 32 * kWave) {
-        if (nb <= 16 * kThreads) select_topk_wg<16>(src, nb, top_k, out, sm);
-        else select_topk_wg<32>(src, nb, top_k, out, sm);
-        return;
-    }
-    if (nb > 4 * kWave) {  // the whole workgroup, up to eight keys per thread
+    if (nb > 4 * kWave) {  // the whole workgroup, up to 32 keys per thread
         if (nb <= 4 * kThreads) select_topk_wg4<4>(src, nb, top_k, out, sm);
-        else select_topk_wg4<8>(src, nb, top_k, out, sm);
+        else if (nb <= 8 * kThreads) select_topk_wg4<8>(src, nb, top_k, out, sm);
+        else if (nb <= 16 * kThreads) select_topk_wg4<16>(src, nb, top_k, out, sm);
+        else select_topk_wg4<32>(src, nb, top_k, out, sm);
         return;
     }
     if (tid >= kWave) return;

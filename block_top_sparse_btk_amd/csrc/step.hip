@@ -79,11 +79,20 @@ constexpr int kRun = 2048;       // blocks per scan run: shares (~550 blocks at 
 // on uniform-length batches of 64 to 512 units: 160 -> 520 rows shortened the
 // ragged steps by 1.4-2.8 us and left the others equal or faster; from about
 // 700 rows on the ragged steps got slower again.
-constexpr int kSegmentCost = 520;
+#ifndef BTK_STEP_SEGMENT_COST
+#define BTK_STEP_SEGMENT_COST 520
+#endif
+constexpr int kSegmentCost = BTK_STEP_SEGMENT_COST;
 // The last 1/kStealFrac of the rows is handed out in chunks of kStealRows to the
 // workgroups that finish their static share first.
-constexpr int kStealFrac = 8;
-constexpr uint32_t kStealRows = 256;
+#ifndef BTK_STEP_STEAL_FRAC
+#define BTK_STEP_STEAL_FRAC 8
+#endif
+#ifndef BTK_STEP_STEAL_ROWS
+#define BTK_STEP_STEAL_ROWS 256
+#endif
+constexpr int kStealFrac = BTK_STEP_STEAL_FRAC;
+constexpr uint32_t kStealRows = BTK_STEP_STEAL_ROWS;
 
 // KV append (APPEND): the newest token of unit (b, g), position L - 1, goes
 // into slot (L - 1) % 16 of its page in both caches.  Phase 1 takes its key
@@ -354,7 +363,7 @@ size_t step_lds_floats(const Dims &d, const AttendPlan &ap) {
     const size_t split_merge = 2 * (size_t)ap.nsplit_max * r + r;
     n = n > wave_merge ? n : wave_merge;
     n = n > split_merge ? n : split_merge;
-    if (d.max_blocks > 32 * kWave && (size_t)d.max_blocks > n) n = d.max_blocks;  // top-k keys
+    if (d.max_blocks > 32 * kWave && n < 512) n = 512;  // top-k bitmaps beyond 2048 blocks
     return n;
 }
 
