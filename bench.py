@@ -150,6 +150,166 @@ def _cpu_baseline(bt, seconds: float):
                       f"{oracle.max_threads()} threads"}
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_rates(bt, seconds: float):
+    """The oracle's sparse step on the host: all threads on the whole batch for
+    about `seconds`, and one thread on one sequence (all its KV heads), both as
+    query-tokens/s of the whole batch's step."""
+    import torch
+    import oracle
+
+    first = (bt.seq_lens - 1).to(torch.int32)
+    cents = oracle.centroids(bt.k_cache, bt.block_table, bt.seq_lens)
+    threads = oracle.max_threads()
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.sparse_step(bt.q, bt.k_cache, bt.v_cache, bt.block_table, bt.seq_lens, bt.top_k,
+                           cents=cents, first_pos=first)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    all_rate = bt.batch * steps / el
+    oracle.set_threads(1)
+    try:
+        n1, t0 = 0, time.perf_counter()
+        while True:
+            b = n1 % bt.batch
+            oracle.sparse_step(bt.q[b:b + 1], bt.k_cache, bt.v_cache, bt.block_table[b:b + 1],
+                               bt.seq_lens[b:b + 1], bt.top_k, cents=cents,
+                               first_pos=first[b:b + 1])
+            n1 += 1
+            el1 = time.perf_counter() - t0
+            if el1 >= seconds / 2 and n1 >= 1:
+                break
+    finally:
+        oracle.set_threads(threads)
+    return {"value": round(all_rate, 1), "unit": "query-tokens/s", "cores": threads,
+            "kind": "oracle", "cpu_model": _cpu_model(),
+            "sample": f"{steps} full steps of the batch in {el:.1f} s on {threads} threads",
+            "one_thread": {"value": round(n1 / el1, 2), "unit": "query-tokens/s", "cores": 1,
+                           "sample": f"{n1} one-sequence steps (all KV heads) in {el1:.1f} s"}}
+
+
+def _pcts(xs):
+    xs = sorted(xs)
+    pick = lambda q: xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]  # noqa: E731
+    return {"p10": round(pick(0.1), 3), "p50": round(pick(0.5), 3), "p90": round(pick(0.9), 3)}
+
+
+def measure_workload(name, bt, dev, steps, cpu_seconds, replicas=None):
+    """One workload's line: the single-launch step and the dense kernel on the same
+    inputs (rotating replicas, HIP events on the library's stream), algorithmic
+    bytes, roofline fraction, bytes per token, p10/p50/p90 of batch averages, the
+    oracle on the host."""
+    import torch
+
+    import block_top_sparse_btk_amd as btk
+
+    B, hq, hkv, D, k = bt.batch, bt.num_q_heads, bt.num_kv_heads, bt.head_dim, bt.top_k
+    e = 2 if bt.dtype == torch.bfloat16 else 4
+    nb0 = algorithmic_bytes(bt.seq_lens.tolist(), hq, hkv, D, k, e)
+    if replicas is None:  # enough copies that consecutive steps miss the last-level cache
+        replicas = max(2, min(16, -(-600_000_000 // max(1, nb0["step"]))))
+    lib = btk._lib()
+    stream = torch.cuda.current_stream(dev)
+    hs = stream.cuda_stream
+    base = bt.to(dev)
+    prob = btk.make_problem(base.q, base.k_cache, base.block_table)
+    first = (base.seq_lens - 1).to(torch.int32)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    reps = []
+    for i in range(replicas):
+        d = base if i == 0 else bt.to(dev)
+        cent = torch.zeros((bt.num_pages, hkv, D), dtype=torch.float32, device=dev)
+        btk.btk_centroid_update(d.k_cache, d.block_table, d.seq_lens, cent, problem=prob)
+        ws = btk.new_workspace(prob, k, dev)
+        idx = torch.empty((B, hkv, k), dtype=torch.int32, device=dev)
+        out, dout = torch.empty_like(d.q), torch.empty_like(d.q)
+        reps.append(dict(d=d, ws=ws, idx=idx, out=out, keep=(cent, dout),
+                         step=(ctypes.byref(prob), p(d.q), p(d.k_cache), p(d.v_cache),
+                               p(d.block_table), p(d.seq_lens), p(first), p(cent), k, p(idx),
+                               p(out), None, p(ws), ws.numel(), hs),
+                         den=(ctypes.byref(prob), p(d.q), p(d.k_cache), p(d.v_cache),
+                              p(d.block_table), p(d.seq_lens), p(dout), None, p(ws), ws.numel(),
+                              hs)))
+    torch.cuda.synchronize()
+
+    def check(st):
+        if st:
+            raise RuntimeError(f"{name}: library call failed: {lib.btk_status_string(st).decode()}")
+
+    def timed(fn_name, key, n, batch):
+        f = getattr(lib, fn_name)
+        for i in range(10):
+            check(f(*reps[i % replicas][key]))
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(max(1, n // batch))]
+        i = 0
+        for e0, e1 in evs:
+            e0.record(stream)
+            for _ in range(batch):
+                check(f(*reps[i % replicas][key]))
+                i += 1
+            e1.record(stream)
+        torch.cuda.synchronize()
+        per = [1e3 * e0.elapsed_time(e1) / batch for e0, e1 in evs]
+        return sum(per) / len(per), per
+
+    step_us, step_per = timed("btk_decode_step", "step", steps, 10)
+    dense_us, dense_per = timed("btk_dense_attend", "den", max(10, steps // 5), 5)
+    for r in reps:
+        if btk.workspace_error_bits(r["ws"]):
+            raise RuntimeError(f"{name}: device-side input guard fired")
+    nb = algorithmic_bytes(bt.seq_lens.tolist(), hq, hkv, D, k, e,
+                           sel_tokens=selected_tokens(reps[0]["idx"].cpu(), bt.seq_lens))
+    gbps = nb["step"] / (step_us * 1e-6) / 1e9
+    dgbps = nb["dense"] / (dense_us * 1e-6) / 1e9
+    res = {"workload": name, "batch": B, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": D,
+           "top_k": k, "seed": bt.seed,
+           "contexts": {"min": int(bt.seq_lens.min()), "mean": round(float(bt.seq_lens.float().mean()), 1),
+                        "max": int(bt.seq_lens.max())},
+           "replicas": replicas,
+           "step": {"kernel": "decode_step_kernel", "us": round(step_us, 3),
+                    "us_batches": _pcts(step_per), "value": round(B / (step_us * 1e-6), 1),
+                    "unit": "query-tokens/s", "gbps": round(gbps, 1),
+                    "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4), "bytes": nb["step"],
+                    "bytes_per_token": round(nb["step"] / B, 1)},
+           "dense": {"kernel": "attend_kernel (every block)", "us": round(dense_us, 3),
+                     "us_batches": _pcts(dense_per), "value": round(B / (dense_us * 1e-6), 1),
+                     "unit": "query-tokens/s", "gbps": round(dgbps, 1),
+                     "frac_of_peak": round(dgbps / HBM_PEAK_GBPS, 4), "bytes": nb["dense"],
+                     "bytes_per_token": round(nb["dense"] / B, 1)},
+           "speedup_vs_dense": round(dense_us / step_us, 2),
+           "bytes_ratio": round(nb["dense"] / nb["step"], 2),
+           "note": "times are HIP-event averages over back-to-back launches; us_batches: "
+                   "percentiles of the averages of batches of 10 (step) / 5 (dense) launches"}
+    del reps, base
+    torch.cuda.empty_cache()
+    if cpu_seconds > 0:
+        res["cpu_baseline"] = _oracle_rates(bt, cpu_seconds)
+    return res
+
+
+WORKLOADS = [("qwen3-0.6b-shaped B=64 L=8192 k=16", 2, None),
+             ("qwen3-30b-a3b-shaped Best-of-N B=16 (2048 shared + 30720) k=64", 4, None),
+             ("qwen3-32b-shaped B=8 L=8192 k=64", 5, 8192),
+             ("qwen3-32b-shaped B=8 L=16384 k=64", 5, 16384),
+             ("qwen3-32b-shaped B=8 L=32768 k=64", 5, 32768),
+             ("qwen3-32b-shaped B=8 L=65536 k=64", 5, 65536)]
+
+
 # ---------------------------------------------------------------- main
 
 def main(argv=None):
@@ -169,6 +329,12 @@ def main(argv=None):
                     help="skip the shared-prefix (Best-of-N) selection comparison")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run plain 1 GiB device copies (counter calibration)")
+    ap.add_argument("--no-workloads", dest="workloads", action="store_false",
+                    help="skip the other workloads (0.6B, 30B-A3B, 32B sweep)")
+    ap.add_argument("--workload-cpu-seconds", type=float, default=3.0,
+                    help="host seconds per workload for the oracle (0: skip)")
+    ap.add_argument("--only-workload", type=int, default=None,
+                    help="time only the other workload with this index (for profiling runs)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -181,6 +347,11 @@ def main(argv=None):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.only_workload is not None:
+        name, cfg, ctx = WORKLOADS[args.only_workload]
+        res = measure_workload(name, synth.make_config(cfg, context=ctx), dev, args.steps, 0.0)
+        print(json.dumps(res), flush=True)
+        return
     bt = synth.make_config(3)
     B, hq, hkv, D, k = bt.batch, bt.num_q_heads, bt.num_kv_heads, bt.head_dim, bt.top_k
     e = 2
@@ -261,6 +432,18 @@ def main(argv=None):
     wall = time.perf_counter() - t0
     ms_per_step = 1e3 * wall / args.steps
     step_us = 1e3 * ev0.elapsed_time(ev1) / args.steps
+    # spread: the same launches in batches of 10, one event pair per batch
+    bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(max(1, args.steps // 10))]
+    i = 0
+    for e0, e1 in bev:
+        e0.record(stream)
+        for _ in range(10):
+            check(f_step(*reps[i % len(reps)]["calls"]["step"]))
+            i += 1
+        e1.record(stream)
+    torch.cuda.synchronize()
+    step_batches = _pcts([1e3 * e0.elapsed_time(e1) / 10 for e0, e1 in bev])
 
     # the same step as three calls: whole-step time, then a per-kernel pass
     t0 = time.perf_counter()
@@ -504,7 +687,8 @@ def main(argv=None):
                      "frac": round(launch_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": _measured_traffic(),
                      "algorithmic_bytes_per_launch": nbytes["step"],
-                     "avg_launch_us": round(step_us, 3)},
+                     "avg_launch_us": round(step_us, 3),
+                     "launch_us_batches": step_batches},
         "three_calls": {"ms_per_step": round(sep_ms, 5),
                         "value": round(B / (sep_ms * 1e-3), 1),
                         "kernels_us": {kk: round(v, 2) for kk, v in kern.items()},
@@ -534,8 +718,22 @@ def main(argv=None):
             "ms_per_step": round(graph_ms, 5), "value": round(B / (graph_ms * 1e-3), 1),
             "step_gbps": round(nbytes["step"] / (graph_ms * 1e-3) / 1e9, 1)},
     }
+    if args.workloads:
+        # the other workloads (each a full line of its own numbers)
+        del reps
+        torch.cuda.empty_cache()
+        result["workloads"] = []
+        for name, cfg, ctx in WORKLOADS:
+            wb = synth.make_config(cfg, context=ctx)
+            result["workloads"].append(
+                measure_workload(name, wb, dev, max(50, args.steps // 2),
+                                 0.0 if args.no_cpu_baseline else args.workload_cpu_seconds))
+            del wb
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = _cpu_baseline(bt, args.cpu_seconds)
+        result["cpu_baseline"]["cpu_model"] = _cpu_model()
+        one = _oracle_rates(bt, 2.0)["one_thread"]  # one sequence at a time on one thread
+        result["cpu_baseline"]["one_thread"] = one
     print(json.dumps(result), flush=True)
 
 
