@@ -67,22 +67,22 @@ uint32_t step_test_flags() { return env_u32("BTK_STEP_TEST_FLAGS", 0u) & 1u; }
 
 namespace btk {
 
-WorkspaceLayout workspace_layout(const Dims &d, int top_k) {
+WorkspaceLayout workspace_layout(const Dims &d, int top_k, bool dense) {
     const size_t units = (size_t)d.B * d.Hkv;
     const AttendPlan sp = plan_attend(d, top_k, false);
     const AttendPlan dp = plan_attend(d, d.max_blocks, true);
-    const size_t nsplit = sp.nsplit_max > dp.nsplit_max ? sp.nsplit_max : dp.nsplit_max;
+    const size_t nsplit =
+        dense && dp.nsplit_max > sp.nsplit_max ? dp.nsplit_max : sp.nsplit_max;
     const size_t row = (size_t)d.group() * d.D + 2 * (size_t)d.group();
     WorkspaceLayout w;
     w.queue = kQueueOffset;
-    w.pflags = 256;
-    w.claims = w.pflags + align256((size_t)kMaxPrefixGroups * d.Hkv * 2 * sizeof(uint32_t));
-    w.sel_counters = w.claims + (size_t)2 * kMaxStepGrid * kClaimStride * sizeof(uint64_t);
-    w.att_counters = w.sel_counters + align256(units * sizeof(uint32_t));
-    w.ready = w.att_counters + align256(units * sizeof(uint32_t));
-    w.scores = w.ready + align256(units * (size_t)kReadyStride * sizeof(uint32_t));
-    w.partials = w.scores + align256(units * d.max_blocks * sizeof(float));
-    w.total = w.partials + align256(units * nsplit * row * sizeof(float));
+    w.claims = 256;
+    w.state = w.claims + (size_t)2 * kMaxStepGrid * kClaimStride * sizeof(uint64_t);
+    w.state_end = w.state + align256(units * kStateStride * sizeof(uint32_t));
+    w.scores = 0;
+    w.partials = align256(units * d.max_blocks * sizeof(float));
+    w.scratch = w.partials + align256(units * nsplit * row * sizeof(float));
+    w.total = w.state_end + w.scratch;
     return w;
 }
 
@@ -92,16 +92,15 @@ TokenWorkspaceLayout token_workspace_layout(const Dims &d, int top_tokens) {
     w.cap = top_tokens < d.max_blocks ? top_tokens : d.max_blocks;
     const AttendPlan ap = plan_attend(d, w.cap, false);
     const size_t row = (size_t)d.group() * d.D + 2 * (size_t)d.group();
-    // state kept from call to call (all zero after a call) first, then scratch,
-    // so that a smaller problem on the same workspace finds zeros there
-    w.counters = 256;
-    w.ranges = w.counters + align256(units * sizeof(uint32_t));
-    w.att_counters = w.ranges + align256(2 * units * sizeof(uint32_t));
-    w.counts = w.att_counters + align256(units * sizeof(uint32_t));
-    w.scores = w.counts + align256(units * sizeof(uint32_t));
+    // the state lines where the block calls keep theirs, the scratch at the end
+    w.state = 256 + (size_t)2 * kMaxStepGrid * kClaimStride * sizeof(uint64_t);
+    w.state_end = w.state + align256(units * kStateStride * sizeof(uint32_t));
+    w.scores = 0;
     w.entries = w.scores + align256(units * (size_t)d.max_blocks * kPage * sizeof(float));
-    w.partials = w.entries + align256(units * (size_t)w.cap * sizeof(uint32_t));
-    w.total = w.partials + align256(units * (size_t)ap.nsplit_max * row * sizeof(float));
+    w.counts = w.entries + align256(units * (size_t)w.cap * sizeof(uint32_t));
+    w.partials = w.counts + align256(units * sizeof(uint32_t));
+    w.scratch = w.partials + align256(units * (size_t)ap.nsplit_max * row * sizeof(float));
+    w.total = w.state_end + w.scratch;
     return w;
 }
 
@@ -154,11 +153,12 @@ btk_status_t btk_select(const btk_problem_t *problem, const void *q, const float
     const btk::WorkspaceLayout w = btk::workspace_layout(d, top_k);
     if (!workspace || workspace_bytes < w.total) return BTK_ERR_WORKSPACE;
     char *ws = static_cast<char *>(workspace);
-    float *sc = scores ? scores : reinterpret_cast<float *>(ws + w.scores);
+    char *scratch = ws + w.scratch_at(workspace_bytes);
+    float *sc = scores ? scores : reinterpret_cast<float *>(scratch + w.scores);
+    uint32_t *state = reinterpret_cast<uint32_t *>(ws + w.state);
     const btk::SelectPlan plan = btk::plan_select(d);
     return hip_status(btk::launch_select(d, plan, q, centroids, block_table, seq_lens, top_k,
-                                         indices, sc,
-                                         reinterpret_cast<uint32_t *>(ws + w.sel_counters),
+                                         indices, sc, state + btk::kStSelect,
                                          reinterpret_cast<uint32_t *>(ws), (hipStream_t)stream));
 }
 
@@ -194,11 +194,12 @@ btk_status_t btk_select_shared(const btk_problem_t *problem, const void *q,
     const btk::WorkspaceLayout w = btk::workspace_layout(d, top_k);
     if (!workspace || workspace_bytes < w.total) return BTK_ERR_WORKSPACE;
     char *ws = static_cast<char *>(workspace);
-    float *sc = scores ? scores : reinterpret_cast<float *>(ws + w.scores);
+    char *scratch = ws + w.scratch_at(workspace_bytes);
+    float *sc = scores ? scores : reinterpret_cast<float *>(scratch + w.scores);
+    uint32_t *state = reinterpret_cast<uint32_t *>(ws + w.state);
     return hip_status(btk::launch_select_shared(
         d, plan, pg, q, centroids, block_table, seq_lens, top_k, indices, sc,
-        reinterpret_cast<uint32_t *>(ws + w.sel_counters),
-        reinterpret_cast<uint32_t *>(ws + w.pflags), reinterpret_cast<uint32_t *>(ws),
+        state + btk::kStSelect, state + btk::kStPrefix, reinterpret_cast<uint32_t *>(ws),
         (hipStream_t)stream));
 }
 
@@ -219,8 +220,10 @@ btk_status_t btk_sparse_attend(const btk_problem_t *problem, const void *q, cons
     const btk::AttendPlan plan = btk::plan_attend(d, top_k, false);
     return hip_status(btk::launch_attend(d, plan, 0, q, k_cache, v_cache, block_table,
                                          seq_lens, indices, top_k, out, lse,
-                                         reinterpret_cast<float *>(ws + w.partials),
-                                         reinterpret_cast<uint32_t *>(ws + w.att_counters),
+                                         reinterpret_cast<float *>(
+                                             ws + w.scratch_at(workspace_bytes) + w.partials),
+                                         reinterpret_cast<uint32_t *>(ws + w.state) +
+                                             btk::kStAttend,
                                          reinterpret_cast<uint32_t *>(ws), (hipStream_t)stream));
 }
 
@@ -239,8 +242,10 @@ btk_status_t btk_dense_attend(const btk_problem_t *problem, const void *q, const
     const btk::AttendPlan plan = btk::plan_attend(d, d.max_blocks, true);
     return hip_status(btk::launch_attend(d, plan, 1, q, k_cache, v_cache, block_table,
                                          seq_lens, nullptr, 0, out, lse,
-                                         reinterpret_cast<float *>(ws + w.partials),
-                                         reinterpret_cast<uint32_t *>(ws + w.att_counters),
+                                         reinterpret_cast<float *>(
+                                             ws + w.scratch_at(workspace_bytes) + w.partials),
+                                         reinterpret_cast<uint32_t *>(ws + w.state) +
+                                             btk::kStAttend,
                                          reinterpret_cast<uint32_t *>(ws), (hipStream_t)stream));
 }
 
@@ -260,8 +265,10 @@ btk_status_t btk_local_attend(const btk_problem_t *problem, const void *q, const
     const btk::AttendPlan plan = btk::plan_attend(d, window_blocks, false);
     return hip_status(btk::launch_attend(d, plan, 2, q, k_cache, v_cache, block_table,
                                          seq_lens, nullptr, window_blocks, out, lse,
-                                         reinterpret_cast<float *>(ws + w.partials),
-                                         reinterpret_cast<uint32_t *>(ws + w.att_counters),
+                                         reinterpret_cast<float *>(
+                                             ws + w.scratch_at(workspace_bytes) + w.partials),
+                                         reinterpret_cast<uint32_t *>(ws + w.state) +
+                                             btk::kStAttend,
                                          reinterpret_cast<uint32_t *>(ws), (hipStream_t)stream));
 }
 
@@ -286,21 +293,22 @@ btk_status_t btk_token_topk_attend(const btk_problem_t *problem, const void *q,
     const btk::TokenWorkspaceLayout w = btk::token_workspace_layout(d, top_tokens);
     if (!workspace || workspace_bytes < w.total) return BTK_ERR_WORKSPACE;
     char *ws = static_cast<char *>(workspace);
+    char *scratch = ws + w.scratch_at(workspace_bytes);
     uint32_t *err = reinterpret_cast<uint32_t *>(ws);
-    uint32_t *entries = reinterpret_cast<uint32_t *>(ws + w.entries);
-    uint32_t *counts = reinterpret_cast<uint32_t *>(ws + w.counts);
+    uint32_t *state = reinterpret_cast<uint32_t *>(ws + w.state);
+    uint32_t *entries = reinterpret_cast<uint32_t *>(scratch + w.entries);
+    uint32_t *counts = reinterpret_cast<uint32_t *>(scratch + w.counts);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = btk::launch_token_select(
         d, q, k_cache, block_table, seq_lens, top_tokens, w.cap,
-        reinterpret_cast<float *>(ws + w.scores), reinterpret_cast<uint32_t *>(ws + w.counters),
-        entries, counts, reinterpret_cast<uint32_t *>(ws + w.ranges), token_indices, err, s);
+        reinterpret_cast<float *>(scratch + w.scores), nullptr, entries, counts,
+        state + btk::kStRange, token_indices, err, s);
     if (e != hipSuccess) return hip_status(e);
     const btk::AttendPlan plan = btk::plan_attend(d, w.cap, false);
     return hip_status(btk::launch_attend(d, plan, 3, q, k_cache, v_cache, block_table, seq_lens,
                                          reinterpret_cast<const int32_t *>(entries), w.cap, out,
-                                         lse, reinterpret_cast<float *>(ws + w.partials),
-                                         reinterpret_cast<uint32_t *>(ws + w.att_counters), err,
-                                         s, counts));
+                                         lse, reinterpret_cast<float *>(scratch + w.partials),
+                                         state + btk::kStAttend, err, s, counts));
 }
 
 // The single-launch step, with (k_new, v_new non-NULL) or without the KV append.
@@ -309,7 +317,8 @@ static btk_status_t decode_step(const btk_problem_t *problem, const void *q, con
                                 const int32_t *block_table, const int32_t *seq_lens,
                                 const int32_t *first_pos, float *centroids, int32_t top_k,
                                 int32_t *indices, void *out, float *lse, void *workspace,
-                                size_t workspace_bytes, void *stream, bool append) {
+                                size_t workspace_bytes, void *stream, bool append,
+                                bool own_scratch = false) {
     btk::Dims d;
     btk_status_t st = check_problem(problem, &d);
     if (st != BTK_OK) return st;
@@ -318,18 +327,20 @@ static btk_status_t decode_step(const btk_problem_t *problem, const void *q, con
     if (append && (!k_new || !v_new)) return BTK_ERR_NULL;
     if (!top_k_ok(top_k)) return BTK_ERR_SHAPE;
     if (d.B > btk::kMaxStepBatch || !btk::step_rows_fit(d)) return BTK_ERR_UNSUPPORTED;
-    const btk::WorkspaceLayout w = btk::workspace_layout(d, top_k);
+    // a caller's workspace has the size btk_workspace_bytes promises; the
+    // library's own scratch holds only what the step needs
+    const btk::WorkspaceLayout w = btk::workspace_layout(d, top_k, !own_scratch);
     if (!workspace || workspace_bytes < w.total) return BTK_ERR_WORKSPACE;
     char *ws = static_cast<char *>(workspace);
+    char *scratch = ws + w.scratch_at(workspace_bytes);
+    uint32_t *state = reinterpret_cast<uint32_t *>(ws + w.state);
     const btk::SelectPlan sp = btk::plan_select(d);
     const btk::AttendPlan ap = btk::plan_attend(d, top_k, false);
     return hip_status(btk::launch_decode_step(
         d, sp, ap, q, k_cache, v_cache, block_table, seq_lens, first_pos, centroids, top_k,
-        indices, reinterpret_cast<float *>(ws + w.scores), out, lse,
-        reinterpret_cast<float *>(ws + w.partials),
-        reinterpret_cast<uint32_t *>(ws + w.sel_counters),
-        reinterpret_cast<uint32_t *>(ws + w.att_counters),
-        reinterpret_cast<uint32_t *>(ws + w.ready), reinterpret_cast<uint32_t *>(ws + w.queue),
+        indices, reinterpret_cast<float *>(scratch + w.scores), out, lse,
+        reinterpret_cast<float *>(scratch + w.partials), state + btk::kStSelect,
+        state + btk::kStAttend, state + btk::kStReady, reinterpret_cast<uint32_t *>(ws + w.queue),
         reinterpret_cast<uint32_t *>(ws + btk::kStealOffset),
         reinterpret_cast<unsigned long long *>(ws + w.claims), btk::kReadySpinLimit,
         step_test_flags(),

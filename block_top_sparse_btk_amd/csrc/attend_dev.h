@@ -187,7 +187,7 @@ struct AttendArgs {
     const int32_t *bt, *seq_lens, *indices;
     void *out;
     float *lse, *partials;
-    uint32_t *counters, *err;
+    uint32_t *counters, *err;  // unit u's arrival counter at counters[u * kStateStride]
     int Hq, Hkv, num_pages, max_blocks, top_k, bps, nsplit_max;
     float scale_log2;
     // token-level baseline only (NULL otherwise): the number of packed entries
@@ -447,7 +447,7 @@ __device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int s
     if (nsplit == 1) return;
 
     // ---- the last split of this unit merges all splits
-    if (!arrive_last(&a.counters[unit], (uint32_t)nsplit, &is_last)) return;
+    if (!arrive_last(&a.counters[(size_t)unit * kStateStride], (uint32_t)nsplit, &is_last)) return;
     // split weights: every (split, head) max and normaliser fetched at once into
     // LDS (reusing the wave-merge area), then w[s][h] = exp2(m_s - M_h)
     float *wm = smem;                  // [nsplit][r] split maxima, then weights

@@ -136,22 +136,31 @@ struct PrefixGroups {
 };
 AttendPlan plan_attend(const Dims &d, int list_len_max, bool dense);
 
-// Workspace layout (bytes, each region 256-aligned):
+// Workspace layout (bytes).  Everything that carries state from call to call
+// sits at the start, at places that do not depend on the problem; the scratch
+// of a call (values written before they are read) sits at the END of the
+// workspace the caller passes.  So a workspace sized for a problem serves any
+// problem whose unit count (B*Hkv) and sizes are at most those: its state words
+// are where the larger problem's are, and its scratch never reaches them.
 //   [0, 256)                   error word; decode-step chunk counter at byte kStealOffset
 //                              and queue words at byte kQueueOffset
-//   shared-prefix flags        kMaxPrefixGroups*Hkv*2 uint32   zero after every call
 //   decode-step claim words    2*kMaxStepGrid*kClaimStride uint64 (the bank the next
 //                              launch uses is zero after every call)
-//   select counters            B*Hkv uint32      zero after every call
-//   attend counters            B*Hkv uint32      zero after every call
-//   ready words                B*Hkv*kReadyStride uint32 (decode step: launch tags)
-//   scores scratch             B*Hkv*max_blocks float
-//   attend partials            B*Hkv*nsplit_max*(r*D + 2r) float (max of sparse, dense)
-// Every region that carries state from call to call comes before the scratch,
-// the ones left at zero first and the tags next, and each grows with B*Hkv: a
-// smaller problem on the same workspace then finds zeros where it needs zeros
-// and, where it reads tags, only zeros or tags of earlier launches.
-constexpr int kReadyStride = 32;     // one 128-byte line per unit: each is polled on its own
+//   state lines                B*Hkv lines of kStateStride uint32 (one 128-byte line per
+//                              unit u, each polled or counted on its own): kStReady the
+//                              decode step's launch tag, kStSelect / kStAttend the select /
+//                              attention arrival counters, kStPrefix two shared-prefix
+//                              flags of (group, KV head) u = group*Hkv + head, kStRange
+//                              two score-range words of the token-level path; all zero
+//                              after every call but the tags
+//   ... unused ...
+//   scores scratch             B*Hkv*max_blocks float        } the last bytes of the
+//   attend partials            B*Hkv*nsplit_max*(r*D + 2r) float } workspace
+// (partials: max of the sparse and the dense plan; the sparse plan only for the
+// decode step's own layout).
+constexpr int kStateStride = 32;
+constexpr int kStReady = 0, kStSelect = 1, kStAttend = 2, kStPrefix = 3, kStRange = 5;
+constexpr int kReadyStride = kStateStride;
 constexpr size_t kQueueOffset = 128;  // 4 uint32: spare, exits, launch counter, claim bank
 constexpr size_t kStealOffset = 64;   // 1 uint32 (decode-step chunk counter), off the queue line
 // Decode step: share claims, one 64-bit word per workgroup share (a 64-byte line
@@ -163,9 +172,14 @@ constexpr int kClaimStride = 8;       // 64-bit words
 // every wait ends well before).
 constexpr uint32_t kReadySpinLimit = 1u << 22;
 struct WorkspaceLayout {
-    size_t pflags, claims, sel_counters, att_counters, scores, partials, ready, queue, total;
+    size_t claims, state, queue;  // offsets from the start
+    size_t scores, partials;      // offsets from the start of the scratch
+    size_t state_end, scratch, total;
+    // the scratch's offset in a workspace of `bytes` bytes (>= total): its last
+    // `scratch` bytes, 256-aligned
+    size_t scratch_at(size_t bytes) const { return (bytes - scratch) & ~(size_t)255; }
 };
-WorkspaceLayout workspace_layout(const Dims &d, int top_k);
+WorkspaceLayout workspace_layout(const Dims &d, int top_k, bool dense = true);
 
 // ---- launchers (return hipError_t of the launch) --------------------------
 
@@ -204,13 +218,16 @@ hipError_t launch_token_select(const Dims &d, const void *q, const void *k_cache
                                uint32_t *entries, uint32_t *counts, uint32_t *ranges,
                                int32_t *token_idx, uint32_t *err, hipStream_t stream);
 
-// Workspace of the token-level baseline (bytes, each region 256-aligned):
-//   [0, 256) error word; counters; score ranges B*Hkv*2 uint32; attend counters
-//   (these three zero after every call); counts B*Hkv uint32; scores
-//   B*Hkv*max_blocks*16 float; entries B*Hkv*cap uint32; partials
+// Workspace of the token-level baseline: the header, the claim words and the
+// state lines as above (kStRange and kStAttend used), and at its end the
+// scratch: scores B*Hkv*max_blocks*16 float, entries B*Hkv*cap uint32, counts
+// B*Hkv uint32, partials.
 struct TokenWorkspaceLayout {
-    size_t counters, scores, entries, counts, ranges, att_counters, partials, total;
+    size_t state;                               // offset from the start (state lines)
+    size_t scores, entries, counts, partials;   // offsets from the start of the scratch
+    size_t state_end, scratch, total;
     int cap;
+    size_t scratch_at(size_t bytes) const { return (bytes - scratch) & ~(size_t)255; }
 };
 TokenWorkspaceLayout token_workspace_layout(const Dims &d, int top_tokens);
 

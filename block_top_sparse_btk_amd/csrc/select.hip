@@ -134,7 +134,7 @@ __device__ __forceinline__ void shared_item(const SelectArgs &a, const PrefixGro
     __syncthreads();
     if (tid == 0) {
         if (flags[kMaxGroupMembers]) flag_error(a.err, kErrPrefix);
-        __hip_atomic_fetch_add(&a.pflags[((size_t)g * a.Hkv + gk) * 2], 1u, __ATOMIC_RELAXED,
+        __hip_atomic_fetch_add(&a.pflags[((size_t)g * a.Hkv + gk) * kStateStride], 1u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     }
 }
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(kThreads, SHARED ? 4 : 5) void select_kernel(Select
     // waits until the group's shared items of its KV head are done, and counts
     // out afterwards; the last member to count out clears the flag
     const bool member = SHARED && grp >= 0 && (completes || (nb < 0 && c == 0));
-    uint32_t *pf = member ? a.pflags + ((size_t)grp * a.Hkv + unit % a.Hkv) * 2 : nullptr;
+    uint32_t *pf = member ? a.pflags + ((size_t)grp * a.Hkv + unit % a.Hkv) * kStateStride : nullptr;
     if (member) {
         const uint32_t shared_items =
             (uint32_t)((pg.item0[grp + 1] - pg.item0[grp]) / a.Hkv);

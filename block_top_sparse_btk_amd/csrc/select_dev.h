@@ -35,7 +35,7 @@ struct SelectArgs {
     const int32_t *seq_lens;
     int32_t *indices;
     float *scores;
-    uint32_t *counters;
+    uint32_t *counters;  // unit u's arrival counter at counters[u * kStateStride]
     uint32_t *err;
     int Hq, Hkv, num_pages, max_blocks, top_k, chunk, nchunk_max;
     float scale;
@@ -44,7 +44,8 @@ struct SelectArgs {
     const void *k_cache;
     const int32_t *first_pos;
     float *cent_out;
-    // shared-prefix form only (NULL otherwise): per (group, KV head) the shared
+    // shared-prefix form only (NULL otherwise): per (group, KV head) u = group *
+    // Hkv + head, at pflags[u * kStateStride] and the word after it, the shared
     // items done and the members that have finished with them
     uint32_t *pflags = nullptr;
     // decode step with the KV append (NULL otherwise): the newest token's key
@@ -750,7 +751,8 @@ __device__ __forceinline__ bool score_chunk(const SelectArgs &a, int unit, int c
     __syncthreads();
     scan_rows<T, D, KU, false>(a, b, g, j0, n, L, fp, sm, crow);
     nb_out = nb;
-    return arrive_last(&a.counters[unit], (uint32_t)(nchunks + extra), sm.flag);
+    return arrive_last(&a.counters[(size_t)unit * kStateStride], (uint32_t)(nchunks + extra),
+                       sm.flag);
 }
 
 // Decode step: scores blocks [j0, j1) of unit (b, g) of a sequence of length L
@@ -812,10 +814,11 @@ __device__ __forceinline__ void count_in(const SelectArgs &a, int unit, int cnt,
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(&a.counters[unit], (uint32_t)cnt,
-                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t *c = &a.counters[(size_t)unit * kStateStride];
+        const uint32_t prev = __hip_atomic_fetch_add(c, (uint32_t)cnt, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
         if (prev + (uint32_t)cnt == (uint32_t)nb) {
-            __hip_atomic_store(&a.counters[unit], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(ready, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }

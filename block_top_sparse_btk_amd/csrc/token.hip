@@ -45,8 +45,9 @@ struct TokArgs {
     float *scores;       // [units][max_blocks * 16]
     uint32_t *entries;   // [units][cap]: block | token mask << 16
     uint32_t *counts;    // [units]
-    uint32_t *ranges;    // [units][2]: max of ~key and max of key over the unit's
-                         // finite scores (0 0 = none; re-armed by the selector)
+    uint32_t *ranges;    // unit u: ranges[u * kStateStride] and the word after it, the
+                         // max of ~key and the max of key over the unit's finite scores
+                         // (0 0 = none; re-armed by the selector)
     int32_t *token_idx;  // [units][top_tokens] or NULL
     uint32_t *err;
     int Hq, Hkv, num_pages, max_blocks, top_tokens, cap, nchunk_max;
@@ -185,9 +186,9 @@ __device__ __forceinline__ void score_tokens(const TokArgs &a, int unit, int c, 
     kmin_c = sel::wave_max_u32(kmin_c);
     kmax = sel::wave_max_u32(kmax);
     if (lane == 0 && kmax != 0u) {
-        __hip_atomic_fetch_max(&a.ranges[2 * unit], kmin_c, __ATOMIC_RELAXED,
+        __hip_atomic_fetch_max(&a.ranges[(size_t)unit * kStateStride], kmin_c, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_fetch_max(&a.ranges[2 * unit + 1], kmax, __ATOMIC_RELAXED,
+        __hip_atomic_fetch_max(&a.ranges[(size_t)unit * kStateStride + 1], kmax, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     }
 }
@@ -280,12 +281,13 @@ __device__ __forceinline__ void select_tokens(const TokArgs &a, int unit, int L,
     // maximum (gathered while scoring), a non-decreasing function of the score,
     // so each bin holds a contiguous run of keys, whose extremes are kept per
     // bin (bins by key bits would crowd a few binades into a few bins)
-    const uint32_t fl = ~a.ranges[2 * unit];
-    const uint32_t fh = a.ranges[2 * unit + 1];
+    const uint32_t fl = ~a.ranges[(size_t)unit * kStateStride];
+    const uint32_t fh = a.ranges[(size_t)unit * kStateStride + 1];
     __syncthreads();
     if (tid == 0) {  // re-armed for the next launch; every chunk has added its range
-        __hip_atomic_store(&a.ranges[2 * unit], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&a.ranges[2 * unit + 1], 0u, __ATOMIC_RELAXED,
+        __hip_atomic_store(&a.ranges[(size_t)unit * kStateStride], 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&a.ranges[(size_t)unit * kStateStride + 1], 0u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
     uint32_t lo = 0u, hi = 0xffffffffu;  // the keys still in range

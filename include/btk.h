@@ -101,9 +101,10 @@ int btk_last_hip_error(void);
  * need for this problem and top_k (host; no HIP call).
  * Returns 0 if the problem is invalid.  The caller allocates it, ZERO-FILLS it
  * once before its first use, and may then reuse it for any number of calls of
- * the same or a smaller problem: each completed call leaves its internal
- * counters at zero again.  Calls that may overlap in time (different streams)
- * need separate workspaces. */
+ * the same or a smaller problem (batch * num_kv_heads and every size at most
+ * those of the problem it was sized for): each completed call leaves its
+ * internal counters at zero again.  Calls that may overlap in time (different
+ * streams) need separate workspaces. */
 size_t btk_workspace_bytes(const btk_problem_t *problem, int32_t top_k);
 
 /* S1 -- centroid update.  (Pith review, "What carries the argument": blocks are

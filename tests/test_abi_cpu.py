@@ -220,3 +220,4 @@ def test_select_shared_validates_groups_before_launch():
     assert lib.btk_select_shared(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, 1,
                                  ctypes.cast(gs, ctypes.c_void_p), ctypes.cast(pb, ctypes.c_void_p),
                                  4, FAKE, None, FAKE, 1 << 40, None) == btk.BTK_ERR_UNSUPPORTED
+

@@ -572,6 +572,44 @@ def test_decode_step_one_workspace_for_problems_of_different_batch():
             assert torch.equal(a[key], b[key]), key
 
 
+def test_one_workspace_small_then_large_and_other_head_counts():
+    # a workspace sized for the largest problem, used for a small problem, then the
+    # large one, then one with another KV head count, then the large one again:
+    # every call's state words sit at the same places and no call's scratch reaches
+    # them, so every result equals a fresh workspace's (separate calls and the
+    # single launch)
+    large = synth.make_config(2, batch=32)  # 256 units of 512 blocks
+    small = synth.make_batch(name="ws-small", batch=2, num_q_heads=4, num_kv_heads=2,
+                             head_dim=128, seq_lens=[900, 37], top_k=16, seed=93)
+    other = synth.make_batch(name="ws-hkv4", batch=6, num_q_heads=16, num_kv_heads=4,
+                             head_dim=128, seq_lens=[3000, 1, 700, 2100, 64, 4100], top_k=16,
+                             seed=94)
+    _say("[ws] small / large / Hkv 4 / large on one workspace")
+    dl = large.to(DEV)
+    pl = btk.make_problem(dl.q, dl.k_cache, dl.block_table)
+    shared = btk.new_workspace(pl, 16, DEV)
+    for bt in (small, large, other, large):
+        d = bt.to(DEV)
+        prob = btk.make_problem(d.q, d.k_cache, d.block_table)
+        assert btk.btk_workspace_bytes(prob, 16) <= shared.numel()
+        cent = torch.zeros((bt.num_pages, bt.num_kv_heads, bt.head_dim), device=DEV)
+        btk.btk_centroid_update(d.k_cache, d.block_table, d.seq_lens, cent, problem=prob)
+        first = (d.seq_lens - 1).to(torch.int32)
+        results = []
+        for ws in (shared, btk.new_workspace(prob, 16, DEV)):
+            for fn in (btk.sparse_decode_step, btk.btk_decode_step):  # three calls, one launch
+                c = cent.clone()
+                lse = torch.empty((bt.batch, bt.num_q_heads), device=DEV)
+                out, idx = fn(d.q, d.k_cache, d.v_cache, d.block_table, d.seq_lens, c, 16, ws,
+                              first_pos=first, lse=lse, problem=prob)
+                torch.cuda.synchronize()
+                results.append((out.cpu(), idx.cpu(), lse.cpu(), c.cpu()))
+            assert btk.workspace_error_bits(ws) == 0
+        for r in results[1:]:
+            for x, y in zip(results[0], r):
+                assert torch.equal(x, y)
+
+
 def test_decode_step_shares_longer_than_one_run():
     # about 1.4M centroid rows: every workgroup's share spans more than one
     # 2048-block run (inputs drawn on the device; the three calls, pinned to the
