@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "btk.h"
 #include "btk_internal.h"
 
@@ -311,6 +313,41 @@ btk_status_t btk_token_topk_attend(const btk_problem_t *problem, const void *q,
                                          state + btk::kStAttend, err, s, counts));
 }
 
+// ---- the allocation-free step: scratch in a library-owned device array
+
+// One array per GPU the library runs on, held until the process ends.  In host
+// code `scratch` names a host-side stand-in: the device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+static __device__ __align__(256) unsigned char scratch[BTK_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// The array's state area: the header, the claim words and the state lines of
+// at most kNoallocMaxUnits units (B * Hkv); every problem's scratch sits after
+// it, in the array's last bytes.
+constexpr size_t kNoallocMaxUnits = 16384;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, or NULL
+bool g_scratch_clear[kMaxDevices];  // the state area still has to be cleared
+
+// Zeroes [0, n) words (the scratch's state area on its first use on a device):
+// a plain kernel, so that a caller may capture it in a graph.
+__global__ void fill_zero_kernel(uint32_t *p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+}  // namespace
+
+namespace btk {
+size_t noalloc_state_bytes() {
+    return 256 + (size_t)2 * kMaxStepGrid * kClaimStride * sizeof(uint64_t) +
+           kNoallocMaxUnits * kStateStride * sizeof(uint32_t);
+}
+}  // namespace btk
+
 // The single-launch step, with (k_new, v_new non-NULL) or without the KV append.
 static btk_status_t decode_step(const btk_problem_t *problem, const void *q, const void *k_new,
                                 const void *v_new, const void *k_cache, const void *v_cache,
@@ -356,6 +393,59 @@ btk_status_t btk_decode_step(const btk_problem_t *problem, const void *q, const 
     return decode_step(problem, q, nullptr, nullptr, k_cache, v_cache, block_table, seq_lens,
                        first_pos, centroids, top_k, indices, out, lse, workspace,
                        workspace_bytes, stream, false);
+}
+
+btk_status_t btk_decode_step_noalloc(const btk_problem_t *problem, const void *q,
+                                     const void *k_cache, const void *v_cache,
+                                     const int32_t *block_table, const int32_t *seq_lens,
+                                     const int32_t *first_pos, float *centroids, int32_t top_k,
+                                     int32_t *indices, void *out, float *lse, void *stream) {
+    btk::Dims d;
+    btk_status_t st = check_problem(problem, &d);
+    if (st != BTK_OK) return st;
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !centroids || !indices || !out)
+        return BTK_ERR_NULL;
+    if (!top_k_ok(top_k)) return BTK_ERR_SHAPE;
+    if (d.B > btk::kMaxStepBatch || !btk::step_rows_fit(d)) return BTK_ERR_UNSUPPORTED;
+    // the step's own layout: no room for the dense comparison's partials
+    const btk::WorkspaceLayout w = btk::workspace_layout(d, top_k, false);
+    if ((size_t)d.B * d.Hkv > kNoallocMaxUnits ||
+        w.scratch > (size_t)BTK_NOALLOC_SCRATCH_BYTES - btk::noalloc_state_bytes())
+        return BTK_ERR_WORKSPACE;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= kMaxDevices) return BTK_ERR_UNSUPPORTED;
+    void *ws = nullptr;
+    bool clear = false;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        if (!g_scratch_ptr[dev]) {
+            void *p = nullptr;
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return hip_status(e);
+            if (!p) return BTK_ERR_HIP;
+            g_scratch_ptr[dev] = p;
+            g_scratch_clear[dev] = true;
+        }
+        ws = g_scratch_ptr[dev];
+        clear = g_scratch_clear[dev];
+        g_scratch_clear[dev] = false;
+    }
+    if (clear) {  // every word that carries state from call to call starts at zero
+        const size_t words = btk::noalloc_state_bytes() / sizeof(uint32_t);
+        hipLaunchKernelGGL(fill_zero_kernel, dim3(256), dim3(256), 0, (hipStream_t)stream,
+                           static_cast<uint32_t *>(ws), words);
+        e = hipGetLastError();
+        if (e != hipSuccess) {
+            std::lock_guard<std::mutex> lock(g_scratch_mu);
+            g_scratch_clear[dev] = true;
+            return hip_status(e);
+        }
+    }
+    return decode_step(problem, q, nullptr, nullptr, k_cache, v_cache, block_table, seq_lens,
+                       first_pos, centroids, top_k, indices, out, lse, ws,
+                       (size_t)BTK_NOALLOC_SCRATCH_BYTES, stream, false, true);
 }
 
 btk_status_t btk_decode_step_append(const btk_problem_t *problem, const void *q,

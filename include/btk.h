@@ -284,6 +284,30 @@ btk_status_t btk_decode_step_append(const btk_problem_t *problem, const void *q,
                                     int32_t *indices, void *out, float *lse, void *workspace,
                                     size_t workspace_bytes, void *stream);
 
+/* btk_decode_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): no
+ * workspace argument; the step's scratch (arrival counters, ready words, claim
+ * words, scores, split partials) lives in a device array of
+ * BTK_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it runs
+ * on, from its first call there until the process ends.  The call allocates
+ * nothing; its first call on a GPU clears the array's state words with a small
+ * fill kernel on `stream` (no memset).  Every call on one GPU shares that GPU's
+ * array, which keeps the last call's contents: calls that may overlap in time on
+ * one GPU (different streams) race and give unspecified results.  Results are
+ * those of btk_decode_step.  Error bits of invalid device inputs are not
+ * reported (there is no workspace to read them from).
+ *   arguments, limits and errors as btk_decode_step, and
+ *   BTK_ERR_WORKSPACE if batch * num_kv_heads > 16384 or the problem's scratch
+ *                  (about 4 * batch * num_kv_heads * max_blocks_per_seq bytes of
+ *                  scores plus the split partials) does not fit the array beside
+ *                  its state words */
+#define BTK_NOALLOC_SCRATCH_BYTES (64u << 20)
+btk_status_t btk_decode_step_noalloc(const btk_problem_t *problem, const void *q,
+                                     const void *k_cache, const void *v_cache,
+                                     const int32_t *block_table, const int32_t *seq_lens,
+                                     const int32_t *first_pos, float *centroids, int32_t top_k,
+                                     int32_t *indices, void *out, float *lse, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

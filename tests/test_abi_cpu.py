@@ -221,3 +221,27 @@ def test_select_shared_validates_groups_before_launch():
                                  ctypes.cast(gs, ctypes.c_void_p), ctypes.cast(pb, ctypes.c_void_p),
                                  4, FAKE, None, FAKE, 1 << 40, None) == btk.BTK_ERR_UNSUPPORTED
 
+
+def test_decode_step_noalloc_validates_before_any_hip_call():
+    """The allocation-free step: the same argument checks as btk_decode_step, and a
+    problem whose scratch exceeds the library's per-GPU array is refused."""
+    lib = btk._lib()
+    prob = _problem()
+    p = ctypes.byref(prob)
+    args = lambda **o: [o.get(n, FAKE) for n in ("q", "k", "v", "bt", "sl")] + \
+        [o.get("fp", None), o.get("cent", FAKE), o.get("k_", 8), o.get("idx", FAKE),
+         o.get("out", FAKE), None, None]  # noqa: E731
+    assert lib.btk_decode_step_noalloc(None, *args()) == btk.BTK_ERR_NULL
+    for name in ("q", "k", "v", "bt", "sl", "cent", "idx", "out"):
+        assert lib.btk_decode_step_noalloc(p, *args(**{name: None})) == btk.BTK_ERR_NULL, name
+    assert lib.btk_decode_step_noalloc(p, *args(k_=0)) == btk.BTK_ERR_SHAPE
+    assert lib.btk_decode_step_noalloc(p, *args(k_=8193)) == btk.BTK_ERR_SHAPE
+    bad = ctypes.byref(_problem(head_dim=96))
+    assert lib.btk_decode_step_noalloc(bad, *args()) == btk.BTK_ERR_UNSUPPORTED
+    big = _problem(batch=1025, max_blocks_per_seq=64)
+    assert lib.btk_decode_step_noalloc(ctypes.byref(big), *args()) == btk.BTK_ERR_UNSUPPORTED
+    # more than 16384 units, or scores beyond the 64 MiB array
+    units = _problem(batch=1024, num_q_heads=32, num_kv_heads=32, max_blocks_per_seq=16)
+    assert lib.btk_decode_step_noalloc(ctypes.byref(units), *args()) == btk.BTK_ERR_WORKSPACE
+    scores = _problem(batch=1024, num_q_heads=16, num_kv_heads=8, max_blocks_per_seq=4096)
+    assert lib.btk_decode_step_noalloc(ctypes.byref(scores), *args()) == btk.BTK_ERR_WORKSPACE
