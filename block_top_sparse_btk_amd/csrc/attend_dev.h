@@ -60,18 +60,16 @@ struct Mfma<uint16_t, D> {
     __device__ static void load_k(KFrag &f, const uint16_t *tile, int lane) {
         const uint16_t *p = tile + (lane & 15) * D + 8 * (lane >> 4);
 #pragma unroll
-        for (int i = 0; i < NK; ++i)
-            f.x[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(p + 32 * i));
+        for (int i = 0; i < NK; ++i) f.x[i] = *reinterpret_cast<const bf16x8_t *>(p + 32 * i);
     }
     // lane l: head l%16 (zero when >= r), same dims as load_k
     __device__ static void load_q(QFrag &f, const uint16_t *qg, int r, int lane) {
         const int h = lane & 15;
         const uint16_t *p = qg + h * D + 8 * (lane >> 4);
 #pragma unroll
-        for (int i = 0; i < NK; ++i) {
-            uint4 w = h < r ? *reinterpret_cast<const uint4 *>(p + 32 * i) : make_uint4(0, 0, 0, 0);
-            f.x[i] = __builtin_bit_cast(bf16x8_t, w);
-        }
+        for (int i = 0; i < NK; ++i)
+            f.x[i] = h < r ? *reinterpret_cast<const bf16x8_t *>(p + 32 * i)
+                           : __builtin_bit_cast(bf16x8_t, u32x4_t{0u, 0u, 0u, 0u});
     }
     __device__ static floatx4_t qk(const KFrag &k, const QFrag &q) {
         floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -84,9 +82,7 @@ struct Mfma<uint16_t, D> {
     __device__ static void load_v(VFrag &f, const uint16_t *tile, int lane) {
         const uint16_t *p = tile + (lane & 15) * kPage + 4 * (lane >> 4);
 #pragma unroll
-        for (int n = 0; n < NV; ++n)
-            f.x[n] = __builtin_bit_cast(short4_t,
-                                        *reinterpret_cast<const uint2 *>(p + 16 * kPage * n));
+        for (int n = 0; n < NV; ++n) f.x[n] = *reinterpret_cast<const short4_t *>(p + 16 * kPage * n);
     }
     // zero the values of tokens outside `mask` (bit t = token t of the page)
     __device__ static void mask_v(VFrag &f, uint32_t mask, int lane) {
@@ -114,10 +110,10 @@ struct Mfma<float, D> {
     static constexpr int NK = D / 4;
     static constexpr int NV = D / 16;
     struct KFrag {
-        float x[NK];
+        floatx4_t x[NK / 4];  // element i of the k-slots: x[i / 4][i % 4]
     };
     struct VFrag {
-        float4 x[NV];
+        floatx4_t x[NV];
     };
     using QFrag = KFrag;
 
@@ -125,60 +121,46 @@ struct Mfma<float, D> {
     __device__ static void load_k(KFrag &f, const float *tile, int lane) {
         const float *p = tile + (lane & 15) * D + (lane >> 4) * (D / 4);
 #pragma unroll
-        for (int i = 0; i < NK; i += 4) {
-            float4 w = *reinterpret_cast<const float4 *>(p + i);
-            f.x[i] = w.x;
-            f.x[i + 1] = w.y;
-            f.x[i + 2] = w.z;
-            f.x[i + 3] = w.w;
-        }
+        for (int i = 0; i < NK / 4; ++i) f.x[i] = *reinterpret_cast<const floatx4_t *>(p + 4 * i);
     }
     __device__ static void load_q(QFrag &f, const float *qg, int r, int lane) {
         const int h = lane & 15;
         const float *p = qg + h * D + (lane >> 4) * (D / 4);
 #pragma unroll
-        for (int i = 0; i < NK; i += 4) {
-            float4 w = h < r ? *reinterpret_cast<const float4 *>(p + i)
-                             : make_float4(0.f, 0.f, 0.f, 0.f);
-            f.x[i] = w.x;
-            f.x[i + 1] = w.y;
-            f.x[i + 2] = w.z;
-            f.x[i + 3] = w.w;
-        }
+        for (int i = 0; i < NK / 4; ++i)
+            f.x[i] = h < r ? *reinterpret_cast<const floatx4_t *>(p + 4 * i)
+                           : floatx4_t{0.f, 0.f, 0.f, 0.f};
     }
     __device__ static floatx4_t qk(const KFrag &k, const QFrag &q) {
         floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < NK; ++i)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k.x[i], q.x[i], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k.x[i / 4][i % 4], q.x[i / 4][i % 4], acc,
+                                                       0, 0, 0);
         return acc;
     }
     // lane l: dim 16*n + l%16, tokens 4*(l/16) .. +4
     __device__ static void load_v(VFrag &f, const float *tile, int lane) {
         const float *p = tile + (lane & 15) * kPage + 4 * (lane >> 4);
 #pragma unroll
-        for (int n = 0; n < NV; ++n) f.x[n] = *reinterpret_cast<const float4 *>(p + 16 * kPage * n);
+        for (int n = 0; n < NV; ++n) f.x[n] = *reinterpret_cast<const floatx4_t *>(p + 16 * kPage * n);
     }
     __device__ static void mask_v(VFrag &f, uint32_t mask, int lane) {
         const uint32_t m = mask >> (4 * (lane >> 4));
 #pragma unroll
-        for (int n = 0; n < NV; ++n) {
-            if (!(m & 1u)) f.x[n].x = 0.f;
-            if (!(m & 2u)) f.x[n].y = 0.f;
-            if (!(m & 4u)) f.x[n].z = 0.f;
-            if (!(m & 8u)) f.x[n].w = 0.f;
-        }
+        for (int n = 0; n < NV; ++n)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (!((m >> e) & 1u)) f.x[n][e] = 0.f;
     }
     __device__ static float round_p(float p) { return p; }
     // MFMA e contracts token 4*(l/16)+e of every lane group
     __device__ static void pv(floatx4_t (&o)[NV], const float (&p)[4], const VFrag &v) {
 #pragma unroll
-        for (int n = 0; n < NV; ++n) {
-            o[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[0], v.x[n].x, o[n], 0, 0, 0);
-            o[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[1], v.x[n].y, o[n], 0, 0, 0);
-            o[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[2], v.x[n].z, o[n], 0, 0, 0);
-            o[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[3], v.x[n].w, o[n], 0, 0, 0);
-        }
+        for (int n = 0; n < NV; ++n)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                o[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[e], v.x[n][e], o[n], 0, 0, 0);
     }
 };
 

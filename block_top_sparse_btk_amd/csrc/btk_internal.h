@@ -27,14 +27,33 @@ constexpr uint32_t kErrIndex = 4u;
 constexpr uint32_t kErrTimeout = 8u;  // decode step: a wait for published data gave up
 constexpr uint32_t kErrPrefix = 16u;  // a declared shared prefix differs between members
 
+// Device code handles vectors only as clang's native vector types (indexed with
+// [], converted with __builtin_bit_cast), never as HIP's float4 / uint4 structs
+// accessed through their .x .. .w union members or through pointers of another
+// type: a build of the fp32 attention with one-block stages, written with those,
+// had the P.V fragments' registers reused before the products read them.
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) short short4_t;
 typedef __attribute__((ext_vector_type(4))) float floatx4_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+
+// Element e of a 16-byte vector of T held as raw bits (8 bf16 or 4 fp32), as float.
+template <typename T>
+__device__ __forceinline__ float vec16_elem(const u32x4_t &w, int e);
 
 // ---- device helpers ------------------------------------------------------
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
     return __uint_as_float(h << 16);
+}
+
+template <>
+__device__ __forceinline__ float vec16_elem<uint16_t>(const u32x4_t &w, int e) {
+    return bf16_bits_to_f32((w[e >> 1] >> ((e & 1) * 16)) & 0xffffu);
+}
+template <>
+__device__ __forceinline__ float vec16_elem<float>(const u32x4_t &w, int e) {
+    return __uint_as_float(w[e]);
 }
 
 // float -> bf16 bits, round to nearest, ties to even (finite inputs).

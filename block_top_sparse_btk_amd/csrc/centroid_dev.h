@@ -8,31 +8,10 @@
 
 namespace btk {
 
+// Elements of T in one 16-byte vector.
 template <typename T>
-struct Vec16;
-template <>
-struct Vec16<uint16_t> {
-    static constexpr int n = 8;
-    __device__ static void add(const void *p, float (&acc)[8]) {
-        uint4 w = *reinterpret_cast<const uint4 *>(p);
-        uint32_t x[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc[2 * i] += bf16_bits_to_f32(x[i] & 0xffffu);
-            acc[2 * i + 1] += bf16_bits_to_f32(x[i] >> 16);
-        }
-    }
-};
-template <>
-struct Vec16<float> {
-    static constexpr int n = 4;
-    __device__ static void add(const void *p, float (&acc)[4]) {
-        float4 w = *reinterpret_cast<const float4 *>(p);
-        acc[0] += w.x;
-        acc[1] += w.y;
-        acc[2] += w.z;
-        acc[3] += w.w;
-    }
+struct Vec16 {
+    static constexpr int n = 16 / (int)sizeof(T);
 };
 
 // Mean of the v valid keys of one token-major (page, head) tile, by one wave.
@@ -49,19 +28,19 @@ struct KeyTile {
     static constexpr int TPI = kWave / LPR;  // token rows per wave instruction
     static constexpr int NI = kPage / TPI;   // instructions per tile
     static_assert(kWave % LPR == 0 && kPage % TPI == 0, "layout");
-    uint4 w[NI];  // raw 16-byte vectors, zero for tokens >= v
+    u32x4_t w[NI];  // raw 16-byte vectors, zero for tokens >= v
 
     __device__ __forceinline__ void load(const T *tile, int v, int lane) {
         const int col = lane % LPR, row = lane / LPR;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int t = i * TPI + row;
-            w[i] = t < v ? *reinterpret_cast<const uint4 *>(tile + (size_t)t * D + col * VEC)
-                         : make_uint4(0u, 0u, 0u, 0u);
+            w[i] = t < v ? *reinterpret_cast<const u32x4_t *>(tile + (size_t)t * D + col * VEC)
+                         : u32x4_t{0u, 0u, 0u, 0u};
         }
     }
     // token t's row, given as this lane's 16-byte slice (dims col*VEC ..)
-    __device__ __forceinline__ void set_row(int t, uint4 slice, int lane) {
+    __device__ __forceinline__ void set_row(int t, u32x4_t slice, int lane) {
         const int row = lane / LPR;
 #pragma unroll
         for (int i = 0; i < NI; ++i)
@@ -74,7 +53,10 @@ struct KeyTile {
         for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
 #pragma unroll
         for (int i = 0; i < NI; ++i)
-            if (i * TPI + row < v) Vec16<T>::add(&w[i], acc);
+            if (i * TPI + row < v) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) acc[e] += vec16_elem<T>(w[i], e);
+            }
 #pragma unroll
         for (int off = LPR; off < kWave; off <<= 1) {
 #pragma unroll
@@ -84,10 +66,10 @@ struct KeyTile {
             const float vf = (float)v;
 #pragma unroll
             for (int e = 0; e < VEC; e += 4) {
-                const float4 o = make_float4(acc[e] / vf, acc[e + 1] / vf, acc[e + 2] / vf,
-                                             acc[e + 3] / vf);
-                *reinterpret_cast<float4 *>(gdst + col * VEC + e) = o;
-                if (ldst) *reinterpret_cast<float4 *>(ldst + col * VEC + e) = o;
+                const floatx4_t o = {acc[e] / vf, acc[e + 1] / vf, acc[e + 2] / vf,
+                                     acc[e + 3] / vf};
+                *reinterpret_cast<floatx4_t *>(gdst + col * VEC + e) = o;
+                if (ldst) *reinterpret_cast<floatx4_t *>(ldst + col * VEC + e) = o;
             }
         }
     }

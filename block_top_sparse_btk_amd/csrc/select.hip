@@ -88,13 +88,13 @@ __device__ __forceinline__ void shared_item(const SelectArgs &a, const PrefixGro
     }
 
     const int col = lane % LPR, rsub = lane / LPR;
-    typedef float4 Row[VPL / 4];
+    typedef floatx4_t Row[VPL / 4];
     auto issue = [&](Row (&cv)[KU], int base) {
 #pragma unroll
         for (int u = 0; u < KU; ++u) {
             const int row = min(base + u * kWaves * RPI + wave * RPI + rsub, n - 1);
             const int p = max(pages[row], 0);
-            const float4 *src = reinterpret_cast<const float4 *>(
+            const floatx4_t *src = reinterpret_cast<const floatx4_t *>(
                 a.cent + ((size_t)p * a.Hkv + gk) * D + col * VPL);
 #pragma unroll
             for (int v = 0; v < VPL / 4; ++v) cv[u][v] = src[v];

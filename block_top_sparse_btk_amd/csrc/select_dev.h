@@ -198,12 +198,12 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
 // *count the number of keys in the bin.  Wave-uniform.
 __device__ __forceinline__ uint32_t locate_bin(const uint32_t *hist, int &need, int lane,
                                                uint32_t *count = nullptr) {
-    const uint4 h = reinterpret_cast<const uint4 *>(hist)[lane];  // bins 4l .. 4l+3
-    const uint32_t lane_sum = h.x + h.y + h.z + h.w;
+    const u32x4_t h = reinterpret_cast<const u32x4_t *>(hist)[lane];  // bins 4l .. 4l+3
+    const uint32_t lane_sum = h[0] + h[1] + h[2] + h[3];
     const uint32_t above_lane = wave_sum_u32(lane_sum) - wave_inclusive_scan(lane_sum);
     int bin = -1;
     uint32_t above_bin = 0u, in_bin = 0u, acc = above_lane;
-    const uint32_t hv[4] = {h.x, h.y, h.z, h.w};
+    const uint32_t hv[4] = {h[0], h[1], h[2], h[3]};
 #pragma unroll
     for (int e = 3; e >= 0; --e) {  // from this lane's top bin down
         if (bin < 0 && acc < (uint32_t)need && acc + hv[e] >= (uint32_t)need) {
@@ -224,7 +224,7 @@ __device__ __forceinline__ void radix_pass(const uint32_t (&key)[N], uint32_t &l
                                            int &need, uint32_t *hist, int lane) {
     const uint32_t span = hi - lo;
     const int shift = max(0, 24 - __builtin_clz(span));  // (span >> shift) < 256
-    reinterpret_cast<uint4 *>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
+    reinterpret_cast<u32x4_t *>(hist)[lane] = u32x4_t{0u, 0u, 0u, 0u};
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int i = 0; i < N; ++i) {
@@ -288,13 +288,13 @@ __device__ __forceinline__ void finish_from_cand(uint32_t *cand, int m, uint32_t
         __builtin_amdgcn_wave_barrier();
         // all 64 slots at once (slots from m on hold 0, below every key)
         const uint32_t mine = lane < m ? cand[lane] : 0u;
-        uint4 c4[kWave / 4];
+        u32x4_t c4[kWave / 4];
 #pragma unroll
-        for (int t = 0; t < kWave / 4; ++t) c4[t] = reinterpret_cast<const uint4 *>(cand)[t];
+        for (int t = 0; t < kWave / 4; ++t) c4[t] = reinterpret_cast<const u32x4_t *>(cand)[t];
         int gt = 0, ge = 0;
 #pragma unroll
         for (int t = 0; t < kWave / 4; ++t) {
-            const uint32_t cv[4] = {c4[t].x, c4[t].y, c4[t].z, c4[t].w};
+            const uint32_t cv[4] = {c4[t][0], c4[t][1], c4[t][2], c4[t][3]};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 gt += cv[e] > mine ? 1 : 0;
@@ -424,7 +424,7 @@ __device__ __forceinline__ void select_topk_wg4(const Src &src, int nb, int top_
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int kb = min(top_k, nb);
     for (int i = tid; i < kTopkPasses * kHistWords / 4; i += kThreads)
-        reinterpret_cast<uint4 *>(sm.hist)[i] = make_uint4(0u, 0u, 0u, 0u);
+        reinterpret_cast<u32x4_t *>(sm.hist)[i] = u32x4_t{0u, 0u, 0u, 0u};
     uint32_t key[KMAX];
     src.fill(key, tid, kThreads, nb);
     uint32_t kmin = 0xffffffffu, kmax = 0u;
@@ -538,15 +538,15 @@ __device__ __forceinline__ float row16_sum(float x) {
 // multiply-adds, then one add; no contraction) so that every kernel computes
 // bit-identical scores whatever its code generation.
 template <int VPL>
-__device__ __forceinline__ float row_partial(const float (&qf)[VPL], const float4 (&cv)[VPL / 4]) {
+__device__ __forceinline__ float row_partial(const float (&qf)[VPL], const floatx4_t (&cv)[VPL / 4]) {
 #pragma clang fp contract(off)
     float s = 0.f;
 #pragma unroll
     for (int v = 0; v < VPL / 4; ++v) {
-        float t = qf[4 * v] * cv[v].x;
-        t = __builtin_fmaf(qf[4 * v + 1], cv[v].y, t);
-        t = __builtin_fmaf(qf[4 * v + 2], cv[v].z, t);
-        t = __builtin_fmaf(qf[4 * v + 3], cv[v].w, t);
+        float t = qf[4 * v] * cv[v][0];
+        t = __builtin_fmaf(qf[4 * v + 1], cv[v][1], t);
+        t = __builtin_fmaf(qf[4 * v + 2], cv[v][2], t);
+        t = __builtin_fmaf(qf[4 * v + 3], cv[v][3], t);
         s = s + t;
     }
     return s;
@@ -620,13 +620,13 @@ __device__ __forceinline__ void scan_rows(const SelectArgs &a, int b, int g, int
     // Loads are unconditional so that the next stage stays in flight while the
     // current one is reduced: rows past the run re-read its last row and an
     // invalid page reads page 0; neither result is kept.
-    typedef float4 Row[VPL / 4];
+    typedef floatx4_t Row[VPL / 4];
     auto issue = [&](Row (&cv)[KU], int base) {
 #pragma unroll
         for (int u = 0; u < KU; ++u) {
             const int row = min(base + u * kWaves * RPI + wave * RPI + rsub, n - 1);
             const int p = max(sm.pages[row], 0);
-            const float4 *src = reinterpret_cast<const float4 *>(
+            const floatx4_t *src = reinterpret_cast<const floatx4_t *>(
                 a.cent + ((size_t)p * a.Hkv + g) * D + col * VPL);
 #pragma unroll
             for (int v = 0; v < VPL / 4; ++v) cv[u][v] = src[v];
@@ -667,7 +667,7 @@ __device__ __forceinline__ void scan_rows(const SelectArgs &a, int b, int g, int
         if (j != jw) kt.load(keys + (size_t)page * page_stride, cached(j), lane);
         if (APPEND && j == jnew)  // this lane's 16-byte slice of the new key (LDS)
             kt.set_row(v - 1,
-                       *reinterpret_cast<const uint4 *>(sm.newtok + (lane % KeyTile<T, D>::LPR) *
+                       *reinterpret_cast<const u32x4_t *>(sm.newtok + (lane % KeyTile<T, D>::LPR) *
                                                         (KeyTile<T, D>::VEC * sizeof(T) / 4)),
                        lane);
         kt.mean(v, a.cent_out + ((size_t)page * a.Hkv + g) * D, row_lds, lane);
@@ -675,7 +675,7 @@ __device__ __forceinline__ void scan_rows(const SelectArgs &a, int b, int g, int
         Row cv;
 #pragma unroll
         for (int vv = 0; vv < VPL / 4; ++vv)
-            cv[vv] = reinterpret_cast<const float4 *>(row_lds + col * VPL)[vv];
+            cv[vv] = reinterpret_cast<const floatx4_t *>(row_lds + col * VPL)[vv];
         const float s = row16_sum(row_partial<VPL>(qf, cv));
         if (lane == 0) sm.sc[j - j0] = s;
         __builtin_amdgcn_wave_barrier();

@@ -64,7 +64,7 @@ struct StepArgs {
     int B, units, nsplit;
 };
 
-constexpr int kStageBlocks = 1;  // bf16 attention pipeline stage (fp32: 2, see attend.hip)
+constexpr int kStageBlocks = 1;  // attention pipeline stage: one block
 constexpr int kScanRows = 4;     // centroid rows per lane per scan stage
 constexpr int kRun = 2048;       // blocks per scan run: shares (~550 blocks at 32 x 8 units of
                                  // 17K tokens) take one run, one page-id round trip; in phase 2
@@ -338,7 +338,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
         // the appended token's cache stores are done before the block can be read
         if (APPEND) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        att::attend_item<T, D, att::kSelected, (sizeof(T) == 4 ? 2 : kStageBlocks)>(
+        att::attend_item<T, D, att::kSelected, kStageBlocks>(
             a.t, unit, split, dyn, &flag, list, L < 0 ? 0 : L, row_lds ? pages : nullptr);
         __syncthreads();  // LDS is reused by the next item
     }

@@ -150,12 +150,12 @@ __device__ __forceinline__ void score_tokens(const TokArgs &a, int unit, int c, 
     // page 0 and a slot past the chunk its last page; neither result is kept)
     uint32_t kmin_c = 0u, kmax = 0u;  // max of ~key and of key over this lane's finite scores
     for (int i0 = wave; i0 < n; i0 += kWaves * kUnroll) {
-        uint4 kv[kUnroll][NI];
+        u32x4_t kv[kUnroll][NI];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int i = min(i0 + u * kWaves, n - 1);
             const int p = max(pages[i], 0);
-            const uint4 *tile = reinterpret_cast<const uint4 *>(
+            const u32x4_t *tile = reinterpret_cast<const u32x4_t *>(
                 static_cast<const T *>(a.k) + ((size_t)p * a.Hkv + g) * kPage * D);
 #pragma unroll
             for (int v = 0; v < NI; ++v) kv[u][v] = tile[v * kWave + lane];
@@ -166,10 +166,9 @@ __device__ __forceinline__ void score_tokens(const TokArgs &a, int unit, int c, 
             const int j = j0 + i;
 #pragma unroll
             for (int v = 0; v < NI; ++v) {
-                const T *x = reinterpret_cast<const T *>(&kv[u][v]);
                 float s = 0.f;
 #pragma unroll
-                for (int e = 0; e < EV; ++e) s += qf[e] * to_f32<T>(x[e]);
+                for (int e = 0; e < EV; ++e) s += qf[e] * vec16_elem<T>(kv[u][v], e);
                 s = lanes_sum<LPR>(s);
                 const int t = v * RPI + rsub;
                 if (i < n && col == 0 && t < min(kPage, L - j * kPage)) {
