@@ -23,7 +23,9 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libbtk.so")
+# BTK_LIB names another build of the same library (the sanitizer test loads a
+# host-instrumented one this way); by default the in-tree libbtk.so.
+LIB_PATH = os.environ.get("BTK_LIB") or os.path.join(_HERE, "libbtk.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "btk.h")
 
 BTK_OK, BTK_ERR_NULL, BTK_ERR_SHAPE, BTK_ERR_UNSUPPORTED, BTK_ERR_WORKSPACE, BTK_ERR_HIP = range(6)

@@ -3,6 +3,7 @@
 // has no side effects and the checks run on machines without a GPU.
 #include <math.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include <mutex>
 
@@ -112,7 +113,11 @@ extern "C" {
 
 int btk_abi_version(void) { return BTK_ABI_VERSION; }
 
-const char *btk_status_string(btk_status_t s) {
+const char *btk_status_string(btk_status_t status) {
+    // A C caller may pass any int here; in C++ an enum object holding a value
+    // outside the enumerators' range is undefined, so read the bytes as an int.
+    int s;
+    memcpy(&s, &status, sizeof s);
     switch (s) {
     case BTK_OK: return "ok";
     case BTK_ERR_NULL: return "a required pointer is NULL";
