@@ -638,11 +638,30 @@ def main(argv=None):
         app = (app_ms, sep_app_ms)
 
     if args.copy_probe:
+        # counter calibration: a 1 GiB device copy (3 dispatches), then the
+        # library's row-read probe with the centroid scan's request shape, over
+        # 1 GiB in order (3 dispatches) and over 2^21 distinct random rows of a
+        # 4 GiB buffer (3 dispatches, a new permutation each)
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
+        del dst
+        for _ in range(3):
+            btk.btk_probe_row_read(src)
+        torch.cuda.synchronize()
+        del src
+        big = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(7)
+        for _ in range(3):
+            ids = torch.randperm(big.numel() // 512, device=dev, generator=gen)[:1 << 21]
+            ids = ids.to(torch.int32)
+            torch.cuda.synchronize()
+            btk.btk_probe_row_read(big, row_ids=ids)
+            torch.cuda.synchronize()
+        del big
 
     # exact S4 bytes from the blocks actually selected (every replica selects the same)
     nbytes = algorithmic_bytes(bt.seq_lens.tolist(), hq, hkv, D, k, e,

@@ -92,6 +92,8 @@ def _lib():
         lib.btk_decode_step_append.restype = st
         lib.btk_decode_step_append.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
                                                vp, sz, vp]
+        lib.btk_probe_row_read.restype = st
+        lib.btk_probe_row_read.argtypes = [vp, sz, vp, ctypes.c_int64, vp, vp]
         _LIB = lib
     return _LIB
 
@@ -417,6 +419,22 @@ def btk_decode_step_noalloc(q, k_cache, v_cache, block_table, seq_lens, centroid
                                         _dev(out, "out", q.dtype, dev), lp, _stream(dev))
     _check(st, "btk_decode_step_noalloc")
     return out, indices
+
+
+def btk_probe_row_read(src, rows=None, row_ids=None, sink=None):
+    """Counter-calibration read of 512-byte rows of ``src`` (a device tensor),
+    in order (``rows`` of them) or at ``row_ids`` (int32); computes nothing."""
+    dev = src.device
+    nbytes = src.numel() * src.element_size()
+    if row_ids is not None:
+        rows = row_ids.numel()
+    elif rows is None:
+        rows = nbytes // 512
+    sink = torch.zeros(1, dtype=torch.int32, device=dev) if sink is None else sink
+    rp = _dev(row_ids, "row_ids", torch.int32, dev) if row_ids is not None else None
+    st = _lib().btk_probe_row_read(_dev(src, "src", None, dev), nbytes, rp, int(rows),
+                                   _dev(sink, "sink", None, dev), _stream(dev))
+    _check(st, "btk_probe_row_read")
 
 
 def btk_decode_step_append(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, centroids,

@@ -464,4 +464,14 @@ btk_status_t btk_decode_step_append(const btk_problem_t *problem, const void *q,
                        stream, true);
 }
 
+btk_status_t btk_probe_row_read(const void *src, size_t src_bytes, const int32_t *row_ids,
+                               int64_t rows, uint32_t *sink, void *stream) {
+    if (!src || !sink) return BTK_ERR_NULL;
+    const int64_t src_rows = (int64_t)(src_bytes / 512);
+    if (rows < 0 || (!row_ids && rows > src_rows)) return BTK_ERR_SHAPE;
+    if (rows == 0) return BTK_OK;
+    return hip_status(btk::launch_row_read_probe(src, src_rows, row_ids, rows, sink,
+                                                 (hipStream_t)stream));
+}
+
 }  // extern "C"

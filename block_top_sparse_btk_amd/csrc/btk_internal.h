@@ -264,4 +264,10 @@ hipError_t launch_decode_step(const Dims &d, const SelectPlan &sp, const AttendP
                               uint32_t test_flags, uint32_t *err, hipStream_t stream,
                               const void *k_new = nullptr, const void *v_new = nullptr);
 
+// Counter calibration (probe.hip): reads `rows` 512-byte rows of src (row ids
+// from row_ids, or 0 .. rows-1 when it is NULL; ids outside [0, src_rows) are
+// skipped) with 16 bytes per lane.
+hipError_t launch_row_read_probe(const void *src, int64_t src_rows, const int32_t *row_ids,
+                                 int64_t rows, uint32_t *sink, hipStream_t stream);
+
 }  // namespace btk

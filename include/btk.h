@@ -308,6 +308,19 @@ btk_status_t btk_decode_step_noalloc(const btk_problem_t *problem, const void *q
                                      const int32_t *first_pos, float *centroids, int32_t top_k,
                                      int32_t *indices, void *out, float *lse, void *stream);
 
+/* Measurement aid, not part of the method: reads `rows` rows of 512 bytes of
+ * src with the request shape of the decode step's centroid scan (16 bytes per
+ * lane, half a wavefront per row) and computes nothing, so that hardware byte
+ * counters (FETCH_SIZE) can be scaled by a kernel of known traffic,
+ * 512 * rows bytes (+ 4 * rows of row ids).
+ *   src      device, src_bytes bytes; row i is bytes [512 i, 512 i + 512)
+ *   row_ids  device [rows] int32 row numbers (ids outside [0, src_bytes / 512)
+ *            are skipped), or NULL for rows 0 .. rows-1 in order
+ *   sink     device, one uint32 that is written only by chance (keeps the loads)
+ * BTK_ERR_SHAPE if rows < 0, or row_ids is NULL and rows > src_bytes / 512. */
+btk_status_t btk_probe_row_read(const void *src, size_t src_bytes, const int32_t *row_ids,
+                                int64_t rows, uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

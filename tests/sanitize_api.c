@@ -220,6 +220,14 @@ int main(void) {
     EXPECT(btk_decode_step_noalloc(&p, dev, dev, dev, di, di, di, wf, 9000, wi, dev, NULL, NULL),
            BTK_ERR_SHAPE);
 
+    /* counter-calibration probe */
+    EXPECT(btk_probe_row_read(NULL, 4096, NULL, 8, (uint32_t *)dev, NULL), BTK_ERR_NULL);
+    EXPECT(btk_probe_row_read(dev, 4096, NULL, 8, NULL, NULL), BTK_ERR_NULL);
+    EXPECT(btk_probe_row_read(dev, 4096, NULL, -1, (uint32_t *)dev, NULL), BTK_ERR_SHAPE);
+    EXPECT(btk_probe_row_read(dev, 4096, NULL, 9, (uint32_t *)dev, NULL), BTK_ERR_SHAPE);
+    EXPECT(btk_probe_row_read(dev, 4096, di, -5, (uint32_t *)dev, NULL), BTK_ERR_SHAPE);
+    EXPECT(btk_probe_row_read(dev, 4096, NULL, 0, (uint32_t *)dev, NULL), BTK_OK);
+
     if (failures) {
         fprintf(stderr, "%d checks failed\n", failures);
         return 1;

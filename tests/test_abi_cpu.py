@@ -245,3 +245,12 @@ def test_decode_step_noalloc_validates_before_any_hip_call():
     assert lib.btk_decode_step_noalloc(ctypes.byref(units), *args()) == btk.BTK_ERR_WORKSPACE
     scores = _problem(batch=1024, num_q_heads=16, num_kv_heads=8, max_blocks_per_seq=4096)
     assert lib.btk_decode_step_noalloc(ctypes.byref(scores), *args()) == btk.BTK_ERR_WORKSPACE
+
+
+def test_probe_row_read_validates_on_host():
+    lib = btk._lib()
+    sink = FAKE
+    assert lib.btk_probe_row_read(None, 4096, None, 8, sink, None) == btk.BTK_ERR_NULL
+    assert lib.btk_probe_row_read(FAKE, 4096, None, -1, sink, None) == btk.BTK_ERR_SHAPE
+    assert lib.btk_probe_row_read(FAKE, 4096, None, 9, sink, None) == btk.BTK_ERR_SHAPE
+    assert lib.btk_probe_row_read(FAKE, 4096, None, 0, sink, None) == btk.BTK_OK

@@ -809,3 +809,15 @@ def test_shared_prefix_mismatch_is_flagged():
                           seq_lens=[300, 400, 500], top_k=4, seed=62, table="shuffled")
     _say("[shared] declared prefix that the tables do not share")
     _select_both(bt, [0, 3], [4], expect_err=16)
+
+
+def test_probe_row_read_runs_and_leaves_sink():
+    """The counter-calibration read completes in order and with row ids (some
+    out of range, which it skips); over zero bytes its sink is never written."""
+    src = torch.zeros(1 << 20, dtype=torch.uint8, device=DEV)
+    sink = torch.full((1,), 7, dtype=torch.int32, device=DEV)
+    btk.btk_probe_row_read(src, sink=sink)
+    ids = torch.tensor([0, 5, 2047, 2048, -1, 3], dtype=torch.int32, device=DEV)
+    btk.btk_probe_row_read(src, row_ids=ids, sink=sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 7

@@ -26,7 +26,7 @@ HIPCC = "/opt/rocm/bin/hipcc"
 CLANG = "/opt/rocm/llvm/bin/clang"
 SAN = ["-fsanitize=address", "-fsanitize=undefined", "-fno-sanitize-recover=all",
        "-fno-omit-frame-pointer"]
-KERNEL_OBJS = ["centroid.o", "select.o", "attend.o", "step.o", "token.o"]
+KERNEL_OBJS = ["centroid.o", "select.o", "attend.o", "step.o", "token.o", "probe.o"]
 
 
 def _host_only(flags):
