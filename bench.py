@@ -207,7 +207,7 @@ def _pcts(xs):
     return {"p10": round(pick(0.1), 3), "p50": round(pick(0.5), 3), "p90": round(pick(0.9), 3)}
 
 
-def measure_workload(name, bt, dev, steps, cpu_seconds, replicas=None):
+def measure_workload(name, bt, dev, steps, cpu_seconds, replicas=None, cpu_sample=None):
     """One workload's line: the single-launch step and the dense kernel on the same
     inputs (rotating replicas, HIP events on the library's stream), algorithmic
     bytes, roofline fraction, bytes per token, p10/p50/p90 of batch averages, the
@@ -221,6 +221,8 @@ def measure_workload(name, bt, dev, steps, cpu_seconds, replicas=None):
     nb0 = algorithmic_bytes(bt.seq_lens.tolist(), hq, hkv, D, k, e)
     if replicas is None:  # enough copies that consecutive steps miss the last-level cache
         replicas = max(2, min(16, -(-600_000_000 // max(1, nb0["step"]))))
+    if bt.k_cache.is_cuda:  # drawn on the device: far larger than the cache already
+        replicas = 1
     lib = btk._lib()
     stream = torch.cuda.current_stream(dev)
     hs = stream.cuda_stream
@@ -273,7 +275,7 @@ def measure_workload(name, bt, dev, steps, cpu_seconds, replicas=None):
         if btk.workspace_error_bits(r["ws"]):
             raise RuntimeError(f"{name}: device-side input guard fired")
     nb = algorithmic_bytes(bt.seq_lens.tolist(), hq, hkv, D, k, e,
-                           sel_tokens=selected_tokens(reps[0]["idx"].cpu(), bt.seq_lens))
+                           sel_tokens=selected_tokens(reps[0]["idx"].cpu(), bt.seq_lens.cpu()))
     gbps = nb["step"] / (step_us * 1e-6) / 1e9
     dgbps = nb["dense"] / (dense_us * 1e-6) / 1e9
     res = {"workload": name, "batch": B, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": D,
@@ -298,8 +300,31 @@ def measure_workload(name, bt, dev, steps, cpu_seconds, replicas=None):
     del reps, base
     torch.cuda.empty_cache()
     if cpu_seconds > 0:
-        res["cpu_baseline"] = _oracle_rates(bt, cpu_seconds)
+        res["cpu_baseline"] = _oracle_rates(cpu_sample if cpu_sample is not None else bt,
+                                            cpu_seconds)
+        if cpu_sample is not None:
+            res["cpu_baseline"]["sample"] += (f" (a sample of {cpu_sample.batch} of the "
+                                              f"{B} sequences, copied to the host)")
     return res
+
+
+# One GPU's share of the Qwen3-8B serving batch of the Kinetics README's block
+# top-k benchmark ("Benchmark Block TopK Attention throughput": batch 4096,
+# 32768-token contexts, 64 pages kept, eight-way tensor parallel so one KV head
+# and its four query heads per GPU).  Its 69 GB of caches are drawn on the
+# device; the oracle's rate is taken on a few of its sequences copied out.
+SHARE = dict(batch=4096, num_q_heads=4, num_kv_heads=1, head_dim=128, context=32768, top_k=64,
+             seed=8004)
+
+
+def workload_batch(cfg, ctx, dev):
+    """(batch, host sample for the oracle's rate or None) of one workload."""
+    import synth
+    if cfg == "share":
+        bt = synth.make_device_batch(device=dev, name="qwen3-8b-share", **SHARE)
+        sample, _ = synth.extract(bt, [0, 1365, 2730, 4095])
+        return bt, sample
+    return synth.make_config(cfg, context=ctx), None
 
 
 WORKLOADS = [("qwen3-0.6b-shaped B=64 L=8192 k=16", 2, None),
@@ -307,7 +332,8 @@ WORKLOADS = [("qwen3-0.6b-shaped B=64 L=8192 k=16", 2, None),
              ("qwen3-32b-shaped B=8 L=8192 k=64", 5, 8192),
              ("qwen3-32b-shaped B=8 L=16384 k=64", 5, 16384),
              ("qwen3-32b-shaped B=8 L=32768 k=64", 5, 32768),
-             ("qwen3-32b-shaped B=8 L=65536 k=64", 5, 65536)]
+             ("qwen3-32b-shaped B=8 L=65536 k=64", 5, 65536),
+             ("qwen3-8b one-GPU share B=4096 Hq=4 Hkv=1 L=32768 k=64", "share", None)]
 
 
 # ---------------------------------------------------------------- main
@@ -349,7 +375,7 @@ def main(argv=None):
     torch.cuda.set_device(dev)
     if args.only_workload is not None:
         name, cfg, ctx = WORKLOADS[args.only_workload]
-        res = measure_workload(name, synth.make_config(cfg, context=ctx), dev, args.steps, 0.0)
+        res = measure_workload(name, workload_batch(cfg, ctx, dev)[0], dev, args.steps, 0.0)
         print(json.dumps(res), flush=True)
         return
     bt = synth.make_config(3)
@@ -743,11 +769,13 @@ def main(argv=None):
         torch.cuda.empty_cache()
         result["workloads"] = []
         for name, cfg, ctx in WORKLOADS:
-            wb = synth.make_config(cfg, context=ctx)
+            wb, sample = workload_batch(cfg, ctx, dev)
             result["workloads"].append(
                 measure_workload(name, wb, dev, max(50, args.steps // 2),
-                                 0.0 if args.no_cpu_baseline else args.workload_cpu_seconds))
-            del wb
+                                 0.0 if args.no_cpu_baseline else args.workload_cpu_seconds,
+                                 cpu_sample=sample))
+            del wb, sample
+            torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = _cpu_baseline(bt, args.cpu_seconds)
         result["cpu_baseline"]["cpu_model"] = _cpu_model()

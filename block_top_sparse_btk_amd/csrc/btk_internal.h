@@ -13,7 +13,7 @@ constexpr int kWave = 64;
 constexpr int kPage = 16;           // tokens per page (block); all kernels assume it
 constexpr int kMaxBlocksPerSeq = 8192;  // select holds one key per block in LDS
 constexpr int kMaxGroup = 16;       // query heads per KV head: MFMA tile rows
-constexpr int kMaxStepBatch = 1024; // decode step: per-sequence item prefix kept in LDS
+constexpr int kMaxStepBatch = 65536; // decode step: batch limit (one LDS row per 1024 sequences)
 constexpr int kMaxTopTokens = kMaxBlocksPerSeq * kPage;  // token-level baseline budget
 // Shared-prefix selection: prefix blocks per shared item.  Each of its rows is
 // scored against every member's mean query, so items are kept short to spread

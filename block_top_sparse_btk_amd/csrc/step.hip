@@ -92,6 +92,10 @@ constexpr int kSegmentCost = BTK_STEP_SEGMENT_COST;
 #define BTK_STEP_STEAL_ROWS 256
 #endif
 constexpr int kStealFrac = BTK_STEP_STEAL_FRAC;
+// Sequences whose row prefix a workgroup holds in LDS at once; a larger batch is
+// walked window by window (the prologue keeps only each window's first row).
+constexpr int kWin = 1024;
+static_assert(kWin % kThreads == 0 && kMaxStepBatch % kWin == 0, "window shape");
 constexpr uint32_t kStealRows = BTK_STEP_STEAL_ROWS;
 
 // KV append (APPEND): the newest token of unit (b, g), position L - 1, goes
@@ -129,6 +133,57 @@ __device__ __forceinline__ void append_to_cache(const StepArgs &a, int b, int g,
         if (lane + i * kWave < D) vd[(size_t)(lane + i * kWave) * kPage] = vv[i];
 }
 
+// A sequence length as the step uses it: -1 when out of range (its unit then
+// writes -1 indices and flags the error).
+__device__ __forceinline__ int valid_len(int L, int max_blocks) {
+    return L >= 1 && L <= max_blocks * kPage ? L : -1;
+}
+// Centroid rows of a sequence's units in the share cut: per unit kSegmentCost
+// charged rows, then one per block (one placeholder row for an invalid length).
+__device__ __forceinline__ uint32_t unit_rows(int L, int Hkv) {
+    return (uint32_t)Hkv * (uint32_t)(kSegmentCost + (L >= 0 ? (L + kPage - 1) / kPage : 1));
+}
+// The position whose block the step refreshes (S1): with the KV append the
+// newest token, else first_pos (none when it is NULL or the length is invalid).
+template <bool APPEND>
+__device__ __forceinline__ int touched_pos(const StepArgs &a, int b, int L) {
+    if (APPEND) return L >= 0 ? L - 1 : -1;
+    return a.s.first_pos ? a.s.first_pos[b] : -1;
+}
+
+// Loads the row prefix of sequences [base, base + wlen) into LDS, rows before
+// the window being `first` (workgroup-uniform call).
+template <bool APPEND>
+__device__ void load_window(const StepArgs &a, int base, int wlen, uint32_t first,
+                            uint32_t *rows, int *lens, int *fps, int *scan_red) {
+    constexpr int kPer = kWin / kThreads;
+    const int tid = threadIdx.x;
+    __syncthreads();  // the previous window is no longer read
+    int Ls[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)  // all in flight together
+        Ls[i] = i * kThreads + tid < wlen ? a.s.seq_lens[base + i * kThreads + tid] : 0;
+    uint32_t carry = first;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int w = i * kThreads + tid;
+        uint32_t n = 0;
+        if (w < wlen) {
+            const int L = valid_len(Ls[i], a.s.max_blocks);
+            n = unit_rows(L, a.s.Hkv);
+            lens[w] = L;
+            fps[w] = touched_pos<APPEND>(a, base + w, L);
+        }
+        const uint32_t before = carry + (uint32_t)sel::wg_exclusive_scan((int)n, scan_red);
+        if (w < wlen) {
+            rows[w] = before;
+            if (w == wlen - 1) rows[w + 1] = before + n;
+        }
+        carry += (uint32_t)(scan_red[0] + scan_red[1] + scan_red[2] + scan_red[3]);
+    }
+    __syncthreads();
+}
+
 // APPEND: the KV append of the step is fused in (a separate instantiation, so
 // that the plain step carries none of its code).
 template <typename T, int D, bool APPEND>
@@ -142,9 +197,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
     __shared__ int scan_red[kWaves];
     __shared__ float crow[kWaves * D];
     __shared__ __align__(16) uint32_t newtok[APPEND ? D * sizeof(T) / 4 : 4];  // new key
-    __shared__ uint32_t rows[kMaxStepBatch + 1];  // centroid rows before each sequence
-    __shared__ int lens[kMaxStepBatch];           // sequence lengths, -1: invalid
-    __shared__ int fps[kMaxStepBatch];            // decode positions (first touched token)
+    // the row prefix of one window of kWin sequences, [base, base + wlen)
+    __shared__ uint32_t rows[kWin + 1];  // centroid rows before each sequence, then the window end
+    __shared__ int lens[kWin];           // sequence lengths, -1: invalid
+    __shared__ int fps[kWin];            // decode positions (first touched token)
+    __shared__ uint32_t wrows[kMaxStepBatch / kWin + 1];  // rows before each window, then R
     __shared__ int item_s, owns_s;
     __shared__ uint32_t tag_s, bank_s;
     // queries while scoring, top-k keys of long contexts, attention merges
@@ -173,23 +230,34 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    for (int b0 = 0; b0 < a.B; b0 += kThreads) {
-        const int b = b0 + tid;
-        uint32_t n = 0;
-        if (b < a.B) {
-            const int L = a.s.seq_lens[b];
-            const bool ok = L >= 1 && L <= a.s.max_blocks * kPage;
-            const int nb = ok ? (L + kPage - 1) / kPage : -1;
-            lens[b] = ok ? L : -1;
-            // with the KV append the newest token (L - 1) is the one touched
-            fps[b] = APPEND ? (ok ? L - 1 : -1) : a.s.first_pos ? a.s.first_pos[b] : -1;
-            n = (uint32_t)Hkv * (uint32_t)(kSegmentCost + (ok ? nb : 1));
+    // (Sequences past the first window only add to the window totals; a window
+    // is loaded when a share first reaches its rows.)
+    {
+        int Lc = tid < a.B ? a.s.seq_lens[tid] : 0;
+        uint32_t carry = 0u;  // rows before b0
+        for (int b0 = 0; b0 < a.B; b0 += kThreads) {
+            const int b = b0 + tid;
+            // the next lengths are in flight during this scan
+            const int Ln = b + kThreads < a.B ? a.s.seq_lens[b + kThreads] : 0;
+            uint32_t n = 0;
+            if (b < a.B) {
+                const int L = valid_len(Lc, a.s.max_blocks);
+                n = unit_rows(L, Hkv);
+                if (b < kWin) {
+                    lens[b] = L;
+                    fps[b] = touched_pos<APPEND>(a, b, L);
+                }
+            }
+            const uint32_t before = carry + (uint32_t)sel::wg_exclusive_scan((int)n, scan_red);
+            if (b < a.B && b < kWin) {
+                rows[b] = before;
+                if (b == min(a.B, kWin) - 1) rows[b + 1] = before + n;
+            }
+            if (b < a.B && b % kWin == 0) wrows[b / kWin] = before;
+            if (b == a.B - 1) wrows[(a.B + kWin - 1) / kWin] = before + n;
+            carry += (uint32_t)(scan_red[0] + scan_red[1] + scan_red[2] + scan_red[3]);
+            Lc = Ln;
         }
-        const uint32_t carry = b0 == 0 ? 0u : rows[b0];
-        const int before = sel::wg_exclusive_scan((int)n, scan_red);
-        if (b < a.B) rows[b + 1] = carry + (uint32_t)before + n;
-        if (b0 == 0 && tid == 0) rows[0] = 0u;
-        __syncthreads();
     }
     if (tid == 0) {
         const uint32_t bank = bank0 & 1u;
@@ -216,8 +284,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
     // claimed it), then chunks of the rest while any are left (shares end at
     // different times: the workgroups that finish first take more of the rest),
     // then, in a workgroup that holds no phase-2 item, any share still unclaimed
-    const uint64_t R = rows[a.B];
+    const int nwin = (a.B + kWin - 1) / kWin;
+    const uint64_t R = wrows[nwin];
     const uint64_t RS = R - R / kStealFrac;
+    int base = 0, wlen = min(a.B, kWin);  // the window in LDS
     uint32_t r = 0, r1 = 0;
     if (owns_s) {
         r = (uint32_t)(RS * blockIdx.x / gridDim.x);
@@ -264,6 +334,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
             b = 0;
             continue;
         }
+        if (r < rows[0] || r >= rows[wlen]) {  // the rows of another window
+            int k = 0;
+            while (k + 1 < nwin && wrows[k + 1] <= r) ++k;
+            base = k * kWin;
+            wlen = min(a.B - base, kWin);
+            load_window<APPEND>(a, base, wlen, wrows[k], rows, lens, fps, scan_red);
+            b = 0;
+        }
         if (rows[b] > r) b = 0;
         while (rows[b + 1] <= r) ++b;
         const int nb = lens[b] < 0 ? -1 : (lens[b] + kPage - 1) / kPage;
@@ -275,8 +353,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
         const int j1 = (int)(e > kSegmentCost ? e - kSegmentCost : 0u);
         if (j1 > j0) {
             sel::score_segment<T, D, kScanRows, kRun, APPEND>(
-                a.s, b, (int)g, j0, j1, nb, lens[b], fps[b], sm, crow,
-                a.ready + ((size_t)b * Hkv + g) * kReadyStride, tag);
+                a.s, base + b, (int)g, j0, j1, nb, lens[b], fps[b], sm, crow,
+                a.ready + ((size_t)(base + b) * Hkv + g) * kReadyStride, tag);
             __syncthreads();  // LDS is reused by the next segment
         }
         r += e - o;
@@ -292,7 +370,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
         if (item >= total) break;
         const int unit = item / a.nsplit, split = item % a.nsplit;
         const int bu = unit / Hkv;
-        const int L = lens[bu];
+        // the length from LDS when the sequence lies in the window held there
+        const int L = bu >= base && bu < base + wlen ? lens[bu - base]
+                                                     : valid_len(a.s.seq_lens[bu], a.s.max_blocks);
         const int nb = L < 0 ? -1 : (L + kPage - 1) / kPage;
         // the sequence's block-table row is requested before the wait, so that
         // the attention finds the selected blocks' pages in LDS

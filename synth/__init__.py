@@ -272,6 +272,92 @@ def make_config(config: int, variant: int = 0, *, context: Optional[int] = None,
     return make_batch(seed=1000 * config + variant, name=name, **spec)
 
 
+def make_device_batch(*, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                      context: int, top_k: int, seed: int, device, dtype=torch.bfloat16,
+                      offset_std: float = 0.5, spare_pages: int = 2, chunk_pages: int = 1 << 16,
+                      name: str = "device") -> Batch:
+    """A batch of equal-length sequences drawn directly in device memory, for shapes
+    whose caches do not fit in host memory (the one-GPU share of a large serving
+    batch).  Same value model and layouts as ``make_batch`` with the shuffled table
+    (no heavy blocks), drawn from a device ``torch.Generator`` seeded with ``seed``
+    in page chunks (so the values differ from ``make_batch``'s for the same seed):
+    per-page key offsets, key noise, values, then queries, then filler for the
+    spare pages and the unused slots of each sequence's last page.  A checker reads
+    the same bytes by copying the pages it needs to the host (``extract``)."""
+    if num_q_heads % num_kv_heads:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    P, hkv, D = PAGE, num_kv_heads, head_dim
+    g = torch.Generator(device=device).manual_seed(int(seed))
+    nb = (context + P - 1) // P
+    used = batch * nb
+    num_pages = used + spare_pages
+    perm = torch.randperm(num_pages, generator=g, device=device)
+    max_blocks = nb + 1
+    bt = torch.empty((batch, max_blocks), dtype=torch.int64, device=device)
+    bt[:, :nb] = perm[:used].view(batch, nb)
+    filler_page = perm[used:used + 1] if spare_pages > 0 else perm[:1]
+    bt[:, nb:] = filler_page
+    k = torch.empty((num_pages, hkv, P, D), dtype=dtype, device=device)
+    v = torch.empty((num_pages, hkv, D, P), dtype=dtype, device=device)
+    for c0 in range(0, num_pages, chunk_pages):
+        c1 = min(num_pages, c0 + chunk_pages)
+        off = torch.randn((c1 - c0, hkv, 1, D), generator=g, device=device) * offset_std
+        kc = torch.randn((c1 - c0, hkv, P, D), generator=g, device=device)
+        kc += off
+        k[c0:c1] = kc.to(dtype)
+        v[c0:c1] = torch.randn((c1 - c0, hkv, D, P), generator=g, device=device).to(dtype)
+        del off, kc
+    q = torch.randn((batch, num_q_heads, D), generator=g, device=device).to(dtype)
+    spare = perm[used:]
+    if spare.numel():
+        k[spare] = (torch.randn((spare.numel(), hkv, P, D), generator=g, device=device)
+                    * FILLER_SCALE).to(dtype)
+        v[spare] = (torch.randn((spare.numel(), hkv, D, P), generator=g, device=device)
+                    * FILLER_SCALE).to(dtype)
+    last_valid = context - (nb - 1) * P
+    if last_valid < P:
+        last = bt[:, nb - 1]
+        n_inv = P - last_valid
+        k[last, :, last_valid:, :] = (torch.randn((batch, hkv, n_inv, D), generator=g,
+                                                  device=device) * FILLER_SCALE).to(dtype)
+        v[last, :, :, last_valid:] = (torch.randn((batch, hkv, D, n_inv), generator=g,
+                                                  device=device) * FILLER_SCALE).to(dtype)
+    lens = torch.full((batch,), context, dtype=torch.int32, device=device)
+    return Batch(name=name, seed=int(seed), batch=batch, num_q_heads=num_q_heads,
+                 num_kv_heads=hkv, head_dim=D, page_size=P, num_pages=num_pages,
+                 max_blocks=max_blocks, top_k=int(top_k), dtype=dtype, q=q, k_cache=k,
+                 v_cache=v, block_table=bt.to(torch.int32), seq_lens=lens,
+                 notes={"table": "shuffled", "device": str(device),
+                        "filler_page": int(filler_page[0])})
+
+
+def extract(bt: Batch, seqs: Sequence[int]) -> tuple[Batch, torch.Tensor]:
+    """The sub-batch of sequences ``seqs`` of ``bt`` (any device) on the host, with
+    their pages renumbered 0 .. n-1 in table order plus one filler page, and the
+    original page id of each new page.  Pure indexing and copies."""
+    sel = torch.as_tensor(list(seqs), dtype=torch.int64, device=bt.block_table.device)
+    lens = bt.seq_lens[sel].to(torch.int64)
+    nbs = (lens + bt.page_size - 1) // bt.page_size
+    table = bt.block_table[sel].to(torch.int64)
+    pages = torch.cat([table[i, :int(nbs[i])] for i in range(len(seqs))])
+    filler = int(bt.notes.get("filler_page", int(table[0, -1])))
+    pages = torch.cat([pages, torch.tensor([filler], device=pages.device)])
+    n = pages.numel()
+    new_bt = torch.full((len(seqs), bt.max_blocks), n - 1, dtype=torch.int32)
+    cur = 0
+    for i in range(len(seqs)):
+        m = int(nbs[i])
+        new_bt[i, :m] = torch.arange(cur, cur + m, dtype=torch.int32)
+        cur += m
+    sub = Batch(name=bt.name + "-extract", seed=bt.seed, batch=len(seqs),
+                num_q_heads=bt.num_q_heads, num_kv_heads=bt.num_kv_heads, head_dim=bt.head_dim,
+                page_size=bt.page_size, num_pages=n, max_blocks=bt.max_blocks, top_k=bt.top_k,
+                dtype=bt.dtype, q=bt.q[sel].cpu(), k_cache=bt.k_cache[pages].cpu(),
+                v_cache=bt.v_cache[pages].cpu(), block_table=new_bt, seq_lens=lens.to(torch.int32).cpu(),
+                notes=dict(bt.notes, extracted=list(seqs)))
+    return sub, pages.cpu()
+
+
 def make_new_tokens(bt: Batch, seed: int, scale: float = 1.0) -> tuple[torch.Tensor, torch.Tensor]:
     """A fresh key and value per (sequence, KV head), [B, Hkv, D] in the batch's dtype:
     the token a decode step appends at position seq_lens - 1.  Keys carry the same

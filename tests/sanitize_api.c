@@ -195,7 +195,7 @@ int main(void) {
            BTK_ERR_WORKSPACE);
     {
         btk_problem_t big = base();
-        big.batch = 1025;
+        big.batch = 65537;
         const size_t nb = btk_workspace_bytes(&big, 64);
         EXPECT(btk_decode_step(&big, dev, dev, dev, di, di, di, wf, 64, wi, dev, NULL, ws, nb, NULL),
                BTK_ERR_UNSUPPORTED);

@@ -145,7 +145,7 @@ def test_local_attend_and_decode_step_validate_before_launch():
     assert lib.btk_decode_step(p, *args(k_=0)) == btk.BTK_ERR_SHAPE
     assert lib.btk_decode_step(p, *args(wsn=need - 1)) == btk.BTK_ERR_WORKSPACE
     assert lib.btk_decode_step(p, *args(ws=None)) == btk.BTK_ERR_WORKSPACE
-    big = _problem(batch=1025, max_blocks_per_seq=64)
+    big = _problem(batch=65537, max_blocks_per_seq=64)
     assert lib.btk_decode_step(ctypes.byref(big), *args(wsn=1 << 40)) == btk.BTK_ERR_UNSUPPORTED
     bad = ctypes.byref(_problem(head_dim=96))
     assert lib.btk_decode_step(bad, *args()) == btk.BTK_ERR_UNSUPPORTED
@@ -238,7 +238,7 @@ def test_decode_step_noalloc_validates_before_any_hip_call():
     assert lib.btk_decode_step_noalloc(p, *args(k_=8193)) == btk.BTK_ERR_SHAPE
     bad = ctypes.byref(_problem(head_dim=96))
     assert lib.btk_decode_step_noalloc(bad, *args()) == btk.BTK_ERR_UNSUPPORTED
-    big = _problem(batch=1025, max_blocks_per_seq=64)
+    big = _problem(batch=65537, max_blocks_per_seq=64)
     assert lib.btk_decode_step_noalloc(ctypes.byref(big), *args()) == btk.BTK_ERR_UNSUPPORTED
     # more than 16384 units, or scores beyond the 64 MiB array
     units = _problem(batch=1024, num_q_heads=32, num_kv_heads=32, max_blocks_per_seq=16)

@@ -357,10 +357,22 @@ STEP_CASES = [("config1", dict(cfg=1)), ("config2", dict(cfg=2)), ("config3", di
                                         dtype=torch.float32))),
               # the largest batch the single launch takes: the row prefix is built
               # over four 256-sequence chunks and 2048 units share 512 workgroups
-              ("max-batch-1024", dict(kw=dict(batch=1024, num_q_heads=8, num_kv_heads=2,
-                                              head_dim=128,
-                                              seq_lens=[1 + (i * 7919) % 700 for i in range(1024)],
-                                              top_k=8, seed=34)))]
+              ("batch-1024", dict(kw=dict(batch=1024, num_q_heads=8, num_kv_heads=2,
+                                          head_dim=128,
+                                          seq_lens=[1 + (i * 7919) % 700 for i in range(1024)],
+                                          top_k=8, seed=34))),
+              # past one 1024-sequence window of the row prefix: shares and stolen
+              # chunks reload the window they fall in, items read lengths directly
+              ("windows-3000-hkv1", dict(kw=dict(batch=3000, num_q_heads=4, num_kv_heads=1,
+                                                 head_dim=128,
+                                                 seq_lens=[1 + (i * 7919) % 400
+                                                           for i in range(3000)],
+                                                 top_k=8, seed=36))),
+              ("windows-2049-hkv2-fp32", dict(kw=dict(batch=2049, num_q_heads=8, num_kv_heads=2,
+                                                      head_dim=64,
+                                                      seq_lens=[1 + (i * 104729) % 333
+                                                                for i in range(2049)],
+                                                      top_k=5, seed=37, dtype=torch.float32)))]
 
 
 @pytest.mark.parametrize("label,spec", STEP_CASES, ids=[c[0] for c in STEP_CASES])

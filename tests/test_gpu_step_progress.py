@@ -54,7 +54,11 @@ CASES = [("config3", dict(cfg=3)),
          # 2048 items: no workgroup is without items, so workgroup 0 claims every share
          ("no-idle-1024", dict(kw=dict(batch=1024, num_q_heads=8, num_kv_heads=2, head_dim=128,
                                        seq_lens=[1 + (i * 7919) % 700 for i in range(1024)],
-                                       top_k=8, seed=34)))]
+                                       top_k=8, seed=34))),
+         # several row-prefix windows: taken-over shares lie in any of them
+         ("windows-2500", dict(kw=dict(batch=2500, num_q_heads=4, num_kv_heads=1, head_dim=128,
+                                       seq_lens=[1 + (i * 7919) % 300 for i in range(2500)],
+                                       top_k=8, seed=38)))]
 
 
 @pytest.mark.parametrize("append", [False, True], ids=["step", "step+append"])
