@@ -566,32 +566,41 @@ def main(argv=None):
     bon = None
     if args.best_of_n:
         b4 = synth.make_config(4)
-        d4 = b4.to(dev)
-        p4 = btk.make_problem(d4.q, d4.k_cache, d4.block_table)
-        c4 = torch.zeros((b4.num_pages, b4.num_kv_heads, b4.head_dim), device=dev)
-        btk.btk_centroid_update(d4.k_cache, d4.block_table, d4.seq_lens, c4, problem=p4)
-        w4 = btk.new_workspace(p4, b4.top_k, dev)
-        i4 = torch.empty((b4.batch, b4.num_kv_heads, b4.top_k), dtype=torch.int32, device=dev)
-        j4 = torch.empty_like(i4)
         prefix = b4.notes.get("shared_prefix", 2048) // 16
-        run_sel = lambda: btk.btk_select(d4.q, c4, d4.block_table, d4.seq_lens, b4.top_k, w4,  # noqa: E731
-                                         indices=i4, problem=p4)
-        run_shr = lambda: btk.btk_select_shared(d4.q, c4, d4.block_table, d4.seq_lens,  # noqa: E731
-                                                [0, b4.batch], [prefix], b4.top_k, w4,
-                                                indices=j4, problem=p4)
+        k4 = b4.top_k
+        # six replicas (about 400 MB of centroid rows) so that cycling through
+        # them misses the 256 MB last-level cache: "cold"; replica 0 alone: "warm"
+        r4 = []
+        for i in range(6):
+            d4 = b4.to(dev)
+            p4 = btk.make_problem(d4.q, d4.k_cache, d4.block_table)
+            c4 = torch.zeros((b4.num_pages, b4.num_kv_heads, b4.head_dim), device=dev)
+            btk.btk_centroid_update(d4.k_cache, d4.block_table, d4.seq_lens, c4, problem=p4)
+            w4 = btk.new_workspace(p4, k4, dev)
+            i4 = torch.empty((b4.batch, b4.num_kv_heads, k4), dtype=torch.int32, device=dev)
+            j4 = torch.empty_like(i4)
+            r4.append((d4, p4, c4, w4, i4, j4))
+
+        def run_sel(r):
+            d4, p4, c4, w4, i4, _ = r
+            btk.btk_select(d4.q, c4, d4.block_table, d4.seq_lens, k4, w4, indices=i4, problem=p4)
+
+        def run_shr(r):
+            d4, p4, c4, w4, _, j4 = r
+            btk.btk_select_shared(d4.q, c4, d4.block_table, d4.seq_lens, [0, b4.batch], [prefix],
+                                  k4, w4, indices=j4, problem=p4)
+
         # each kernel is about as short as the host's time to issue it, so a host
         # stall would land in a plain loop's time: the calls are captured in a
-        # HIP graph (20 back to back) and the median of 10 timed replays is kept
-        times = {}
-        per_graph = 20
-        for name, fn in (("select", run_sel), ("select_shared", run_shr)):
-            for _ in range(5):
-                fn()
+        # HIP graph (24 back to back) and the median of 10 timed replays is kept
+        def graph_us(fn, rs):
+            for r in rs:
+                fn(r)
             torch.cuda.synchronize()
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                for _ in range(per_graph):
-                    fn()
+                for i in range(24):
+                    fn(rs[i % len(rs)])
             g.replay()
             torch.cuda.synchronize()
             reps_us = []
@@ -601,19 +610,29 @@ def main(argv=None):
                 g.replay()
                 e1.record(stream)
                 torch.cuda.synchronize()
-                reps_us.append(1e3 * e0.elapsed_time(e1) / per_graph)
-            times[name] = sorted(reps_us)[len(reps_us) // 2]
-        if not torch.equal(i4, j4) or btk.workspace_error_bits(w4):
-            raise RuntimeError("shared-prefix selection disagrees with select")
+                reps_us.append(1e3 * e0.elapsed_time(e1) / 24)
+            return sorted(reps_us)[len(reps_us) // 2]
+
+        times = {"select_cold": graph_us(run_sel, r4), "select_shared_cold": graph_us(run_shr, r4),
+                 "select_warm": graph_us(run_sel, r4[:1]),
+                 "select_shared_warm": graph_us(run_shr, r4[:1])}
+        for _, _, _, w4, i4, j4 in r4:
+            if not torch.equal(i4, j4) or btk.workspace_error_bits(w4):
+                raise RuntimeError("shared-prefix selection disagrees with select")
         sel4 = algorithmic_bytes(b4.seq_lens.tolist(), b4.num_q_heads, b4.num_kv_heads,
                                  b4.head_dim, b4.top_k, 2)["select"]
         saved = (b4.batch - 1) * b4.num_kv_heads * prefix * 4 * b4.head_dim
         bon = {"workload": "qwen3-30b-a3b-shaped Best-of-N: B=16 samples sharing a 2048-token "
                            "prompt + 30720 private tokens, Hq=32, Hkv=4, D=128, bf16, top_k=64",
-               "select_us": round(times["select"], 2),
-               "select_shared_us": round(times["select_shared"], 2),
+               "select_us": round(times["select_cold"], 2),
+               "select_shared_us": round(times["select_shared_cold"], 2),
+               "select_warm_us": round(times["select_warm"], 2),
+               "select_shared_warm_us": round(times["select_shared_warm"], 2),
                "select_bytes": sel4, "select_shared_bytes": sel4 - saved,
-               "note": "same inputs, caches warm for both; identical indices; median of 10 replays of a HIP graph of 20 calls"}
+               "note": "cold: six replicas in turn (about 400 MB of centroid rows, more than the "
+                       "256 MB last-level cache); warm: one replica; identical indices; median "
+                       "of 10 replays of a HIP graph of 24 calls"}
+        del r4
 
     # the step with the KV append fused in (btk_decode_step_append): the appended
     # key and value are each sequence's newest token as drawn, so every replica's
