@@ -215,7 +215,9 @@ enum ListMode : int { kSelected = 0, kAll = 1, kRecent = 2, kMasked = 3 };
 // lds_list, the split's share of the selection in LDS (entry i of the list at
 // lds_list[i - split * bps]) instead of a.indices; L_known >= 0, the sequence
 // length; lds_pages (or NULL), the sequence's block-table row in LDS.
-template <typename T, int D, int MODE, int kG>
+// SPLITS = false: the caller guarantees one split per unit (nsplit_max = 1), and
+// the split-merge code is left out of the instance.
+template <typename T, int D, int MODE, int kG, bool SPLITS = true>
 __device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int split, float *smem,
                                             int *is_last_p, const int32_t *lds_list = nullptr,
                                             int L_known = -1,
@@ -415,7 +417,7 @@ __device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int s
                 }
             }
         }
-        if (nsplit == 1) {
+        if (!SPLITS || nsplit == 1) {
             store_out<T>(outp + (size_t)h * D + d, acc / Z);
             if (d == 0 && a.lse) a.lse[(size_t)b * a.Hq + (size_t)g * r + h] = M * kLn2 + logf(Z);
         } else {
@@ -426,7 +428,7 @@ __device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int s
             }
         }
     }
-    if (nsplit == 1) return;
+    if (!SPLITS || nsplit == 1) return;
 
     // ---- the last split of this unit merges all splits
     if (!arrive_last(&a.counters[(size_t)unit * kStateStride], (uint32_t)nsplit, &is_last)) return;
@@ -437,6 +439,26 @@ __device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int s
     float *hz = wz + nsplit * r;       // [r] merged normaliser
     __syncthreads();                   // the wave-merge area is free again
     const float *parts = a.partials + (size_t)unit * a.nsplit_max * row;
+    // With few splits the split outputs are requested together with the maxima
+    // and normalisers (one round trip instead of two): at most 4 splits of at
+    // most 4 values per thread, held in registers until the weights are known
+    // (the four-split steps of 64 units took 2.5-2.8 us less; allowing 8 splits
+    // gained less, from the registers it holds).
+    constexpr int kFastSplits = 4, kFastPer = 4;
+    const bool fast = nsplit <= kFastSplits && r * D <= kFastPer * kThreads;
+    float ov[kFastPer][kFastSplits];
+    if (fast) {
+#pragma unroll
+        for (int i = 0; i < kFastPer; ++i) {
+            const int idx = tid + i * kThreads;
+            const float *src = parts + min(idx, r * D - 1);  // per-lane address, advanced by row
+#pragma unroll
+            for (int sp = 0; sp < kFastSplits; ++sp) {
+                ov[i][sp] = sp < nsplit ? load_relaxed(src) : 0.f;
+                src += row;
+            }
+        }
+    }
     for (int i = tid; i < nsplit * r; i += kThreads) {
         const int sp = i / r, h = i % r;
         wm[i] = load_relaxed(parts + (size_t)sp * row + r * D + h);
@@ -457,6 +479,21 @@ __device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int s
         if (a.lse) a.lse[(size_t)b * a.Hq + (size_t)g * r + tid] = M * kLn2 + logf(Z);
     }
     __syncthreads();
+    if (fast) {  // the same sums, in the same order, from registers
+#pragma unroll
+        for (int i = 0; i < kFastPer; ++i) {
+            const int idx = tid + i * kThreads;
+            if (idx < r * D) {
+                const int h = idx / D;
+                float acc = 0.f;
+#pragma unroll
+                for (int sp = 0; sp < kFastSplits; ++sp)
+                    if (sp < nsplit) acc += wm[sp * r + h] * ov[i][sp];
+                store_out<T>(outp + idx, acc / hz[h]);
+            }
+        }
+        return;
+    }
     // weighted sum of the split outputs: loads of eight splits in flight per thread
     for (int idx = tid; idx < r * D; idx += kThreads) {
         const int h = idx / D;

@@ -185,8 +185,10 @@ __device__ void load_window(const StepArgs &a, int base, int wlen, uint32_t firs
 }
 
 // APPEND: the KV append of the step is fused in (a separate instantiation, so
-// that the plain step carries none of its code).
-template <typename T, int D, bool APPEND>
+// that the plain step carries none of its code).  SPLITS: the attention of a
+// unit may be split over several items (instances without it carry no split
+// merge, whose code alone made the one-split step slower).
+template <typename T, int D, bool APPEND, bool SPLITS>
 __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
     __shared__ float qs[D];
     __shared__ int pages[kRun];
@@ -418,7 +420,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
         // the appended token's cache stores are done before the block can be read
         if (APPEND) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        att::attend_item<T, D, att::kSelected, kStageBlocks>(
+        att::attend_item<T, D, att::kSelected, kStageBlocks, SPLITS>(
             a.t, unit, split, dyn, &flag, list, L < 0 ? 0 : L, row_lds ? pages : nullptr);
         __syncthreads();  // LDS is reused by the next item
     }
@@ -448,7 +450,7 @@ size_t step_lds_floats(const Dims &d, const AttendPlan &ap) {
 }
 
 // resident workgroups of the step kernel on this device (cached per device)
-template <typename T, int D, bool APPEND>
+template <typename T, int D, bool APPEND, bool SPLITS>
 hipError_t resident_workgroups(size_t lds, int *out) {
     static int cached[64][2] = {};
     int dev = 0;
@@ -460,8 +462,8 @@ hipError_t resident_workgroups(size_t lds, int *out) {
         return hipSuccess;
     }
     int per_cu = 0, cus = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_step_kernel<T, D, APPEND>,
-                                                     kThreads, lds);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &per_cu, decode_step_kernel<T, D, APPEND, SPLITS>, kThreads, lds);
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
@@ -472,24 +474,26 @@ hipError_t resident_workgroups(size_t lds, int *out) {
     return hipSuccess;
 }
 
+template <typename T, int D, bool APPEND, bool SPLITS>
+hipError_t launch_instance(size_t lds, const StepArgs &a, hipStream_t stream) {
+    int grid = 0;
+    const hipError_t e = resident_workgroups<T, D, APPEND, SPLITS>(lds, &grid);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_step_kernel<T, D, APPEND, SPLITS>), dim3(grid), dim3(kThreads),
+                       lds, stream, a);
+    return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t launch(const Dims &d, const SelectPlan &sp, const AttendPlan &ap, StepArgs a,
                   hipStream_t stream) {
     const size_t lds = sizeof(float) * step_lds_floats(d, ap);
-    int grid = 0;
-    hipError_t e;
-    if (a.s.k_new) {
-        e = resident_workgroups<T, D, true>(lds, &grid);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((decode_step_kernel<T, D, true>), dim3(grid), dim3(kThreads), lds,
-                           stream, a);
-    } else {
-        e = resident_workgroups<T, D, false>(lds, &grid);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((decode_step_kernel<T, D, false>), dim3(grid), dim3(kThreads), lds,
-                           stream, a);
-    }
-    return hipGetLastError();
+    const bool splits = ap.nsplit_max > 1;
+    if (a.s.k_new)
+        return splits ? launch_instance<T, D, true, true>(lds, a, stream)
+                      : launch_instance<T, D, true, false>(lds, a, stream);
+    return splits ? launch_instance<T, D, false, true>(lds, a, stream)
+                  : launch_instance<T, D, false, false>(lds, a, stream);
 }
 
 }  // namespace
