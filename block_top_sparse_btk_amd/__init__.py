@@ -140,6 +140,30 @@ def workspace_error_bits(workspace: torch.Tensor) -> int:
     return int(workspace[:4].view(torch.int32).item())
 
 
+# workspace word 0, as include/btk.h defines it
+ERROR_BITS = {1: "sequence length out of range", 2: "page id out of range",
+              4: "block index out of range", 8: "decode-step wait gave up",
+              16: "declared shared prefix differs between members"}
+
+
+class BtkDeviceError(RuntimeError):
+    """Raised by check_workspace when a kernel flagged an input or a wait."""
+
+    def __init__(self, bits: int, what: str):
+        names = [n for b, n in ERROR_BITS.items() if bits & b] or [f"bits {bits:#x}"]
+        super().__init__(f"{what}: device error bits {bits:#x} ({'; '.join(names)})")
+        self.bits = bits
+
+
+def check_workspace(workspace: torch.Tensor, what: str = "btk") -> None:
+    """Waits for the workspace's device (a synchronisation) and raises
+    BtkDeviceError if any error bit is set (the bits are sticky: clear word 0 to
+    reuse the workspace after an error)."""
+    bits = workspace_error_bits(workspace)
+    if bits:
+        raise BtkDeviceError(bits, what)
+
+
 def _dev(t: torch.Tensor, name: str, dtype=None, device=None) -> int:
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
@@ -366,8 +390,10 @@ def btk_token_topk_attend(q, k_cache, v_cache, block_table, seq_lens, top_tokens
 
 def btk_decode_step(q, k_cache, v_cache, block_table, seq_lens, centroids, top_k, workspace,
                     first_pos=None, indices=None, out=None, lse=None, sm_scale: float = 0.0,
-                    problem: Optional[btk_problem_t] = None):
-    """S1 (touched pages) + S2 + S3 + S4 in one launch; returns (out, indices)."""
+                    problem: Optional[btk_problem_t] = None, check: bool = False):
+    """S1 (touched pages) + S2 + S3 + S4 in one launch; returns (out, indices).
+    check=True synchronises and raises BtkDeviceError if the launch set an error
+    bit (an out-of-range input, or bit 8: a wait that gave up)."""
     dev = q.device
     problem = problem or make_problem(q, k_cache, block_table, sm_scale)
     out = torch.empty_like(q) if out is None else out
@@ -390,6 +416,8 @@ def btk_decode_step(q, k_cache, v_cache, block_table, seq_lens, centroids, top_k
                                 _dev(workspace, "workspace", torch.uint8, dev), workspace.numel(),
                                 _stream(dev))
     _check(st, "btk_decode_step")
+    if check:
+        check_workspace(workspace, "btk_decode_step")
     return out, indices
 
 
@@ -439,9 +467,10 @@ def btk_probe_row_read(src, rows=None, row_ids=None, sink=None):
 
 def btk_decode_step_append(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, centroids,
                            top_k, workspace, indices=None, out=None, lse=None, sm_scale: float = 0.0,
-                           problem: Optional[btk_problem_t] = None):
+                           problem: Optional[btk_problem_t] = None, check: bool = False):
     """The decode step with the KV append fused in: k_new / v_new [B, Hkv, D] are written
-    into the caches at position seq_lens - 1, then S1 + S2 + S3 + S4; returns (out, indices)."""
+    into the caches at position seq_lens - 1, then S1 + S2 + S3 + S4; returns (out, indices).
+    check: as btk_decode_step."""
     dev = q.device
     problem = problem or make_problem(q, k_cache, block_table, sm_scale)
     out = torch.empty_like(q) if out is None else out
@@ -468,17 +497,23 @@ def btk_decode_step_append(q, k_new, v_new, k_cache, v_cache, block_table, seq_l
                                        _dev(workspace, "workspace", torch.uint8, dev),
                                        workspace.numel(), _stream(dev))
     _check(st, "btk_decode_step_append")
+    if check:
+        check_workspace(workspace, "btk_decode_step_append")
     return out, indices
 
 
 def sparse_decode_step(q, k_cache, v_cache, block_table, seq_lens, centroids, top_k, workspace,
                        first_pos=None, out=None, indices=None, lse=None, scores=None,
-                       sm_scale: float = 0.0, problem: Optional[btk_problem_t] = None):
-    """One decode step of the method: S1 (touched pages), S2+S3, S4, all on the current stream."""
+                       sm_scale: float = 0.0, problem: Optional[btk_problem_t] = None,
+                       check: bool = False):
+    """One decode step of the method: S1 (touched pages), S2+S3, S4, all on the current stream.
+    check: as btk_decode_step."""
     problem = problem or make_problem(q, k_cache, block_table, sm_scale)
     btk_centroid_update(k_cache, block_table, seq_lens, centroids, first_pos, problem=problem)
     indices = btk_select(q, centroids, block_table, seq_lens, top_k, workspace,
                          indices=indices, scores=scores, problem=problem)
     out = btk_sparse_attend(q, k_cache, v_cache, block_table, seq_lens, indices, workspace,
                             out=out, lse=lse, problem=problem)
+    if check:
+        check_workspace(workspace, "sparse_decode_step")
     return out, indices

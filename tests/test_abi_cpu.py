@@ -254,3 +254,14 @@ def test_probe_row_read_validates_on_host():
     assert lib.btk_probe_row_read(FAKE, 4096, None, -1, sink, None) == btk.BTK_ERR_SHAPE
     assert lib.btk_probe_row_read(FAKE, 4096, None, 9, sink, None) == btk.BTK_ERR_SHAPE
     assert lib.btk_probe_row_read(FAKE, 4096, None, 0, sink, None) == btk.BTK_OK
+
+
+def test_check_workspace_names_the_error_bits():
+    import torch
+    ws = torch.zeros(256, dtype=torch.uint8)
+    btk.check_workspace(ws)  # no bits: no error
+    ws[:4].view(torch.int32)[0] = 8 | 2
+    with pytest.raises(btk.BtkDeviceError) as e:
+        btk.check_workspace(ws, "step")
+    assert e.value.bits == 10
+    assert "wait gave up" in str(e.value) and "page id" in str(e.value)
