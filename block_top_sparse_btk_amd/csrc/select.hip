@@ -213,9 +213,52 @@ __global__ __launch_bounds__(kThreads, SHARED ? 4 : 5) void select_kernel(Select
     }
 }
 
+// Compute units of the current device (cached per device).
+hipError_t device_cus(int *out) {
+    static int cached[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    int &c = cached[dev & 63];
+    if (c <= 0) {
+        e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        if (c <= 0) c = 1;
+    }
+    *out = c;
+    return hipSuccess;
+}
+
+// The chunk: the smallest multiple of 64 blocks from 128 up whose chunks all fit
+// in one round of resident workgroups (five per CU by the kernel's launch
+// bounds, four in the shared-prefix form, whose shared items come first) even
+// if every sequence had max_blocks blocks.  Smaller chunks shorten the tail in
+// which only the largest chunks are still streaming; chunks that wait for a
+// free slot lengthen it more.  Measured on the Qwen3-8B-shaped batch: chunks of
+// 512 blocks 40.2 us, 448 37.5 us (this rule), 256 44.4 us (about as many
+// chunks as slots); the other workloads within 1 us of their best size.
+SelectPlan fit_chunks(const Dims &d, int cus, int per_cu, int extra) {
+    const size_t units = (size_t)d.B * d.Hkv;
+    const size_t slots = (size_t)cus * per_cu;
+    int chunk = 128;
+    while (chunk < kMaxChunk &&
+           units * (size_t)((d.max_blocks + chunk - 1) / chunk) + (size_t)extra > slots)
+        chunk += 64;
+    SelectPlan p;
+    p.chunk = chunk;
+    p.nchunk_max = (d.max_blocks + chunk - 1) / chunk;
+    return p;
+}
+
 template <typename T, int D>
-hipError_t launch(const Dims &d, const SelectPlan &plan, SelectArgs a, const PrefixGroups *pg,
+hipError_t launch(const Dims &d, const SelectPlan &, SelectArgs a, const PrefixGroups *pg,
                   hipStream_t stream) {
+    int cus = 0;
+    const hipError_t e = device_cus(&cus);
+    if (e != hipSuccess) return e;
+    const SelectPlan plan = fit_chunks(d, cus, pg ? 4 : 5, pg ? pg->item0[pg->n] : 0);
+    a.chunk = plan.chunk;
+    a.nchunk_max = plan.nchunk_max;
     const size_t grid = (size_t)d.B * d.Hkv * plan.nchunk_max;
     // the top-k bitmaps of more than 2048 blocks (two words per 32 blocks)
     const size_t lds = d.max_blocks > 32 * kWave ? sizeof(uint32_t) * 512 : 0;
@@ -231,10 +274,9 @@ hipError_t launch(const Dims &d, const SelectPlan &plan, SelectArgs a, const Pre
 }  // namespace
 
 SelectPlan plan_select(const Dims &d) {
-    // At least about 1024 chunks (four per resident workgroup at two per CU),
-    // each as large as that allows: a chunk's setup (queries, page list, length)
-    // and its closing store-and-count are round trips in which the workgroup
-    // streams nothing, so fewer, larger chunks keep more bytes in flight.
+    // (host default without a device query; the select launch refits the chunk
+    // to the device, see fit_chunks)
+    // At least about 1024 chunks, each as large as that allows.
     const size_t rows = (size_t)d.B * d.Hkv * d.max_blocks;
     int chunk = 64;
     while (chunk < kMaxChunk && rows / (size_t)(chunk * 2) >= 1024) chunk *= 2;
