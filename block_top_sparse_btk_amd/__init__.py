@@ -92,6 +92,12 @@ def _lib():
         lib.btk_decode_step_append.restype = st
         lib.btk_decode_step_append.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
                                                vp, sz, vp]
+        lib.btk_sketch_bytes.restype = sz
+        lib.btk_sketch_bytes.argtypes = [P]
+        lib.btk_sketch_update.restype = st
+        lib.btk_sketch_update.argtypes = [P, vp, vp, vp, vp, vp, sz, vp, sz, vp]
+        lib.btk_select_sketch.restype = st
+        lib.btk_select_sketch.argtypes = [P, vp, vp, vp, sz, vp, vp, i32, vp, vp, sz, vp]
         lib.btk_probe_row_read.restype = st
         lib.btk_probe_row_read.argtypes = [vp, sz, vp, ctypes.c_int64, vp, vp]
         _LIB = lib
@@ -250,6 +256,58 @@ def btk_select(q, centroids, block_table, seq_lens, top_k, workspace, indices=No
                            _dev(workspace, "workspace", torch.uint8, dev), workspace.numel(),
                            _stream(dev))
     _check(st, "btk_select")
+    return indices
+
+
+def new_sketch(problem: btk_problem_t, device) -> torch.Tensor:
+    """A zero-filled sketch buffer for the problem (no row is usable until
+    btk_sketch_update has written it)."""
+    n = int(_lib().btk_sketch_bytes(ctypes.byref(problem)))
+    if n == 0:
+        raise ValueError("invalid problem for a sketch")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def btk_sketch_update(centroids, block_table, seq_lens, sketch, workspace, first_pos=None,
+                      problem: Optional[btk_problem_t] = None, q=None, k_cache=None):
+    """Writes the sketch rows of the blocks touched since first_pos (all when None)
+    from the fp32 centroids.  problem (or q and k_cache to build it) is required."""
+    dev = centroids.device
+    if problem is None:
+        problem = make_problem(q, k_cache, block_table)
+    _check_shapes(problem, block_table=block_table, seq_lens=seq_lens, centroids=centroids,
+                  first_pos=first_pos)
+    fp = _dev(first_pos, "first_pos", torch.int32, dev) if first_pos is not None else None
+    st = _lib().btk_sketch_update(ctypes.byref(problem), _dev(centroids, "centroids", torch.float32, dev),
+                                  _dev(block_table, "block_table", torch.int32, dev),
+                                  _dev(seq_lens, "seq_lens", torch.int32, dev), fp,
+                                  _dev(sketch, "sketch", torch.uint8, dev), sketch.numel(),
+                                  _dev(workspace, "workspace", torch.uint8, dev), workspace.numel(),
+                                  _stream(dev))
+    _check(st, "btk_sketch_update")
+
+
+def btk_select_sketch(q, centroids, sketch, block_table, seq_lens, top_k, workspace, indices=None,
+                      sm_scale: float = 0.0, problem: Optional[btk_problem_t] = None,
+                      k_cache=None):
+    """S2 + S3 through the sketch; the indices equal btk_select's."""
+    dev = q.device
+    if problem is None:
+        problem = make_problem(q, k_cache, block_table, sm_scale)
+    if indices is None:
+        indices = torch.empty((problem.batch, problem.num_kv_heads, int(top_k)), dtype=torch.int32,
+                              device=dev)
+    _check_shapes(problem, q=q, block_table=block_table, seq_lens=seq_lens, centroids=centroids,
+                  indices=indices, top_k=top_k)
+    st = _lib().btk_select_sketch(ctypes.byref(problem), _dev(q, "q", None, dev),
+                                  _dev(centroids, "centroids", torch.float32, dev),
+                                  _dev(sketch, "sketch", torch.uint8, dev), sketch.numel(),
+                                  _dev(block_table, "block_table", torch.int32, dev),
+                                  _dev(seq_lens, "seq_lens", torch.int32, dev), int(top_k),
+                                  _dev(indices, "indices", torch.int32, dev),
+                                  _dev(workspace, "workspace", torch.uint8, dev), workspace.numel(),
+                                  _stream(dev))
+    _check(st, "btk_select_sketch")
     return indices
 
 

@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 SOURCES = ["api.hip", "centroid.hip", "select.hip", "attend.hip", "step.hip", "token.hip",
-           "probe.hip"]
+           "probe.hip", "sketch.hip"]
 LIB = os.path.join(HERE, "libbtk.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

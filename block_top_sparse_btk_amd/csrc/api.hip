@@ -85,6 +85,12 @@ WorkspaceLayout workspace_layout(const Dims &d, int top_k, bool dense) {
     w.scores = 0;
     w.partials = align256(units * d.max_blocks * sizeof(float));
     w.scratch = w.partials + align256(units * nsplit * row * sizeof(float));
+    w.sk_lo = w.sk_hi = 0;
+    if (dense) {  // the sketch selection's interval ends
+        w.sk_lo = w.scratch;
+        w.sk_hi = w.sk_lo + align256(units * d.max_blocks * sizeof(float));
+        w.scratch = w.sk_hi + align256(units * d.max_blocks * sizeof(float));
+    }
     w.total = w.state_end + w.scratch;
     return w;
 }
@@ -167,6 +173,53 @@ btk_status_t btk_select(const btk_problem_t *problem, const void *q, const float
     return hip_status(btk::launch_select(d, plan, q, centroids, block_table, seq_lens, top_k,
                                          indices, sc, state + btk::kStSelect,
                                          reinterpret_cast<uint32_t *>(ws), (hipStream_t)stream));
+}
+
+size_t btk_sketch_bytes(const btk_problem_t *problem) {
+    btk::Dims d;
+    if (check_problem(problem, &d) != BTK_OK) return 0;
+    return btk::sketch_bytes(d);
+}
+
+btk_status_t btk_sketch_update(const btk_problem_t *problem, const float *centroids,
+                               const int32_t *block_table, const int32_t *seq_lens,
+                               const int32_t *first_pos, void *sketch, size_t sketch_bytes,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+    btk::Dims d;
+    btk_status_t st = check_problem(problem, &d);
+    if (st != BTK_OK) return st;
+    if (!centroids || !block_table || !seq_lens || !sketch) return BTK_ERR_NULL;
+    if (sketch_bytes < btk::sketch_bytes(d)) return BTK_ERR_WORKSPACE;
+    // the error word only: any workspace of this problem
+    const btk::WorkspaceLayout w = btk::workspace_layout(d, 1);
+    if (!workspace || workspace_bytes < w.total) return BTK_ERR_WORKSPACE;
+    return hip_status(btk::launch_sketch_update(d, centroids, block_table, seq_lens, first_pos,
+                                                sketch, reinterpret_cast<uint32_t *>(workspace),
+                                                (hipStream_t)stream));
+}
+
+btk_status_t btk_select_sketch(const btk_problem_t *problem, const void *q,
+                               const float *centroids, const void *sketch, size_t sketch_bytes,
+                               const int32_t *block_table, const int32_t *seq_lens,
+                               int32_t top_k, int32_t *indices, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+    btk::Dims d;
+    btk_status_t st = check_problem(problem, &d);
+    if (st != BTK_OK) return st;
+    if (!q || !centroids || !sketch || !block_table || !seq_lens || !indices)
+        return BTK_ERR_NULL;
+    if (!top_k_ok(top_k)) return BTK_ERR_SHAPE;
+    if (sketch_bytes < btk::sketch_bytes(d)) return BTK_ERR_WORKSPACE;
+    const btk::WorkspaceLayout w = btk::workspace_layout(d, top_k);
+    if (!workspace || workspace_bytes < w.total) return BTK_ERR_WORKSPACE;
+    char *ws = static_cast<char *>(workspace);
+    char *scratch = ws + w.scratch_at(workspace_bytes);
+    uint32_t *state = reinterpret_cast<uint32_t *>(ws + w.state);
+    return hip_status(btk::launch_select_sketch(
+        d, q, centroids, sketch, block_table, seq_lens, top_k, indices,
+        reinterpret_cast<float *>(scratch + w.sk_lo), reinterpret_cast<float *>(scratch + w.sk_hi),
+        reinterpret_cast<float *>(scratch + w.scores), state + btk::kStSelect,
+        reinterpret_cast<uint32_t *>(ws), (hipStream_t)stream));
 }
 
 btk_status_t btk_select_shared(const btk_problem_t *problem, const void *q,

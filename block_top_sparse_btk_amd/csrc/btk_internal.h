@@ -193,12 +193,26 @@ constexpr uint32_t kReadySpinLimit = 1u << 22;
 struct WorkspaceLayout {
     size_t claims, state, queue;  // offsets from the start
     size_t scores, partials;      // offsets from the start of the scratch
+    size_t sk_lo, sk_hi;          // the sketch selection's interval ends (full layout only)
     size_t state_end, scratch, total;
     // the scratch's offset in a workspace of `bytes` bytes (>= total): its last
     // `scratch` bytes, 256-aligned
     size_t scratch_at(size_t bytes) const { return (bytes - scratch) & ~(size_t)255; }
 };
 WorkspaceLayout workspace_layout(const Dims &d, int top_k, bool dense = true);
+
+// Block sketches (sketch.hip): bytes of a problem's sketch, where its code rows
+// start, the sketch update and the selection that uses it.
+size_t sketch_bytes(const Dims &d);
+size_t sketch_rows_offset(const Dims &d);
+hipError_t launch_sketch_update(const Dims &d, const float *centroids, const int32_t *block_table,
+                                const int32_t *seq_lens, const int32_t *first_pos, void *sketch,
+                                uint32_t *err, hipStream_t stream);
+hipError_t launch_select_sketch(const Dims &d, const void *q, const float *centroids,
+                                const void *sketch, const int32_t *block_table,
+                                const int32_t *seq_lens, int top_k, int32_t *indices,
+                                float *lo, float *hi, float *exact, uint32_t *counters,
+                                uint32_t *err, hipStream_t stream);
 
 // ---- launchers (return hipError_t of the launch) --------------------------
 

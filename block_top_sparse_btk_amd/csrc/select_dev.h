@@ -89,7 +89,11 @@ struct TopkOut {
     int32_t *idx;            // [top_k] or NULL
     int32_t *lds = nullptr;  // [hi - lo] or NULL
     int lo = 0, hi = 0;
+    // the keys were a subset of the blocks, in ascending block order: key i is
+    // block map[i] (LDS); NULL: key i is block i
+    const int32_t *map = nullptr;
     __device__ __forceinline__ void put(int pos, int32_t j) const {
+        if (map && j >= 0) j = map[j];
         if (idx) store_relaxed_i32(idx + pos, j);
         if (lds && pos >= lo && pos < hi) lds[pos - lo] = j;
     }

@@ -147,6 +147,56 @@ btk_status_t btk_select(const btk_problem_t *problem, const void *q, const float
                         int32_t *indices, float *scores, void *workspace,
                         size_t workspace_bytes, void *stream);
 
+/* Block sketches: an 8-bit copy of every block's fp32 centroid, kept per
+ * sequence in block-table order, from which btk_select_sketch rules blocks out
+ * of the top-k before reading their fp32 centroid rows.  Its selections are
+ * those of btk_select (the rule-out is provably safe, see btk_select_sketch).
+ * (Pith review, "What carries the argument": the method's block scores and
+ * top-k; the sketch is this library's way of reading fewer bytes for them.)
+ * Layout (btk_sketch_bytes bytes, owned by the caller): for row
+ * i = (b * num_kv_heads + g) * max_blocks_per_seq + j, an 8-byte header
+ * {int32 page + 1 (0: none), float32 scale} at offset 8 i, and head_dim code
+ * bytes at offset R + head_dim * i, R = 8 * rows rounded up to 256; code_d =
+ * rint(c_d / scale) + 128 with scale = max_d |c_d| / 127.  A sketch belongs to
+ * one (batch, num_kv_heads, max_blocks_per_seq, head_dim).  Any contents are
+ * safe: a row whose header does not name block j's current page is simply not
+ * used to rule it out; a row that names it must have been built from that
+ * page's current centroid (call btk_sketch_update after every
+ * btk_centroid_update, with the same first_pos).  Returns 0 for an invalid
+ * problem. */
+size_t btk_sketch_bytes(const btk_problem_t *problem);
+
+/* Writes the sketch rows of every block j >= first_pos[b] / 16 (every block when
+ * first_pos is NULL; negative positions count as 0) of every sequence and KV
+ * head from centroids[block_table[b][j]][g] (fp32, as btk_centroid_update left
+ * them).  A block whose page id is out of range gets an empty header and sets
+ * workspace bit 2; an invalid length sets bit 1.
+ *   sketch     in/out, sketch_bytes >= btk_sketch_bytes(problem)
+ *   workspace  any workspace of this problem (its error word is used) */
+btk_status_t btk_sketch_update(const btk_problem_t *problem, const float *centroids,
+                               const int32_t *block_table, const int32_t *seq_lens,
+                               const int32_t *first_pos, void *sketch, size_t sketch_bytes,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/* S2 + S3 with the same indices as btk_select, reading each unit's sketch rows
+ * and only the fp32 centroid rows of the blocks the sketch cannot rule out.
+ * For unit (b, g) every block gets an interval [sa - e, sa + e] from its
+ * sketch row (sa: the sketch's score; e = 0.51 * scale * sum_d |qs_d|, qs the
+ * scaled mean query), which holds the block's fp32 score as btk_select computes
+ * it, rounding included.  With tau the k_b-th largest lower end, blocks whose
+ * upper end is below tau score below k_b others and are dropped; the others are
+ * scored from their fp32 centroid rows exactly as btk_select scores them and the
+ * k_b best are kept with btk_select's tie rule.  Rows that do not name the
+ * block's current page are never dropped.
+ *   sketch     as built by btk_sketch_update, sketch_bytes >= btk_sketch_bytes()
+ *   indices    out [B][Hkv][top_k] int32, equal to btk_select's
+ *   workspace  btk_workspace_bytes(problem, top_k) bytes, as btk_select */
+btk_status_t btk_select_sketch(const btk_problem_t *problem, const void *q,
+                               const float *centroids, const void *sketch, size_t sketch_bytes,
+                               const int32_t *block_table, const int32_t *seq_lens,
+                               int32_t top_k, int32_t *indices, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
 /* S2 + S3 for Best-of-N batches, reading each shared prompt page once.  The
  * pages' cost model counts a prompt's KV as read once for all N samples (Pith
  * review, "What carries the argument", and its referee report on the

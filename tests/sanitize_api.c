@@ -220,6 +220,26 @@ int main(void) {
     EXPECT(btk_decode_step_noalloc(&p, dev, dev, dev, di, di, di, wf, 9000, wi, dev, NULL, NULL),
            BTK_ERR_SHAPE);
 
+    /* block sketches */
+    {
+        const size_t sk = btk_sketch_bytes(&p);
+        if (sk == 0) ++failures;
+        EXPECT(btk_sketch_bytes(NULL), 0);
+        EXPECT(btk_sketch_update(&p, wf, di, di, NULL, NULL, sk, ws, need, NULL), BTK_ERR_NULL);
+        EXPECT(btk_sketch_update(&p, wf, di, di, NULL, dev, sk - 1, ws, need, NULL),
+               BTK_ERR_WORKSPACE);
+        EXPECT(btk_sketch_update(&p, wf, di, di, NULL, dev, sk, NULL, need, NULL),
+               BTK_ERR_WORKSPACE);
+        EXPECT(btk_select_sketch(&p, dev, wf, dev, sk, di, di, 0, wi, ws, need, NULL),
+               BTK_ERR_SHAPE);
+        EXPECT(btk_select_sketch(&p, dev, wf, NULL, sk, di, di, 64, wi, ws, need, NULL),
+               BTK_ERR_NULL);
+        EXPECT(btk_select_sketch(&p, dev, wf, dev, sk - 1, di, di, 64, wi, ws, need, NULL),
+               BTK_ERR_WORKSPACE);
+        EXPECT(btk_select_sketch(&p, dev, wf, dev, sk, di, di, 64, wi, ws, need - 1, NULL),
+               BTK_ERR_WORKSPACE);
+    }
+
     /* counter-calibration probe */
     EXPECT(btk_probe_row_read(NULL, 4096, NULL, 8, (uint32_t *)dev, NULL), BTK_ERR_NULL);
     EXPECT(btk_probe_row_read(dev, 4096, NULL, 8, NULL, NULL), BTK_ERR_NULL);

@@ -265,3 +265,27 @@ def test_check_workspace_names_the_error_bits():
         btk.check_workspace(ws, "step")
     assert e.value.bits == 10
     assert "wait gave up" in str(e.value) and "page id" in str(e.value)
+
+
+def test_sketch_calls_validate_on_host():
+    lib = btk._lib()
+    p = _problem()
+    pp = ctypes.byref(p)
+    sk = lib.btk_sketch_bytes(pp)
+    # B * Hkv * max_blocks rows: 8-byte headers (256-aligned) then head_dim code bytes
+    rows = p.batch * p.num_kv_heads * p.max_blocks_per_seq
+    assert sk == ((8 * rows + 255) // 256) * 256 + rows * p.head_dim
+    assert lib.btk_sketch_bytes(ctypes.byref(_problem(head_dim=96))) == 0
+    need = btk.btk_workspace_bytes(p, 8)
+    args = lambda **o: [o.get("cent", FAKE), FAKE, FAKE, None, o.get("sk", FAKE), o.get("skn", sk),
+                        o.get("ws", FAKE), o.get("wsn", need), None]  # noqa: E731
+    assert lib.btk_sketch_update(pp, *args(sk=None)) == btk.BTK_ERR_NULL
+    assert lib.btk_sketch_update(pp, *args(cent=None)) == btk.BTK_ERR_NULL
+    assert lib.btk_sketch_update(pp, *args(skn=sk - 1)) == btk.BTK_ERR_WORKSPACE
+    assert lib.btk_sketch_update(pp, *args(ws=None)) == btk.BTK_ERR_WORKSPACE
+    sel = lambda **o: [FAKE, FAKE, o.get("sk", FAKE), o.get("skn", sk), FAKE, FAKE, o.get("k_", 8),
+                       FAKE, FAKE, o.get("wsn", need), None]  # noqa: E731
+    assert lib.btk_select_sketch(pp, *sel(sk=None)) == btk.BTK_ERR_NULL
+    assert lib.btk_select_sketch(pp, *sel(k_=0)) == btk.BTK_ERR_SHAPE
+    assert lib.btk_select_sketch(pp, *sel(skn=sk - 1)) == btk.BTK_ERR_WORKSPACE
+    assert lib.btk_select_sketch(pp, *sel(wsn=need - 1)) == btk.BTK_ERR_WORKSPACE
