@@ -26,7 +26,10 @@ HIPCC = "/opt/rocm/bin/hipcc"
 CLANG = "/opt/rocm/llvm/bin/clang"
 SAN = ["-fsanitize=address", "-fsanitize=undefined", "-fno-sanitize-recover=all",
        "-fno-omit-frame-pointer"]
-KERNEL_OBJS = ["centroid.o", "select.o", "attend.o", "step.o", "token.o", "probe.o"]
+# every object of the normal build except the C ABI's own
+from block_top_sparse_btk_amd import build as _hip_build  # noqa: E402
+
+KERNEL_OBJS = [s.replace(".hip", ".o") for s in _hip_build.SOURCES if s != "api.hip"]
 
 
 def _host_only(flags):
