@@ -104,6 +104,34 @@ def algorithmic_bytes(seq_lens, num_q_heads, num_kv_heads, head_dim, top_k, elem
             "dense": dense, "local": local, "token": token}
 
 
+def sketch_step_bytes(seq_lens, num_q_heads, num_kv_heads, head_dim, top_k, elem_bytes,
+                      cand_counts, sel_tokens, page=16):
+    """Bytes the step through the block sketch must move (btk_decode_step_sketch).
+
+    Per unit, as the full step (algorithmic_bytes) except the centroid scan:
+      S1:     the newest token's page keys (v_last*D*e), its centroid (4*D) and its
+              rebuilt sketch row (D + 8)
+      S2+S3:  group queries (r*D*e), every block's sketch row (n_b*(D + 8): codes and
+              header), the fp32 centroid rows of the unit's m candidates (4*D*m),
+              k indices (4*k); the sequence's block table (4*n_b) once per sequence
+      S4:     as in the full step
+    cand_counts[b][g] = m (0 when every block is kept), sel_tokens as for
+    algorithmic_bytes.
+    """
+    r, D, e, P = num_q_heads // num_kv_heads, head_dim, elem_bytes, page
+    total = 0
+    for b, L in enumerate([int(x) for x in seq_lens]):
+        nb = (L + P - 1) // P
+        v_last = L - (nb - 1) * P
+        total += 4 * nb
+        for g in range(num_kv_heads):
+            m = int(cand_counts[b][g])
+            total += v_last * D * e + 4 * D + D + 8
+            total += r * D * e + nb * (D + 8) + 4 * D * m + 4 * top_k
+            total += 8 * top_k + 2 * r * D * e + 2 * sel_tokens[b][g] * D * e
+    return total
+
+
 # ---------------------------------------------------------------- helpers
 
 def _sources_digest() -> str:
@@ -238,10 +266,19 @@ def measure_workload(name, bt, dev, steps, cpu_seconds, replicas=None, cpu_sampl
         ws = btk.new_workspace(prob, k, dev)
         idx = torch.empty((B, hkv, k), dtype=torch.int32, device=dev)
         out, dout = torch.empty_like(d.q), torch.empty_like(d.q)
-        reps.append(dict(d=d, ws=ws, idx=idx, out=out, keep=(cent, dout),
+        sk = btk.new_sketch(prob, dev)
+        btk.btk_sketch_update(cent, d.block_table, d.seq_lens, sk, ws, problem=prob)
+        sidx, sout = torch.empty_like(idx), torch.empty_like(out)
+        cc = torch.zeros((B, hkv), dtype=torch.int32, device=dev)
+        reps.append(dict(d=d, ws=ws, idx=idx, out=out, sidx=sidx, sout=sout, cc=cc,
+                         keep=(cent, dout, sk),
                          step=(ctypes.byref(prob), p(d.q), p(d.k_cache), p(d.v_cache),
                                p(d.block_table), p(d.seq_lens), p(first), p(cent), k, p(idx),
                                p(out), None, p(ws), ws.numel(), hs),
+                         sk=(ctypes.byref(prob), p(d.q), p(d.k_cache), p(d.v_cache),
+                             p(d.block_table), p(d.seq_lens), p(first), p(cent), p(sk),
+                             sk.numel(), k, p(sidx), p(sout), None, p(cc), p(ws), ws.numel(),
+                             hs),
                          den=(ctypes.byref(prob), p(d.q), p(d.k_cache), p(d.v_cache),
                               p(d.block_table), p(d.seq_lens), p(dout), None, p(ws), ws.numel(),
                               hs)))
@@ -270,12 +307,18 @@ def measure_workload(name, bt, dev, steps, cpu_seconds, replicas=None, cpu_sampl
         return sum(per) / len(per), per
 
     step_us, step_per = timed("btk_decode_step", "step", steps, 10)
+    sk_us, sk_per = timed("btk_decode_step_sketch", "sk", steps, 10)
     dense_us, dense_per = timed("btk_dense_attend", "den", max(10, steps // 5), 5)
     for r in reps:
         if btk.workspace_error_bits(r["ws"]):
             raise RuntimeError(f"{name}: device-side input guard fired")
-    nb = algorithmic_bytes(bt.seq_lens.tolist(), hq, hkv, D, k, e,
-                           sel_tokens=selected_tokens(reps[0]["idx"].cpu(), bt.seq_lens.cpu()))
+        if not (torch.equal(r["sidx"], r["idx"]) and torch.equal(r["sout"], r["out"])):
+            raise RuntimeError(f"{name}: the sketched step disagrees with the step")
+    sel_toks = selected_tokens(reps[0]["idx"].cpu(), bt.seq_lens.cpu())
+    nb = algorithmic_bytes(bt.seq_lens.tolist(), hq, hkv, D, k, e, sel_tokens=sel_toks)
+    cc = reps[0]["cc"].cpu()
+    sk_bytes = sketch_step_bytes(bt.seq_lens.tolist(), hq, hkv, D, k, e, cc.tolist(), sel_toks)
+    sk_gbps = sk_bytes / (sk_us * 1e-6) / 1e9
     gbps = nb["step"] / (step_us * 1e-6) / 1e9
     dgbps = nb["dense"] / (dense_us * 1e-6) / 1e9
     res = {"workload": name, "batch": B, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": D,
@@ -293,6 +336,14 @@ def measure_workload(name, bt, dev, steps, cpu_seconds, replicas=None, cpu_sampl
                      "unit": "query-tokens/s", "gbps": round(dgbps, 1),
                      "frac_of_peak": round(dgbps / HBM_PEAK_GBPS, 4), "bytes": nb["dense"],
                      "bytes_per_token": round(nb["dense"] / B, 1)},
+           "sketch_step": {"kernel": "decode_step_kernel (sketch instance)",
+                           "us": round(sk_us, 3), "us_batches": _pcts(sk_per),
+                           "value": round(B / (sk_us * 1e-6), 1), "unit": "query-tokens/s",
+                           "gbps": round(sk_gbps, 1),
+                           "frac_of_peak": round(sk_gbps / HBM_PEAK_GBPS, 4), "bytes": sk_bytes,
+                           "bytes_per_token": round(sk_bytes / B, 1),
+                           "candidates_per_unit": round(float(cc.float().mean()), 1),
+                           "speedup_vs_dense": round(dense_us / sk_us, 2)},
            "speedup_vs_dense": round(dense_us / step_us, 2),
            "bytes_ratio": round(nb["dense"] / nb["step"], 2),
            "note": "times are HIP-event averages over back-to-back launches; us_batches: "
@@ -392,9 +443,15 @@ def main(argv=None):
         d = base if i == 0 else bt.to(dev)
         cent = torch.zeros((bt.num_pages, hkv, D), dtype=torch.float32, device=dev)
         btk.btk_centroid_update(d.k_cache, d.block_table, d.seq_lens, cent, problem=prob)
-        reps.append(dict(d=d, cent=cent, ws=btk.new_workspace(prob, k, dev),
+        ws = btk.new_workspace(prob, k, dev)
+        sk = btk.new_sketch(prob, dev)
+        btk.btk_sketch_update(cent, d.block_table, d.seq_lens, sk, ws, problem=prob)
+        reps.append(dict(d=d, cent=cent, ws=ws, sk=sk,
                          idx=torch.empty((B, hkv, k), dtype=torch.int32, device=dev),
-                         out=torch.empty_like(d.q), first=first.clone()))
+                         out=torch.empty_like(d.q), first=first.clone(),
+                         kidx=torch.empty((B, hkv, k), dtype=torch.int32, device=dev),
+                         kout=torch.empty_like(d.q),
+                         cc=torch.zeros((B, hkv), dtype=torch.int32, device=dev)))
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     lib = btk._lib()
@@ -411,6 +468,10 @@ def main(argv=None):
         return {"step": (P, p(d.q), p(d.k_cache), p(d.v_cache), p(d.block_table),
                          p(d.seq_lens), p(rep["first"]), p(rep["cent"]), k, p(rep["idx"]),
                          p(rep["out"]), None, ws, wsn, hs),
+                "sk": (P, p(d.q), p(d.k_cache), p(d.v_cache), p(d.block_table),
+                       p(d.seq_lens), p(rep["first"]), p(rep["cent"]), p(rep["sk"]),
+                       rep["sk"].numel(), k, p(rep["kidx"]), p(rep["kout"]), None, p(rep["cc"]),
+                       ws, wsn, hs),
                 "cen": (P, p(d.k_cache), p(d.block_table), p(d.seq_lens), p(rep["first"]),
                         p(rep["cent"]), hs),
                 "sel": (P, p(d.q), p(rep["cent"]), p(d.block_table), p(d.seq_lens), k,
@@ -470,6 +531,29 @@ def main(argv=None):
         e1.record(stream)
     torch.cuda.synchronize()
     step_batches = _pcts([1e3 * e0.elapsed_time(e1) / 10 for e0, e1 in bev])
+
+    # the same step through the block sketches (btk_decode_step_sketch): same
+    # launches, same event brackets; results must equal the step's bit for bit
+    f_sk = lib.btk_decode_step_sketch
+    for i in range(args.warmup):
+        check(f_sk(*reps[i % len(reps)]["calls"]["sk"]))
+    torch.cuda.synchronize()
+    sev0, sev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sev0.record(stream)
+    for i in range(args.steps):
+        check(f_sk(*reps[i % len(reps)]["calls"]["sk"]))
+    sev1.record(stream)
+    torch.cuda.synchronize()
+    sk_us = 1e3 * sev0.elapsed_time(sev1) / args.steps
+    i = 0
+    for e0, e1 in bev:
+        e0.record(stream)
+        for _ in range(10):
+            check(f_sk(*reps[i % len(reps)]["calls"]["sk"]))
+            i += 1
+        e1.record(stream)
+    torch.cuda.synchronize()
+    sk_batches = _pcts([1e3 * e0.elapsed_time(e1) / 10 for e0, e1 in bev])
 
     # the same step as three calls: whole-step time, then a per-kernel pass
     t0 = time.perf_counter()
@@ -556,9 +640,11 @@ def main(argv=None):
     for r in reps:
         if btk.workspace_error_bits(r["ws"]):
             raise RuntimeError("device-side input guard fired during the benchmark")
-    for r in reps:  # the two forms of the step agree
+    for r in reps:  # the three forms of the step agree
         if not torch.equal(r["out"], r["sout"]):
             raise RuntimeError("single-launch and three-call steps disagree")
+        if not (torch.equal(r["out"], r["kout"]) and torch.equal(r["idx"], r["kidx"])):
+            raise RuntimeError("the step and the sketched step disagree")
 
     # Best-of-N: the Qwen3-30B-A3B-shaped batch (16 samples sharing a 2048-token
     # prompt), select vs the shared-prefix select that reads the prompt's centroid
@@ -715,6 +801,24 @@ def main(argv=None):
     launch_gbps = nbytes["step"] / (step_us * 1e-6) / 1e9
     dense_gbps = nbytes["dense"] / (dense_ms * 1e-3) / 1e9
     value = B / (ms_per_step * 1e-3)
+    sel_toks = selected_tokens(reps[0]["idx"].cpu(), bt.seq_lens)
+    cc = reps[0]["cc"].cpu()
+    sk_bytes = sketch_step_bytes(bt.seq_lens.tolist(), hq, hkv, D, k, e, cc.tolist(), sel_toks)
+    sk_gbps = sk_bytes / (sk_us * 1e-6) / 1e9
+    sketch = {"kernel": "decode_step_kernel (sketch instance): btk_decode_step_sketch",
+              "avg_launch_us": round(sk_us, 3), "launch_us_batches": sk_batches,
+              "value": round(B / (sk_us * 1e-6), 1), "unit": "query-tokens/s",
+              "algorithmic_bytes_per_launch": sk_bytes, "achieved": round(sk_gbps, 1),
+              "frac": round(sk_gbps / HBM_PEAK_GBPS, 4),
+              "bytes_per_token": round(sk_bytes / B, 1),
+              "candidates_per_unit": {"mean": round(float(cc.float().mean()), 1),
+                                      "max": int(cc.max())},
+              "speedup_vs_step": round(step_us / sk_us, 3),
+              "speedup_vs_dense": round(1e3 * dense_ms / sk_us, 2),
+              "note": "the step reading 8-bit block sketches and only the candidates' fp32 "
+                      "centroid rows; indices and outputs identical to btk_decode_step (checked "
+                      "on every replica); bytes: sketch rows, candidate rows, the rest as the "
+                      "step"}
     if app is not None:
         app_bytes = nbytes["step"] + 4 * B * hkv * D * e  # new K,V read and written
         app = {"ms_per_step": round(app[0], 5), "value": round(B / (app[0] * 1e-3), 1),
@@ -776,6 +880,7 @@ def main(argv=None):
                        "frac_of_peak": round(nbytes["token"] / (token_ms * 1e-3) / 1e9
                                              / HBM_PEAK_GBPS, 4),
                        "bytes_per_step": nbytes["token"]},
+        "sketch_step": sketch,
         "best_of_n": bon,
         "fused_append": app,
         "graph_replay": None if graph_ms is None else {

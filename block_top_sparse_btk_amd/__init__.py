@@ -87,6 +87,9 @@ def _lib():
         lib.btk_token_topk_attend.argtypes = [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
         lib.btk_decode_step.restype = st
         lib.btk_decode_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
+        lib.btk_decode_step_sketch.restype = st
+        lib.btk_decode_step_sketch.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, vp, vp,
+                                               vp, vp, vp, sz, vp]
         lib.btk_decode_step_noalloc.restype = st
         lib.btk_decode_step_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp]
         lib.btk_decode_step_append.restype = st
@@ -476,6 +479,45 @@ def btk_decode_step(q, k_cache, v_cache, block_table, seq_lens, centroids, top_k
     _check(st, "btk_decode_step")
     if check:
         check_workspace(workspace, "btk_decode_step")
+    return out, indices
+
+
+def btk_decode_step_sketch(q, k_cache, v_cache, block_table, seq_lens, centroids, sketch, top_k,
+                           workspace, first_pos=None, indices=None, out=None, lse=None,
+                           cand_counts=None, sm_scale: float = 0.0,
+                           problem: Optional[btk_problem_t] = None, check: bool = False):
+    """btk_decode_step through the block sketch (results identical); the touched
+    blocks' sketch rows are rebuilt in the call.  cand_counts ([B, Hkv] int32) receives
+    per unit the number of blocks scored from their fp32 rows.  Returns (out, indices)."""
+    dev = q.device
+    problem = problem or make_problem(q, k_cache, block_table, sm_scale)
+    out = torch.empty_like(q) if out is None else out
+    if indices is None:
+        indices = torch.empty((problem.batch, problem.num_kv_heads, int(top_k)), dtype=torch.int32,
+                              device=dev)
+    _check_shapes(problem, q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
+                  seq_lens=seq_lens, centroids=centroids, indices=indices, out=out, lse=lse,
+                  first_pos=first_pos, top_k=top_k)
+    if cand_counts is not None and tuple(cand_counts.shape) != (problem.batch, problem.num_kv_heads):
+        raise ValueError(f"cand_counts: expected shape {(problem.batch, problem.num_kv_heads)}, "
+                         f"got {tuple(cand_counts.shape)}")
+    fp = _dev(first_pos, "first_pos", torch.int32, dev) if first_pos is not None else None
+    lp = _dev(lse, "lse", torch.float32, dev) if lse is not None else None
+    cc = _dev(cand_counts, "cand_counts", torch.int32, dev) if cand_counts is not None else None
+    st = _lib().btk_decode_step_sketch(ctypes.byref(problem), _dev(q, "q", None, dev),
+                                       _dev(k_cache, "k_cache", q.dtype, dev),
+                                       _dev(v_cache, "v_cache", q.dtype, dev),
+                                       _dev(block_table, "block_table", torch.int32, dev),
+                                       _dev(seq_lens, "seq_lens", torch.int32, dev), fp,
+                                       _dev(centroids, "centroids", torch.float32, dev),
+                                       _dev(sketch, "sketch", torch.uint8, dev), sketch.numel(),
+                                       int(top_k), _dev(indices, "indices", torch.int32, dev),
+                                       _dev(out, "out", q.dtype, dev), lp, cc,
+                                       _dev(workspace, "workspace", torch.uint8, dev),
+                                       workspace.numel(), _stream(dev))
+    _check(st, "btk_decode_step_sketch")
+    if check:
+        check_workspace(workspace, "btk_decode_step_sketch")
     return out, indices
 
 

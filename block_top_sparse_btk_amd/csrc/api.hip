@@ -413,7 +413,8 @@ static btk_status_t decode_step(const btk_problem_t *problem, const void *q, con
                                 const int32_t *first_pos, float *centroids, int32_t top_k,
                                 int32_t *indices, void *out, float *lse, void *workspace,
                                 size_t workspace_bytes, void *stream, bool append,
-                                bool own_scratch = false) {
+                                bool own_scratch = false, void *sketch = nullptr,
+                                size_t sketch_bytes = 0, int32_t *cand_counts = nullptr) {
     btk::Dims d;
     btk_status_t st = check_problem(problem, &d);
     if (st != BTK_OK) return st;
@@ -421,7 +422,9 @@ static btk_status_t decode_step(const btk_problem_t *problem, const void *q, con
         return BTK_ERR_NULL;
     if (append && (!k_new || !v_new)) return BTK_ERR_NULL;
     if (!top_k_ok(top_k)) return BTK_ERR_SHAPE;
-    if (d.B > btk::kMaxStepBatch || !btk::step_rows_fit(d)) return BTK_ERR_UNSUPPORTED;
+    if (d.B > btk::kMaxStepBatch || !btk::step_rows_fit(d, sketch != nullptr))
+        return BTK_ERR_UNSUPPORTED;
+    if (sketch && sketch_bytes < btk::sketch_bytes(d)) return BTK_ERR_WORKSPACE;
     // a caller's workspace has the size btk_workspace_bytes promises; the
     // library's own scratch holds only what the step needs
     const btk::WorkspaceLayout w = btk::workspace_layout(d, top_k, !own_scratch);
@@ -430,7 +433,10 @@ static btk_status_t decode_step(const btk_problem_t *problem, const void *q, con
     char *scratch = ws + w.scratch_at(workspace_bytes);
     uint32_t *state = reinterpret_cast<uint32_t *>(ws + w.state);
     const btk::SelectPlan sp = btk::plan_select(d);
-    const btk::AttendPlan ap = btk::plan_attend(d, top_k, false);
+#ifndef BTK_STEP_SKETCH_ITEMS
+#define BTK_STEP_SKETCH_ITEMS 256
+#endif
+    const btk::AttendPlan ap = btk::plan_attend(d, top_k, false, sketch ? BTK_STEP_SKETCH_ITEMS : 256);
     return hip_status(btk::launch_decode_step(
         d, sp, ap, q, k_cache, v_cache, block_table, seq_lens, first_pos, centroids, top_k,
         indices, reinterpret_cast<float *>(scratch + w.scores), out, lse,
@@ -440,7 +446,22 @@ static btk_status_t decode_step(const btk_problem_t *problem, const void *q, con
         reinterpret_cast<unsigned long long *>(ws + w.claims), btk::kReadySpinLimit,
         step_test_flags(),
         reinterpret_cast<uint32_t *>(ws), (hipStream_t)stream, append ? k_new : nullptr,
-        append ? v_new : nullptr));
+        append ? v_new : nullptr, sketch,
+        sketch ? reinterpret_cast<float *>(scratch + w.sk_lo) : nullptr,
+        sketch ? reinterpret_cast<float *>(scratch + w.sk_hi) : nullptr, cand_counts));
+}
+
+btk_status_t btk_decode_step_sketch(const btk_problem_t *problem, const void *q,
+                                    const void *k_cache, const void *v_cache,
+                                    const int32_t *block_table, const int32_t *seq_lens,
+                                    const int32_t *first_pos, float *centroids, void *sketch,
+                                    size_t sketch_bytes, int32_t top_k, int32_t *indices,
+                                    void *out, float *lse, int32_t *cand_counts, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+    if (!sketch) return BTK_ERR_NULL;
+    return decode_step(problem, q, nullptr, nullptr, k_cache, v_cache, block_table, seq_lens,
+                       first_pos, centroids, top_k, indices, out, lse, workspace,
+                       workspace_bytes, stream, false, false, sketch, sketch_bytes, cand_counts);
 }
 
 btk_status_t btk_decode_step(const btk_problem_t *problem, const void *q, const void *k_cache,

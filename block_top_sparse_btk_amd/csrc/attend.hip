@@ -42,7 +42,7 @@ hipError_t launch_dtype(const Dims &d, const AttendPlan &plan, int mode, AttendA
 
 }  // namespace
 
-AttendPlan plan_attend(const Dims &d, int list_len_max, bool dense) {
+AttendPlan plan_attend(const Dims &d, int list_len_max, bool dense, int target) {
     // The split merge keeps nsplit * r maxima and normalisers in LDS: at most
     // kMaxSplitHeads of each.  A wave holds at most 64 list entries (one per lane).
     constexpr int kMaxSplitHeads = 2048;
@@ -53,11 +53,11 @@ AttendPlan plan_attend(const Dims &d, int list_len_max, bool dense) {
     if (dense) {
         p.bps = 128;  // 32 blocks (256 KiB of bf16 K+V at D=128) per wave
     } else {
-        // about 256 workgroups (whole lists where that gives enough of them:
+        // about `target` (256) workgroups (whole lists where that gives enough of them:
         // a split costs a round of partial stores and loads), each wave with
         // at least two blocks when the list allows it and at most 64, and the
         // list spread evenly over the four waves of a split
-        const int want = (int)((256 + units - 1) / units);
+        const int want = (int)((target + units - 1) / units);
         int ns = want < list_len_max / 8 ? want : list_len_max / 8;
         if (ns < 1) ns = 1;
         if (ns < (list_len_max + 4 * kWave - 1) / (4 * kWave))

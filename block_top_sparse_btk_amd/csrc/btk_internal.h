@@ -153,7 +153,7 @@ struct PrefixGroups {
     int blocks[kMaxPrefixGroups];
     int item0[kMaxPrefixGroups + 1];
 };
-AttendPlan plan_attend(const Dims &d, int list_len_max, bool dense);
+AttendPlan plan_attend(const Dims &d, int list_len_max, bool dense, int target = 256);
 
 // Workspace layout (bytes).  Everything that carries state from call to call
 // sits at the start, at places that do not depend on the problem; the scratch
@@ -264,9 +264,9 @@ struct TokenWorkspaceLayout {
 };
 TokenWorkspaceLayout token_workspace_layout(const Dims &d, int top_tokens);
 
-// Whether the decode step's row count (every unit charged a fixed number of
+// Whether the decode step's row count (with sketches: sketch rows) (every unit charged a fixed number of
 // rows beyond its blocks) fits its 32-bit counters.
-bool step_rows_fit(const Dims &d);
+bool step_rows_fit(const Dims &d, bool sketch = false);
 hipError_t launch_decode_step(const Dims &d, const SelectPlan &sp, const AttendPlan &ap,
                               const void *q, const void *k_cache, const void *v_cache,
                               const int32_t *block_table, const int32_t *seq_lens,
@@ -276,7 +276,9 @@ hipError_t launch_decode_step(const Dims &d, const SelectPlan &sp, const AttendP
                               uint32_t *ready, uint32_t *queue, uint32_t *steal,
                               unsigned long long *claims, uint32_t spin_limit,
                               uint32_t test_flags, uint32_t *err, hipStream_t stream,
-                              const void *k_new = nullptr, const void *v_new = nullptr);
+                              const void *k_new = nullptr, const void *v_new = nullptr,
+                              void *sketch = nullptr, float *sk_lo = nullptr,
+                              float *sk_hi = nullptr, int32_t *cand_counts = nullptr);
 
 // Counter calibration (probe.hip): reads `rows` 512-byte rows of src (row ids
 // from row_ids, or 0 .. rows-1 when it is NULL; ids outside [0, src_rows) are

@@ -2,32 +2,9 @@
 // result as btk_select).  (Pith review of "Kinetics: Rethinking Test-Time
 // Scaling Laws", "What carries the argument": blocks are scored by their
 // averaged keys and the k best are kept.  The sketch changes which centroid
-// rows are read, not which blocks are selected.)
-//
-// A sketch row is an 8-bit copy of one block's fp32 centroid, kept per sequence
-// in block-table order, so that a unit's sketch is one contiguous stream:
-//   header[i] = {page + 1 (0: no sketch), scale = amax / 127}
-//   codes[i][d] = rint(c_d / scale) + 128  (in 1 .. 255; 128 when amax = 0)
-// for row i = (b * Hkv + g) * max_blocks + j (block j of sequence b, KV head g).
-//
-// Why the selection is unchanged.  With c the fp32 centroid, qs the scaled mean
-// query and s = qs . c, the sketch gives sa = scale * (sum_d qs_d * code_d -
-// 128 * sum_d qs_d).  Rounding c_d / scale to an integer moves each term by at
-// most 0.50001 * scale * |qs_d| (the fp32 quotient is within 127 * 2^-24 of
-// exact), and the fp32 evaluation of either sum, in any order, by at most
-// 127 * 2^-24 * (255 + 128) * scale * |qs|_1 (the sketch's) and
-// 127 * 2^-24 * 127 * scale * |qs|_1 (the exact score's), about 0.004 *
-// scale * |qs|_1 together.  So every score s computed by the fp32 scan lies in
-// [sa - e, sa + e] with e = 0.51 * scale * |qs|_1 (the margin also covers the
-// rounding of sa - e and sa + e themselves).  With tau the kb-th largest lower
-// end, at least kb blocks score at least tau; a block whose upper end is below
-// tau therefore scores below kb others and cannot be selected under any tie
-// rule.  The remaining candidates are scored exactly as btk_select scores them
-// (the same code, the same bits) and the top kb of those are selected with the
-// same tie rule, so the indices equal btk_select's.  A row whose header does
-// not name the block's current page (not built, stale, invalid page) is always
-// a candidate; when candidates exceed the LDS map every block is scored.
-#include "select_dev.h"
+// rows are read, not which blocks are selected.)  The row layout and the proof
+// that the selection is unchanged are in sketch_dev.h.
+#include "sketch_dev.h"
 
 namespace btk {
 namespace {
@@ -36,20 +13,9 @@ using sel::kThreads;
 using sel::kWaves;
 using sel::kMaxChunk;
 
-struct SketchHdr {
-    int32_t page1;
-    float scale;
-};
-
-constexpr float kBoundFactor = 0.51f;
+using skt::SketchArgs;
+using skt::SketchHdr;
 constexpr int kCandCap = 2048;  // candidates whose block ids fit the LDS map
-
-struct SketchArgs {
-    const SketchHdr *hdr;   // [units * max_blocks]
-    const uint8_t *codes;   // [units * max_blocks][D]
-    float *lo, *hi;         // [units * max_blocks] interval ends (workspace)
-    float *exact;           // [units * max_blocks] exact scores of candidates (workspace)
-};
 
 // ---- building the sketch -------------------------------------------------
 //
@@ -93,233 +59,11 @@ __global__ __launch_bounds__(kThreads) void sketch_update_kernel(
         float x[E];
 #pragma unroll
         for (int e = 0; e < E; ++e) x[e] = src[e];
-        uint32_t m = 0u;
-#pragma unroll
-        for (int e = 0; e < E; ++e) m = max(m, __float_as_uint(fabsf(x[e])));
-        const float amax = __uint_as_float(sel::wave_max_u32(m));
-        const float scale = amax / 127.0f;
-        uint32_t packed = 0u;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            float qv = amax > 0.f ? rintf(x[e] / scale) : 0.f;
-            qv = fminf(fmaxf(qv, -127.f), 127.f);
-            packed |= (uint32_t)((int)qv + 128) << (8 * e);
-        }
-        uint8_t *dst = codes + row * D + lane * E;
-        if constexpr (E == 2)
-            *reinterpret_cast<uint16_t *>(dst) = (uint16_t)packed;
-        else
-            *dst = (uint8_t)packed;
-        if (lane == 0) hdr[row] = SketchHdr{page + 1, scale};
+        skt::encode_row<D>(x, page, row, hdr, codes, lane);
     }
 }
 
 // ---- the selection ---------------------------------------------------------
-
-// The kb-th largest of the nb keys of src (order-preserving score keys; 0 = no
-// key), returned as a key tau such that at least kb keys are >= tau and every
-// key above the kb-th largest is >= tau.  The radix passes of select_topk_wg4;
-// every thread gets the result.
-template <int KMAX, typename Src>
-__device__ uint32_t kth_key_wg4(const Src &src, int nb, int kb, sel::TopkSmem &sm) {
-    uint32_t *red = sm.red;
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    for (int i = tid; i < sel::kTopkPasses * sel::kHistWords / 4; i += kThreads)
-        reinterpret_cast<u32x4_t *>(sm.hist)[i] = u32x4_t{0u, 0u, 0u, 0u};
-    uint32_t key[KMAX];
-    src.fill(key, tid, kThreads, nb);
-    uint32_t kmin = 0xffffffffu, kmax = 0u;
-#pragma unroll
-    for (int i = 0; i < KMAX; ++i) {
-        const int j = i * kThreads + tid;
-        key[i] = j < nb ? score_key(__uint_as_float(key[i])) : 0u;
-        kmin = j < nb ? min(kmin, key[i]) : kmin;
-        kmax = max(kmax, key[i]);
-    }
-    // a lower bound of the result: for kb <= 64, in each wave the smallest of
-    // the largest keys of its first kb lanes (0 if one of them holds none)
-    const uint32_t bound = kb <= kWave ? (lane < kb ? kmax : 0xffffffffu) : kmin;
-    const uint32_t wave_lo = ~sel::wave_max_u32(~bound);
-    kmax = sel::wave_max_u32(kmax);
-    if (lane == 0) {
-        red[wave] = wave_lo;
-        red[kWaves + wave] = kmax;
-    }
-    __syncthreads();
-    uint32_t lo = kb <= kWave ? max(max(red[0], red[1]), max(red[2], red[3]))
-                              : min(min(red[0], red[1]), min(red[2], red[3]));
-    uint32_t hi = max(max(red[kWaves], red[kWaves + 1]), max(red[kWaves + 2], red[kWaves + 3]));
-    int need = kb;
-#pragma unroll 1
-    for (int p = 0; p < sel::kTopkPasses && lo < hi; ++p) {
-        uint32_t *hist = sm.hist + p * sel::kHistWords;
-        const uint32_t span = hi - lo;
-        const int shift = max(0, 24 - __builtin_clz(span));
-#pragma unroll
-        for (int i = 0; i < KMAX; ++i) {
-            const uint32_t off = key[i] - lo;
-            atomicAdd(&hist[off <= span ? (off >> shift) : 256u + lane], 1u);
-        }
-        __syncthreads();
-        uint32_t in_bin;
-        const uint32_t b_sel = sel::locate_bin(hist, need, lane, &in_bin);
-        const uint32_t top = (b_sel << shift) + ((1u << shift) - 1u);
-        if (top < span) hi = lo + top;
-        lo += b_sel << shift;
-        if (in_bin == (uint32_t)need && lo < hi) break;  // the bin is kept whole: tau = lo
-    }
-    __syncthreads();  // the histograms and red are reused by the caller
-    return lo;  // a bin kept whole: exactly kb keys are >= lo; else lo = hi = the kb-th key
-}
-
-template <typename Src>
-__device__ uint32_t kth_key(const Src &src, int nb, int kb, sel::TopkSmem &sm) {
-    if (nb <= 4 * kThreads) return kth_key_wg4<4>(src, nb, kb, sm);
-    if (nb <= 8 * kThreads) return kth_key_wg4<8>(src, nb, kb, sm);
-    if (nb <= 16 * kThreads) return kth_key_wg4<16>(src, nb, kb, sm);
-    return kth_key_wg4<32>(src, nb, kb, sm);
-}
-
-// Block ids j < nb with score_key(hi[j]) >= tau, in ascending order, into
-// map[0 .. m) when m <= kCandCap; returns m (workgroup-uniform).
-template <int KMAX>
-__device__ int compact_candidates(const float *hi, int nb, uint32_t tau, int32_t *map,
-                                  uint32_t *count, int *total) {
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    float hv[KMAX];
-#pragma unroll
-    for (int i = 0; i < KMAX; ++i) hv[i] = load_relaxed(hi + min(i * kThreads + tid, nb - 1));
-    uint32_t flags = 0u;
-#pragma unroll
-    for (int i = 0; i < KMAX; ++i) {
-        const bool f = i * kThreads + tid < nb && score_key(hv[i]) >= tau;
-        flags |= (uint32_t)f << i;
-        const uint64_t bal = __ballot(f);
-        if (lane == 0) count[i * kWaves + wave] = (uint32_t)__popcll(bal);
-    }
-    __syncthreads();
-    if (wave == 0) {  // exclusive prefix over (slot, wave) in block order
-        constexpr int N = KMAX * kWaves;  // <= 128
-        const uint32_t c0 = 2 * lane < N ? count[2 * lane] : 0u;
-        const uint32_t c1 = 2 * lane + 1 < N ? count[2 * lane + 1] : 0u;
-        const uint32_t incl = sel::wave_inclusive_scan(c0 + c1);
-        const uint32_t excl = incl - (c0 + c1);
-        if (2 * lane < N) count[2 * lane] = excl;
-        if (2 * lane + 1 < N) count[2 * lane + 1] = excl + c0;
-        if (lane == kWave - 1) *total = (int)incl;
-    }
-    __syncthreads();
-    const int m = *total;
-    if (m <= kCandCap) {
-#pragma unroll
-        for (int i = 0; i < KMAX; ++i) {
-            const bool f = (flags >> i) & 1u;
-            const uint64_t bal = __ballot(f);
-            if (f) {
-                const int pos = (int)count[i * kWaves + wave] +
-                                (int)__builtin_amdgcn_mbcnt_hi(
-                                    (uint32_t)(bal >> 32),
-                                    __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-                map[pos] = i * kThreads + tid;
-            }
-        }
-    }
-    __syncthreads();
-    return m;
-}
-
-__device__ int candidates(const float *hi, int nb, uint32_t tau, int32_t *map, uint32_t *count,
-                          int *total) {
-    if (nb <= 4 * kThreads) return compact_candidates<4>(hi, nb, tau, map, count, total);
-    if (nb <= 8 * kThreads) return compact_candidates<8>(hi, nb, tau, map, count, total);
-    if (nb <= 16 * kThreads) return compact_candidates<16>(hi, nb, tau, map, count, total);
-    return compact_candidates<32>(hi, nb, tau, map, count, total);
-}
-
-// Interval ends of the sketch scores of blocks [j0, j0 + n) of unit (b, g):
-// LPR lanes per row (16 codes each), KU rows per lane group in each of two
-// stages in flight.  qs: the scaled mean query in sm.qs; q128 = 128 * sum(qs),
-// qn1 = sum |qs|.
-template <int D, int KU>
-__device__ __forceinline__ void scan_sketch(const sel::SelectArgs &a, const SketchArgs &s, int b,
-                                            int g, int j0, int n, const float *qs, float q128,
-                                            float qn1) {
-    constexpr int LPR = D / 16;          // lanes per row
-    constexpr int RPW = kWave / LPR;     // rows per wave per load
-    constexpr int ROWS = kWaves * RPW * KU;
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const int part = lane % LPR, rsub = lane / LPR;
-    const size_t urow = ((size_t)b * a.Hkv + g) * a.max_blocks;
-    float qf[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) qf[e] = qs[16 * part + e];
-    const float ebase = kBoundFactor * qn1;
-    struct Stage {
-        u32x4_t c[KU];
-        uint32_t h0[KU], h1[KU];
-        int32_t pg[KU];
-    };
-    auto issue = [&](Stage &st, int base) {
-#pragma unroll
-        for (int u = 0; u < KU; ++u) {
-            const int row = min(base + u * kWaves * RPW + wave * RPW + rsub, n - 1);
-            const size_t i = urow + j0 + row;
-            st.c[u] = *reinterpret_cast<const u32x4_t *>(s.codes + i * D + 16 * part);
-            const uint32_t *hp = reinterpret_cast<const uint32_t *>(s.hdr + i);
-            st.h0[u] = hp[0];
-            st.h1[u] = hp[1];
-            st.pg[u] = a.bt[(size_t)b * a.max_blocks + j0 + row];
-        }
-    };
-    auto reduce = [&](const Stage &st, int base) {
-#pragma unroll
-        for (int u = 0; u < KU; ++u) {
-            const int row = base + u * kWaves * RPW + wave * RPW + rsub;
-            // this lane's 16 codes against its 16 query values, in a fixed order
-            float t = 0.f;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t cw = st.c[u][w];
-                t = __builtin_fmaf(qf[4 * w + 0], (float)(cw & 0xffu), t);
-                t = __builtin_fmaf(qf[4 * w + 1], (float)((cw >> 8) & 0xffu), t);
-                t = __builtin_fmaf(qf[4 * w + 2], (float)((cw >> 16) & 0xffu), t);
-                t = __builtin_fmaf(qf[4 * w + 3], (float)(cw >> 24), t);
-            }
-            // sum over the row's LPR lanes (quad xor 1, quad xor 2, half-row mirror)
-            t += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                               0, __builtin_bit_cast(int, t), 0xB1, 0xF, 0xF, false));
-            t += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                               0, __builtin_bit_cast(int, t), 0x4E, 0xF, 0xF, false));
-            if constexpr (LPR == 8)
-                t += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                                   0, __builtin_bit_cast(int, t), 0x141, 0xF, 0xF,
-                                                   false));
-            const int page = st.pg[u];
-            const float scale = __uint_as_float(st.h1[u]);
-            const bool valid = page >= 0 && page < a.num_pages && (int)st.h0[u] == page + 1;
-            const float sa = scale * (t - q128);
-            const float e = scale * ebase;
-            if (part == 0 && row < n) {
-                store_relaxed(s.lo + urow + j0 + row, valid ? sa - e : -INFINITY);
-                store_relaxed(s.hi + urow + j0 + row, valid ? sa + e : INFINITY);
-            }
-        }
-    };
-    if (n > 0) {
-        Stage sa_, sb_;
-        issue(sa_, 0);
-        for (int base = 0;;) {
-            issue(sb_, base + ROWS);
-            reduce(sa_, base);
-            base += ROWS;
-            if (base >= n) break;
-            issue(sa_, base + ROWS);
-            reduce(sb_, base);
-            base += ROWS;
-            if (base >= n) break;
-        }
-    }
-}
 
 // One workgroup per (unit, chunk of blocks): sketch bounds of the chunk; the
 // workgroup that completes the unit selects (threshold, candidates, exact
@@ -342,7 +86,7 @@ __global__ __launch_bounds__(kThreads, 4) void select_sketch_kernel(sel::SelectA
     extern __shared__ uint32_t keys[];  // 512 words: top-k bitmaps beyond 2048 blocks
     sel::ScoreSmem sm{qraw, qs, pages, sc_lds, &is_last};
     sel::TopkSmem tk{hist, cand, red, scan_red, keys};
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int tid = threadIdx.x;
     const int unit = blockIdx.x / a.nchunk_max, c = blockIdx.x % a.nchunk_max;
     const int b = unit / a.Hkv, g = unit % a.Hkv;
     int32_t *out = a.indices + (size_t)unit * a.top_k;
@@ -365,24 +109,17 @@ __global__ __launch_bounds__(kThreads, 4) void select_sketch_kernel(sel::SelectA
     const int n = min(nb, j0 + a.chunk) - j0;
     sel::mean_query<D>(a, sm);
     __syncthreads();
-    if (wave == 0) {  // sum(qs) and sum|qs|
-        float s0 = 0.f, s1 = 0.f;
-        for (int d = lane; d < D; d += kWave) {
-            s0 += qs[d];
-            s1 += fabsf(qs[d]);
-        }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            s0 += __shfl_xor(s0, off);
-            s1 += __shfl_xor(s1, off);
-        }
-        if (lane == 0) {
-            qsum_s[0] = 128.f * s0;
-            qsum_s[1] = s1;
-        }
-    }
+    skt::query_sums<D>(qs, qsum_s);
     __syncthreads();
-    scan_sketch<D, 4>(a, s, b, g, j0, n, qs, qsum_s[0], qsum_s[1]);
+    // in runs of up to kMaxChunk blocks staged in LDS (sc_lds, and pages as floats)
+    float *lo_lds = sc_lds, *hi_lds = reinterpret_cast<float *>(pages);
+    for (int s0 = j0; s0 < j0 + n; s0 += kMaxChunk) {
+        const int nr = min(kMaxChunk, j0 + n - s0);
+        skt::scan_sketch<D, 1>(a, s, b, g, s0, nr, qs, qsum_s[0], qsum_s[1], nb, lo_lds, hi_lds);
+        __syncthreads();
+        skt::store_intervals(s, (size_t)unit * a.max_blocks, s0, nr, lo_lds, hi_lds);
+        __syncthreads();  // the staging areas are reused
+    }
     if (!arrive_last(&a.counters[(size_t)unit * kStateStride], (uint32_t)nchunks, &is_last))
         return;
 
@@ -393,8 +130,8 @@ __global__ __launch_bounds__(kThreads, 4) void select_sketch_kernel(sel::SelectA
         for (int i = tid; i < a.top_k; i += kThreads) store_relaxed_i32(out + i, i < nb ? i : -1);
         return;
     }
-    const uint32_t tau = kth_key(sel::PlainScores{s.lo + urow}, nb, kb, tk);
-    int m = candidates(s.hi + urow, nb, tau, cmap, ccount, &ctotal);
+    int m = skt::threshold_candidates(s.lo + urow, s.hi + urow, nb, kb, cmap, kCandCap, tk, ccount,
+                                      &ctotal);
     const bool mapped = m <= kCandCap;
     if (!mapped) m = nb;  // every block is scored
     // exact scores of the candidates, in runs, with the select kernel's scan
@@ -483,8 +220,9 @@ hipError_t launch_select_sketch(const Dims &d, const void *q, const float *centr
     sel::SelectArgs a{q, centroids, block_table, seq_lens, indices, exact, counters, err,
                       d.Hq, d.Hkv, d.num_pages, d.max_blocks, top_k, 0, 0,
                       d.sm_scale, nullptr, nullptr, nullptr};
-    SketchArgs s{static_cast<const SketchHdr *>(sketch),
-                 static_cast<const uint8_t *>(sketch) + sketch_rows_offset(d), lo, hi, exact};
+    // the selection only reads the sketch
+    SketchHdr *hdr = static_cast<SketchHdr *>(const_cast<void *>(sketch));
+    SketchArgs s{hdr, reinterpret_cast<uint8_t *>(hdr) + sketch_rows_offset(d), lo, hi, exact};
     if (d.dtype == 0)
         return d.D == 128 ? launch_sel<uint16_t, 128>(d, a, s, stream)
                           : launch_sel<uint16_t, 64>(d, a, s, stream);

@@ -1,0 +1,461 @@
+// Device code of the block sketches, shared by the stand-alone sketch kernels
+// (sketch.hip) and the single-launch decode step with sketches (step.hip).
+// (Pith review of "Kinetics: Rethinking Test-Time Scaling Laws", "What carries
+// the argument": blocks are scored by their averaged keys and the k best are
+// kept.  A sketch changes which centroid rows are read, not which blocks are
+// selected.)
+//
+// A sketch row is an 8-bit copy of one block's fp32 centroid, kept per sequence
+// in block-table order, so that a unit's sketch is one contiguous stream:
+//   header[i] = {page + 1 (0: no sketch), scale = amax / 127}
+//   codes[i][d] = rint(c_d / scale) + 128  (in 1 .. 255; 128 when amax = 0)
+// for row i = (b * Hkv + g) * max_blocks + j (block j of sequence b, KV head g).
+//
+// Why a selection through the sketch keeps exactly the same blocks.  With c the
+// fp32 centroid, qs the scaled mean query and s = qs . c, the sketch gives
+// sa = scale * (sum_d qs_d * code_d - 128 * sum_d qs_d).  Rounding c_d / scale
+// to an integer moves each term by at most 0.50001 * scale * |qs_d| (the fp32
+// quotient is within 127 * 2^-24 of exact), and the fp32 evaluation of either
+// sum, in any order, by at most 127 * 2^-24 * (255 + 128) * scale * |qs|_1
+// (the sketch's) and 127 * 2^-24 * 127 * scale * |qs|_1 (the exact score's),
+// about 0.004 * scale * |qs|_1 together.  So every score s computed by the
+// fp32 scan lies in [sa - e, sa + e] with e = 0.51 * scale * |qs|_1 (the margin
+// also covers the rounding of sa - e and sa + e themselves).  With tau the
+// kb-th largest lower end, at least kb blocks score at least tau; a block whose
+// upper end is below tau therefore scores below kb others and cannot be
+// selected under any tie rule.  The remaining candidates are scored exactly as
+// the full scan scores them (the same arithmetic, the same bits) and the top kb
+// of those are selected with the same tie rule, so the indices equal those of
+// the full scan.  A row whose header does not name the block's current page
+// (not built, stale, invalid page) and a block refreshed in the same call are
+// always candidates.
+#pragma once
+#include "select_dev.h"
+
+namespace btk {
+namespace skt {
+
+using sel::kThreads;
+using sel::kWaves;
+
+struct SketchHdr {
+    int32_t page1;
+    float scale;
+};
+
+constexpr float kBoundFactor = 0.51f;
+
+struct SketchArgs {
+    SketchHdr *hdr;   // [units * max_blocks] (written only by refreshes)
+    uint8_t *codes;   // [units * max_blocks][D]
+    float *lo, *hi;   // [units * max_blocks] interval ends (workspace)
+    float *exact;     // [units * max_blocks] exact scores when every block is scored (workspace)
+};
+
+// Writes sketch row `row` from a centroid of which this lane holds dims
+// lane * E .. lane * E + E - 1 (E = D / 64), page id `page` (wave-uniform call).
+template <int D>
+__device__ __forceinline__ void encode_row(const float (&x)[D / kWave], int page, size_t row,
+                                           SketchHdr *hdr, uint8_t *codes, int lane) {
+    constexpr int E = D / kWave;
+    uint32_t m = 0u;
+#pragma unroll
+    for (int e = 0; e < E; ++e) m = max(m, __float_as_uint(fabsf(x[e])));
+    const float amax = __uint_as_float(sel::wave_max_u32(m));
+    const float scale = amax / 127.0f;
+    uint32_t packed = 0u;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        float qv = amax > 0.f ? rintf(x[e] / scale) : 0.f;
+        qv = fminf(fmaxf(qv, -127.f), 127.f);
+        packed |= (uint32_t)((int)qv + 128) << (8 * e);
+    }
+    uint8_t *dst = codes + row * D + lane * E;
+    if constexpr (E == 2)
+        *reinterpret_cast<uint16_t *>(dst) = (uint16_t)packed;
+    else
+        *dst = (uint8_t)packed;
+    if (lane == 0) hdr[row] = SketchHdr{page + 1, scale};
+}
+
+// Scores read from LDS (see sel::PlainScores).
+struct LdsScores {
+    const float *sc;  // [nb]
+    template <int N>
+    __device__ __forceinline__ void fill(uint32_t (&bits)[N], int first, int stride, int nb) const {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            bits[i] = i * stride + first < nb ? __float_as_uint(sc[i * stride + first]) : 0u;
+    }
+};
+
+// The scaled mean query's sums for the bound: q128 = 128 * sum(qs), qn1 =
+// sum |qs| (wave 0 computes them into out[0], out[1]; the caller synchronises).
+template <int D>
+__device__ __forceinline__ void query_sums(const float *qs, float *out) {
+    const int tid = threadIdx.x;
+    if (tid < kWave) {
+        float s0 = 0.f, s1 = 0.f;
+        for (int d = tid; d < D; d += kWave) {
+            s0 += qs[d];
+            s1 += fabsf(qs[d]);
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            s0 += __shfl_xor(s0, off);
+            s1 += __shfl_xor(s1, off);
+        }
+        if (tid == 0) {
+            out[0] = 128.f * s0;
+            out[1] = s1;
+        }
+    }
+}
+
+// The threshold and the candidates of one unit, over the workgroup: tau is
+// the kb-th largest lower end (order-preserving keys, as sel::score_key), the
+// candidates are the blocks j < nb whose upper end's key is >= tau, written in
+// ascending order to map[0 .. m) when m <= cap.  Returns m (workgroup-uniform).
+// Up to 2048 blocks (KMAX <= 8) the lower and upper ends are requested
+// together; beyond, the upper ends once tau is known (fewer registers).  The
+// lower ends go through the radix passes of the four-wave top-k
+// (sel::select_topk_wg4).  count: LDS of KMAX * kWaves words (may alias
+// sm.cand), total: one LDS word.
+template <int KMAX>
+__device__ __forceinline__ int threshold_candidates_wg4(const float *lo_src, const float *hi_src, int nb, int kb,
+                                        int32_t *map, int cap, sel::TopkSmem &sm,
+                                        uint32_t *count, int *total) {
+    uint32_t *red = sm.red;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    for (int i = tid; i < sel::kTopkPasses * sel::kHistWords / 4; i += kThreads)
+        reinterpret_cast<u32x4_t *>(sm.hist)[i] = u32x4_t{0u, 0u, 0u, 0u};
+    constexpr bool kHiEarly = KMAX <= 8;
+    uint32_t key[KMAX], hk[kHiEarly ? KMAX : 1];
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {  // unconditional (clamped): all in flight together
+        key[i] = __float_as_uint(load_relaxed(lo_src + min(i * kThreads + tid, nb - 1)));
+        if constexpr (kHiEarly)
+            hk[i] = __float_as_uint(load_relaxed(hi_src + min(i * kThreads + tid, nb - 1)));
+    }
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {
+        const int j = i * kThreads + tid;
+        key[i] = j < nb ? score_key(__uint_as_float(key[i])) : 0u;
+        kmin = j < nb ? min(kmin, key[i]) : kmin;
+        kmax = max(kmax, key[i]);
+    }
+    // a lower bound of the result: for kb <= 64, in each wave the smallest of
+    // the largest keys of its first kb lanes (0 if one of them holds none)
+    const uint32_t bound = kb <= kWave ? (lane < kb ? kmax : 0xffffffffu) : kmin;
+    const uint32_t wave_lo = ~sel::wave_max_u32(~bound);
+    kmax = sel::wave_max_u32(kmax);
+    if (lane == 0) {
+        red[wave] = wave_lo;
+        red[kWaves + wave] = kmax;
+    }
+    __syncthreads();
+    uint32_t lo = kb <= kWave ? max(max(red[0], red[1]), max(red[2], red[3]))
+                              : min(min(red[0], red[1]), min(red[2], red[3]));
+    uint32_t hi = max(max(red[kWaves], red[kWaves + 1]), max(red[kWaves + 2], red[kWaves + 3]));
+    int need = kb;
+#pragma unroll 1
+    for (int p = 0; p < sel::kTopkPasses && lo < hi; ++p) {
+        uint32_t *hist = sm.hist + p * sel::kHistWords;
+        const uint32_t span = hi - lo;
+        const int shift = max(0, 24 - __builtin_clz(span));
+#pragma unroll
+        for (int i = 0; i < KMAX; ++i) {
+            const uint32_t off = key[i] - lo;
+            atomicAdd(&hist[off <= span ? (off >> shift) : 256u + lane], 1u);
+        }
+        __syncthreads();
+        uint32_t in_bin;
+        const uint32_t b_sel = sel::locate_bin(hist, need, lane, &in_bin);
+        const uint32_t top = (b_sel << shift) + ((1u << shift) - 1u);
+        if (top < span) hi = lo + top;
+        lo += b_sel << shift;
+        if (in_bin == (uint32_t)need && lo < hi) break;  // the bin is kept whole: tau = lo
+    }
+    // a bin kept whole: exactly kb keys are >= lo; else lo = hi = the kb-th key
+    const uint32_t tau = lo;
+
+    // the candidates, in block order: a count per (slot, wave), an exclusive
+    // prefix over them, then each flagged lane writes its place
+    uint32_t flags = 0u;
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {
+        const uint32_t hv = kHiEarly ? hk[kHiEarly ? i : 0]
+                                     : __float_as_uint(load_relaxed(hi_src + min(i * kThreads + tid, nb - 1)));
+        const bool f = i * kThreads + tid < nb && score_key(__uint_as_float(hv)) >= tau;
+        flags |= (uint32_t)f << i;
+        const uint64_t bal = __ballot(f);
+        if (lane == 0) count[i * kWaves + wave] = (uint32_t)__popcll(bal);
+    }
+    __syncthreads();
+    if (wave == 0) {  // exclusive prefix over (slot, wave) in block order
+        constexpr int N = KMAX * kWaves;  // <= 128
+        const uint32_t c0 = 2 * lane < N ? count[2 * lane] : 0u;
+        const uint32_t c1 = 2 * lane + 1 < N ? count[2 * lane + 1] : 0u;
+        const uint32_t incl = sel::wave_inclusive_scan(c0 + c1);
+        const uint32_t excl = incl - (c0 + c1);
+        if (2 * lane < N) count[2 * lane] = excl;
+        if (2 * lane + 1 < N) count[2 * lane + 1] = excl + c0;
+        if (lane == kWave - 1) *total = (int)incl;
+    }
+    __syncthreads();
+    const int m = *total;
+    if (m <= cap) {
+#pragma unroll
+        for (int i = 0; i < KMAX; ++i) {
+            const bool f = (flags >> i) & 1u;
+            const uint64_t bal = __ballot(f);
+            if (f) {
+                const int pos = (int)count[i * kWaves + wave] +
+                                (int)__builtin_amdgcn_mbcnt_hi(
+                                    (uint32_t)(bal >> 32),
+                                    __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+                map[pos] = i * kThreads + tid;
+            }
+        }
+    }
+    __syncthreads();  // map, count, the histograms and red are read or reused next
+    return m;
+}
+
+// Dispatch on nb (at most 32 keys per thread: 8192 blocks), kb < nb.
+__device__ __forceinline__ int threshold_candidates(const float *lo, const float *hi, int nb,
+                                                    int kb, int32_t *map, int cap,
+                                                    sel::TopkSmem &sm, uint32_t *count,
+                                                    int *total) {
+    if (nb <= 4 * kThreads)
+        return threshold_candidates_wg4<4>(lo, hi, nb, kb, map, cap, sm, count, total);
+    if (nb <= 8 * kThreads)
+        return threshold_candidates_wg4<8>(lo, hi, nb, kb, map, cap, sm, count, total);
+    if (nb <= 16 * kThreads)
+        return threshold_candidates_wg4<16>(lo, hi, nb, kb, map, cap, sm, count, total);
+    return threshold_candidates_wg4<32>(lo, hi, nb, kb, map, cap, sm, count, total);
+}
+
+// Interval ends of the sketch scores of blocks [j0, j0 + n) of unit (b, g)
+// into lo_lds[0 .. n) and hi_lds[0 .. n) (LDS; see store_intervals).  LPR =
+// D / 16 lanes hold a row (16 codes each), so a wave instruction covers RPW =
+// 64 / LPR rows; a pipeline stage is KU = HK * LPR such instructions per lane,
+// two stages in flight.  A row's header and page id are needed once per row,
+// not once per lane: each lane loads those of HK rows of the stage (lane l:
+// rows l and l + 64 in the wave's row order) and the lanes holding a row take
+// its scale from there (a lane permute), so a stage costs 4 KU + 3 HK
+// registers instead of 7 KU.  qs: the scaled mean query (LDS); q128 = 128 *
+// sum(qs), qn1 = sum |qs|.  Blocks j >= jforce (refreshed in this call) and
+// rows whose header does not name the block's page get (-inf, +inf): always
+// candidates.  Nothing is stored to memory inside the loop: stores count in the
+// same in-order memory counter as the loads, so a store issued there would hold
+// up the wait for the next stage's rows until it completed.
+template <int D, int HK>
+__device__ __forceinline__ void scan_sketch(const sel::SelectArgs &a, const SketchArgs &s, int b,
+                                            int g, int j0, int n, const float *qs, float q128,
+                                            float qn1, int jforce, float *lo_lds,
+                                            float *hi_lds) {
+    constexpr int LPR = D / 16;          // lanes per row
+    constexpr int RPW = kWave / LPR;     // rows per wave per load
+    constexpr int KU = HK * LPR;         // load steps per stage: HK * 64 rows per wave
+    constexpr int ROWS = kWaves * RPW * KU;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int part = lane % LPR, rsub = lane / LPR;
+    const size_t urow = ((size_t)b * a.Hkv + g) * a.max_blocks;
+    const int32_t *bt = a.bt + (size_t)b * a.max_blocks;
+    float qf[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) qf[e] = qs[16 * part + e];
+    const float ebase = kBoundFactor * qn1;
+    // row of load step u, row group rs, in a stage starting at base
+    auto row_of = [&](int base, int u, int rs) { return base + u * kWaves * RPW + wave * RPW + rs; };
+    struct Stage {
+        u32x4_t c[KU];
+        uint32_t h0[HK], h1[HK];
+        int32_t pg[HK];
+    };
+    auto issue = [&](Stage &st, int base) {
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+            const int row = min(row_of(base, u, rsub), n - 1);
+            st.c[u] = *reinterpret_cast<const u32x4_t *>(s.codes + (urow + j0 + row) * D +
+                                                         16 * part);
+        }
+#pragma unroll
+        for (int h = 0; h < HK; ++h) {  // this lane's rows: step u = lane / RPW + h * LPR
+            const int row = min(row_of(base, lane / RPW + h * LPR, lane % RPW), n - 1);
+            const uint32_t *hp = reinterpret_cast<const uint32_t *>(s.hdr + urow + j0 + row);
+            st.h0[h] = hp[0];
+            st.h1[h] = hp[1];
+            st.pg[h] = bt[j0 + row];
+        }
+    };
+    auto reduce = [&](const Stage &st, int base) {
+        // the scale of each of this lane's rows, or -1: always a candidate
+        float sv[HK];
+#pragma unroll
+        for (int h = 0; h < HK; ++h) {
+            const int row = row_of(base, lane / RPW + h * LPR, lane % RPW);
+            const int page = st.pg[h];
+            const bool valid = page >= 0 && page < a.num_pages && (int)st.h0[h] == page + 1 &&
+                               j0 + row < jforce;
+            const float sc = __uint_as_float(st.h1[h]);
+            sv[h] = valid && sc < INFINITY ? sc : -1.f;  // (NaN and inf: candidates)
+        }
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+            const int row = row_of(base, u, rsub);
+            // this lane's 16 codes against its 16 query values, in a fixed order
+            float t = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t cw = st.c[u][w];
+                t = __builtin_fmaf(qf[4 * w + 0], (float)(cw & 0xffu), t);
+                t = __builtin_fmaf(qf[4 * w + 1], (float)((cw >> 8) & 0xffu), t);
+                t = __builtin_fmaf(qf[4 * w + 2], (float)((cw >> 16) & 0xffu), t);
+                t = __builtin_fmaf(qf[4 * w + 3], (float)(cw >> 24), t);
+            }
+            // sum over the row's LPR lanes (quad xor 1, quad xor 2, half-row mirror)
+            t += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                               0, __builtin_bit_cast(int, t), 0xB1, 0xF, 0xF, false));
+            t += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                               0, __builtin_bit_cast(int, t), 0x4E, 0xF, 0xF, false));
+            if constexpr (LPR == 8)
+                t += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                                   0, __builtin_bit_cast(int, t), 0x141, 0xF, 0xF,
+                                                   false));
+            // the lane that loaded this row's header: (u % LPR) * RPW + rsub, slot u / LPR
+            const float scale = __shfl(sv[u / LPR], (u % LPR) * RPW + rsub);
+            const float sa = scale * (t - q128);
+            const float e = scale * ebase;
+            if (part == 0 && row < n) {
+                lo_lds[row] = scale >= 0.f ? sa - e : -INFINITY;
+                hi_lds[row] = scale >= 0.f ? sa + e : INFINITY;
+            }
+        }
+    };
+    if (n > 0) {
+        Stage sa_, sb_;
+        issue(sa_, 0);
+        for (int base = 0;;) {
+            issue(sb_, base + ROWS);
+            reduce(sa_, base);
+            base += ROWS;
+            if (base >= n) break;
+            issue(sa_, base + ROWS);
+            reduce(sb_, base);
+            base += ROWS;
+            if (base >= n) break;
+        }
+    }
+}
+
+// The k best of m <= 256 candidate scores sc[0 .. m) (LDS, in ascending block
+// order), by rank, over the workgroup: candidate t is kept when fewer than
+// kb = min(top_k, m) candidates beat it, a candidate beating t when its score
+// is larger or equal with a lower index (equal scores go to the lower block;
+// -0.0 equals +0.0).  This is the rule of sel::select_topk, so the same blocks
+// are kept; they are written in ascending order through out (which maps
+// candidate numbers to blocks), then -1 up to top_k.  keys: 256 LDS words
+// (may alias sm.cand), wcount: kWaves LDS words (may alias sm.red).
+__device__ __forceinline__ void select_ranked(const float *sc, int m, int top_k,
+                                              const sel::TopkOut &out, uint32_t *keys,
+                                              uint32_t *wcount) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int kb = min(top_k, m);
+    const uint32_t mine = tid < m ? score_key(sc[tid]) : 0u;
+    keys[tid] = mine;  // candidates from m on hold 0
+    __syncthreads();
+    int beat = 0;
+    const int n4 = (m + 3) / 4;
+    for (int i4 = 0; i4 < n4; ++i4) {
+        const u32x4_t k4 = reinterpret_cast<const u32x4_t *>(keys)[i4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 4 * i4 + e;
+            beat += (k4[e] > mine || (k4[e] == mine && i < tid)) ? 1 : 0;
+        }
+    }
+    const bool keep = tid < m && beat < kb;
+    const uint64_t bal = __ballot(keep);
+    if (lane == 0) wcount[wave] = (uint32_t)__popcll(bal);
+    __syncthreads();
+    int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                             __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+    for (int w = 0; w < wave; ++w) pos += (int)wcount[w];
+    if (keep) out.put(pos, tid);
+    for (int i = kb + tid; i < top_k; i += kThreads) out.put(i, -1);
+    __syncthreads();  // keys and wcount are reused
+}
+
+// Stores the n interval ends staged by scan_sketch for blocks [j0, j0 + n) of
+// the unit whose rows start at urow, contiguously, with agent-scope stores (the
+// unit's selection may run in a workgroup on another XCD).  Called with the
+// staged values visible to every thread; ends with the stores issued.
+__device__ __forceinline__ void store_intervals(const SketchArgs &s, size_t urow, int j0, int n,
+                                                const float *lo_lds, const float *hi_lds) {
+    for (int i = threadIdx.x; i < n; i += kThreads) {
+        store_relaxed(s.lo + urow + j0 + i, lo_lds[i]);
+        store_relaxed(s.hi + urow + j0 + i, hi_lds[i]);
+    }
+}
+
+// Exact scores of the m blocks map[0 .. m) of unit (b, g) into sc[0 .. m)
+// (LDS), with the full scan's arithmetic (sel::row_partial, sel::row16_sum;
+// 16 lanes per centroid row), so each equals the full scan's score bit for bit;
+// an out-of-range page scores -inf and sets the error bit, as in the full scan.
+// Page ids come from pages[map[i]] (LDS, the block-table row) or, when pages is
+// NULL, from the block table.  qs: the scaled mean query (LDS).  Blocks j >= jk
+// take their score from known[j] instead (blocks whose centroid another
+// workgroup recomputed in the same launch: their fresh row may not be visible
+// here, the score stored beside it with an agent-scope store is).
+template <int D>
+__device__ __forceinline__ void rescore(const sel::SelectArgs &a, int b, int g,
+                                        const int32_t *map, int m, const int *pages,
+                                        const float *qs, float *sc, const float *known = nullptr,
+                                        int jk = 0x7fffffff) {
+    constexpr int LPR = 16, VPL = D / LPR, RPI = kWave / LPR;
+    constexpr int KU = 4, ROWS = kWaves * RPI * KU;  // 64 rows per pass
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int col = lane % LPR, rsub = lane / LPR;
+    const int32_t *bt = a.bt + (size_t)b * a.max_blocks;
+    float qf[VPL];
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) qf[e] = qs[col * VPL + e];
+    typedef floatx4_t Row[VPL / 4];
+    for (int base = 0; base < m; base += ROWS) {
+        int pg[KU], jj[KU];
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+            const int row = min(base + u * kWaves * RPI + wave * RPI + rsub, m - 1);
+            jj[u] = map[row];
+            pg[u] = pages ? pages[jj[u]] : bt[jj[u]];
+        }
+        float kn[KU];
+#pragma unroll
+        for (int u = 0; u < KU; ++u) kn[u] = known ? load_relaxed(known + min(jj[u], jk)) : 0.f;
+        Row cv[KU];
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+            const int p = pg[u] >= 0 && pg[u] < a.num_pages ? pg[u] : 0;
+            const floatx4_t *src = reinterpret_cast<const floatx4_t *>(
+                a.cent + ((size_t)p * a.Hkv + g) * D + col * VPL);
+#pragma unroll
+            for (int v = 0; v < VPL / 4; ++v) cv[u][v] = src[v];
+        }
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+            const int row = base + u * kWaves * RPI + wave * RPI + rsub;
+            const float s = sel::row16_sum(sel::row_partial<VPL>(qf, cv[u]));
+            const bool ok = pg[u] >= 0 && pg[u] < a.num_pages;
+            if (col == 0 && row < m) {
+                sc[row] = !ok ? -INFINITY : jj[u] >= jk ? kn[u] : s;
+                if (!ok) flag_error(a.err, kErrPage);
+            }
+        }
+    }
+}
+
+}  // namespace skt
+}  // namespace btk

@@ -310,6 +310,38 @@ btk_status_t btk_decode_step(const btk_problem_t *problem, const void *q, const 
                              int32_t top_k, int32_t *indices, void *out, float *lse,
                              void *workspace, size_t workspace_bytes, void *stream);
 
+/* btk_decode_step reading each unit's sketch rows (see btk_sketch_bytes) in
+ * place of its fp32 centroid rows, with results identical to btk_decode_step
+ * (indices, out, lse and centroids bit for bit).  Phase 1 computes every
+ * block's sketch interval (as btk_select_sketch); the touched blocks (j >=
+ * first_pos[b] / 16) get their centroid recomputed from the keys and then their
+ * sketch row rebuilt from it, as btk_centroid_update and btk_sketch_update with
+ * the same first_pos would, and are always kept as candidates.  Each (sequence,
+ * KV head) then takes the k_b-th largest lower end as threshold, scores the
+ * blocks whose upper end reaches it from their fp32 centroid rows exactly as
+ * btk_select scores them, keeps the k_b best with btk_select's tie rule and
+ * attends.  A unit with more than 1024 such candidates scores every block.
+ * The sketch must hold rows for the blocks before first_pos built from their
+ * current centroids (btk_sketch_update after prefill; every call keeps the
+ * rows of the blocks it touches current); a row that does not name its block's
+ * page is never used to drop it, so any contents give the same results, only
+ * more slowly.  (Pith review, "What carries the argument": the method's block
+ * scores and top-k; the sketch is this library's way of reading fewer bytes
+ * for them.)
+ *   sketch       in/out, sketch_bytes >= btk_sketch_bytes(problem)
+ *   cand_counts  out [B][Hkv] int32, or NULL: per unit the number of blocks
+ *                whose fp32 centroid row the selection read (0 when every
+ *                block is kept)
+ *   other arguments, limits and errors as btk_decode_step, with
+ *   batch * num_kv_heads * (max_blocks_per_seq + 512) < 2^32. */
+btk_status_t btk_decode_step_sketch(const btk_problem_t *problem, const void *q,
+                                    const void *k_cache, const void *v_cache,
+                                    const int32_t *block_table, const int32_t *seq_lens,
+                                    const int32_t *first_pos, float *centroids, void *sketch,
+                                    size_t sketch_bytes, int32_t top_k, int32_t *indices,
+                                    void *out, float *lse, int32_t *cand_counts, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+
 /* btk_decode_step with the KV append of the step fused in: the newest token of
  * each sequence, at position seq_lens[b] - 1 (seq_lens count it), is written
  * into its cache slot from k_new / v_new before it is averaged into its

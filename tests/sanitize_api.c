@@ -238,6 +238,21 @@ int main(void) {
                BTK_ERR_WORKSPACE);
         EXPECT(btk_select_sketch(&p, dev, wf, dev, sk, di, di, 64, wi, ws, need - 1, NULL),
                BTK_ERR_WORKSPACE);
+        EXPECT(btk_decode_step_sketch(NULL, dev, dev, dev, di, di, di, wf, dev, sk, 64, wi, dev,
+                                      NULL, NULL, ws, need, NULL),
+               BTK_ERR_NULL);
+        EXPECT(btk_decode_step_sketch(&p, dev, dev, dev, di, di, di, wf, NULL, sk, 64, wi, dev,
+                                      NULL, NULL, ws, need, NULL),
+               BTK_ERR_NULL);
+        EXPECT(btk_decode_step_sketch(&p, dev, dev, dev, di, di, di, wf, dev, sk, 0, wi, dev,
+                                      NULL, NULL, ws, need, NULL),
+               BTK_ERR_SHAPE);
+        EXPECT(btk_decode_step_sketch(&p, dev, dev, dev, di, di, di, wf, dev, sk - 1, 64, wi, dev,
+                                      NULL, NULL, ws, need, NULL),
+               BTK_ERR_WORKSPACE);
+        EXPECT(btk_decode_step_sketch(&p, dev, dev, dev, di, di, di, wf, dev, sk, 64, wi, dev,
+                                      NULL, NULL, ws, need - 1, NULL),
+               BTK_ERR_WORKSPACE);
     }
 
     /* counter-calibration probe */

@@ -289,3 +289,18 @@ def test_sketch_calls_validate_on_host():
     assert lib.btk_select_sketch(pp, *sel(k_=0)) == btk.BTK_ERR_SHAPE
     assert lib.btk_select_sketch(pp, *sel(skn=sk - 1)) == btk.BTK_ERR_WORKSPACE
     assert lib.btk_select_sketch(pp, *sel(wsn=need - 1)) == btk.BTK_ERR_WORKSPACE
+    # the step through the sketch: the step's checks, then the sketch's
+    need_k = btk.btk_workspace_bytes(p, 64)
+    st = lambda **o: [FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, o.get("sk", FAKE),
+                      o.get("skn", sk), o.get("k_", 64), o.get("idx", FAKE), FAKE, None, None,
+                      o.get("ws", FAKE), o.get("wsn", need_k), None]  # noqa: E731
+    assert lib.btk_decode_step_sketch(None, *st()) == btk.BTK_ERR_NULL
+    assert lib.btk_decode_step_sketch(pp, *st(sk=None)) == btk.BTK_ERR_NULL
+    assert lib.btk_decode_step_sketch(pp, *st(idx=None)) == btk.BTK_ERR_NULL
+    assert lib.btk_decode_step_sketch(pp, *st(k_=0)) == btk.BTK_ERR_SHAPE
+    assert lib.btk_decode_step_sketch(pp, *st(skn=sk - 1)) == btk.BTK_ERR_WORKSPACE
+    assert lib.btk_decode_step_sketch(pp, *st(wsn=need_k - 1)) == btk.BTK_ERR_WORKSPACE
+    assert lib.btk_decode_step_sketch(pp, *st(ws=None)) == btk.BTK_ERR_WORKSPACE
+    # rows beyond the 32-bit counters (batch * Hkv * (max_blocks + 512) >= 2^32)
+    big = _problem(batch=65536, num_q_heads=8, num_kv_heads=8, max_blocks_per_seq=8192)
+    assert lib.btk_decode_step_sketch(ctypes.byref(big), *st()) == btk.BTK_ERR_UNSUPPORTED
