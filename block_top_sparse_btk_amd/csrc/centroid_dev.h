@@ -46,7 +46,15 @@ struct KeyTile {
         for (int i = 0; i < NI; ++i)
             if (i * TPI + row == t) w[i] = slice;
     }
+    // The mean of the v valid rows to gdst (global) and, when ldst is not NULL,
+    // to ldst (LDS, the caller's copy; the test is made on a flag because the
+    // compiler folded a NULL test of an LDS pointer into an operand form that
+    // gfx950 does not encode).
     __device__ __forceinline__ void mean(int v, float *gdst, float *ldst, int lane) const {
+        mean_to(v, gdst, ldst, ldst != nullptr, lane);
+    }
+    __device__ __forceinline__ void mean_to(int v, float *gdst, float *ldst, bool to_lds,
+                                            int lane) const {
         const int col = lane % LPR, row = lane / LPR;
         float acc[VEC];
 #pragma unroll
@@ -69,7 +77,7 @@ struct KeyTile {
                 const floatx4_t o = {acc[e] / vf, acc[e + 1] / vf, acc[e + 2] / vf,
                                      acc[e + 3] / vf};
                 *reinterpret_cast<floatx4_t *>(gdst + col * VEC + e) = o;
-                if (ldst) *reinterpret_cast<floatx4_t *>(ldst + col * VEC + e) = o;
+                if (to_lds) *reinterpret_cast<floatx4_t *>(ldst + col * VEC + e) = o;
             }
         }
     }

@@ -84,18 +84,21 @@ struct TopkSmem {
 
 // Where a selection goes: the caller's index row (or NULL) and, inside a
 // decode step, the entries [lo, hi) of it into LDS for the workgroup's own
-// attention (lds[i - lo] holds entry i).
+// attention (lds[i - lo] holds entry i; lo = hi = 0 when there is none).
+// Pointers into LDS are never tested against NULL here: the compiler folded
+// such a test into an operand form that gfx950 does not encode.
 struct TopkOut {
     int32_t *idx;            // [top_k] or NULL
     int32_t *lds = nullptr;  // [hi - lo] or NULL
     int lo = 0, hi = 0;
     // the keys were a subset of the blocks, in ascending block order: key i is
-    // block map[i] (LDS); NULL: key i is block i
+    // block map[i] (LDS) when mapped, else block i
     const int32_t *map = nullptr;
+    bool mapped = false;
     __device__ __forceinline__ void put(int pos, int32_t j) const {
-        if (map && j >= 0) j = map[j];
+        if (mapped && j >= 0) j = map[j];
         if (idx) store_relaxed_i32(idx + pos, j);
-        if (lds && pos >= lo && pos < hi) lds[pos - lo] = j;
+        if (pos >= lo && pos < hi) lds[pos - lo] = j;
     }
 };
 
@@ -674,7 +677,7 @@ __device__ __forceinline__ void scan_rows(const SelectArgs &a, int b, int g, int
                        *reinterpret_cast<const u32x4_t *>(sm.newtok + (lane % KeyTile<T, D>::LPR) *
                                                         (KeyTile<T, D>::VEC * sizeof(T) / 4)),
                        lane);
-        kt.mean(v, a.cent_out + ((size_t)page * a.Hkv + g) * D, row_lds, lane);
+        kt.mean_to(v, a.cent_out + ((size_t)page * a.Hkv + g) * D, row_lds, true, lane);
         __builtin_amdgcn_wave_barrier();
         Row cv;
 #pragma unroll

@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kThreads, 4) void select_sketch_kernel(sel::SelectA
     float *lo_lds = sc_lds, *hi_lds = reinterpret_cast<float *>(pages);
     for (int s0 = j0; s0 < j0 + n; s0 += kMaxChunk) {
         const int nr = min(kMaxChunk, j0 + n - s0);
-        skt::scan_sketch<D, 1>(a, s, b, g, s0, nr, qs, qsum_s[0], qsum_s[1], nb, lo_lds, hi_lds);
+        skt::scan_sketch<D, 1>(a, s, b, g, s0, nr, qs, qsum_s, nb, lo_lds, hi_lds, [] {});
         __syncthreads();
         skt::store_intervals(s, (size_t)unit * a.max_blocks, s0, nr, lo_lds, hi_lds);
         __syncthreads();  // the staging areas are reused
@@ -152,7 +152,8 @@ __global__ __launch_bounds__(kThreads, 4) void select_sketch_kernel(sel::SelectA
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the exact scores are stored
     __syncthreads();
     sel::TopkOut o{out};
-    o.map = mapped ? cmap : nullptr;
+    o.map = cmap;
+    o.mapped = mapped;
     sel::select_topk(sel::PlainScores{s.exact + urow}, m, a.top_k, o, tk);
 }
 

@@ -245,17 +245,20 @@ __device__ __forceinline__ int threshold_candidates(const float *lo, const float
 // not once per lane: each lane loads those of HK rows of the stage (lane l:
 // rows l and l + 64 in the wave's row order) and the lanes holding a row take
 // its scale from there (a lane permute), so a stage costs 4 KU + 3 HK
-// registers instead of 7 KU.  qs: the scaled mean query (LDS); q128 = 128 *
-// sum(qs), qn1 = sum |qs|.  Blocks j >= jforce (refreshed in this call) and
-// rows whose header does not name the block's page get (-inf, +inf): always
-// candidates.  Nothing is stored to memory inside the loop: stores count in the
-// same in-order memory counter as the loads, so a store issued there would hold
-// up the wait for the next stage's rows until it completed.
-template <int D, int HK>
+// registers instead of 7 KU.  qs: the scaled mean query (LDS); qsum (LDS):
+// q128 = 128 * sum(qs), qn1 = sum |qs|; both are read after prep(), which the
+// scan calls (workgroup-uniformly) once its first stage is requested, so that
+// the caller can form them while those rows are in flight.  Blocks j >= jforce
+// (refreshed in this call) and rows whose header does not name the block's page
+// get (-inf, +inf): always candidates.  Nothing is stored to memory inside the
+// loop: stores count in the same in-order memory counter as the loads, so a
+// store issued there would hold up the wait for the next stage's rows until it
+// completed.
+template <int D, int HK, typename Prep>
 __device__ __forceinline__ void scan_sketch(const sel::SelectArgs &a, const SketchArgs &s, int b,
-                                            int g, int j0, int n, const float *qs, float q128,
-                                            float qn1, int jforce, float *lo_lds,
-                                            float *hi_lds) {
+                                            int g, int j0, int n, const float *qs,
+                                            const float *qsum, int jforce, float *lo_lds,
+                                            float *hi_lds, Prep &&prep) {
     constexpr int LPR = D / 16;          // lanes per row
     constexpr int RPW = kWave / LPR;     // rows per wave per load
     constexpr int KU = HK * LPR;         // load steps per stage: HK * 64 rows per wave
@@ -265,9 +268,7 @@ __device__ __forceinline__ void scan_sketch(const sel::SelectArgs &a, const Sket
     const size_t urow = ((size_t)b * a.Hkv + g) * a.max_blocks;
     const int32_t *bt = a.bt + (size_t)b * a.max_blocks;
     float qf[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) qf[e] = qs[16 * part + e];
-    const float ebase = kBoundFactor * qn1;
+    float q128 = 0.f, ebase = 0.f;
     // row of load step u, row group rs, in a stage starting at base
     auto row_of = [&](int base, int u, int rs) { return base + u * kWaves * RPW + wave * RPW + rs; };
     struct Stage {
@@ -338,6 +339,11 @@ __device__ __forceinline__ void scan_sketch(const sel::SelectArgs &a, const Sket
     if (n > 0) {
         Stage sa_, sb_;
         issue(sa_, 0);
+        prep();
+#pragma unroll
+        for (int e = 0; e < 16; ++e) qf[e] = qs[16 * part + e];
+        q128 = qsum[0];
+        ebase = kBoundFactor * qsum[1];
         for (int base = 0;;) {
             issue(sb_, base + ROWS);
             reduce(sa_, base);
@@ -405,16 +411,16 @@ __device__ __forceinline__ void store_intervals(const SketchArgs &s, size_t urow
 // (LDS), with the full scan's arithmetic (sel::row_partial, sel::row16_sum;
 // 16 lanes per centroid row), so each equals the full scan's score bit for bit;
 // an out-of-range page scores -inf and sets the error bit, as in the full scan.
-// Page ids come from pages[map[i]] (LDS, the block-table row) or, when pages is
-// NULL, from the block table.  qs: the scaled mean query (LDS).  Blocks j >= jk
+// Page ids come from pages[map[i]] (LDS, the block-table row) when row_lds,
+// else from the block table.  qs: the scaled mean query (LDS).  Blocks j >= jk
 // take their score from known[j] instead (blocks whose centroid another
 // workgroup recomputed in the same launch: their fresh row may not be visible
 // here, the score stored beside it with an agent-scope store is).
 template <int D>
 __device__ __forceinline__ void rescore(const sel::SelectArgs &a, int b, int g,
                                         const int32_t *map, int m, const int *pages,
-                                        const float *qs, float *sc, const float *known = nullptr,
-                                        int jk = 0x7fffffff) {
+                                        bool row_lds, const float *qs, float *sc,
+                                        const float *known, int jk) {
     constexpr int LPR = 16, VPL = D / LPR, RPI = kWave / LPR;
     constexpr int KU = 4, ROWS = kWaves * RPI * KU;  // 64 rows per pass
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -424,35 +430,54 @@ __device__ __forceinline__ void rescore(const sel::SelectArgs &a, int b, int g,
 #pragma unroll
     for (int e = 0; e < VPL; ++e) qf[e] = qs[col * VPL + e];
     typedef floatx4_t Row[VPL / 4];
-    for (int base = 0; base < m; base += ROWS) {
+    struct Stage {
+        Row cv[KU];
         int pg[KU], jj[KU];
+        float kn[KU];
+    };
+    // two stages of ROWS rows in flight: the page ids come from LDS (or the
+    // block table), then every row of the stage is requested at once
+    auto issue = [&](Stage &st, int base) {
 #pragma unroll
         for (int u = 0; u < KU; ++u) {
             const int row = min(base + u * kWaves * RPI + wave * RPI + rsub, m - 1);
-            jj[u] = map[row];
-            pg[u] = pages ? pages[jj[u]] : bt[jj[u]];
+            st.jj[u] = map[row];
+            st.pg[u] = row_lds ? pages[st.jj[u]] : bt[st.jj[u]];
         }
-        float kn[KU];
-#pragma unroll
-        for (int u = 0; u < KU; ++u) kn[u] = known ? load_relaxed(known + min(jj[u], jk)) : 0.f;
-        Row cv[KU];
 #pragma unroll
         for (int u = 0; u < KU; ++u) {
-            const int p = pg[u] >= 0 && pg[u] < a.num_pages ? pg[u] : 0;
+            const int p = st.pg[u] >= 0 && st.pg[u] < a.num_pages ? st.pg[u] : 0;
             const floatx4_t *src = reinterpret_cast<const floatx4_t *>(
                 a.cent + ((size_t)p * a.Hkv + g) * D + col * VPL);
 #pragma unroll
-            for (int v = 0; v < VPL / 4; ++v) cv[u][v] = src[v];
+            for (int v = 0; v < VPL / 4; ++v) st.cv[u][v] = src[v];
+            st.kn[u] = load_relaxed(known + min(st.jj[u], jk));
         }
+    };
+    auto reduce = [&](const Stage &st, int base) {
 #pragma unroll
         for (int u = 0; u < KU; ++u) {
             const int row = base + u * kWaves * RPI + wave * RPI + rsub;
-            const float s = sel::row16_sum(sel::row_partial<VPL>(qf, cv[u]));
-            const bool ok = pg[u] >= 0 && pg[u] < a.num_pages;
+            const float s = sel::row16_sum(sel::row_partial<VPL>(qf, st.cv[u]));
+            const bool ok = st.pg[u] >= 0 && st.pg[u] < a.num_pages;
             if (col == 0 && row < m) {
-                sc[row] = !ok ? -INFINITY : jj[u] >= jk ? kn[u] : s;
+                sc[row] = !ok ? -INFINITY : st.jj[u] >= jk ? st.kn[u] : s;
                 if (!ok) flag_error(a.err, kErrPage);
             }
+        }
+    };
+    if (m > 0) {
+        Stage sa_, sb_;
+        issue(sa_, 0);
+        for (int base = 0;;) {
+            if (base + ROWS < m) issue(sb_, base + ROWS);
+            reduce(sa_, base);
+            base += ROWS;
+            if (base >= m) break;
+            if (base + ROWS < m) issue(sa_, base + ROWS);
+            reduce(sb_, base);
+            base += ROWS;
+            if (base >= m) break;
         }
     }
 }

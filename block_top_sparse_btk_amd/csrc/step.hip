@@ -102,6 +102,8 @@ constexpr uint32_t segment_cost() {
 // threshold) that a phase-2 item scores exactly from LDS; beyond, it scores
 // every block of the unit.
 constexpr int kStepCand = 1024;
+constexpr int kRowPer = kRun / kThreads;  // block-table entries per thread (phase 2)
+constexpr int step_qn(int D) { return (kMaxGroup * D + kThreads - 1) / kThreads; }
 // Header loads per lane per sketch-scan stage (a stage is 64 * HK rows per wave).
 #ifndef BTK_SKETCH_HK
 #define BTK_SKETCH_HK 1
@@ -121,7 +123,8 @@ constexpr int kStealFrac = BTK_STEP_STEAL_FRAC;
 #endif
 template <bool SKETCH>
 constexpr uint64_t stolen_rows(uint64_t R) {
-    return SKETCH ? (BTK_STEP_SKETCH_STEAL_FRAC > 0 ? R / BTK_STEP_SKETCH_STEAL_FRAC : 0)
+    constexpr uint64_t kSketchFrac = BTK_STEP_SKETCH_STEAL_FRAC;
+    return SKETCH ? (kSketchFrac > 0 ? R / (kSketchFrac > 0 ? kSketchFrac : 1) : 0)
                   : R / kStealFrac;
 }
 // Sequences whose row prefix a workgroup holds in LDS at once; a larger batch is
@@ -200,20 +203,35 @@ __device__ __forceinline__ void sketch_segment(const StepArgs &a, int b, int g, 
     }
     const bool refresh = a.s.first_pos && fp >= 0 && fp < L;
     const int jt = refresh ? fp / kPage : nb;  // the first touched block
-    // setup in one round trip: the group's queries
-    sel::load_setup<T, D, kThreads>(a.s, b, g, j0, 0, sm);
-    __syncthreads();
-    sel::mean_query<D>(a.s, sm);
-    __syncthreads();
-    skt::query_sums<D>(sm.qs, qsum);
-    __syncthreads();
+    // the group's queries are requested first; they go to LDS and form the
+    // scaled mean query while the scan's first rows are in flight
+    const int tid = threadIdx.x, r = a.s.Hq / a.s.Hkv;
+    const T *qp = static_cast<const T *>(a.s.q) + ((size_t)b * a.s.Hq + (size_t)g * r) * D;
+    float qv[step_qn(D)];
+#pragma unroll
+    for (int k = 0; k < step_qn(D); ++k)
+        qv[k] = sel::load_q<T>(qp + min(k * kThreads + tid, r * D - 1));
+    auto prep = [&]() {
+#pragma unroll
+        for (int k = 0; k < step_qn(D); ++k)
+            if (k * kThreads + tid < r * D) sm.qraw[k * kThreads + tid] = qv[k];
+        __syncthreads();
+        sel::mean_query<D>(a.s, sm);
+        __syncthreads();
+        skt::query_sums<D>(sm.qs, qsum);
+        __syncthreads();
+    };
     // in runs of up to kRun blocks staged in LDS (sm.sc, and sm.pages as floats)
     float *lo_lds = sm.sc, *hi_lds = reinterpret_cast<float *>(sm.pages);
     const size_t urow = (size_t)unit * a.s.max_blocks;
     for (int s0 = j0; s0 < j1; s0 += kRun) {
         const int n = min(kRun, j1 - s0);
-        skt::scan_sketch<D, BTK_SKETCH_HK>(a.s, a.k, b, g, s0, n, sm.qs, qsum[0], qsum[1], jt,
-                                           lo_lds, hi_lds);
+        if (s0 == j0)
+            skt::scan_sketch<D, BTK_SKETCH_HK>(a.s, a.k, b, g, s0, n, sm.qs, qsum, jt, lo_lds,
+                                               hi_lds, prep);
+        else
+            skt::scan_sketch<D, BTK_SKETCH_HK>(a.s, a.k, b, g, s0, n, sm.qs, qsum, jt, lo_lds,
+                                               hi_lds, [] {});
         __syncthreads();
         skt::store_intervals(a.k, urow, s0, n, lo_lds, hi_lds);
         __syncthreads();  // the staging areas are reused
@@ -258,8 +276,6 @@ __device__ __forceinline__ void load_window(const StepArgs &a, int base, int wle
 // that the plain step carries none of its code).  SPLITS: the attention of a
 // unit may be split over several items (instances without it carry no split
 // merge, whose code alone made the one-split step slower).
-constexpr int kRowPer = kRun / kThreads;  // block-table entries per thread (phase 2)
-constexpr int step_qn(int D) { return (kMaxGroup * D + kThreads - 1) / kThreads; }
 
 // With sketches, a phase-2 item up to its unit being ready: the group's
 // queries and, when row_lds, the block-table row go to LDS and the scaled mean
@@ -319,7 +335,7 @@ __device__ __forceinline__ void sketch_item_setup(const StepArgs &a, int unit, i
         const int v = min(kPage, L - j * kPage);
         float *row_lds = crow + wave * D;
         if (j != jw) kt.load(keys + (size_t)page * page_stride, v, lane);
-        kt.mean(v, a.s.cent_out + ((size_t)page * a.s.Hkv + g) * D, row_lds, lane);
+        kt.mean_to(v, a.s.cent_out + ((size_t)page * a.s.Hkv + g) * D, row_lds, true, lane);
         __builtin_amdgcn_wave_barrier();
         floatx4_t cv[VPL / 4];
 #pragma unroll
@@ -363,11 +379,12 @@ __device__ __forceinline__ void select_sketched(const StepArgs &a, int unit, int
         const int m = skt::threshold_candidates(a.k.lo + urow, a.k.hi + urow, nb, kb, cmap,
                                                 kStepCand, tk, tk.cand, ctot);
         if (m <= kStepCand) {
-            skt::rescore<D>(a.s, b, g, cmap, m, row_lds ? sm.pages : nullptr, sm.qs, cex,
-                            a.k.exact + urow, jt);
+            skt::rescore<D>(a.s, b, g, cmap, m, sm.pages, row_lds, sm.qs, cex, a.k.exact + urow,
+                            jt);
             __syncthreads();
             sel::TopkOut o{idx, list, lo, hi};
             o.map = cmap;
+            o.mapped = true;
             if (m <= kThreads)
                 skt::select_ranked(cex, m, a.s.top_k, o, tk.cand, tk.red);
             else
