@@ -54,7 +54,8 @@ bool top_k_ok(int32_t top_k) { return top_k >= 1 && top_k <= btk::kMaxBlocksPerS
 // Test hook of the decode step, read from the environment at each call (results
 // never depend on it): BTK_STEP_TEST_FLAGS bit 0 makes every workgroup leave its
 // own share for workgroup 0 and the workgroups without phase-2 items to claim,
-// as if it had not started.
+// as if it had not started; with sketches, bit 1 takes the one-workgroup-per-unit
+// kernel whenever its limits allow (however few the units), bit 2 never.
 uint32_t env_u32(const char *name, uint32_t dflt) {
     const char *e = getenv(name);
     if (e && *e) {
@@ -64,7 +65,7 @@ uint32_t env_u32(const char *name, uint32_t dflt) {
     }
     return dflt;
 }
-uint32_t step_test_flags() { return env_u32("BTK_STEP_TEST_FLAGS", 0u) & 1u; }
+uint32_t step_test_flags() { return env_u32("BTK_STEP_TEST_FLAGS", 0u) & 7u; }
 
 }  // namespace
 

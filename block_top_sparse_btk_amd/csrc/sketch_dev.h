@@ -120,11 +120,14 @@ __device__ __forceinline__ void query_sums(const float *qs, float *out) {
 // together; beyond, the upper ends once tau is known (fewer registers).  The
 // lower ends go through the radix passes of the four-wave top-k
 // (sel::select_topk_wg4).  count: LDS of KMAX * kWaves words (may alias
-// sm.cand), total: one LDS word.
-template <int KMAX>
+// sm.cand), total: one LDS word.  LDS: the ends are in this workgroup's LDS
+// (plain loads) instead of the workspace (agent-scope loads); every end is read
+// before the first barrier, so map may alias lo_src (KMAX <= 8).
+template <int KMAX, bool LDS = false>
 __device__ __forceinline__ int threshold_candidates_wg4(const float *lo_src, const float *hi_src, int nb, int kb,
                                         int32_t *map, int cap, sel::TopkSmem &sm,
                                         uint32_t *count, int *total) {
+    auto ld = [](const float *p) { return LDS ? *p : load_relaxed(p); };
     uint32_t *red = sm.red;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     for (int i = tid; i < sel::kTopkPasses * sel::kHistWords / 4; i += kThreads)
@@ -133,9 +136,9 @@ __device__ __forceinline__ int threshold_candidates_wg4(const float *lo_src, con
     uint32_t key[KMAX], hk[kHiEarly ? KMAX : 1];
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) {  // unconditional (clamped): all in flight together
-        key[i] = __float_as_uint(load_relaxed(lo_src + min(i * kThreads + tid, nb - 1)));
+        key[i] = __float_as_uint(ld(lo_src + min(i * kThreads + tid, nb - 1)));
         if constexpr (kHiEarly)
-            hk[i] = __float_as_uint(load_relaxed(hi_src + min(i * kThreads + tid, nb - 1)));
+            hk[i] = __float_as_uint(ld(hi_src + min(i * kThreads + tid, nb - 1)));
     }
     uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
@@ -186,7 +189,7 @@ __device__ __forceinline__ int threshold_candidates_wg4(const float *lo_src, con
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) {
         const uint32_t hv = kHiEarly ? hk[kHiEarly ? i : 0]
-                                     : __float_as_uint(load_relaxed(hi_src + min(i * kThreads + tid, nb - 1)));
+                                     : __float_as_uint(ld(hi_src + min(i * kThreads + tid, nb - 1)));
         const bool f = i * kThreads + tid < nb && score_key(__uint_as_float(hv)) >= tau;
         flags |= (uint32_t)f << i;
         const uint64_t bal = __ballot(f);
@@ -223,15 +226,17 @@ __device__ __forceinline__ int threshold_candidates_wg4(const float *lo_src, con
     return m;
 }
 
-// Dispatch on nb (at most 32 keys per thread: 8192 blocks), kb < nb.
+// Dispatch on nb (at most 32 keys per thread: 8192 blocks; ends in LDS: at
+// most 2048 blocks), kb < nb.
+template <bool LDS = false>
 __device__ __forceinline__ int threshold_candidates(const float *lo, const float *hi, int nb,
                                                     int kb, int32_t *map, int cap,
                                                     sel::TopkSmem &sm, uint32_t *count,
                                                     int *total) {
     if (nb <= 4 * kThreads)
-        return threshold_candidates_wg4<4>(lo, hi, nb, kb, map, cap, sm, count, total);
-    if (nb <= 8 * kThreads)
-        return threshold_candidates_wg4<8>(lo, hi, nb, kb, map, cap, sm, count, total);
+        return threshold_candidates_wg4<4, LDS>(lo, hi, nb, kb, map, cap, sm, count, total);
+    if (LDS || nb <= 8 * kThreads)
+        return threshold_candidates_wg4<8, LDS>(lo, hi, nb, kb, map, cap, sm, count, total);
     if (nb <= 16 * kThreads)
         return threshold_candidates_wg4<16>(lo, hi, nb, kb, map, cap, sm, count, total);
     return threshold_candidates_wg4<32>(lo, hi, nb, kb, map, cap, sm, count, total);

@@ -65,7 +65,8 @@ struct StepArgs {
     skt::SketchArgs k;
     int32_t *cand_counts;
     uint32_t spin_limit;         // bound of a phase-2 wait (polls)
-    uint32_t test_flags;         // bit 0: owners leave their shares unclaimed (tests only)
+    uint32_t test_flags;         // bit 0: owners leave their shares unclaimed; bits 1, 2:
+                                 // the unit kernel always / never (tests only)
     int B, units, nsplit;
 };
 
@@ -284,8 +285,9 @@ __device__ __forceinline__ void load_window(const StepArgs &a, int base, int wle
 // 1, jt + w + 2, ... in wave w): centroid recomputed from the keys (stored;
 // each split stores the same values), exact score (as the full scan scores a
 // refreshed block, into the workspace's score area) and sketch row rebuilt.
-// None of the refresh reads what phase 1 writes.
-template <typename T, int D>
+// None of the refresh reads what phase 1 writes.  WAIT = false: no wait (the
+// unit's intervals are this workgroup's own).
+template <typename T, int D, bool WAIT = true>
 __device__ __forceinline__ void sketch_item_setup(const StepArgs &a, int unit, int b, int L, int nb, int jt,
                                   const float (&qv)[step_qn(D)], bool row_lds,
                                   const int32_t (&prow)[kRowPer], sel::ScoreSmem &sm,
@@ -318,7 +320,7 @@ __device__ __forceinline__ void sketch_item_setup(const StepArgs &a, int unit, i
 #pragma unroll
     for (int e = 0; e < VPL; ++e) qf[e] = sm.qs[(lane % 16) * VPL + e];
     const size_t urow = (size_t)unit * a.s.max_blocks;
-    if (tid == 0) {
+    if (WAIT && tid == 0) {
         const uint32_t *rw = a.ready + (size_t)unit * kReadyStride;
         uint32_t spins = 0;
         while (__hip_atomic_load(rw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != tag) {
@@ -358,12 +360,14 @@ __device__ __forceinline__ void sketch_item_setup(const StepArgs &a, int unit, i
 // indices equal the full scan's.  A unit with more than kStepCand candidates
 // scores every block (the full scan's code, into the workspace's score area).
 // Ends with the split's entries in `list` and the row in sm.pages, like the
-// full-scan item.
-template <typename T, int D>
+// full-scan item.  IV_LDS: the interval ends lo_iv / hi_iv are in LDS (the
+// unit kernel's own; cmap and cex may alias them), else in the workspace.
+template <typename T, int D, bool IV_LDS = false>
 __device__ __forceinline__ void select_sketched(const StepArgs &a, int unit, int split, int b, int L, int nb,
                                 int fp, int jt, int lo, int hi, bool row_lds,
                                 sel::ScoreSmem &sm, sel::TopkSmem &tk, int32_t *list,
-                                int32_t *cmap, float *cex, int *ctot, float *crow) {
+                                int32_t *cmap, float *cex, int *ctot, float *crow,
+                                const float *lo_iv, const float *hi_iv) {
     const int tid = threadIdx.x, g = unit % a.s.Hkv;
     int32_t *idx = split == 0 ? a.s.indices + (size_t)unit * a.s.top_k : nullptr;
     const int kb = min(a.s.top_k, nb);
@@ -376,7 +380,7 @@ __device__ __forceinline__ void select_sketched(const StepArgs &a, int unit, int
         sel::select_topk(skt::LdsScores{cex}, nb, a.s.top_k, sel::TopkOut{idx, list, lo, hi}, tk);
     } else {
         const size_t urow = (size_t)unit * a.s.max_blocks;
-        const int m = skt::threshold_candidates(a.k.lo + urow, a.k.hi + urow, nb, kb, cmap,
+        const int m = skt::threshold_candidates<IV_LDS>(lo_iv, hi_iv, nb, kb, cmap,
                                                 kStepCand, tk, tk.cand, ctot);
         if (m <= kStepCand) {
             skt::rescore<D>(a.s, b, g, cmap, m, sm.pages, row_lds, sm.qs, cex, a.k.exact + urow,
@@ -667,7 +671,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
         const int lo = split * a.t.bps, hi = min(a.s.top_k, lo + a.t.bps);
         if (SKETCH && nb >= 0) {
             select_sketched<T, D>(a, unit, split, bu, L, nb, fp, jt, lo, hi, row_lds, sm, tk, list,
-                                  cmap, cex, &ctot, crow);
+                                  cmap, cex, &ctot, crow,
+                                  a.k.lo + (size_t)unit * a.s.max_blocks,
+                                  a.k.hi + (size_t)unit * a.s.max_blocks);
         } else if (!SKETCH && nb >= 0) {
             __builtin_amdgcn_s_setprio(3);
             sel::select_topk(sel::PlainScores{a.s.scores + (size_t)unit * a.s.max_blocks}, nb,
@@ -702,6 +708,123 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
                                __HIP_MEMORY_SCOPE_AGENT);
         }
     }
+}
+
+// With sketches, when the units fill the device: one workgroup per (sequence,
+// KV head) unit does the whole step for it, so no workgroup waits for another.
+// The unit's sketch rows are scanned into intervals held in LDS (the first
+// stage of rows is in flight while the queries are averaged and the touched
+// blocks refreshed), the threshold and the candidates come from those
+// intervals, the candidates are scored exactly from their fp32 rows, the k
+// best kept, and the unit attended with more blocks in flight.  One
+// workgroup per SIMD set (launch bounds 256 x 1): the registers hold deeper
+// pipelines than the two-per-CU persistent kernel can.  Limits (checked on the
+// host): at most kRun blocks per sequence, one attention split, top_k <= 256
+// and a group of at most 8 heads.  Results are those of the persistent form
+// (the same device functions in the same order per unit).
+// Attention stages in flight in the unit kernel (one block each, computed in
+// the order of the persistent kernel's two-stage pipeline, so the same bits).
+#ifndef BTK_UNIT_NST
+#define BTK_UNIT_NST 4
+#endif
+#ifndef BTK_UNIT_HK
+#define BTK_UNIT_HK 2
+#endif
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads, 1) void decode_step_unit_kernel(StepArgs a) {
+    __shared__ float qs[D];
+    __shared__ int pages[kRun];
+    __shared__ float lo_lds[kRun], hi_lds[kRun];  // interval ends; then candidates (cmap, cex)
+    __shared__ int flag;
+    __shared__ uint32_t hist[sel::kTopkPasses * sel::kHistWords], cand[4 * kWave];
+    __shared__ uint32_t red[2 * kWaves];
+    __shared__ int scan_red[kWaves];
+    __shared__ float crow[kWaves * D];
+    __shared__ int32_t list[4 * kWave];  // the selection (top_k <= 256)
+    __shared__ float qsum[2];
+    __shared__ int ctot;
+    extern __shared__ float dyn[];  // queries, then the attention's wave merge
+    sel::ScoreSmem sm{dyn, qs, pages, lo_lds, &flag, nullptr};
+    sel::TopkSmem tk{hist, cand, red, scan_red, reinterpret_cast<uint32_t *>(dyn)};
+    const int tid = threadIdx.x, Hkv = a.s.Hkv;
+    const int unit = (int)blockIdx.x, b = unit / Hkv, g = unit % Hkv;
+    const int L = valid_len(a.s.seq_lens[b], a.s.max_blocks);
+    if (L < 0) {  // -1 indices, the error flagged; no output (as the persistent form)
+        for (int i = tid; i < a.s.top_k; i += kThreads)
+            a.s.indices[(size_t)unit * a.s.top_k + i] = -1;
+        if (tid == 0) {
+            flag_error(a.s.err, kErrSeqLen);
+            if (a.cand_counts) a.cand_counts[unit] = 0;
+        }
+        return;
+    }
+    const int nb = (L + kPage - 1) / kPage;
+    const int fp = touched_pos<false>(a, b, L);
+    const int jt = a.s.first_pos && fp >= 0 && fp < L ? fp / kPage : nb;
+    const int r = a.s.Hq / Hkv;
+    // the queries and the block-table row, requested first
+    const T *qp = static_cast<const T *>(a.s.q) + ((size_t)b * a.s.Hq + (size_t)g * r) * D;
+    float qv[step_qn(D)];
+#pragma unroll
+    for (int k = 0; k < step_qn(D); ++k)
+        qv[k] = sel::load_q<T>(qp + min(k * kThreads + tid, r * D - 1));
+    int32_t prow[kRowPer];
+    {
+        const int32_t *bt_row = a.s.bt + (size_t)b * a.s.max_blocks;
+#pragma unroll
+        for (int i = 0; i < kRowPer; ++i) prow[i] = bt_row[min(i * kThreads + tid, nb - 1)];
+    }
+    // S2 (sketch): every block's interval into LDS; the touched blocks j >= jt
+    // are refreshed (S1) while the first rows are in flight, and are candidates
+    skt::scan_sketch<D, BTK_UNIT_HK>(a.s, a.k, b, g, 0, nb, sm.qs, qsum, jt, lo_lds, hi_lds,
+                                     [&] {
+                                         sketch_item_setup<T, D, false>(a, unit, b, L, nb, jt, qv,
+                                                                         true, prow, sm, crow, 0u);
+                                         skt::query_sums<D>(sm.qs, qsum);
+                                         __syncthreads();
+                                     });
+    __syncthreads();
+    // S3: threshold, candidates scored exactly, the k best (cmap, cex alias the ends)
+    select_sketched<T, D, true>(a, unit, 0, b, L, nb, fp, jt, 0, a.s.top_k, true, sm, tk, list,
+                                reinterpret_cast<int32_t *>(lo_lds), hi_lds, &ctot, crow,
+                                lo_lds, hi_lds);
+    __syncthreads();
+    // S4
+    att::attend_item<T, D, att::kSelected, kStageBlocks, false, BTK_UNIT_NST>(
+        a.t, unit, 0, dyn, &flag, list, L, pages);
+}
+
+template <typename T, int D>
+hipError_t launch_unit(const Dims &d, const StepArgs &a, hipStream_t stream) {
+    const size_t r = d.group();
+    size_t n = r * D;                                                 // queries
+    const size_t wave_merge = (size_t)att::kWaves * r * D + 2 * att::kWaves * 16;
+    n = n > wave_merge ? n : wave_merge;
+    hipLaunchKernelGGL((decode_step_unit_kernel<T, D>), dim3((unsigned)a.units), dim3(kThreads),
+                       sizeof(float) * n, stream, a);
+    return hipGetLastError();
+}
+
+// CUs of the current device (cached per device), or 0 on error.
+int device_cus() {
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    int &c = cached[dev & 63];
+    if (c == 0 && hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        c = 0;
+    return c;
+}
+
+// The unit kernel serves problems whose units fill the device (at least one per
+// CU) and fit its limits; test_flags bit 1 / bit 2 force it on / off.
+bool use_unit_kernel(const Dims &d, const AttendPlan &ap, int top_k, uint32_t test_flags) {
+    const bool fits = d.max_blocks <= kRun && ap.nsplit_max == 1 && top_k <= 4 * kWave &&
+                      d.group() <= 8;
+    if (!fits || (test_flags & 4u)) return false;
+    if (test_flags & 2u) return true;
+    const int cus = device_cus();
+    return cus > 0 && (long)d.B * d.Hkv >= cus;
 }
 
 size_t step_lds_floats(const Dims &d, const AttendPlan &ap) {
@@ -755,6 +878,8 @@ hipError_t launch(const Dims &d, const SelectPlan &sp, const AttendPlan &ap, Ste
                   hipStream_t stream) {
     const size_t lds = sizeof(float) * step_lds_floats(d, ap);
     const bool splits = ap.nsplit_max > 1;
+    if (a.k.hdr && use_unit_kernel(d, ap, a.s.top_k, a.test_flags))
+        return launch_unit<T, D>(d, a, stream);
     if (a.k.hdr)
         return splits ? launch_instance<T, D, false, true, true>(lds, a, stream)
                       : launch_instance<T, D, false, false, true>(lds, a, stream);

@@ -122,10 +122,32 @@ def _check_counts(counts, bt, k):
     assert ((counts[~keep_all] >= kb[~keep_all]) & (counts[~keep_all] <= nb[~keep_all])).all()
 
 
-@pytest.mark.parametrize("label,spec", CASES, ids=[c[0] for c in CASES])
-def test_sketch_step_equals_step_and_oracle(label, spec):
+# Which kernel the sketched step runs (BTK_STEP_TEST_FLAGS, read at each call):
+# "auto" the library's choice (one workgroup per unit when the units fill the
+# device, else the persistent two-phase kernel), "unit" the one-workgroup-per-
+# unit kernel wherever its limits allow (small batches too; the Best-of-N and
+# 32B cases exceed them), "persistent" never (the batches where auto takes the
+# unit kernel).
+MODES = {"auto": "0", "unit": "2", "persistent": "4"}
+_UNIT_AUTO = {"config2", "config3", "batch-1024", "windows-3000-hkv1"}
+MODE_CASES = ([(lab, sp, "auto") for lab, sp in CASES]
+              + [(lab, sp, "unit") for lab, sp in CASES
+                 if sp.get("cfg") not in (4, 5) and lab not in _UNIT_AUTO]
+              + [(lab, sp, "persistent") for lab, sp in CASES if lab in _UNIT_AUTO])
+
+
+@pytest.fixture
+def kernel_mode(request, monkeypatch):
+    mode = getattr(request, "param", "auto")
+    monkeypatch.setenv("BTK_STEP_TEST_FLAGS", MODES[mode])
+    return mode
+
+
+@pytest.mark.parametrize("label,spec,kernel_mode", MODE_CASES,
+                         ids=[f"{c[0]}-{c[2]}" for c in MODE_CASES], indirect=["kernel_mode"])
+def test_sketch_step_equals_step_and_oracle(label, spec, kernel_mode):
     bt = _batch(label, spec)
-    _say(f"[sketch-step] {label}")
+    _say(f"[sketch-step] {label} ({kernel_mode})")
     d = bt.to(DEV)
     prob = btk.make_problem(d.q, d.k_cache, d.block_table)
     k = bt.top_k
@@ -166,8 +188,9 @@ def test_sketch_step_equals_step_and_oracle(label, spec):
          f"candidates mean {c.mean():.1f} max {int(c.max())}")
 
 
+@pytest.mark.parametrize("kernel_mode", ["auto", "unit"], indirect=True)
 @pytest.mark.parametrize("top_k", [32, 64, 100])
-def test_sketch_step_keeps_exact_ties(top_k):
+def test_sketch_step_keeps_exact_ties(top_k, kernel_mode):
     """Runs of exactly tied scores: every tied block stays a candidate and the
     lowest indices win, as in the full step."""
     bt = synth.make_tie_batch(seq_lens=[700, 2000, 4096, 333, 1500, 8000], top_k=top_k, seed=41)
@@ -185,8 +208,11 @@ def test_sketch_step_keeps_exact_ties(top_k):
                   sum_units=sum_factor(bt.group, bt.head_dim))
 
 
-@pytest.mark.parametrize("label,spec", [CASES[2], CASES[7]], ids=["config3", "config5-64k"])
-def test_sketch_step_with_a_sketch_never_built(label, spec):
+@pytest.mark.parametrize("label,spec,kernel_mode",
+                         [CASES[2] + ("auto",), CASES[2] + ("persistent",), CASES[7] + ("auto",)],
+                         ids=["config3", "config3-persistent", "config5-64k"],
+                         indirect=["kernel_mode"])
+def test_sketch_step_with_a_sketch_never_built(label, spec, kernel_mode):
     """An all-zero sketch names no page: every block is a candidate (units of up
     to 1024 blocks are scored exactly from LDS, longer ones by the full scan),
     with the same results."""
@@ -205,7 +231,8 @@ def test_sketch_step_with_a_sketch_never_built(label, spec):
     assert torch.equal(counts.cpu(), torch.where(nb <= k, torch.zeros_like(nb), nb).to(torch.int32))
 
 
-def test_sketch_step_flags_invalid_lengths_and_pages_like_the_step():
+@pytest.mark.parametrize("kernel_mode", ["auto", "unit"], indirect=True)
+def test_sketch_step_flags_invalid_lengths_and_pages_like_the_step(kernel_mode):
     bt = synth.make_batch(name="sketch-guards", batch=5, num_q_heads=8, num_kv_heads=2,
                           head_dim=128, seq_lens=[700, 40, 2500, 300, 900], top_k=8, seed=41)
     _say("[sketch-step] invalid lengths and pages")
@@ -231,7 +258,8 @@ def test_sketch_step_flags_invalid_lengths_and_pages_like_the_step():
     assert not (b["idx"][4] == 5).any()  # the bad page's block is never selected
 
 
-def test_sketch_step_three_decode_steps_on_one_sketch():
+@pytest.mark.parametrize("kernel_mode", ["auto", "unit"], indirect=True)
+def test_sketch_step_three_decode_steps_on_one_sketch(kernel_mode):
     """Three decode steps in a row, each appending a token: the sketch is built
     once before the first and then kept current only by the sketched step; every
     step's results equal the full step's on the same caches."""
