@@ -3,9 +3,13 @@
 A step is one decode step of the method over the whole batch, all on one HIP
 stream: S1 centroid update of the page holding each sequence's newest token,
 S2+S3 group scoring and top-k selection, S4 attention over the selected blocks.
-The timed step is the library's single-launch form (btk_decode_step); the same
-step as three calls (btk_centroid_update, btk_select, btk_sparse_attend) is
-timed beside it with a per-kernel breakdown.  The KV append itself is the
+The timed step is the library's single-launch form through the block sketches
+(btk_decode_step_sketch: every block's 8-bit sketch row bounds its score, only
+the blocks that could be selected are scored from their fp32 centroid rows;
+indices, outputs and centroids identical to btk_decode_step, checked on every
+replica).  Beside it: the single launch that scans every fp32 centroid row
+(btk_decode_step), and the same step as three calls (btk_centroid_update,
+btk_select, btk_sparse_attend) with a per-kernel breakdown.  The KV append itself is the
 caller's op and is not timed; lengths stay fixed so every step is the same
 work.  The workload is the Qwen3-8B-shaped decode layer (B=32, Hq=32, Hkv=8,
 D=128, bf16, ragged contexts U[4096, 32768], shuffled 16-token pages, top-k =
@@ -37,10 +41,11 @@ HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 METRIC = "sparse decode attention query-tokens/s + achieved HBM GB/s (% of peak), vs dense"
 WORKLOAD = ("qwen3-8b-shaped decode layer: B=32, Hq=32, Hkv=8 (group 4), D=128, bf16, "
             "contexts U[4096,32768], 16-token pages, shuffled block table, top_k=32 blocks")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_kernel_qwen3-8b_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_unit_kernel_qwen3-8b_traffic.json")
+PLAIN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_kernel_qwen3-8b_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "block_top_sparse_btk_amd", "csrc", f)
                   for f in ("step.hip", "select_dev.h", "attend_dev.h", "centroid_dev.h",
-                            "btk_internal.h")]
+                            "sketch_dev.h", "btk_internal.h")]
 
 
 # ---------------------------------------------------------------- byte model
@@ -142,11 +147,11 @@ def _sources_digest() -> str:
     return h.hexdigest()
 
 
-def _measured_traffic():
+def _measured_traffic(path=TRAFFIC_FILE):
     """HBM bytes per decode-step launch from the committed rocprofv3 counter
     runs, or None if the kernel source changed since they were taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -336,7 +341,9 @@ def measure_workload(name, bt, dev, steps, cpu_seconds, replicas=None, cpu_sampl
                      "unit": "query-tokens/s", "gbps": round(dgbps, 1),
                      "frac_of_peak": round(dgbps / HBM_PEAK_GBPS, 4), "bytes": nb["dense"],
                      "bytes_per_token": round(nb["dense"] / B, 1)},
-           "sketch_step": {"kernel": "decode_step_kernel (sketch instance)",
+           "sketch_step": {"kernel": ("decode_step_unit_kernel" if B * hkv >= torch.cuda.
+                                      get_device_properties(dev).multi_processor_count
+                                      else "decode_step_kernel (sketch instance)"),
                            "us": round(sk_us, 3), "us_batches": _pcts(sk_per),
                            "value": round(B / (sk_us * 1e-6), 1), "unit": "query-tokens/s",
                            "gbps": round(sk_gbps, 1),
@@ -345,6 +352,8 @@ def measure_workload(name, bt, dev, steps, cpu_seconds, replicas=None, cpu_sampl
                            "candidates_per_unit": round(float(cc.float().mean()), 1),
                            "speedup_vs_dense": round(dense_us / sk_us, 2)},
            "speedup_vs_dense": round(dense_us / step_us, 2),
+           "best_step_us": round(min(step_us, sk_us), 3),
+           "best_speedup_vs_dense": round(dense_us / min(step_us, sk_us), 2),
            "bytes_ratio": round(nb["dense"] / nb["step"], 2),
            "note": "times are HIP-event averages over back-to-back launches; us_batches: "
                    "percentiles of the averages of batches of 10 (step) / 5 (dense) launches"}
@@ -499,9 +508,11 @@ def main(argv=None):
         c = rep["calls"]
         check(f_cen(*c["cen"]) | f_sel(*c["sel"]) | f_att(*c["att"]))
 
+    # the step through the block sketches first warmed up; results must equal
+    # the fp32-scan step's bit for bit (checked on every replica below)
+    f_sk = lib.btk_decode_step_sketch
     for i in range(args.warmup):
-        check(f_step(*reps[i % len(reps)]["calls"]["step"]))
-        sep_step(reps[i % len(reps)])
+        check(f_sk(*reps[i % len(reps)]["calls"]["sk"]))
     torch.cuda.synchronize()
 
     # timed region: exactly K steps (one kernel each), bracketed by synchronize
@@ -513,38 +524,15 @@ def main(argv=None):
     t0 = time.perf_counter()
     ev0.record(stream)
     for i in range(args.steps):
-        check(f_step(*reps[i % len(reps)]["calls"]["step"]))
+        check(f_sk(*reps[i % len(reps)]["calls"]["sk"]))
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = 1e3 * wall / args.steps
-    step_us = 1e3 * ev0.elapsed_time(ev1) / args.steps
+    sk_us = 1e3 * ev0.elapsed_time(ev1) / args.steps
     # spread: the same launches in batches of 10, one event pair per batch
     bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(max(1, args.steps // 10))]
-    i = 0
-    for e0, e1 in bev:
-        e0.record(stream)
-        for _ in range(10):
-            check(f_step(*reps[i % len(reps)]["calls"]["step"]))
-            i += 1
-        e1.record(stream)
-    torch.cuda.synchronize()
-    step_batches = _pcts([1e3 * e0.elapsed_time(e1) / 10 for e0, e1 in bev])
-
-    # the same step through the block sketches (btk_decode_step_sketch): same
-    # launches, same event brackets; results must equal the step's bit for bit
-    f_sk = lib.btk_decode_step_sketch
-    for i in range(args.warmup):
-        check(f_sk(*reps[i % len(reps)]["calls"]["sk"]))
-    torch.cuda.synchronize()
-    sev0, sev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    sev0.record(stream)
-    for i in range(args.steps):
-        check(f_sk(*reps[i % len(reps)]["calls"]["sk"]))
-    sev1.record(stream)
-    torch.cuda.synchronize()
-    sk_us = 1e3 * sev0.elapsed_time(sev1) / args.steps
     i = 0
     for e0, e1 in bev:
         e0.record(stream)
@@ -554,6 +542,31 @@ def main(argv=None):
         e1.record(stream)
     torch.cuda.synchronize()
     sk_batches = _pcts([1e3 * e0.elapsed_time(e1) / 10 for e0, e1 in bev])
+
+    # the single launch that scans every fp32 centroid row (btk_decode_step):
+    # same launches, same event brackets
+    for i in range(args.warmup):
+        check(f_step(*reps[i % len(reps)]["calls"]["step"]))
+        sep_step(reps[i % len(reps)])
+    torch.cuda.synchronize()
+    sev0, sev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    sev0.record(stream)
+    for i in range(args.steps):
+        check(f_step(*reps[i % len(reps)]["calls"]["step"]))
+    sev1.record(stream)
+    torch.cuda.synchronize()
+    plain_ms = 1e3 * (time.perf_counter() - t0) / args.steps
+    step_us = 1e3 * sev0.elapsed_time(sev1) / args.steps
+    i = 0
+    for e0, e1 in bev:
+        e0.record(stream)
+        for _ in range(10):
+            check(f_step(*reps[i % len(reps)]["calls"]["step"]))
+            i += 1
+        e1.record(stream)
+    torch.cuda.synchronize()
+    step_batches = _pcts([1e3 * e0.elapsed_time(e1) / 10 for e0, e1 in bev])
 
     # the same step as three calls: whole-step time, then a per-kernel pass
     t0 = time.perf_counter()
@@ -583,10 +596,10 @@ def main(argv=None):
         side.wait_stream(stream)
         with torch.cuda.stream(side):
             for rep in reps:  # capture on a side stream; the call names it explicitly
-                c = tuple(x if x is not hs else side.cuda_stream for x in rep["calls"]["step"])
+                c = tuple(x if x is not hs else side.cuda_stream for x in rep["calls"]["sk"])
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=side):
-                    check(f_step(*c))
+                    check(f_sk(*c))
                 graphs.append(g)
         stream.wait_stream(side)
         for i in range(args.warmup):
@@ -797,28 +810,32 @@ def main(argv=None):
     # exact S4 bytes from the blocks actually selected (every replica selects the same)
     nbytes = algorithmic_bytes(bt.seq_lens.tolist(), hq, hkv, D, k, e,
                                sel_tokens=selected_tokens(reps[0]["idx"].cpu(), bt.seq_lens))
-    step_gbps = nbytes["step"] / (ms_per_step * 1e-3) / 1e9
-    launch_gbps = nbytes["step"] / (step_us * 1e-6) / 1e9
-    dense_gbps = nbytes["dense"] / (dense_ms * 1e-3) / 1e9
     value = B / (ms_per_step * 1e-3)
+    dense_gbps = nbytes["dense"] / (dense_ms * 1e-3) / 1e9
     sel_toks = selected_tokens(reps[0]["idx"].cpu(), bt.seq_lens)
     cc = reps[0]["cc"].cpu()
+    # the headline kernel's own algorithmic bytes: sketch rows, the candidates'
+    # fp32 centroid rows, the rest as the fp32-scan step
     sk_bytes = sketch_step_bytes(bt.seq_lens.tolist(), hq, hkv, D, k, e, cc.tolist(), sel_toks)
+    sk_step_gbps = sk_bytes / (ms_per_step * 1e-3) / 1e9
     sk_gbps = sk_bytes / (sk_us * 1e-6) / 1e9
-    sketch = {"kernel": "decode_step_kernel (sketch instance): btk_decode_step_sketch",
-              "avg_launch_us": round(sk_us, 3), "launch_us_batches": sk_batches,
-              "value": round(B / (sk_us * 1e-6), 1), "unit": "query-tokens/s",
-              "algorithmic_bytes_per_launch": sk_bytes, "achieved": round(sk_gbps, 1),
-              "frac": round(sk_gbps / HBM_PEAK_GBPS, 4),
-              "bytes_per_token": round(sk_bytes / B, 1),
-              "candidates_per_unit": {"mean": round(float(cc.float().mean()), 1),
-                                      "max": int(cc.max())},
-              "speedup_vs_step": round(step_us / sk_us, 3),
-              "speedup_vs_dense": round(1e3 * dense_ms / sk_us, 2),
-              "note": "the step reading 8-bit block sketches and only the candidates' fp32 "
-                      "centroid rows; indices and outputs identical to btk_decode_step (checked "
-                      "on every replica); bytes: sketch rows, candidate rows, the rest as the "
-                      "step"}
+    plain_gbps = nbytes["step"] / (step_us * 1e-6) / 1e9
+    fp32_scan = {"kernel": "decode_step_kernel (persistent, every fp32 centroid row scanned): "
+                           "btk_decode_step",
+                 "ms_per_step": round(plain_ms, 5), "value": round(B / (plain_ms * 1e-3), 1),
+                 "unit": "query-tokens/s", "avg_launch_us": round(step_us, 3),
+                 "launch_us_batches": step_batches,
+                 "algorithmic_bytes_per_launch": nbytes["step"],
+                 "achieved": round(plain_gbps, 1), "frac": round(plain_gbps / HBM_PEAK_GBPS, 4),
+                 "traffic": _measured_traffic(PLAIN_TRAFFIC_FILE),
+                 "bytes_per_token": round(nbytes["step"] / B, 1),
+                 "speedup_vs_dense": round(1e3 * dense_ms / step_us, 2),
+                 "method_bytes_rate_of_headline": {
+                     "gbps": round(nbytes["step"] / (sk_us * 1e-6) / 1e9, 1),
+                     "note": "the bytes this fp32-scan step must move, over the headline "
+                             "kernel's launch time: the rate at which the sketched kernel does "
+                             "the fp32-scan step's work (it reads fewer bytes, so this is not a "
+                             "bandwidth it sustains)"}}
     if app is not None:
         app_bytes = nbytes["step"] + 4 * B * hkv * D * e  # new K,V read and written
         app = {"ms_per_step": round(app[0], 5), "value": round(B / (app[0] * 1e-3), 1),
@@ -845,18 +862,22 @@ def main(argv=None):
                    "head_dim": D, "page_size": 16, "top_k": k, "seed": bt.seed,
                    "mean_context": round(float(bt.seq_lens.float().mean()), 1),
                    "replicas": args.replicas},
-        "step_gbps": round(step_gbps, 1),
-        "step_frac_of_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
-        "bytes_per_step": nbytes["step"],
-        "bytes_per_token": round(nbytes["step"] / B, 1),
+        "step_gbps": round(sk_step_gbps, 1),
+        "step_frac_of_peak": round(sk_step_gbps / HBM_PEAK_GBPS, 4),
+        "bytes_per_step": sk_bytes,
+        "bytes_per_token": round(sk_bytes / B, 1),
         "roofline": {"bound": "hbm",
-                     "kernel": "decode_step_kernel (S1 + S2 + S3 + S4 in one launch)",
-                     "achieved": round(launch_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(launch_gbps / HBM_PEAK_GBPS, 4),
+                     "kernel": "decode_step_unit_kernel (S1 + S2 + S3 + S4 in one launch, "
+                               "through the block sketches, one workgroup per unit)",
+                     "achieved": round(sk_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(sk_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": _measured_traffic(),
-                     "algorithmic_bytes_per_launch": nbytes["step"],
-                     "avg_launch_us": round(step_us, 3),
-                     "launch_us_batches": step_batches},
+                     "algorithmic_bytes_per_launch": sk_bytes,
+                     "avg_launch_us": round(sk_us, 3),
+                     "launch_us_batches": sk_batches,
+                     "candidates_per_unit": {"mean": round(float(cc.float().mean()), 1),
+                                             "max": int(cc.max())}},
+        "fp32_scan_step": fp32_scan,
         "three_calls": {"ms_per_step": round(sep_ms, 5),
                         "value": round(B / (sep_ms * 1e-3), 1),
                         "kernels_us": {kk: round(v, 2) for kk, v in kern.items()},
@@ -880,12 +901,11 @@ def main(argv=None):
                        "frac_of_peak": round(nbytes["token"] / (token_ms * 1e-3) / 1e9
                                              / HBM_PEAK_GBPS, 4),
                        "bytes_per_step": nbytes["token"]},
-        "sketch_step": sketch,
         "best_of_n": bon,
         "fused_append": app,
         "graph_replay": None if graph_ms is None else {
             "ms_per_step": round(graph_ms, 5), "value": round(B / (graph_ms * 1e-3), 1),
-            "step_gbps": round(nbytes["step"] / (graph_ms * 1e-3) / 1e9, 1)},
+            "step_gbps": round(sk_bytes / (graph_ms * 1e-3) / 1e9, 1)},
     }
     if args.workloads:
         # the other workloads (each a full line of its own numbers)

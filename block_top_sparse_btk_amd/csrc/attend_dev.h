@@ -216,10 +216,8 @@ enum ListMode : int { kSelected = 0, kAll = 1, kRecent = 2, kMasked = 3 };
 // lds_list[i - split * bps]) instead of a.indices; L_known >= 0, the sequence
 // length; lds_pages (or NULL), the sequence's block-table row in LDS.
 // SPLITS = false: the caller guarantees one split per unit (nsplit_max = 1), and
-// the split-merge code is left out of the instance.  kNst: pipeline stages in
-// flight (a stage's loads are issued again as soon as it is computed); the
-// blocks are computed in the same order, so the results do not depend on it.
-template <typename T, int D, int MODE, int kG, bool SPLITS = true, int kNst = 2>
+// the split-merge code is left out of the instance.
+template <typename T, int D, int MODE, int kG, bool SPLITS = true>
 __device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int split, float *smem,
                                             int *is_last_p, const int32_t *lds_list = nullptr,
                                             int L_known = -1,
@@ -364,37 +362,17 @@ __device__ __forceinline__ void attend_item(const AttendArgs &a, int unit, int s
     };
 
     if (cnt > 0) {
-        if constexpr (kNst == 2) {
-            Stage<F, kG> sa, sb;
-            issue(sa, 0);
-            for (int m0 = 0;;) {
-                issue(sb, m0 + kG);
-                compute(sa, m0);
-                m0 += kG;
-                if (m0 >= cnt) break;
-                issue(sa, m0 + kG);
-                compute(sb, m0);
-                m0 += kG;
-                if (m0 >= cnt) break;
-            }
-        } else {
-            // a ring of kNst stages: stage s holds blocks m0 .. m0 + kG - 1 and
-            // takes blocks m0 + kNst * kG .. once computed
-            Stage<F, kG> st[kNst];
-#pragma unroll
-            for (int s = 0; s < kNst; ++s) issue(st[s], s * kG);
-            bool more = true;
-            for (int m0 = 0; more;) {
-#pragma unroll
-                for (int s = 0; s < kNst; ++s) {
-                    if (more) {
-                        compute(st[s], m0);
-                        m0 += kG;
-                        more = m0 < cnt;
-                        if (more) issue(st[s], m0 + (kNst - 1) * kG);
-                    }
-                }
-            }
+        Stage<F, kG> sa, sb;
+        issue(sa, 0);
+        for (int m0 = 0;;) {
+            issue(sb, m0 + kG);
+            compute(sa, m0);
+            m0 += kG;
+            if (m0 >= cnt) break;
+            issue(sa, m0 + kG);
+            compute(sb, m0);
+            m0 += kG;
+            if (m0 >= cnt) break;
         }
     }
 

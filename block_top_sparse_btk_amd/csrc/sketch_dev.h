@@ -123,7 +123,10 @@ __device__ __forceinline__ void query_sums(const float *qs, float *out) {
 // sm.cand), total: one LDS word.  LDS: the ends are in this workgroup's LDS
 // (plain loads) instead of the workspace (agent-scope loads); every end is read
 // before the first barrier, so map may alias lo_src (KMAX <= 8).
-template <int KMAX, bool LDS = false>
+// MAXP: at most that many radix passes; tau is then a lower bound of the kb-th
+// largest lower end (the lower edge of its bin), which admits more candidates
+// but keeps every block that can be selected.
+template <int KMAX, bool LDS = false, int MAXP = sel::kTopkPasses>
 __device__ __forceinline__ int threshold_candidates_wg4(const float *lo_src, const float *hi_src, int nb, int kb,
                                         int32_t *map, int cap, sel::TopkSmem &sm,
                                         uint32_t *count, int *total) {
@@ -163,7 +166,7 @@ __device__ __forceinline__ int threshold_candidates_wg4(const float *lo_src, con
     uint32_t hi = max(max(red[kWaves], red[kWaves + 1]), max(red[kWaves + 2], red[kWaves + 3]));
     int need = kb;
 #pragma unroll 1
-    for (int p = 0; p < sel::kTopkPasses && lo < hi; ++p) {
+    for (int p = 0; p < MAXP && lo < hi; ++p) {
         uint32_t *hist = sm.hist + p * sel::kHistWords;
         const uint32_t span = hi - lo;
         const int shift = max(0, 24 - __builtin_clz(span));
@@ -181,6 +184,7 @@ __device__ __forceinline__ int threshold_candidates_wg4(const float *lo_src, con
         if (in_bin == (uint32_t)need && lo < hi) break;  // the bin is kept whole: tau = lo
     }
     // a bin kept whole: exactly kb keys are >= lo; else lo = hi = the kb-th key
+    // (or, after MAXP passes, lo <= the kb-th key)
     const uint32_t tau = lo;
 
     // the candidates, in block order: a count per (slot, wave), an exclusive
@@ -228,15 +232,15 @@ __device__ __forceinline__ int threshold_candidates_wg4(const float *lo_src, con
 
 // Dispatch on nb (at most 32 keys per thread: 8192 blocks; ends in LDS: at
 // most 2048 blocks), kb < nb.
-template <bool LDS = false>
+template <bool LDS = false, int MAXP = sel::kTopkPasses>
 __device__ __forceinline__ int threshold_candidates(const float *lo, const float *hi, int nb,
                                                     int kb, int32_t *map, int cap,
                                                     sel::TopkSmem &sm, uint32_t *count,
                                                     int *total) {
     if (nb <= 4 * kThreads)
-        return threshold_candidates_wg4<4, LDS>(lo, hi, nb, kb, map, cap, sm, count, total);
+        return threshold_candidates_wg4<4, LDS, MAXP>(lo, hi, nb, kb, map, cap, sm, count, total);
     if (LDS || nb <= 8 * kThreads)
-        return threshold_candidates_wg4<8, LDS>(lo, hi, nb, kb, map, cap, sm, count, total);
+        return threshold_candidates_wg4<8, LDS, MAXP>(lo, hi, nb, kb, map, cap, sm, count, total);
     if (nb <= 16 * kThreads)
         return threshold_candidates_wg4<16>(lo, hi, nb, kb, map, cap, sm, count, total);
     return threshold_candidates_wg4<32>(lo, hi, nb, kb, map, cap, sm, count, total);
@@ -379,14 +383,19 @@ __device__ __forceinline__ void select_ranked(const float *sc, int m, int top_k,
     keys[tid] = mine;  // candidates from m on hold 0
     __syncthreads();
     int beat = 0;
-    const int n4 = (m + 3) / 4;
-    for (int i4 = 0; i4 < n4; ++i4) {
-        const u32x4_t k4 = reinterpret_cast<const u32x4_t *>(keys)[i4];
+    // 32 keys (eight LDS reads in flight) at a time; keys past m hold 0 and
+    // never beat a candidate (their index is above every candidate's)
+    for (int c = 0; c < (m + 31) / 32; ++c) {
+        u32x4_t k4[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = 4 * i4 + e;
-            beat += (k4[e] > mine || (k4[e] == mine && i < tid)) ? 1 : 0;
-        }
+        for (int q = 0; q < 8; ++q) k4[q] = reinterpret_cast<const u32x4_t *>(keys)[8 * c + q];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 32 * c + 4 * q + e;
+                beat += (k4[q][e] > mine || (k4[q][e] == mine && i < tid)) ? 1 : 0;
+            }
     }
     const bool keep = tid < m && beat < kb;
     const uint64_t bal = __ballot(keep);
@@ -420,8 +429,9 @@ __device__ __forceinline__ void store_intervals(const SketchArgs &s, size_t urow
 // else from the block table.  qs: the scaled mean query (LDS).  Blocks j >= jk
 // take their score from known[j] instead (blocks whose centroid another
 // workgroup recomputed in the same launch: their fresh row may not be visible
-// here, the score stored beside it with an agent-scope store is).
-template <int D>
+// here, the score stored beside it with an agent-scope store is).  KNOWN_LDS:
+// known[j - jk] is in this workgroup's LDS (it recomputed them itself).
+template <int D, bool KNOWN_LDS = false>
 __device__ __forceinline__ void rescore(const sel::SelectArgs &a, int b, int g,
                                         const int32_t *map, int m, const int *pages,
                                         bool row_lds, const float *qs, float *sc,
@@ -456,7 +466,10 @@ __device__ __forceinline__ void rescore(const sel::SelectArgs &a, int b, int g,
                 a.cent + ((size_t)p * a.Hkv + g) * D + col * VPL);
 #pragma unroll
             for (int v = 0; v < VPL / 4; ++v) st.cv[u][v] = src[v];
-            st.kn[u] = load_relaxed(known + min(st.jj[u], jk));
+            if constexpr (KNOWN_LDS)
+                st.kn[u] = 0.f;  // read from LDS when the row is reduced
+            else
+                st.kn[u] = load_relaxed(known + min(st.jj[u], jk));
         }
     };
     auto reduce = [&](const Stage &st, int base) {
@@ -466,7 +479,9 @@ __device__ __forceinline__ void rescore(const sel::SelectArgs &a, int b, int g,
             const float s = sel::row16_sum(sel::row_partial<VPL>(qf, st.cv[u]));
             const bool ok = st.pg[u] >= 0 && st.pg[u] < a.num_pages;
             if (col == 0 && row < m) {
-                sc[row] = !ok ? -INFINITY : st.jj[u] >= jk ? st.kn[u] : s;
+                const float kn = KNOWN_LDS ? (st.jj[u] >= jk ? known[st.jj[u] - jk] : 0.f)
+                                           : st.kn[u];
+                sc[row] = !ok ? -INFINITY : st.jj[u] >= jk ? kn : s;
                 if (!ok) flag_error(a.err, kErrPage);
             }
         }

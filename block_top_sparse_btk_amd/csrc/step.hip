@@ -712,29 +712,87 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
 
 // With sketches, when the units fill the device: one workgroup per (sequence,
 // KV head) unit does the whole step for it, so no workgroup waits for another.
-// The unit's sketch rows are scanned into intervals held in LDS (the first
-// stage of rows is in flight while the queries are averaged and the touched
-// blocks refreshed), the threshold and the candidates come from those
-// intervals, the candidates are scored exactly from their fp32 rows, the k
-// best kept, and the unit attended with more blocks in flight.  One
-// workgroup per SIMD set (launch bounds 256 x 1): the registers hold deeper
-// pipelines than the two-per-CU persistent kernel can.  Limits (checked on the
-// host): at most kRun blocks per sequence, one attention split, top_k <= 256
-// and a group of at most 8 heads.  Results are those of the persistent form
-// (the same device functions in the same order per unit).
-// Attention stages in flight in the unit kernel (one block each, computed in
-// the order of the persistent kernel's two-stage pipeline, so the same bits).
-#ifndef BTK_UNIT_NST
-#define BTK_UNIT_NST 4
-#endif
+// The queries, the length, the block-table row, the touched block's page id
+// and keys are requested first; the unit's sketch rows are scanned into
+// intervals held in LDS (the mean query is formed while the first rows are in
+// flight); then the touched blocks are refreshed (S1: centroid, exact score
+// kept in LDS, sketch row), the threshold and the candidates taken from the
+// intervals in LDS, the candidates scored exactly from their fp32 rows, the k
+// best kept, and the unit attended.  Launch bounds 256 x 1: the kernel may use
+// more registers than the persistent one (two workgroups per CU still fit at
+// D = 128 bf16).  Limits (checked on the host): at
+// most kRun blocks per sequence, one attention split, top_k <= 256 and a
+// group of at most 8 heads.  Results are those of the persistent form (the
+// same arithmetic per unit, blocks in the same order).
+// Sketch-row header loads per lane per scan stage: 1, two stages of 256 rows in
+// flight per workgroup.  With every CU scanning at once the memory system is
+// saturated, and more requests in flight only lengthen each one: 2 (512-row
+// stages) took the Qwen3-8B-shaped step from 37.8 to 41.1 us.  Likewise the
+// attention keeps the two one-block stages per wave of the persistent kernel
+// (four or six stages: 11.8 / 13.0 instead of 10.0 us per unit).
 #ifndef BTK_UNIT_HK
-#define BTK_UNIT_HK 2
+#define BTK_UNIT_HK 1
 #endif
+// Radix passes of the threshold: any lower bound of the k-th largest lower end
+// keeps every block that can be selected, so the search may stop at the
+// threshold bin's lower edge.  After two passes the candidates are those of the
+// exact threshold (50 mean, 69 at most on the Qwen3-8B-shaped layer); after one
+// they were 63 / 242 and the longer rescore and rank cost more than the pass.
+#ifndef BTK_UNIT_TPASSES
+#define BTK_UNIT_TPASSES 2
+#endif
+
+// The unit kernel's S1: waves 1-3 refresh the touched blocks jt + w - 1,
+// jt + w + 2, ... below j1 (centroid from the keys, stored; exact score as the
+// full scan computes it, into kex[j - jt] in LDS; sketch row rebuilt).  kt
+// holds the keys of the wave's first touched block (page pw), requested before
+// the scan.
+template <typename T, int D>
+__device__ __forceinline__ void unit_refresh(const StepArgs &a, int unit, int b, int L, int j1,
+                                             int jt, int pw, KeyTile<T, D> &kt,
+                                             const float *qs, float *crow, float *kex) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int g = unit % a.s.Hkv;
+    const int32_t *bt_row = a.s.bt + (size_t)b * a.s.max_blocks;
+    const T *keys = static_cast<const T *>(a.s.k_cache) + (size_t)g * kPage * D;
+    const size_t page_stride = (size_t)a.s.Hkv * kPage * D;
+    constexpr int kRefWaves = kWaves - 1, E = D / kWave, VPL = D / 16;
+    const int jw = wave == 0 ? j1 : jt + wave - 1;
+    float qf[VPL];
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) qf[e] = qs[(lane % 16) * VPL + e];
+    const size_t urow = (size_t)unit * a.s.max_blocks;
+    for (int j = jw; j < j1; j += kRefWaves) {
+        const int page = j == jw ? pw : bt_row[j];
+        if (page < 0 || page >= a.s.num_pages) {  // scored (and flagged) as -inf
+            if (lane == 0) kex[j - jt] = -INFINITY;
+            continue;
+        }
+        const int v = min(kPage, L - j * kPage);
+        float *row_lds = crow + wave * D;
+        if (j != jw) kt.load(keys + (size_t)page * page_stride, v, lane);
+        kt.mean_to(v, a.s.cent_out + ((size_t)page * a.s.Hkv + g) * D, row_lds, true, lane);
+        __builtin_amdgcn_wave_barrier();
+        floatx4_t cv[VPL / 4];
+#pragma unroll
+        for (int vv = 0; vv < VPL / 4; ++vv)
+            cv[vv] = reinterpret_cast<const floatx4_t *>(row_lds + (lane % 16) * VPL)[vv];
+        const float sc = sel::row16_sum(sel::row_partial<VPL>(qf, cv));
+        if (lane == 0) kex[j - jt] = sc;
+        float x[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[e] = row_lds[lane * E + e];
+        skt::encode_row<D>(x, page, urow + j, a.k.hdr, a.k.codes, lane);
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 1) void decode_step_unit_kernel(StepArgs a) {
     __shared__ float qs[D];
     __shared__ int pages[kRun];
     __shared__ float lo_lds[kRun], hi_lds[kRun];  // interval ends; then candidates (cmap, cex)
+    __shared__ float kex[kRun];                    // exact scores of the touched blocks
     __shared__ int flag;
     __shared__ uint32_t hist[sel::kTopkPasses * sel::kHistWords], cand[4 * kWave];
     __shared__ uint32_t red[2 * kWaves];
@@ -746,9 +804,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_unit_kernel(StepArgs 
     extern __shared__ float dyn[];  // queries, then the attention's wave merge
     sel::ScoreSmem sm{dyn, qs, pages, lo_lds, &flag, nullptr};
     sel::TopkSmem tk{hist, cand, red, scan_red, reinterpret_cast<uint32_t *>(dyn)};
-    const int tid = threadIdx.x, Hkv = a.s.Hkv;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave, Hkv = a.s.Hkv;
     const int unit = (int)blockIdx.x, b = unit / Hkv, g = unit % Hkv;
+    const int r = a.s.Hq / Hkv;
+    // the queries, the length and the decode position, requested together
+    const T *qp = static_cast<const T *>(a.s.q) + ((size_t)b * a.s.Hq + (size_t)g * r) * D;
+    float qv[step_qn(D)];
+#pragma unroll
+    for (int k = 0; k < step_qn(D); ++k)
+        qv[k] = sel::load_q<T>(qp + min(k * kThreads + tid, r * D - 1));
     const int L = valid_len(a.s.seq_lens[b], a.s.max_blocks);
+    const int fp = touched_pos<false>(a, b, L);
     if (L < 0) {  // -1 indices, the error flagged; no output (as the persistent form)
         for (int i = tid; i < a.s.top_k; i += kThreads)
             a.s.indices[(size_t)unit * a.s.top_k + i] = -1;
@@ -759,50 +825,86 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_unit_kernel(StepArgs 
         return;
     }
     const int nb = (L + kPage - 1) / kPage;
-    const int fp = touched_pos<false>(a, b, L);
-    const int jt = a.s.first_pos && fp >= 0 && fp < L ? fp / kPage : nb;
-    const int r = a.s.Hq / Hkv;
-    // the queries and the block-table row, requested first
-    const T *qp = static_cast<const T *>(a.s.q) + ((size_t)b * a.s.Hq + (size_t)g * r) * D;
-    float qv[step_qn(D)];
-#pragma unroll
-    for (int k = 0; k < step_qn(D); ++k)
-        qv[k] = sel::load_q<T>(qp + min(k * kThreads + tid, r * D - 1));
+    const int jt = a.s.first_pos && fp >= 0 && fp < L ? fp / kPage : nb;  // first touched block
+    // the block-table row and the page id of this wave's first touched block
+    const int32_t *bt_row = a.s.bt + (size_t)b * a.s.max_blocks;
+    const int jw = wave == 0 ? nb : jt + wave - 1;
+    const int pw = jw < nb ? bt_row[jw] : -1;
     int32_t prow[kRowPer];
-    {
-        const int32_t *bt_row = a.s.bt + (size_t)b * a.s.max_blocks;
 #pragma unroll
-        for (int i = 0; i < kRowPer; ++i) prow[i] = bt_row[min(i * kThreads + tid, nb - 1)];
-    }
-    // S2 (sketch): every block's interval into LDS; the touched blocks j >= jt
-    // are refreshed (S1) while the first rows are in flight, and are candidates
-    skt::scan_sketch<D, BTK_UNIT_HK>(a.s, a.k, b, g, 0, nb, sm.qs, qsum, jt, lo_lds, hi_lds,
-                                     [&] {
-                                         sketch_item_setup<T, D, false>(a, unit, b, L, nb, jt, qv,
-                                                                         true, prow, sm, crow, 0u);
-                                         skt::query_sums<D>(sm.qs, qsum);
-                                         __syncthreads();
-                                     });
+    for (int i = 0; i < kRowPer; ++i) prow[i] = bt_row[min(i * kThreads + tid, nb - 1)];
+    // S2 (sketch): every block's interval into LDS (the touched blocks j >= jt:
+    // always candidates); the mean query is formed and the touched keys are
+    // requested while the first rows are in flight
+    KeyTile<T, D> kt;
+    skt::scan_sketch<D, BTK_UNIT_HK>(a.s, a.k, b, g, 0, nb, sm.qs, qsum, jt, lo_lds, hi_lds, [&] {
+#pragma unroll
+        for (int k = 0; k < step_qn(D); ++k)
+            if (k * kThreads + tid < r * D) sm.qraw[k * kThreads + tid] = qv[k];
+#pragma unroll
+        for (int i = 0; i < kRowPer; ++i)
+            if (i * kThreads + tid < nb) pages[i * kThreads + tid] = prow[i];
+        if (pw >= 0 && pw < a.s.num_pages)
+            kt.load(static_cast<const T *>(a.s.k_cache) +
+                        ((size_t)pw * Hkv + g) * kPage * D,
+                    min(kPage, L - jw * kPage), lane);
+        __syncthreads();
+        sel::mean_query<D>(a.s, sm);
+        __syncthreads();
+        skt::query_sums<D>(sm.qs, qsum);
+        __syncthreads();
+    });
+    // S1 for the touched blocks, then S3
+    unit_refresh<T, D>(a, unit, b, L, nb, jt, pw, kt, sm.qs, crow, kex);
     __syncthreads();
-    // S3: threshold, candidates scored exactly, the k best (cmap, cex alias the ends)
-    select_sketched<T, D, true>(a, unit, 0, b, L, nb, fp, jt, 0, a.s.top_k, true, sm, tk, list,
-                                reinterpret_cast<int32_t *>(lo_lds), hi_lds, &ctot, crow,
-                                lo_lds, hi_lds);
+    int32_t *idx = a.s.indices + (size_t)unit * a.s.top_k;
+    const int kb = min(a.s.top_k, nb);
+    int32_t *cmap = reinterpret_cast<int32_t *>(lo_lds);  // (the ends are read first)
+    float *cex = hi_lds;
+    int m = 0;  // candidates, scored exactly
+    __builtin_amdgcn_s_setprio(3);
+    if (kb == nb) {  // every block is kept (no score is read)
+        sel::select_topk(skt::LdsScores{hi_lds}, nb, a.s.top_k, sel::TopkOut{idx, list, 0, a.s.top_k},
+                         tk);
+    } else {
+        m = skt::threshold_candidates<true, BTK_UNIT_TPASSES>(lo_lds, hi_lds, nb, kb, cmap,
+                                                              kStepCand, tk, tk.cand, &ctot);
+        if (m <= kStepCand) {
+            skt::rescore<D, true>(a.s, b, g, cmap, m, pages, true, sm.qs, cex, kex, jt);
+            __syncthreads();
+        }
+        sel::TopkOut o{idx, list, 0, a.s.top_k};
+        o.map = cmap;
+        o.mapped = true;
+        if (m <= kThreads)
+            skt::select_ranked(cex, m, a.s.top_k, o, tk.cand, tk.red);
+        else if (m <= kStepCand)
+            sel::select_topk(skt::LdsScores{cex}, m, a.s.top_k, o, tk);
+        else {  // every block, with the full scan's code (the touched blocks again)
+            sel::SelectArgs ax = a.s;
+            ax.scores = a.k.exact;
+            const size_t urow = (size_t)unit * a.s.max_blocks;
+            __syncthreads();  // pages and lo_lds are free
+            for (int i = tid; i < nb; i += kThreads) pages[i] = bt_row[i];
+            __syncthreads();
+            sel::check_pages(a.s, sm, nb);
+            __syncthreads();
+            sel::scan_rows<T, D, kScanRows, true>(ax, b, g, 0, nb, L, fp, sm, crow);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the scores are stored
+            __syncthreads();
+            sel::select_topk(sel::PlainScores{a.k.exact + urow}, nb, a.s.top_k,
+                             sel::TopkOut{idx, list, 0, a.s.top_k}, tk);
+            m = nb;
+            __syncthreads();
+            for (int i = tid; i < nb; i += kThreads) pages[i] = bt_row[i];  // for the attention
+        }
+    }
+    __builtin_amdgcn_s_setprio(0);
+    if (tid == 0 && a.cand_counts) a.cand_counts[unit] = m;
     __syncthreads();
     // S4
-    att::attend_item<T, D, att::kSelected, kStageBlocks, false, BTK_UNIT_NST>(
-        a.t, unit, 0, dyn, &flag, list, L, pages);
-}
-
-template <typename T, int D>
-hipError_t launch_unit(const Dims &d, const StepArgs &a, hipStream_t stream) {
-    const size_t r = d.group();
-    size_t n = r * D;                                                 // queries
-    const size_t wave_merge = (size_t)att::kWaves * r * D + 2 * att::kWaves * 16;
-    n = n > wave_merge ? n : wave_merge;
-    hipLaunchKernelGGL((decode_step_unit_kernel<T, D>), dim3((unsigned)a.units), dim3(kThreads),
-                       sizeof(float) * n, stream, a);
-    return hipGetLastError();
+    att::attend_item<T, D, att::kSelected, kStageBlocks, false>(a.t, unit, 0, dyn, &flag, list,
+                                                                L, pages);
 }
 
 // CUs of the current device (cached per device), or 0 on error.
@@ -814,6 +916,17 @@ int device_cus() {
     if (c == 0 && hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         c = 0;
     return c;
+}
+
+template <typename T, int D>
+hipError_t launch_unit(const Dims &d, const StepArgs &a, hipStream_t stream) {
+    const size_t r = d.group();
+    size_t n = r * D;                                                 // queries
+    const size_t wave_merge = (size_t)att::kWaves * r * D + 2 * att::kWaves * 16;
+    n = n > wave_merge ? n : wave_merge;
+    hipLaunchKernelGGL((decode_step_unit_kernel<T, D>), dim3((unsigned)a.units), dim3(kThreads),
+                       sizeof(float) * n, stream, a);
+    return hipGetLastError();
 }
 
 // The unit kernel serves problems whose units fill the device (at least one per

@@ -321,6 +321,11 @@ btk_status_t btk_decode_step(const btk_problem_t *problem, const void *q, const 
  * blocks whose upper end reaches it from their fp32 centroid rows exactly as
  * btk_select scores them, keeps the k_b best with btk_select's tie rule and
  * attends.  A unit with more than 1024 such candidates scores every block.
+ * When there are at least as many units as compute units and the problem fits
+ * one workgroup per unit (max_blocks_per_seq <= 2048, top_k <= 256, at most 8
+ * query heads per KV head, one attention split), each unit is done whole by one
+ * workgroup and no workgroup waits for another; otherwise the step runs in the
+ * persistent form of btk_decode_step.  The results do not depend on which.
  * The sketch must hold rows for the blocks before first_pos built from their
  * current centroids (btk_sketch_update after prefill; every call keeps the
  * rows of the blocks it touches current); a row that does not name its block's
