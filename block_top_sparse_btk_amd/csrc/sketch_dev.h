@@ -372,29 +372,32 @@ __device__ __forceinline__ void scan_sketch(const sel::SelectArgs &a, const Sket
 // is larger or equal with a lower index (equal scores go to the lower block;
 // -0.0 equals +0.0).  This is the rule of sel::select_topk, so the same blocks
 // are kept; they are written in ascending order through out (which maps
-// candidate numbers to blocks), then -1 up to top_k.  keys: 256 LDS words
-// (may alias sm.cand), wcount: kWaves LDS words (may alias sm.red).
+// candidate numbers to blocks), then -1 up to top_k.  Each candidate's rank
+// key is 64 bits, its score key above the complement of its number, so that
+// "beats" is one unsigned comparison.  keys: 512 LDS words, 16-byte aligned
+// (may alias sm.hist), wcount: kWaves LDS words (may alias sm.red).
 __device__ __forceinline__ void select_ranked(const float *sc, int m, int top_k,
                                               const sel::TopkOut &out, uint32_t *keys,
                                               uint32_t *wcount) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int kb = min(top_k, m);
-    const uint32_t mine = tid < m ? score_key(sc[tid]) : 0u;
-    keys[tid] = mine;  // candidates from m on hold 0
+    const uint64_t mine =
+        tid < m ? ((uint64_t)score_key(sc[tid]) << 32) | (uint64_t)(~(uint32_t)tid) : 0ull;
+    reinterpret_cast<uint64_t *>(keys)[tid] = mine;  // candidates from m on hold 0
     __syncthreads();
     int beat = 0;
-    // 32 keys (eight LDS reads in flight) at a time; keys past m hold 0 and
-    // never beat a candidate (their index is above every candidate's)
+    // 32 keys (sixteen LDS reads in flight) at a time; keys past m hold 0 and
+    // beat no candidate
     for (int c = 0; c < (m + 31) / 32; ++c) {
-        u32x4_t k4[8];
+        u32x4_t k4[16];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) k4[q] = reinterpret_cast<const u32x4_t *>(keys)[8 * c + q];
+        for (int q = 0; q < 16; ++q) k4[q] = reinterpret_cast<const u32x4_t *>(keys)[16 * c + q];
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
+        for (int q = 0; q < 16; ++q)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 32 * c + 4 * q + e;
-                beat += (k4[q][e] > mine || (k4[q][e] == mine && i < tid)) ? 1 : 0;
+            for (int e = 0; e < 2; ++e) {
+                const uint64_t k = ((uint64_t)k4[q][2 * e + 1] << 32) | k4[q][2 * e];
+                beat += k > mine ? 1 : 0;
             }
     }
     const bool keep = tid < m && beat < kb;

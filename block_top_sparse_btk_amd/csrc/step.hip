@@ -390,7 +390,7 @@ __device__ __forceinline__ void select_sketched(const StepArgs &a, int unit, int
             o.map = cmap;
             o.mapped = true;
             if (m <= kThreads)
-                skt::select_ranked(cex, m, a.s.top_k, o, tk.cand, tk.red);
+                skt::select_ranked(cex, m, a.s.top_k, o, tk.hist, tk.red);
             else
                 sel::select_topk(skt::LdsScores{cex}, m, a.s.top_k, o, tk);
             mc = m;
@@ -433,10 +433,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
     __shared__ int pages[kRun];
     __shared__ float sc_lds[kRun];
     __shared__ int flag;
-    __shared__ uint32_t hist[sel::kTopkPasses * sel::kHistWords], cand[4 * kWave];
+    // read as 16-byte vectors (histogram bins, candidate keys): 16-byte aligned
+    __shared__ __align__(16) uint32_t hist[sel::kTopkPasses * sel::kHistWords];
+    __shared__ __align__(16) uint32_t cand[4 * kWave];
     __shared__ uint32_t red[2 * kWaves];
     __shared__ int scan_red[kWaves];
-    __shared__ float crow[kWaves * D];
+    __shared__ __align__(16) float crow[kWaves * D];
     __shared__ __align__(16) uint32_t newtok[APPEND ? D * sizeof(T) / 4 : 4];  // new key
     // the row prefix of one window of kWin sequences, [base, base + wlen)
     __shared__ uint32_t rows[kWin + 1];  // centroid rows before each sequence, then the window end
@@ -794,10 +796,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_unit_kernel(StepArgs 
     __shared__ float lo_lds[kRun], hi_lds[kRun];  // interval ends; then candidates (cmap, cex)
     __shared__ float kex[kRun];                    // exact scores of the touched blocks
     __shared__ int flag;
-    __shared__ uint32_t hist[sel::kTopkPasses * sel::kHistWords], cand[4 * kWave];
+    // read as 16-byte vectors (histogram bins, candidate keys): 16-byte aligned
+    __shared__ __align__(16) uint32_t hist[sel::kTopkPasses * sel::kHistWords];
+    __shared__ __align__(16) uint32_t cand[4 * kWave];
     __shared__ uint32_t red[2 * kWaves];
     __shared__ int scan_red[kWaves];
-    __shared__ float crow[kWaves * D];
+    __shared__ __align__(16) float crow[kWaves * D];
     __shared__ int32_t list[4 * kWave];  // the selection (top_k <= 256)
     __shared__ float qsum[2];
     __shared__ int ctot;
@@ -877,7 +881,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_unit_kernel(StepArgs 
         o.map = cmap;
         o.mapped = true;
         if (m <= kThreads)
-            skt::select_ranked(cex, m, a.s.top_k, o, tk.cand, tk.red);
+            skt::select_ranked(cex, m, a.s.top_k, o, tk.hist, tk.red);
         else if (m <= kStepCand)
             sel::select_topk(skt::LdsScores{cex}, m, a.s.top_k, o, tk);
         else {  // every block, with the full scan's code (the touched blocks again)
