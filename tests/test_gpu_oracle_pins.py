@@ -144,9 +144,10 @@ SCALE_CASES = [
 
 
 @pytest.mark.parametrize("label,spec", SCALE_CASES, ids=[c[0] for c in SCALE_CASES])
-def test_explicit_sm_scale_against_oracle(label, spec):
+def test_explicit_sm_scale_against_oracle(label, spec, monkeypatch):
     """sm_scale > 0 scales the block scores and the attention logits of select,
-    sparse/dense/local attention and both single-launch steps."""
+    sparse/dense/local attention and the single-launch steps (the step through
+    the sketches in both of its kernels must equal the step bit for bit)."""
     s = spec["scale"]
     if "cfg" in spec:
         bt = synth.make_config(spec["cfg"], batch=spec.get("batch"))
@@ -197,9 +198,29 @@ def test_explicit_sm_scale_against_oracle(label, spec):
     alse = torch.empty_like(lse)
     aout, aidx = btk.btk_decode_step_append(d.q, kn, vn, kc, vc, d.block_table, d.seq_lens, c3, k,
                                             ws3, lse=alse, problem=prob)
+    # the step through the block sketches, built from the stale centroids, in the
+    # library's choice of kernel and in the one-workgroup-per-unit kernel
+    sk_runs = []
+    for flags in ("0", "2"):
+        monkeypatch.setenv("BTK_STEP_TEST_FLAGS", flags)
+        sk = btk.new_sketch(prob, DEV)
+        wsk = btk.new_workspace(prob, k, DEV)
+        c4 = stale.to(DEV)
+        btk.btk_sketch_update(c4, d.block_table, d.seq_lens, sk, wsk, problem=prob)
+        klse = torch.empty_like(lse)
+        kout, kidx = btk.btk_decode_step_sketch(d.q, d.k_cache, d.v_cache, d.block_table,
+                                                d.seq_lens, c4, sk, k, wsk,
+                                                first_pos=first.to(DEV), lse=klse, problem=prob)
+        torch.cuda.synchronize()
+        sk_runs.append((wsk, c4, kidx, kout, klse))
+    monkeypatch.delenv("BTK_STEP_TEST_FLAGS")
     torch.cuda.synchronize()
     for w in (ws, ws2, ws3):
         assert btk.workspace_error_bits(w) == 0
+    for wsk, c4, kidx, kout, klse in sk_runs:
+        assert btk.workspace_error_bits(wsk) == 0
+        assert torch.equal(kidx, sidx) and torch.equal(kout, sout) and torch.equal(klse, slse)
+        assert torch.equal(c4, c2)
     s_err = 0.0
     for b, nb in enumerate(n_blocks(bt.seq_lens)):
         s_err = max(s_err, max_abs(sc[b, :, :nb].cpu(), ora["scores"][b, :, :nb]))
