@@ -110,7 +110,7 @@ def algorithmic_bytes(seq_lens, num_q_heads, num_kv_heads, head_dim, top_k, elem
 
 
 def sketch_step_bytes(seq_lens, num_q_heads, num_kv_heads, head_dim, top_k, elem_bytes,
-                      cand_counts, sel_tokens, page=16):
+                      cand_counts, sel_tokens, page=16, fp32_scan=False):
     """Bytes the step through the block sketch must move (btk_decode_step_sketch).
 
     Per unit, as the full step (algorithmic_bytes) except the centroid scan:
@@ -121,7 +121,9 @@ def sketch_step_bytes(seq_lens, num_q_heads, num_kv_heads, head_dim, top_k, elem
               k indices (4*k); the sequence's block table (4*n_b) once per sequence
       S4:     as in the full step
     cand_counts[b][g] = m (0 when every block is kept), sel_tokens as for
-    algorithmic_bytes.
+    algorithmic_bytes. fp32_scan: the launch took the persistent fp32-scan kernel (too
+    few units to fill the device), which reads every block's fp32 row (4*D*n_b) and no
+    sketch row, and writes the refreshed block's sketch row as above.
     """
     r, D, e, P = num_q_heads // num_kv_heads, head_dim, elem_bytes, page
     total = 0
@@ -132,12 +134,25 @@ def sketch_step_bytes(seq_lens, num_q_heads, num_kv_heads, head_dim, top_k, elem
         for g in range(num_kv_heads):
             m = int(cand_counts[b][g])
             total += v_last * D * e + 4 * D + D + 8
-            total += r * D * e + nb * (D + 8) + 4 * D * m + 4 * top_k
+            if fp32_scan:
+                total += r * D * e + 4 * D * nb + 4 * top_k
+            else:
+                total += r * D * e + nb * (D + 8) + 4 * D * m + 4 * top_k
             total += 8 * top_k + 2 * r * D * e + 2 * sel_tokens[b][g] * D * e
     return total
 
 
 # ---------------------------------------------------------------- helpers
+
+def _sketch_takes_unit_kernel(B, hkv, max_blocks, dev) -> bool:
+    """Which kernel btk_decode_step_sketch launches for these workloads: one workgroup per
+    (sequence, KV head) unit when the units fill the device (at least one per compute unit)
+    and the table fits its block limit (3072), else the persistent fp32-scan kernel. Its other
+    limits (top-k <= 256, group <= 8, one attention split) hold for every workload here."""
+    import torch
+    return (B * hkv >= torch.cuda.get_device_properties(dev).multi_processor_count
+            and max_blocks <= 3072)
+
 
 def _sources_digest() -> str:
     h = hashlib.sha256()
@@ -322,7 +337,9 @@ def measure_workload(name, bt, dev, steps, cpu_seconds, replicas=None, cpu_sampl
     sel_toks = selected_tokens(reps[0]["idx"].cpu(), bt.seq_lens.cpu())
     nb = algorithmic_bytes(bt.seq_lens.tolist(), hq, hkv, D, k, e, sel_tokens=sel_toks)
     cc = reps[0]["cc"].cpu()
-    sk_bytes = sketch_step_bytes(bt.seq_lens.tolist(), hq, hkv, D, k, e, cc.tolist(), sel_toks)
+    unit = _sketch_takes_unit_kernel(B, hkv, bt.block_table.shape[1], dev)
+    sk_bytes = sketch_step_bytes(bt.seq_lens.tolist(), hq, hkv, D, k, e, cc.tolist(), sel_toks,
+                                 fp32_scan=not unit)
     sk_gbps = sk_bytes / (sk_us * 1e-6) / 1e9
     gbps = nb["step"] / (step_us * 1e-6) / 1e9
     dgbps = nb["dense"] / (dense_us * 1e-6) / 1e9
@@ -341,9 +358,9 @@ def measure_workload(name, bt, dev, steps, cpu_seconds, replicas=None, cpu_sampl
                      "unit": "query-tokens/s", "gbps": round(dgbps, 1),
                      "frac_of_peak": round(dgbps / HBM_PEAK_GBPS, 4), "bytes": nb["dense"],
                      "bytes_per_token": round(nb["dense"] / B, 1)},
-           "sketch_step": {"kernel": ("decode_step_unit_kernel" if B * hkv >= torch.cuda.
-                                      get_device_properties(dev).multi_processor_count
-                                      else "decode_step_kernel (sketch instance)"),
+           "sketch_step": {"kernel": ("decode_step_unit_kernel" if unit
+                                      else "decode_step_kernel (fp32 scan, sketch rows kept "
+                                           "current)"),
                            "us": round(sk_us, 3), "us_batches": _pcts(sk_per),
                            "value": round(B / (sk_us * 1e-6), 1), "unit": "query-tokens/s",
                            "gbps": round(sk_gbps, 1),
@@ -816,6 +833,9 @@ def main(argv=None):
     cc = reps[0]["cc"].cpu()
     # the headline kernel's own algorithmic bytes: sketch rows, the candidates'
     # fp32 centroid rows, the rest as the fp32-scan step
+    if not _sketch_takes_unit_kernel(B, hkv, bt.block_table.shape[1], dev):
+        raise RuntimeError("the headline layer's units do not fill this device: the roofline "
+                           "below is for decode_step_unit_kernel")
     sk_bytes = sketch_step_bytes(bt.seq_lens.tolist(), hq, hkv, D, k, e, cc.tolist(), sel_toks)
     sk_step_gbps = sk_bytes / (ms_per_step * 1e-3) / 1e9
     sk_gbps = sk_bytes / (sk_us * 1e-6) / 1e9

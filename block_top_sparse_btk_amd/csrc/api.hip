@@ -423,7 +423,7 @@ static btk_status_t decode_step(const btk_problem_t *problem, const void *q, con
         return BTK_ERR_NULL;
     if (append && (!k_new || !v_new)) return BTK_ERR_NULL;
     if (!top_k_ok(top_k)) return BTK_ERR_SHAPE;
-    if (d.B > btk::kMaxStepBatch || !btk::step_rows_fit(d, sketch != nullptr))
+    if (d.B > btk::kMaxStepBatch || !btk::step_rows_fit(d))
         return BTK_ERR_UNSUPPORTED;
     if (sketch && sketch_bytes < btk::sketch_bytes(d)) return BTK_ERR_WORKSPACE;
     // a caller's workspace has the size btk_workspace_bytes promises; the
@@ -434,10 +434,7 @@ static btk_status_t decode_step(const btk_problem_t *problem, const void *q, con
     char *scratch = ws + w.scratch_at(workspace_bytes);
     uint32_t *state = reinterpret_cast<uint32_t *>(ws + w.state);
     const btk::SelectPlan sp = btk::plan_select(d);
-#ifndef BTK_STEP_SKETCH_ITEMS
-#define BTK_STEP_SKETCH_ITEMS 256
-#endif
-    const btk::AttendPlan ap = btk::plan_attend(d, top_k, false, sketch ? BTK_STEP_SKETCH_ITEMS : 256);
+    const btk::AttendPlan ap = btk::plan_attend(d, top_k, false);
     return hip_status(btk::launch_decode_step(
         d, sp, ap, q, k_cache, v_cache, block_table, seq_lens, first_pos, centroids, top_k,
         indices, reinterpret_cast<float *>(scratch + w.scores), out, lse,

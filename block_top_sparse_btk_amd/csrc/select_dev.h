@@ -22,6 +22,16 @@
 #include "centroid_dev.h"
 
 namespace btk {
+namespace skt {
+// A block sketch row's header (the layout and the rows are described with the
+// sketch code, sketch_dev.h): the page the row was built from + 1 (0: none) and
+// the scale of its codes.
+struct SketchHdr {
+    int32_t page1;
+    float scale;
+};
+}  // namespace skt
+
 namespace sel {
 
 constexpr int kThreads = 256;
@@ -54,6 +64,10 @@ struct SelectArgs {
     // slot, position L - 1) and the caches they are written to
     const void *k_new = nullptr, *v_new = nullptr;
     void *k_out = nullptr, *v_out = nullptr;
+    // decode step keeping block sketches current (NULL otherwise): the touched
+    // blocks' sketch rows are rebuilt from their recomputed centroids
+    skt::SketchHdr *sk_hdr = nullptr;
+    uint8_t *sk_codes = nullptr;
 };
 
 // LDS used by one chunk's scan.
@@ -598,6 +612,38 @@ __device__ __forceinline__ void load_setup(const SelectArgs &a, int b, int g, in
 // re-scored here.  KU: rows per lane per pipeline stage (two stages of
 // 4 * 4 * KU rows are in flight).  Called with sm.pages and sm.qs visible to
 // every thread; ends with the stores issued (not waited for).
+}  // namespace sel
+
+namespace skt {
+// Writes sketch row `row` from a centroid of which this lane holds dims
+// lane * E .. lane * E + E - 1 (E = D / 64), page id `page` (wave-uniform call).
+template <int D>
+__device__ __forceinline__ void encode_row(const float (&x)[D / kWave], int page, size_t row,
+                                           SketchHdr *hdr, uint8_t *codes, int lane) {
+    constexpr int E = D / kWave;
+    uint32_t m = 0u;
+#pragma unroll
+    for (int e = 0; e < E; ++e) m = max(m, __float_as_uint(fabsf(x[e])));
+    const float amax = __uint_as_float(sel::wave_max_u32(m));
+    const float scale = amax / 127.0f;
+    uint32_t packed = 0u;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        float qv = amax > 0.f ? rintf(x[e] / scale) : 0.f;
+        qv = fminf(fmaxf(qv, -127.f), 127.f);
+        packed |= (uint32_t)((int)qv + 128) << (8 * e);
+    }
+    uint8_t *dst = codes + row * D + lane * E;
+    if constexpr (E == 2)
+        *reinterpret_cast<uint16_t *>(dst) = (uint16_t)packed;
+    else
+        *dst = (uint8_t)packed;
+    if (lane == 0) hdr[row] = SketchHdr{page + 1, scale};
+}
+}  // namespace skt
+
+namespace sel {
+
 template <typename T, int D, int KU, bool REFRESH, bool APPEND = false>
 __device__ __forceinline__ void scan_rows(const SelectArgs &a, int b, int g, int j0, int n, int L,
                                           int fp, ScoreSmem &sm, float *crow) {
@@ -685,6 +731,14 @@ __device__ __forceinline__ void scan_rows(const SelectArgs &a, int b, int g, int
             cv[vv] = reinterpret_cast<const floatx4_t *>(row_lds + col * VPL)[vv];
         const float s = row16_sum(row_partial<VPL>(qf, cv));
         if (lane == 0) sm.sc[j - j0] = s;
+        if (a.sk_hdr) {  // the block's sketch row, from the same centroid
+            constexpr int E = D / kWave;
+            float x[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) x[e] = row_lds[lane * E + e];
+            skt::encode_row<D>(x, page, ((size_t)b * a.Hkv + g) * a.max_blocks + j, a.sk_hdr,
+                               a.sk_codes, lane);
+        }
         __builtin_amdgcn_wave_barrier();
     }
     __syncthreads();

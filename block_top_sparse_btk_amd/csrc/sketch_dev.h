@@ -38,10 +38,6 @@ namespace skt {
 using sel::kThreads;
 using sel::kWaves;
 
-struct SketchHdr {
-    int32_t page1;
-    float scale;
-};
 
 constexpr float kBoundFactor = 0.51f;
 
@@ -52,31 +48,6 @@ struct SketchArgs {
     float *exact;     // [units * max_blocks] exact scores when every block is scored (workspace)
 };
 
-// Writes sketch row `row` from a centroid of which this lane holds dims
-// lane * E .. lane * E + E - 1 (E = D / 64), page id `page` (wave-uniform call).
-template <int D>
-__device__ __forceinline__ void encode_row(const float (&x)[D / kWave], int page, size_t row,
-                                           SketchHdr *hdr, uint8_t *codes, int lane) {
-    constexpr int E = D / kWave;
-    uint32_t m = 0u;
-#pragma unroll
-    for (int e = 0; e < E; ++e) m = max(m, __float_as_uint(fabsf(x[e])));
-    const float amax = __uint_as_float(sel::wave_max_u32(m));
-    const float scale = amax / 127.0f;
-    uint32_t packed = 0u;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        float qv = amax > 0.f ? rintf(x[e] / scale) : 0.f;
-        qv = fminf(fmaxf(qv, -127.f), 127.f);
-        packed |= (uint32_t)((int)qv + 128) << (8 * e);
-    }
-    uint8_t *dst = codes + row * D + lane * E;
-    if constexpr (E == 2)
-        *reinterpret_cast<uint16_t *>(dst) = (uint16_t)packed;
-    else
-        *dst = (uint8_t)packed;
-    if (lane == 0) hdr[row] = SketchHdr{page + 1, scale};
-}
 
 // Scores read from LDS (see sel::PlainScores).
 struct LdsScores {
@@ -122,7 +93,7 @@ __device__ __forceinline__ void query_sums(const float *qs, float *out) {
 // (sel::select_topk_wg4).  count: LDS of KMAX * kWaves words (may alias
 // sm.cand), total: one LDS word.  LDS: the ends are in this workgroup's LDS
 // (plain loads) instead of the workspace (agent-scope loads); every end is read
-// before the first barrier, so map may alias lo_src (KMAX <= 8).
+// before map is written (two barriers later), so map may alias lo_src.
 // MAXP: at most that many radix passes; tau is then a lower bound of the kb-th
 // largest lower end (the lower edge of its bin), which admits more candidates
 // but keeps every block that can be selected.
@@ -231,7 +202,7 @@ __device__ __forceinline__ int threshold_candidates_wg4(const float *lo_src, con
 }
 
 // Dispatch on nb (at most 32 keys per thread: 8192 blocks; ends in LDS: at
-// most 2048 blocks), kb < nb.
+// most 4096 blocks), kb < nb.
 template <bool LDS = false, int MAXP = sel::kTopkPasses>
 __device__ __forceinline__ int threshold_candidates(const float *lo, const float *hi, int nb,
                                                     int kb, int32_t *map, int cap,
@@ -239,10 +210,10 @@ __device__ __forceinline__ int threshold_candidates(const float *lo, const float
                                                     int *total) {
     if (nb <= 4 * kThreads)
         return threshold_candidates_wg4<4, LDS, MAXP>(lo, hi, nb, kb, map, cap, sm, count, total);
-    if (LDS || nb <= 8 * kThreads)
+    if (nb <= 8 * kThreads)
         return threshold_candidates_wg4<8, LDS, MAXP>(lo, hi, nb, kb, map, cap, sm, count, total);
-    if (nb <= 16 * kThreads)
-        return threshold_candidates_wg4<16>(lo, hi, nb, kb, map, cap, sm, count, total);
+    if (LDS || nb <= 16 * kThreads)  // (the ends in LDS: at most 4096 blocks)
+        return threshold_candidates_wg4<16, LDS, MAXP>(lo, hi, nb, kb, map, cap, sm, count, total);
     return threshold_candidates_wg4<32>(lo, hi, nb, kb, map, cap, sm, count, total);
 }
 

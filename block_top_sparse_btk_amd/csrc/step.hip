@@ -59,8 +59,8 @@ struct StepArgs {
     uint32_t *steal;  // scan chunks taken (a line of its own)
     unsigned long long *claims;  // [2][kMaxStepGrid * kClaimStride]: a share is taken when
                                  // its word's low 32 bits go from 0 to 1
-    // with sketches (NULL hdr otherwise): the sketch rows, the interval ends and
-    // the exact scores of a unit whose candidates exceed kStepCand; per unit the
+    // with sketches (NULL hdr otherwise): the sketch rows and the exact-score
+    // area of a unit that scores every block (the unit kernel); per unit the
     // number of blocks whose fp32 row the selection read, or NULL
     skt::SketchArgs k;
     int32_t *cand_counts;
@@ -89,26 +89,17 @@ constexpr int kRun = 2048;       // blocks per scan run: shares (~550 blocks at 
 #define BTK_STEP_SEGMENT_COST 520
 #endif
 constexpr int kSegmentCost = BTK_STEP_SEGMENT_COST;
-// The same with sketches: a sketch row streams ~136 bytes instead of a 512-byte
-// centroid row, so a segment's fixed costs stand for more rows.
-#ifndef BTK_STEP_SKETCH_SEGMENT_COST
-#define BTK_STEP_SKETCH_SEGMENT_COST 512
-#endif
-constexpr int kSketchSegmentCost = BTK_STEP_SKETCH_SEGMENT_COST;
-template <bool SKETCH>
-constexpr uint32_t segment_cost() {
-    return SKETCH ? (uint32_t)kSketchSegmentCost : (uint32_t)kSegmentCost;
-}
-// With sketches: candidates (blocks whose sketch interval reaches the
-// threshold) that a phase-2 item scores exactly from LDS; beyond, it scores
-// every block of the unit.
+// With sketches (the unit kernel): candidates (blocks whose sketch interval
+// reaches the threshold) scored exactly from LDS; beyond, every block is scored.
 constexpr int kStepCand = 1024;
 constexpr int kRowPer = kRun / kThreads;  // block-table entries per thread (phase 2)
+// The unit kernel's block limit per sequence: its intervals, page ids and
+// touched-block scores sit in LDS (16 bytes a block, 48 KB at 3072 blocks),
+// leaving two workgroups per CU at D = 128 bf16.  Tables a little wider than
+// a power of two (a slot kept for the next page) stay within it.
+constexpr int kUnitRun = 3072;
+constexpr int kUnitRowPer = kUnitRun / kThreads;
 constexpr int step_qn(int D) { return (kMaxGroup * D + kThreads - 1) / kThreads; }
-// Header loads per lane per sketch-scan stage (a stage is 64 * HK rows per wave).
-#ifndef BTK_SKETCH_HK
-#define BTK_SKETCH_HK 1
-#endif
 // The last 1/kStealFrac of the rows is handed out in chunks of kStealRows to the
 // workgroups that finish their static share first.
 #ifndef BTK_STEP_STEAL_FRAC
@@ -118,16 +109,6 @@ constexpr int step_qn(int D) { return (kMaxGroup * D + kThreads - 1) / kThreads;
 #define BTK_STEP_STEAL_ROWS 256
 #endif
 constexpr int kStealFrac = BTK_STEP_STEAL_FRAC;
-// The same with sketches (0: no stolen chunks, every row in the static shares).
-#ifndef BTK_STEP_SKETCH_STEAL_FRAC
-#define BTK_STEP_SKETCH_STEAL_FRAC 0
-#endif
-template <bool SKETCH>
-constexpr uint64_t stolen_rows(uint64_t R) {
-    constexpr uint64_t kSketchFrac = BTK_STEP_SKETCH_STEAL_FRAC;
-    return SKETCH ? (kSketchFrac > 0 ? R / (kSketchFrac > 0 ? kSketchFrac : 1) : 0)
-                  : R / kStealFrac;
-}
 // Sequences whose row prefix a workgroup holds in LDS at once; a larger batch is
 // walked window by window (the prologue keeps only each window's first row).
 constexpr int kWin = 1024;
@@ -174,11 +155,10 @@ __device__ __forceinline__ void append_to_cache(const StepArgs &a, int b, int g,
 __device__ __forceinline__ int valid_len(int L, int max_blocks) {
     return L >= 1 && L <= max_blocks * kPage ? L : -1;
 }
-// Rows of a sequence's units in the share cut: per unit segment_cost() charged
+// Rows of a sequence's units in the share cut: per unit kSegmentCost charged
 // rows, then one per block (one placeholder row for an invalid length).
-template <bool SKETCH>
 __device__ __forceinline__ uint32_t unit_rows(int L, int Hkv) {
-    return (uint32_t)Hkv * (segment_cost<SKETCH>() + (uint32_t)(L >= 0 ? (L + kPage - 1) / kPage : 1));
+    return (uint32_t)Hkv * ((uint32_t)kSegmentCost + (uint32_t)(L >= 0 ? (L + kPage - 1) / kPage : 1));
 }
 // The position whose block the step refreshes (S1): with the KV append the
 // newest token, else first_pos (none when it is NULL or the length is invalid).
@@ -188,61 +168,9 @@ __device__ __forceinline__ int touched_pos(const StepArgs &a, int b, int L) {
     return a.s.first_pos ? a.s.first_pos[b] : -1;
 }
 
-// With sketches: the sketch intervals of blocks [j0, j1) of unit (b, g) (a
-// sequence of length L with nb blocks, decode position fp; nb < 0: an invalid
-// length, whose single placeholder row writes -1 indices) into the workspace,
-// then counted in on the unit.  The touched blocks (j >= fp / 16) get (-inf,
-// +inf): the unit's phase-2 item recomputes them (S1) and scores them itself.
-template <typename T, int D>
-__device__ __forceinline__ void sketch_segment(const StepArgs &a, int b, int g, int j0, int j1, int nb, int L,
-                               int fp, sel::ScoreSmem &sm, float *qsum, uint32_t *ready,
-                               uint32_t tag) {
-    const int unit = b * a.s.Hkv + g;
-    if (nb < 0) {
-        sel::invalid_unit(a.s, unit, ready, tag);
-        return;
-    }
-    const bool refresh = a.s.first_pos && fp >= 0 && fp < L;
-    const int jt = refresh ? fp / kPage : nb;  // the first touched block
-    // the group's queries are requested first; they go to LDS and form the
-    // scaled mean query while the scan's first rows are in flight
-    const int tid = threadIdx.x, r = a.s.Hq / a.s.Hkv;
-    const T *qp = static_cast<const T *>(a.s.q) + ((size_t)b * a.s.Hq + (size_t)g * r) * D;
-    float qv[step_qn(D)];
-#pragma unroll
-    for (int k = 0; k < step_qn(D); ++k)
-        qv[k] = sel::load_q<T>(qp + min(k * kThreads + tid, r * D - 1));
-    auto prep = [&]() {
-#pragma unroll
-        for (int k = 0; k < step_qn(D); ++k)
-            if (k * kThreads + tid < r * D) sm.qraw[k * kThreads + tid] = qv[k];
-        __syncthreads();
-        sel::mean_query<D>(a.s, sm);
-        __syncthreads();
-        skt::query_sums<D>(sm.qs, qsum);
-        __syncthreads();
-    };
-    // in runs of up to kRun blocks staged in LDS (sm.sc, and sm.pages as floats)
-    float *lo_lds = sm.sc, *hi_lds = reinterpret_cast<float *>(sm.pages);
-    const size_t urow = (size_t)unit * a.s.max_blocks;
-    for (int s0 = j0; s0 < j1; s0 += kRun) {
-        const int n = min(kRun, j1 - s0);
-        if (s0 == j0)
-            skt::scan_sketch<D, BTK_SKETCH_HK>(a.s, a.k, b, g, s0, n, sm.qs, qsum, jt, lo_lds,
-                                               hi_lds, prep);
-        else
-            skt::scan_sketch<D, BTK_SKETCH_HK>(a.s, a.k, b, g, s0, n, sm.qs, qsum, jt, lo_lds,
-                                               hi_lds, [] {});
-        __syncthreads();
-        skt::store_intervals(a.k, urow, s0, n, lo_lds, hi_lds);
-        __syncthreads();  // the staging areas are reused
-    }
-    sel::count_in(a.s, unit, j1 - j0, nb, ready, tag);
-}
-
 // Loads the row prefix of sequences [base, base + wlen) into LDS, rows before
 // the window being `first` (workgroup-uniform call).
-template <bool APPEND, bool SKETCH>
+template <bool APPEND>
 __device__ __forceinline__ void load_window(const StepArgs &a, int base, int wlen, uint32_t first,
                             uint32_t *rows, int *lens, int *fps, int *scan_red) {
     constexpr int kPer = kWin / kThreads;
@@ -259,7 +187,7 @@ __device__ __forceinline__ void load_window(const StepArgs &a, int base, int wle
         uint32_t n = 0;
         if (w < wlen) {
             const int L = valid_len(Ls[i], a.s.max_blocks);
-            n = unit_rows<SKETCH>(L, a.s.Hkv);
+            n = unit_rows(L, a.s.Hkv);
             lens[w] = L;
             fps[w] = touched_pos<APPEND>(a, base + w, L);
         }
@@ -278,157 +206,8 @@ __device__ __forceinline__ void load_window(const StepArgs &a, int base, int wle
 // unit may be split over several items (instances without it carry no split
 // merge, whose code alone made the one-split step slower).
 
-// With sketches, a phase-2 item up to its unit being ready: the group's
-// queries and, when row_lds, the block-table row go to LDS and the scaled mean
-// query is formed; then wave 0 waits for the unit (bounded spin on its ready
-// word) while waves 1-3 refresh the touched blocks j >= jt (S1: blocks jt + w -
-// 1, jt + w + 2, ... in wave w): centroid recomputed from the keys (stored;
-// each split stores the same values), exact score (as the full scan scores a
-// refreshed block, into the workspace's score area) and sketch row rebuilt.
-// None of the refresh reads what phase 1 writes.  WAIT = false: no wait (the
-// unit's intervals are this workgroup's own).
-template <typename T, int D, bool WAIT = true>
-__device__ __forceinline__ void sketch_item_setup(const StepArgs &a, int unit, int b, int L, int nb, int jt,
-                                  const float (&qv)[step_qn(D)], bool row_lds,
-                                  const int32_t (&prow)[kRowPer], sel::ScoreSmem &sm,
-                                  float *crow, uint32_t tag) {
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const int g = unit % a.s.Hkv, r = a.s.Hq / a.s.Hkv;
-    const int32_t *bt_row = a.s.bt + (size_t)b * a.s.max_blocks;
-    const T *keys = static_cast<const T *>(a.s.k_cache) + (size_t)g * kPage * D;
-    const size_t page_stride = (size_t)a.s.Hkv * kPage * D;
-    // the wave's first touched block: its page id and keys are requested first
-    constexpr int kRefWaves = kWaves - 1;
-    const int jw = wave == 0 ? nb : jt + wave - 1;
-    const int pw = jw < nb ? bt_row[jw] : -1;
-#pragma unroll
-    for (int k = 0; k < step_qn(D); ++k)
-        if (k * kThreads + tid < r * D) sm.qraw[k * kThreads + tid] = qv[k];
-    if (row_lds) {
-#pragma unroll
-        for (int i = 0; i < kRowPer; ++i)
-            if (i * kThreads + tid < nb) sm.pages[i * kThreads + tid] = prow[i];
-    }
-    KeyTile<T, D> kt;
-    const bool pw_ok = pw >= 0 && pw < a.s.num_pages;
-    if (pw_ok) kt.load(keys + (size_t)pw * page_stride, min(kPage, L - jw * kPage), lane);
-    __syncthreads();
-    sel::mean_query<D>(a.s, sm);
-    __syncthreads();
-    constexpr int E = D / kWave, VPL = D / 16;
-    float qf[VPL];
-#pragma unroll
-    for (int e = 0; e < VPL; ++e) qf[e] = sm.qs[(lane % 16) * VPL + e];
-    const size_t urow = (size_t)unit * a.s.max_blocks;
-    if (WAIT && tid == 0) {
-        const uint32_t *rw = a.ready + (size_t)unit * kReadyStride;
-        uint32_t spins = 0;
-        while (__hip_atomic_load(rw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != tag) {
-            if (++spins > a.spin_limit) {  // never expected: report, do not hang
-                flag_error(a.s.err, kErrTimeout);
-                break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-        }
-    }
-    for (int j = jw; j < nb; j += kRefWaves) {
-        const int page = j == jw ? pw : bt_row[j];
-        if (page < 0 || page >= a.s.num_pages) continue;  // scored (and flagged) as -inf
-        const int v = min(kPage, L - j * kPage);
-        float *row_lds = crow + wave * D;
-        if (j != jw) kt.load(keys + (size_t)page * page_stride, v, lane);
-        kt.mean_to(v, a.s.cent_out + ((size_t)page * a.s.Hkv + g) * D, row_lds, true, lane);
-        __builtin_amdgcn_wave_barrier();
-        floatx4_t cv[VPL / 4];
-#pragma unroll
-        for (int vv = 0; vv < VPL / 4; ++vv)
-            cv[vv] = reinterpret_cast<const floatx4_t *>(row_lds + (lane % 16) * VPL)[vv];
-        const float sc = sel::row16_sum(sel::row_partial<VPL>(qf, cv));
-        if (lane == 0) store_relaxed(a.k.exact + urow + j, sc);
-        float x[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) x[e] = row_lds[lane * E + e];
-        skt::encode_row<D>(x, page, urow + j, a.k.hdr, a.k.codes, lane);
-        __builtin_amdgcn_wave_barrier();
-    }
-}
-
-// With sketches, a phase-2 item's selection once its unit is ready (S2 for the
-// candidates, S3): the threshold and the candidates come from the unit's
-// sketch intervals; the candidates are scored exactly from their fp32 rows (the
-// touched blocks' scores from sketch_item_setup) and the k best kept, so the
-// indices equal the full scan's.  A unit with more than kStepCand candidates
-// scores every block (the full scan's code, into the workspace's score area).
-// Ends with the split's entries in `list` and the row in sm.pages, like the
-// full-scan item.  IV_LDS: the interval ends lo_iv / hi_iv are in LDS (the
-// unit kernel's own; cmap and cex may alias them), else in the workspace.
-template <typename T, int D, bool IV_LDS = false>
-__device__ __forceinline__ void select_sketched(const StepArgs &a, int unit, int split, int b, int L, int nb,
-                                int fp, int jt, int lo, int hi, bool row_lds,
-                                sel::ScoreSmem &sm, sel::TopkSmem &tk, int32_t *list,
-                                int32_t *cmap, float *cex, int *ctot, float *crow,
-                                const float *lo_iv, const float *hi_iv) {
-    const int tid = threadIdx.x, g = unit % a.s.Hkv;
-    int32_t *idx = split == 0 ? a.s.indices + (size_t)unit * a.s.top_k : nullptr;
-    const int kb = min(a.s.top_k, nb);
-    int mc = 0;  // blocks whose fp32 row was read
-    // the touched blocks' exact scores are stored (and their sketch rows written)
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    __builtin_amdgcn_s_setprio(3);
-    if (kb == nb) {  // every block is kept (no score is read)
-        sel::select_topk(skt::LdsScores{cex}, nb, a.s.top_k, sel::TopkOut{idx, list, lo, hi}, tk);
-    } else {
-        const size_t urow = (size_t)unit * a.s.max_blocks;
-        const int m = skt::threshold_candidates<IV_LDS>(lo_iv, hi_iv, nb, kb, cmap,
-                                                kStepCand, tk, tk.cand, ctot);
-        if (m <= kStepCand) {
-            skt::rescore<D>(a.s, b, g, cmap, m, sm.pages, row_lds, sm.qs, cex, a.k.exact + urow,
-                            jt);
-            __syncthreads();
-            sel::TopkOut o{idx, list, lo, hi};
-            o.map = cmap;
-            o.mapped = true;
-            if (m <= kThreads)
-                skt::select_ranked(cex, m, a.s.top_k, o, tk.hist, tk.red);
-            else
-                sel::select_topk(skt::LdsScores{cex}, m, a.s.top_k, o, tk);
-            mc = m;
-        } else {  // every block, with the full scan's code
-            sel::SelectArgs ax = a.s;
-            ax.scores = a.k.exact;
-            for (int s0 = 0; s0 < nb; s0 += kRun) {
-                const int n = min(kRun, nb - s0);
-                __syncthreads();  // sm.pages and sm.sc are free
-                for (int i = tid; i < n; i += kThreads)
-                    sm.pages[i] = a.s.bt[(size_t)b * a.s.max_blocks + s0 + i];
-                __syncthreads();
-                sel::check_pages(a.s, sm, n);
-                __syncthreads();
-                // (the touched blocks are recomputed from their keys, as in the full step)
-                sel::scan_rows<T, D, kScanRows, true>(ax, b, g, s0, n, L, fp, sm, crow);
-            }
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the scores are stored
-            __syncthreads();
-            sel::select_topk(sel::PlainScores{a.k.exact + urow}, nb, a.s.top_k,
-                             sel::TopkOut{idx, list, lo, hi}, tk);
-            mc = nb;
-            __syncthreads();
-            if (row_lds) {  // the attention reads the row from LDS
-                for (int i = tid; i < nb; i += kThreads)
-                    sm.pages[i] = a.s.bt[(size_t)b * a.s.max_blocks + i];
-            }
-        }
-    }
-    __builtin_amdgcn_s_setprio(0);
-    if (split == 0 && tid == 0 && a.cand_counts) a.cand_counts[unit] = mc;
-}
-
-// SKETCH: phase 1 scans the sketch rows and phase 2 scores only the candidates
-// exactly (APPEND is not combined with it).
-template <typename T, int D, bool APPEND, bool SPLITS, bool SKETCH>
+template <typename T, int D, bool APPEND, bool SPLITS>
 __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
-    static_assert(!(APPEND && SKETCH), "the fused append has no sketch instance");
     __shared__ float qs[D];
     __shared__ int pages[kRun];
     __shared__ float sc_lds[kRun];
@@ -447,12 +226,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
     __shared__ uint32_t wrows[kMaxStepBatch / kWin + 1];  // rows before each window, then R
     __shared__ int item_s, owns_s;
     __shared__ uint32_t tag_s, bank_s;
-    // with sketches: a unit's candidates (block ids, exact scores), the query
-    // sums of the bound and the candidate count
-    __shared__ int32_t cmap[SKETCH ? kStepCand : 1];
-    __shared__ float cex[SKETCH ? kStepCand : 1];
-    __shared__ float qsum[2];
-    __shared__ int ctot;
     // queries while scoring, top-k keys of long contexts, attention merges
     extern __shared__ float dyn[];
     sel::ScoreSmem sm{dyn, qs, pages, sc_lds, &flag, newtok};
@@ -491,7 +264,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
             uint32_t n = 0;
             if (b < a.B) {
                 const int L = valid_len(Lc, a.s.max_blocks);
-                n = unit_rows<SKETCH>(L, Hkv);
+                n = unit_rows(L, Hkv);
                 if (b < kWin) {
                     lens[b] = L;
                     fps[b] = touched_pos<APPEND>(a, b, L);
@@ -535,7 +308,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
     // then, in a workgroup that holds no phase-2 item, any share still unclaimed
     const int nwin = (a.B + kWin - 1) / kWin;
     const uint64_t R = wrows[nwin];
-    const uint64_t RS = R - stolen_rows<SKETCH>(R);
+    const uint64_t RS = R - R / kStealFrac;
     int base = 0, wlen = min(a.B, kWin);  // the window in LDS
     uint32_t r = 0, r1 = 0;
     if (owns_s) {
@@ -588,13 +361,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
             while (k + 1 < nwin && wrows[k + 1] <= r) ++k;
             base = k * kWin;
             wlen = min(a.B - base, kWin);
-            load_window<APPEND, SKETCH>(a, base, wlen, wrows[k], rows, lens, fps, scan_red);
+            load_window<APPEND>(a, base, wlen, wrows[k], rows, lens, fps, scan_red);
             b = 0;
         }
         if (rows[b] > r) b = 0;
         while (rows[b + 1] <= r) ++b;
         const int nb = lens[b] < 0 ? -1 : (lens[b] + kPage - 1) / kPage;
-        constexpr uint32_t kCost = segment_cost<SKETCH>();
+        constexpr uint32_t kCost = kSegmentCost;
         const uint32_t per_unit = kCost + (nb < 0 ? 1u : (uint32_t)nb);
         const uint32_t off = r - rows[b];
         const uint32_t g = off / per_unit, o = off % per_unit;  // o < kCost: charged rows
@@ -602,14 +375,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
         const int j0 = (int)(o > kCost ? o - kCost : 0u);
         const int j1 = (int)(e > kCost ? e - kCost : 0u);
         if (j1 > j0) {
-            if constexpr (SKETCH)
-                sketch_segment<T, D>(a, base + b, (int)g, j0, j1, nb, lens[b], fps[b], sm, qsum,
-                                     a.ready + ((size_t)(base + b) * Hkv + g) * kReadyStride,
-                                     tag);
-            else
-                sel::score_segment<T, D, kScanRows, kRun, APPEND>(
-                    a.s, base + b, (int)g, j0, j1, nb, lens[b], fps[b], sm, crow,
-                    a.ready + ((size_t)(base + b) * Hkv + g) * kReadyStride, tag);
+            sel::score_segment<T, D, kScanRows, kRun, APPEND>(
+                a.s, base + b, (int)g, j0, j1, nb, lens[b], fps[b], sm, crow,
+                a.ready + ((size_t)(base + b) * Hkv + g) * kReadyStride, tag);
             __syncthreads();  // LDS is reused by the next segment
         }
         r += e - o;
@@ -641,24 +409,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
         }
         if (APPEND && nb >= 0 && tid >= kWave && tid < 2 * kWave)  // wave 1, beside the poll
             append_to_cache<T, D>(a, bu, unit % Hkv, L, tid - kWave);
-        // with sketches, before the wait: the queries and the row to LDS, and the
-        // touched blocks refreshed (none of it depends on phase 1)
-        int fp = -1, jt = 0;
-        if constexpr (SKETCH) {
-            if (nb >= 0) {
-                fp = bu >= base && bu < base + wlen ? fps[bu - base] : touched_pos<false>(a, bu, L);
-                jt = a.s.first_pos && fp >= 0 && fp < L ? fp / kPage : nb;
-                const int r = a.s.Hq / Hkv;
-                const T *qp = static_cast<const T *>(a.s.q) + ((size_t)bu * a.s.Hq +
-                                                               (size_t)(unit % Hkv) * r) * D;
-                float qv[step_qn(D)];
-#pragma unroll
-                for (int k = 0; k < step_qn(D); ++k)
-                    qv[k] = sel::load_q<T>(qp + min(k * kThreads + tid, r * D - 1));
-                sketch_item_setup<T, D>(a, unit, bu, L, nb, jt, qv, row_lds, prow, sm, crow, tag);
-            }
-        }
-        if (tid == 0 && !(SKETCH && nb >= 0)) {  // (the sketch setup waits itself)
+        if (tid == 0) {
             const uint32_t *rw = a.ready + (size_t)unit * kReadyStride;
             uint32_t spins = 0;
             while (__hip_atomic_load(rw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != tag) {
@@ -671,12 +422,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
         }
         __syncthreads();
         const int lo = split * a.t.bps, hi = min(a.s.top_k, lo + a.t.bps);
-        if (SKETCH && nb >= 0) {
-            select_sketched<T, D>(a, unit, split, bu, L, nb, fp, jt, lo, hi, row_lds, sm, tk, list,
-                                  cmap, cex, &ctot, crow,
-                                  a.k.lo + (size_t)unit * a.s.max_blocks,
-                                  a.k.hi + (size_t)unit * a.s.max_blocks);
-        } else if (!SKETCH && nb >= 0) {
+        if (nb >= 0) {
             __builtin_amdgcn_s_setprio(3);
             sel::select_topk(sel::PlainScores{a.s.scores + (size_t)unit * a.s.max_blocks}, nb,
                              a.s.top_k,
@@ -686,7 +432,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
                              tk);
             __builtin_amdgcn_s_setprio(0);
         }
-        if (!SKETCH && row_lds) {
+        // through btk_decode_step_sketch: every block's fp32 row was read
+        if (a.cand_counts && split == 0 && tid == 0)
+            a.cand_counts[unit] = nb > a.s.top_k ? nb : 0;
+        if (row_lds) {
 #pragma unroll
             for (int i = 0; i < kRowPer; ++i)
                 if (i * kThreads + tid < nb) pages[i * kThreads + tid] = prow[i];
@@ -722,8 +471,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
 // intervals in LDS, the candidates scored exactly from their fp32 rows, the k
 // best kept, and the unit attended.  Launch bounds 256 x 1: the kernel may use
 // more registers than the persistent one (two workgroups per CU still fit at
-// D = 128 bf16).  Limits (checked on the host): at
-// most kRun blocks per sequence, one attention split, top_k <= 256 and a
+// D = 128 bf16).  Limits (checked on the host): a block table of at
+// most kUnitRun blocks, one attention split, top_k <= 256 and a
 // group of at most 8 heads.  Results are those of the persistent form (the
 // same arithmetic per unit, blocks in the same order).
 // Sketch-row header loads per lane per scan stage: 1, two stages of 256 rows in
@@ -792,9 +541,9 @@ __device__ __forceinline__ void unit_refresh(const StepArgs &a, int unit, int b,
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 1) void decode_step_unit_kernel(StepArgs a) {
     __shared__ float qs[D];
-    __shared__ int pages[kRun];
-    __shared__ float lo_lds[kRun], hi_lds[kRun];  // interval ends; then candidates (cmap, cex)
-    __shared__ float kex[kRun];                    // exact scores of the touched blocks
+    __shared__ int pages[kUnitRun];
+    __shared__ float lo_lds[kUnitRun], hi_lds[kUnitRun];  // interval ends; then candidates
+    __shared__ float kex[kUnitRun];                        // exact scores of the touched blocks
     __shared__ int flag;
     // read as 16-byte vectors (histogram bins, candidate keys): 16-byte aligned
     __shared__ __align__(16) uint32_t hist[sel::kTopkPasses * sel::kHistWords];
@@ -834,9 +583,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_unit_kernel(StepArgs 
     const int32_t *bt_row = a.s.bt + (size_t)b * a.s.max_blocks;
     const int jw = wave == 0 ? nb : jt + wave - 1;
     const int pw = jw < nb ? bt_row[jw] : -1;
-    int32_t prow[kRowPer];
+    int32_t prow[kUnitRowPer];
 #pragma unroll
-    for (int i = 0; i < kRowPer; ++i) prow[i] = bt_row[min(i * kThreads + tid, nb - 1)];
+    for (int i = 0; i < kUnitRowPer; ++i)  // (beyond kRun blocks only for long sequences)
+        prow[i] = i < kRowPer || i * kThreads < nb ? bt_row[min(i * kThreads + tid, nb - 1)] : 0;
     // S2 (sketch): every block's interval into LDS (the touched blocks j >= jt:
     // always candidates); the mean query is formed and the touched keys are
     // requested while the first rows are in flight
@@ -846,7 +596,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_unit_kernel(StepArgs 
         for (int k = 0; k < step_qn(D); ++k)
             if (k * kThreads + tid < r * D) sm.qraw[k * kThreads + tid] = qv[k];
 #pragma unroll
-        for (int i = 0; i < kRowPer; ++i)
+        for (int i = 0; i < kUnitRowPer; ++i)
             if (i * kThreads + tid < nb) pages[i * kThreads + tid] = prow[i];
         if (pw >= 0 && pw < a.s.num_pages)
             kt.load(static_cast<const T *>(a.s.k_cache) +
@@ -928,6 +678,7 @@ hipError_t launch_unit(const Dims &d, const StepArgs &a, hipStream_t stream) {
     size_t n = r * D;                                                 // queries
     const size_t wave_merge = (size_t)att::kWaves * r * D + 2 * att::kWaves * 16;
     n = n > wave_merge ? n : wave_merge;
+    if (d.max_blocks > 32 * kWave && n < 512) n = 512;  // top-k bitmaps beyond 2048 blocks
     hipLaunchKernelGGL((decode_step_unit_kernel<T, D>), dim3((unsigned)a.units), dim3(kThreads),
                        sizeof(float) * n, stream, a);
     return hipGetLastError();
@@ -936,7 +687,7 @@ hipError_t launch_unit(const Dims &d, const StepArgs &a, hipStream_t stream) {
 // The unit kernel serves problems whose units fill the device (at least one per
 // CU) and fit its limits; test_flags bit 1 / bit 2 force it on / off.
 bool use_unit_kernel(const Dims &d, const AttendPlan &ap, int top_k, uint32_t test_flags) {
-    const bool fits = d.max_blocks <= kRun && ap.nsplit_max == 1 && top_k <= 4 * kWave &&
+    const bool fits = d.max_blocks <= kUnitRun && ap.nsplit_max == 1 && top_k <= 4 * kWave &&
                       d.group() <= 8;
     if (!fits || (test_flags & 4u)) return false;
     if (test_flags & 2u) return true;
@@ -956,7 +707,7 @@ size_t step_lds_floats(const Dims &d, const AttendPlan &ap) {
 }
 
 // resident workgroups of the step kernel on this device (cached per device)
-template <typename T, int D, bool APPEND, bool SPLITS, bool SKETCH>
+template <typename T, int D, bool APPEND, bool SPLITS>
 hipError_t resident_workgroups(size_t lds, int *out) {
     static int cached[64][2] = {};
     int dev = 0;
@@ -969,7 +720,7 @@ hipError_t resident_workgroups(size_t lds, int *out) {
     }
     int per_cu = 0, cus = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, decode_step_kernel<T, D, APPEND, SPLITS, SKETCH>, kThreads, lds);
+        &per_cu, decode_step_kernel<T, D, APPEND, SPLITS>, kThreads, lds);
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
@@ -980,12 +731,12 @@ hipError_t resident_workgroups(size_t lds, int *out) {
     return hipSuccess;
 }
 
-template <typename T, int D, bool APPEND, bool SPLITS, bool SKETCH>
+template <typename T, int D, bool APPEND, bool SPLITS>
 hipError_t launch_instance(size_t lds, const StepArgs &a, hipStream_t stream) {
     int grid = 0;
-    const hipError_t e = resident_workgroups<T, D, APPEND, SPLITS, SKETCH>(lds, &grid);
+    const hipError_t e = resident_workgroups<T, D, APPEND, SPLITS>(lds, &grid);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_step_kernel<T, D, APPEND, SPLITS, SKETCH>), dim3(grid), dim3(kThreads),
+    hipLaunchKernelGGL((decode_step_kernel<T, D, APPEND, SPLITS>), dim3(grid), dim3(kThreads),
                        lds, stream, a);
     return hipGetLastError();
 }
@@ -997,21 +748,21 @@ hipError_t launch(const Dims &d, const SelectPlan &sp, const AttendPlan &ap, Ste
     const bool splits = ap.nsplit_max > 1;
     if (a.k.hdr && use_unit_kernel(d, ap, a.s.top_k, a.test_flags))
         return launch_unit<T, D>(d, a, stream);
-    if (a.k.hdr)
-        return splits ? launch_instance<T, D, false, true, true>(lds, a, stream)
-                      : launch_instance<T, D, false, false, true>(lds, a, stream);
+    if (a.k.hdr) {  // too few units: the persistent fp32 scan, keeping the sketch current
+        a.s.sk_hdr = a.k.hdr;
+        a.s.sk_codes = a.k.codes;
+    }
     if (a.s.k_new)
-        return splits ? launch_instance<T, D, true, true, false>(lds, a, stream)
-                      : launch_instance<T, D, true, false, false>(lds, a, stream);
-    return splits ? launch_instance<T, D, false, true, false>(lds, a, stream)
-                  : launch_instance<T, D, false, false, false>(lds, a, stream);
+        return splits ? launch_instance<T, D, true, true>(lds, a, stream)
+                      : launch_instance<T, D, true, false>(lds, a, stream);
+    return splits ? launch_instance<T, D, false, true>(lds, a, stream)
+                  : launch_instance<T, D, false, false>(lds, a, stream);
 }
 
 }  // namespace
 
-bool step_rows_fit(const Dims &d, bool sketch) {
-    const uint64_t cost = sketch ? kSketchSegmentCost : kSegmentCost;
-    return (uint64_t)d.B * (uint64_t)d.Hkv * ((uint64_t)d.max_blocks + cost) <
+bool step_rows_fit(const Dims &d) {
+    return (uint64_t)d.B * (uint64_t)d.Hkv * ((uint64_t)d.max_blocks + kSegmentCost) <
            ((uint64_t)1 << 32);
 }
 

@@ -312,20 +312,21 @@ btk_status_t btk_decode_step(const btk_problem_t *problem, const void *q, const 
 
 /* btk_decode_step reading each unit's sketch rows (see btk_sketch_bytes) in
  * place of its fp32 centroid rows, with results identical to btk_decode_step
- * (indices, out, lse and centroids bit for bit).  Phase 1 computes every
- * block's sketch interval (as btk_select_sketch); the touched blocks (j >=
- * first_pos[b] / 16) get their centroid recomputed from the keys and then their
- * sketch row rebuilt from it, as btk_centroid_update and btk_sketch_update with
- * the same first_pos would, and are always kept as candidates.  Each (sequence,
- * KV head) then takes the k_b-th largest lower end as threshold, scores the
- * blocks whose upper end reaches it from their fp32 centroid rows exactly as
- * btk_select scores them, keeps the k_b best with btk_select's tie rule and
- * attends.  A unit with more than 1024 such candidates scores every block.
- * When there are at least as many units as compute units and the problem fits
- * one workgroup per unit (max_blocks_per_seq <= 2048, top_k <= 256, at most 8
- * query heads per KV head, one attention split), each unit is done whole by one
- * workgroup and no workgroup waits for another; otherwise the step runs in the
- * persistent form of btk_decode_step.  The results do not depend on which.
+ * (indices, out, lse and centroids bit for bit).  When there are at least as
+ * many (sequence, KV head) units as compute units and the problem fits one
+ * workgroup per unit (max_blocks_per_seq <= 3072, top_k <= 256, at most 8 query
+ * heads per KV head, one attention split), each unit is done whole by one
+ * workgroup, and no workgroup waits for another: it computes every block's
+ * sketch interval (as btk_select_sketch); recomputes the touched blocks' (j >=
+ * first_pos[b] / 16) centroids from the keys and rebuilds their sketch rows
+ * from them, as btk_centroid_update and btk_sketch_update with the same
+ * first_pos would, keeping them as candidates; takes the k_b-th largest lower
+ * end as threshold, scores the blocks whose upper end reaches it from their
+ * fp32 centroid rows exactly as btk_select scores them (every block when more
+ * than 1024 do), keeps the k_b best with btk_select's tie rule and attends.
+ * With fewer units the step is btk_decode_step's persistent fp32 scan (faster
+ * there), which also rebuilds the touched blocks' sketch rows.  The results do
+ * not depend on which.
  * The sketch must hold rows for the blocks before first_pos built from their
  * current centroids (btk_sketch_update after prefill; every call keeps the
  * rows of the blocks it touches current); a row that does not name its block's
@@ -336,9 +337,8 @@ btk_status_t btk_decode_step(const btk_problem_t *problem, const void *q, const 
  *   sketch       in/out, sketch_bytes >= btk_sketch_bytes(problem)
  *   cand_counts  out [B][Hkv] int32, or NULL: per unit the number of blocks
  *                whose fp32 centroid row the selection read (0 when every
- *                block is kept)
- *   other arguments, limits and errors as btk_decode_step, with
- *   batch * num_kv_heads * (max_blocks_per_seq + 512) < 2^32. */
+ *                block is kept; n_b in the fp32 scan)
+ *   other arguments, limits and errors as btk_decode_step. */
 btk_status_t btk_decode_step_sketch(const btk_problem_t *problem, const void *q,
                                     const void *k_cache, const void *v_cache,
                                     const int32_t *block_table, const int32_t *seq_lens,

@@ -57,7 +57,15 @@ CASES = [("config1", dict(cfg=1)), ("config2", dict(cfg=2)), ("config3", dict(cf
          ("windows-3000-hkv1", dict(kw=dict(batch=3000, num_q_heads=4, num_kv_heads=1,
                                             head_dim=128,
                                             seq_lens=[1 + (i * 7919) % 400 for i in range(3000)],
-                                            top_k=8, seed=36)))]
+                                            top_k=8, seed=36))),
+         # block tables wider than 2048 blocks, up to the unit kernel's 3072
+         ("long-3072-blocks", dict(kw=dict(batch=3, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                                           seq_lens=[3072 * 16, 2049 * 16 + 3, 700], top_k=40,
+                                           seed=40, max_blocks=3072))),
+         ("long-2600-fp32-d64", dict(kw=dict(batch=2, num_q_heads=4, num_kv_heads=1,
+                                             head_dim=64, seq_lens=[2600 * 16 - 9, 2100 * 16],
+                                             top_k=17, seed=41, max_blocks=2601,
+                                             dtype=torch.float32)))]
 
 _CACHE = {}
 
@@ -124,10 +132,10 @@ def _check_counts(counts, bt, k):
 
 # Which kernel the sketched step runs (BTK_STEP_TEST_FLAGS, read at each call):
 # "auto" the library's choice (one workgroup per unit when the units fill the
-# device, else the persistent two-phase kernel), "unit" the one-workgroup-per-
-# unit kernel wherever its limits allow (small batches too; the Best-of-N and
-# 32B cases exceed them), "persistent" never (the batches where auto takes the
-# unit kernel).
+# device, else the persistent kernel's fp32 scan, which rebuilds the touched
+# blocks' sketch rows), "unit" the one-workgroup-per-unit kernel wherever its
+# limits allow (small batches too; the Best-of-N and 32B cases exceed them),
+# "persistent" never (the batches where auto takes the unit kernel).
 MODES = {"auto": "0", "unit": "2", "persistent": "4"}
 _UNIT_AUTO = {"config2", "config3", "batch-1024", "windows-3000-hkv1"}
 MODE_CASES = ([(lab, sp, "auto") for lab, sp in CASES]
