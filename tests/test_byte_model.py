@@ -72,3 +72,24 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode != 0
     assert "one GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
+
+
+def test_sketch_step_bytes():
+    lens, hq, hkv, D, k, e = [1000, 20, 4000], 8, 2, 128, 16, 2
+    sel = [[16 * k] * hkv, [20] * hkv, [16 * k] * hkv]
+    step = bench.algorithmic_bytes(lens, hq, hkv, D, k, e, sel_tokens=sel)["step"]
+    units = len(lens) * hkv
+    nbs = [(L + 15) // 16 for L in lens]
+    # the fp32-scan kernel: the step's bytes plus the rebuilt sketch row of each unit
+    fp32 = bench.sketch_step_bytes(lens, hq, hkv, D, k, e, [[n] * hkv for n in nbs], sel,
+                                   fp32_scan=True)
+    assert fp32 == step + units * (D + 8)
+    # the unit kernel: every fp32 row replaced by the block's sketch row, plus the
+    # m candidates' fp32 rows
+    m = [[3, 5], [0, 0], [40, 7]]
+    unit = bench.sketch_step_bytes(lens, hq, hkv, D, k, e, m, sel)
+    want = step + units * (D + 8)
+    for n, mm in zip(nbs, m):
+        for x in mm:
+            want += n * (D + 8) - 4 * D * n + 4 * D * x
+    assert unit == want
