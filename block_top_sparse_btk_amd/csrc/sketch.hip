@@ -117,7 +117,8 @@ __global__ __launch_bounds__(kThreads, 4) void select_sketch_kernel(sel::SelectA
     float *lo_lds = sc_lds, *hi_lds = reinterpret_cast<float *>(pages);
     for (int s0 = j0; s0 < j0 + n; s0 += kMaxChunk) {
         const int nr = min(kMaxChunk, j0 + n - s0);
-        skt::scan_sketch<D, 1>(a, s, b, g, s0, nr, qs, qsum_s, nb, lo_lds, hi_lds, [] {});
+        skt::scan_sketch<D, 1>(a, s, b, g, s0, nr, [&] { return make_int2(nr, nb); }, qs, qsum_s,
+                               lo_lds, hi_lds, [] {});
         __syncthreads();
         skt::store_intervals(s, (size_t)unit * a.max_blocks, s0, nr, lo_lds, hi_lds);
         __syncthreads();  // the staging areas are reused

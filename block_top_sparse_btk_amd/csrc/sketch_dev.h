@@ -228,17 +228,21 @@ __device__ __forceinline__ int threshold_candidates(const float *lo, const float
 // registers instead of 7 KU.  qs: the scaled mean query (LDS); qsum (LDS):
 // q128 = 128 * sum(qs), qn1 = sum |qs|; both are read after prep(), which the
 // scan calls (workgroup-uniformly) once its first stage is requested, so that
-// the caller can form them while those rows are in flight.  Blocks j >= jforce
-// (refreshed in this call) and rows whose header does not name the block's page
-// get (-inf, +inf): always candidates.  Nothing is stored to memory inside the
+// the caller can form them while those rows are in flight.  The first stage's
+// rows are clamped to cap rows (cap >= n, within the unit's rows) and only then
+// is lens() called for (n, jforce), so a caller whose length is still in flight
+// passes cap = the table width and reads the length in lens(); prep() runs only
+// when n > 0.  Blocks j >= jforce (refreshed in this call) and rows whose header
+// does not name the block's page get (-inf, +inf): always candidates.  Nothing is stored to memory inside the
 // loop: stores count in the same in-order memory counter as the loads, so a
 // store issued there would hold up the wait for the next stage's rows until it
 // completed.
-template <int D, int HK, typename Prep>
+template <int D, int HK, typename Lens, typename Prep>
 __device__ __forceinline__ void scan_sketch(const sel::SelectArgs &a, const SketchArgs &s, int b,
-                                            int g, int j0, int n, const float *qs,
-                                            const float *qsum, int jforce, float *lo_lds,
-                                            float *hi_lds, Prep &&prep) {
+                                            int g, int j0, int cap, Lens &&lens, const float *qs,
+                                            const float *qsum, float *lo_lds, float *hi_lds,
+                                            Prep &&prep) {
+    int n = cap, jforce = 0;  // (n: the first stage's clamp until lens() is read)
     constexpr int LPR = D / 16;          // lanes per row
     constexpr int RPW = kWave / LPR;     // rows per wave per load
     constexpr int KU = HK * LPR;         // load steps per stage: HK * 64 rows per wave
@@ -316,9 +320,14 @@ __device__ __forceinline__ void scan_sketch(const sel::SelectArgs &a, const Sket
             }
         }
     };
+    Stage sa_, sb_;
+    if (cap > 0) issue(sa_, 0);
+    {
+        const int2 nj = lens();
+        n = nj.x;
+        jforce = nj.y;
+    }
     if (n > 0) {
-        Stage sa_, sb_;
-        issue(sa_, 0);
         prep();
 #pragma unroll
         for (int e = 0; e < 16; ++e) qf[e] = qs[16 * part + e];

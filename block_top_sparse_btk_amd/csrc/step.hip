@@ -463,10 +463,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepArgs a) {
 
 // With sketches, when the units fill the device: one workgroup per (sequence,
 // KV head) unit does the whole step for it, so no workgroup waits for another.
-// The queries, the length, the block-table row, the touched block's page id
-// and keys are requested first; the unit's sketch rows are scanned into
-// intervals held in LDS (the mean query is formed while the first rows are in
-// flight); then the touched blocks are refreshed (S1: centroid, exact score
+// The queries, the length, the block-table row (clamped to the table) and the
+// first 256 sketch rows (likewise) are requested together, before the length
+// is known; the unit's sketch rows are scanned into intervals held in LDS (the
+// mean query is formed, and the touched block's keys are requested, while the
+// first rows are in flight); then the touched blocks are refreshed (S1: centroid, exact score
 // kept in LDS, sketch row), the threshold and the candidates taken from the
 // intervals in LDS, the candidates scored exactly from their fp32 rows, the k
 // best kept, and the unit attended.  Launch bounds 256 x 1: the kernel may use
@@ -566,8 +567,43 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_unit_kernel(StepArgs 
 #pragma unroll
     for (int k = 0; k < step_qn(D); ++k)
         qv[k] = sel::load_q<T>(qp + min(k * kThreads + tid, r * D - 1));
-    const int L = valid_len(a.s.seq_lens[b], a.s.max_blocks);
-    const int fp = touched_pos<false>(a, b, L);
+    const int Lraw = a.s.seq_lens[b];
+    const int fpraw = a.s.first_pos ? a.s.first_pos[b] : -1;
+    const int32_t *bt_row = a.s.bt + (size_t)b * a.s.max_blocks;
+    // the block-table row, clamped to the table (requested before the length is known)
+    int32_t prow[kUnitRowPer];
+#pragma unroll
+    for (int i = 0; i < kUnitRowPer; ++i)
+        prow[i] = i < kRowPer || i * kThreads < a.s.max_blocks
+                      ? bt_row[min(i * kThreads + tid, a.s.max_blocks - 1)] : 0;
+    int L = -1, fp = -1, nb = 0, jt = 0, jw = 0, pw = -1;
+    KeyTile<T, D> kt;
+    skt::scan_sketch<D, BTK_UNIT_HK>(a.s, a.k, b, g, 0, a.s.max_blocks, [&] {
+        L = valid_len(Lraw, a.s.max_blocks);
+        fp = L >= 0 ? fpraw : -1;
+        nb = L >= 0 ? (L + kPage - 1) / kPage : 0;
+        jt = a.s.first_pos && fp >= 0 && fp < L ? fp / kPage : nb;
+        return make_int2(nb, jt);
+    }, sm.qs, qsum, lo_lds, hi_lds, [&] {
+#pragma unroll
+        for (int k = 0; k < step_qn(D); ++k)
+            if (k * kThreads + tid < r * D) sm.qraw[k * kThreads + tid] = qv[k];
+#pragma unroll
+        for (int i = 0; i < kUnitRowPer; ++i)
+            if (i * kThreads + tid < nb) pages[i * kThreads + tid] = prow[i];
+        __syncthreads();
+        // this wave's first touched block's page (from LDS) and keys
+        jw = wave == 0 ? nb : jt + wave - 1;
+        pw = jw < nb ? pages[jw] : -1;
+        if (pw >= 0 && pw < a.s.num_pages)
+            kt.load(static_cast<const T *>(a.s.k_cache) +
+                        ((size_t)pw * Hkv + g) * kPage * D,
+                    min(kPage, L - jw * kPage), lane);
+        sel::mean_query<D>(a.s, sm);
+        __syncthreads();
+        skt::query_sums<D>(sm.qs, qsum);
+        __syncthreads();
+    });
     if (L < 0) {  // -1 indices, the error flagged; no output (as the persistent form)
         for (int i = tid; i < a.s.top_k; i += kThreads)
             a.s.indices[(size_t)unit * a.s.top_k + i] = -1;
@@ -577,37 +613,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_unit_kernel(StepArgs 
         }
         return;
     }
-    const int nb = (L + kPage - 1) / kPage;
-    const int jt = a.s.first_pos && fp >= 0 && fp < L ? fp / kPage : nb;  // first touched block
-    // the block-table row and the page id of this wave's first touched block
-    const int32_t *bt_row = a.s.bt + (size_t)b * a.s.max_blocks;
-    const int jw = wave == 0 ? nb : jt + wave - 1;
-    const int pw = jw < nb ? bt_row[jw] : -1;
-    int32_t prow[kUnitRowPer];
-#pragma unroll
-    for (int i = 0; i < kUnitRowPer; ++i)  // (beyond kRun blocks only for long sequences)
-        prow[i] = i < kRowPer || i * kThreads < nb ? bt_row[min(i * kThreads + tid, nb - 1)] : 0;
-    // S2 (sketch): every block's interval into LDS (the touched blocks j >= jt:
-    // always candidates); the mean query is formed and the touched keys are
-    // requested while the first rows are in flight
-    KeyTile<T, D> kt;
-    skt::scan_sketch<D, BTK_UNIT_HK>(a.s, a.k, b, g, 0, nb, sm.qs, qsum, jt, lo_lds, hi_lds, [&] {
-#pragma unroll
-        for (int k = 0; k < step_qn(D); ++k)
-            if (k * kThreads + tid < r * D) sm.qraw[k * kThreads + tid] = qv[k];
-#pragma unroll
-        for (int i = 0; i < kUnitRowPer; ++i)
-            if (i * kThreads + tid < nb) pages[i * kThreads + tid] = prow[i];
-        if (pw >= 0 && pw < a.s.num_pages)
-            kt.load(static_cast<const T *>(a.s.k_cache) +
-                        ((size_t)pw * Hkv + g) * kPage * D,
-                    min(kPage, L - jw * kPage), lane);
-        __syncthreads();
-        sel::mean_query<D>(a.s, sm);
-        __syncthreads();
-        skt::query_sums<D>(sm.qs, qsum);
-        __syncthreads();
-    });
     // S1 for the touched blocks, then S3
     unit_refresh<T, D>(a, unit, b, L, nb, jt, pw, kt, sm.qs, crow, kex);
     __syncthreads();
